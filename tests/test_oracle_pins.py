@@ -1,0 +1,533 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle:
+closed forms, invariants, special cases that reduce to library routines,
+brute-force ranking on tiny inputs and hand-derived fixtures.
+
+Each group names the property of the pages it checks.  A plausible mistake in
+the oracle (a dropped term, a wrong sign or index, a transposed operand, a
+wrong block boundary) fails at least one of them; see the
+``test_planted_mistakes_are_caught`` group at the end, which plants such
+mistakes in copies of oracle functions and checks that the pins notice.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs as oc
+from oracle import csa as O
+
+RNG = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------------------
+# codecs: against the format definitions and torch's own conversions
+# ---------------------------------------------------------------------------
+def test_bf16_decode_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint16)
+    ours = oc.bf16_to_f64(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3_decode_all_codes_match_torch_and_closed_form():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oc.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6 and ours[0x38] == 1.0
+    assert ours[0x80] == 0.0 and math.copysign(1, ours[0x80]) == -1
+
+
+def test_bf16_rne_matches_torch_and_ties():
+    x = RNG.standard_normal(20000).astype(np.float32) * np.float32(1e3)
+    ours = oc.f64_to_bf16_value(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(ours, ref)
+    # ties go to even: 1 + 2^-8 is halfway between 1 and 1 + 2^-7
+    assert oc.f64_to_bf16_value(1 + 2.0 ** -8) == 1.0
+    assert oc.f64_to_bf16_value(1 + 3 * 2.0 ** -8) == 1 + 2.0 ** -6
+    assert oc.f64_to_bf16_value(2.0 ** -133) == 2.0 ** -133          # smallest subnormal
+    assert oc.f64_to_bf16_value(2.0 ** -134) == 0.0                   # tie to even (0)
+
+
+def test_e4m3_rne_sat_matches_torch_and_ties():
+    x = (RNG.standard_normal(20000) * 60).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ours = oc.f64_to_e4m3_value(x.astype(np.float64))
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(ours, ref)
+    assert oc.f64_to_e4m3_value(1 + 1 / 16) == 1.0
+    assert oc.f64_to_e4m3_value(1 + 3 / 16) == 1.25
+    assert oc.f64_to_e4m3_value(500.0) == 448.0 and oc.f64_to_e4m3_value(-1e9) == -448.0
+    assert oc.f64_to_e4m3_value(2.0 ** -10) == 0.0                    # half the min subnormal
+    assert oc.f64_to_e4m3_value(3 * 2.0 ** -10) == 2.0 ** -8
+    assert np.array_equal(oc.e4m3_code([1.0, -448.0, 2.0 ** -9]), [0x38, 0xFE, 0x01])
+
+
+def test_oracle_fp8_row_quantisation_is_faithful():
+    E = RNG.standard_normal((5, 128))
+    E[2] = 0.0
+    codes, scale = O.quantize_rows_e4m3(E)
+    assert scale[2] == 1.0 and np.all(codes[2] == 0)
+    dec = oc.e4m3_to_f64(codes) * scale[:, None].astype(np.float64)
+    # |error| <= half an e4m3 ulp at the element's binade (relative 2^-4), plus subnormal slack
+    err = np.abs(dec - E)
+    bound = np.maximum(np.abs(E) * 2.0 ** -4, scale[:, None] * 2.0 ** -10) * 1.0001
+    assert np.all(err <= bound)
+    # the row maximum maps to +-448 exactly
+    j = np.argmax(np.abs(E[0]))
+    assert abs(oc.e4m3_to_f64(codes[0, j])) == 448.0
+
+
+# ---------------------------------------------------------------------------
+# a1 compressor: geometry, convexity, closed forms
+# ---------------------------------------------------------------------------
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def test_compress_golden_geometry(golden_dir):
+    g = _load(golden_dir, "compress_geometry.json")
+    T = g["T"]
+    Ca = np.array(g["C_a"], dtype=np.float64)[:, None]
+    Cb = np.array(g["C_b"], dtype=np.float64)[:, None]
+    for case in g["cases"]:
+        E = O.pool_entries(Ca, None, Cb, None, m=case["m"], overlap=case["overlap"], T=T)
+        assert E.shape == (len(case["expected"]), 1)
+        assert np.allclose(E[:, 0], case["expected"], rtol=0, atol=1e-12), case
+
+
+@pytest.mark.parametrize("T,m,n", [(256, 4, 64), (257, 4, 65), (255, 4, 64), (1, 4, 1),
+                                   (1048576, 128, 8192), (1048577, 128, 8193)])
+def test_entry_count_is_ceil(T, m, n):
+    assert O.num_entries(T, m) == n
+
+
+def test_entry_count_from_pooling():
+    c = 3
+    for T in (256, 257):
+        C = RNG.standard_normal((T, c))
+        E = O.pool_entries(C, C, C, C, m=4, overlap=1, T=T)
+        assert E.shape[0] == math.ceil(T / 4)
+
+
+def test_each_token_feeds_exactly_two_entries():
+    # count candidate memberships from the candidate sets themselves
+    T, m = 37, 4
+    hits = np.zeros(T, dtype=int)
+    for s in range(O.num_entries(T, m)):
+        for _, t in O.candidate_tokens(s, m, 1, T):
+            hits[t] += 1
+    # every token but those of the last (partial) block feeds two entries
+    last_block_start = m * (O.num_entries(T, m) - 1)
+    assert np.all(hits[:last_block_start] == 2)
+    assert np.all(hits[last_block_start:] == 1)
+
+
+def test_constant_rows_pool_to_constant():
+    T, c = 23, 5
+    v = RNG.standard_normal(c)
+    C = np.tile(v, (T, 1))
+    Za, Zb = RNG.standard_normal((T, c)) * 5, RNG.standard_normal((T, c)) * 5
+    for m, ov in ((4, 1), (4, 0), (8, 1), (128, 0)):
+        E = O.pool_entries(C, Za, C, Zb, m=m, overlap=ov, T=T)
+        assert np.allclose(E, v, atol=1e-13)
+
+
+def test_dominant_logit_selects_previous_block_candidate():
+    # C_b / Z_b of token tau feed entry tau//m + 1 (the "previous block" set)
+    T, m, c = 24, 4, 3
+    for tau in (0, 5, 11, 19):
+        Ca = np.zeros((T, c)); Cb = np.zeros((T, c))
+        Za = np.zeros((T, c)); Zb = np.zeros((T, c))
+        Cb[tau] = [1.0, 2.0, 3.0]
+        Zb[tau] = 50.0
+        E = O.pool_entries(Ca, Za, Cb, Zb, m=m, overlap=1, T=T)
+        s = tau // m + 1
+        assert np.allclose(E[s], [1.0, 2.0, 3.0], rtol=1e-15, atol=1e-17 * 1e3 + 1e-20)
+        others = np.delete(E, s, axis=0)
+        assert np.all(others == 0.0)
+
+
+def test_dominant_logit_selects_own_block_candidate():
+    T, m, c = 24, 4, 2
+    tau = 9
+    Ca = RNG.standard_normal((T, c)); Cb = RNG.standard_normal((T, c))
+    Za = np.zeros((T, c)); Zb = np.zeros((T, c))
+    Za[tau] = 60.0
+    E = O.pool_entries(Ca, Za, Cb, Zb, m=m, overlap=1, T=T)
+    assert np.allclose(E[tau // m], Ca[tau], atol=1e-20 + 1e-12)
+
+
+def test_identity_at_m1_without_overlap():
+    T, c = 17, 6
+    C = RNG.standard_normal((T, c))
+    Z = RNG.standard_normal((T, c)) * 10
+    E = O.pool_entries(C, Z, None, None, m=1, overlap=0, T=T)
+    assert np.array_equal(E, C)
+
+
+def test_channels_independent_and_linear_in_C():
+    T, c, m = 30, 7, 4
+    Ca, Cb = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    Za, Zb = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    E = O.pool_entries(Ca, Za, Cb, Zb, m=m, overlap=1, T=T)
+    perm = RNG.permutation(c)
+    Ep = O.pool_entries(Ca[:, perm], Za[:, perm], Cb[:, perm], Zb[:, perm], m=m, overlap=1, T=T)
+    assert np.allclose(Ep, E[:, perm], atol=1e-14)
+    Ca2, Cb2 = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    E2 = O.pool_entries(Ca2, Za, Cb2, Zb, m=m, overlap=1, T=T)
+    E3 = O.pool_entries(2 * Ca - 3 * Ca2, Za, 2 * Cb - 3 * Cb2, Zb, m=m, overlap=1, T=T)
+    assert np.allclose(E3, 2 * E - 3 * E2, atol=1e-12)
+
+
+def test_logit_shift_invariance():
+    # a softmax is unchanged by adding a per-channel constant to all of one entry's logits
+    T, c, m = 16, 4, 4
+    Ca, Cb = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    Z = RNG.standard_normal((T, c))
+    E = O.pool_entries(Ca, Z, Cb, Z, m=m, overlap=1, T=T)
+    E2 = O.pool_entries(Ca, Z + 7.5, Cb, Z + 7.5, m=m, overlap=1, T=T)
+    assert np.allclose(E, E2, atol=1e-13)
+
+
+def test_tok_base_window_of_rows():
+    # compressing from a slice of rows equals compressing from all rows
+    T, c, m = 40, 3, 4
+    Ca, Cb = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    Za, Zb = RNG.standard_normal((T, c)), RNG.standard_normal((T, c))
+    full = O.pool_entries(Ca, Za, Cb, Zb, m=m, overlap=1, T=T)
+    base = 4 * 6 - 4
+    part = O.pool_entries(Ca[base:], Za[base:], Cb[base:], Zb[base:], m=m, overlap=1, T=T,
+                          tok_base=base, s_begin=6, s_end=10)
+    assert np.array_equal(part, full[6:10])
+    with pytest.raises(ValueError):
+        O.pool_entries(Ca[base + 1:], Za[base + 1:], Cb[base + 1:], Zb[base + 1:], m=m,
+                       overlap=1, T=T, tok_base=base + 1, s_begin=6, s_end=7)
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm and RoPE
+# ---------------------------------------------------------------------------
+def test_rmsnorm_closed_form():
+    x = RNG.standard_normal((9, 64)) * 3
+    eps = 1e-3
+    y = O.rmsnorm(x, None, eps)
+    ms = np.mean(x * x, axis=-1)
+    assert np.allclose(np.mean(y * y, axis=-1), ms / (ms + eps), rtol=1e-13)
+    assert np.allclose(O.rmsnorm(5.0 * x, None, 0.0), O.rmsnorm(x, None, 0.0), rtol=1e-13)
+    g = RNG.standard_normal(64)
+    assert np.allclose(O.rmsnorm(x, g, eps), y * g, rtol=1e-14)
+    assert np.all(O.rmsnorm(np.zeros((1, 8)), None, 1e-6) == 0)
+
+
+def test_rope_closed_forms():
+    # r = 2: theta_0 = base^0 = 1, pair (1, 0) at position 1 -> (cos 1, sin 1)
+    x = np.array([5.0, 1.0, 0.0])
+    y = O.rope(x, 1, 2)
+    assert y[0] == 5.0 and np.allclose(y[1:], [math.cos(1), math.sin(1)], rtol=1e-15)
+    # r = 4, base 10000: theta_1 = 10000^(-1/2) = 0.01; at p = 100 the second pair turns by 1 rad
+    x = np.array([0.0, 0.0, 1.0, 0.0])
+    y = O.rope(x, 100, 4, 10000.0)
+    assert np.allclose(y, [0.0, 0.0, math.cos(1), math.sin(1)], atol=1e-12)
+    x = np.array([1.0, 0.0, 0.0, 0.0])
+    assert np.allclose(O.rope(x, 100, 4, 10000.0), [math.cos(100), math.sin(100), 0, 0], atol=1e-12)
+
+
+def test_rope_group_properties():
+    x = RNG.standard_normal((6, 64))
+    r = 16
+    for p in (0, 3, 1000, 1048576):
+        y = O.rope(x, p, r)
+        assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+        assert np.array_equal(y[:, : 64 - r], x[:, : 64 - r])
+    assert np.allclose(O.rope(x, 0, r), x, atol=0)
+    assert np.allclose(O.rope(O.rope(x, 17, r), 25, r), O.rope(x, 42, r), atol=1e-12)
+    assert np.allclose(O.rope(O.rope(x, 77, r), -77, r), x, atol=1e-12)
+    # relative: <R_i q, R_j k> depends only on i - j
+    q, k = RNG.standard_normal(64), RNG.standard_normal(64)
+    a = O.rope(q, 10, r) @ O.rope(k, 3, r)
+    b = O.rope(q, 1010, r) @ O.rope(k, 1003, r)
+    assert np.isclose(a, b, rtol=1e-11)
+
+
+def test_compress_applies_norm_then_rope_at_block_start():
+    T, c, m, r = 16, 8, 4, 4
+    C = RNG.standard_normal((T, c))
+    E = O.compress(C, None, C, None, m=m, overlap=0, T=T, rope_dim=r, eps=0.0)
+    pooled = np.stack([C[m * s:m * s + m].mean(axis=0) for s in range(T // m)])
+    normed = pooled / np.sqrt(np.mean(pooled ** 2, axis=-1, keepdims=True))
+    for s in range(T // m):
+        assert np.allclose(O.rope(E[s], -m * s, r), normed[s], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# a2 indexer score
+# ---------------------------------------------------------------------------
+def test_index_score_scaled_keys_are_linear_in_index():
+    Tq, H, dI, N, m = 3, 5, 8, 40, 1
+    q = RNG.standard_normal((Tq, H, dI))
+    w = RNG.uniform(size=(Tq, H))
+    v = RNG.standard_normal(dI)
+    K = np.arange(N)[:, None] * v[None, :]          # K_s = s * v
+    I = O.index_score(q, w, K, [N - 1] * Tq, m=m)
+    ref = np.array([np.sum(w[t] * np.maximum(q[t] @ v, 0)) for t in range(Tq)])
+    assert np.allclose(I, np.arange(N)[None, :] * ref[:, None], rtol=1e-13)
+
+
+def test_index_score_relu_sign_and_weights():
+    H, dI = 4, 16
+    v = RNG.standard_normal(dI)
+    K = np.tile(v, (6, 1))
+    w = RNG.uniform(size=(1, H))
+    q_pos_all = [5]
+    I_neg = O.index_score(-np.tile(v, (1, H, 1)), w, K, q_pos_all, m=1)
+    assert np.all(I_neg == 0.0)
+    I_pos = O.index_score(np.tile(v, (1, H, 1)), w, K, q_pos_all, m=1)
+    assert np.allclose(I_pos, w.sum() * (v @ v), rtol=1e-13)
+    # mixed: head 0 positive, others negative -> only w0 * |v|^2 survives
+    q = -np.tile(v, (1, H, 1)); q[0, 0] = v
+    assert np.allclose(O.index_score(q, w, K, q_pos_all, m=1), w[0, 0] * (v @ v), rtol=1e-13)
+
+
+def test_index_score_visibility_rule_and_mask():
+    Tq, H, dI, N, m = 20, 2, 4, 6, 4
+    q = RNG.standard_normal((Tq, H, dI)); w = RNG.uniform(size=(Tq, H))
+    K = RNG.standard_normal((N, dI))
+    pos = np.arange(Tq)
+    I = O.index_score(q, w, K, pos, m=m)
+    for t, i in enumerate(pos):
+        finite = np.isfinite(I[t])
+        n = min(N, (i + 1) // m)
+        assert finite.sum() == n and np.all(finite[:n])
+        assert np.all(I[t, n:] == -np.inf)
+        # entry s is visible iff all its tokens m s .. m s + m - 1 are <= i
+        for s in range(N):
+            assert finite[s] == (m * s + m - 1 <= i)
+    assert np.all(I[np.isfinite(I)] >= 0)                    # w >= 0 -> I >= 0
+
+
+def test_index_score_positive_homogeneity_in_key_scale():
+    q = RNG.standard_normal((2, 3, 8)); w = RNG.standard_normal((2, 3))
+    K = RNG.standard_normal((10, 8))
+    scales = RNG.uniform(0.1, 3.0, size=10)
+    I1 = O.index_score(q, w, K * scales[:, None], [39, 39], m=4)
+    I2 = O.index_score(q, w, K, [39, 39], m=4) * scales[None, :]
+    assert np.allclose(I1, I2, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# a3 top-k
+# ---------------------------------------------------------------------------
+def test_topk_golden_ties(golden_dir):
+    g = _load(golden_dir, "topk_ties.json")
+    s = np.array([float(v) for v in g["scores"]])
+    assert math.copysign(1, s[4]) == -1
+    for case in g["cases"]:
+        idx, vals = O.topk(s[None, :], [g["q_pos"]], m=g["m"], k=case["k"])
+        assert list(idx[0]) == case["expected"], case
+
+
+def _rank_select(scores, k):
+    """Brute force by counting: element s is beaten by s' if it scores more,
+    or the same with a lower index; keep the k least beaten."""
+    n = len(scores)
+    beaten = [sum(1 for j in range(n) if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+              for i in range(n)]
+    order = sorted(range(n), key=lambda i: beaten[i])
+    return order[:min(k, n)]
+
+
+def test_topk_exhaustive_tiny_against_rank_counting():
+    vals = [-1.0, 0.0, -0.0, 1.0, 2.0]
+    rng = np.random.default_rng(7)
+    for n in range(1, 8):
+        for trial in range(40):
+            row = rng.choice(vals, size=n)
+            for k in range(1, n + 2):
+                idx, _ = O.topk(row[None, :], [n - 1], m=1, k=k)
+                exp = _rank_select(list(row), k)
+                assert list(idx[0, :len(exp)]) == exp
+                assert np.all(idx[0, len(exp):] == -1)
+
+
+def test_topk_respects_visibility():
+    N, m = 50, 4
+    row = RNG.standard_normal(N)
+    row[40:] = 1e9                                       # huge but invisible scores
+    idx, _ = O.topk(row[None, :], [4 * 10 - 1], m=m, k=100)
+    assert set(idx[0][idx[0] >= 0]) == set(range(10))
+    assert np.sum(idx[0] >= 0) == 10
+
+
+# ---------------------------------------------------------------------------
+# a4 / a5 attention
+# ---------------------------------------------------------------------------
+def test_sink_closed_forms(golden_dir):
+    g = _load(golden_dir, "attention_sink.json")
+    q = np.array([g["q"]]); kv = np.array(g["kv"])
+    for case in g["cases"]:
+        KV = np.tile(kv, (case["n"], 1))
+        sig = float(case["sigma"])
+        o = O.attend_one(q, KV, i=0, eps=0.0, sink=[sig], scale=g["scale"])
+        assert np.allclose(o[0], kv * case["weight"], rtol=1e-14), case
+
+
+def test_no_keys_no_sink_is_zero_and_sink_only_is_zero():
+    q = RNG.standard_normal((2, 8))
+    assert np.all(O.attend_one(q, np.zeros((0, 8)), i=3, sink=None, scale=0.3) == 0)
+    assert np.all(O.attend_one(q, np.zeros((0, 8)), i=3, sink=[0.5, -1.0], scale=0.3) == 0)
+
+
+def test_north_star_special_case_equals_textbook_causal_attention():
+    """m = 1 without overlap (entries = normalised raw rows), k >= n, no window,
+    no sink, no RoPE: CSA is textbook causal softmax attention with K = V."""
+    T, n_h, d, H, dI = 24, 3, 16, 2, 8
+    raw = RNG.standard_normal((T, d))
+    E = O.compress(raw, None, None, None, m=1, overlap=0, T=T, rope_dim=0, eps=1e-6)
+    q = RNG.standard_normal((T, n_h, d))
+    qI = RNG.standard_normal((T, H, dI)); w = RNG.uniform(size=(T, H))
+    KI = RNG.standard_normal((T, dI))
+    pos = np.arange(T)
+    I = O.index_score(qI, w, KI, pos, m=1)
+    idx, _ = O.topk(I, pos, m=1, k=T)
+    out = O.sparse_mqa(q, E, idx, None, q_pos=pos, n_win=0, eps=1e-6, sink=None,
+                       rope_dim=0, scale=1 / math.sqrt(d))
+    qh = torch.from_numpy(O.rmsnorm(q, None, 1e-6)).permute(1, 0, 2)      # [n_h, T, d]
+    kv = torch.from_numpy(E)[None].expand(n_h, T, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qh, kv, kv, is_causal=True)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sparse_with_all_entries_equals_dense():
+    T, n_h, d, m, r = 40, 2, 16, 4, 4
+    E = RNG.standard_normal((T // m, d)); W = RNG.standard_normal((64, d))
+    q = RNG.standard_normal((T, n_h, d)); sink = RNG.standard_normal(n_h)
+    pos = np.arange(T)
+    idx = np.array([[s if s < (i + 1) // m else -1 for s in range(T // m)] for i in pos])
+    a = O.sparse_mqa(q, E, idx, W, q_pos=pos, n_win=8, sink=sink, rope_dim=r, scale=0.25)
+    b = O.dense_mqa(q, E, W, q_pos=pos, m=m, n_win=8, sink=sink, rope_dim=r, scale=0.25)
+    assert np.allclose(a, b, atol=1e-14)
+
+
+def test_constant_values_give_value_times_total_weight():
+    n_h, d, r, i = 3, 16, 4, 57
+    v = RNG.standard_normal(d)
+    KV = np.tile(v, (9, 1))
+    q = RNG.standard_normal((n_h, d)); sink = RNG.standard_normal(n_h)
+    scale = 0.2
+    o = O.attend_one(q, KV, i=i, sink=sink, rope_dim=r, scale=scale)
+    qh = O.rope(O.rmsnorm(q, None, 1e-6), i, r)
+    for h in range(n_h):
+        l = scale * qh[h] @ v
+        p = 9 * math.exp(l) / (9 * math.exp(l) + math.exp(sink[h]))
+        assert np.allclose(o[h], O.rope(p * v, -i, r), rtol=1e-12, atol=1e-14)
+        assert p < 1
+
+
+def test_window_extent_and_ring_rows():
+    # one-hot rows mark which tokens enter the window; q = 0 makes logits equal
+    d, n_win, W_cap = 64, 5, 16
+    W = np.zeros((W_cap, d))
+    for row in range(W_cap):
+        W[row, row] = 1.0
+    q = np.zeros((1, 1, d))
+    for i in (0, 3, 4, 20, 35):
+        out = O.sparse_mqa(q, np.zeros((1, d)), np.array([[-1]]), W, q_pos=[i], n_win=n_win,
+                           W_cap=W_cap, eps=1.0, rope_dim=0, scale=1.0)
+        toks = list(range(max(0, i - n_win + 1), i + 1))
+        exp = np.zeros(d)
+        for t in toks:
+            exp[t % W_cap] += 1.0 / len(toks)
+        assert np.allclose(out[0, 0], exp, atol=1e-15)
+
+
+def test_idx_permutation_invariance():
+    d, n_h = 32, 2
+    E = RNG.standard_normal((30, d)); W = RNG.standard_normal((8, d))
+    q = RNG.standard_normal((1, n_h, d))
+    idx = np.array([[3, 17, 5, 29, -1, 0]])
+    a = O.sparse_mqa(q, E, idx, W, q_pos=[200], n_win=4, W_cap=8, sink=[0.1, -0.3],
+                     rope_dim=8, scale=0.2)
+    b = O.sparse_mqa(q, E, idx[:, ::-1].copy(), W, q_pos=[200], n_win=4, W_cap=8,
+                     sink=[0.1, -0.3], rope_dim=8, scale=0.2)
+    assert np.allclose(a, b, atol=1e-14)
+
+
+def test_shift_invariance_needs_output_rotation_at_minus_i():
+    """Shifting the query, every entry and every window token by D leaves the
+    de-rotated output unchanged (the output is rotated again at -i)."""
+    d, r, n_h, m = 32, 8, 2, 4
+    raw_E = RNG.standard_normal((12, d)); raw_W = RNG.standard_normal((16, d))
+    q = RNG.standard_normal((1, n_h, d)); sink = RNG.standard_normal(n_h)
+    i = 50
+    idx = np.array([[0, 3, 7, 11]])
+
+    def run(D):
+        E = np.stack([O.rope(raw_E[s], m * s + D, r) for s in range(12)])
+        W = np.zeros((16 + 64, d))
+        for tau in range(i - 15, i + 1):
+            W[(tau + D) % 80] = O.rope(raw_W[tau - (i - 15)], tau + D, r)
+        return O.sparse_mqa(q, E, idx, W, q_pos=[i + D], n_win=16, W_cap=80, sink=sink,
+                            rope_dim=r, scale=0.2)
+
+    a, b = run(0), run(12345)
+    assert np.allclose(a, b, rtol=1e-9, atol=1e-11)
+    assert not np.allclose(O.rope(a, 7, r), a)   # the rotation is not trivial here
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: the pins above must notice plausible oracle bugs
+# ---------------------------------------------------------------------------
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
+    g = _load(golden_dir, "compress_geometry.json")
+    T = g["T"]
+    Ca = np.array(g["C_a"], dtype=np.float64)[:, None]
+    Cb = np.array(g["C_b"], dtype=np.float64)[:, None]
+
+    # (1) wrong block for set b: the next block instead of the previous one
+    def bad_candidates(s, m, overlap, T):
+        a = [("a", t) for t in range(m * s, min(m * (s + 1), T))]
+        b = [("b", t) for t in range(m * (s + 1), min(m * (s + 2), T))] if overlap else []
+        return a + b
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "candidate_tokens", bad_candidates)
+        E = O.pool_entries(Ca, None, Cb, None, m=4, overlap=1, T=T)
+        assert not np.allclose(E[:, 0], g["cases"][0]["expected"])
+
+    # (2) visibility off by one (a query seeing its own block)
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "n_visible", lambda i, m, N: min(N, i // m + 1))
+        I = O.index_score(np.ones((1, 1, 2)), np.ones((1, 1)), np.ones((4, 2)), [5], m=4)
+        assert np.isfinite(I[0]).sum() != 1           # the pin expects floor(6/4) = 1
+
+    # (3) output rotated at +i instead of -i breaks shift invariance
+    real_rope = O.rope
+
+    def attend_wrong_sign(q, KV, *, i, **kw):
+        out = O_attend_orig(q, KV, i=i, **kw)
+        r = kw.get("rope_dim", 0)
+        return real_rope(real_rope(out, i, r), i, r)  # = rotated at +i overall
+    O_attend_orig = O.attend_one
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "attend_one", attend_wrong_sign)
+        with pytest.raises(AssertionError):
+            test_shift_invariance_needs_output_rotation_at_minus_i()
+
+    # (4) sink added to the numerator too (total weight 1) breaks the closed form
+    def attend_sink_as_key(q, KV, *, i, sink=None, **kw):
+        return O_attend_orig(q, KV, i=i, sink=None, **kw)
+    with monkeypatch.context() as mp:
+        mp.setattr(O, "attend_one", attend_sink_as_key)
+        with pytest.raises(AssertionError):
+            test_sink_closed_forms(golden_dir)
