@@ -1,0 +1,114 @@
+// Device-side helpers shared by the HIP kernels of the CSA/HCA core (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+// ---- scalar conversions ---------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7fffu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+// two fp32 -> packed bf16x2 (low half = a)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// OCP e4m3fn encode, round to nearest even, saturating to +-448 (NaN -> 0x7f).
+// Subnormal range |v| < 2^-6 has a fixed step of 2^-9.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+  if (v != v) return 0x7f;
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fminf(fabsf(v), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {                       // 2^-6
+    code = (uint32_t)rintf(a * 512.0f);      // 0..8 (8 is the smallest normal)
+  } else {
+    int ex;
+    float mant = frexpf(a, &ex);             // a = mant * 2^ex, mant in [0.5, 1)
+    int E = ex - 1;
+    uint32_t f = (uint32_t)rintf((mant * 2.0f - 1.0f) * 8.0f);
+    if (f == 8u) { f = 0u; ++E; }
+    code = ((uint32_t)(E + 7) << 3) | f;
+  }
+  return (uint8_t)(sign | code);
+}
+
+// order-preserving map of a float score to uint32 (-0.0 canonicalised to +0.0)
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u << 1) == 0u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---- loads of one element of any supported storage type --------------------
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* p, size_t i) {
+  if constexpr (DT == DT_F32) return ((const float*)p)[i];
+  else return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_from_f32(void* p, size_t i, float v) {
+  if constexpr (DT == DT_F32) ((float*)p)[i] = v;
+  else ((uint16_t*)p)[i] = f32_to_bf16_bits(v);
+}
+
+// ---- RoPE angle, computed in fp64 so that positions up to 2^31 keep full
+// fp32 accuracy in cos / sin (an fp32 product p * theta loses ~p * 2^-24 rad).
+__device__ __forceinline__ void rope_cos_sin(long long pos, int u, int rope_dim, float base,
+                                             float* c, float* s) {
+  double theta = pow((double)base, -2.0 * (double)u / (double)rope_dim);
+  double ang = (double)pos * theta;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  *c = (float)cs;
+  *s = (float)sn;
+}
+
+// ---- wave / block reductions ------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// block-wide sum / max; `red` is __shared__ float[>= blockDim/64]; all threads get the result
+template <bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = MAX ? wave_max(v) : wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < nw; ++w) r = MAX ? fmaxf(r, red[w]) : (r + red[w]);
+  return r;
+}
+
+}  // namespace csa

@@ -1,0 +1,520 @@
+// a4 / a5 — shared-KV multi-query attention over compressed entries, a sliding
+// window and an attention sink, for gfx950.
+//
+// DeepSeek-V4 method page, section 3.3: core attention is MQA where each
+// compressed entry is both key and value; RMSNorm on the query; partial RoPE
+// on the last dims of query, entries and output, the output rotated again at
+// position -i; a window of n_win uncompressed KV rows because a query cannot
+// see its own block.  CSA attends to the top-k entries, HCA to every visible
+// entry.  Report digest: learnable sink logits let a head's total attention
+// weight fall below 1 (a sink adds e^sigma to the softmax denominator).
+//
+// Key slots of a query: slots [0, n_sel) are entries (idx[j] for CSA, j for
+// HCA), slots [n_sel, n_sel + n_w) the window tokens i-n_w+1 .. i.
+//
+// Matrix-core kernel (bf16): a workgroup takes one query, 64 heads (16 per
+// wave) and a contiguous range of key slots, staged 32 rows at a time in LDS.
+//   S^T = KV . q^T  with v_mfma_f32_16x16x32_bf16, keys as M, heads as N, so a
+//   lane ends with 4+4 key scores of ONE head: exactly the A operand layout of
+//   P.V for that head (the contraction order over keys is permuted the same
+//   way on both operands);
+//   V is read transposed from row-major LDS with ds_read_b64_tr_b16;
+//   an online softmax (running max / sum per head) rescales O per 32 keys.
+// Decode queries split their slots across workgroups (fixed 256-slot ranges,
+// independent of the batch) and a combine kernel merges the partial
+// (max, sum, O) in a fixed order.
+#include "csa_device.h"
+#include "csa_internal.h"
+
+namespace csa {
+
+static constexpr int MQ_CH = 32;          // key rows per LDS chunk
+static constexpr int MQ_SPLIT_KEYS = 256; // slots per workgroup when a query is split
+static constexpr int MQ_SPLIT_BELOW_TQ = 16;
+static constexpr int VALU_MAX_SLOTS = 8192;
+
+struct QuerySlots {
+  long long n_sel, n_w, win_lo, n_slots;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ QuerySlots query_slots(long long i, long long N_cap, int k, int m, int n_win) {
+  QuerySlots s;
+  s.n_sel = DENSE ? min(N_cap, (i + 1) / m) : (long long)k;
+  s.n_w = min((long long)n_win, i + 1);
+  s.win_lo = i - s.n_w + 1;
+  s.n_slots = s.n_sel + s.n_w;
+  return s;
+}
+
+// element offset of the row of a slot, or -1 for an empty slot
+template <bool DENSE>
+__device__ __forceinline__ long long slot_row(long long slot, const QuerySlots& qs,
+                                              const int* __restrict__ idx_row, int b,
+                                              long long N_cap, int W_cap, int d, bool* in_E) {
+  if (slot < qs.n_sel) {
+    long long e = DENSE ? slot : (long long)idx_row[slot];
+    *in_E = true;
+    if (e < 0 || e >= N_cap) return -1;
+    return ((long long)b * N_cap + e) * d;
+  }
+  *in_E = false;
+  const long long tau = qs.win_lo + (slot - qs.n_sel);
+  return ((long long)b * W_cap + (tau % W_cap)) * d;
+}
+
+// ---------------------------------------------------------------------------
+// generic path (fp32 or bf16 storage): one workgroup per (query, head)
+// ---------------------------------------------------------------------------
+template <int DT, bool DENSE>
+__global__ __launch_bounds__(256) void mqa_valu_kernel(
+    const void* __restrict__ q, const float* __restrict__ gamma_q, float eps, const void* __restrict__ E,
+    long long N_cap, const int* __restrict__ idx, int k, int m, const void* __restrict__ W, int W_cap,
+    int n_win, const float* __restrict__ sink, const int* __restrict__ q_pos, int Tq, int n_h, int d,
+    int rope_dim, float rope_base, float scale, void* __restrict__ out) {
+  extern __shared__ float sm[];
+  float* qh = sm;                                  // [d]
+  float* red = qh + d;                             // [4]
+  float* pr = red + 4;                             // [VALU_MAX_SLOTS]
+  long long* roff = (long long*)(pr + VALU_MAX_SLOTS);   // [VALU_MAX_SLOTS] (8-byte aligned: d, 4 even)
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const size_t row = (size_t)b * Tq + t;
+  const long long i = q_pos[row];
+  const size_t qoff = (row * n_h + h) * (size_t)d;
+
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    const float v = load_as_f32<DT>(q, qoff + j);
+    qh[j] = v;
+    ss += v * v;
+  }
+  const float rinv = 1.f / sqrtf(block_reduce<false>(ss, red) / (float)d + eps);
+  for (int j = threadIdx.x; j < d; j += blockDim.x) qh[j] *= rinv * (gamma_q ? gamma_q[j] : 1.f);
+  __syncthreads();
+  for (int u = threadIdx.x; u < rope_dim / 2; u += blockDim.x) {
+    const int j0 = d - rope_dim + 2 * u;
+    float cs, sn;
+    rope_cos_sin(i, u, rope_dim, rope_base, &cs, &sn);
+    const float x0 = qh[j0], x1 = qh[j0 + 1];
+    qh[j0] = x0 * cs - x1 * sn;
+    qh[j0 + 1] = x0 * sn + x1 * cs;
+  }
+  __syncthreads();
+
+  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
+  const int* idx_row = DENSE ? nullptr : idx + row * (size_t)k;
+  float mx = -INFINITY;
+  for (long long s = threadIdx.x; s < qs.n_slots; s += blockDim.x) {
+    bool in_E;
+    const long long off = slot_row<DENSE>(s, qs, idx_row, b, N_cap, W_cap, d, &in_E);
+    roff[s] = in_E ? off : (off < 0 ? -1 : -2 - off);   // window rows encoded below -1
+    float l = -INFINITY;
+    if (off >= 0) {
+      const void* base = in_E ? E : W;
+      float dot = 0.f;
+      for (int j = 0; j < d; ++j) dot += qh[j] * load_as_f32<DT>(base, (size_t)off + j);
+      l = dot * scale;
+    }
+    pr[s] = l;
+    mx = fmaxf(mx, l);
+  }
+  const float sig = sink ? sink[h] : -INFINITY;
+  const float M = fmaxf(block_reduce<true>(mx, red), sig);
+  float sum = 0.f;
+  for (long long s = threadIdx.x; s < qs.n_slots; s += blockDim.x) {
+    const float p = (pr[s] == -INFINITY) ? 0.f : __expf(pr[s] - M);
+    pr[s] = p;
+    sum += p;
+  }
+  float Z = block_reduce<false>(sum, red);
+  if (sig != -INFINITY) Z += __expf(sig - M);
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  __syncthreads();
+
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    float o = 0.f;
+    for (long long s = 0; s < qs.n_slots; ++s) {
+      const long long ro = roff[s];
+      if (ro == -1) continue;
+      const float p = pr[s];
+      o += p * (ro >= 0 ? load_as_f32<DT>(E, (size_t)ro + j) : load_as_f32<DT>(W, (size_t)(-2 - ro) + j));
+    }
+    qh[j] = o * inv;   // every thread finished reading qh before the barrier above
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    float v = qh[j];
+    if (j >= d - rope_dim) {
+      const int u = (j - (d - rope_dim)) >> 1;
+      float cs, sn;
+      rope_cos_sin(-i, u, rope_dim, rope_base, &cs, &sn);
+      const float other = qh[j ^ 1];
+      v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+    }
+    store_from_f32<DT>(out, qoff + j, v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// matrix-core path (bf16), D in {128, 256, 512}, n_h % 16 == 0
+// ---------------------------------------------------------------------------
+template <int D, bool DENSE>
+__global__ __launch_bounds__(256) void mqa_mfma_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
+    const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
+    const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    int kps, int n_split, uint16_t* __restrict__ out, float* __restrict__ ws) {
+  constexpr int KS = D / 32;         // 8-dim chunks per lane group (S^T K-steps)
+  constexpr int GW = D / 4;          // dims per lane group
+  constexpr int NT = D / 16;         // 16-dim output tiles
+  constexpr int ROWB = D * 2 + 32;   // padded LDS row, bytes
+  constexpr int PPR = D * 2 / 16;    // 16-byte pieces per row
+  constexpr int PIECES = MQ_CH * PPR;
+  __shared__ __attribute__((aligned(16))) uint8_t kv[MQ_CH * ROWB];
+  __shared__ int slot_ok[MQ_CH];
+  __shared__ float rope_cs[D];   // (cos, sin) of the angle i * theta_u, u < rope_dim / 2
+
+  const int n_hg = (n_h + 63) / 64;
+  const int hg = blockIdx.x % n_hg, sp = blockIdx.x / n_hg;
+  const int t = blockIdx.y, b = blockIdx.z;
+  const size_t row = (size_t)b * Tq + t;
+  const long long i = q_pos[row];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int h0 = 64 * hg + 16 * wave;
+  const bool wact = h0 < n_h;
+  const int hq = wact ? h0 + j : 0;
+
+  for (int u = threadIdx.x; u < rope_dim / 2; u += 256)
+    rope_cos_sin(i, u, rope_dim, rope_base, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
+  __syncthreads();
+
+  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
+  const int* idx_row = DENSE ? nullptr : idx + row * (size_t)k;
+  const long long s0 = (long long)sp * kps;
+  const long long s1 = min(s0 + (long long)kps, qs.n_slots);
+
+  // ---- q^ = RoPE_i(RMSNorm(q)) as the B operand of S^T: head hq, dims GW*g + 8ks + e
+  bf16x8_t qf[KS];
+  {
+    u32x4_t raw[KS];
+    float ss = 0.f;
+    const uint16_t* qp = q + (row * n_h + hq) * (size_t)D + GW * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      raw[ks] = *(const u32x4_t*)(qp + 8 * ks);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(raw[ks][e] << 16);
+        const float x1 = __uint_as_float(raw[ks][e] & 0xffff0000u);
+        ss += x0 * x0 + x1 * x1;
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float rinv = 1.f / sqrtf(ss / (float)D + eps);
+    const int rbeg = D - rope_dim;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t packed;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int dim = GW * g + 8 * ks + 2 * e;
+        float v0 = __uint_as_float(raw[ks][e] << 16) * rinv * (gamma_q ? gamma_q[dim] : 1.f);
+        float v1 = __uint_as_float(raw[ks][e] & 0xffff0000u) * rinv * (gamma_q ? gamma_q[dim + 1] : 1.f);
+        if (dim >= rbeg) {
+          const float cs = rope_cs[dim - rbeg], sn = rope_cs[dim - rbeg + 1];
+          const float r0 = v0 * cs - v1 * sn, r1 = v0 * sn + v1 * cs;
+          v0 = r0;
+          v1 = r1;
+        }
+        packed[e] = pack_bf16x2(v0, v1);
+      }
+      qf[ks] = __builtin_bit_cast(bf16x8_t, packed);
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;    // softmax state of head hq
+  f32x4_t O[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (long long c0 = s0; c0 < s1; c0 += MQ_CH) {
+    // ---- stage the chunk's rows (row-major, padded) into LDS
+    for (int p = threadIdx.x; p < PIECES; p += 256) {
+      const int r = p / PPR, c16 = p % PPR;
+      const long long slot = c0 + r;
+      long long off = -1;
+      bool in_E = true;
+      if (slot < s1) off = slot_row<DENSE>(slot, qs, idx_row, b, N_cap, W_cap, D, &in_E);
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (off >= 0) v = *(const u32x4_t*)((in_E ? E : W) + off + 8 * c16);
+      *(u32x4_t*)(&kv[r * ROWB + c16 * 16]) = v;
+      if (c16 == 0) slot_ok[r] = off >= 0;
+    }
+    __syncthreads();
+    if (wact) {
+      // ---- S^T: keys (M) x heads (N), two tiles of 16 keys
+      f32x4_t S[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t a = *(const bf16x8_t*)(&kv[(16 * kt + j) * ROWB + (GW * g + 8 * ks) * 2]);
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], S[kt], 0, 0, 0);
+        }
+      }
+      // lane (g, j): S[kt][r] = score of key 16 kt + 4 g + r for head hq
+      float lg[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = slot_ok[16 * kt + 4 * g + r] != 0;
+          lg[kt][r] = ok ? S[kt][r] * scale : -INFINITY;
+          mx = fmaxf(mx, lg[kt][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
+      float p[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[kt][r] = (lg[kt][r] == -INFINITY) ? 0.f : __expf(lg[kt][r] - m_new);
+          psum += p[kt][r];
+        }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      // O rows are heads 4g + r: fetch their alpha from lane 4g + r
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * g + r, 64);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) O[nt][r] *= ar;
+        }
+      }
+      // ---- P (A operand: head j, keys {4g..4g+3, 16+4g..16+4g+3}) times V
+      u32x4_t pw;
+      pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+      pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+      pw[2] = pack_bf16x2(p[1][0], p[1][1]);
+      pw[3] = pack_bf16x2(p[1][2], p[1][3]);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
+      const int trow = 4 * g + (j >> 2);
+      const int tcol = 4 * (j & 3);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(&kv[trow * ROWB + (16 * nt + tcol) * 2]));
+        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(&kv[(16 + trow) * ROWB + (16 * nt + tcol) * 2]));
+        u32x4_t vw;
+        vw[0] = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
+        vw[1] = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
+        vw[2] = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
+        vw[3] = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
+        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8_t, vw), O[nt], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  if (!wact) return;
+
+  if (n_split == 1) {
+    // ---- finish: sink, normalise, rotate the last rope_dim dims at -i, store
+    const float sig = sink ? sink[hq] : -INFINITY;
+    const float M = fmaxf(m_run, sig);
+    float Z = 0.f;
+    if (m_run != -INFINITY) Z += l_run * __expf(m_run - M);
+    if (sig != -INFINITY) Z += __expf(sig - M);
+    const float f = (Z > 0.f && m_run != -INFINITY) ? __expf(m_run - M) / Z : 0.f;
+    float fr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fr[r] = __shfl(f, 4 * g + r, 64);
+    const int rbeg = D - rope_dim;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int dim = 16 * nt + j;
+      float cs = 1.f, sn = 0.f;   // rotation at -i: cos(-x) = cos x, sin(-x) = -sin x
+      if (dim >= rbeg) {
+        cs = rope_cs[(dim - rbeg) & ~1];
+        sn = -rope_cs[((dim - rbeg) & ~1) + 1];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = O[nt][r] * fr[r];
+        const float other = __shfl_xor(v, 1, 64);
+        float o = v;
+        if (dim >= rbeg) o = (dim & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+        out[(row * n_h + h0 + 4 * g + r) * (size_t)D + dim] = f32_to_bf16_bits(o);
+      }
+    }
+  } else {
+    // ---- partial state: O (unnormalised, relative to m_run), then m_run, l_run
+    const size_t pbase = (row * n_split + sp) * (size_t)n_h;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ws[(pbase + h0 + 4 * g + r) * (D + 2) + 16 * nt + j] = O[nt][r];
+    if (g == 0) {
+      ws[(pbase + hq) * (D + 2) + D] = m_run;
+      ws[(pbase + hq) * (D + 2) + D + 1] = l_run;
+    }
+  }
+}
+
+// merge the split partial states of one (query, head) in split order
+__global__ __launch_bounds__(256) void mqa_combine_kernel(
+    const float* __restrict__ ws, const float* __restrict__ sink, const int* __restrict__ q_pos,
+    int Tq, int n_h, int D, int n_split, int rope_dim, float rope_base, uint16_t* __restrict__ out) {
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const size_t row = (size_t)b * Tq + t;
+  const long long i = q_pos[row];
+  const float sig = sink ? sink[h] : -INFINITY;
+  auto part = [&](int s) { return ws + ((row * n_split + s) * (size_t)n_h + h) * (D + 2); };
+  float M = sig;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part(s)[D]);
+  float Z = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float ms = part(s)[D];
+      if (ms != -INFINITY) Z += part(s)[D + 1] * __expf(ms - M);
+    }
+    if (sig != -INFINITY) Z += __expf(sig - M);
+  }
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  const int rbeg = D - rope_dim;
+  for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
+    const int d0 = 2 * u;
+    float o0 = 0.f, o1 = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float* ps = part(s);
+      const float ms = ps[D];
+      if (ms == -INFINITY) continue;
+      const float f = __expf(ms - M);
+      o0 += ps[d0] * f;
+      o1 += ps[d0 + 1] * f;
+    }
+    o0 *= inv;
+    o1 *= inv;
+    if (d0 >= rbeg) {
+      float cs, sn;
+      rope_cos_sin(-i, (d0 - rbeg) >> 1, rope_dim, rope_base, &cs, &sn);
+      const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
+      o0 = r0;
+      o1 = r1;
+    }
+    const size_t ob = (row * n_h + h) * (size_t)D + d0;
+    out[ob] = f32_to_bf16_bits(o0);
+    out[ob + 1] = f32_to_bf16_bits(o1);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+static bool mqa_mfma_ok(const MqaArgs& a) {
+  return a.dtype == DT_BF16 && (a.d == 128 || a.d == 256 || a.d == 512) && a.n_h % 16 == 0;
+}
+
+long long mqa_slots_max(const MqaArgs& a) {
+  return (a.idx ? (long long)a.k : a.N_cap) + a.n_win;
+}
+
+static void mqa_split(int Tq, long long slots_max, int* kps, int* n_split) {
+  if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
+    long long s = ((slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH;
+    *kps = (int)(s > 0 ? s : MQ_CH);
+    *n_split = 1;
+  } else {
+    *kps = MQ_SPLIT_KEYS;
+    *n_split = (int)((slots_max + MQ_SPLIT_KEYS - 1) / MQ_SPLIT_KEYS);
+  }
+}
+
+size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max, int dtype) {
+  if (!(dtype == DT_BF16 && (d == 128 || d == 256 || d == 512) && n_h % 16 == 0)) return 0;
+  int kps, n_split;
+  mqa_split(Tq, n_slots_max, &kps, &n_split);
+  if (n_split == 1) return 0;
+  return (size_t)B * Tq * n_split * n_h * (size_t)(d + 2) * sizeof(float);
+}
+
+template <int D, bool DENSE>
+static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
+  const int n_hg = (a.n_h + 63) / 64;
+  dim3 grid((unsigned)(n_split * n_hg), (unsigned)a.Tq, (unsigned)a.B);
+  hipLaunchKernelGGL((mqa_mfma_kernel<D, DENSE>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
+                     a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx, a.k, a.m,
+                     (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
+                     a.rope_dim, a.rope_base, a.scale, kps, n_split, (uint16_t*)a.out, (float*)a.ws);
+  if (n_split > 1)
+    hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
+                       dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
+                       n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
+}
+
+int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
+  const bool dense = a.idx == nullptr;
+  const long long slots_max = mqa_slots_max(a);
+  if (mqa_mfma_ok(a)) {
+    int kps, n_split;
+    mqa_split(a.Tq, slots_max, &kps, &n_split);
+    if (n_split > 1 && a.ws_bytes < mqa_workspace_bytes(a.B, a.Tq, a.n_h, a.d, slots_max, a.dtype)) {
+      *why = "workspace smaller than csa_mqa_workspace_size()";
+      return 5;
+    }
+#define CSA_MQA_D(DV)                                                  \
+  do {                                                                 \
+    if (dense) launch_mfma_d<DV, true>(a, kps, n_split, st);           \
+    else launch_mfma_d<DV, false>(a, kps, n_split, st);                \
+  } while (0)
+    if (a.d == 128) CSA_MQA_D(128);
+    else if (a.d == 256) CSA_MQA_D(256);
+    else CSA_MQA_D(512);
+#undef CSA_MQA_D
+  } else {
+    if (slots_max > VALU_MAX_SLOTS) {
+      *why = "the generic (fp32 / unaligned-shape) attention path holds at most 8192 key slots";
+      return 4;
+    }
+    const size_t lds = (size_t)(a.d + 4 + VALU_MAX_SLOTS) * sizeof(float) + VALU_MAX_SLOTS * sizeof(long long);
+    dim3 grid((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B);
+#define CSA_MQA_VALU(DT, DN)                                                                        \
+  do {                                                                                              \
+    auto kfn = mqa_valu_kernel<DT, DN>;                                                             \
+    if (hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize,           \
+                            (int)lds) != hipSuccess) {                                              \
+      *why = "cannot reserve LDS for the generic attention kernel";                                 \
+      return 6;                                                                                     \
+    }                                                                                               \
+    hipLaunchKernelGGL(kfn, grid, dim3(256), lds, st, a.q, a.gamma_q, a.eps, a.E, a.N_cap, a.idx, \
+                       a.k, a.m, a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h, a.d,          \
+                       a.rope_dim, a.rope_base, a.scale, a.out);                                    \
+  } while (0)
+    if (a.dtype == DT_F32) {
+      if (dense) CSA_MQA_VALU(DT_F32, true); else CSA_MQA_VALU(DT_F32, false);
+    } else {
+      if (dense) CSA_MQA_VALU(DT_BF16, true); else CSA_MQA_VALU(DT_BF16, false);
+    }
+#undef CSA_MQA_VALU
+  }
+  if (hipGetLastError() != hipSuccess) {
+    *why = "kernel launch failed";
+    return 6;
+  }
+  return 0;
+}
+
+}  // namespace csa
