@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA/HCA attention core on one MI355X.
+
+Workload: 1M-context CSA decode, Pro-like -- 16 sequences, 1,048,576 cached
+tokens each (262,144 compressed entries, m = 4), fp8 (e4m3) indexer keys with
+per-row scales (64 heads x 128), top-k 1024, bf16 MQA over 512-wide entries for
+128 query heads, 128-token window, sink.  One step = the whole hot path for
+one new token per sequence: compress (window row, newest entry, newest indexer
+key), indexer score, top-k, sparse MQA.  Inputs are synthetic (seeded N(0,1),
+U(0,1) head weights) and resident in HBM before timing starts.
+
+Prints ONE JSON line.  Also reported: the prefill indexer (16,384 queries x
+32,768 entries, 64 heads x 128, bf16) in TFLOP/s, and the fp64 oracle timed on
+a bounded sample of the decode workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences the oracle runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (3x) to calibrate HBM byte counters")
+    return ap.parse_args()
+
+
+def traffic_from_profiles(kernel_tag: str, src_file: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE,
+    copy-kernel calibrated), valid only while the kernel source is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}.pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    if not (m_b and m_h):
+        return None
+    cur = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if cur == m_h.group(1) else None
+
+
+def cpu_baseline(run, n_seq: int):
+    """The fp64 oracle on n_seq sequences of the same workload (host cores)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import steps
+    from tests._util import to_f64
+
+    wl = run.wl
+    n_seq = max(1, min(n_seq, wl.B))
+    # decode the stored inputs of the sampled sequences first (not timed)
+    inputs = []
+    for b in range(n_seq):
+        KI = to_f64(run.KI[b])
+        if run.KI_scale is not None:
+            KI = KI * to_f64(run.KI_scale[b])[:, None]
+        p = dict(i=run.i, m=wl.m, N=wl.N_cap, k=wl.k, n_win=wl.n_win, d_I=wl.d_I, rope_dim=wl.rope_dim,
+                 rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.dtype, k_dtype=wl.k_dtype,
+                 KI=KI, win_raw=to_f64(run.win_raw[b]),
+                 Ca=to_f64(run.Ca[b]), Za=to_f64(run.Za[b]), Cb=to_f64(run.Cb[b]), Zb=to_f64(run.Zb[b]),
+                 ICa=to_f64(run.ICa[b]), IZa=to_f64(run.IZa[b]), ICb=to_f64(run.ICb[b]),
+                 IZb=to_f64(run.IZb[b]), qI=to_f64(run.qI[b, 0]), w=to_f64(run.wI[b, 0]),
+                 q=to_f64(run.q[b, 0]), sink=to_f64(run.sink))
+        raw_b = run.kv_raw[b]
+        inputs.append((p, raw_b))
+    t0 = time.perf_counter()
+    for p, raw_b in inputs:
+        def rows(s, raw_b=raw_b):
+            import torch
+            return to_f64(raw_b[torch.as_tensor(s, device=raw_b.device)])
+        steps.csa_decode_sequence(p, rows)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": round(n_seq / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_seq} of {wl.B} sequences, full step each (fp64 numpy; BLAS threads "
+                      f"{threads}, host nproc {os.cpu_count()})",
+            "seconds": round(dt, 3)}
+
+
+def prefill_indexer(steps: int, warmup: int):
+    """csa_index_score on the chunked-prefill shapes: 16,384 queries over 32,768 entries."""
+    import torch
+
+    import long_context_attention_02_amd as csa
+    from synth import Gen
+    from synth.workloads import CSA_PREFILL_PRO as wl, T_KI, T_QI, T_WI
+
+    g = Gen(wl.wid, "cuda")
+    qI = g.normal(T_QI, (1, wl.Tq, wl.H_I, wl.d_I), "bf16")
+    wI = g.uniform(T_WI, (1, wl.Tq, wl.H_I))
+    K = g.normal(T_KI, (1, wl.N_cap, wl.d_I), "bf16")
+    pos = (wl.q_pos0 + torch.arange(wl.Tq, dtype=torch.int32, device="cuda")).view(1, -1).contiguous()
+    I = torch.empty((1, wl.Tq, wl.N_cap), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    pairs = sum(min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq))
+    flops = 2.0 * pairs * wl.H_I * wl.d_I
+    tfs = flops / (ms * 1e-3) / 1e12
+    del qI, wI, K, I
+    return {"workload": wl.name, "ms": round(ms, 4), "TFLOP/s": round(tfs, 2),
+            "causal_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the CSA/HCA core "
+              "runs on a single MI355X here)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from long_context_attention_02_amd.pipeline import CSADecode
+    from synth.workloads import CSA_DECODE_1M as wl
+
+    torch.cuda.set_device(0)
+    run = CSADecode(wl, "cuda", keep_raw=not args.no_cpu_baseline)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        run.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_idx = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(K):
+        run.step(index_events=ev_idx[s])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+    idx_ms = sum(a.elapsed_time(b) for a, b in ev_idx) / K
+
+    ab = run.algorithmic_bytes()
+    tokens_s = wl.B / (ms_step * 1e-3)
+    idx_gbs = ab["index_kernel"] / (idx_ms * 1e-3) / 1e9
+    step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
+    src = os.path.join(ROOT, "long_context_attention_02_amd", "csrc", "index_score.hip")
+    traffic = traffic_from_profiles("index_score_decode_1M_fp8", src)
+
+    result = {
+        "metric": "CSA decode tokens/s + HBM GB/s at 1M ctx; indexer prefill TFLOP/s (%peak)",
+        "value": round(tokens_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "context_tokens": wl.ctx,
+                   "compressed_entries": wl.N_cap, "m": wl.m, "top_k": wl.k, "indexer": "64x128 e4m3",
+                   "query_heads": wl.n_h, "entry_dim": wl.d, "window": wl.n_win},
+        "step_hbm_GBps": round(step_gbs, 1),
+        "step_algorithmic_bytes": ab["step"],
+        "roofline": {"bound": "hbm", "kernel": "index_mfma_decode (csa_index_score)",
+                     "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": ab["index_kernel"],
+                     "avg_launch_ms": round(idx_ms, 5)},
+    }
+    if args.copy_calibration:
+        src_t = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        for _ in range(3):
+            dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes_each_way"] = 512 << 20
+        del src_t, dst_t
+    if not args.no_prefill:
+        del run.I
+        torch.cuda.empty_cache()
+        result["prefill_indexer"] = prefill_indexer(steps=10, warmup=3)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(run, args.cpu_sample)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

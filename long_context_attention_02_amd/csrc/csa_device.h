@@ -7,6 +7,7 @@
 namespace csa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -76,12 +77,21 @@ __device__ __forceinline__ void store_from_f32(void* p, size_t i, float v) {
 
 // ---- RoPE angle, computed in fp64 so that positions up to 2^31 keep full
 // fp32 accuracy in cos / sin (an fp32 product p * theta loses ~p * 2^-24 rad).
+// The angle is reduced modulo 2*pi with a two-part constant (Cody-Waite, with FMA
+// the product k * hi is exact for |k| < 2^29) before sincos, which keeps the
+// library on its short-argument path for positions up to 2^31.
 __device__ __forceinline__ void rope_cos_sin(long long pos, int u, int rope_dim, float base,
                                              float* c, float* s) {
-  double theta = pow((double)base, -2.0 * (double)u / (double)rope_dim);
-  double ang = (double)pos * theta;
+  const double kTwoPiHi = 6.283185307179586;          // nearest double to 2*pi
+  const double kTwoPiLo = 2.4492935982947064e-16;      // 2*pi - kTwoPiHi
+  const double kInvTwoPi = 0.15915494309189535;
+  const double theta = pow((double)base, -2.0 * (double)u / (double)rope_dim);
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * kInvTwoPi);
+  double r = fma(-k, kTwoPiHi, ang);
+  r = fma(-k, kTwoPiLo, r);
   double sn, cs;
-  sincos(ang, &sn, &cs);
+  sincos(r, &sn, &cs);
   *c = (float)cs;
   *s = (float)sn;
 }

@@ -160,14 +160,99 @@ __device__ __forceinline__ void load_key_frags(bf16x8_t (&Bf)[KS], const void* _
 
 // ---------------------------------------------------------------------------
 // decode: few query rows, keys streamed from HBM straight into registers.
-// Each wave owns kpw consecutive keys of one query row.
+// Each wave owns kpw consecutive keys of one query row and walks them in
+// subtiles of 16 keys with a prefetch ring of PF subtiles in flight.  Four
+// subtiles form a group: every lane first sums its 16 head rows per subtile,
+// then a reduce-scatter across the 4 lane groups (3 cross-lane adds) leaves
+// lane (g, j) with the full score of key j of subtile g, so each group ends
+// in one coalesced 256-byte store.
 // ---------------------------------------------------------------------------
+template <int KS, int KDT>
+struct RawSub {                       // one lane's bytes of one key row for one subtile
+  static constexpr int WORDS = (KDT == DT_FP8 ? 8 * KS : 16 * KS) / 4;
+  uint32_t w[WORDS];
+};
+
+template <int KS, int KDT>
+__device__ __forceinline__ void load_raw(RawSub<KS, KDT>& r, const void* __restrict__ K, size_t row,
+                                         int g, bool valid) {
+  constexpr int BYTES = RawSub<KS, KDT>::WORDS * 4;   // contiguous bytes of this lane
+  const uint8_t* p = (const uint8_t*)K + row * (size_t)(BYTES * 4) + (size_t)BYTES * g;
+  if (valid) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int c = 0; c < BYTES / 16; ++c) {
+        const u32x4_t v = *(const u32x4_t*)(p + 16 * c);
+        r.w[4 * c] = v[0]; r.w[4 * c + 1] = v[1]; r.w[4 * c + 2] = v[2]; r.w[4 * c + 3] = v[3];
+      }
+    } else {
+      const u32x2_t v = *(const u32x2_t*)p;
+      r.w[0] = v[0]; r.w[1] = v[1];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < RawSub<KS, KDT>::WORDS; ++c) r.w[c] = 0u;
+  }
+}
+
+template <int KS, int KDT>
+__device__ __forceinline__ void raw_to_frags(const RawSub<KS, KDT>& r, bf16x8_t (&Bf)[KS]) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if constexpr (KDT == DT_FP8) {
+      // 8 codes -> 8 bf16, exactly (gfx950 conversion, scale 1)
+      bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, false);
+      bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, true);
+      bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, false);
+      bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, true);
+      u32x4_t o;
+      o[0] = __builtin_bit_cast(uint32_t, a); o[1] = __builtin_bit_cast(uint32_t, b);
+      o[2] = __builtin_bit_cast(uint32_t, c); o[3] = __builtin_bit_cast(uint32_t, d);
+      Bf[ks] = __builtin_bit_cast(bf16x8_t, o);
+    } else {
+      u32x4_t o;
+      o[0] = r.w[4 * ks]; o[1] = r.w[4 * ks + 1]; o[2] = r.w[4 * ks + 2]; o[3] = r.w[4 * ks + 3];
+      Bf[ks] = __builtin_bit_cast(bf16x8_t, o);
+    }
+  }
+}
+
+// this lane's share (its 4*QH head rows) of sum_h w * ReLU(dot) for its key column
+template <int QH, int KS>
+__device__ __forceinline__ float partial_column(const IdxFrags<QH, KS>& f, const bf16x8_t (&Bf)[KS]) {
+  f32x4_t acc[QH];
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int mt = 0; mt < QH; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.A[mt][ks], Bf[ks], acc[mt], 0, 0, 0);
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part += f.wv[mt][r] * fmaxf(acc[mt][r], 0.f);
+  return part;
+}
+
+// P[u] = lane group g's share for subtile u; returns the full sum for subtile g
+__device__ __forceinline__ float reduce_scatter4(const float (&P)[4], int g) {
+  const bool hi = (g >> 1) & 1, lo = g & 1;
+  const float s0 = hi ? P[0] : P[2], s1 = hi ? P[1] : P[3];
+  const float k0 = (hi ? P[2] : P[0]) + __shfl_xor(s0, 32, 64);   // subtile 2*hi
+  const float k1 = (hi ? P[3] : P[1]) + __shfl_xor(s1, 32, 64);   // subtile 2*hi + 1
+  const float s = lo ? k0 : k1;
+  return (lo ? k1 : k0) + __shfl_xor(s, 16, 64);                  // subtile 2*hi + lo = g
+}
+
 template <int QH, int KS, int KDT>
 __global__ __launch_bounds__(256) void index_mfma_decode(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ K,
     const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
     int kpw, float* __restrict__ out) {
   constexpr int H = 16 * QH, DI = 32 * KS;
+  constexpr int PF = (KDT == DT_FP8) ? 4 : 2;   // subtiles in flight per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int b = blockIdx.z, t = blockIdx.y;
@@ -175,6 +260,7 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
   const long long k0 = ((long long)blockIdx.x * 4 + wave) * kpw;
   if (k0 >= N_cap) return;
   const long long k1 = min(k0 + (long long)kpw, N_cap);
+  const int nst = (int)((k1 - k0 + 15) / 16);
   const long long i = q_pos[qrow];
   const long long nvis = min(N_cap, (i + 1) / m);
 
@@ -183,16 +269,33 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
   const size_t kbase = (size_t)b * (size_t)N_cap;
   float* orow = out + qrow * (size_t)N_cap;
 
-  for (long long kb = k0; kb < k1; kb += 16) {
-    const long long key = kb + j;
-    const bool kin = key < k1;
-    bf16x8_t Bf[KS];
-    load_key_frags<KS, KDT>(Bf, K, kbase + (size_t)(kin ? key : k0), g, kin);
-    float v = score_column<QH, KS>(f, Bf);
-    if (g == 0 && kin) {
-      if constexpr (KDT == DT_FP8) v *= Ks[kbase + (size_t)key];
-      orow[key] = key < nvis ? v : -INFINITY;
+  RawSub<KS, KDT> ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const long long key = k0 + 16 * p + j;
+    load_raw<KS, KDT>(ring[p], K, kbase + (size_t)(key < k1 ? key : k0), g, p < nst && key < k1);
+  }
+  for (int st0 = 0; st0 < nst; st0 += 4) {
+    // this lane's store target and (fp8) row scale, fetched early
+    const long long okey = k0 + 16LL * (st0 + g) + j;
+    const bool ook = okey < k1;
+    float osc = 1.f;
+    if constexpr (KDT == DT_FP8) osc = ook ? Ks[kbase + (size_t)okey] : 1.f;
+    float P[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = st0 + u;
+      RawSub<KS, KDT> cur = ring[u % PF];
+      const int nx = st + PF;
+      const long long nkey = k0 + 16LL * nx + j;
+      load_raw<KS, KDT>(ring[u % PF], K, kbase + (size_t)(nkey < k1 ? nkey : k0), g,
+                        nx < nst && nkey < k1);
+      bf16x8_t Bf[KS];
+      raw_to_frags<KS, KDT>(cur, Bf);
+      P[u] = partial_column<QH, KS>(f, Bf);
     }
+    const float v = reduce_scatter4(P, g);
+    if (ook) orow[okey] = okey < nvis ? v * osc : -INFINITY;
   }
 }
 
@@ -333,6 +436,21 @@ bool index_mfma_supported(const IndexArgs& a) {
   return true;
 }
 
+// waves of a kernel that fit on the whole device at once (cached per kernel)
+static long long resident_waves(const void* kfn, int block) {
+  static thread_local const void* last_fn = nullptr;
+  static thread_local long long last = 0;
+  if (kfn == last_fn) return last;
+  int dev = 0, cus = 256, per_cu = 1;
+  if (hipGetDevice(&dev) == hipSuccess)
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, block, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  last_fn = kfn;
+  last = (long long)cus * per_cu * (block / 64);
+  return last;
+}
+
 static constexpr int PF_MIN_TQ = 8;   // query rows per sequence at which the LDS-tiled kernel is used
 static constexpr int PF_QPW = 2;
 
@@ -344,12 +462,13 @@ static void launch_mfma(const IndexArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((index_mfma_prefill<QH, KS, KDT, PF_QPW>), grid, dim3(256), 0, st, q, a.w,
                        a.K, a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out);
   } else {
-    // about 8k waves over the whole launch, each wave at least 64 keys
+    // one round of resident waves over the chip, each wave at least 64 keys
+    auto kfn = index_mfma_decode<QH, KS, KDT>;
+    const long long waves = resident_waves((const void*)kfn, 256);
     long long rows = (long long)a.B * a.Tq;
-    long long kpw = (a.N_cap * rows + 8191) / 8192;
+    long long kpw = (a.N_cap * rows + waves - 1) / waves;
     kpw = ((kpw + 63) / 64) * 64;
     if (kpw < 64) kpw = 64;
-    if (kpw > 4096) kpw = 4096;
     long long nblk = (a.N_cap + 4 * kpw - 1) / (4 * kpw);
     dim3 grid((unsigned)nblk, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((index_mfma_decode<QH, KS, KDT>), grid, dim3(256), 0, st, q, a.w, a.K,

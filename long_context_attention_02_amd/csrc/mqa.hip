@@ -29,7 +29,7 @@
 namespace csa {
 
 static constexpr int MQ_CH = 32;          // key rows per LDS chunk
-static constexpr int MQ_SPLIT_KEYS = 256; // slots per workgroup when a query is split
+static constexpr int MQ_SPLIT_KEYS = 128; // slots per workgroup when a query is split
 static constexpr int MQ_SPLIT_BELOW_TQ = 16;
 static constexpr int VALU_MAX_SLOTS = 8192;
 
@@ -157,28 +157,59 @@ __global__ __launch_bounds__(256) void mqa_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // matrix-core path (bf16), D in {128, 256, 512}, n_h % 16 == 0
+//
+// Key slots are processed in groups of 128 held in LDS at once: all scores of
+// the group first (the group maximum is then exact, so P needs no rescaling
+// inside the group), then P.V.  Across groups (long slot lists, prefill) the
+// reference maximum moves only when a group maximum exceeds it by more than 8
+// (natural log units): P stays <= e^8 and O is rescaled rarely; the result is
+// the same softmax, only the fp32 reference point differs.
+//
+// LDS layout: rows of D bf16, no padding; the 16-byte piece c of row r sits at
+// piece position c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1), which
+// keeps the two read patterns conflict-free: 16 lanes reading the same piece
+// of 16 consecutive rows (S^T operand) and 16 lanes reading two pieces of 4
+// consecutive rows (transpose read of V).  Rows arrive with global_load_lds
+// (16 bytes per lane; lane l fills piece position l of the wave's 1 KB window).
 // ---------------------------------------------------------------------------
-template <int D, bool DENSE>
+static constexpr int MQ_GROUP = 128;   // slots resident in LDS at once (4 chunks of 32)
+static constexpr float MQ_REF_SLACK = 8.f;
+
+__device__ __forceinline__ int mq_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ uint32_t pack2_bf16_hw(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 v2bf;
+  const v2bf v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32 (round to nearest even)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int D, bool DENSE, bool MULTI>
 __global__ __launch_bounds__(256) void mqa_mfma_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
     const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
-    int kps, int n_split, uint16_t* __restrict__ out, float* __restrict__ ws) {
-  constexpr int KS = D / 32;         // 8-dim chunks per lane group (S^T K-steps)
-  constexpr int GW = D / 4;          // dims per lane group
-  constexpr int NT = D / 16;         // 16-dim output tiles
-  constexpr int ROWB = D * 2 + 32;   // padded LDS row, bytes
-  constexpr int PPR = D * 2 / 16;    // 16-byte pieces per row
-  constexpr int PIECES = MQ_CH * PPR;
-  __shared__ __attribute__((aligned(16))) uint8_t kv[MQ_CH * ROWB];
-  __shared__ int slot_ok[MQ_CH];
-  __shared__ float rope_cs[D];   // (cos, sin) of the angle i * theta_u, u < rope_dim / 2
+    int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
+  constexpr int KS = D / 32;          // 8-dim chunks per lane group (S^T K-steps)
+  constexpr int GW = D / 4;           // dims per lane group
+  constexpr int NT = D / 16;          // 16-dim output tiles
+  constexpr int RB = D * 2;           // row bytes
+  constexpr int CPR = RB / 16;        // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;       // rows per 1 KB load instruction
+  constexpr int NKT = MQ_GROUP / 16;  // key tiles per group
+  extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_GROUP * RB bytes
+  __shared__ const uint16_t* srow[MQ_GROUP];   // row pointer of each slot (nullptr = empty)
+  __shared__ float rope_cs[D];                 // (cos, sin) at i * theta_u, u < rope_dim / 2
 
+  // ---- unit of work; the n_hg head groups of a unit are 8 workgroups apart (same XCD)
   const int n_hg = (n_h + 63) / 64;
-  const int hg = blockIdx.x % n_hg, sp = blockIdx.x / n_hg;
-  const int t = blockIdx.y, b = blockIdx.z;
-  const size_t row = (size_t)b * Tq + t;
+  const long long L = blockIdx.x;
+  const int hg = (int)((L / 8) % n_hg);
+  const long long unit = (L / (8LL * n_hg)) * 8 + (L % 8);
+  if (unit >= n_units) return;
+  const int sp = (int)(unit % n_split);
+  const size_t row = (size_t)(unit / n_split);
+  const int b = (int)(row / Tq);
   const long long i = q_pos[row];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, j = lane & 15;
@@ -188,12 +219,13 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
 
   for (int u = threadIdx.x; u < rope_dim / 2; u += 256)
     rope_cos_sin(i, u, rope_dim, rope_base, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
-  __syncthreads();
 
   const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
   const int* idx_row = DENSE ? nullptr : idx + row * (size_t)k;
   const long long s0 = (long long)sp * kps;
   const long long s1 = min(s0 + (long long)kps, qs.n_slots);
+  const uint16_t* dummy = E + (size_t)b * (size_t)N_cap * D;   // a valid row for empty slots
+  __syncthreads();
 
   // ---- q^ = RoPE_i(RMSNorm(q)) as the B operand of S^T: head hq, dims GW*g + 8ks + e
   bf16x8_t qf[KS];
@@ -229,104 +261,136 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
           v0 = r0;
           v1 = r1;
         }
-        packed[e] = pack_bf16x2(v0, v1);
+        packed[e] = pack2_bf16_hw(v0, v1);
       }
       qf[ks] = __builtin_bit_cast(bf16x8_t, packed);
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.f;    // softmax state of head hq
+  float m_run = -INFINITY, l_run = 0.f;    // softmax state of head hq (m_run: reference maximum)
   f32x4_t O[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) O[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (long long c0 = s0; c0 < s1; c0 += MQ_CH) {
-    // ---- stage the chunk's rows (row-major, padded) into LDS
-    for (int p = threadIdx.x; p < PIECES; p += 256) {
-      const int r = p / PPR, c16 = p % PPR;
-      const long long slot = c0 + r;
-      long long off = -1;
-      bool in_E = true;
-      if (slot < s1) off = slot_row<DENSE>(slot, qs, idx_row, b, N_cap, W_cap, D, &in_E);
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (off >= 0) v = *(const u32x4_t*)((in_E ? E : W) + off + 8 * c16);
-      *(u32x4_t*)(&kv[r * ROWB + c16 * 16]) = v;
-      if (c16 == 0) slot_ok[r] = off >= 0;
+  for (long long g0 = s0; g0 < s1; g0 += MQ_GROUP) {
+    const int nrows = (int)min((long long)MQ_GROUP, s1 - g0);
+    const int nch = (nrows + 31) / 32;                 // 32-row chunks holding slots
+    // ---- resolve the group's slots, then copy their rows into LDS (swizzled pieces)
+    if (threadIdx.x < MQ_GROUP) {
+      const uint16_t* p = nullptr;
+      if (threadIdx.x < nrows) {
+        bool in_E;
+        const long long off = slot_row<DENSE>(g0 + threadIdx.x, qs, idx_row, b, N_cap, W_cap, D, &in_E);
+        if (off >= 0) p = (in_E ? E : W) + off;
+      }
+      srow[threadIdx.x] = p;
     }
     __syncthreads();
+    for (int r0 = wave * RPI; r0 < nch * 32; r0 += 4 * RPI) {
+      const int r = r0 + lane / CPR;
+      const int c = (lane % CPR) ^ mq_swz(r);
+      const uint16_t* p = srow[r];
+      const uint8_t* src = (const uint8_t*)(p ? p : dummy) + 16 * c;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (__attribute__((address_space(3))) void*)(kv + r0 * RB), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     if (wact) {
-      // ---- S^T: keys (M) x heads (N), two tiles of 16 keys
-      f32x4_t S[2];
+      // ---- phase 1: S^T for every key tile of the group (keys as M, heads as N).
+      // K-step outer, 8 independent accumulators inner, so the LDS reads of a step
+      // overlap.  Tiles past the group's rows read stale LDS; their scores are masked.
+      f32x4_t S[NKT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < NKT; ++kt) S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8_t a = *(const bf16x8_t*)(&kv[(16 * kt + j) * ROWB + (GW * g + 8 * ks) * 2]);
-          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], S[kt], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        bf16x8_t a[NKT];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          const int rr = 16 * kt + j;
+          a[kt] = *(const bf16x8_t*)(kv + rr * RB + 16 * ((GW * g / 8 + ks) ^ mq_swz(rr)));
         }
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+          S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kt], qf[ks], S[kt], 0, 0, 0);
       }
       // lane (g, j): S[kt][r] = score of key 16 kt + 4 g + r for head hq
-      float lg[2][4];
       float mx = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const bool ok = slot_ok[16 * kt + 4 * g + r] != 0;
-          lg[kt][r] = ok ? S[kt][r] * scale : -INFINITY;
-          mx = fmaxf(mx, lg[kt][r]);
+          const int rr = 16 * kt + 4 * g + r;
+          const bool ok = rr < nrows && srow[rr] != nullptr;
+          S[kt][r] = ok ? S[kt][r] * scale : -INFINITY;
+          mx = fmaxf(mx, S[kt][r]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __expf(m_run - m_new);
-      float p[2][4];
-      float psum = 0.f;
+      if constexpr (MULTI) {
+        // move the reference maximum only when it would be exceeded by more than the slack
+        if (__any(mx > m_run + MQ_REF_SLACK)) {
+          const float m_new = (mx > m_run + MQ_REF_SLACK) ? mx : m_run;
+          const float alpha = (m_run == -INFINITY) ? 0.f : __expf(m_run - m_new);
+          l_run *= alpha;
+          m_run = m_new;
+          if (__any(alpha != 0.f)) {   // O is still zero while nothing has been accumulated
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+            for (int r = 0; r < 4; ++r) {
+              const float ar = __shfl(alpha, 4 * g + r, 64);
+#pragma unroll
+              for (int nt = 0; nt < NT; ++nt) O[nt][r] *= ar;
+            }
+          }
+        }
+      } else {
+        m_run = mx;   // a single group: its maximum is the reference
+      }
+      float psum = 0.f;
+      bf16x8_t pf[NKT / 2];
+#pragma unroll
+      for (int kk = 0; kk < NKT / 2; ++kk) {
+        float p[8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[kt][r] = (lg[kt][r] == -INFINITY) ? 0.f : __expf(lg[kt][r] - m_new);
-          psum += p[kt][r];
+          p[r] = (S[2 * kk][r] == -INFINITY) ? 0.f : __expf(S[2 * kk][r] - m_run);
+          p[4 + r] = (S[2 * kk + 1][r] == -INFINITY) ? 0.f : __expf(S[2 * kk + 1][r] - m_run);
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) psum += p[e];
+        u32x4_t pw;
+        pw[0] = pack2_bf16_hw(p[0], p[1]);
+        pw[1] = pack2_bf16_hw(p[2], p[3]);
+        pw[2] = pack2_bf16_hw(p[4], p[5]);
+        pw[3] = pack2_bf16_hw(p[6], p[7]);
+        pf[kk] = __builtin_bit_cast(bf16x8_t, pw);
+      }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      // O rows are heads 4g + r: fetch their alpha from lane 4g + r
-      if (__any(alpha != 1.f)) {
+      l_run += psum;
+      // ---- phase 2: P (A operand: head j, keys {4g..4g+3, 16+4g..16+4g+3} of each
+      // 32-key step) times V (transpose reads of the swizzled rows)
+      const int half = 8 * (j & 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = __shfl(alpha, 4 * g + r, 64);
+      for (int kk = 0; kk < NKT / 2; ++kk) {
+        if (kk < nch) {
+          const int tr0 = 32 * kk + 4 * g + (j >> 2), tr1 = tr0 + 16;
+          const int sw0 = mq_swz(tr0), sw1 = mq_swz(tr1);
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt) O[nt][r] *= ar;
+          for (int nt = 0; nt < NT; ++nt) {
+            const int pc = 2 * nt + ((j & 3) >> 1);
+            const u32x2_t v0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4_t*)(kv + tr0 * RB + 16 * (pc ^ sw0) + half)));
+            const u32x2_t v1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) short4_t*)(kv + tr1 * RB + 16 * (pc ^ sw1) + half)));
+            const u32x4_t vw = {v0[0], v0[1], v1[0], v1[1]};
+            O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[kk], __builtin_bit_cast(bf16x8_t, vw), O[nt], 0, 0, 0);
+          }
         }
       }
-      // ---- P (A operand: head j, keys {4g..4g+3, 16+4g..16+4g+3}) times V
-      u32x4_t pw;
-      pw[0] = pack_bf16x2(p[0][0], p[0][1]);
-      pw[1] = pack_bf16x2(p[0][2], p[0][3]);
-      pw[2] = pack_bf16x2(p[1][0], p[1][1]);
-      pw[3] = pack_bf16x2(p[1][2], p[1][3]);
-      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pw);
-      const int trow = 4 * g + (j >> 2);
-      const int tcol = 4 * (j & 3);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(&kv[trow * ROWB + (16 * nt + tcol) * 2]));
-        const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(&kv[(16 + trow) * ROWB + (16 * nt + tcol) * 2]));
-        u32x4_t vw;
-        vw[0] = (uint32_t)(uint16_t)v0[0] | ((uint32_t)(uint16_t)v0[1] << 16);
-        vw[1] = (uint32_t)(uint16_t)v0[2] | ((uint32_t)(uint16_t)v0[3] << 16);
-        vw[2] = (uint32_t)(uint16_t)v1[0] | ((uint32_t)(uint16_t)v1[1] << 16);
-        vw[3] = (uint32_t)(uint16_t)v1[2] | ((uint32_t)(uint16_t)v1[3] << 16);
-        O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, __builtin_bit_cast(bf16x8_t, vw), O[nt], 0, 0, 0);
-      }
     }
-    __syncthreads();
+    __syncthreads();   // LDS rows and srow are rewritten by the next group
   }
   if (!wact) return;
 
@@ -374,7 +438,262 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
   }
 }
 
-// merge the split partial states of one (query, head) in split order
+// ---------------------------------------------------------------------------
+// single-group kernel (every split holds <= 128 slots: decode).  Phase 1 as in
+// the multi-group kernel (wave w: S^T of head tile w over the 128 slots); P
+// goes to LDS; phase 2 gives wave w the output dims [w D/4, (w+1) D/4) of all
+// 64 heads, so each transposed V fragment read from LDS feeds four MFMAs
+// (one per head tile) and the accumulators are not live during phase 1.
+// ---------------------------------------------------------------------------
+template <int D, bool DENSE>
+__global__ __launch_bounds__(256) void mqa_group_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
+    const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
+    const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
+  constexpr int KS = D / 32, GW = D / 4, RB = D * 2, CPR = RB / 16, RPI = 64 / CPR;
+  constexpr int NKT = MQ_GROUP / 16;   // key tiles (8)
+  constexpr int NKK = MQ_GROUP / 32;   // 32-key MFMA steps of P.V (4)
+  constexpr int NTW = D / 64;          // 16-dim output tiles per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_GROUP * RB bytes
+  __shared__ const uint16_t* srow[MQ_GROUP];
+  __shared__ float rope_cs[D];
+  __shared__ u32x4_t pbuf[4][NKK][64];   // P fragments: [head tile][32-key step][lane]
+  __shared__ float fstat[64], mstat[64], lstat[64];
+
+  const int n_hg = (n_h + 63) / 64;
+  const long long L = blockIdx.x;
+  const int hg = (int)((L / 8) % n_hg);
+  const long long unit = (L / (8LL * n_hg)) * 8 + (L % 8);
+  if (unit >= n_units) return;
+  const int sp = (int)(unit % n_split);
+  const size_t row = (size_t)(unit / n_split);
+  const int b = (int)(row / Tq);
+  const long long i = q_pos[row];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int hbase = 64 * hg;
+  const int ntiles = min(4, (n_h - hbase) / 16);   // valid head tiles of this workgroup
+  const bool wact = wave < ntiles;
+  const int hq = wact ? hbase + 16 * wave + j : 0;
+
+  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
+  const int* idx_row = DENSE ? nullptr : idx + row * (size_t)k;
+  const long long s0 = (long long)sp * kps;
+  const long long s1 = min(s0 + (long long)kps, qs.n_slots);
+  const int nrows = (int)max(0LL, min((long long)MQ_GROUP, s1 - s0));
+  const int nch = (nrows + 31) / 32;
+  const uint16_t* dummy = E + (size_t)b * (size_t)N_cap * D;
+
+  for (int u = threadIdx.x; u < rope_dim / 2; u += 256)
+    rope_cos_sin(i, u, rope_dim, rope_base, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
+  if (threadIdx.x < MQ_GROUP) {
+    const uint16_t* p = nullptr;
+    if (threadIdx.x < nrows) {
+      bool in_E;
+      const long long off = slot_row<DENSE>(s0 + threadIdx.x, qs, idx_row, b, N_cap, W_cap, D, &in_E);
+      if (off >= 0) p = (in_E ? E : W) + off;
+    }
+    srow[threadIdx.x] = p;
+  }
+  __syncthreads();
+  for (int r0 = wave * RPI; r0 < nch * 32; r0 += 4 * RPI) {
+    const int r = r0 + lane / CPR;
+    const int c = (lane % CPR) ^ mq_swz(r);
+    const uint16_t* p = srow[r];
+    const uint8_t* src = (const uint8_t*)(p ? p : dummy) + 16 * c;
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (__attribute__((address_space(3))) void*)(kv + r0 * RB), 16, 0, 0);
+  }
+
+  // ---- phase 1 (wave w = head tile w): q^, S^T over the group, softmax statistics, P
+  if (wact) {
+    bf16x8_t qf[KS];
+    {
+      u32x4_t raw[KS];
+      float ss = 0.f;
+      const uint16_t* qp = q + (row * n_h + hq) * (size_t)D + GW * g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        raw[ks] = *(const u32x4_t*)(qp + 8 * ks);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x0 = __uint_as_float(raw[ks][e] << 16);
+          const float x1 = __uint_as_float(raw[ks][e] & 0xffff0000u);
+          ss += x0 * x0 + x1 * x1;
+        }
+      }
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float rinv = 1.f / sqrtf(ss / (float)D + eps);
+      const int rbeg = D - rope_dim;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t packed;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dim = GW * g + 8 * ks + 2 * e;
+          float v0 = __uint_as_float(raw[ks][e] << 16) * rinv * (gamma_q ? gamma_q[dim] : 1.f);
+          float v1 = __uint_as_float(raw[ks][e] & 0xffff0000u) * rinv * (gamma_q ? gamma_q[dim + 1] : 1.f);
+          if (dim >= rbeg) {
+            const float cs = rope_cs[dim - rbeg], sn = rope_cs[dim - rbeg + 1];
+            const float r0 = v0 * cs - v1 * sn, r1 = v0 * sn + v1 * cs;
+            v0 = r0;
+            v1 = r1;
+          }
+          packed[e] = pack2_bf16_hw(v0, v1);
+        }
+        qf[ks] = __builtin_bit_cast(bf16x8_t, packed);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // (a) rows landed
+    f32x4_t S[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) S[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t a[NKT];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        const int rr = 16 * kt + j;
+        a[kt] = *(const bf16x8_t*)(kv + rr * RB + 16 * ((GW * g / 8 + ks) ^ mq_swz(rr)));
+      }
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+        S[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kt], qf[ks], S[kt], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = 16 * kt + 4 * g + r;
+        const bool ok = rr < nrows && srow[rr] != nullptr;
+        S[kt][r] = ok ? S[kt][r] * scale : -INFINITY;
+        mx = fmaxf(mx, S[kt][r]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float psum = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = (S[2 * kk][r] == -INFINITY) ? 0.f : __expf(S[2 * kk][r] - mx);
+        p[4 + r] = (S[2 * kk + 1][r] == -INFINITY) ? 0.f : __expf(S[2 * kk + 1][r] - mx);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) psum += p[e];
+      u32x4_t pw;
+      pw[0] = pack2_bf16_hw(p[0], p[1]);
+      pw[1] = pack2_bf16_hw(p[2], p[3]);
+      pw[2] = pack2_bf16_hw(p[4], p[5]);
+      pw[3] = pack2_bf16_hw(p[6], p[7]);
+      pbuf[wave][kk][lane] = pw;
+    }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+    if (g == 0) {
+      const int hl = 16 * wave + j;
+      mstat[hl] = mx;
+      lstat[hl] = psum;
+      const float sig = sink ? sink[hq] : -INFINITY;
+      const float M = fmaxf(mx, sig);
+      float Z = 0.f;
+      if (mx != -INFINITY) Z += psum * __expf(mx - M);
+      if (sig != -INFINITY) Z += __expf(sig - M);
+      fstat[hl] = (Z > 0.f && mx != -INFINITY) ? __expf(mx - M) / Z : 0.f;
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // (a)
+  }
+  __syncthreads();     // (b) P and the statistics are visible
+
+  // ---- phase 2 (wave w = output dims [w D/4, (w+1) D/4) of every head tile)
+  f32x4_t O[4][NTW];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) O[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int dbase = wave * (D / 4);
+  const int half = 8 * (j & 1);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (kk < nch) {
+      const int tr0 = 32 * kk + 4 * g + (j >> 2), tr1 = tr0 + 16;
+      const int sw0 = mq_swz(tr0), sw1 = mq_swz(tr1);
+      bf16x8_t vf[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int pc = (dbase + 16 * nt) / 8 + ((j & 3) >> 1);
+        const u32x2_t v0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(kv + tr0 * RB + 16 * (pc ^ sw0) + half)));
+        const u32x2_t v1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(kv + tr1 * RB + 16 * (pc ^ sw1) + half)));
+        const u32x4_t vw = {v0[0], v0[1], v1[0], v1[1]};
+        vf[nt] = __builtin_bit_cast(bf16x8_t, vw);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt < ntiles) {
+          const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, pbuf[mt][kk][lane]);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            O[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf[nt], O[mt][nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- output: lane (g, j) of tile (mt, nt) holds heads 16mt + 4g + r, dim dbase + 16nt + j
+  const int rbeg = D - rope_dim;
+  if (n_split == 1) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= ntiles) continue;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int dim = dbase + 16 * nt + j;
+        float cs = 1.f, sn = 0.f;   // rotation at -i: cos(-x) = cos x, sin(-x) = -sin x
+        if (dim >= rbeg) {
+          cs = rope_cs[(dim - rbeg) & ~1];
+          sn = -rope_cs[((dim - rbeg) & ~1) + 1];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hl = 16 * mt + 4 * g + r;
+          const float v = O[mt][nt][r] * fstat[hl];
+          const float other = __shfl_xor(v, 1, 64);
+          float o = v;
+          if (dim >= rbeg) o = (dim & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+          out[(row * n_h + hbase + hl) * (size_t)D + dim] = f32_to_bf16_bits(o);
+        }
+      }
+    }
+  } else {
+    const size_t pbase = (row * n_split + sp) * (size_t)n_h + hbase;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt >= ntiles) continue;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ws[(pbase + 16 * mt + 4 * g + r) * (D + 2) + dbase + 16 * nt + j] = O[mt][nt][r];
+    }
+    if (threadIdx.x < 16 * ntiles) {
+      ws[(pbase + threadIdx.x) * (D + 2) + D] = mstat[threadIdx.x];
+      ws[(pbase + threadIdx.x) * (D + 2) + D + 1] = lstat[threadIdx.x];
+    }
+  }
+}
+
+// merge the split partial states of one (query, head) in split order, one pass
+// with a running maximum; each thread owns one pair of output dims
 __global__ __launch_bounds__(256) void mqa_combine_kernel(
     const float* __restrict__ ws, const float* __restrict__ sink, const int* __restrict__ q_pos,
     int Tq, int n_h, int D, int n_split, int rope_dim, float rope_base, uint16_t* __restrict__ out) {
@@ -382,30 +701,28 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const size_t row = (size_t)b * Tq + t;
   const long long i = q_pos[row];
   const float sig = sink ? sink[h] : -INFINITY;
-  auto part = [&](int s) { return ws + ((row * n_split + s) * (size_t)n_h + h) * (D + 2); };
-  float M = sig;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part(s)[D]);
-  float Z = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float ms = part(s)[D];
-      if (ms != -INFINITY) Z += part(s)[D + 1] * __expf(ms - M);
-    }
-    if (sig != -INFINITY) Z += __expf(sig - M);
-  }
-  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  const float* base = ws + (row * n_split * (size_t)n_h + h) * (D + 2);
+  const size_t sstride = (size_t)n_h * (D + 2);
   const int rbeg = D - rope_dim;
+  float M = sig;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * sstride + D]);
+  float Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
+  for (int s = 0; s < n_split; ++s) {
+    const float ms = base[s * sstride + D];
+    if (ms != -INFINITY) Z += base[s * sstride + D + 1] * __expf(ms - M);
+  }
   for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
     const int d0 = 2 * u;
     float o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
     for (int s = 0; s < n_split; ++s) {
-      const float* ps = part(s);
+      const float* ps = base + s * sstride;
       const float ms = ps[D];
-      if (ms == -INFINITY) continue;
-      const float f = __expf(ms - M);
+      const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
       o0 += ps[d0] * f;
       o1 += ps[d0 + 1] * f;
     }
+    const float inv = Z > 0.f ? 1.f / Z : 0.f;
     o0 *= inv;
     o1 *= inv;
     if (d0 >= rbeg) {
@@ -435,6 +752,7 @@ long long mqa_slots_max(const MqaArgs& a) {
 static void mqa_split(int Tq, long long slots_max, int* kps, int* n_split) {
   if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
     long long s = ((slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH;
+    if (s > 2147483647LL) s = 2147483647LL;
     *kps = (int)(s > 0 ? s : MQ_CH);
     *n_split = 1;
   } else {
@@ -451,18 +769,30 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
   return (size_t)B * Tq * n_split * n_h * (size_t)(d + 2) * sizeof(float);
 }
 
-template <int D, bool DENSE>
-static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
+template <int D, bool DENSE, bool MULTI>
+static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   const int n_hg = (a.n_h + 63) / 64;
-  dim3 grid((unsigned)(n_split * n_hg), (unsigned)a.Tq, (unsigned)a.B);
-  hipLaunchKernelGGL((mqa_mfma_kernel<D, DENSE>), grid, dim3(256), 0, st, (const uint16_t*)a.q,
-                     a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx, a.k, a.m,
-                     (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
-                     a.rope_dim, a.rope_base, a.scale, kps, n_split, (uint16_t*)a.out, (float*)a.ws);
+  const long long units = (long long)a.B * a.Tq * n_split;
+  const long long blocks = ((units + 7) / 8) * 8 * n_hg;
+  const size_t lds = (size_t)MQ_GROUP * D * 2;
+  auto kfn = MULTI ? mqa_mfma_kernel<D, DENSE, true> : mqa_group_kernel<D, DENSE>;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(256), lds, st,
+                     (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
+                     a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
+                     a.rope_dim, a.rope_base, a.scale, kps, n_split, units, (uint16_t*)a.out,
+                     (float*)a.ws);
   if (n_split > 1)
     hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
                        dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
                        n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
+}
+
+template <int D, bool DENSE>
+static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
+  if (kps <= MQ_GROUP) launch_mfma_v<D, DENSE, false>(a, kps, n_split, st);
+  else launch_mfma_v<D, DENSE, true>(a, kps, n_split, st);
 }
 
 int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {

@@ -1,0 +1,106 @@
+"""The oracle's own composition of one workload step, per sequence.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__.py``): used by the full-size parity
+tests and by the CPU-baseline leg of the benchmark.  It chains the fp64
+functions of ``oracle.csa`` in the order of the DeepSeek-V4 method page
+(section 3.3): the entries that complete are compressed and stored, the
+indexer scores every visible entry, the top-k is taken, and the query attends
+over the selected entries, the window rows and the sink.
+
+Stored rows are rounded to their storage format (bf16 entries and window rows,
+e4m3 indexer keys with a per-row scale) because the caches hold those bytes.
+Inputs are fp64 arrays of the exact stored input values; the raw rows of the
+entry cache are fetched on demand through a callable, so only the rows a
+query touches are ever decoded.
+"""
+from __future__ import annotations
+
+from typing import Callable
+
+import numpy as np
+
+from . import csa as O
+from .codecs import e4m3_to_f64, f64_to_bf16_value
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f64_to_bf16_value(x) if dtype == "bf16" else np.asarray(x, dtype=np.float64)
+
+
+def entry_rows(raw_rows: np.ndarray, s: np.ndarray, *, m: int, rope_dim: int, rope_base: float,
+               eps: float, dtype: str) -> np.ndarray:
+    """Cache rows built from pre-norm rows: RMSNorm, RoPE at position m*s, storage rounding."""
+    E = O.rope(O.rmsnorm(raw_rows, None, eps), m * np.asarray(s), rope_dim, rope_base)
+    return _store(E, dtype)
+
+
+def window_rows(raw_rows: np.ndarray, toks: np.ndarray, *, rope_dim: int, rope_base: float,
+                eps: float, dtype: str) -> np.ndarray:
+    W = O.rope(O.rmsnorm(raw_rows, None, eps), np.asarray(toks), rope_dim, rope_base)
+    return _store(W, dtype)
+
+
+def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
+    """One CSA decode step of one sequence.
+
+    p holds: i, m, N, k, n_win, d_I, rope_dim, rope_base, eps, scale, dtype, k_dtype;
+    KI (N x d_I fp64, fp8 keys already times their scale), win_raw (n_win x d,
+    tokens i-n_win+1..i), Ca/Za/Cb/Zb (2m x d, tokens m(N-2)..mN-1),
+    ICa/IZa/ICb/IZb (2m x d_I), qI (H x d_I), w (H), q (n_h x d), sink (n_h).
+    kv_raw_rows(s) returns the pre-norm rows of entries s.
+    """
+    i, m, N, k, n_win = p["i"], p["m"], p["N"], p["k"], p["n_win"]
+    r, base, eps = p["rope_dim"], p["rope_base"], p["eps"]
+    T = m * N
+    tok_base = m * (N - 2)
+    # newest complete block: KV entry (norm + RoPE) and indexer key (no norm, stored format)
+    e_new = O.compress(p["Ca"], p["Za"], p["Cb"], p["Zb"], m=m, overlap=1, T=T, tok_base=tok_base,
+                       s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]
+    e_new = _store(e_new, p["dtype"])
+    k_new = O.compress(p["ICa"], p["IZa"], p["ICb"], p["IZb"], m=m, overlap=1, T=T, tok_base=tok_base,
+                       s_begin=N - 1, s_end=N, normalize=False)
+    if p["k_dtype"] == "e4m3":
+        codes, sc = O.quantize_rows_e4m3(k_new)
+        k_new = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
+    else:
+        k_new = _store(k_new, p["k_dtype"])
+    KI = p["KI"].copy()
+    KI[N - 1] = k_new[0]
+    # index, top-k
+    I = O.index_score(p["qI"][None], p["w"][None], KI, [i], m=m)
+    idx, vals = O.topk(I, [i], m=m, k=k)
+    # rows the query reads
+    sel = idx[0][idx[0] >= 0]
+    rows = np.zeros((len(sel), p["q"].shape[-1]))
+    old = sel[sel != N - 1]
+    if len(old):
+        rows[sel != N - 1] = entry_rows(kv_raw_rows(old), old, m=m, rope_dim=r, rope_base=base,
+                                        eps=eps, dtype=p["dtype"])
+    rows[sel == N - 1] = e_new
+    toks = np.arange(i - n_win + 1, i + 1)
+    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
+    out = O.attend_one(p["q"], np.concatenate([rows, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
+                       rope_base=base, scale=p["scale"])
+    return {"I": I[0], "idx": idx[0], "vals": vals[0], "out": out}
+
+
+def hca_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
+    """One HCA decode step of one sequence: recompress the just-completed block,
+    then dense attention over every visible entry, the window and the sink.
+    p holds: i, m, N, n_win, rope_dim, rope_base, eps, scale, dtype, C, Z (m x d),
+    win_raw, q, sink."""
+    i, m, N, n_win = p["i"], p["m"], p["N"], p["n_win"]
+    r, base, eps = p["rope_dim"], p["rope_base"], p["eps"]
+    n_vis = O.n_visible(i, m, N)
+    s = np.arange(n_vis)
+    E = np.zeros((n_vis, p["q"].shape[-1]))
+    E[: N - 1] = entry_rows(kv_raw_rows(s[: N - 1]), s[: N - 1], m=m, rope_dim=r, rope_base=base,
+                            eps=eps, dtype=p["dtype"])
+    e_new = O.compress(p["C"], p["Z"], None, None, m=m, overlap=0, T=m * N, tok_base=m * (N - 1),
+                       s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]
+    E[N - 1] = _store(e_new, p["dtype"])
+    toks = np.arange(i - n_win + 1, i + 1)
+    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
+    out = O.attend_one(p["q"], np.concatenate([E, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
+                       rope_base=base, scale=p["scale"])
+    return {"out": out}
