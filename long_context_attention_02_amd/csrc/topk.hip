@@ -4,18 +4,20 @@
 // top-k of its indexer scores (k = 512 / 1024 in the report digest).  Order:
 // score descending, ties to the lower index; -0.0 equals +0.0.
 //
-// Every visible element becomes a unique 64-bit key
+// Every visible element has a unique 64-bit key
 //     K64 = ord(score) << 32 | (0xFFFFFFFF - index)
 // where ord() is the order-preserving map of a float onto uint32.  The k
-// largest K64 are exactly the requested selection in the requested order, so
-// an MSD radix select on K64 finds the k-th largest key T without any tie
-// special case, one pass collects all K64 >= T, and a bitonic sort in LDS
-// orders them.  No atomic decides anything but the slot an element lands in
-// before the sort, so results are deterministic.
+// largest K64 are exactly the requested selection in the requested order.  An
+// MSD radix select finds the threshold: 10-bit digits of the 32-bit score key
+// first (LDS histograms, the digit located by one wave), and only when the k-th
+// score is tied, further digits of the index half among the tied elements.
+// One pass collects the k keys and a bitonic sort in LDS orders them.  No
+// atomic decides anything but the slot an element lands in before the sort,
+// so results are deterministic.
 //
 // The elements of a row (or chunk) are first copied into LDS once; on the way
-// the block forms the AND and the OR of all keys, so the bits every key shares
-// are skipped and the 11-bit digits start at the highest bit that differs.
+// the block forms the AND and the OR of all score keys, so the bits every key
+// shares are skipped and the digits start at the highest bit that differs.
 // Long rows with few queries (decode) run in two stages: workgroups select
 // the top-k of chunks of 16k elements (any global top-k element is in its
 // chunk's top-k), then one workgroup per row selects from their union.
@@ -26,135 +28,181 @@ namespace csa {
 
 static constexpr int TK_THREADS = 1024;
 static constexpr int TK_KMAX = 2048;
-static constexpr int TK_BINS = 2048;
+static constexpr int TK_BINS = 1024;      // 10-bit digits
 static constexpr int TK_LDS_BYTES = 128 * 1024;           // element cache per workgroup
 static constexpr int TK_CACHE32 = TK_LDS_BYTES / 4;       // score rows cached as ord keys
 static constexpr int TK_CACHE64 = TK_LDS_BYTES / 8;       // K64 candidate lists
 
-__device__ __forceinline__ uint64_t make_key(float score, uint32_t idx) {
-  return ((uint64_t)ord_key(score) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
-}
-
-struct RowSrc {        // scores in global memory; index = base + position
-  const float* p;
-  long long base;
-  __device__ __forceinline__ uint64_t get(long long e) const { return make_key(p[e], (uint32_t)(base + e)); }
-};
+// Element sources: hi(e) = ord(score), lo(e) = 0xFFFFFFFF - index.
 struct LdsRowSrc {     // ord keys cached in LDS; index = base + position
   const uint32_t* p;
   long long base;
-  __device__ __forceinline__ uint64_t get(long long e) const {
-    return ((uint64_t)p[e] << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(base + e));
-  }
+  __device__ __forceinline__ uint32_t hi(long long e) const { return p[e]; }
+  __device__ __forceinline__ uint32_t lo(long long e) const { return 0xFFFFFFFFu - (uint32_t)(base + e); }
+};
+struct RowSrc {        // scores in global memory; index = base + position
+  const float* p;
+  long long base;
+  __device__ __forceinline__ uint32_t hi(long long e) const { return ord_key(p[e]); }
+  __device__ __forceinline__ uint32_t lo(long long e) const { return 0xFFFFFFFFu - (uint32_t)(base + e); }
 };
 struct KeySrc {        // explicit K64 candidates, global or LDS (0 = padding, below every real key)
   const uint64_t* p;
-  __device__ __forceinline__ uint64_t get(long long e) const { return p[e]; }
+  __device__ __forceinline__ uint32_t hi(long long e) const { return (uint32_t)(p[e] >> 32); }
+  __device__ __forceinline__ uint32_t lo(long long e) const { return (uint32_t)p[e]; }
 };
 
 struct TopkShared {
-  uint32_t hist[TK_BINS];
+  uint32_t hist[2][TK_BINS];   // double-buffered: one is cleared while the other is read
   uint64_t buf[TK_KMAX];
-  uint64_t red_and[TK_THREADS / 64], red_or[TK_THREADS / 64];
-  int wsum[TK_THREADS / 64];
+  uint32_t red_and[TK_THREADS / 64], red_or[TK_THREADS / 64];
   int digit, cum, cnt_d, count;
 };
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// block-wide AND / OR of 64-bit values (every thread gets both)
-__device__ __forceinline__ void block_and_or(uint64_t& a, uint64_t& o, TopkShared& sh) {
+// block-wide AND / OR of 32-bit values (every thread gets both)
+__device__ __forceinline__ void block_and_or(uint32_t& a, uint32_t& o, TopkShared& sh) {
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) {
-    a &= shfl_xor_u64(a, s);
-    o |= shfl_xor_u64(o, s);
+    a &= (uint32_t)__shfl_xor((int)a, s, 64);
+    o |= (uint32_t)__shfl_xor((int)o, s, 64);
   }
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) { sh.red_and[wid] = a; sh.red_or[wid] = o; }
   __syncthreads();
-  a = ~0ull; o = 0ull;
+  a = ~0u; o = 0u;
   for (int w = 0; w < TK_THREADS / 64; ++w) { a &= sh.red_and[w]; o |= sh.red_or[w]; }
-  __syncthreads();
 }
 
-// exclusive prefix sum over the block (in thread order) of v; returns the sum before this thread
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
+// wave 0 finds the digit where the count from the top reaches `need` in hist
+// (bins in descending order); writes sh.digit / cum / cnt_d
+__device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkShared& sh) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  constexpr int PER = TK_BINS / 64;           // bins per lane, lane 0 holds the top bins
+  const int top = TK_BINS - 1 - PER * lane;
+  int sum = 0;
+#pragma unroll 8
+  for (int q = 0; q < PER; ++q) sum += (int)hist[top - q];
+  int incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
   }
-  if (lane == 63) wsum[wid] = x;
-  __syncthreads();
-  int off = 0;
-  for (int w = 0; w < wid; ++w) off += wsum[w];
-  __syncthreads();
-  return off + x - v;
+  const int above = incl - sum;
+  if (above < need && need <= incl) {
+    int run = above;
+    for (int q = 0; q < PER; ++q) {
+      const int c = (int)hist[top - q];
+      if (need <= run + c) {
+        sh.digit = top - q; sh.cum = run; sh.cnt_d = c;
+        break;
+      }
+      run += c;
+    }
+  }
 }
 
-// k largest K64 of n elements (whose AND / OR are k_and / k_or) -> sh.buf[0 .. min(k, n)),
-// sorted descending when SORT.  Returns min(k, n).
+// Radix select on one 32-bit half of the keys among the elements whose other
+// half / prefix matches.  HALF = 0: hi keys; HALF = 1: lo keys of the elements
+// whose hi key equals hi_val.  Returns the decided bits in *prefix and the
+// count still needed from the final group in *need; *tied reports whether the
+// final group holds more elements than needed (only possible for HALF = 0).
+template <class Src, int HALF>
+__device__ void radix_half(const Src& src, long long n, uint32_t k_and, uint32_t k_or, uint32_t hi_val,
+                           int& need, uint32_t& prefix, bool& tied, TopkShared& sh, int& hb) {
+  const int tid = threadIdx.x;
+  const uint32_t diff = k_and ^ k_or;
+  tied = false;
+  if (diff == 0u) {            // the whole group shares this half
+    prefix = k_and;
+    tied = true;               // every element of the group is equal here
+    return;
+  }
+  int top = 31 - __clz((int)diff);
+  const uint32_t common = (top == 31) ? 0u : ~((2u << top) - 1u);
+  prefix = k_and & common;
+  uint32_t pmask = common;
+  // the buffer cleared for this pass is hist[hb]
+  for (int e = tid; e < TK_BINS; e += TK_THREADS) sh.hist[hb][e] = 0u;
+  __syncthreads();
+  while (true) {
+    const int width = top + 1 < 10 ? top + 1 : 10;
+    const int shift = top + 1 - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* hist = sh.hist[hb];
+    for (long long e = tid; e < n; e += TK_THREADS) {
+      const uint32_t h = src.hi(e);
+      uint32_t key;
+      if (HALF == 0) {
+        key = h;
+      } else {
+        if (h != hi_val) continue;
+        key = src.lo(e);
+      }
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    }
+    // clear the other buffer for the next pass while this one is complete
+    for (int e = tid; e < TK_BINS; e += TK_THREADS) sh.hist[hb ^ 1][e] = 0u;
+    __syncthreads();
+    find_digit(hist, need, sh);
+    __syncthreads();
+    prefix |= (uint32_t)sh.digit << shift;
+    pmask |= dmask << shift;
+    need -= sh.cum;
+    hb ^= 1;
+    if (sh.cnt_d == need) return;
+    if (shift == 0) { tied = true; return; }
+    top = shift - 1;
+  }
+}
+
+// k largest K64 = hi << 32 | lo among n elements -> sh.buf[0 .. min(k, n)), sorted
+// descending when SORT.  hi_and / hi_or: AND / OR of every element's hi key.
 template <class Src, bool SORT>
-__device__ int select_topk(const Src& src, long long n, int k, uint64_t k_and, uint64_t k_or,
+__device__ int select_topk(const Src& src, long long n, int k, uint32_t hi_and, uint32_t hi_or,
                            TopkShared& sh) {
   const int tid = threadIdx.x;
   const int want = (int)min((long long)k, n);
   if (want <= 0) return 0;
-  uint64_t prefix = 0;
+  // threshold: select hi > thr_hi, plus hi == thr_hi with lo >= thr_lo
+  uint32_t thr_hi = 0u, thr_lo = 0u;
+  bool all_eq_hi = false;    // true: every element with hi == thr_hi's prefix group is taken
   if (want < n) {
-    // bits shared by every key are already decided; digits start at the highest differing bit
-    const uint64_t diff = k_and ^ k_or;            // nonzero: keys are unique and n > 1
-    int top = 63 - __clzll((long long)diff);
-    const uint64_t common = (top == 63) ? 0ull : ~((2ull << top) - 1ull);
-    prefix = k_and & common;
-    uint64_t pmask = common;
-    int need = want;
-    while (true) {
-      const int width = top + 1 < 11 ? top + 1 : 11;
-      const int shift = top + 1 - width;
-      const uint64_t dmask = (1ull << width) - 1ull;
-      for (int e = tid; e < TK_BINS; e += TK_THREADS) sh.hist[e] = 0u;
+    int need = want, hb = 0;
+    bool tied;
+    uint32_t pre;
+    radix_half<Src, 0>(src, n, hi_and, hi_or, 0u, need, pre, tied, sh, hb);
+    thr_hi = pre;
+    if (!tied) {
+      all_eq_hi = true;       // take every element whose hi >= pre (pre has zero low bits)
+    } else {
+      // ties on the full hi key: resolve among them by the lo key (the index)
+      uint32_t l_and = ~0u, l_or = 0u;
+      for (long long e = tid; e < n; e += TK_THREADS)
+        if (src.hi(e) == thr_hi) { const uint32_t l = src.lo(e); l_and &= l; l_or |= l; }
+      block_and_or(l_and, l_or, sh);
       __syncthreads();
-      for (long long e = tid; e < n; e += TK_THREADS) {
-        const uint64_t key = src.get(e);
-        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      // bins in descending order; thread t holds bins 2047-2t and 2046-2t
-      const int c0 = (int)sh.hist[TK_BINS - 1 - 2 * tid];
-      const int c1 = (int)sh.hist[TK_BINS - 2 - 2 * tid];
-      const int above = block_excl_scan(c0 + c1, sh.wsum);
-      if (above < need && need <= above + c0 + c1) {
-        if (need <= above + c0) {
-          sh.digit = TK_BINS - 1 - 2 * tid; sh.cum = above; sh.cnt_d = c0;
-        } else {
-          sh.digit = TK_BINS - 2 - 2 * tid; sh.cum = above + c0; sh.cnt_d = c1;
-        }
-      }
-      __syncthreads();
-      prefix |= (uint64_t)sh.digit << shift;
-      pmask |= dmask << shift;
-      need -= sh.cum;
-      const bool done = (sh.cnt_d == need) || shift == 0;
-      __syncthreads();
-      if (done) break;
-      top = shift - 1;
+      uint32_t lpre;
+      bool t2;
+      radix_half<Src, 1>(src, n, l_and, l_or, thr_hi, need, lpre, t2, sh, hb);
+      thr_lo = lpre;
     }
+  } else {
+    all_eq_hi = true;
+    thr_hi = 0u;
   }
-  // collect every key >= threshold (exactly `want` of them)
+  // collect every selected key (exactly `want` of them)
   if (tid == 0) sh.count = 0;
   __syncthreads();
   for (long long e = tid; e < n; e += TK_THREADS) {
-    const uint64_t key = src.get(e);
-    if (key >= prefix) {
+    const uint32_t h = src.hi(e);
+    bool take;
+    if (all_eq_hi) take = h >= thr_hi;
+    else take = h > thr_hi || (h == thr_hi && src.lo(e) >= thr_lo);
+    if (take) {
       const int slot = atomicAdd(&sh.count, 1);
-      if (slot < TK_KMAX) sh.buf[slot] = key;   // exactly `want` <= TK_KMAX keys qualify
+      if (slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h << 32) | src.lo(e);
     }
   }
   __syncthreads();
@@ -183,25 +231,35 @@ __device__ int select_topk(const Src& src, long long n, int k, uint64_t k_and, u
 template <bool SORT>
 __device__ int select_row(const float* __restrict__ p, long long n, long long base, int k,
                           uint32_t* cache, bool use_cache, TopkShared& sh) {
-  uint64_t a = ~0ull, o = 0ull;
+  uint32_t a = ~0u, o = 0u;
   if (use_cache) {
-    for (long long e = threadIdx.x; e < n; e += TK_THREADS) {
+    const long long n4 = (((uintptr_t)p & 15u) == 0) ? (n & ~3LL) : 0;   // vector part if aligned
+    for (long long e = 4LL * threadIdx.x; e < n4; e += 4LL * TK_THREADS) {
+      const f32x4_t v = *(const f32x4_t*)(p + e);
+      u32x4_t ok;
+      ok[0] = ord_key(v[0]); ok[1] = ord_key(v[1]); ok[2] = ord_key(v[2]); ok[3] = ord_key(v[3]);
+      *(u32x4_t*)(cache + e) = ok;
+      a &= ok[0] & ok[1] & ok[2] & ok[3];
+      o |= ok[0] | ok[1] | ok[2] | ok[3];
+    }
+    for (long long e = n4 + threadIdx.x; e < n; e += TK_THREADS) {
       const uint32_t ok = ord_key(p[e]);
       cache[e] = ok;
-      const uint64_t key = ((uint64_t)ok << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(base + e));
-      a &= key;
-      o |= key;
+      a &= ok;
+      o |= ok;
     }
-    block_and_or(a, o, sh);   // its barriers also publish the cache
+    block_and_or(a, o, sh);   // its barrier also publishes the cache
+    __syncthreads();
     return select_topk<LdsRowSrc, SORT>(LdsRowSrc{cache, base}, n, k, a, o, sh);
   }
   const RowSrc src{p, base};
   for (long long e = threadIdx.x; e < n; e += TK_THREADS) {
-    const uint64_t key = src.get(e);
-    a &= key;
-    o |= key;
+    const uint32_t ok = src.hi(e);
+    a &= ok;
+    o |= ok;
   }
   block_and_or(a, o, sh);
+  __syncthreads();
   return select_topk<RowSrc, SORT>(src, n, k, a, o, sh);
 }
 
@@ -214,7 +272,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rows_kernel(
     const float* __restrict__ I, const int* __restrict__ q_pos, long long N_cap, int m, int k,
     int use_cache, int* __restrict__ idx_out, float* __restrict__ val_out) {
   __shared__ TopkShared sh;
-  extern __shared__ uint32_t cache[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t cache[];
   const size_t row = blockIdx.x;
   const long long n = row_nvis(q_pos, row, N_cap, m);
   const float* rp = I + row * (size_t)N_cap;
@@ -236,7 +294,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     const float* __restrict__ I, const int* __restrict__ q_pos, long long N_cap, int m, int k,
     long long chunk, int nchunks, int use_cache, uint64_t* __restrict__ cand) {
   __shared__ TopkShared sh;
-  extern __shared__ uint32_t cache[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t cache[];
   const size_t row = blockIdx.y;
   const int c = blockIdx.x;
   const long long n = row_nvis(q_pos, row, N_cap, m);
@@ -255,30 +313,32 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
     long long N_cap, int m, int k, int nchunks, int use_cache, int* __restrict__ idx_out,
     float* __restrict__ val_out) {
   __shared__ TopkShared sh;
-  extern __shared__ uint64_t cache64[];
+  extern __shared__ __attribute__((aligned(16))) uint64_t cache64[];
   const size_t row = blockIdx.x;
   const long long n = row_nvis(q_pos, row, N_cap, m);
   const int want = (int)min((long long)k, n);
   const long long ncand = (long long)nchunks * k;
   const uint64_t* cp = cand + row * (size_t)ncand;
   // padding keys (0) rank below every real key and `want` never exceeds the real ones
-  uint64_t a = ~0ull, o = 0ull;
+  uint32_t a = ~0u, o = 0u;
   int got;
   if (use_cache) {
     for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
       const uint64_t key = cp[e];
       cache64[e] = key;
-      a &= key;
-      o |= key;
+      a &= (uint32_t)(key >> 32);
+      o |= (uint32_t)(key >> 32);
     }
     block_and_or(a, o, sh);
+    __syncthreads();
     got = select_topk<KeySrc, true>(KeySrc{cache64}, ncand, want, a, o, sh);
   } else {
     for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
-      a &= cp[e];
-      o |= cp[e];
+      a &= (uint32_t)(cp[e] >> 32);
+      o |= (uint32_t)(cp[e] >> 32);
     }
     block_and_or(a, o, sh);
+    __syncthreads();
     got = select_topk<KeySrc, true>(KeySrc{cp}, ncand, want, a, o, sh);
   }
   const float* rp = I + row * (size_t)N_cap;

@@ -177,6 +177,8 @@ TOPK_CASES = [
     ("two_stage_ties", 2, 1, 40000, 1, 1024, "ties", "all"),
     ("two_stage_k512_flash_like", 2, 1, 16384, 4, 512, "normal", "all"),
     ("prefill_rows", 1, 600, 2000, 4, 1024, "normal", "prefill"),
+    ("decode_1M_full_shape", 16, 1, 262144, 4, 1024, "normal", "all"),
+    ("prefill_full_row_length", 1, 40, 32768, 4, 1024, "normal", "prefill"),
 ]
 
 
