@@ -60,34 +60,16 @@ def traffic_from_profiles(kernel_tag: str, src_file: str):
 
 def cpu_baseline(run, n_seq: int):
     """The fp64 oracle on n_seq sequences of the same workload (host cores)."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import steps
-    from tests._util import to_f64
+    from tests._pipeline_ref import csa_decode_params
 
     wl = run.wl
     n_seq = max(1, min(n_seq, wl.B))
-    # decode the stored inputs of the sampled sequences first (not timed)
-    inputs = []
-    for b in range(n_seq):
-        KI = to_f64(run.KI[b])
-        if run.KI_scale is not None:
-            KI = KI * to_f64(run.KI_scale[b])[:, None]
-        p = dict(i=run.i, m=wl.m, N=wl.N_cap, k=wl.k, n_win=wl.n_win, d_I=wl.d_I, rope_dim=wl.rope_dim,
-                 rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.dtype, k_dtype=wl.k_dtype,
-                 KI=KI, win_raw=to_f64(run.win_raw[b]),
-                 Ca=to_f64(run.Ca[b]), Za=to_f64(run.Za[b]), Cb=to_f64(run.Cb[b]), Zb=to_f64(run.Zb[b]),
-                 ICa=to_f64(run.ICa[b]), IZa=to_f64(run.IZa[b]), ICb=to_f64(run.ICb[b]),
-                 IZb=to_f64(run.IZb[b]), qI=to_f64(run.qI[b, 0]), w=to_f64(run.wI[b, 0]),
-                 q=to_f64(run.q[b, 0]), sink=to_f64(run.sink))
-        raw_b = run.kv_raw[b]
-        inputs.append((p, raw_b))
+    inputs = [csa_decode_params(run, b) for b in range(n_seq)]   # decoding the bytes is not timed
     t0 = time.perf_counter()
-    for p, raw_b in inputs:
-        def rows(s, raw_b=raw_b):
-            import torch
-            return to_f64(raw_b[torch.as_tensor(s, device=raw_b.device)])
+    for p, rows in inputs:
         steps.csa_decode_sequence(p, rows)
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])

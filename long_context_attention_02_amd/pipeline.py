@@ -224,6 +224,7 @@ class CSAPrefill(_Common):
         self._fill_entries(self.E, kv_raw, m, True, True)
         self.kv_raw = kv_raw if keep_raw else None
         self.KI = g.normal(W_.T_KI, (B, N, wl.d_I), wl.k_dtype)
+        self.KI_init = self.KI.clone() if keep_raw else None   # the cache before the step
         # window ring: the 127 tokens before the chunk from set-up, the chunk's own rows per step
         self._window_setup(g, wl, p0 - (wl.n_win - 1), wl.n_win - 1, W_.T_WINRAW)
         self.chunk_raw = g.normal(W_.T_WINRAW + 100, (B, Tq, d), wl.dtype)

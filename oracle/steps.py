@@ -81,7 +81,7 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
     out = O.attend_one(p["q"], np.concatenate([rows, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
                        rope_base=base, scale=p["scale"])
-    return {"I": I[0], "idx": idx[0], "vals": vals[0], "out": out}
+    return {"I": I[0], "idx": idx[0], "vals": vals[0], "out": out, "k_new": k_new[0]}
 
 
 def hca_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
@@ -104,3 +104,57 @@ def hca_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     out = O.attend_one(p["q"], np.concatenate([E, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
                        rope_base=base, scale=p["scale"])
     return {"out": out}
+
+
+def csa_prefill_queries(p: dict, ts, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
+    """Chunked CSA prefill, evaluated for the chunk queries ``ts`` only.
+
+    The chunk holds queries at positions p0 .. p0 + Tq - 1.  Entries s0 = p0/m ..
+    s1 = min(N, (p0 + Tq)/m) complete inside the chunk and are compressed from
+    the chunk's candidates (KV entries with norm + RoPE, indexer keys without);
+    earlier entries come from the cache.  Each query then scores every visible
+    entry, takes its top-k and attends over those entries, its window and the sink.
+
+    p holds: p0, Tq, m, N, k, n_win, rope_dim, rope_base, eps, scale, dtype, k_dtype;
+    KI (N x d_I stored key values), tok_base, Ca/Za/Cb/Zb (rows of tokens
+    tok_base ..), ICa/IZa/ICb/IZb, win_before (raw window rows of tokens
+    p0 - n_win + 1 .. p0 - 1), chunk_raw (raw rows of tokens p0 .. p0 + Tq - 1),
+    qI [len(ts), H, d_I], w [len(ts), H], q [len(ts), n_h, d], sink.
+    kv_raw_rows(s) returns the pre-norm rows of cached entries s.
+    """
+    p0, Tq, m, N, k, n_win = p["p0"], p["Tq"], p["m"], p["N"], p["k"], p["n_win"]
+    r, base, eps = p["rope_dim"], p["rope_base"], p["eps"]
+    T = p0 + Tq
+    s0, s1 = p0 // m, min(N, T // m)
+    E_new = _store(O.compress(p["Ca"], p["Za"], p["Cb"], p["Zb"], m=m, overlap=1, T=T,
+                              tok_base=p["tok_base"], s_begin=s0, s_end=s1, eps=eps,
+                              rope_dim=r, rope_base=base), p["dtype"])
+    K_new = _store(O.compress(p["ICa"], p["IZa"], p["ICb"], p["IZb"], m=m, overlap=1, T=T,
+                              tok_base=p["tok_base"], s_begin=s0, s_end=s1, normalize=False),
+                   p["k_dtype"])
+    KI = p["KI"].copy()
+    KI[s0:s1] = K_new
+    tok_lo = p0 - (n_win - 1)
+    W = window_rows(np.concatenate([p["win_before"], p["chunk_raw"]]), np.arange(tok_lo, T),
+                    rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
+    res = {"I": [], "idx": [], "out": []}
+    for j, t in enumerate(ts):
+        i = p0 + int(t)
+        I = O.index_score(p["qI"][j][None], p["w"][j][None], KI, [i], m=m)
+        idx, _ = O.topk(I, [i], m=m, k=k)
+        sel = idx[0][idx[0] >= 0]
+        rows = np.zeros((len(sel), p["q"].shape[-1]))
+        old = sel < s0
+        if old.any():
+            rows[old] = entry_rows(kv_raw_rows(sel[old]), sel[old], m=m, rope_dim=r, rope_base=base,
+                                   eps=eps, dtype=p["dtype"])
+        rows[~old] = E_new[sel[~old] - s0]
+        toks = np.arange(i - n_win + 1, i + 1)
+        out = O.attend_one(p["q"][j], np.concatenate([rows, W[toks - tok_lo]]), i=i, eps=eps,
+                           sink=p["sink"], rope_dim=r, rope_base=base, scale=p["scale"])
+        res["I"].append(I[0])
+        res["idx"].append(idx[0])
+        res["out"].append(out)
+    res = {key: np.stack(v) for key, v in res.items()}
+    res.update(E_new=E_new, KI_new=K_new, s0=s0)
+    return res

@@ -531,3 +531,49 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir):
         mp.setattr(O, "attend_one", attend_sink_as_key)
         with pytest.raises(AssertionError):
             test_sink_closed_forms(golden_dir)
+
+
+def test_chunked_prefill_equals_whole_sequence():
+    """Chunked-prefill equivalence: the composition that takes cached entries
+    for the blocks before the chunk and compresses the rest must give, for every
+    chunk query, what the whole-sequence chain (compress all tokens, score,
+    select, attend) gives.  Pins the composition's offsets (s0, tok_base,
+    window rows) against the plain chain."""
+    from oracle import steps
+    rng = np.random.default_rng(7)
+    T, m, c, dI, H, n_h, k, n_win, r = 96, 4, 16, 8, 2, 3, 5, 6, 4
+    p0 = 48
+    C = {n: rng.standard_normal((T, c)) for n in ("Ca", "Za", "Cb", "Zb")}
+    IC = {n: rng.standard_normal((T, dI)) for n in ("ICa", "IZa", "ICb", "IZb")}
+    win_raw = rng.standard_normal((T, c))
+    qI = rng.standard_normal((T, H, dI))
+    w = rng.uniform(size=(T, H))
+    q = rng.standard_normal((T, n_h, c))
+    sink = rng.standard_normal(n_h)
+    N = T // m
+    eps, scale, base = 1e-6, 1 / np.sqrt(c), 10000.0
+    # whole sequence
+    E = O.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, eps=eps, rope_dim=r)
+    K = O.compress(IC["ICa"], IC["IZa"], IC["ICb"], IC["IZb"], m=m, overlap=1, T=T, normalize=False)
+    W = O.compress(win_raw, None, None, None, m=1, overlap=0, T=T, eps=eps, rope_dim=r, pos_stride=1)
+    pos = np.arange(p0, T)
+    I = O.index_score(qI[p0:], w[p0:], K, pos, m=m)
+    idx, _ = O.topk(I, pos, m=m, k=k)
+    out = O.sparse_mqa(q[p0:], E, idx, W, q_pos=pos, n_win=n_win, eps=eps, sink=sink, rope_dim=r,
+                       rope_base=base, scale=scale)
+    # chunked: entries before the chunk from the cache (pre-norm pooled rows), the rest compressed
+    s0 = p0 // m
+    pre = O.pool_entries(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, s_begin=0, s_end=s0)
+    KI = np.zeros((N, dI))
+    KI[:s0] = K[:s0]
+    tb = m * (s0 - 1)
+    p = dict(p0=p0, Tq=T - p0, m=m, N=N, k=k, n_win=n_win, rope_dim=r, rope_base=base, eps=eps,
+             scale=scale, dtype="f32", k_dtype="f32", KI=KI, tok_base=tb,
+             **{n: v[tb:] for n, v in C.items()}, **{n: v[tb:] for n, v in IC.items()},
+             win_before=win_raw[p0 - n_win + 1:p0], chunk_raw=win_raw[p0:],
+             qI=qI[p0:], w=w[p0:], q=q[p0:], sink=sink)
+    ts = np.arange(T - p0)
+    got = steps.csa_prefill_queries(p, ts, lambda s: pre[np.asarray(s)])
+    np.testing.assert_allclose(got["I"], I, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(got["idx"], idx)
+    np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)

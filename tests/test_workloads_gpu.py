@@ -1,0 +1,244 @@
+"""Whole-step parity on the GPU at the workloads' full sizes, in the launch
+configuration the benchmark times (the device-resident steps of
+``long_context_attention_02_amd.pipeline``), against the fp64 oracle.
+
+Each side scores the entries itself, so the selections may differ only where
+the oracle's scores lie within the fp32 rounding band of the k-th score
+(``check_selection``); the attention outputs are compared on every query whose
+selection matches the oracle's exactly.  Also: the tiny fp32 workload end to
+end (every query of a 256-token causal prefill), bitwise run-to-run
+determinism and batch invariance.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa as O
+from oracle import steps
+from tests._pipeline_ref import (check_selection, csa_decode_params, csa_prefill_params,
+                                 hca_decode_params, new_key_slack, score_slack)
+from tests._util import TOL_BF16, TOL_F32, row_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import long_context_attention_02_amd as csa
+    return csa
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _check_decode_rows(got_I, got_idx, got_out, refs, tol_out, slacks=None):
+    """Compare per-query results of a CSA step; returns (swaps, compared).
+
+    Scores: |got - ref| <= TOL_F32 * max|ref| + slack per entry (slack is 0
+    except for keys the step itself compressed into bf16, see score_slack)."""
+    swaps, compared = 0, 0
+    for b, ref in enumerate(refs):
+        fin = np.isfinite(ref["I"])
+        assert np.array_equal(np.isfinite(got_I[b]), fin), ("mask", b)
+        sl = np.zeros(len(fin)) if slacks is None else slacks[b]
+        g, r = np.where(fin, got_I[b], 0.0), np.where(fin, ref["I"], 0.0)
+        excess = np.abs(g - r) - sl - TOL_F32 * np.max(np.abs(r))
+        assert np.all(excess <= 0), ("index score", b, int(np.argmax(excess)), float(np.max(excess)))
+        n = check_selection(got_idx[b], ref["idx"], ref["I"], sl)
+        swaps += n
+        if n == 0:
+            err = row_rel_err(got_out[b], ref["out"])
+            assert err <= tol_out, ("attention output", b, err)
+            compared += 1
+    return swaps, compared
+
+
+# ---------------------------------------------------------------------------
+# tiny fp32 workload: T = 256, every query, each stage against the oracle
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_end_to_end(lib):
+    from synth import Gen
+    from synth import workloads as W_
+    wl = W_.TINY
+    g = Gen(wl.wid, "cuda")
+    T, c, dI, m, r = wl.ctx, wl.d, wl.d_I, wl.m, wl.rope_dim
+    Ca, Za, Cb, Zb = (g.normal(t, (1, T, c), "f32") for t in (W_.T_CA, W_.T_ZA, W_.T_CB, W_.T_ZB))
+    ICa, IZa, ICb, IZb = (g.normal(t, (1, T, dI), "f32") for t in (W_.T_ICA, W_.T_IZA, W_.T_ICB, W_.T_IZB))
+    win_raw = g.normal(W_.T_WINRAW, (1, T, c), "f32")
+    qI = g.normal(W_.T_QI, (1, T, wl.H_I, dI), "f32")
+    wI = g.uniform(W_.T_WI, (1, T, wl.H_I))
+    q = g.normal(W_.T_Q, (1, T, wl.n_h, c), "f32")
+    sink = torch.zeros(wl.n_h, dtype=torch.float32, device="cuda")
+    gamma = torch.ones(c, dtype=torch.float32, device="cuda")
+    pos = torch.arange(T, dtype=torch.int32, device="cuda").view(1, T).contiguous()
+    N = wl.N_cap
+    E = torch.empty((1, N, c), dtype=torch.float32, device="cuda")
+    K = torch.empty((1, N, dI), dtype=torch.float32, device="cuda")
+    W = torch.empty((1, wl.W_cap, c), dtype=torch.float32, device="cuda")
+    I = torch.empty((1, T, N), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, T, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lib.csa_compress(Ca, Za, Cb, Zb, E, T=T, m=m, overlap=1, s_begin=0, s_end=N, gamma=gamma,
+                     eps=wl.eps, rope_dim=r, rope_base=wl.rope_base)
+    lib.csa_compress(ICa, IZa, ICb, IZb, K, T=T, m=m, overlap=1, s_begin=0, s_end=N)
+    lib.csa_compress(win_raw, None, None, None, W, T=T, m=1, overlap=0, s_begin=0, s_end=T,
+                     gamma=gamma, eps=wl.eps, rope_dim=r, rope_base=wl.rope_base, pos_stride=1,
+                     out_ring=wl.W_cap)
+    lib.csa_index_score(qI, wI, K, pos, I, m=m)
+    ws = torch.empty(max(lib.csa_topk_workspace_size(1, T, N, wl.k), 1), dtype=torch.uint8, device="cuda")
+    lib.csa_topk(I, pos, idx, m=m, k=wl.k, workspace=ws)
+    mws = torch.empty(max(lib.csa_mqa_workspace_size(1, T, wl.n_h, c, wl.k + wl.n_win), 1),
+                      dtype=torch.uint8, device="cuda")
+    lib.csa_sparse_mqa(q, E, idx, W, pos, out, n_win=wl.n_win, sink=sink, gamma_q=gamma, eps=wl.eps,
+                       rope_dim=r, rope_base=wl.rope_base, scale=wl.scale, workspace=mws)
+    torch.cuda.synchronize()
+
+    f = lambda t: to_f64(t[0])
+    rE = O.compress(f(Ca), f(Za), f(Cb), f(Zb), m=m, overlap=1, T=T, eps=wl.eps, rope_dim=r,
+                    rope_base=wl.rope_base)
+    rK = O.compress(f(ICa), f(IZa), f(ICb), f(IZb), m=m, overlap=1, T=T, normalize=False)
+    rW = O.compress(f(win_raw), None, None, None, m=1, overlap=0, T=T, eps=wl.eps, rope_dim=r,
+                    rope_base=wl.rope_base, pos_stride=1)
+    assert row_rel_err(f(E), rE) <= TOL_F32
+    assert row_rel_err(f(K), rK) <= TOL_F32
+    assert row_rel_err(f(W), rW) <= TOL_F32
+    rng = np.arange(T)
+    rI = O.index_score(f(qI), f(wI), rK, rng, m=m)
+    ridx, _ = O.topk(rI, rng, m=m, k=wl.k)
+    rout = O.sparse_mqa(f(q), rE, ridx, rW, q_pos=rng, n_win=wl.n_win, eps=wl.eps, sink=np.zeros(wl.n_h),
+                        rope_dim=r, rope_base=wl.rope_base, scale=wl.scale)
+    got_I, got_idx, got_out = f(I), idx[0].cpu().numpy(), f(out)
+    refs = [{"I": rI[t], "idx": ridx[t], "out": rout[t]} for t in range(T)]
+    swaps, compared = _check_decode_rows(got_I, got_idx, got_out, refs, TOL_F32)
+    assert compared >= 0.9 * T, (swaps, compared)
+
+
+# ---------------------------------------------------------------------------
+# decode workloads at full size
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["csa_decode_flash_b8_ctx65536", "csa_decode_pro_b16_ctx1M_fp8keys"])
+def test_csa_decode_full_size(lib, name):
+    from long_context_attention_02_amd.pipeline import CSADecode
+    from synth.workloads import WORKLOADS
+    wl = WORKLOADS[name]
+    run = CSADecode(wl, "cuda", keep_raw=True)
+    torch.cuda.synchronize()
+    params = [csa_decode_params(run, b) for b in range(wl.B)]   # stored inputs, before the step
+    run.step()
+    torch.cuda.synchronize()
+    got_I, got_idx, got_out = to_f64(run.I[:, 0]), run.idx[:, 0].cpu().numpy(), to_f64(run.out[:, 0])
+    refs = [steps.csa_decode_sequence(p, rows) for p, rows in params]
+    slacks = np.zeros((wl.B, wl.N_cap))
+    for b, (p, _) in enumerate(params):   # the newest key is stored by the step itself
+        slacks[b, wl.N_cap - 1] = new_key_slack(p["qI"], p["w"], refs[b]["k_new"], wl.k_dtype)
+    swaps, compared = _check_decode_rows(got_I, got_idx, got_out, refs, TOL_BF16, slacks)
+    print(f"{name}: {compared}/{wl.B} outputs compared, {swaps} boundary swaps")
+    assert compared >= wl.B // 2
+    del run
+    _free()
+
+
+def test_hca_decode_full_size(lib):
+    from long_context_attention_02_amd.pipeline import HCADecode
+    from synth.workloads import HCA_DECODE as wl
+    run = HCADecode(wl, "cuda", keep_raw=True)
+    torch.cuda.synchronize()
+    params = [hca_decode_params(run, b) for b in range(wl.B)]
+    run.step()
+    torch.cuda.synchronize()
+    got = to_f64(run.out[:, 0])
+    for b, (p, rows) in enumerate(params):
+        ref = steps.hca_decode_sequence(p, rows)["out"]
+        err = row_rel_err(got[b], ref)
+        assert err <= TOL_BF16, (b, err)
+    del run
+    _free()
+
+
+def test_csa_prefill_full_size_sampled_rows(lib):
+    """The 16,384-query chunk at 131,072 context: one full step on the GPU,
+    64 strided query rows (first and last included) checked against the oracle."""
+    from long_context_attention_02_amd.pipeline import CSAPrefill
+    from synth.workloads import CSA_PREFILL_PRO as wl
+    run = CSAPrefill(wl, "cuda", keep_raw=True)
+    run.step()
+    torch.cuda.synchronize()
+    ts = np.unique(np.r_[np.linspace(0, wl.Tq - 1, 60).astype(np.int64), [1, 2, 3, wl.Tq - 2]])
+    ts_t = torch.as_tensor(ts, device="cuda")
+    got_I = to_f64(run.I[0, ts_t])
+    got_idx = run.idx[0, ts_t].cpu().numpy()
+    got_out = to_f64(run.out[0, ts_t])
+    p, rows = csa_prefill_params(run, ts)
+    ref = steps.csa_prefill_queries(p, ts, rows)
+    # the entries and indexer keys this step compressed (bf16 outputs)
+    s0, s1 = ref["s0"], ref["s0"] + len(ref["KI_new"])
+    assert row_rel_err(to_f64(run.E[0, s0:s1]), ref["E_new"]) <= TOL_BF16
+    assert row_rel_err(to_f64(run.KI[0, s0:s1]), ref["KI_new"]) <= TOL_BF16
+    slacks = np.zeros((len(ts), wl.N_cap))
+    for j in range(len(ts)):
+        slacks[j, s0:s1] = score_slack(p["qI"][j], p["w"][j], ref["KI_new"])
+    refs = [{"I": ref["I"][j], "idx": ref["idx"][j], "out": ref["out"][j]} for j in range(len(ts))]
+    swaps, compared = _check_decode_rows(got_I, got_idx, got_out, refs, TOL_BF16, slacks)
+    print(f"prefill: {compared}/{len(ts)} outputs compared, {swaps} boundary swaps")
+    assert compared >= len(ts) // 2
+    del run
+    _free()
+
+
+# ---------------------------------------------------------------------------
+# determinism and batch invariance
+# ---------------------------------------------------------------------------
+def test_decode_bitwise_repeatable_and_batch_invariant(lib):
+    """Two runs of the step give identical bytes, and one sequence run alone
+    gives the same bytes as inside the batch (no split depends on B)."""
+    from long_context_attention_02_amd.pipeline import CSADecode, HCADecode
+    from synth.workloads import CSA_DECODE_FLASH, HCA_DECODE
+    run = CSADecode(CSA_DECODE_FLASH, "cuda", keep_raw=False)
+    run.step()
+    first = [t.clone() for t in (run.I, run.idx, run.out)]
+    run.step()
+    for a, b in zip(first, (run.I, run.idx, run.out)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+    wl, b = run.wl, 5
+    sl = slice(b, b + 1)
+    I1 = torch.empty_like(run.I[sl])
+    idx1 = torch.empty_like(run.idx[sl])
+    out1 = torch.empty_like(run.out[sl])
+    lib.csa_index_score(run.qI[sl], run.wI[sl], run.KI[sl], run.q_pos[sl], I1, m=wl.m)
+    ws = torch.empty(max(lib.csa_topk_workspace_size(1, 1, wl.N_cap, wl.k), 1), dtype=torch.uint8,
+                     device="cuda")
+    lib.csa_topk(I1, run.q_pos[sl], idx1, m=wl.m, k=wl.k, workspace=ws)
+    mws = torch.empty(max(lib.csa_mqa_workspace_size(1, 1, wl.n_h, wl.d, wl.k + wl.n_win), 1),
+                      dtype=torch.uint8, device="cuda")
+    lib.csa_sparse_mqa(run.q[sl], run.E[sl], idx1, run.W[sl], run.q_pos[sl], out1, n_win=wl.n_win,
+                       sink=run.sink, gamma_q=run.gamma_q, eps=wl.eps, rope_dim=wl.rope_dim,
+                       rope_base=wl.rope_base, scale=wl.scale, workspace=mws)
+    torch.cuda.synchronize()
+    assert torch.equal(I1, run.I[sl])
+    assert torch.equal(idx1, run.idx[sl])
+    assert torch.equal(out1.view(torch.uint8), run.out[sl].view(torch.uint8))
+    del run
+    _free()
+
+    run = HCADecode(HCA_DECODE, "cuda", keep_raw=False)
+    run.step()
+    o_first = run.out.clone()
+    run.step()
+    assert torch.equal(o_first.view(torch.uint8), run.out.view(torch.uint8))
+    wl, b = run.wl, 2
+    sl = slice(b, b + 1)
+    out1 = torch.empty_like(run.out[sl])
+    mws = torch.empty(max(lib.csa_mqa_workspace_size(1, 1, wl.n_h, wl.d, wl.N_cap + wl.n_win), 1),
+                      dtype=torch.uint8, device="cuda")
+    lib.hca_dense_mqa(run.q[sl], run.E[sl], run.W[sl], run.q_pos[sl], out1, m=wl.m, n_win=wl.n_win,
+                      sink=run.sink, gamma_q=run.gamma_q, eps=wl.eps, rope_dim=wl.rope_dim,
+                      rope_base=wl.rope_base, scale=wl.scale, workspace=mws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.uint8), run.out[sl].view(torch.uint8))
+    del run
+    _free()
