@@ -20,7 +20,7 @@
 //   way on both operands);
 //   V is read transposed from row-major LDS with ds_read_b64_tr_b16;
 //   an online softmax (running max / sum per head) rescales O per 32 keys.
-// Decode queries split their slots across workgroups (fixed 256-slot ranges,
+// Decode queries split their slots across workgroups (fixed 128-slot ranges,
 // independent of the batch) and a combine kernel merges the partial
 // (max, sum, O) in a fixed order.
 #include "csa_device.h"
