@@ -692,6 +692,455 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode kernel (few queries per sequence, heads a multiple of 32).
+//
+// A workgroup takes one query, a group of 32 NW heads and a fixed range of at
+// most MQ_DEC_SPLIT key slots.  Wave w owns 32 heads of the group (two 16-head
+// tiles) over all D dims, so scores, softmax and P.V stay inside the wave and
+// need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
+// MQ_DEC_NBUF chunks filled with global_load_lds, MQ_DEC_NBUF - 1 chunks ahead,
+// so each row is fetched from memory once per workgroup and then read from LDS
+// by every wave.  Rows sit at a stride of 2D + 16 bytes: 16 lanes reading one
+// 16-byte piece of 16 consecutive rows (the S^T operand) hit distinct banks,
+// and the transposed reads of V take constant offsets along a row.  Row
+// addresses come straight from the selection (wave-uniform loads), so the first
+// chunks are in flight before the query is even normalised.  The split depends
+// only on the slot count; a combine kernel merges split partials in order.
+// ---------------------------------------------------------------------------
+static constexpr int MQ_DEC_SPLIT = 288;   // key slots per workgroup
+static constexpr int MQ_DEC_NBUF = 3;      // LDS chunk ring
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete
+// (lgkmcnt 0) and its vector-memory operations drop to at most VM outstanding
+// (gfx9 s_waitcnt encoding; 63 = no wait), then s_barrier.  __syncthreads()
+// would also drain every global_load_lds still in flight (vmcnt 0), which
+// defeats the chunk prefetch.  The empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+template <int VM>
+__device__ __forceinline__ void lds_sync() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Sixteen transposed 64-bit LDS reads (ds_read_b64_tr_b16): eight 16-dim tiles
+// at byte offsets 0, 32, ..., 224 from a0 (rows 4g..4g+3 of the chunk) and a1
+// (rows 16+4g..), completed inside the statement.  The builtin form makes the
+// compiler wait for every global_load_lds in flight (vmcnt 0) before the read,
+// because it cannot tell the addresses apart from the prefetched chunks.
+__device__ __forceinline__ void lds_read_tr16(uint32_t a0, uint32_t a1, u32x2_t (&r)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:96\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:128\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:160\n\t"
+      "ds_read_b64_tr_b16 %11, %17 offset:160\n\t"
+      "ds_read_b64_tr_b16 %12, %16 offset:192\n\t"
+      "ds_read_b64_tr_b16 %13, %17 offset:192\n\t"
+      "ds_read_b64_tr_b16 %14, %16 offset:224\n\t"
+      "ds_read_b64_tr_b16 %15, %17 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+// where the rows of one workgroup's slot range come from (all wave-uniform)
+struct DecRows {
+  const int* idx_sp;          // selection of the range's first slot (sparse)
+  const uint16_t* E_b;        // this sequence's entries
+  const uint16_t* W_b;        // this sequence's window ring
+  const uint16_t* dummy;      // a valid row, loaded for absent slots (their scores are masked)
+  long long s0;               // first slot of the range
+  int n_rows;                 // slots in the range
+  int n_sel;                  // of them, entry slots (the rest are window slots)
+  int ring0;                  // ring row of the range's first window slot
+  int W_cap;
+  int N_cap;                  // entries per sequence, clamped to int
+};
+
+// start loading chunk c (rows RPW w .. RPW w + RPW - 1 of it are this wave's) and
+// record which of those rows exist, one byte per 8 rows, in mbytes
+template <int D, bool DENSE, int NW>
+__device__ __forceinline__ void dec_issue(int c, const DecRows& R, uint8_t* buf, uint8_t* mbytes,
+                                          int wave, int lane) {
+  constexpr int RBP = 2 * D + 16, CPR = 2 * D / 16, RPW = MQ_CH / NW;
+  const int rel0 = MQ_CH * c + RPW * wave;
+  // the wave's selected entries, read together (clamped to the range's entry slots)
+  int ev[RPW];
+  if (!DENSE && R.n_sel > 0) {
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) ev[rr] = R.idx_sp[min(rel0 + rr, R.n_sel - 1)];
+  }
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const int rel = rel0 + rr;
+    const uint16_t* p = R.dummy;
+    bool ok = false;
+    if (rel < R.n_rows) {
+      if (rel < R.n_sel) {
+        if (DENSE) {
+          p = R.E_b + (size_t)(R.s0 + rel) * D;
+          ok = true;
+        } else {
+          const int e = ev[rr];
+          if (e >= 0 && e < R.N_cap) {
+            p = R.E_b + (size_t)e * D;
+            ok = true;
+          }
+        }
+      } else {
+        int ring = R.ring0 + (rel - R.n_sel);   // fewer window slots than ring rows: one wrap at most
+        if (ring >= R.W_cap) ring -= R.W_cap;
+        p = R.W_b + (size_t)ring * D;
+        ok = true;
+      }
+    }
+    bits |= (ok ? 1u : 0u) << rr;
+    if (lane < CPR)
+      __builtin_amdgcn_global_load_lds((const void*)(p + 8 * lane),
+                                       (__attribute__((address_space(3))) void*)(buf + (RPW * wave + rr) * RBP),
+                                       16, 0, 0);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int q8 = 0; q8 < RPW / 8; ++q8) mbytes[(RPW / 8) * wave + q8] = (uint8_t)(bits >> (8 * q8));
+  }
+}
+
+// head tiles (16 heads each) per wave: two while the output accumulators of
+// 32 heads fit the register file next to the query fragments, one at D = 512
+template <int D>
+__host__ __device__ constexpr int dec_htw() { return D >= 512 ? 1 : 2; }
+
+template <int D, bool DENSE, int NW>
+__global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
+    const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
+    const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
+  constexpr int HTW = dec_htw<D>();   // head tiles per wave
+  constexpr int KS = D / 32;          // S^T K-steps (8 dims per lane each)
+  constexpr int NT = D / 16;          // 16-dim output tiles
+  constexpr int RBP = 2 * D + 16;     // LDS row stride
+  constexpr int RPW = MQ_CH / NW;     // rows each wave loads per chunk
+  constexpr int CHB = MQ_CH * RBP;    // bytes per chunk
+  constexpr int HG = 16 * HTW * NW;   // heads per workgroup
+  constexpr int PF = MQ_DEC_NBUF - 1;
+  constexpr int GPT = (D + 64 * NW - 1) / (64 * NW);   // gamma values per thread
+  static_assert((PF - 1) * RPW <= 63, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_DEC_NBUF * CHB
+  __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
+  __shared__ float gam[D];
+  __shared__ uint32_t cmask[MQ_DEC_NBUF];   // bit r: row r of the chunk exists
+  __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
+
+  const int n_hg = n_h / HG;
+  const long long L = blockIdx.x;
+  const int hg = (int)((L / 8) % n_hg);
+  const long long unit = (L / (8LL * n_hg)) * 8 + (L % 8);
+  if (unit >= n_units) return;
+  const int sp = (int)(unit % n_split);
+  const size_t row = (size_t)(unit / n_split);
+  const int b = (int)(row / Tq);
+  const long long i = q_pos[row];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int h0 = HG * hg + 16 * HTW * wave;   // first head of this wave
+
+  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
+  DecRows R;
+  R.s0 = (long long)sp * MQ_DEC_SPLIT;
+  R.n_rows = (int)max(0LL, min((long long)MQ_DEC_SPLIT, qs.n_slots - R.s0));
+  R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
+  R.idx_sp = DENSE ? nullptr : idx + row * (size_t)k + R.s0;
+  R.E_b = E + (size_t)b * (size_t)N_cap * D;
+  R.W_b = W ? W + (size_t)b * (size_t)W_cap * D : nullptr;
+  R.dummy = R.E_b;
+  R.W_cap = W_cap;
+  R.N_cap = (int)min(N_cap, 2147483647LL);
+  R.ring0 = W_cap > 0 ? (int)((qs.win_lo + max(0LL, R.s0 - qs.n_sel)) % W_cap) : 0;
+  const int nch = (R.n_rows + MQ_CH - 1) / MQ_CH;
+
+  // query pieces and gamma first: waiting on them later must not wait on the chunks
+  u32x4_t raw[HTW][KS];
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht) {
+    const uint16_t* qp = q + (row * n_h + h0 + 16 * ht + j) * (size_t)D + (D / 4) * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) raw[ht][ks] = *(const u32x4_t*)(qp + 8 * ks);
+  }
+  float gv[GPT];
+#pragma unroll
+  for (int e = 0; e < GPT; ++e) {
+    const int t = threadIdx.x + 64 * NW * e;
+    gv[e] = (t < D && gamma_q) ? gamma_q[t] : 1.f;
+  }
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+    if (c < nch) dec_issue<D, DENSE, NW>(c, R, kv + c * CHB, (uint8_t*)&cmask[c], wave, lane);
+  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
+    const int u = t - (D - rope_dim) / 2;
+    float cs = 1.f, sn = 0.f;
+    if (u >= 0) rope_cos_sin(i, u, rope_dim, rope_base, &cs, &sn);
+    rope_cs[2 * t] = cs;
+    rope_cs[2 * t + 1] = sn;
+  }
+#pragma unroll
+  for (int e = 0; e < GPT; ++e) {
+    const int t = threadIdx.x + 64 * NW * e;
+    if (t < D) gam[t] = gv[e];
+  }
+  float rinv[HTW];
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht) {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(raw[ht][ks][e] << 16);
+        const float x1 = __uint_as_float(raw[ht][ks][e] & 0xffff0000u);
+        ss += x0 * x0 + x1 * x1;
+      }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    rinv[ht] = 1.f / sqrtf(ss / (float)D + eps);
+    // opaque to the compiler: the fp32 values unpacked for the sum are not kept
+    // alive (twice the registers of the packed pieces) for the conversion below
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(raw[ht][ks]));
+  }
+  lds_sync<63>();   // RoPE table and gamma visible; the chunks stay in flight
+
+  // q^ = RoPE_i(RMSNorm(q)) as bf16 B fragments of S^T: lane (g, j) holds head 16 ht + j,
+  // dims (D/4) g + 8 ks + 0..7; the RoPE table holds (1, 0) for dims that are not rotated
+  bf16x8_t qf[HTW][KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int d0 = (D / 4) * g + 8 * ks;
+    const f32x4_t ga = *(const f32x4_t*)&gam[d0], gb = *(const f32x4_t*)&gam[d0 + 4];
+    const f32x4_t ra = *(const f32x4_t*)&rope_cs[d0], rb = *(const f32x4_t*)&rope_cs[d0 + 4];
+    const float gw[8] = {ga[0], ga[1], ga[2], ga[3], gb[0], gb[1], gb[2], gb[3]};
+    const float rc[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht) {
+      u32x4_t packed;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v0 = __uint_as_float(raw[ht][ks][e] << 16) * rinv[ht] * gw[2 * e];
+        const float v1 = __uint_as_float(raw[ht][ks][e] & 0xffff0000u) * rinv[ht] * gw[2 * e + 1];
+        const float cs = rc[2 * e], sn = rc[2 * e + 1];
+        packed[e] = pack2_bf16_hw(v0 * cs - v1 * sn, v0 * sn + v1 * cs);
+      }
+      qf[ht][ks] = __builtin_bit_cast(bf16x8_t, packed);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  f32x4_t O[HTW][NT];
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) O[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float ref[HTW], lsum[HTW];   // of head 16 ht + j
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht) {
+    ref[ht] = -INFINITY;
+    lsum[ht] = 0.f;
+  }
+  const int tr0 = 4 * g + (j >> 2), tr1 = tr0 + 16;
+
+  for (int c = 0; c < nch; ++c) {
+    // chunk c landed for every wave (later chunks may stay in flight); chunk c - 1 is consumed
+    if (c + 1 < nch && PF >= 2) lds_sync<(PF >= 2 ? RPW : 0)>();
+    else lds_sync<0>();
+    const uint32_t vmask = cmask[c % MQ_DEC_NBUF];
+    if (c + PF < nch)
+      dec_issue<D, DENSE, NW>(c + PF, R, kv + ((c + PF) % MQ_DEC_NBUF) * CHB,
+                              (uint8_t*)&cmask[(c + PF) % MQ_DEC_NBUF], wave, lane);
+    const uint8_t* kb = kv + (c % MQ_DEC_NBUF) * CHB;
+
+    // S^T: 32 keys x 16 HTW heads over all D dims
+    f32x4_t S[2][HTW];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ht = 0; ht < HTW; ++ht) S[kt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8_t a = *(const bf16x8_t*)(kb + (16 * kt + j) * RBP + 16 * ((D / 32) * g + ks));
+#pragma unroll
+        for (int ht = 0; ht < HTW; ++ht)
+          S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], S[kt][ht], 0, 0, 0);
+      }
+      // bound how far the scheduler hoists operand reads (each costs 4 registers)
+      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // online softmax per head; the reference only moves when a chunk maximum
+    // exceeds it by MQ_REF_SLACK, so O is rarely rescaled
+    float alpha[HTW];
+    bool moved = false;
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht) {
+      float cm = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (vmask >> (16 * kt + 4 * g + r)) & 1u;
+          S[kt][ht][r] = ok ? S[kt][ht][r] * scale : -INFINITY;
+          cm = fmaxf(cm, S[kt][ht][r]);
+        }
+      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      const float nr = (cm > ref[ht] + MQ_REF_SLACK) ? cm : ref[ht];
+      alpha[ht] = (nr == ref[ht]) ? 1.f : (ref[ht] == -INFINITY ? 0.f : __expf(ref[ht] - nr));
+      moved |= nr != ref[ht];
+      float ps = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = (S[kt][ht][r] == -INFINITY) ? 0.f : __expf(S[kt][ht][r] - nr);
+          S[kt][ht][r] = e;
+          ps += e;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lsum[ht] = lsum[ht] * alpha[ht] + ps;
+      ref[ht] = nr;
+    }
+    if (__any(moved)) {
+      // Rare (a chunk maximum passed the reference by MQ_REF_SLACK).  O is scaled
+      // through this wave's LDS scratch, eight tiles at a time, so that on the
+      // common path it only ever feeds the matrix cores and stays in AGPRs.
+      f32x4_t* tw = rs_tmp + wave * 8 * 64;
+#pragma unroll
+      for (int ht = 0; ht < HTW; ++ht) {
+        float a4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a4[r] = __shfl(alpha[ht], 4 * g + r, 64);
+#pragma unroll
+        for (int n0 = 0; n0 < NT; n0 += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) tw[u * 64 + lane] = O[ht][n0 + u];
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            f32x4_t v = tw[u * 64 + lane];
+            v[0] *= a4[0];
+            v[1] *= a4[1];
+            v[2] *= a4[2];
+            v[3] *= a4[3];
+            tw[u * 64 + lane] = v;
+          }
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int u = 0; u < 8; ++u) O[ht][n0 + u] = tw[u * 64 + lane];
+          asm volatile("" ::: "memory");
+        }
+      }
+    }
+    bf16x8_t pf[HTW];
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht) {
+      u32x4_t pw;
+      pw[0] = pack2_bf16_hw(S[0][ht][0], S[0][ht][1]);
+      pw[1] = pack2_bf16_hw(S[0][ht][2], S[0][ht][3]);
+      pw[2] = pack2_bf16_hw(S[1][ht][0], S[1][ht][1]);
+      pw[3] = pack2_bf16_hw(S[1][ht][2], S[1][ht][3]);
+      pf[ht] = __builtin_bit_cast(bf16x8_t, pw);
+    }
+    // P.V: V read transposed (keys 4g..4g+3 and 16+4g..16+4g+3 of column j of each tile)
+    const uint32_t b0 = lds_addr(kb) + tr0 * RBP + 8 * (j & 3);
+    const uint32_t b1 = lds_addr(kb) + tr1 * RBP + 8 * (j & 3);
+#pragma unroll
+    for (int mb = 0; mb < NT / 8; ++mb) {
+      u32x2_t vr[16];
+      lds_read_tr16(b0 + 256 * mb, b1 + 256 * mb, vr);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4_t vw = {vr[2 * u][0], vr[2 * u][1], vr[2 * u + 1][0], vr[2 * u + 1][1]};
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
+#pragma unroll
+        for (int ht = 0; ht < HTW; ++ht)
+          O[ht][8 * mb + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vf, O[ht][8 * mb + u], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- output: lane (g, j) of tile (ht, nt) holds heads h0 + 16 ht + 4 g + r, dim 16 nt + j
+  if (n_split == 1) {
+    float f[HTW];
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht) {
+      const float sig = sink ? sink[h0 + 16 * ht + j] : -INFINITY;
+      const float M = fmaxf(ref[ht], sig);
+      float Z = 0.f;
+      if (ref[ht] != -INFINITY) Z += lsum[ht] * __expf(ref[ht] - M);
+      if (sig != -INFINITY) Z += __expf(sig - M);
+      f[ht] = (Z > 0.f && ref[ht] != -INFINITY) ? __expf(ref[ht] - M) / Z : 0.f;
+    }
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float fr = __shfl(f[ht], 4 * g + r, 64);
+        const size_t obase = (row * n_h + h0 + 16 * ht + 4 * g + r) * (size_t)D;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const int dim = 16 * nt + j;
+          const float v = O[ht][nt][r] * fr;
+          const float other = __shfl_xor(v, 1, 64);
+          // rotation at -i: cos(-x) = cos x, sin(-x) = -sin x ((1, 0) outside the rotated dims)
+          const float cs = rope_cs[dim & ~1], sn = -rope_cs[(dim & ~1) + 1];
+          const float o = (dim & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+          out[obase + dim] = f32_to_bf16_bits(o);
+        }
+      }
+  } else {
+    const size_t pb = (row * n_split + sp) * (size_t)n_h + h0;
+#pragma unroll
+    for (int ht = 0; ht < HTW; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = ws + (pb + 16 * ht + 4 * g + r) * (D + 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dst[16 * nt + j] = O[ht][nt][r];
+      }
+    if (g == 0) {
+#pragma unroll
+      for (int ht = 0; ht < HTW; ++ht) {
+        ws[(pb + 16 * ht + j) * (D + 2) + D] = ref[ht];
+        ws[(pb + 16 * ht + j) * (D + 2) + D + 1] = lsum[ht];
+      }
+    }
+  }
+}
+
 // merge the split partial states of one (query, head) in split order, one pass
 // with a running maximum; each thread owns one pair of output dims
 __global__ __launch_bounds__(256) void mqa_combine_kernel(
@@ -749,8 +1198,18 @@ long long mqa_slots_max(const MqaArgs& a) {
   return (a.idx ? (long long)a.k : a.N_cap) + a.n_win;
 }
 
-static void mqa_split(int Tq, long long slots_max, int* kps, int* n_split) {
-  if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
+static int dec_heads_per_wave(int d) { return d >= 512 ? 16 * dec_htw<512>() : 16 * dec_htw<256>(); }
+
+static bool mqa_decode_ok(int Tq, int n_h, int d) {
+  return Tq < MQ_SPLIT_BELOW_TQ && n_h % dec_heads_per_wave(d) == 0;
+}
+
+// slots per workgroup and splits per query; depends on the shape only, never on B
+static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int* n_split) {
+  if (mqa_decode_ok(Tq, n_h, d)) {
+    *kps = MQ_DEC_SPLIT;
+    *n_split = (int)max(1LL, (slots_max + MQ_DEC_SPLIT - 1) / MQ_DEC_SPLIT);
+  } else if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
     long long s = ((slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH;
     if (s > 2147483647LL) s = 2147483647LL;
     *kps = (int)(s > 0 ? s : MQ_CH);
@@ -764,7 +1223,7 @@ static void mqa_split(int Tq, long long slots_max, int* kps, int* n_split) {
 size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max, int dtype) {
   if (!(dtype == DT_BF16 && (d == 128 || d == 256 || d == 512) && n_h % 16 == 0)) return 0;
   int kps, n_split;
-  mqa_split(Tq, n_slots_max, &kps, &n_split);
+  mqa_split(Tq, n_h, d, n_slots_max, &kps, &n_split);
   if (n_split == 1) return 0;
   return (size_t)B * Tq * n_split * n_h * (size_t)(d + 2) * sizeof(float);
 }
@@ -789,9 +1248,39 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
                        n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
 }
 
+template <int D, bool DENSE, int NW>
+static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
+  const int n_hg = a.n_h / (16 * dec_htw<D>() * NW);
+  const long long units = (long long)a.B * a.Tq * n_split;
+  const long long blocks = ((units + 7) / 8) * 8 * n_hg;
+  const size_t lds = (size_t)MQ_DEC_NBUF * MQ_CH * (2 * D + 16);
+  auto kfn = mqa_decode_kernel<D, DENSE, NW>;
+  if (lds > 65536)
+    (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
+                     (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
+                     a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
+                     a.rope_dim, a.rope_base, a.scale, n_split, units, (uint16_t*)a.out,
+                     (float*)a.ws);
+  if (n_split > 1)
+    hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
+                       dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
+                       n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
+}
+
+// waves per workgroup: as many head groups of one wave as divide n_h, up to four
+template <int D, bool DENSE>
+static void launch_decode(const MqaArgs& a, int n_split, hipStream_t st) {
+  constexpr int HW = 16 * dec_htw<D>();
+  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4>(a, n_split, st);
+  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2>(a, n_split, st);
+  else launch_decode_nw<D, DENSE, 1>(a, n_split, st);
+}
+
 template <int D, bool DENSE>
 static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
-  if (kps <= MQ_GROUP) launch_mfma_v<D, DENSE, false>(a, kps, n_split, st);
+  if (mqa_decode_ok(a.Tq, a.n_h, a.d)) launch_decode<D, DENSE>(a, n_split, st);
+  else if (kps <= MQ_GROUP) launch_mfma_v<D, DENSE, false>(a, kps, n_split, st);
   else launch_mfma_v<D, DENSE, true>(a, kps, n_split, st);
 }
 
@@ -800,7 +1289,7 @@ int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
   const long long slots_max = mqa_slots_max(a);
   if (mqa_mfma_ok(a)) {
     int kps, n_split;
-    mqa_split(a.Tq, slots_max, &kps, &n_split);
+    mqa_split(a.Tq, a.n_h, a.d, slots_max, &kps, &n_split);
     if (n_split > 1 && a.ws_bytes < mqa_workspace_bytes(a.B, a.Tq, a.n_h, a.d, slots_max, a.dtype)) {
       *why = "workspace smaller than csa_mqa_workspace_size()";
       return 5;

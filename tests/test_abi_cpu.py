@@ -128,7 +128,7 @@ def test_mqa_validation(lib):
     assert sparse(r=130) == CSA_E_SHAPE
     assert sparse(k=0) == CSA_E_SHAPE
     # a split decode query needs workspace
-    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 9 * 128 * 514 * 4
+    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 4 * 128 * 514 * 4
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED

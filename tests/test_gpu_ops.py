@@ -228,6 +228,8 @@ MQA_CASES = [
     ("bf16_dense_prefill", True, "bf16", 1, 20, 32, 256, 90, 0, 4, 32, 512, 32, "none", True, "prefill"),
     ("bf16_sparse_d128_nowindow", False, "bf16", 2, 2, 16, 128, 200, 40, 4, 0, 0, 128, "none", False, "partial"),
     ("bf16_generic_h8", False, "bf16", 1, 2, 8, 64, 100, 20, 4, 10, 10, 16, "normal", True, "all"),
+    ("bf16_decode_one_split_h32_d256", False, "bf16", 2, 3, 32, 256, 300, 100, 4, 64, 64, 32, "normal", True, "partial"),
+    ("bf16_decode_dense_h96_d128", True, "bf16", 2, 1, 96, 128, 700, 0, 4, 16, 32, 32, "none", False, "all"),
 ]
 
 
@@ -277,7 +279,7 @@ def test_mqa_parity(csa, case):
 
 def test_mqa_empty_key_set_is_zero(csa):
     """k slots all empty, no window, no sink: the output row is 0 (both paths)."""
-    for dt, d, n_h in (("bf16", 128, 16), ("f32", 64, 4)):
+    for dt, d, n_h in (("bf16", 128, 16), ("bf16", 512, 32), ("f32", 64, 4)):
         g = Gen(480, DEV)
         q = g.normal(1, (1, 2, n_h, d), dt)
         E = g.normal(2, (1, 10, d), dt)
