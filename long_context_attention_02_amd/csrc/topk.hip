@@ -11,7 +11,8 @@
 // MSD radix select finds the threshold: 10-bit digits of the 32-bit score key
 // first (LDS histograms, the digit located by one wave), and only when the k-th
 // score is tied, further digits of the index half among the tied elements.
-// One pass collects the k keys and a bitonic sort in LDS orders them.  No
+// One pass collects the k keys (one atomic per wave) and a bitonic sort orders
+// them (lane shuffles for partners within a wave, LDS beyond).  No
 // atomic decides anything but the slot an element lands in before the sort,
 // so results are deterministic.
 //
@@ -19,7 +20,7 @@
 // the block forms the AND and the OR of all score keys, so the bits every key
 // shares are skipped and the digits start at the highest bit that differs.
 // Long rows with few queries (decode) run in two stages: workgroups select
-// the top-k of chunks of 16k elements (any global top-k element is in its
+// the top-k of chunks of 32k elements (any global top-k element is in its
 // chunk's top-k), then one workgroup per row selects from their union.
 #include "csa_device.h"
 #include "csa_internal.h"
@@ -33,39 +34,82 @@ static constexpr int TK_LDS_BYTES = 128 * 1024;           // element cache per w
 static constexpr int TK_CACHE32 = TK_LDS_BYTES / 4;       // score rows cached as ord keys
 static constexpr int TK_CACHE64 = TK_LDS_BYTES / 8;       // K64 candidate lists
 
-// Element sources: hi(e) = ord(score), lo(e) = 0xFFFFFFFF - index.
+// Element sources: hi = ord(score), lo = 0xFFFFFFFF - index.  load<V>(e0)
+// gives elements e0 .. e0 + V - 1 (V per thread and pass); sources held in LDS
+// read V at once (their buffers are padded to 16 bytes, so a group that runs
+// past n stays inside the allocation; such elements are masked by the caller).
 struct LdsRowSrc {     // ord keys cached in LDS; index = base + position
+  static constexpr int V = 4;
   const uint32_t* p;
   long long base;
-  __device__ __forceinline__ uint32_t hi(long long e) const { return p[e]; }
-  __device__ __forceinline__ uint32_t lo(long long e) const { return 0xFFFFFFFFu - (uint32_t)(base + e); }
+  __device__ __forceinline__ void load(long long e0, uint32_t (&h)[V], uint32_t (&l)[V]) const {
+    const u32x4_t q = *(const u32x4_t*)(p + e0);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      h[v] = q[v];
+      l[v] = 0xFFFFFFFFu - (uint32_t)(base + e0 + v);
+    }
+  }
 };
 struct RowSrc {        // scores in global memory; index = base + position
+  static constexpr int V = 1;
   const float* p;
   long long base;
-  __device__ __forceinline__ uint32_t hi(long long e) const { return ord_key(p[e]); }
-  __device__ __forceinline__ uint32_t lo(long long e) const { return 0xFFFFFFFFu - (uint32_t)(base + e); }
+  __device__ __forceinline__ void load(long long e0, uint32_t (&h)[V], uint32_t (&l)[V]) const {
+    h[0] = ord_key(p[e0]);
+    l[0] = 0xFFFFFFFFu - (uint32_t)(base + e0);
+  }
 };
-struct KeySrc {        // explicit K64 candidates, global or LDS (0 = padding, below every real key)
+struct KeyLdsSrc {     // K64 candidates cached in LDS (0 = padding, below every real key)
+  static constexpr int V = 2;
   const uint64_t* p;
-  __device__ __forceinline__ uint32_t hi(long long e) const { return (uint32_t)(p[e] >> 32); }
-  __device__ __forceinline__ uint32_t lo(long long e) const { return (uint32_t)p[e]; }
+  __device__ __forceinline__ void load(long long e0, uint32_t (&h)[V], uint32_t (&l)[V]) const {
+    const u32x4_t q = *(const u32x4_t*)(p + e0);   // little endian: {lo0, hi0, lo1, hi1}
+    l[0] = q[0]; h[0] = q[1];
+    l[1] = q[2]; h[1] = q[3];
+  }
+};
+struct KeySrc {        // K64 candidates in global memory
+  static constexpr int V = 1;
+  const uint64_t* p;
+  __device__ __forceinline__ void load(long long e0, uint32_t (&h)[V], uint32_t (&l)[V]) const {
+    const uint64_t x = p[e0];
+    h[0] = (uint32_t)(x >> 32);
+    l[0] = (uint32_t)x;
+  }
 };
 
 struct TopkShared {
   uint32_t hist[2][TK_BINS];   // double-buffered: one is cleared while the other is read
   uint64_t buf[TK_KMAX];
   uint32_t red_and[TK_THREADS / 64], red_or[TK_THREADS / 64];
+  int wcount[TK_THREADS / 64];
   int digit, cum, cnt_d, count;
 };
 
+// Wave-wide reductions: a butterfly inside each row of 16 lanes through DPP
+// (quad permutes, half-row and row mirrors), then the four row results read
+// as scalars.  Every lane gets the result.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+struct OpAnd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a & b; } };
+struct OpOr { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+
 // block-wide AND / OR of 32-bit values (every thread gets both)
 __device__ __forceinline__ void block_and_or(uint32_t& a, uint32_t& o, TopkShared& sh) {
-#pragma unroll
-  for (int s = 32; s > 0; s >>= 1) {
-    a &= (uint32_t)__shfl_xor((int)a, s, 64);
-    o |= (uint32_t)__shfl_xor((int)o, s, 64);
-  }
+  a = wave_reduce_u32(a, OpAnd{});
+  o = wave_reduce_u32(o, OpOr{});
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) { sh.red_and[wid] = a; sh.red_or[wid] = o; }
   __syncthreads();
@@ -73,16 +117,43 @@ __device__ __forceinline__ void block_and_or(uint32_t& a, uint32_t& o, TopkShare
   for (int w = 0; w < TK_THREADS / 64; ++w) { a &= sh.red_and[w]; o |= sh.red_or[w]; }
 }
 
+// Lower bound for the selection: t = min over the threads that hold elements of
+// each thread's largest hi key.  At least that many elements (one per such
+// thread) have hi >= t, so when they are at least `want`, no element with
+// hi < t can be among the k largest and t = 0 otherwise.  lmax = ~0u marks a
+// thread without elements.
+__device__ __forceinline__ uint32_t block_lower_bound(uint32_t lmax, int want, TopkShared& sh) {
+  const bool has = lmax != ~0u;
+  const uint32_t mn = wave_reduce_u32(has ? lmax : ~0u, OpMin{});
+  const int cnt = __popcll(__ballot(has));
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();   // red_and / wcount may still be read by an earlier reduction
+  if (lane == 0) { sh.red_and[wid] = mn; sh.wcount[wid] = cnt; }
+  __syncthreads();
+  uint32_t t = ~0u;
+  int total = 0;
+  for (int w = 0; w < TK_THREADS / 64; ++w) { t = min(t, sh.red_and[w]); total += sh.wcount[w]; }
+  __syncthreads();   // the reads above finish before the next reduction reuses the buffers
+  return (total >= want && total > 0) ? t : 0u;
+}
+
 // wave 0 finds the digit where the count from the top reaches `need` in hist
-// (bins in descending order); writes sh.digit / cum / cnt_d
+// (bins in descending order); writes sh.digit / cum / cnt_d.  Lane l holds the
+// 16 bins just below TK_BINS - 16 l in registers.
 __device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkShared& sh) {
+  static_assert(TK_BINS == 1024, "16 bins per lane");
   if (threadIdx.x >= 64) return;
   const int lane = threadIdx.x;
-  constexpr int PER = TK_BINS / 64;           // bins per lane, lane 0 holds the top bins
-  const int top = TK_BINS - 1 - PER * lane;
+  const int lo_bin = TK_BINS - 16 * (lane + 1);      // lane's bins: lo_bin .. lo_bin + 15
+  uint32_t c[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u32x4_t v = *(const u32x4_t*)(hist + lo_bin + 4 * q);
+    c[4 * q] = v[0]; c[4 * q + 1] = v[1]; c[4 * q + 2] = v[2]; c[4 * q + 3] = v[3];
+  }
   int sum = 0;
-#pragma unroll 8
-  for (int q = 0; q < PER; ++q) sum += (int)hist[top - q];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) sum += (int)c[q];
   int incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -90,16 +161,18 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkS
     if (lane >= o) incl += y;
   }
   const int above = incl - sum;
-  if (above < need && need <= incl) {
-    int run = above;
-    for (int q = 0; q < PER; ++q) {
-      const int c = (int)hist[top - q];
-      if (need <= run + c) {
-        sh.digit = top - q; sh.cum = run; sh.cnt_d = c;
-        break;
-      }
-      run += c;
+  if (above < need && need <= incl) {   // exactly one lane
+    int run = above, dig = lo_bin, cum = above, cnt = 0;
+    bool found = false;
+#pragma unroll
+    for (int q = 15; q >= 0; --q) {      // top bin first
+      const int cq = (int)c[q];
+      const bool hit = !found && need <= run + cq;
+      if (hit) { dig = lo_bin + q; cum = run; cnt = cq; }
+      found = found || hit;
+      run += cq;
     }
+    sh.digit = dig; sh.cum = cum; sh.cnt_d = cnt;
   }
 }
 
@@ -109,8 +182,10 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkS
 // count still needed from the final group in *need; *tied reports whether the
 // final group holds more elements than needed (only possible for HALF = 0).
 template <class Src, int HALF>
-__device__ void radix_half(const Src& src, long long n, uint32_t k_and, uint32_t k_or, uint32_t hi_val,
-                           int& need, uint32_t& prefix, bool& tied, TopkShared& sh, int& hb) {
+__device__ void radix_half(const Src& src, long long n, uint32_t lb, uint32_t k_and, uint32_t k_or,
+                           uint32_t hi_val, int& need, uint32_t& prefix, bool& tied, TopkShared& sh,
+                           int& hb) {
+  constexpr int V = Src::V;
   const int tid = threadIdx.x;
   const uint32_t diff = k_and ^ k_or;
   tied = false;
@@ -131,16 +206,17 @@ __device__ void radix_half(const Src& src, long long n, uint32_t k_and, uint32_t
     const int shift = top + 1 - width;
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* hist = sh.hist[hb];
-    for (long long e = tid; e < n; e += TK_THREADS) {
-      const uint32_t h = src.hi(e);
-      uint32_t key;
-      if (HALF == 0) {
-        key = h;
-      } else {
-        if (h != hi_val) continue;
-        key = src.lo(e);
+    for (long long e0 = (long long)V * tid; e0 < n; e0 += (long long)V * TK_THREADS) {
+      uint32_t h[V], l[V];
+      src.load(e0, h, l);
+      const int rem = (int)min(n - e0, (long long)V);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const uint32_t key = HALF == 0 ? h[v] : l[v];
+        unsigned ok = (unsigned)(v < rem) & (unsigned)(h[v] >= lb) & (unsigned)((key & pmask) == prefix);
+        if (HALF == 1) ok &= (unsigned)(h[v] == hi_val);
+        if (ok) atomicAdd(&hist[(key >> shift) & dmask], 1u);
       }
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
     }
     // clear the other buffer for the next pass while this one is complete
     for (int e = tid; e < TK_BINS; e += TK_THREADS) sh.hist[hb ^ 1][e] = 0u;
@@ -157,11 +233,84 @@ __device__ void radix_half(const Src& src, long long n, uint32_t k_and, uint32_t
   }
 }
 
+// value of lane (lane ^ M) for M < 64: DPP quad permutes for 1 and 2,
+// ds_swizzle (bit mode, xor mask) for 4..16, ds_bpermute for 32
+template <int M>
+__device__ __forceinline__ uint32_t xchg_u32(uint32_t v) {
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
+  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);
+  else if constexpr (M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  else return (uint32_t)__shfl_xor((int)v, M, 64);
+}
+
+// one compare-exchange step of a descending bitonic sort at (size, stride):
+// thread t holds element t
+template <int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int t, int size, TopkShared& sh, int P) {
+  uint64_t y;
+  if constexpr (STRIDE >= 64) {
+    __syncthreads();
+    if (t < P) sh.buf[t] = x;
+    __syncthreads();
+    y = t < P ? sh.buf[t ^ STRIDE] : 0ull;
+  } else {
+    const uint32_t lo = xchg_u32<STRIDE>((uint32_t)x), hi = xchg_u32<STRIDE>((uint32_t)(x >> 32));
+    y = ((uint64_t)hi << 32) | lo;
+  }
+  const bool desc = (t & size) == 0;
+  const bool lower = (t & STRIDE) == 0;
+  const uint64_t mx = x > y ? x : y, mn = x > y ? y : x;
+  return (lower == desc) ? mx : mn;
+}
+
+// all strides of one merge size, largest first (compile-time strides)
+template <int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t x, int t, int size, TopkShared& sh, int P) {
+  if (STRIDE < size) x = bitonic_step<STRIDE>(x, t, size, sh, P);
+  if constexpr (STRIDE > 1) x = bitonic_merge<STRIDE / 2>(x, t, size, sh, P);
+  return x;
+}
+
+// Bitonic sort of sh.buf[0 .. P), descending, P a power of two <= TK_THREADS:
+// thread t holds element t; partners closer than 64 sit in the same wave and
+// trade through DPP / swizzles / lane permutes, farther ones through LDS.
+__device__ void sort_desc_regs(TopkShared& sh, int P) {
+  const int t = threadIdx.x;
+  uint64_t x = t < P ? sh.buf[t] : 0ull;
+  for (int size = 2; size <= P; size <<= 1) x = bitonic_merge<TK_THREADS / 2>(x, t, size, sh, P);
+  __syncthreads();
+  if (t < P) sh.buf[t] = x;
+  __syncthreads();
+}
+
+// the same order for P up to TK_KMAX, every compare-exchange through LDS
+__device__ void sort_desc_lds(TopkShared& sh, int P) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      for (int i = tid; i < P / 2; i += TK_THREADS) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = sh.buf[lo], y = sh.buf[hi];
+        if ((x < y) == desc) { sh.buf[lo] = y; sh.buf[hi] = x; }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // k largest K64 = hi << 32 | lo among n elements -> sh.buf[0 .. min(k, n)), sorted
-// descending when SORT.  hi_and / hi_or: AND / OR of every element's hi key.
+// descending when SORT.  Only elements with hi >= lb take part (lb from
+// block_lower_bound, which keeps at least min(k, n) of them); hi_and / hi_or:
+// AND / OR of their hi keys.
 template <class Src, bool SORT>
-__device__ int select_topk(const Src& src, long long n, int k, uint32_t hi_and, uint32_t hi_or,
-                           TopkShared& sh) {
+__device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint32_t hi_and,
+                           uint32_t hi_or, TopkShared& sh) {
+  constexpr int V = Src::V;
   const int tid = threadIdx.x;
   const int want = (int)min((long long)k, n);
   if (want <= 0) return 0;
@@ -172,37 +321,78 @@ __device__ int select_topk(const Src& src, long long n, int k, uint32_t hi_and, 
     int need = want, hb = 0;
     bool tied;
     uint32_t pre;
-    radix_half<Src, 0>(src, n, hi_and, hi_or, 0u, need, pre, tied, sh, hb);
+    radix_half<Src, 0>(src, n, lb, hi_and, hi_or, 0u, need, pre, tied, sh, hb);
     thr_hi = pre;
     if (!tied) {
       all_eq_hi = true;       // take every element whose hi >= pre (pre has zero low bits)
     } else {
       // ties on the full hi key: resolve among them by the lo key (the index)
       uint32_t l_and = ~0u, l_or = 0u;
-      for (long long e = tid; e < n; e += TK_THREADS)
-        if (src.hi(e) == thr_hi) { const uint32_t l = src.lo(e); l_and &= l; l_or |= l; }
+      for (long long e0 = (long long)V * tid; e0 < n; e0 += (long long)V * TK_THREADS) {
+        uint32_t h[V], l[V];
+        src.load(e0, h, l);
+        const int rem = (int)min(n - e0, (long long)V);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const bool tie = (v < rem) & (h[v] == thr_hi);
+          l_and &= tie ? l[v] : ~0u;
+          l_or |= tie ? l[v] : 0u;
+        }
+      }
       block_and_or(l_and, l_or, sh);
       __syncthreads();
       uint32_t lpre;
       bool t2;
-      radix_half<Src, 1>(src, n, l_and, l_or, thr_hi, need, lpre, t2, sh, hb);
+      radix_half<Src, 1>(src, n, lb, l_and, l_or, thr_hi, need, lpre, t2, sh, hb);
       thr_lo = lpre;
     }
   } else {
     all_eq_hi = true;
     thr_hi = 0u;
   }
-  // collect every selected key (exactly `want` of them)
-  if (tid == 0) sh.count = 0;
+  // collect every selected key (exactly `want` of them): each wave counts its
+  // selected elements, the waves' ranges follow in wave order, and lanes take
+  // their slots in ballot order (the slot only decides placement before the sort)
+  const int lane = tid & 63, wid = tid >> 6;
+  const long long step = (long long)V * TK_THREADS;
+  const bool by_lo = !all_eq_hi;
+  int mine = 0;
+  for (long long g0 = 0; g0 < n; g0 += step) {
+    const long long e0 = g0 + (long long)V * tid;
+    uint32_t h[V] = {}, l[V] = {};
+    int rem = 0;
+    if (e0 < n) {
+      src.load(e0, h, l);
+      rem = (int)min(n - e0, (long long)V);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const bool sel = by_lo ? ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo))) : (h[v] >= thr_hi);
+      const bool take = (v < rem) & (h[v] >= lb) & sel;
+      mine += __popcll(__ballot(take));
+    }
+  }
+  if (lane == 0) sh.wcount[wid] = mine;
   __syncthreads();
-  for (long long e = tid; e < n; e += TK_THREADS) {
-    const uint32_t h = src.hi(e);
-    bool take;
-    if (all_eq_hi) take = h >= thr_hi;
-    else take = h > thr_hi || (h == thr_hi && src.lo(e) >= thr_lo);
-    if (take) {
-      const int slot = atomicAdd(&sh.count, 1);
-      if (slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h << 32) | src.lo(e);
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += sh.wcount[w];
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (long long g0 = 0; g0 < n; g0 += step) {
+    const long long e0 = g0 + (long long)V * tid;
+    uint32_t h[V] = {}, l[V] = {};
+    int rem = 0;
+    if (e0 < n) {
+      src.load(e0, h, l);
+      rem = (int)min(n - e0, (long long)V);
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const bool sel = by_lo ? ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo))) : (h[v] >= thr_hi);
+      const bool take = (v < rem) & (h[v] >= lb) & sel;
+      const uint64_t bal = __ballot(take);
+      const int slot = base + __popcll(bal & below);
+      if (take && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
+      base += __popcll(bal);
     }
   }
   __syncthreads();
@@ -210,19 +400,9 @@ __device__ int select_topk(const Src& src, long long n, int k, uint32_t hi_and, 
     int P = 1;
     while (P < want) P <<= 1;
     for (int e = want + tid; e < P; e += TK_THREADS) sh.buf[e] = 0ull;
-    for (int size = 2; size <= P; size <<= 1) {
-      for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        __syncthreads();
-        for (int i = tid; i < P / 2; i += TK_THREADS) {
-          const int lo = 2 * i - (i & (stride - 1));
-          const int hi = lo + stride;
-          const bool desc = (lo & size) == 0;
-          const uint64_t x = sh.buf[lo], y = sh.buf[hi];
-          if ((x < y) == desc) { sh.buf[lo] = y; sh.buf[hi] = x; }
-        }
-      }
-    }
     __syncthreads();
+    if (P <= TK_THREADS) sort_desc_regs(sh, P);
+    else sort_desc_lds(sh, P);
   }
   return want;
 }
@@ -231,7 +411,8 @@ __device__ int select_topk(const Src& src, long long n, int k, uint32_t hi_and, 
 template <bool SORT>
 __device__ int select_row(const float* __restrict__ p, long long n, long long base, int k,
                           uint32_t* cache, bool use_cache, TopkShared& sh) {
-  uint32_t a = ~0u, o = 0u;
+  const int want = (int)min((long long)k, n);
+  uint32_t a = ~0u, o = 0u, lmax = ~0u;
   if (use_cache) {
     const long long n4 = (((uintptr_t)p & 15u) == 0) ? (n & ~3LL) : 0;   // vector part if aligned
     for (long long e = 4LL * threadIdx.x; e < n4; e += 4LL * TK_THREADS) {
@@ -239,28 +420,36 @@ __device__ int select_row(const float* __restrict__ p, long long n, long long ba
       u32x4_t ok;
       ok[0] = ord_key(v[0]); ok[1] = ord_key(v[1]); ok[2] = ord_key(v[2]); ok[3] = ord_key(v[3]);
       *(u32x4_t*)(cache + e) = ok;
-      a &= ok[0] & ok[1] & ok[2] & ok[3];
-      o |= ok[0] | ok[1] | ok[2] | ok[3];
+      const uint32_t m4 = max(max(ok[0], ok[1]), max(ok[2], ok[3]));
+      lmax = lmax == ~0u ? m4 : max(lmax, m4);
     }
     for (long long e = n4 + threadIdx.x; e < n; e += TK_THREADS) {
       const uint32_t ok = ord_key(p[e]);
       cache[e] = ok;
-      a &= ok;
-      o |= ok;
+      lmax = lmax == ~0u ? ok : max(lmax, ok);
     }
-    block_and_or(a, o, sh);   // its barrier also publishes the cache
+    const uint32_t lb = block_lower_bound(lmax, want, sh);   // its barriers also publish the cache
+    const LdsRowSrc src{cache, base};
+    for (long long e0 = 4LL * threadIdx.x; e0 < n; e0 += 4LL * TK_THREADS) {
+      uint32_t h[4], l[4];
+      src.load(e0, h, l);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (e0 + v < n && h[v] >= lb) { a &= h[v]; o |= h[v]; }
+    }
+    block_and_or(a, o, sh);
     __syncthreads();
-    return select_topk<LdsRowSrc, SORT>(LdsRowSrc{cache, base}, n, k, a, o, sh);
+    return select_topk<LdsRowSrc, SORT>(src, n, lb, k, a, o, sh);
   }
   const RowSrc src{p, base};
   for (long long e = threadIdx.x; e < n; e += TK_THREADS) {
-    const uint32_t ok = src.hi(e);
+    const uint32_t ok = ord_key(p[e]);
     a &= ok;
     o |= ok;
   }
   block_and_or(a, o, sh);
   __syncthreads();
-  return select_topk<RowSrc, SORT>(src, n, k, a, o, sh);
+  return select_topk<RowSrc, SORT>(src, n, 0u, k, a, o, sh);
 }
 
 __device__ __forceinline__ long long row_nvis(const int* q_pos, size_t row, long long N_cap, int m) {
@@ -323,15 +512,42 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   uint32_t a = ~0u, o = 0u;
   int got;
   if (use_cache) {
-    for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
-      const uint64_t key = cp[e];
-      cache64[e] = key;
-      a &= (uint32_t)(key >> 32);
-      o |= (uint32_t)(key >> 32);
+    uint32_t lmax = ~0u;
+    if ((ncand & 1) == 0) {   // rows start 16-byte aligned: two keys per load
+      typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+      for (long long e = 2LL * threadIdx.x; e < ncand; e += 2LL * TK_THREADS) {
+        const u64x2_t kk = *(const u64x2_t*)(cp + e);
+        *(u64x2_t*)(cache64 + e) = kk;
+        const uint32_t m2 = max((uint32_t)(kk[0] >> 32), (uint32_t)(kk[1] >> 32));
+        lmax = lmax == ~0u ? m2 : max(lmax, m2);
+      }
+    } else {
+      for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
+        const uint64_t key = cp[e];
+        cache64[e] = key;
+        lmax = lmax == ~0u ? (uint32_t)(key >> 32) : max(lmax, (uint32_t)(key >> 32));
+      }
+    }
+    // padding keys (0) only ever lower the bound
+    const uint32_t lb = block_lower_bound(lmax, want, sh);
+    const KeyLdsSrc src{cache64};
+    if ((ncand & 1) == 0) {
+      for (long long e0 = 2LL * threadIdx.x; e0 < ncand; e0 += 2LL * TK_THREADS) {
+        uint32_t h[2], l[2];
+        src.load(e0, h, l);
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+          if (h[v] >= lb) { a &= h[v]; o |= h[v]; }
+      }
+    } else {
+      for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
+        const uint32_t h = (uint32_t)(cache64[e] >> 32);
+        if (h >= lb) { a &= h; o |= h; }
+      }
     }
     block_and_or(a, o, sh);
     __syncthreads();
-    got = select_topk<KeySrc, true>(KeySrc{cache64}, ncand, want, a, o, sh);
+    got = select_topk<KeyLdsSrc, true>(src, ncand, lb, want, a, o, sh);
   } else {
     for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
       a &= (uint32_t)(cp[e] >> 32);
@@ -339,7 +555,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
     }
     block_and_or(a, o, sh);
     __syncthreads();
-    got = select_topk<KeySrc, true>(KeySrc{cp}, ncand, want, a, o, sh);
+    got = select_topk<KeySrc, true>(KeySrc{cp}, ncand, 0u, want, a, o, sh);
   }
   const float* rp = I + row * (size_t)N_cap;
   for (int e = threadIdx.x; e < k; e += TK_THREADS) {
@@ -355,7 +571,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 }
 
 static bool topk_two_stage(long long rows, long long N_cap, int k, long long* chunk, int* nchunks) {
-  const long long ch = 16LL * k;
+  const long long ch = 32LL * k;
   if (rows >= 512 || N_cap < 2 * ch) return false;
   *chunk = ch;
   *nchunks = (int)((N_cap + ch - 1) / ch);
@@ -384,7 +600,8 @@ int launch_topk(const TopkArgs& a, hipStream_t st) {
     const bool c1 = chunk <= TK_CACHE32;
     const long long ncand = (long long)nchunks * a.k;
     const bool c2 = ncand <= TK_CACHE64;
-    const size_t l1 = c1 ? (size_t)chunk * 4 : 0, l2 = c2 ? (size_t)ncand * 8 : 0;
+    // caches padded to 16 bytes: vector reads of the last group stay inside them
+    const size_t l1 = c1 ? ((size_t)chunk * 4 + 15) / 16 * 16 : 0, l2 = c2 ? ((size_t)ncand * 8 + 15) / 16 * 16 : 0;
     if (!set_lds((const void*)topk_chunk_kernel, l1) || !set_lds((const void*)topk_merge_kernel, l2))
       return -1;
     hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS),
@@ -393,7 +610,7 @@ int launch_topk(const TopkArgs& a, hipStream_t st) {
                        a.q_pos, a.N_cap, a.m, a.k, nchunks, (int)c2, a.idx, a.val);
   } else {
     const bool c1 = a.N_cap <= TK_CACHE32;
-    const size_t l1 = c1 ? (size_t)a.N_cap * 4 : 0;
+    const size_t l1 = c1 ? ((size_t)a.N_cap * 4 + 15) / 16 * 16 : 0;
     if (!set_lds((const void*)topk_rows_kernel, l1)) return -1;
     hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)rows), dim3(TK_THREADS), l1, st, a.I,
                        a.q_pos, a.N_cap, a.m, a.k, (int)c1, a.idx, a.val);
