@@ -173,25 +173,30 @@ struct RawSub {                       // one lane's bytes of one key row for one
   uint32_t w[WORDS];
 };
 
+// Lane (g, j) reads row j of the subtile in 16-byte pieces at bytes 64 c + 16 g:
+// load instruction c then covers 64 contiguous bytes of each of the 16 rows.
+// The dims a lane ends up with per K-step are given by dec_dim below, and the
+// query fragments follow the same order.
 template <int KS, int KDT>
 __device__ __forceinline__ void load_raw(RawSub<KS, KDT>& r, const void* __restrict__ K, size_t row,
-                                         int g, bool valid) {
-  constexpr int BYTES = RawSub<KS, KDT>::WORDS * 4;   // contiguous bytes of this lane
-  const uint8_t* p = (const uint8_t*)K + row * (size_t)(BYTES * 4) + (size_t)BYTES * g;
-  if (valid) {
-    if constexpr (BYTES % 16 == 0) {
+                                         int g) {
+  // Unconditional: the caller clamps row to a key of the sequence, and the
+  // score of a slot past the end is never stored (a slot only feeds its own
+  // key column), so no masking, and no select that would wait on the load.
+  constexpr int BYTES = RawSub<KS, KDT>::WORDS * 4;   // bytes of this lane
+  const uint8_t* base = (const uint8_t*)K + row * (size_t)(BYTES * 4);
+  if constexpr (BYTES % 16 == 0) {
+    const uint8_t* p = base + 16 * g;
 #pragma unroll
-      for (int c = 0; c < BYTES / 16; ++c) {
-        const u32x4_t v = *(const u32x4_t*)(p + 16 * c);
-        r.w[4 * c] = v[0]; r.w[4 * c + 1] = v[1]; r.w[4 * c + 2] = v[2]; r.w[4 * c + 3] = v[3];
-      }
-    } else {
-      const u32x2_t v = *(const u32x2_t*)p;
-      r.w[0] = v[0]; r.w[1] = v[1];
+    for (int c = 0; c < BYTES / 16; ++c) {   // streamed once: non-temporal
+      const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(p + 64 * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.w[4 * c + e] = v[e];
     }
   } else {
-#pragma unroll
-    for (int c = 0; c < RawSub<KS, KDT>::WORDS; ++c) r.w[c] = 0u;
+    const u32x2_t v = *(const u32x2_t*)(base + BYTES * g);
+    r.w[0] = v[0];
+    r.w[1] = v[1];
   }
 }
 
@@ -236,6 +241,68 @@ __device__ __forceinline__ float partial_column(const IdxFrags<QH, KS>& f, const
   return part;
 }
 
+// first of the 8 dims lane group g holds in K-step ks of a decode subtile
+template <int KS, int KDT>
+__device__ __forceinline__ int dec_dim(int ks, int g) {
+  if constexpr (KDT == DT_FP8) {
+    if constexpr (KS == 1) return 8 * g;                 // one 8-byte piece at 8 g
+    else return 64 * (ks / 2) + 16 * g + 8 * (ks % 2);   // two K-steps per 16-byte piece
+  } else {
+    return 32 * ks + 8 * g;                              // one K-step per 16-byte piece
+  }
+}
+
+template <int QH, int KS, int KDT>
+__device__ __forceinline__ void load_query_frags_dec(IdxFrags<QH, KS>& f, const uint16_t* __restrict__ qp,
+                                                     const float* __restrict__ wp, int g, int j) {
+  constexpr int DI = 32 * KS;
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      f.A[mt][ks] = *(const bf16x8_t*)(qp + (size_t)(16 * mt + j) * DI + dec_dim<KS, KDT>(ks, g));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f.wv[mt][r] = wp[16 * mt + 4 * g + r];
+  }
+}
+
+// partial_column straight from the raw key bytes, converting one K-step at a
+// time (fewer registers live than converting the whole subtile first)
+template <int QH, int KS, int KDT>
+__device__ __forceinline__ float partial_column_raw(const IdxFrags<QH, KS>& f, const RawSub<KS, KDT>& r) {
+  f32x4_t acc[QH];
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8_t b;
+    if constexpr (KDT == DT_FP8) {
+      const bf16x2_t x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, false);
+      const bf16x2_t x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, true);
+      const bf16x2_t x2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, false);
+      const bf16x2_t x3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, true);
+      const u32x4_t o = {__builtin_bit_cast(uint32_t, x0), __builtin_bit_cast(uint32_t, x1),
+                         __builtin_bit_cast(uint32_t, x2), __builtin_bit_cast(uint32_t, x3)};
+      b = __builtin_bit_cast(bf16x8_t, o);
+    } else {
+      const u32x4_t o = {r.w[4 * ks], r.w[4 * ks + 1], r.w[4 * ks + 2], r.w[4 * ks + 3]};
+      b = __builtin_bit_cast(bf16x8_t, o);
+    }
+#pragma unroll
+    for (int mt = 0; mt < QH; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.A[mt][ks], b, acc[mt], 0, 0, 0);
+  }
+  // ReLU as a signed-integer max on the bits: negative floats (and -0.0) are
+  // negative integers, so one v_max_i32 clears them
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      part += f.wv[mt][r4] * __int_as_float(max(__float_as_int(acc[mt][r4]), 0));
+  return part;
+}
+
 // P[u] = lane group g's share for subtile u; returns the full sum for subtile g
 __device__ __forceinline__ float reduce_scatter4(const float (&P)[4], int g) {
   const bool hi = (g >> 1) & 1, lo = g & 1;
@@ -246,13 +313,15 @@ __device__ __forceinline__ float reduce_scatter4(const float (&P)[4], int g) {
   return (lo ? k1 : k0) + __shfl_xor(s, 16, 64);                  // subtile 2*hi + lo = g
 }
 
+static constexpr int IDX_STAGE = 2048;   // keys per wave whose scores are staged in LDS
+
 template <int QH, int KS, int KDT>
 __global__ __launch_bounds__(256) void index_mfma_decode(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ K,
     const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
     int kpw, float* __restrict__ out) {
   constexpr int H = 16 * QH, DI = 32 * KS;
-  constexpr int PF = (KDT == DT_FP8) ? 4 : 2;   // subtiles in flight per wave
+  constexpr int PF = 4;   // subtiles in flight per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, j = lane & 15;
   const int b = blockIdx.z, t = blockIdx.y;
@@ -265,37 +334,75 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
   const long long nvis = min(N_cap, (i + 1) / m);
 
   IdxFrags<QH, KS> f;
-  load_query_frags<QH, KS>(f, q + qrow * (size_t)(H * DI), w + qrow * H, g, j);
+  load_query_frags_dec<QH, KS, KDT>(f, q + qrow * (size_t)(H * DI), w + qrow * H, g, j);
+  // Retire the query loads here, before the loop: an (empty) use of every
+  // fragment makes the compiler wait for them at this point, so the loop's wait
+  // counts are fixed by the key ring alone (otherwise every iteration waits for
+  // all keys in flight, as the first one must for these loads).
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(f.A[mt][ks]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(f.wv[mt][r]));
+  }
   const size_t kbase = (size_t)b * (size_t)N_cap;
   float* orow = out + qrow * (size_t)N_cap;
 
+  // The key ring holds PF = 4 subtiles in flight (slot u of a group of four);
+  // a slot is consumed, then refilled with the subtile one group later.
   RawSub<KS, KDT> ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
     const long long key = k0 + 16 * p + j;
-    load_raw<KS, KDT>(ring[p], K, kbase + (size_t)(key < k1 ? key : k0), g, p < nst && key < k1);
+    load_raw<KS, KDT>(ring[p], K, kbase + (size_t)(key < k1 ? key : k0), g);
+    __builtin_amdgcn_sched_barrier(0);   // issue in slot order, as the loop refills them
   }
+  // Unscaled scores are staged in LDS and written once the wave's keys are all
+  // read: stores share the memory counter with the loads (waiting for a key
+  // would also wait for every store before it), and the (fp8) row scales and
+  // the visibility mask are applied in that pass with coalesced loads.
+  __shared__ __attribute__((aligned(16))) float stage[4][IDX_STAGE];
+#pragma unroll 1
   for (int st0 = 0; st0 < nst; st0 += 4) {
-    // this lane's store target and (fp8) row scale, fetched early
-    const long long okey = k0 + 16LL * (st0 + g) + j;
-    const bool ook = okey < k1;
-    float osc = 1.f;
-    if constexpr (KDT == DT_FP8) osc = ook ? Ks[kbase + (size_t)okey] : 1.f;
     float P[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int st = st0 + u;
-      RawSub<KS, KDT> cur = ring[u % PF];
-      const int nx = st + PF;
-      const long long nkey = k0 + 16LL * nx + j;
-      load_raw<KS, KDT>(ring[u % PF], K, kbase + (size_t)(nkey < k1 ? nkey : k0), g,
-                        nx < nst && nkey < k1);
-      bf16x8_t Bf[KS];
-      raw_to_frags<KS, KDT>(cur, Bf);
-      P[u] = partial_column<QH, KS>(f, Bf);
+      static_assert(PF == 4, "slot u of each group");
+      P[u] = partial_column_raw<QH, KS, KDT>(f, ring[u]);
+      // the sum is materialised here, so the epilogue is not sunk below the
+      // later subtiles (which would keep 64 accumulators live instead of 16)
+      asm volatile("" : "+v"(P[u]));
+      const long long nkey = k0 + 16LL * (st0 + u + PF) + j;
+      load_raw<KS, KDT>(ring[u], K, kbase + (size_t)(nkey < k1 ? nkey : k0), g);
+      // keep the next slot's conversions out of this one (they would wait on its load)
+      __builtin_amdgcn_sched_barrier(0);
     }
     const float v = reduce_scatter4(P, g);
-    if (ook) orow[okey] = okey < nvis ? v * osc : -INFINITY;
+    if (k0 + 16LL * (st0 + g) + j < k1) stage[wave][16 * (st0 + g) + j] = v;
+  }
+  const int n = (int)(k1 - k0);
+  float* dst = orow + k0;
+  const float* srow = Ks + kbase + k0;
+  const bool vec = (((uintptr_t)dst) & 15u) == 0 && (KDT != DT_FP8 || (((uintptr_t)srow) & 15u) == 0);
+  const int nv = (int)max(0LL, min((long long)n, nvis - k0));   // visible keys of the wave
+  for (int e = 4 * lane; e < n; e += 256) {
+    if (vec && e + 4 <= n) {
+      f32x4_t v = *(const f32x4_t*)&stage[wave][e];
+      if constexpr (KDT == DT_FP8) {
+        const f32x4_t s4 = __builtin_nontemporal_load((const f32x4_t*)(srow + e));
+        v = v * s4;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = e + c < nv ? v[c] : -INFINITY;
+      __builtin_nontemporal_store(v, (f32x4_t*)(dst + e));
+    } else {
+      for (int c = e; c < min(e + 4, n); ++c) {
+        float v = stage[wave][c];
+        if constexpr (KDT == DT_FP8) v *= srow[c];
+        dst[c] = c < nv ? v : -INFINITY;
+      }
+    }
   }
 }
 
@@ -469,6 +576,7 @@ static void launch_mfma(const IndexArgs& a, hipStream_t st) {
     long long kpw = (a.N_cap * rows + waves - 1) / waves;
     kpw = ((kpw + 63) / 64) * 64;
     if (kpw < 64) kpw = 64;
+    if (kpw > IDX_STAGE) kpw = IDX_STAGE;   // a wave's scores fit its LDS stage
     long long nblk = (a.N_cap + 4 * kpw - 1) / (4 * kpw);
     dim3 grid((unsigned)nblk, (unsigned)a.Tq, (unsigned)a.B);
     hipLaunchKernelGGL((index_mfma_decode<QH, KS, KDT>), grid, dim3(256), 0, st, q, a.w, a.K,
