@@ -4,9 +4,11 @@ Usage: ``python -m long_context_attention_02_amd.build`` or ``build()``.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -15,28 +17,50 @@ SOURCES = ["compress.hip", "index_score.hip", "topk.hip", "mqa.hip", "csa_abi.hi
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 ops stay off: hand-written and compiler-formed v_pk_*_f32 are avoided
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# per-source additions: the decode indexer's MFMA results feed VALU work
+# directly, so they are formed in VGPRs (no accumulator-to-VGPR copies)
+EXTRA_FLAGS = {
+    "index_score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
+def _noise(stderr: str) -> list[str]:
+    # the host pass does not know the packed-fp32 feature and says so; that is harmless
+    return [ln for ln in (stderr or "").splitlines()
+            if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
 
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(HERE, "..", "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 feature and says so; that is harmless
-    noise = [ln for ln in (res.stderr or "").splitlines()
-             if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(noise))
-    if verbose and noise:
-        print("\n".join(noise), file=sys.stderr)
+    inc = ["-I", os.path.join(HERE, "..", "include")]
+    with tempfile.TemporaryDirectory(prefix="csa_build_") as tmpdir:
+        def compile_one(src: str) -> str:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), *inc, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(_noise(res.stderr)))
+            if verbose and _noise(res.stderr):
+                print("\n".join(_noise(res.stderr)), file=sys.stderr)
+            return obj
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+            objs = list(pool.map(compile_one, SOURCES))
+        tmp = LIB + ".tmp"
+        cmd = [hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc link failed:\n" + "\n".join(_noise(res.stderr)))
     os.replace(tmp, LIB)
     return LIB
 

@@ -159,86 +159,91 @@ __device__ __forceinline__ void load_key_frags(bf16x8_t (&Bf)[KS], const void* _
 }
 
 // ---------------------------------------------------------------------------
-// decode: few query rows, keys streamed from HBM straight into registers.
-// Each wave owns kpw consecutive keys of one query row and walks them in
-// subtiles of 16 keys with a prefetch ring of PF subtiles in flight.  Four
-// subtiles form a group: every lane first sums its 16 head rows per subtile,
-// then a reduce-scatter across the 4 lane groups (3 cross-lane adds) leaves
-// lane (g, j) with the full score of key j of subtile g, so each group ends
-// in one coalesced 256-byte store.
+// decode: few query rows, keys streamed from HBM through registers.
+// The waves of one query row share its keys and walk them in subtiles of 16
+// keys, with a register ring of PF subtiles in flight.  A subtile is loaded
+// contiguously (each load instruction covers whole 128-byte lines: a layout
+// with 16 rows per instruction, each read in part, streams markedly slower)
+// and turned into the MFMA operand layout through a small wave-private LDS
+// tile.  Four subtiles form a group: every lane first sums its 16 head rows
+// per subtile, then a reduce-scatter across the 4 lane groups (3 cross-lane
+// adds) leaves lane (g, j) with the full score of key j of subtile g.
 // ---------------------------------------------------------------------------
 template <int KS, int KDT>
-struct RawSub {                       // one lane's bytes of one key row for one subtile
+struct RawSub {                       // one lane's bytes of one subtile
   static constexpr int WORDS = (KDT == DT_FP8 ? 8 * KS : 16 * KS) / 4;
   uint32_t w[WORDS];
 };
 
-// Lane (g, j) reads row j of the subtile in 16-byte pieces at bytes 64 c + 16 g:
-// load instruction c then covers 64 contiguous bytes of each of the 16 rows.
-// The dims a lane ends up with per K-step are given by dec_dim below, and the
-// query fragments follow the same order.
 template <int KS, int KDT>
-__device__ __forceinline__ void load_raw(RawSub<KS, KDT>& r, const void* __restrict__ K, size_t row,
-                                         int g) {
-  // Unconditional: the caller clamps row to a key of the sequence, and the
-  // score of a slot past the end is never stored (a slot only feeds its own
-  // key column), so no masking, and no select that would wait on the load.
-  constexpr int BYTES = RawSub<KS, KDT>::WORDS * 4;   // bytes of this lane
-  const uint8_t* base = (const uint8_t*)K + row * (size_t)(BYTES * 4);
-  if constexpr (BYTES % 16 == 0) {
-    const uint8_t* p = base + 16 * g;
+struct SubGeom {
+  static constexpr int RB = KDT == DT_FP8 ? 32 * KS : 64 * KS;   // bytes per key row
+  static constexpr int SB = 16 * RB;                             // bytes per subtile
+  static constexpr int LB = SB / 64;                             // bytes per lane
+  static constexpr int NP = RB / 16;                             // 16-byte pieces per row
+  static constexpr int RPB = RB >= 256 ? 1 : 256 / RB;           // rows per 256 LDS bytes
+  // LDS slot of piece P of row R: pieces are XOR-swizzled within their row so
+  // that the 16 rows one lane group reads land on distinct banks
+  static __device__ __forceinline__ int slot(int R, int P) { return RB * R + 16 * (P ^ ((R / RPB) % NP)); }
+};
+
+// Contiguous load of subtile rows row0 .. row0 + 15 (rows past klast read row
+// klast instead: their scores are never stored, and a slot only feeds its own
+// key column).  Lane l holds bytes [64 c + 16 l, +16) of instruction c of the
+// subtile (8 bytes at 8 l when a lane's share is 8 bytes).  Unconditional, so
+// no select waits on the load; streamed once, so non-temporal.
+template <int KS, int KDT>
+__device__ __forceinline__ void load_lin(RawSub<KS, KDT>& r, const uint8_t* __restrict__ Kb, int row0,
+                                         int klast, int lane) {
+  // Kb: the sequence's first key row; rows are < 2^31 (the entry point checks N_cap)
+  using G = SubGeom<KS, KDT>;
+  if constexpr (G::LB >= 16) {
 #pragma unroll
-    for (int c = 0; c < BYTES / 16; ++c) {   // streamed once: non-temporal
-      const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)(p + 64 * c));
+    for (int c = 0; c < G::LB / 16; ++c) {
+      const int L = 64 * c + lane;
+      const uint32_t row = min((uint32_t)row0 + (uint32_t)(L / G::NP), (uint32_t)klast);
+      const u32x4_t v = __builtin_nontemporal_load(
+          (const u32x4_t*)(Kb + (size_t)row * G::RB + 16 * (L % G::NP)));
 #pragma unroll
       for (int e = 0; e < 4; ++e) r.w[4 * c + e] = v[e];
     }
   } else {
-    const u32x2_t v = *(const u32x2_t*)(base + BYTES * g);
+    static_assert(G::LB == 8, "8-byte lane share");
+    const uint32_t row = min((uint32_t)row0 + (uint32_t)((8 * lane) / G::RB), (uint32_t)klast);
+    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)(Kb + (size_t)row * G::RB + (8 * lane) % G::RB));
     r.w[0] = v[0];
     r.w[1] = v[1];
   }
 }
 
+// Linear subtile bytes -> the decode operand layout through the wave's LDS tile:
+// lane (g, j) gets row j, 16-byte pieces g + 4 c (bytes 64 c + 16 g), or the
+// 8 bytes at 8 g when its share is 8 bytes.  The wave's own LDS operations run
+// in order, so the read sees the write without a barrier.
 template <int KS, int KDT>
-__device__ __forceinline__ void raw_to_frags(const RawSub<KS, KDT>& r, bf16x8_t (&Bf)[KS]) {
+__device__ __forceinline__ void lds_transpose(RawSub<KS, KDT>& out, const RawSub<KS, KDT>& in,
+                                              uint8_t* tile, int lane, int g, int j) {
+  using G = SubGeom<KS, KDT>;
+  if constexpr (G::LB >= 16) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if constexpr (KDT == DT_FP8) {
-      // 8 codes -> 8 bf16, exactly (gfx950 conversion, scale 1)
-      bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, false);
-      bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks], 1.0f, true);
-      bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, false);
-      bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.w[2 * ks + 1], 1.0f, true);
-      u32x4_t o;
-      o[0] = __builtin_bit_cast(uint32_t, a); o[1] = __builtin_bit_cast(uint32_t, b);
-      o[2] = __builtin_bit_cast(uint32_t, c); o[3] = __builtin_bit_cast(uint32_t, d);
-      Bf[ks] = __builtin_bit_cast(bf16x8_t, o);
-    } else {
-      u32x4_t o;
-      o[0] = r.w[4 * ks]; o[1] = r.w[4 * ks + 1]; o[2] = r.w[4 * ks + 2]; o[3] = r.w[4 * ks + 3];
-      Bf[ks] = __builtin_bit_cast(bf16x8_t, o);
+    for (int c = 0; c < G::LB / 16; ++c) {
+      const int L = 64 * c + lane;
+      const u32x4_t v = {in.w[4 * c], in.w[4 * c + 1], in.w[4 * c + 2], in.w[4 * c + 3]};
+      *(u32x4_t*)(tile + G::slot(L / G::NP, L % G::NP)) = v;
     }
+#pragma unroll
+    for (int c = 0; c < G::LB / 16; ++c) {
+      const u32x4_t v = *(const u32x4_t*)(tile + G::slot(j, g + 4 * c));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out.w[4 * c + e] = v[e];
+    }
+  } else {
+    const int byte = 8 * lane;
+    *(u32x2_t*)(tile + G::slot(byte / G::RB, (byte % G::RB) / 16) + (byte & 8)) = u32x2_t{in.w[0], in.w[1]};
+    const u32x2_t v = *(const u32x2_t*)(tile + G::slot(j, g / 2) + 8 * (g & 1));
+    out.w[0] = v[0];
+    out.w[1] = v[1];
   }
-}
-
-// this lane's share (its 4*QH head rows) of sum_h w * ReLU(dot) for its key column
-template <int QH, int KS>
-__device__ __forceinline__ float partial_column(const IdxFrags<QH, KS>& f, const bf16x8_t (&Bf)[KS]) {
-  f32x4_t acc[QH];
-#pragma unroll
-  for (int mt = 0; mt < QH; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int mt = 0; mt < QH; ++mt)
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.A[mt][ks], Bf[ks], acc[mt], 0, 0, 0);
-  float part = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < QH; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) part += f.wv[mt][r] * fmaxf(acc[mt][r], 0.f);
-  return part;
 }
 
 // first of the 8 dims lane group g holds in K-step ks of a decode subtile
@@ -314,94 +319,152 @@ __device__ __forceinline__ float reduce_scatter4(const float (&P)[4], int g) {
 }
 
 static constexpr int IDX_STAGE = 2048;   // keys per wave whose scores are staged in LDS
+static constexpr int IDX_UNIT = 4;       // subtiles of 16 keys per interleaving unit
+static constexpr int IDX_FLUSH = 32;     // staged subtiles written out together (0: all at the end)
+static_assert(IDX_FLUSH % 16 == 0 && IDX_FLUSH * 16 <= IDX_STAGE, "flush windows of whole store rounds");
+// a wave gets at most ceil(units / W) units, W >= units * 16 * IDX_UNIT / IDX_STAGE (launcher)
+static_assert(IDX_STAGE % (16 * IDX_UNIT) == 0, "stage holds whole units");
 
+// Decode (few query rows): the waves of one query row interleave over its keys
+// in units of IDX_UNIT subtiles (wave w takes units w, w + W, w + 2W, ...), so
+// at any moment the device reads a few narrow moving windows of the key array
+// rather than one far-apart stream per wave.
 template <int QH, int KS, int KDT>
 __global__ __launch_bounds__(256) void index_mfma_decode(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ K,
     const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
-    int kpw, float* __restrict__ out) {
+    float* __restrict__ out, int flush_ok) {
   constexpr int H = 16 * QH, DI = 32 * KS;
   constexpr int PF = 4;   // subtiles in flight per wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int U = IDX_UNIT;
+  // the wave index through readfirstlane: the compiler then knows everything
+  // derived from it is wave-uniform (scalar registers, uniform branches)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
   const int b = blockIdx.z, t = blockIdx.y;
   const size_t qrow = (size_t)b * Tq + t;
-  const long long k0 = ((long long)blockIdx.x * 4 + wave) * kpw;
-  if (k0 >= N_cap) return;
-  const long long k1 = min(k0 + (long long)kpw, N_cap);
-  const int nst = (int)((k1 - k0 + 15) / 16);
+  const long long W = 4LL * gridDim.x;                  // waves of this query row
+  const long long wid = 4LL * blockIdx.x + wave;
+  const long long nunits = (N_cap + 16 * U - 1) / (16 * U);
+  if (wid >= nunits) return;
+  const int nls = (int)((nunits - 1 - wid) / W + 1) * U;   // subtiles of this wave
+  // (at least one: stated so that the ring's first loads are not sunk into a
+  // loop guard, behind the wait for the query loads)
+  __builtin_assume(nls >= 1);
   const long long i = q_pos[qrow];
   const long long nvis = min(N_cap, (i + 1) / m);
+  // first key of the wave's local subtile ls (32-bit: keys are < 2^31, and a
+  // subtile index up to PF past the wave's last one stays far below that)
+  const int wid32 = (int)wid, W32 = (int)W;
+  auto key0 = [&](int ls) -> int { return 16 * ((wid32 + W32 * (ls / U)) * U + ls % U); };
 
   IdxFrags<QH, KS> f;
   load_query_frags_dec<QH, KS, KDT>(f, q + qrow * (size_t)(H * DI), w + qrow * H, g, j);
-  // Retire the query loads here, before the loop: an (empty) use of every
-  // fragment makes the compiler wait for them at this point, so the loop's wait
-  // counts are fixed by the key ring alone (otherwise every iteration waits for
-  // all keys in flight, as the first one must for these loads).
-#pragma unroll
-  for (int mt = 0; mt < QH; ++mt) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(f.A[mt][ks]));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) asm volatile("" ::"v"(f.wv[mt][r]));
-  }
   const size_t kbase = (size_t)b * (size_t)N_cap;
   float* orow = out + qrow * (size_t)N_cap;
+  const int klast = (int)(N_cap - 1);   // absent keys load this row (their scores are never stored)
+  const uint8_t* Kb = (const uint8_t*)K + kbase * SubGeom<KS, KDT>::RB;
+
+  // Scores are staged in LDS (slot 16 ls + j for key j of local subtile ls)
+  // and written once the wave's keys are all read: stores share the memory
+  // counter with the loads, and waiting for a key would also wait for every
+  // store issued before it.  For fp8 keys the slots first receive the keys'
+  // row scales, straight from memory (4-byte LDS DMA, one key per lane).
+  __shared__ __attribute__((aligned(16))) float stage[4][IDX_STAGE];
+  if constexpr (KDT == DT_FP8) {
+    // a fixed count of DMAs (slots past the wave's keys read row klast), so the
+    // compiler can count the loads in flight after them
+    const float* sb = Ks + kbase;
+#pragma unroll
+    for (int c = 0; c < IDX_STAGE / 64; ++c) {
+      const int e = 64 * c + lane;
+      const int key = (e >> 4) < nls ? min(key0(e >> 4) + (e & 15), klast) : klast;
+      __builtin_amdgcn_global_load_lds((const void*)(sb + key),
+                                       (__attribute__((address_space(3))) void*)&stage[wave][64 * c], 4, 0, 0);
+    }
+  }
 
   // The key ring holds PF = 4 subtiles in flight (slot u of a group of four);
-  // a slot is consumed, then refilled with the subtile one group later.
+  // a slot is consumed (moved through the LDS tile), then refilled with the
+  // subtile one group later.
   RawSub<KS, KDT> ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
-    const long long key = k0 + 16 * p + j;
-    load_raw<KS, KDT>(ring[p], K, kbase + (size_t)(key < k1 ? key : k0), g);
+    load_lin<KS, KDT>(ring[p], Kb, p < nls ? key0(p) : klast, klast, lane);
     __builtin_amdgcn_sched_barrier(0);   // issue in slot order, as the loop refills them
   }
-  // Unscaled scores are staged in LDS and written once the wave's keys are all
-  // read: stores share the memory counter with the loads (waiting for a key
-  // would also wait for every store before it), and the (fp8) row scales and
-  // the visibility mask are applied in that pass with coalesced loads.
-  __shared__ __attribute__((aligned(16))) float stage[4][IDX_STAGE];
+  // Retire the query loads here, with the ring already in flight: an (empty,
+  // register-only) rewrite of every fragment makes the compiler wait for them
+  // at this point, so the loop's wait counts are fixed by the ring alone
+  // (otherwise every iteration would wait for all keys in flight, as the first
+  // one must for these loads).  Not volatile: a volatile asm counts as a
+  // memory access and would also wait for the scale DMA and the whole ring.
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) asm("" : "+v"(f.A[mt][ks]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm("" : "+v"(f.wv[mt][r]));
+  }
+  __shared__ __attribute__((aligned(16))) uint8_t tile[4][SubGeom<KS, KDT>::SB];
+  int flushed = 0;   // subtiles already written out
 #pragma unroll 1
-  for (int st0 = 0; st0 < nst; st0 += 4) {
+  for (int st0 = 0; st0 < nls; st0 += 4) {
     float P[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       static_assert(PF == 4, "slot u of each group");
-      P[u] = partial_column_raw<QH, KS, KDT>(f, ring[u]);
+      RawSub<KS, KDT> T;
+      lds_transpose<KS, KDT>(T, ring[u], tile[wave], lane, g, j);
+      const int nx = st0 + u + PF;
+      load_lin<KS, KDT>(ring[u], Kb, nx < nls ? key0(nx) : klast, klast, lane);
+      P[u] = partial_column_raw<QH, KS, KDT>(f, T);
       // the sum is materialised here, so the epilogue is not sunk below the
       // later subtiles (which would keep 64 accumulators live instead of 16)
       asm volatile("" : "+v"(P[u]));
-      const long long nkey = k0 + 16LL * (st0 + u + PF) + j;
-      load_raw<KS, KDT>(ring[u], K, kbase + (size_t)(nkey < k1 ? nkey : k0), g);
       // keep the next slot's conversions out of this one (they would wait on its load)
       __builtin_amdgcn_sched_barrier(0);
     }
+    // (the scale fetch is older than every key load waited for above, and the
+    // memory counter retires loads in order, so the scales are in LDS by now)
     const float v = reduce_scatter4(P, g);
-    if (k0 + 16LL * (st0 + g) + j < k1) stage[wave][16 * (st0 + g) + j] = v;
-  }
-  const int n = (int)(k1 - k0);
-  float* dst = orow + k0;
-  const float* srow = Ks + kbase + k0;
-  const bool vec = (((uintptr_t)dst) & 15u) == 0 && (KDT != DT_FP8 || (((uintptr_t)srow) & 15u) == 0);
-  const int nv = (int)max(0LL, min((long long)n, nvis - k0));   // visible keys of the wave
-  for (int e = 4 * lane; e < n; e += 256) {
-    if (vec && e + 4 <= n) {
-      f32x4_t v = *(const f32x4_t*)&stage[wave][e];
-      if constexpr (KDT == DT_FP8) {
-        const f32x4_t s4 = __builtin_nontemporal_load((const f32x4_t*)(srow + e));
-        v = v * s4;
-      }
+    const int ls = st0 + g;
+    if (ls < nls) {
+      const int e = 16 * ls + j;
+      float r = v;
+      if constexpr (KDT == DT_FP8) r *= stage[wave][e];
+      stage[wave][e] = key0(ls) + j < nvis ? r : -INFINITY;
+    }
+    // Every IDX_FLUSH subtiles, write the window out: spreading the stores
+    // over the loop keeps them off the wave's tail.  flush_ok (set by the
+    // launcher) says every output row is 16-byte aligned and every unit lies
+    // inside the sequence, so a window of the wave's subtiles holds only keys
+    // that exist.  (A test in terms other than nls and such a flag here makes
+    // the compiler lose its count of the loads in flight and wait for all.)
+    if constexpr (IDX_FLUSH > 0) {
+      if ((st0 + 4) % IDX_FLUSH == 0 && st0 + 4 <= nls && flush_ok) {
+        const int e0 = 16 * (st0 + 4 - IDX_FLUSH) + 4 * lane;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = e + c < nv ? v[c] : -INFINITY;
-      __builtin_nontemporal_store(v, (f32x4_t*)(dst + e));
-    } else {
-      for (int c = e; c < min(e + 4, n); ++c) {
-        float v = stage[wave][c];
-        if constexpr (KDT == DT_FP8) v *= srow[c];
-        dst[c] = c < nv ? v : -INFINITY;
+        for (int c = 0; c < IDX_FLUSH / 16; ++c) {
+          const int e = e0 + 256 * c;
+          __builtin_nontemporal_store(*(const f32x4_t*)&stage[wave][e],
+                                      (f32x4_t*)(orow + key0(e >> 4) + (e & 15)));
+        }
+        flushed = st0 + 4;
       }
+    }
+  }
+  // write pass for the rest: four keys per lane, 16 lanes per subtile, LDS to memory only
+  for (int e = 16 * flushed + 4 * lane; e < 16 * nls; e += 256) {
+    const int key = key0(e >> 4) + (e & 15);
+    if (key > klast) continue;
+    const f32x4_t v = *(const f32x4_t*)&stage[wave][e];
+    if (key + 3 <= klast && (((uintptr_t)(orow + key)) & 15u) == 0) {
+      __builtin_nontemporal_store(v, (f32x4_t*)(orow + key));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (key + c <= klast) orow[key + c] = v[c];
     }
   }
 }
@@ -569,18 +632,20 @@ static void launch_mfma(const IndexArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((index_mfma_prefill<QH, KS, KDT, PF_QPW>), grid, dim3(256), 0, st, q, a.w,
                        a.K, a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out);
   } else {
-    // one round of resident waves over the chip, each wave at least 64 keys
+    // one round of resident waves over the chip, shared evenly by the query
+    // rows; enough waves per row that each wave's scores fit its LDS stage
     auto kfn = index_mfma_decode<QH, KS, KDT>;
     const long long waves = resident_waves((const void*)kfn, 256);
-    long long rows = (long long)a.B * a.Tq;
-    long long kpw = (a.N_cap * rows + waves - 1) / waves;
-    kpw = ((kpw + 63) / 64) * 64;
-    if (kpw < 64) kpw = 64;
-    if (kpw > IDX_STAGE) kpw = IDX_STAGE;   // a wave's scores fit its LDS stage
-    long long nblk = (a.N_cap + 4 * kpw - 1) / (4 * kpw);
-    dim3 grid((unsigned)nblk, (unsigned)a.Tq, (unsigned)a.B);
+    const long long rows = (long long)a.B * a.Tq;
+    const long long nunits = (a.N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT);
+    long long wpr = max(1LL, waves / rows);
+    wpr = max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
+    wpr = min(wpr, nunits);
+    dim3 grid((unsigned)((wpr + 3) / 4), (unsigned)a.Tq, (unsigned)a.B);
+    // early flushes use 16-byte stores of whole units
+    const int flush_ok = (((uintptr_t)a.out) & 15u) == 0 && a.N_cap % (16 * IDX_UNIT) == 0;
     hipLaunchKernelGGL((index_mfma_decode<QH, KS, KDT>), grid, dim3(256), 0, st, q, a.w, a.K,
-                       a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, (int)kpw, a.out);
+                       a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out, flush_ok);
   }
 }
 
