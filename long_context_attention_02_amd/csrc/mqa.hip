@@ -693,12 +693,12 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode kernel (few queries per sequence, heads a multiple of 32).
+// decode kernel (few queries per sequence, heads a multiple of 16 per wave).
 //
-// A workgroup takes one query, a group of 32 NW heads and a fixed range of at
-// most MQ_DEC_SPLIT key slots.  Wave w owns 32 heads of the group (two 16-head
-// tiles) over all D dims, so scores, softmax and P.V stay inside the wave and
-// need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
+// A workgroup takes one query, a group of 16 HTW NW heads and a fixed range of
+// at most MQ_DEC_SPLIT key slots.  Wave w owns HTW 16-head tiles of the group
+// (one at D = 512, two below) over all D dims, so scores, softmax and P.V stay
+// inside the wave and need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
 // MQ_DEC_NBUF chunks filled with global_load_lds, MQ_DEC_NBUF - 1 chunks ahead,
 // so each row is fetched from memory once per workgroup and then read from LDS
 // by every wave.  Rows sit at a stride of 2D + 16 bytes: 16 lanes reading one
