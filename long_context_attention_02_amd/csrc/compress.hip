@@ -20,13 +20,14 @@ namespace csa {
 
 static constexpr int COMP_THREADS = 512;
 static constexpr int COMP_MAX_G = 8;
+static constexpr int COMP_JU = 8;   // channels per thread whose loads are issued together
 
 template <int IDT, int ODT>
 __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
     const void* __restrict__ Ca, const void* __restrict__ Za, const void* __restrict__ Cb,
     const void* __restrict__ Zb, long long in_bs, long long tok_base, long long T, int c, int m,
     int overlap, long long s_begin, int G, const float* __restrict__ gamma, float eps, int rope_dim,
-    float rope_base, long long pos_stride, long long pos_offset, void* __restrict__ E,
+    RopeRatio rope, long long pos_stride, long long pos_offset, void* __restrict__ E,
     float* __restrict__ E_scale, long long out_bs, long long out_ring) {
   extern __shared__ float smem[];
   float* pmax = smem;                 // [G][c]
@@ -54,31 +55,54 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
   const int tg = threadIdx.x % tpg;
 
   // ---- partial online softmax over candidates g, g+G, g+2G, ...
-  for (int j = tg; j < c; j += tpg) {
-    float mx = -INFINITY, sum = 0.f, acc = 0.f;
-#pragma unroll 4
+  // COMP_JU channels per thread at a time, so their loads are all in flight
+  // before any is used (one channel at a time, every channel costs a memory
+  // latency, and at decode one workgroup per sequence is all the parallelism)
+  for (int j0 = tg; j0 < c; j0 += tpg * COMP_JU) {
+    float mx[COMP_JU], sum[COMP_JU], acc[COMP_JU];
+#pragma unroll
+    for (int u = 0; u < COMP_JU; ++u) {
+      mx[u] = -INFINITY;
+      sum[u] = 0.f;
+      acc[u] = 0.f;
+    }
+#pragma unroll 2
     for (long long q = g; q < ncand; q += G) {
       const bool in_a = q < na;
       const long long tok = in_a ? a_lo + q : b_lo + (q - na);
-      const size_t off = base + (size_t)(tok - tok_base) * (size_t)c + (size_t)j;
+      const size_t off0 = base + (size_t)(tok - tok_base) * (size_t)c;
       const void* Cp = in_a ? Ca : Cb;
       const void* Zp = in_a ? Za : Zb;
-      const float x = load_as_f32<IDT>(Cp, off);
-      const float z = Zp ? load_as_f32<IDT>(Zp, off) : 0.f;
-      if (z > mx) {
-        const float r = __expf(mx - z);   // mx = -inf on the first candidate gives 0
-        sum = sum * r + 1.f;
-        acc = acc * r + x;
-        mx = z;
-      } else {
-        const float e = __expf(z - mx);
-        sum += e;
-        acc += e * x;
+      float x[COMP_JU], z[COMP_JU];
+#pragma unroll
+      for (int u = 0; u < COMP_JU; ++u) {
+        const int j = j0 + u * tpg;
+        x[u] = j < c ? load_as_f32<IDT>(Cp, off0 + (size_t)j) : 0.f;
+        z[u] = (j < c && Zp) ? load_as_f32<IDT>(Zp, off0 + (size_t)j) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < COMP_JU; ++u) {
+        if (z[u] > mx[u]) {
+          const float r = __expf(mx[u] - z[u]);   // mx = -inf on the first candidate gives 0
+          sum[u] = sum[u] * r + 1.f;
+          acc[u] = acc[u] * r + x[u];
+          mx[u] = z[u];
+        } else {
+          const float e = __expf(z[u] - mx[u]);
+          sum[u] += e;
+          acc[u] += e * x[u];
+        }
       }
     }
-    pmax[g * c + j] = mx;
-    psum[g * c + j] = sum;
-    pacc[g * c + j] = acc;
+#pragma unroll
+    for (int u = 0; u < COMP_JU; ++u) {
+      const int j = j0 + u * tpg;
+      if (j < c) {
+        pmax[g * c + j] = mx[u];
+        psum[g * c + j] = sum[u];
+        pacc[g * c + j] = acc[u];
+      }
+    }
   }
   __syncthreads();
 
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
     if (j >= rbeg) {
       const int u = (j - rbeg) >> 1;
       float cs, sn;
-      rope_cos_sin(pos, u, rope_dim, rope_base, &cs, &sn);
+      rope_cos_sin(pos, u, rope, &cs, &sn);
       const float other = row[j ^ 1] * rinv * (gamma ? gamma[j ^ 1] : 1.f);
       v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
     }
@@ -142,6 +166,7 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
 }
 
 int launch_compress(const CompressArgs& a, hipStream_t st) {
+  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const int ncand_max = a.overlap ? 2 * a.m : a.m;
   int G = ncand_max < COMP_MAX_G ? ncand_max : COMP_MAX_G;
   if (G < 1) G = 1;
@@ -157,7 +182,7 @@ int launch_compress(const CompressArgs& a, hipStream_t st) {
       return -1;                                                                                   \
     hipLaunchKernelGGL(kfn, grid, block, lds, st, a.C_a, a.Z_a, a.C_b, a.Z_b, a.in_bs, a.tok_base, \
                        a.T, a.c, a.m, a.overlap, a.s_begin, G, a.gamma, a.eps, a.rope_dim,         \
-                       a.rope_base, a.pos_stride, a.pos_offset, a.E, a.E_scale, a.out_bs,          \
+                       rope_rr, a.pos_stride, a.pos_offset, a.E, a.E_scale, a.out_bs,          \
                        a.out_ring);                                                                \
   } while (0)
   if (a.in_dtype == DT_F32) {

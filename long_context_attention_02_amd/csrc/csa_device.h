@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 
 namespace csa {
 
@@ -75,25 +76,48 @@ __device__ __forceinline__ void store_from_f32(void* p, size_t i, float v) {
   else ((uint16_t*)p)[i] = f32_to_bf16_bits(v);
 }
 
-// ---- RoPE angle, computed in fp64 so that positions up to 2^31 keep full
-// fp32 accuracy in cos / sin (an fp32 product p * theta loses ~p * 2^-24 rad).
-// The angle is reduced modulo 2*pi with a two-part constant (Cody-Waite, with FMA
-// the product k * hi is exact for |k| < 2^29) before sincos, which keeps the
-// library on its short-argument path for positions up to 2^31.
-__device__ __forceinline__ void rope_cos_sin(long long pos, int u, int rope_dim, float base,
-                                             float* c, float* s) {
+// ---- RoPE angle.  theta_u = base^(-2u/rope_dim) = r^u with r = base^(-2/rope_dim):
+// the host supplies r in fp64 and the relative rounding error of r (RopeRatio,
+// from an 80-bit power), the device raises r to u by square-and-multiply and
+// removes r's own error amplified u-fold, leaving ~2 log2(u) roundings (about
+// 1e-15 relative).  The angle p * theta_u is formed and reduced modulo 2*pi in
+// fp64 (Cody-Waite with a two-part constant; with FMA k * hi is exact for
+// |k| < 2^29), so the angle error stays below 2e-8 rad for positions up to
+// 2^24 and below 3e-6 rad up to 2^31; cos and sin of the reduced angle
+// (|r| <= pi) are taken in fp32, a few 1e-8 from exact.  All of it is a few
+// dozen instructions: a library pow and sincos in fp64 cost ~2k cycles of
+// latency and most of a kernel's registers where this sits on a short path.
+struct RopeRatio {
+  double r;     // base^(-2 / rope_dim), rounded
+  double rel;   // (exact - r) / r
+};
+
+// (host) the ratio for rope_dim and base, from an 80-bit power
+static inline RopeRatio rope_ratio(int rope_dim, float base) {
+  if (rope_dim <= 0) return RopeRatio{1.0, 0.0};
+  const long double rl = powl((long double)base, -2.0L / (long double)rope_dim);
+  const double r = (double)rl;
+  return RopeRatio{r, (double)((rl - (long double)r) / (long double)r)};
+}
+
+__device__ __forceinline__ void rope_cos_sin(long long pos, int u, RopeRatio rr, float* c, float* s) {
   const double kTwoPiHi = 6.283185307179586;          // nearest double to 2*pi
   const double kTwoPiLo = 2.4492935982947064e-16;      // 2*pi - kTwoPiHi
   const double kInvTwoPi = 0.15915494309189535;
-  const double theta = pow((double)base, -2.0 * (double)u / (double)rope_dim);
+  double t = 1.0, p = rr.r;
+  for (int e = u; e > 0; e >>= 1) {
+    if (e & 1) t *= p;
+    p *= p;
+  }
+  const double theta = fma(t, (double)u * rr.rel, t);   // r^u (1 + u rel)
   const double ang = (double)pos * theta;
   const double k = rint(ang * kInvTwoPi);
   double r = fma(-k, kTwoPiHi, ang);
   r = fma(-k, kTwoPiLo, r);
-  double sn, cs;
-  sincos(r, &sn, &cs);
-  *c = (float)cs;
-  *s = (float)sn;
+  float sn, cs;
+  sincosf((float)r, &sn, &cs);
+  *c = cs;
+  *s = sn;
 }
 
 // ---- wave / block reductions ------------------------------------------------

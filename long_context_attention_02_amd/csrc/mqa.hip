@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void mqa_valu_kernel(
     const void* __restrict__ q, const float* __restrict__ gamma_q, float eps, const void* __restrict__ E,
     long long N_cap, const int* __restrict__ idx, int k, int m, const void* __restrict__ W, int W_cap,
     int n_win, const float* __restrict__ sink, const int* __restrict__ q_pos, int Tq, int n_h, int d,
-    int rope_dim, float rope_base, float scale, void* __restrict__ out) {
+    int rope_dim, RopeRatio rope, float scale, void* __restrict__ out) {
   extern __shared__ float sm[];
   float* qh = sm;                                  // [d]
   float* red = qh + d;                             // [4]
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void mqa_valu_kernel(
   for (int u = threadIdx.x; u < rope_dim / 2; u += blockDim.x) {
     const int j0 = d - rope_dim + 2 * u;
     float cs, sn;
-    rope_cos_sin(i, u, rope_dim, rope_base, &cs, &sn);
+    rope_cos_sin(i, u, rope, &cs, &sn);
     const float x0 = qh[j0], x1 = qh[j0 + 1];
     qh[j0] = x0 * cs - x1 * sn;
     qh[j0 + 1] = x0 * sn + x1 * cs;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(256) void mqa_valu_kernel(
     if (j >= d - rope_dim) {
       const int u = (j - (d - rope_dim)) >> 1;
       float cs, sn;
-      rope_cos_sin(-i, u, rope_dim, rope_base, &cs, &sn);
+      rope_cos_sin(-i, u, rope, &cs, &sn);
       const float other = qh[j ^ 1];
       v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
     }
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
-    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
     int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
   constexpr int KS = D / 32;          // 8-dim chunks per lane group (S^T K-steps)
   constexpr int GW = D / 4;           // dims per lane group
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
   const int hq = wact ? h0 + j : 0;
 
   for (int u = threadIdx.x; u < rope_dim / 2; u += 256)
-    rope_cos_sin(i, u, rope_dim, rope_base, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
+    rope_cos_sin(i, u, rope, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
 
   const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
   const int* idx_row = DENSE ? nullptr : idx + row * (size_t)k;
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
-    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
     int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
   constexpr int KS = D / 32, GW = D / 4, RB = D * 2, CPR = RB / 16, RPI = 64 / CPR;
   constexpr int NKT = MQ_GROUP / 16;   // key tiles (8)
@@ -487,7 +487,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
   const uint16_t* dummy = E + (size_t)b * (size_t)N_cap * D;
 
   for (int u = threadIdx.x; u < rope_dim / 2; u += 256)
-    rope_cos_sin(i, u, rope_dim, rope_base, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
+    rope_cos_sin(i, u, rope, &rope_cs[2 * u], &rope_cs[2 * u + 1]);
   if (threadIdx.x < MQ_GROUP) {
     const uint16_t* p = nullptr;
     if (threadIdx.x < nrows) {
@@ -835,7 +835,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
-    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, float rope_base, float scale,
+    const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
     int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
   constexpr int HTW = dec_htw<D>();   // head tiles per wave
   constexpr int KS = D / 32;          // S^T K-steps (8 dims per lane each)
@@ -901,7 +901,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
     const int u = t - (D - rope_dim) / 2;
     float cs = 1.f, sn = 0.f;
-    if (u >= 0) rope_cos_sin(i, u, rope_dim, rope_base, &cs, &sn);
+    if (u >= 0) rope_cos_sin(i, u, rope, &cs, &sn);
     rope_cs[2 * t] = cs;
     rope_cs[2 * t + 1] = sn;
   }
@@ -1145,7 +1145,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 // with a running maximum; each thread owns one pair of output dims
 __global__ __launch_bounds__(256) void mqa_combine_kernel(
     const float* __restrict__ ws, const float* __restrict__ sink, const int* __restrict__ q_pos,
-    int Tq, int n_h, int D, int n_split, int rope_dim, float rope_base, uint16_t* __restrict__ out) {
+    int Tq, int n_h, int D, int n_split, int rope_dim, RopeRatio rope, uint16_t* __restrict__ out) {
+  constexpr int CB = 8;   // splits whose partials are loaded in one batch
   const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const size_t row = (size_t)b * Tq + t;
   const long long i = q_pos[row];
@@ -1153,30 +1154,58 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const float* base = ws + (row * n_split * (size_t)n_h + h) * (D + 2);
   const size_t sstride = (size_t)n_h * (D + 2);
   const int rbeg = D - rope_dim;
-  float M = sig;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * sstride + D]);
-  float Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float ms = base[s * sstride + D];
-    if (ms != -INFINITY) Z += base[s * sstride + D + 1] * __expf(ms - M);
-  }
   for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
     const int d0 = 2 * u;
-    float o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-    for (int s = 0; s < n_split; ++s) {
-      const float* ps = base + s * sstride;
-      const float ms = ps[D];
-      const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-      o0 += ps[d0] * f;
-      o1 += ps[d0 + 1] * f;
+    float M = sig, Z, o0 = 0.f, o1 = 0.f;
+    if (n_split <= CB) {
+      // every split's (max, sum) and this pair of its output, all in flight at once
+      float ms[CB], ls[CB], a0[CB], a1[CB];
+#pragma unroll
+      for (int s = 0; s < CB; ++s) {
+        if (s < n_split) {
+          const float* ps = base + s * sstride;
+          ms[s] = ps[D];
+          ls[s] = ps[D + 1];
+          a0[s] = ps[d0];
+          a1[s] = ps[d0 + 1];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < CB; ++s)
+        if (s < n_split) M = fmaxf(M, ms[s]);
+      Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
+#pragma unroll
+      for (int s = 0; s < CB; ++s)
+        if (s < n_split && ms[s] != -INFINITY) Z += ls[s] * __expf(ms[s] - M);
+#pragma unroll
+      for (int s = 0; s < CB; ++s) {
+        if (s < n_split) {
+          const float f = (ms[s] == -INFINITY) ? 0.f : __expf(ms[s] - M);
+          o0 += a0[s] * f;
+          o1 += a1[s] * f;
+        }
+      }
+    } else {
+      for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * sstride + D]);
+      Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
+      for (int s = 0; s < n_split; ++s) {
+        const float ms = base[s * sstride + D];
+        if (ms != -INFINITY) Z += base[s * sstride + D + 1] * __expf(ms - M);
+      }
+      for (int s = 0; s < n_split; ++s) {
+        const float* ps = base + s * sstride;
+        const float ms = ps[D];
+        const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
+        o0 += ps[d0] * f;
+        o1 += ps[d0 + 1] * f;
+      }
     }
     const float inv = Z > 0.f ? 1.f / Z : 0.f;
     o0 *= inv;
     o1 *= inv;
     if (d0 >= rbeg) {
       float cs, sn;
-      rope_cos_sin(-i, (d0 - rbeg) >> 1, rope_dim, rope_base, &cs, &sn);
+      rope_cos_sin(-i, (d0 - rbeg) >> 1, rope, &cs, &sn);
       const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
       o0 = r0;
       o1 = r1;
@@ -1230,6 +1259,7 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
 
 template <int D, bool DENSE, bool MULTI>
 static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
+  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const int n_hg = (a.n_h + 63) / 64;
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
@@ -1240,16 +1270,17 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(256), lds, st,
                      (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
-                     a.rope_dim, a.rope_base, a.scale, kps, n_split, units, (uint16_t*)a.out,
+                     a.rope_dim, rope_rr, a.scale, kps, n_split, units, (uint16_t*)a.out,
                      (float*)a.ws);
   if (n_split > 1)
     hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
                        dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
-                       n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
+                       n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
 }
 
 template <int D, bool DENSE, int NW>
 static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
+  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const int n_hg = a.n_h / (16 * dec_htw<D>() * NW);
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
@@ -1260,12 +1291,12 @@ static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
                      (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
-                     a.rope_dim, a.rope_base, a.scale, n_split, units, (uint16_t*)a.out,
+                     a.rope_dim, rope_rr, a.scale, n_split, units, (uint16_t*)a.out,
                      (float*)a.ws);
   if (n_split > 1)
     hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
                        dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
-                       n_split, a.rope_dim, a.rope_base, (uint16_t*)a.out);
+                       n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
 }
 
 // waves per workgroup: as many head groups of one wave as divide n_h, up to four
@@ -1285,6 +1316,7 @@ static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st
 }
 
 int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
+  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const bool dense = a.idx == nullptr;
   const long long slots_max = mqa_slots_max(a);
   if (mqa_mfma_ok(a)) {
@@ -1320,7 +1352,7 @@ int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
     }                                                                                               \
     hipLaunchKernelGGL(kfn, grid, dim3(256), lds, st, a.q, a.gamma_q, a.eps, a.E, a.N_cap, a.idx, \
                        a.k, a.m, a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h, a.d,          \
-                       a.rope_dim, a.rope_base, a.scale, a.out);                                    \
+                       a.rope_dim, rope_rr, a.scale, a.out);                                    \
   } while (0)
     if (a.dtype == DT_F32) {
       if (dense) CSA_MQA_VALU(DT_F32, true); else CSA_MQA_VALU(DT_F32, false);

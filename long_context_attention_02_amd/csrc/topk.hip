@@ -11,7 +11,7 @@
 // MSD radix select finds the threshold: 10-bit digits of the 32-bit score key
 // first (LDS histograms, the digit located by one wave), and only when the k-th
 // score is tied, further digits of the index half among the tied elements.
-// One pass collects the k keys (one atomic per wave) and a bitonic sort orders
+// One pass collects the k keys (one atomic per wave and group) and a bitonic sort orders
 // them (lane shuffles for partners within a wave, LDS beyond).  No
 // atomic decides anything but the slot an element lands in before the sort,
 // so results are deterministic.
@@ -33,6 +33,7 @@ static constexpr int TK_BINS = 1024;      // 10-bit digits
 static constexpr int TK_LDS_BYTES = 128 * 1024;           // element cache per workgroup
 static constexpr int TK_CACHE32 = TK_LDS_BYTES / 4;       // score rows cached as ord keys
 static constexpr int TK_CACHE64 = TK_LDS_BYTES / 8;       // K64 candidate lists
+static constexpr int TK_LDU = 8;                          // global loads in flight per thread when caching
 
 // Element sources: hi = ord(score), lo = 0xFFFFFFFF - index.  load<V>(e0)
 // gives elements e0 .. e0 + V - 1 (V per thread and pass); sources held in LDS
@@ -350,32 +351,16 @@ __device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint
     all_eq_hi = true;
     thr_hi = 0u;
   }
-  // collect every selected key (exactly `want` of them): each wave counts its
-  // selected elements, the waves' ranges follow in wave order, and lanes take
-  // their slots in ballot order (the slot only decides placement before the sort)
-  const int lane = tid & 63, wid = tid >> 6;
+  // collect every selected key (exactly `want` of them) in one pass: per
+  // group of V elements a wave takes one range of slots with one LDS atomic
+  // and its lanes fill it in ballot order.  The slot only decides where an
+  // element sits before the sort (or before the merge's own exact selection),
+  // so the result does not depend on the order in which waves get ranges.
+  const int lane = tid & 63;
   const long long step = (long long)V * TK_THREADS;
   const bool by_lo = !all_eq_hi;
-  int mine = 0;
-  for (long long g0 = 0; g0 < n; g0 += step) {
-    const long long e0 = g0 + (long long)V * tid;
-    uint32_t h[V] = {}, l[V] = {};
-    int rem = 0;
-    if (e0 < n) {
-      src.load(e0, h, l);
-      rem = (int)min(n - e0, (long long)V);
-    }
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const bool sel = by_lo ? ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo))) : (h[v] >= thr_hi);
-      const bool take = (v < rem) & (h[v] >= lb) & sel;
-      mine += __popcll(__ballot(take));
-    }
-  }
-  if (lane == 0) sh.wcount[wid] = mine;
+  if (tid == 0) sh.count = 0;
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += sh.wcount[w];
   const uint64_t below = (1ull << lane) - 1ull;
   for (long long g0 = 0; g0 < n; g0 += step) {
     const long long e0 = g0 + (long long)V * tid;
@@ -385,14 +370,26 @@ __device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint
       src.load(e0, h, l);
       rem = (int)min(n - e0, (long long)V);
     }
+    bool take[V];
+    uint64_t bal[V];
+    int tot = 0;
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const bool sel = by_lo ? ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo))) : (h[v] >= thr_hi);
-      const bool take = (v < rem) & (h[v] >= lb) & sel;
-      const uint64_t bal = __ballot(take);
-      const int slot = base + __popcll(bal & below);
-      if (take && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
-      base += __popcll(bal);
+      take[v] = (v < rem) & (h[v] >= lb) & sel;
+      bal[v] = __ballot(take[v]);
+      tot += __popcll(bal[v]);
+    }
+    if (tot != 0) {   // wave-uniform
+      int off = 0;
+      if (lane == 0) off = atomicAdd(&sh.count, tot);
+      off = __builtin_amdgcn_readfirstlane(off);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int slot = off + __popcll(bal[v] & below);
+        if (take[v] && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
+        off += __popcll(bal[v]);
+      }
     }
   }
   __syncthreads();
@@ -415,13 +412,26 @@ __device__ int select_row(const float* __restrict__ p, long long n, long long ba
   uint32_t a = ~0u, o = 0u, lmax = ~0u;
   if (use_cache) {
     const long long n4 = (((uintptr_t)p & 15u) == 0) ? (n & ~3LL) : 0;   // vector part if aligned
-    for (long long e = 4LL * threadIdx.x; e < n4; e += 4LL * TK_THREADS) {
-      const f32x4_t v = *(const f32x4_t*)(p + e);
-      u32x4_t ok;
-      ok[0] = ord_key(v[0]); ok[1] = ord_key(v[1]); ok[2] = ord_key(v[2]); ok[3] = ord_key(v[3]);
-      *(u32x4_t*)(cache + e) = ok;
-      const uint32_t m4 = max(max(ok[0], ok[1]), max(ok[2], ok[3]));
-      lmax = lmax == ~0u ? m4 : max(lmax, m4);
+    // TK_LDU loads in flight per thread before any is used (one at a time, the
+    // copy would take one memory latency per iteration)
+    for (long long e = 4LL * threadIdx.x; e < n4; e += 4LL * TK_THREADS * TK_LDU) {
+      f32x4_t v[TK_LDU];
+#pragma unroll
+      for (int u = 0; u < TK_LDU; ++u) {
+        const long long eu = e + 4LL * TK_THREADS * u;
+        if (eu < n4) v[u] = *(const f32x4_t*)(p + eu);
+      }
+#pragma unroll
+      for (int u = 0; u < TK_LDU; ++u) {
+        const long long eu = e + 4LL * TK_THREADS * u;
+        if (eu < n4) {
+          u32x4_t ok;
+          ok[0] = ord_key(v[u][0]); ok[1] = ord_key(v[u][1]); ok[2] = ord_key(v[u][2]); ok[3] = ord_key(v[u][3]);
+          *(u32x4_t*)(cache + eu) = ok;
+          const uint32_t m4 = max(max(ok[0], ok[1]), max(ok[2], ok[3]));
+          lmax = lmax == ~0u ? m4 : max(lmax, m4);
+        }
+      }
     }
     for (long long e = n4 + threadIdx.x; e < n; e += TK_THREADS) {
       const uint32_t ok = ord_key(p[e]);
@@ -515,11 +525,22 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
     uint32_t lmax = ~0u;
     if ((ncand & 1) == 0) {   // rows start 16-byte aligned: two keys per load
       typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
-      for (long long e = 2LL * threadIdx.x; e < ncand; e += 2LL * TK_THREADS) {
-        const u64x2_t kk = *(const u64x2_t*)(cp + e);
-        *(u64x2_t*)(cache64 + e) = kk;
-        const uint32_t m2 = max((uint32_t)(kk[0] >> 32), (uint32_t)(kk[1] >> 32));
-        lmax = lmax == ~0u ? m2 : max(lmax, m2);
+      for (long long e = 2LL * threadIdx.x; e < ncand; e += 2LL * TK_THREADS * TK_LDU) {
+        u64x2_t kk[TK_LDU];
+#pragma unroll
+        for (int u = 0; u < TK_LDU; ++u) {
+          const long long eu = e + 2LL * TK_THREADS * u;
+          if (eu < ncand) kk[u] = *(const u64x2_t*)(cp + eu);
+        }
+#pragma unroll
+        for (int u = 0; u < TK_LDU; ++u) {
+          const long long eu = e + 2LL * TK_THREADS * u;
+          if (eu < ncand) {
+            *(u64x2_t*)(cache64 + eu) = kk[u];
+            const uint32_t m2 = max((uint32_t)(kk[u][0] >> 32), (uint32_t)(kk[u][1] >> 32));
+            lmax = lmax == ~0u ? m2 : max(lmax, m2);
+          }
+        }
       }
     } else {
       for (long long e = threadIdx.x; e < ncand; e += TK_THREADS) {
