@@ -10,8 +10,10 @@ key), indexer score, top-k, sparse MQA.  Inputs are synthetic (seeded N(0,1),
 U(0,1) head weights) and resident in HBM before timing starts.
 
 Prints ONE JSON line.  Also reported: the prefill indexer (16,384 queries x
-32,768 entries, 64 heads x 128, bf16) in TFLOP/s, and the fp64 oracle timed on
-a bounded sample of the decode workload on the host cores.
+32,768 entries, 64 heads x 128, bf16) in TFLOP/s; the HCA dense decode (4
+sequences x 8,192 entries) and each call of the chunked-prefill step, each
+against its roofline; and the fp64 oracle timed on a bounded sample of the
+decode workload on the host cores.
 """
 from __future__ import annotations
 
@@ -36,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the HCA decode and prefill-step measurements")
     ap.add_argument("--cpu-sample", type=int, default=16, help="sequences the oracle runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (3x) to calibrate HBM byte counters")
@@ -113,6 +117,84 @@ def prefill_indexer(steps: int, warmup: int):
                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}}
 
 
+def _timed(fn, steps: int, warmup: int) -> float:
+    """Average ms of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def _roof(achieved: float, bound: str) -> dict:
+    peak, unit = (HBM_PEAK_GBS, "GB/s") if bound == "hbm" else (MFMA_BF16_PEAK_TFS, "TFLOP/s")
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
+
+
+def hca_decode(steps: int, warmup: int):
+    """Dense MQA (HCA) decode: 4 sequences over 8,192 entries of 128 tokens each (1M
+    context) plus window and sink; the step also recompresses the newest block."""
+    import torch
+
+    from long_context_attention_02_amd.pipeline import HCADecode
+    from synth.workloads import HCA_DECODE as wl
+
+    run = HCADecode(wl, "cuda", keep_raw=False)
+    step_ms = _timed(run.step, steps, warmup)
+    attn_ms = _timed(run.attend, steps, warmup)
+    n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
+    rows = wl.B * (n_vis + wl.n_win)
+    attn_bytes = rows * wl.d * 2 + 2 * wl.B * wl.n_h * wl.d * 2          # rows read; q and out
+    attn_flops = 4.0 * wl.B * wl.n_h * (n_vis + wl.n_win) * wl.d
+    del run
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "step_ms": round(step_ms, 5), "tokens/s": round(wl.B / (step_ms * 1e-3), 1),
+            "hca_dense_mqa_ms": round(attn_ms, 5), "algorithmic_bytes": attn_bytes,
+            "flops": attn_flops, "TFLOP/s": round(attn_flops / (attn_ms * 1e-3) / 1e12, 2),
+            "roofline": _roof(attn_bytes / (attn_ms * 1e-3) / 1e9, "hbm")}
+
+
+def prefill_rows(steps: int, warmup: int):
+    """The chunked-prefill step (16,384 queries over 32,768 entries, k = 1024) call by
+    call: compression of the chunk, indexer, top-k and sparse MQA."""
+    import torch
+
+    from long_context_attention_02_amd.pipeline import CSAPrefill
+    from synth.workloads import CSA_PREFILL_PRO as wl
+
+    run = CSAPrefill(wl, "cuda", keep_raw=False)
+    ms = {"compress": _timed(run.compress_new, steps, warmup), "index": _timed(run.index, steps, warmup),
+          "topk": _timed(run.select, steps, warmup), "sparse_mqa": _timed(run.attend, steps, warmup)}
+    n_new = run.s_new1 - run.s_new0
+    n_vis = [min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq)]
+    # compress: window rows (read + write), candidates of the new KV entries and indexer keys
+    # (C and Z of sets a and b, 2 * 2m rows each), entries written
+    comp_bytes = (2 * wl.B * wl.Tq * wl.d * 2 + wl.B * n_new * (4 * wl.m * (wl.d + wl.d_I) * 2
+                                                                + (wl.d + wl.d_I) * 2))
+    topk_bytes = 4 * wl.B * sum(n_vis) + 4 * wl.B * wl.Tq * wl.k
+    attn_flops = 4.0 * wl.B * wl.Tq * wl.n_h * (wl.k + wl.n_win) * wl.d
+    index_flops = 2.0 * wl.B * sum(n_vis) * wl.H_I * wl.d_I
+    out = {"workload": wl.name, "ms": {k: round(v, 4) for k, v in ms.items()},
+           "compress": {"algorithmic_bytes": comp_bytes,
+                        "roofline": _roof(comp_bytes / (ms["compress"] * 1e-3) / 1e9, "hbm")},
+           "index": {"flops": index_flops,
+                     "roofline": _roof(index_flops / (ms["index"] * 1e-3) / 1e12, "mfma")},
+           "topk": {"algorithmic_bytes": topk_bytes,
+                    "roofline": _roof(topk_bytes / (ms["topk"] * 1e-3) / 1e9, "hbm")},
+           "sparse_mqa": {"flops": attn_flops,
+                          "roofline": _roof(attn_flops / (ms["sparse_mqa"] * 1e-3) / 1e12, "mfma")}}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -187,6 +269,12 @@ def main():
         del run.I
         torch.cuda.empty_cache()
         result["prefill_indexer"] = prefill_indexer(steps=10, warmup=3)
+    if not args.no_secondary:
+        if hasattr(run, "I"):
+            del run.I
+        torch.cuda.empty_cache()
+        result["hca_decode"] = hca_decode(steps=20, warmup=5)
+        result["prefill_step"] = prefill_rows(steps=3, warmup=1)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(run, args.cpu_sample)
     print(json.dumps(result))
