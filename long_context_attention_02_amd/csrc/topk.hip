@@ -304,6 +304,84 @@ __device__ void sort_desc_lds(TopkShared& sh, int P) {
   __syncthreads();
 }
 
+// Collection of the selected keys into sh.buf (sh.count = 0 on entry).  Lanes
+// of a wave take consecutive slots of the range the wave claimed, by ballot
+// rank (mbcnt); the range is claimed once per group of V elements.
+template <class Src>
+__device__ __forceinline__ void collect_group(const uint32_t (&h)[Src::V], const uint32_t (&l)[Src::V],
+                                              const bool (&take)[Src::V], TopkShared& sh) {
+  constexpr int V = Src::V;
+  uint64_t bal[V];
+  int tot = 0;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    bal[v] = __ballot(take[v]);
+    tot += __popcll(bal[v]);
+  }
+  if (tot == 0) return;   // wave-uniform
+  int off = 0;
+  if ((threadIdx.x & 63) == 0) off = atomicAdd(&sh.count, tot);
+  off = __builtin_amdgcn_readfirstlane(off);
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int slot = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[v] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal[v], 0u));
+    if (take[v] && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
+    off += __popcll(bal[v]);
+  }
+}
+
+// every element with hi >= t (no tie to resolve)
+template <class Src>
+__device__ void collect_ge(const Src& src, long long n, uint32_t t, TopkShared& sh) {
+  constexpr int V = Src::V;
+  const long long step = (long long)V * TK_THREADS;
+  const long long nfull = (n / step) * step;
+  for (long long g0 = 0; g0 < nfull; g0 += step) {   // whole groups: no bounds tests
+    uint32_t h[V], l[V];
+    src.load(g0 + (long long)V * threadIdx.x, h, l);
+    bool take[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) take[v] = h[v] >= t;
+    collect_group<Src>(h, l, take, sh);
+  }
+  if (nfull < n) {
+    const long long e0 = nfull + (long long)V * threadIdx.x;
+    uint32_t h[V] = {}, l[V] = {};
+    int rem = 0;
+    if (e0 < n) {
+      src.load(e0, h, l);
+      rem = (int)min(n - e0, (long long)V);
+    }
+    bool take[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) take[v] = (v < rem) & (h[v] >= t);
+    collect_group<Src>(h, l, take, sh);
+  }
+}
+
+// hi > thr_hi, plus hi == thr_hi with lo >= thr_lo (the k-th score is tied)
+template <class Src>
+__device__ void collect_tied(const Src& src, long long n, uint32_t lb, uint32_t thr_hi, uint32_t thr_lo,
+                             TopkShared& sh) {
+  constexpr int V = Src::V;
+  const long long step = (long long)V * TK_THREADS;
+  for (long long g0 = 0; g0 < n; g0 += step) {
+    const long long e0 = g0 + (long long)V * threadIdx.x;
+    uint32_t h[V] = {}, l[V] = {};
+    int rem = 0;
+    if (e0 < n) {
+      src.load(e0, h, l);
+      rem = (int)min(n - e0, (long long)V);
+    }
+    bool take[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      take[v] = (v < rem) & (h[v] >= lb) & ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo)));
+    collect_group<Src>(h, l, take, sh);
+  }
+}
+
 // k largest K64 = hi << 32 | lo among n elements -> sh.buf[0 .. min(k, n)), sorted
 // descending when SORT.  Only elements with hi >= lb take part (lb from
 // block_lower_bound, which keeps at least min(k, n) of them); hi_and / hi_or:
@@ -356,42 +434,10 @@ __device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint
   // and its lanes fill it in ballot order.  The slot only decides where an
   // element sits before the sort (or before the merge's own exact selection),
   // so the result does not depend on the order in which waves get ranges.
-  const int lane = tid & 63;
-  const long long step = (long long)V * TK_THREADS;
-  const bool by_lo = !all_eq_hi;
   if (tid == 0) sh.count = 0;
   __syncthreads();
-  const uint64_t below = (1ull << lane) - 1ull;
-  for (long long g0 = 0; g0 < n; g0 += step) {
-    const long long e0 = g0 + (long long)V * tid;
-    uint32_t h[V] = {}, l[V] = {};
-    int rem = 0;
-    if (e0 < n) {
-      src.load(e0, h, l);
-      rem = (int)min(n - e0, (long long)V);
-    }
-    bool take[V];
-    uint64_t bal[V];
-    int tot = 0;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const bool sel = by_lo ? ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo))) : (h[v] >= thr_hi);
-      take[v] = (v < rem) & (h[v] >= lb) & sel;
-      bal[v] = __ballot(take[v]);
-      tot += __popcll(bal[v]);
-    }
-    if (tot != 0) {   // wave-uniform
-      int off = 0;
-      if (lane == 0) off = atomicAdd(&sh.count, tot);
-      off = __builtin_amdgcn_readfirstlane(off);
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int slot = off + __popcll(bal[v] & below);
-        if (take[v] && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
-        off += __popcll(bal[v]);
-      }
-    }
-  }
+  if (all_eq_hi) collect_ge(src, n, max(thr_hi, lb), sh);   // (the radix only counted hi >= lb)
+  else collect_tied(src, n, lb, thr_hi, thr_lo, sh);
   __syncthreads();
   if (SORT) {
     int P = 1;
