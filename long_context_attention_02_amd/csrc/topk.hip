@@ -20,7 +20,7 @@
 // the block forms the AND and the OR of all score keys, so the bits every key
 // shares are skipped and the digits start at the highest bit that differs.
 // Long rows with few queries (decode) run in two stages: workgroups select
-// the top-k of chunks of 32k elements (any global top-k element is in its
+// the top-k of chunks of 16 k elements (any global top-k element is in its
 // chunk's top-k), then one workgroup per row selects from their union.
 #include "csa_device.h"
 #include "csa_internal.h"
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 }
 
 static bool topk_two_stage(long long rows, long long N_cap, int k, long long* chunk, int* nchunks) {
-  const long long ch = 32LL * k;
+  const long long ch = 16LL * k;
   if (rows >= 512 || N_cap < 2 * ch) return false;
   *chunk = ch;
   *nchunks = (int)((N_cap + ch - 1) / ch);

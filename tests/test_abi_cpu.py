@@ -105,7 +105,7 @@ def test_topk_validation_and_workspace(lib):
     assert call(k=0) == CSA_E_SHAPE
     assert call(k=2049) == CSA_E_SHAPE
     need = lib.csa_topk_workspace_size(16, 1, 262144, 1024)
-    assert need == 16 * 8 * 1024 * 8                          # 8 chunks of 32k per row
+    assert need == 16 * 16 * 1024 * 8                         # 16 chunks of 16k per row
     assert lib.csa_topk_workspace_size(1, 16384, 32768, 1024) == 0
     assert call(k=1024, N=262144, B=16, wsb=need - 1, ws=FAKE) == CSA_E_WORKSPACE
     assert call(k=1024, N=262144, B=16) == CSA_E_WORKSPACE
