@@ -126,7 +126,7 @@ __device__ __forceinline__ float score_column(const IdxFrags<QH, KS>& f, const b
 #pragma unroll
   for (int mt = 0; mt < QH; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) part += f.wv[mt][r] * fmaxf(acc[mt][r], 0.f);
+    for (int r = 0; r < 4; ++r) part += f.wv[mt][r] * __int_as_float(max(__float_as_int(acc[mt][r]), 0));   // ReLU
   part += __shfl_xor(part, 16, 64);
   part += __shfl_xor(part, 32, 64);
   return part;
@@ -491,9 +491,12 @@ __global__ __launch_bounds__(256) void index_mfma_prefill(
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][PF_TK * ROWB];
   __shared__ float ksc[2][PF_TK];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane: a wave's query rows, their visible
+  // counts and output rows are then scalar (registers are what bound occupancy here)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
   const int b = blockIdx.y;
+  const int ncap = (int)N_cap;   // < 2^31 (the entry point checks)
   const int t0 = blockIdx.x * (4 * QPW);
 
   // visible range of the whole workgroup
@@ -505,15 +508,17 @@ __global__ __launch_bounds__(256) void index_mfma_prefill(
   const long long ntiles = (kend + PF_TK - 1) / PF_TK;
 
   IdxFrags<QH, KS> f[QPW];
-  long long nvis[QPW];
+  int nvis[QPW];
   bool tok[QPW];
+  float* orow[QPW];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     const int t = t0 + wave * QPW + qq;
     tok[qq] = t < Tq;
     const size_t qrow = (size_t)b * Tq + (tok[qq] ? t : t0);
     load_query_frags<QH, KS>(f[qq], q + qrow * (size_t)(H * DI), w + qrow * H, g, j);
-    nvis[qq] = min(N_cap, ((long long)q_pos[qrow] + 1) / m);
+    nvis[qq] = (int)min(N_cap, ((long long)q_pos[qrow] + 1) / m);
+    orow[qq] = out + qrow * (size_t)N_cap;
   }
   const size_t kbase = (size_t)b * (size_t)N_cap;
 
@@ -571,14 +576,13 @@ __global__ __launch_bounds__(256) void index_mfma_prefill(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         Bf[ks] = *(const bf16x8_t*)(&kt[buf][(16 * st + j) * ROWB + (GW * g + 8 * ks) * 2]);
-      const long long key = tile * PF_TK + 16 * st + j;
+      const int key = (int)tile * PF_TK + 16 * st + j;
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         float v = score_column<QH, KS>(f[qq], Bf);
-        if (g == 0 && tok[qq] && key < N_cap) {
+        if (g == 0 && tok[qq] && key < ncap) {
           if constexpr (KDT == DT_FP8) v *= ksc[buf][16 * st + j];
-          const int t = t0 + wave * QPW + qq;
-          out[((size_t)b * Tq + t) * (size_t)N_cap + key] = key < nvis[qq] ? v : -INFINITY;
+          orow[qq][key] = key < nvis[qq] ? v : -INFINITY;
         }
       }
     }
@@ -589,9 +593,7 @@ __global__ __launch_bounds__(256) void index_mfma_prefill(
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     if (!tok[qq]) continue;
-    const int t = t0 + wave * QPW + qq;
-    float* orow = out + ((size_t)b * Tq + t) * (size_t)N_cap;
-    for (long long key = ntiles * PF_TK + lane; key < N_cap; key += 64) orow[key] = -INFINITY;
+    for (long long key = ntiles * PF_TK + lane; key < N_cap; key += 64) orow[qq][key] = -INFINITY;
   }
 }
 
