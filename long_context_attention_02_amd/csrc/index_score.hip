@@ -111,9 +111,10 @@ __device__ __forceinline__ void load_query_frags(IdxFrags<QH, KS>& f, const uint
   }
 }
 
-// sum over heads of w * ReLU(dot) for the key column of this lane, complete in every lane
+// this lane's share (its 4 QH head rows) of sum_h w * ReLU(dot) for its key
+// column; reduce_scatter4 completes four of them
 template <int QH, int KS>
-__device__ __forceinline__ float score_column(const IdxFrags<QH, KS>& f, const bf16x8_t (&Bf)[KS]) {
+__device__ __forceinline__ float partial_column(const IdxFrags<QH, KS>& f, const bf16x8_t (&Bf)[KS]) {
   f32x4_t acc[QH];
 #pragma unroll
   for (int mt = 0; mt < QH; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -127,8 +128,6 @@ __device__ __forceinline__ float score_column(const IdxFrags<QH, KS>& f, const b
   for (int mt = 0; mt < QH; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) part += f.wv[mt][r] * __int_as_float(max(__float_as_int(acc[mt][r]), 0));   // ReLU
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
   return part;
 }
 
@@ -570,20 +569,31 @@ __global__ __launch_bounds__(256) void index_mfma_prefill(
   for (long long tile = 0; tile < ntiles; ++tile) {
     const int buf = (int)(tile & 1);
     if (tile + 1 < ntiles) gload(tile + 1);
+    // per query, the lanes' shares of the tile's four subtiles, then one
+    // reduce-scatter leaves lane (g, j) with key 16 g + j: a 256-byte store
+    static_assert(PF_TK == 64, "four subtiles per tile");
+    float P[QPW][4];
 #pragma unroll
-    for (int st = 0; st < PF_TK / 16; ++st) {
+    for (int st = 0; st < 4; ++st) {
       bf16x8_t Bf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         Bf[ks] = *(const bf16x8_t*)(&kt[buf][(16 * st + j) * ROWB + (GW * g + 8 * ks) * 2]);
-      const int key = (int)tile * PF_TK + 16 * st + j;
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
-        float v = score_column<QH, KS>(f[qq], Bf);
-        if (g == 0 && tok[qq] && key < ncap) {
-          if constexpr (KDT == DT_FP8) v *= ksc[buf][16 * st + j];
-          orow[qq][key] = key < nvis[qq] ? v : -INFINITY;
-        }
+        P[qq][st] = partial_column<QH, KS>(f[qq], Bf);
+        // materialised here, so the epilogue is not sunk below later subtiles
+        // (which would keep their accumulators live: too many registers)
+        asm volatile("" : "+v"(P[qq][st]));
+      }
+    }
+    const int key = (int)tile * PF_TK + 16 * g + j;
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      float v = reduce_scatter4(P[qq], g);
+      if (tok[qq] && key < ncap) {
+        if constexpr (KDT == DT_FP8) v *= ksc[buf][16 * g + j];
+        __builtin_nontemporal_store(key < nvis[qq] ? v : -INFINITY, orow[qq] + key);
       }
     }
     if (tile + 1 < ntiles) lstore(buf ^ 1);
