@@ -703,9 +703,10 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // so each row is fetched from memory once per workgroup and then read from LDS
 // by every wave.  Rows sit at a stride of 2D + 16 bytes: 16 lanes reading one
 // 16-byte piece of 16 consecutive rows (the S^T operand) hit distinct banks,
-// and the transposed reads of V take constant offsets along a row.  Row
-// addresses come straight from the selection (wave-uniform loads), so the first
-// chunks are in flight before the query is even normalised.  The split depends
+// and the transposed reads of V take constant offsets along a row.  The
+// range's selected entries are staged in LDS with the query loads, so a chunk's
+// row addresses cost an LDS read, not a memory round trip.  The first chunk
+// of a range skips the output rescale (O is still 0).  The split depends
 // only on the slot count; a combine kernel merges split partials in order.
 // ---------------------------------------------------------------------------
 static constexpr int MQ_DEC_SPLIT = 288;   // key slots per workgroup
@@ -763,7 +764,6 @@ __device__ __forceinline__ void lds_read_tr16(uint32_t a0, uint32_t a1, u32x2_t 
 
 // where the rows of one workgroup's slot range come from (all wave-uniform)
 struct DecRows {
-  const int* idx_sp;          // selection of the range's first slot (sparse)
   const uint16_t* E_b;        // this sequence's entries
   const uint16_t* W_b;        // this sequence's window ring
   const uint16_t* dummy;      // a valid row, loaded for absent slots (their scores are masked)
@@ -775,54 +775,56 @@ struct DecRows {
   int N_cap;                  // entries per sequence, clamped to int
 };
 
-// start loading chunk c (rows RPW w .. RPW w + RPW - 1 of it are this wave's) and
-// record which of those rows exist, one byte per 8 rows, in mbytes
-template <int D, bool DENSE, int NW>
-__device__ __forceinline__ void dec_issue(int c, const DecRows& R, uint8_t* buf, uint8_t* mbytes,
-                                          int wave, int lane) {
+// row of slot `rel` of the range (e = its selected entry when sparse); *ok is
+// false for an absent slot, whose row is the dummy
+template <int D, bool DENSE>
+__device__ __forceinline__ const uint16_t* dec_slot_row(int rel, int e, const DecRows& R, bool* ok) {
+  *ok = false;
+  if (rel >= R.n_rows) return R.dummy;
+  if (rel < R.n_sel) {
+    if (DENSE) e = (int)(R.s0 + rel);
+    if (!DENSE && (e < 0 || e >= R.N_cap)) return R.dummy;
+    *ok = true;
+    return R.E_b + (size_t)e * D;
+  }
+  int ring = R.ring0 + (rel - R.n_sel);   // fewer window slots than ring rows: one wrap at most
+  if (ring >= R.W_cap) ring -= R.W_cap;
+  *ok = true;
+  return R.W_b + (size_t)ring * D;
+}
+
+// start loading chunk c: rows RPW w .. RPW w + RPW - 1 of it are this wave's,
+// their addresses read from the workgroup's slot table
+template <int D, int NW>
+__device__ __forceinline__ void dec_issue(int c, const uint16_t* const* sptr, uint8_t* buf, int wave,
+                                          int lane) {
   constexpr int RBP = 2 * D + 16, CPR = 2 * D / 16, RPW = MQ_CH / NW;
   const int rel0 = MQ_CH * c + RPW * wave;
-  // the wave's selected entries, read together (clamped to the range's entry slots)
-  int ev[RPW];
-  if (!DENSE && R.n_sel > 0) {
+  const uint16_t* p[RPW];
 #pragma unroll
-    for (int rr = 0; rr < RPW; ++rr) ev[rr] = R.idx_sp[min(rel0 + rr, R.n_sel - 1)];
-  }
-  uint32_t bits = 0u;
+  for (int rr = 0; rr < RPW; ++rr) p[rr] = sptr[rel0 + rr];
 #pragma unroll
-  for (int rr = 0; rr < RPW; ++rr) {
-    const int rel = rel0 + rr;
-    const uint16_t* p = R.dummy;
-    bool ok = false;
-    if (rel < R.n_rows) {
-      if (rel < R.n_sel) {
-        if (DENSE) {
-          p = R.E_b + (size_t)(R.s0 + rel) * D;
-          ok = true;
-        } else {
-          const int e = ev[rr];
-          if (e >= 0 && e < R.N_cap) {
-            p = R.E_b + (size_t)e * D;
-            ok = true;
-          }
-        }
-      } else {
-        int ring = R.ring0 + (rel - R.n_sel);   // fewer window slots than ring rows: one wrap at most
-        if (ring >= R.W_cap) ring -= R.W_cap;
-        p = R.W_b + (size_t)ring * D;
-        ok = true;
-      }
-    }
-    bits |= (ok ? 1u : 0u) << rr;
+  for (int rr = 0; rr < RPW; ++rr)
     if (lane < CPR)
-      __builtin_amdgcn_global_load_lds((const void*)(p + 8 * lane),
+      __builtin_amdgcn_global_load_lds((const void*)(p[rr] + 8 * lane),
                                        (__attribute__((address_space(3))) void*)(buf + (RPW * wave + rr) * RBP),
                                        16, 0, 0);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int q8 = 0; q8 < RPW / 8; ++q8) mbytes[(RPW / 8) * wave + q8] = (uint8_t)(bits >> (8 * q8));
-  }
+}
+
+// the maximum and the sum of x over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
+// lane groups of an MFMA tile column), with the gfx950 row swaps; each swap
+// leaves a lane its own value and its partner's, in either order
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // head tiles (16 heads each) per wave: two while the output accumulators of
@@ -850,7 +852,10 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_DEC_NBUF * CHB
   __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
   __shared__ float gam[D];
-  __shared__ uint32_t cmask[MQ_DEC_NBUF];   // bit r: row r of the chunk exists
+  constexpr int NCH_MAX = MQ_DEC_SPLIT / MQ_CH;
+  static_assert(MQ_DEC_SPLIT % MQ_CH == 0, "whole chunks per range");
+  __shared__ const uint16_t* sptr[MQ_DEC_SPLIT];   // row of every slot of the range
+  __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
   const int n_hg = n_h / HG;
@@ -872,7 +877,6 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   R.s0 = (long long)sp * MQ_DEC_SPLIT;
   R.n_rows = (int)max(0LL, min((long long)MQ_DEC_SPLIT, qs.n_slots - R.s0));
   R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
-  R.idx_sp = DENSE ? nullptr : idx + row * (size_t)k + R.s0;
   R.E_b = E + (size_t)b * (size_t)N_cap * D;
   R.W_b = W ? W + (size_t)b * (size_t)W_cap * D : nullptr;
   R.dummy = R.E_b;
@@ -881,7 +885,21 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   R.ring0 = W_cap > 0 ? (int)((qs.win_lo + max(0LL, R.s0 - qs.n_sel)) % W_cap) : 0;
   const int nch = (R.n_rows + MQ_CH - 1) / MQ_CH;
 
-  // query pieces and gamma first: waiting on them later must not wait on the chunks
+  // the range's selection, the query pieces and gamma are loaded and used
+  // before any chunk load is issued: a wait on an ordinary load issued before an
+  // LDS-DMA load becomes a wait on every load in flight
+  constexpr int IPT = (MQ_DEC_SPLIT + 64 * NW - 1) / (64 * NW);
+  int iv[IPT];
+  if (!DENSE) {
+    // bounded by the row's k selections only, so these loads need not wait for q_pos
+    const int* idx_sp = idx + row * (size_t)k + R.s0;
+    const int kcap = (int)max(0LL, min((long long)MQ_DEC_SPLIT, (long long)k - R.s0));
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int t = threadIdx.x + 64 * NW * e;
+      iv[e] = t < kcap ? idx_sp[t] : -1;
+    }
+  }
   u32x4_t raw[HTW][KS];
 #pragma unroll
   for (int ht = 0; ht < HTW; ++ht) {
@@ -895,9 +913,16 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const int t = threadIdx.x + 64 * NW * e;
     gv[e] = (t < D && gamma_q) ? gamma_q[t] : 1.f;
   }
+  // slot table: thread t resolves slot t of the range once, for every wave
 #pragma unroll
-  for (int c = 0; c < PF; ++c)
-    if (c < nch) dec_issue<D, DENSE, NW>(c, R, kv + c * CHB, (uint8_t*)&cmask[c], wave, lane);
+  for (int e = 0; e < IPT; ++e) {
+    const int t = threadIdx.x + 64 * NW * e;
+    bool ok;
+    const uint16_t* p = dec_slot_row<D, DENSE>(t, DENSE ? 0 : iv[e], R, &ok);
+    if (t < MQ_DEC_SPLIT) sptr[t] = p;
+    const unsigned long long bal = __ballot(ok);
+    if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
+  }
   for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
     const int u = t - (D - rope_dim) / 2;
     float cs = 1.f, sn = 0.f;
@@ -930,7 +955,10 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(raw[ht][ks]));
   }
-  lds_sync<63>();   // RoPE table and gamma visible; the chunks stay in flight
+  lds_sync<0>();   // selection, RoPE table and gamma visible
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+    if (c < nch) dec_issue<D, NW>(c, sptr, kv + c * CHB, wave, lane);
 
   // q^ = RoPE_i(RMSNorm(q)) as bf16 B fragments of S^T: lane (g, j) holds head 16 ht + j,
   // dims (D/4) g + 8 ks + 0..7; the RoPE table holds (1, 0) for dims that are not rotated
@@ -962,7 +990,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   for (int ht = 0; ht < HTW; ++ht)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) O[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float ref[HTW], lsum[HTW];   // of head 16 ht + j
+  float ref[HTW], lsum[HTW];   // of head 16 ht + j; lsum is this lane's share until the loop ends
 #pragma unroll
   for (int ht = 0; ht < HTW; ++ht) {
     ref[ht] = -INFINITY;
@@ -974,29 +1002,44 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     // chunk c landed for every wave (later chunks may stay in flight); chunk c - 1 is consumed
     if (c + 1 < nch && PF >= 2) lds_sync<(PF >= 2 ? RPW : 0)>();
     else lds_sync<0>();
-    const uint32_t vmask = cmask[c % MQ_DEC_NBUF];
-    if (c + PF < nch)
-      dec_issue<D, DENSE, NW>(c + PF, R, kv + ((c + PF) % MQ_DEC_NBUF) * CHB,
-                              (uint8_t*)&cmask[(c + PF) % MQ_DEC_NBUF], wave, lane);
+    const uint32_t vmask = smask[c];
+    if (c + PF < nch) dec_issue<D, NW>(c + PF, sptr, kv + ((c + PF) % MQ_DEC_NBUF) * CHB, wave, lane);
     const uint8_t* kb = kv + (c % MQ_DEC_NBUF) * CHB;
 
-    // S^T: 32 keys x 16 HTW heads over all D dims
+    // S^T: 32 keys x 16 HTW heads over all D dims.  The key operands stream in
+    // groups of four K-steps (both key tiles); a group's LDS reads are issued
+    // before the previous group's MFMAs, so their latency hides behind them.
     f32x4_t S[2][HTW];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ht = 0; ht < HTW; ++ht) S[kt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int NGRP = KS / 4;
+    static_assert(KS % 4 == 0, "K-steps in groups of four");
+    bf16x8_t ka[2][8];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int grp = 0; grp <= NGRP; ++grp) {
+      if (grp < NGRP) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8_t a = *(const bf16x8_t*)(kb + (16 * kt + j) * RBP + 16 * ((D / 32) * g + ks));
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int ht = 0; ht < HTW; ++ht)
-          S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ht][ks], S[kt][ht], 0, 0, 0);
+          for (int kt = 0; kt < 2; ++kt)
+            ka[grp & 1][2 * u + kt] =
+                *(const bf16x8_t*)(kb + (16 * kt + j) * RBP + 16 * ((D / 32) * g + 4 * grp + u));
       }
-      // bound how far the scheduler hoists operand reads (each costs 4 registers)
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp > 0) {
+        const int pg = grp - 1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ht = 0; ht < HTW; ++ht)
+              S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[pg & 1][2 * u + kt], qf[ht][4 * pg + u],
+                                                                  S[kt][ht], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // online softmax per head; the reference only moves when a chunk maximum
@@ -1014,11 +1057,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
           S[kt][ht][r] = ok ? S[kt][ht][r] * scale : -INFINITY;
           cm = fmaxf(cm, S[kt][ht][r]);
         }
-      cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-      cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+      cm = quad_max(cm);
       const float nr = (cm > ref[ht] + MQ_REF_SLACK) ? cm : ref[ht];
       alpha[ht] = (nr == ref[ht]) ? 1.f : (ref[ht] == -INFINITY ? 0.f : __expf(ref[ht] - nr));
-      moved |= nr != ref[ht];
+      // while the reference is -inf every P so far was 0 and O is still 0
+      moved |= nr != ref[ht] && ref[ht] != -INFINITY;
       float ps = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -1028,8 +1071,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
           S[kt][ht][r] = e;
           ps += e;
         }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
+      // this lane's share of the head's sum; the four shares add up after the loop
       lsum[ht] = lsum[ht] * alpha[ht] + ps;
       ref[ht] = nr;
     }
@@ -1091,6 +1133,9 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       }
     }
   }
+
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht) lsum[ht] = quad_sum(lsum[ht]);
 
   // ---- output: lane (g, j) of tile (ht, nt) holds heads h0 + 16 ht + 4 g + r, dim 16 nt + j
   if (n_split == 1) {
