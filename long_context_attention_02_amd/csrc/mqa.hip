@@ -709,7 +709,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // of a range skips the output rescale (O is still 0).  The split depends
 // only on the slot count; a combine kernel merges split partials in order.
 // ---------------------------------------------------------------------------
-static constexpr int MQ_DEC_SPLIT = 288;   // key slots per workgroup
+static constexpr int MQ_DEC_SPLIT = 192;   // key slots per workgroup (whole chunks)
 static constexpr int MQ_DEC_NBUF = 3;      // LDS chunk ring
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations complete
@@ -858,14 +858,17 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
-  const int n_hg = n_h / HG;
-  const long long L = blockIdx.x;
-  const int hg = (int)((L / 8) % n_hg);
-  const long long unit = (L / (8LL * n_hg)) * 8 + (L % 8);
-  if (unit >= n_units) return;
-  const int sp = (int)(unit % n_split);
-  const size_t row = (size_t)(unit / n_split);
-  const int b = (int)(row / Tq);
+  // 32-bit index arithmetic (the host keeps the grid below 2^31 workgroups):
+  // 64-bit divisions would put a few hundred instructions in front of the first load
+  const unsigned n_hg = (unsigned)(n_h / HG);
+  const unsigned L = blockIdx.x;
+  const int hg = (int)((L / 8u) % n_hg);
+  const unsigned unit = (L / (8u * n_hg)) * 8u + (L % 8u);
+  if ((long long)unit >= n_units) return;
+  const int sp = (int)(unit % (unsigned)n_split);
+  const unsigned row32 = unit / (unsigned)n_split;
+  const size_t row = row32;
+  const int b = (int)(row32 / (unsigned)Tq);
   const long long i = q_pos[row];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1003,7 +1006,6 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     if (c + 1 < nch && PF >= 2) lds_sync<(PF >= 2 ? RPW : 0)>();
     else lds_sync<0>();
     const uint32_t vmask = smask[c];
-    if (c + PF < nch) dec_issue<D, NW>(c + PF, sptr, kv + ((c + PF) % MQ_DEC_NBUF) * CHB, wave, lane);
     const uint8_t* kb = kv + (c % MQ_DEC_NBUF) * CHB;
 
     // S^T: 32 keys x 16 HTW heads over all D dims.  The key operands stream in
@@ -1041,6 +1043,9 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the next chunk into the slot that chunk c - 1 left (every wave is past it);
+    // issued after the scores, so a full load queue cannot hold them up
+    if (c + PF < nch) dec_issue<D, NW>(c + PF, sptr, kv + ((c + PF) % MQ_DEC_NBUF) * CHB, wave, lane);
 
     // online softmax per head; the reference only moves when a chunk maximum
     // exceeds it by MQ_REF_SLACK, so O is rarely rescaled
@@ -1370,6 +1375,11 @@ int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
     if (n_split > 1 && a.ws_bytes < mqa_workspace_bytes(a.B, a.Tq, a.n_h, a.d, slots_max, a.dtype)) {
       *why = "workspace smaller than csa_mqa_workspace_size()";
       return 5;
+    }
+    if (mqa_decode_ok(a.Tq, a.n_h, a.d) &&
+        (((long long)a.B * a.Tq * n_split + 7) / 8) * 8 * (a.n_h / 16) > 2147483647LL) {
+      *why = "decode attention: more (query, split, head group) units than one grid holds";
+      return 4;
     }
 #define CSA_MQA_D(DV)                                                  \
   do {                                                                 \

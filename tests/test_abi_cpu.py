@@ -128,7 +128,8 @@ def test_mqa_validation(lib):
     assert sparse(r=130) == CSA_E_SHAPE
     assert sparse(k=0) == CSA_E_SHAPE
     # a split decode query needs workspace
-    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 4 * 128 * 514 * 4
+    # 1152 slots in ranges of 192: 6 split partials of (O, max, sum) per (query, head)
+    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * 514 * 4
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED
