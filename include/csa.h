@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 /* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities). */
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 };
@@ -91,6 +91,41 @@ int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* 
                  long long pos_stride, long long pos_offset,
                  void* E, int out_dtype, float* E_scale, long long out_batch_stride,
                  long long out_ring, void* stream);
+
+/*
+ * a1, batched: n_jobs compressions in one kernel launch.  jobs[q] holds the
+ * arguments of one csa_compress call, with the same meaning, layout and
+ * checks; the results equal those of the n_jobs separate calls bit for bit.
+ * One launch lets the jobs' memory and barrier latencies overlap: a decode
+ * step compresses a window row, a KV entry and an indexer key, each a few
+ * microseconds of latency for a few kilobytes of data.
+ *
+ *  jobs   : host array of n_jobs job descriptors, read during the call only.
+ *  n_jobs : 1 .. CSA_COMPRESS_MAX_JOBS.
+ *  Jobs must not write overlapping output rows (they run concurrently); a job
+ *  with s_end == s_begin is a no-op.  Every job is checked before anything is
+ *  launched; the first failing job's status is returned and csa_last_error()
+ *  names its index.
+ */
+#define CSA_COMPRESS_MAX_JOBS 8
+typedef struct csa_compress_job {
+  const void *C_a, *Z_a, *C_b, *Z_b;
+  int in_dtype;
+  int B;
+  long long R, in_batch_stride, tok_base, T;
+  int c, m, overlap;
+  long long s_begin, s_end;
+  const float* gamma;
+  float eps;
+  int rope_dim;
+  float rope_base;
+  long long pos_stride, pos_offset;
+  void* E;
+  int out_dtype;
+  float* E_scale;
+  long long out_batch_stride, out_ring;
+} csa_compress_job;
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
 
 /*
  * a2 — lightning-indexer score (method page §3.3):

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_index_score", "csa_topk",
+    "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_index_score",
+    "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_workspace_size",
     "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3",
 ]
@@ -44,6 +45,20 @@ _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_compress.restype = _I
 _lib.csa_compress.argtypes = [_P, _P, _P, _P, _I, _I, _L, _L, _L, _L, _I, _I, _I, _L, _L, _P, _F, _I,
                               _F, _L, _L, _P, _I, _P, _L, _L, _P]
+
+
+class _CompressJob(ctypes.Structure):
+    """csa_compress_job of include/csa.h (C layout, natural alignment)."""
+    _fields_ = [("C_a", _P), ("Z_a", _P), ("C_b", _P), ("Z_b", _P), ("in_dtype", _I), ("B", _I),
+                ("R", _L), ("in_batch_stride", _L), ("tok_base", _L), ("T", _L),
+                ("c", _I), ("m", _I), ("overlap", _I), ("s_begin", _L), ("s_end", _L),
+                ("gamma", _P), ("eps", _F), ("rope_dim", _I), ("rope_base", _F),
+                ("pos_stride", _L), ("pos_offset", _L), ("E", _P), ("out_dtype", _I),
+                ("E_scale", _P), ("out_batch_stride", _L), ("out_ring", _L)]
+
+
+_lib.csa_compress_batch.restype = _I
+_lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _I, _P]
 _lib.csa_index_score.restype = _I
 _lib.csa_index_score.argtypes = [_P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P]
 _lib.csa_topk_workspace_size.restype = _S
@@ -105,13 +120,11 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def csa_compress(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_begin: int, s_end: int,
-                 tok_base: int = 0, gamma=None, eps: float = 1e-6, rope_dim: int = 0,
-                 rope_base: float = 10000.0, pos_stride: int | None = None, pos_offset: int = 0,
-                 E_scale=None, out_ring: int = 0):
-    """a1.  C_a/Z_a/C_b/Z_b: [B, R, c] (Z may be None; C_b None when overlap=0),
-    E: [B, rows, c] float32 / bfloat16 / float8_e4m3fn, E_scale: [B, rows] fp32
-    for fp8 output.  Row r of the candidates is token tok_base + r."""
+def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_begin: int,
+                   s_end: int, tok_base: int = 0, gamma=None, eps: float = 1e-6, rope_dim: int = 0,
+                   rope_base: float = 10000.0, pos_stride: int | None = None, pos_offset: int = 0,
+                   E_scale=None, out_ring: int = 0):
+    """The C arguments of one compression (without the stream), in csa_compress order."""
     B, R, c = C_a.shape
     for name, t in (("Z_a", Z_a), ("C_b", C_b), ("Z_b", Z_b)):
         if t is not None and (t.shape != C_a.shape or t.dtype != C_a.dtype):
@@ -122,13 +135,30 @@ def csa_compress(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_begin
         raise ValueError("E has fewer rows than the entries written")
     if E_scale is not None and tuple(E_scale.shape) != (B, E.shape[1]):
         raise ValueError("E_scale must be [B, rows]")
-    _check(_lib.csa_compress(
-        _ptr(C_a, "C_a", dims=3), _ptr(Z_a, "Z_a"), _ptr(C_b, "C_b"), _ptr(Z_b, "Z_b"), _dt(C_a),
-        B, R, R * c, tok_base, T, c, m, overlap, s_begin, s_end,
-        _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
-        m if pos_stride is None else pos_stride, pos_offset,
-        _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.float32), E.shape[1] * c, out_ring,
-        _stream()))
+    return (_ptr(C_a, "C_a", dims=3), _ptr(Z_a, "Z_a"), _ptr(C_b, "C_b"), _ptr(Z_b, "Z_b"), _dt(C_a),
+            B, R, R * c, tok_base, T, c, m, overlap, s_begin, s_end,
+            _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
+            m if pos_stride is None else pos_stride, pos_offset,
+            _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.float32), E.shape[1] * c, out_ring)
+
+
+def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
+    """a1.  C_a/Z_a/C_b/Z_b: [B, R, c] (Z may be None; C_b None when overlap=0),
+    E: [B, rows, c] float32 / bfloat16 / float8_e4m3fn, E_scale: [B, rows] fp32
+    for fp8 output.  Row r of the candidates is token tok_base + r.  Keywords:
+    T, m, overlap, s_begin, s_end (required); tok_base, gamma, eps, rope_dim,
+    rope_base, pos_stride (default m), pos_offset, E_scale, out_ring."""
+    _check(_lib.csa_compress(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw), _stream()))
+
+
+def csa_compress_batch(jobs):
+    """a1, several compressions in one launch.  ``jobs`` is a list of
+    (C_a, Z_a, C_b, Z_b, E, kwargs) with the arguments of csa_compress; the
+    outputs equal those of the separate calls."""
+    arr = (_CompressJob * max(len(jobs), 1))()
+    for q, (C_a, Z_a, C_b, Z_b, E, kw) in enumerate(jobs):
+        arr[q] = _CompressJob(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw))
+    _check(_lib.csa_compress_batch(arr, len(jobs), _stream()))
 
 
 def csa_index_score(q_I, w_I, K_I, q_pos, I_out, *, m: int, K_scale=None):

@@ -13,6 +13,11 @@
 // G partial results are merged in LDS.  This keeps a 128-candidate HCA block
 // from serialising 128 dependent loads per thread.  Reads are coalesced along
 // the channel axis; HBM traffic is one pass over C and Z.
+//
+// One launch runs a batch of independent jobs (blockIdx.z): a decode step's
+// window row, KV entry and indexer key are each a few microseconds of memory
+// and barrier latency, which overlap in one launch instead of adding up.  Each
+// job's dtypes are chosen at run time (uniform per workgroup).
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -21,15 +26,38 @@ namespace csa {
 static constexpr int COMP_THREADS = 512;
 static constexpr int COMP_MAX_G = 8;
 static constexpr int COMP_JU = 8;   // channels per thread whose loads are issued together
+static constexpr int COMP_MAX_JOBS = 8;
+
+// one job's arguments as the kernel reads them (validated on the host)
+struct CompressJob {
+  const void *Ca, *Za, *Cb, *Zb;
+  const float* gamma;
+  void* E;
+  float* E_scale;
+  long long in_bs, tok_base, T, s_begin, n_entries, pos_stride, pos_offset, out_bs, out_ring;
+  RopeRatio rope;
+  float eps;
+  int in_dtype, out_dtype, B, c, m, overlap, G, rope_dim;
+};
+struct CompressBatch {
+  CompressJob job[COMP_MAX_JOBS];
+};
 
 template <int IDT, int ODT>
-__global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
-    const void* __restrict__ Ca, const void* __restrict__ Za, const void* __restrict__ Cb,
-    const void* __restrict__ Zb, long long in_bs, long long tok_base, long long T, int c, int m,
-    int overlap, long long s_begin, int G, const float* __restrict__ gamma, float eps, int rope_dim,
-    RopeRatio rope, long long pos_stride, long long pos_offset, void* __restrict__ E,
-    float* __restrict__ E_scale, long long out_bs, long long out_ring) {
-  extern __shared__ float smem[];
+__device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem) {
+  const void* __restrict__ Ca = J.Ca;
+  const void* __restrict__ Za = J.Za;
+  const void* __restrict__ Cb = J.Cb;
+  const void* __restrict__ Zb = J.Zb;
+  const float* __restrict__ gamma = J.gamma;
+  void* __restrict__ E = J.E;
+  float* __restrict__ E_scale = J.E_scale;
+  const long long in_bs = J.in_bs, tok_base = J.tok_base, T = J.T, s_begin = J.s_begin;
+  const long long pos_stride = J.pos_stride, pos_offset = J.pos_offset, out_bs = J.out_bs;
+  const long long out_ring = J.out_ring;
+  const RopeRatio rope = J.rope;
+  const float eps = J.eps;
+  const int c = J.c, m = J.m, overlap = J.overlap, G = J.G, rope_dim = J.rope_dim;
   float* pmax = smem;                 // [G][c]
   float* psum = pmax + G * c;         // [G][c]
   float* pacc = psum + G * c;         // [G][c]
@@ -165,36 +193,58 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(
   }
 }
 
-int launch_compress(const CompressArgs& a, hipStream_t st) {
-  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
-  const int ncand_max = a.overlap ? 2 * a.m : a.m;
-  int G = ncand_max < COMP_MAX_G ? ncand_max : COMP_MAX_G;
-  if (G < 1) G = 1;
-  const size_t lds = (size_t)(3 * G * a.c + a.c + COMP_THREADS / 64) * sizeof(float);
-  dim3 grid((unsigned)(a.s_end - a.s_begin), (unsigned)a.B);
-  dim3 block(COMP_THREADS);
-#define CSA_COMP_LAUNCH(IDT, ODT)                                                                  \
-  do {                                                                                             \
-    auto kfn = compress_kernel<IDT, ODT>;                                                          \
-    if (lds > 65536 &&                                                                             \
-        hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize,         \
-                            (int)lds) != hipSuccess)                                               \
-      return -1;                                                                                   \
-    hipLaunchKernelGGL(kfn, grid, block, lds, st, a.C_a, a.Z_a, a.C_b, a.Z_b, a.in_bs, a.tok_base, \
-                       a.T, a.c, a.m, a.overlap, a.s_begin, G, a.gamma, a.eps, a.rope_dim,         \
-                       rope_rr, a.pos_stride, a.pos_offset, a.E, a.E_scale, a.out_bs,          \
-                       a.out_ring);                                                                \
-  } while (0)
-  if (a.in_dtype == DT_F32) {
-    if (a.out_dtype == DT_F32) CSA_COMP_LAUNCH(DT_F32, DT_F32);
-    else if (a.out_dtype == DT_BF16) CSA_COMP_LAUNCH(DT_F32, DT_BF16);
-    else CSA_COMP_LAUNCH(DT_F32, DT_FP8);
-  } else {
-    if (a.out_dtype == DT_F32) CSA_COMP_LAUNCH(DT_BF16, DT_F32);
-    else if (a.out_dtype == DT_BF16) CSA_COMP_LAUNCH(DT_BF16, DT_BF16);
-    else CSA_COMP_LAUNCH(DT_BF16, DT_FP8);
+__global__ __launch_bounds__(COMP_THREADS) void compress_kernel(const CompressBatch jb) {
+  extern __shared__ float smem[];
+  const CompressJob& J = jb.job[blockIdx.z];
+  if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
+  switch (J.in_dtype * 3 + J.out_dtype) {
+    case DT_F32 * 3 + DT_F32: compress_entry<DT_F32, DT_F32>(J, smem); break;
+    case DT_F32 * 3 + DT_BF16: compress_entry<DT_F32, DT_BF16>(J, smem); break;
+    case DT_F32 * 3 + DT_FP8: compress_entry<DT_F32, DT_FP8>(J, smem); break;
+    case DT_BF16 * 3 + DT_F32: compress_entry<DT_BF16, DT_F32>(J, smem); break;
+    case DT_BF16 * 3 + DT_BF16: compress_entry<DT_BF16, DT_BF16>(J, smem); break;
+    default: compress_entry<DT_BF16, DT_FP8>(J, smem); break;
   }
-#undef CSA_COMP_LAUNCH
+}
+
+static size_t compress_lds_bytes(int G, int c) {
+  return (size_t)(3 * G * c + c + COMP_THREADS / 64) * sizeof(float);
+}
+
+int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
+  if (n_jobs < 1 || n_jobs > COMP_MAX_JOBS) return -1;
+  CompressBatch jb{};
+  size_t lds = 0;
+  long long gx = 1;
+  int gy = 1;
+  for (int q = 0; q < n_jobs; ++q) {
+    const CompressArgs& x = a[q];
+    const int ncand_max = x.overlap ? 2 * x.m : x.m;
+    int G = ncand_max < COMP_MAX_G ? ncand_max : COMP_MAX_G;
+    if (G < 1) G = 1;
+    CompressJob& J = jb.job[q];
+    J.Ca = x.C_a; J.Za = x.Z_a; J.Cb = x.C_b; J.Zb = x.Z_b;
+    J.gamma = x.gamma; J.E = x.E; J.E_scale = x.E_scale;
+    J.in_bs = x.in_bs; J.tok_base = x.tok_base; J.T = x.T; J.s_begin = x.s_begin;
+    J.n_entries = x.s_end - x.s_begin;
+    J.pos_stride = x.pos_stride; J.pos_offset = x.pos_offset;
+    J.out_bs = x.out_bs; J.out_ring = x.out_ring;
+    J.rope = rope_ratio(x.rope_dim, x.rope_base);
+    J.eps = x.eps;
+    J.in_dtype = x.in_dtype; J.out_dtype = x.out_dtype;
+    J.B = x.B; J.c = x.c; J.m = x.m; J.overlap = x.overlap; J.G = G; J.rope_dim = x.rope_dim;
+    const size_t l = compress_lds_bytes(G, x.c);
+    if (l > lds) lds = l;
+    if (J.n_entries > gx) gx = J.n_entries;
+    if (x.B > gy) gy = x.B;
+  }
+  if (gx > 2147483647LL || gy > 65535) return -1;
+  if (lds > 65536 && hipFuncSetAttribute((const void*)compress_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds) != hipSuccess)
+    return -1;
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)n_jobs),
+                     dim3(COMP_THREADS), lds, st, jb);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

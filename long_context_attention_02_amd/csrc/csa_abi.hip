@@ -28,6 +28,67 @@ bool dtype_valid(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_F
 
 }  // namespace
 
+// the checks of one compression (also every job of a batch); CSA_OK or the
+// status of the first failure, with `who` naming the call in the message
+static int check_compress(const csa_compress_job& j, const char* who) {
+  const void *C_a = j.C_a, *C_b = j.C_b, *E = j.E;
+  const float* gamma = j.gamma;
+  const float* E_scale = j.E_scale;
+  const int in_dtype = j.in_dtype, out_dtype = j.out_dtype, B = j.B, c = j.c, m = j.m;
+  const int overlap = j.overlap, rope_dim = j.rope_dim;
+  const long long R = j.R, in_batch_stride = j.in_batch_stride, tok_base = j.tok_base, T = j.T;
+  const long long s_begin = j.s_begin, s_end = j.s_end, out_ring = j.out_ring;
+  const long long out_batch_stride = j.out_batch_stride;
+  const float eps = j.eps;
+  if (!C_a || !E) return fail(CSA_E_NULL, "%s: C_a and E are required", who);
+  if (overlap != 0 && overlap != 1) return fail(CSA_E_SHAPE, "%s: overlap must be 0 or 1", who);
+  if (overlap && !C_b) return fail(CSA_E_NULL, "%s: C_b is required when overlap = 1", who);
+  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16)
+    return fail(CSA_E_DTYPE, "%s: in_dtype must be F32 or BF16", who);
+  if (!dtype_valid(out_dtype)) return fail(CSA_E_DTYPE, "%s: unknown out_dtype", who);
+  if (out_dtype == CSA_FP8_E4M3 && !E_scale)
+    return fail(CSA_E_NULL, "%s: E_scale is required for FP8 output", who);
+  if (B < 1 || R < 1 || c < 1 || m < 1 || T < 1)
+    return fail(CSA_E_SHAPE, "%s: B, R, c, m and T must be >= 1", who);
+  if (c > 1024) return fail(CSA_E_UNSUPPORTED, "%s: c = %d exceeds 1024", who, c);
+  if (in_batch_stride < R * c)
+    return fail(CSA_E_SHAPE, "%s: in_batch_stride %lld < R * c", who, in_batch_stride);
+  if (tok_base < 0) return fail(CSA_E_SHAPE, "%s: tok_base < 0", who);
+  if (s_begin < 0 || s_end < s_begin) return fail(CSA_E_SHAPE, "%s: bad entry range", who);
+  const long long n_entries = (T + m - 1) / m;
+  if (s_end > n_entries)
+    return fail(CSA_E_SHAPE, "%s: s_end %lld > ceil(T/m) = %lld", who, s_end, n_entries);
+  if (s_end - s_begin > 2147483647LL) return fail(CSA_E_UNSUPPORTED, "%s: too many entries", who);
+  if (rope_dim < 0 || rope_dim > c || (rope_dim & 1) || ((c - rope_dim) & 1))
+    return fail(CSA_E_SHAPE, "%s: rope_dim must be even, <= c, with c - rope_dim even", who);
+  if (gamma && !(eps >= 0.f)) return fail(CSA_E_SHAPE, "%s: eps must be >= 0", who);
+  if (out_ring < 0) return fail(CSA_E_SHAPE, "%s: out_ring < 0", who);
+  if (out_ring > 0 && s_end - s_begin > out_ring)
+    return fail(CSA_E_SHAPE, "%s: more entries than ring rows (rows would collide)", who);
+  const long long rows_out = out_ring > 0 ? out_ring : s_end;
+  if (out_batch_stride < rows_out * c && B > 1)
+    return fail(CSA_E_SHAPE, "%s: out_batch_stride too small for the rows written", who);
+  if (out_dtype == CSA_FP8_E4M3 && out_batch_stride % c)
+    return fail(CSA_E_SHAPE, "%s: FP8 output needs out_batch_stride %% c == 0", who);
+  if (s_end > s_begin) {
+    // every candidate token < T of the requested entries must be among the given rows
+    const long long first = overlap ? (m * (s_begin - 1) > 0 ? m * (s_begin - 1) : 0) : m * s_begin;
+    const long long last = (m * s_end < T ? m * s_end : T) - 1;
+    if (first < tok_base || last >= tok_base + R)
+      return fail(CSA_E_SHAPE,
+                  "%s: tokens [%lld, %lld] needed but rows hold [%lld, %lld)", who, first,
+                  last, tok_base, tok_base + R);
+  }
+  return CSA_OK;
+}
+
+static csa::CompressArgs compress_args(const csa_compress_job& j) {
+  return csa::CompressArgs{j.C_a, j.Z_a, j.C_b, j.Z_b, j.in_dtype, j.B, j.R, j.in_batch_stride,
+                           j.tok_base, j.T, j.c, j.m, j.overlap, j.s_begin, j.s_end, j.gamma, j.eps,
+                           j.rope_dim, j.rope_base, j.pos_stride, j.pos_offset, j.E, j.out_dtype,
+                           j.E_scale, j.out_batch_stride, j.out_ring};
+}
+
 extern "C" {
 
 int csa_abi_version(void) { return CSA_ABI_VERSION; }
@@ -54,52 +115,34 @@ int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* 
                  long long pos_stride, long long pos_offset,
                  void* E, int out_dtype, float* E_scale, long long out_batch_stride,
                  long long out_ring, void* stream) {
-  if (!C_a || !E) return fail(CSA_E_NULL, "csa_compress: C_a and E are required");
-  if (overlap != 0 && overlap != 1) return fail(CSA_E_SHAPE, "csa_compress: overlap must be 0 or 1");
-  if (overlap && !C_b) return fail(CSA_E_NULL, "csa_compress: C_b is required when overlap = 1");
-  if (in_dtype != CSA_F32 && in_dtype != CSA_BF16)
-    return fail(CSA_E_DTYPE, "csa_compress: in_dtype must be F32 or BF16");
-  if (!dtype_valid(out_dtype)) return fail(CSA_E_DTYPE, "csa_compress: unknown out_dtype");
-  if (out_dtype == CSA_FP8_E4M3 && !E_scale)
-    return fail(CSA_E_NULL, "csa_compress: E_scale is required for FP8 output");
-  if (B < 1 || R < 1 || c < 1 || m < 1 || T < 1)
-    return fail(CSA_E_SHAPE, "csa_compress: B, R, c, m and T must be >= 1");
-  if (c > 1024) return fail(CSA_E_UNSUPPORTED, "csa_compress: c = %d exceeds 1024", c);
-  if (in_batch_stride < R * c)
-    return fail(CSA_E_SHAPE, "csa_compress: in_batch_stride %lld < R * c", in_batch_stride);
-  if (tok_base < 0) return fail(CSA_E_SHAPE, "csa_compress: tok_base < 0");
-  if (s_begin < 0 || s_end < s_begin) return fail(CSA_E_SHAPE, "csa_compress: bad entry range");
-  const long long n_entries = (T + m - 1) / m;
-  if (s_end > n_entries)
-    return fail(CSA_E_SHAPE, "csa_compress: s_end %lld > ceil(T/m) = %lld", s_end, n_entries);
-  if (s_end - s_begin > 2147483647LL) return fail(CSA_E_UNSUPPORTED, "csa_compress: too many entries");
-  if (rope_dim < 0 || rope_dim > c || (rope_dim & 1) || ((c - rope_dim) & 1))
-    return fail(CSA_E_SHAPE, "csa_compress: rope_dim must be even, <= c, with c - rope_dim even");
-  if (gamma && !(eps >= 0.f)) return fail(CSA_E_SHAPE, "csa_compress: eps must be >= 0");
-  if (out_ring < 0) return fail(CSA_E_SHAPE, "csa_compress: out_ring < 0");
-  if (out_ring > 0 && s_end - s_begin > out_ring)
-    return fail(CSA_E_SHAPE, "csa_compress: more entries than ring rows (rows would collide)");
-  const long long rows_out = out_ring > 0 ? out_ring : s_end;
-  if (out_batch_stride < rows_out * c && B > 1)
-    return fail(CSA_E_SHAPE, "csa_compress: out_batch_stride too small for the rows written");
-  if (out_dtype == CSA_FP8_E4M3 && out_batch_stride % c)
-    return fail(CSA_E_SHAPE, "csa_compress: FP8 output needs out_batch_stride % c == 0");
-  if (s_end > s_begin) {
-    // every candidate token < T of the requested entries must be among the given rows
-    const long long first = overlap ? (m * (s_begin - 1) > 0 ? m * (s_begin - 1) : 0) : m * s_begin;
-    const long long last = (m * s_end < T ? m * s_end : T) - 1;
-    if (first < tok_base || last >= tok_base + R)
-      return fail(CSA_E_SHAPE,
-                  "csa_compress: tokens [%lld, %lld] needed but rows hold [%lld, %lld)", first,
-                  last, tok_base, tok_base + R);
-  } else {
-    return ok();
-  }
-  csa::CompressArgs a{C_a, Z_a, C_b, Z_b, in_dtype, B, R, in_batch_stride, tok_base, T, c, m,
-                      overlap, s_begin, s_end, gamma, eps, rope_dim, rope_base, pos_stride,
-                      pos_offset, E, out_dtype, E_scale, out_batch_stride, out_ring};
-  if (csa::launch_compress(a, (hipStream_t)stream) != 0)
+  const csa_compress_job j{C_a, Z_a, C_b, Z_b, in_dtype, B, R, in_batch_stride, tok_base, T, c, m,
+                           overlap, s_begin, s_end, gamma, eps, rope_dim, rope_base, pos_stride,
+                           pos_offset, E, out_dtype, E_scale, out_batch_stride, out_ring};
+  const int st = check_compress(j, "csa_compress");
+  if (st != CSA_OK) return st;
+  if (s_end == s_begin) return ok();
+  const csa::CompressArgs a = compress_args(j);
+  if (csa::launch_compress(&a, 1, (hipStream_t)stream) != 0)
     return fail(CSA_E_HIP, "csa_compress: kernel launch failed");
+  return ok();
+}
+
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
+  if (!jobs) return fail(CSA_E_NULL, "csa_compress_batch: jobs is NULL");
+  if (n_jobs < 1 || n_jobs > CSA_COMPRESS_MAX_JOBS)
+    return fail(CSA_E_SHAPE, "csa_compress_batch: n_jobs = %d outside [1, %d]", n_jobs,
+                CSA_COMPRESS_MAX_JOBS);
+  csa::CompressArgs a[CSA_COMPRESS_MAX_JOBS];
+  int n = 0;
+  for (int q = 0; q < n_jobs; ++q) {
+    char who[48];
+    snprintf(who, sizeof(who), "csa_compress_batch: job %d", q);
+    const int st = check_compress(jobs[q], who);
+    if (st != CSA_OK) return st;
+    if (jobs[q].s_end > jobs[q].s_begin) a[n++] = compress_args(jobs[q]);
+  }
+  if (n > 0 && csa::launch_compress(a, n, (hipStream_t)stream) != 0)
+    return fail(CSA_E_HIP, "csa_compress_batch: kernel launch failed");
   return ok();
 }
 

@@ -25,7 +25,8 @@ struct CompressArgs {
   float* E_scale;
   long long out_bs, out_ring;
 };
-int launch_compress(const CompressArgs& a, hipStream_t st);
+// n_jobs (1 .. 8) independent compressions in one launch
+int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st);
 
 struct IndexArgs {
   const void* q;

@@ -696,7 +696,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // decode kernel (few queries per sequence, heads a multiple of 16 per wave).
 //
 // A workgroup takes one query, a group of 16 HTW NW heads and a fixed range of
-// at most MQ_DEC_SPLIT key slots.  Wave w owns HTW 16-head tiles of the group
+// at most MQ_DEC_SPLIT_MAX key slots.  Wave w owns HTW 16-head tiles of the group
 // (one at D = 512, two below) over all D dims, so scores, softmax and P.V stay
 // inside the wave and need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
 // MQ_DEC_NBUF chunks filled with global_load_lds, MQ_DEC_NBUF - 1 chunks ahead,
@@ -709,7 +709,12 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // of a range skips the output rescale (O is still 0).  The split depends
 // only on the slot count; a combine kernel merges split partials in order.
 // ---------------------------------------------------------------------------
-static constexpr int MQ_DEC_SPLIT = 192;   // key slots per workgroup (whole chunks)
+// key slots per workgroup (whole chunks), a function of the query's slot count:
+// 192 up to 1,536 slots (more workgroups for a sparse selection), 288 above
+// (fewer split partials to merge for a long dense context)
+static constexpr int MQ_DEC_SPLIT_MAX = 288;
+static constexpr int MQ_DEC_SPLIT_SMALL = 192;
+static constexpr long long MQ_DEC_SMALL_UPTO = 1536;
 static constexpr int MQ_DEC_NBUF = 3;      // LDS chunk ring
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations complete
@@ -838,7 +843,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
     const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
-    int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
+    int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
   constexpr int HTW = dec_htw<D>();   // head tiles per wave
   constexpr int KS = D / 32;          // S^T K-steps (8 dims per lane each)
   constexpr int NT = D / 16;          // 16-dim output tiles
@@ -852,9 +857,9 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_DEC_NBUF * CHB
   __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
   __shared__ float gam[D];
-  constexpr int NCH_MAX = MQ_DEC_SPLIT / MQ_CH;
-  static_assert(MQ_DEC_SPLIT % MQ_CH == 0, "whole chunks per range");
-  __shared__ const uint16_t* sptr[MQ_DEC_SPLIT];   // row of every slot of the range
+  constexpr int NCH_MAX = MQ_DEC_SPLIT_MAX / MQ_CH;
+  static_assert(MQ_DEC_SPLIT_MAX % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0, "whole chunks per range");
+  __shared__ const uint16_t* sptr[MQ_DEC_SPLIT_MAX];   // row of every slot of the range
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
@@ -877,8 +882,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 
   const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
   DecRows R;
-  R.s0 = (long long)sp * MQ_DEC_SPLIT;
-  R.n_rows = (int)max(0LL, min((long long)MQ_DEC_SPLIT, qs.n_slots - R.s0));
+  R.s0 = (long long)sp * kps;
+  R.n_rows = (int)max(0LL, min((long long)kps, qs.n_slots - R.s0));
   R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
   R.E_b = E + (size_t)b * (size_t)N_cap * D;
   R.W_b = W ? W + (size_t)b * (size_t)W_cap * D : nullptr;
@@ -891,12 +896,12 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   // the range's selection, the query pieces and gamma are loaded and used
   // before any chunk load is issued: a wait on an ordinary load issued before an
   // LDS-DMA load becomes a wait on every load in flight
-  constexpr int IPT = (MQ_DEC_SPLIT + 64 * NW - 1) / (64 * NW);
+  constexpr int IPT = (MQ_DEC_SPLIT_MAX + 64 * NW - 1) / (64 * NW);
   int iv[IPT];
   if (!DENSE) {
     // bounded by the row's k selections only, so these loads need not wait for q_pos
     const int* idx_sp = idx + row * (size_t)k + R.s0;
-    const int kcap = (int)max(0LL, min((long long)MQ_DEC_SPLIT, (long long)k - R.s0));
+    const int kcap = (int)max(0LL, min((long long)kps, (long long)k - R.s0));
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
       const int t = threadIdx.x + 64 * NW * e;
@@ -922,7 +927,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const int t = threadIdx.x + 64 * NW * e;
     bool ok;
     const uint16_t* p = dec_slot_row<D, DENSE>(t, DENSE ? 0 : iv[e], R, &ok);
-    if (t < MQ_DEC_SPLIT) sptr[t] = p;
+    if (t < MQ_DEC_SPLIT_MAX) sptr[t] = p;
     const unsigned long long bal = __ballot(ok);
     if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
   }
@@ -1286,8 +1291,8 @@ static bool mqa_decode_ok(int Tq, int n_h, int d) {
 // slots per workgroup and splits per query; depends on the shape only, never on B
 static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int* n_split) {
   if (mqa_decode_ok(Tq, n_h, d)) {
-    *kps = MQ_DEC_SPLIT;
-    *n_split = (int)max(1LL, (slots_max + MQ_DEC_SPLIT - 1) / MQ_DEC_SPLIT);
+    *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_MAX;
+    *n_split = (int)max(1LL, (slots_max + *kps - 1) / *kps);
   } else if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
     long long s = ((slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH;
     if (s > 2147483647LL) s = 2147483647LL;
@@ -1329,7 +1334,7 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
 }
 
 template <int D, bool DENSE, int NW>
-static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
+static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const int n_hg = a.n_h / (16 * dec_htw<D>() * NW);
   const long long units = (long long)a.B * a.Tq * n_split;
@@ -1341,7 +1346,7 @@ static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
                      (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
-                     a.rope_dim, rope_rr, a.scale, n_split, units, (uint16_t*)a.out,
+                     a.rope_dim, rope_rr, a.scale, kps, n_split, units, (uint16_t*)a.out,
                      (float*)a.ws);
   if (n_split > 1)
     hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
@@ -1351,16 +1356,16 @@ static void launch_decode_nw(const MqaArgs& a, int n_split, hipStream_t st) {
 
 // waves per workgroup: as many head groups of one wave as divide n_h, up to four
 template <int D, bool DENSE>
-static void launch_decode(const MqaArgs& a, int n_split, hipStream_t st) {
+static void launch_decode(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   constexpr int HW = 16 * dec_htw<D>();
-  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4>(a, n_split, st);
-  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2>(a, n_split, st);
-  else launch_decode_nw<D, DENSE, 1>(a, n_split, st);
+  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4>(a, kps, n_split, st);
+  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2>(a, kps, n_split, st);
+  else launch_decode_nw<D, DENSE, 1>(a, kps, n_split, st);
 }
 
 template <int D, bool DENSE>
 static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
-  if (mqa_decode_ok(a.Tq, a.n_h, a.d)) launch_decode<D, DENSE>(a, n_split, st);
+  if (mqa_decode_ok(a.Tq, a.n_h, a.d)) launch_decode<D, DENSE>(a, kps, n_split, st);
   else if (kps <= MQ_GROUP) launch_mfma_v<D, DENSE, false>(a, kps, n_split, st);
   else launch_mfma_v<D, DENSE, true>(a, kps, n_split, st);
 }

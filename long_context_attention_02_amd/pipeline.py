@@ -17,8 +17,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (csa_compress, csa_index_score, csa_mqa_workspace_size, csa_sparse_mqa,
-               csa_topk, csa_topk_workspace_size, hca_dense_mqa)
+from . import (csa_compress, csa_compress_batch, csa_index_score, csa_mqa_workspace_size,
+               csa_sparse_mqa, csa_topk, csa_topk_workspace_size, hca_dense_mqa)
 
 _TD = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -35,11 +35,17 @@ class _Common:
         self.W = torch.zeros((B, wl.W_cap, d), dtype=_TD[wl.dtype], device=self.dev)
         self._win_rows(lo_tok, lo_tok + n_rows, self.win_raw, lo_tok)
 
-    def _win_rows(self, s0: int, s1: int, raw: torch.Tensor, tok_base: int):
+    def _win_job(self, s0: int, s1: int, raw: torch.Tensor, tok_base: int):
+        """The window rows of tokens s0 .. s1 - 1 as a compression job (m = 1)."""
         wl = self.wl
-        csa_compress(raw, None, None, None, self.W, T=s1, m=1, overlap=0, s_begin=s0, s_end=s1,
-                     tok_base=tok_base, gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim,
-                     rope_base=wl.rope_base, pos_stride=1, out_ring=wl.W_cap)
+        return (raw, None, None, None, self.W,
+                dict(T=s1, m=1, overlap=0, s_begin=s0, s_end=s1, tok_base=tok_base, gamma=self.gamma_kv,
+                     eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base, pos_stride=1,
+                     out_ring=wl.W_cap))
+
+    def _win_rows(self, s0: int, s1: int, raw: torch.Tensor, tok_base: int):
+        C_a, Z_a, C_b, Z_b, E, kw = self._win_job(s0, s1, raw, tok_base)
+        csa_compress(C_a, Z_a, C_b, Z_b, E, **kw)
 
     def _fill_entries(self, E, raw, m: int, normalize: bool, rope: bool, E_scale=None):
         wl = self.wl
@@ -101,14 +107,19 @@ class CSADecode(_Common):
 
     # -- the step ------------------------------------------------------------
     def compress_new(self):
+        """The new token's window row, the newest KV entry and its indexer key:
+        three independent compressions, one launch."""
         wl, i, N = self.wl, self.i, self.wl.N_cap
-        self._win_rows(i, i + 1, self.win_new, i)
         T_done = wl.m * N
-        csa_compress(self.Ca, self.Za, self.Cb, self.Zb, self.E, T=T_done, m=wl.m, overlap=1,
-                     s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base, gamma=self.gamma_kv,
-                     eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)
-        csa_compress(self.ICa, self.IZa, self.ICb, self.IZb, self.KI, T=T_done, m=wl.m, overlap=1,
-                     s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base, E_scale=self.KI_scale)
+        csa_compress_batch([
+            self._win_job(i, i + 1, self.win_new, i),
+            (self.Ca, self.Za, self.Cb, self.Zb, self.E,
+             dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
+                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)),
+            (self.ICa, self.IZa, self.ICb, self.IZb, self.KI,
+             dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
+                  E_scale=self.KI_scale)),
+        ])
 
     def index(self):
         csa_index_score(self.qI, self.wI, self.KI, self.q_pos, self.I, m=self.wl.m, K_scale=self.KI_scale)
@@ -186,11 +197,14 @@ class HCADecode(_Common):
         self.ws_mqa = _ws(csa_mqa_workspace_size(B, 1, wl.n_h, d, N + wl.n_win), self.dev)
 
     def compress_new(self):
+        """The new token's window row and the just-completed block's entry, one launch."""
         wl, i, N = self.wl, self.i, self.wl.N_cap
-        self._win_rows(i, i + 1, self.win_new, i)
-        csa_compress(self.C, self.Z, None, None, self.E, T=wl.m * N, m=wl.m, overlap=0, s_begin=N - 1,
-                     s_end=N, tok_base=self.blk_tok_base, gamma=self.gamma_kv, eps=wl.eps,
-                     rope_dim=wl.rope_dim, rope_base=wl.rope_base)
+        csa_compress_batch([
+            self._win_job(i, i + 1, self.win_new, i),
+            (self.C, self.Z, None, None, self.E,
+             dict(T=wl.m * N, m=wl.m, overlap=0, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
+                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)),
+        ])
 
     def attend(self):
         wl = self.wl
@@ -247,15 +261,19 @@ class CSAPrefill(_Common):
         self.ws_mqa = _ws(csa_mqa_workspace_size(B, Tq, wl.n_h, d, wl.k + wl.n_win), self.dev)
 
     def compress_new(self):
+        """The chunk's window rows, its complete KV entries and their indexer
+        keys: three independent compressions, one launch."""
         wl = self.wl
         p0, Tq = wl.q_pos0, wl.Tq
-        self._win_rows(p0, p0 + Tq, self.chunk_raw, p0)
         T = p0 + Tq
-        csa_compress(self.Ca, self.Za, self.Cb, self.Zb, self.E, T=T, m=wl.m, overlap=1,
-                     s_begin=self.s_new0, s_end=self.s_new1, tok_base=self.tok_base,
-                     gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)
-        csa_compress(self.ICa, self.IZa, self.ICb, self.IZb, self.KI, T=T, m=wl.m, overlap=1,
-                     s_begin=self.s_new0, s_end=self.s_new1, tok_base=self.tok_base)
+        csa_compress_batch([
+            self._win_job(p0, p0 + Tq, self.chunk_raw, p0),
+            (self.Ca, self.Za, self.Cb, self.Zb, self.E,
+             dict(T=T, m=wl.m, overlap=1, s_begin=self.s_new0, s_end=self.s_new1, tok_base=self.tok_base,
+                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)),
+            (self.ICa, self.IZa, self.ICb, self.IZb, self.KI,
+             dict(T=T, m=wl.m, overlap=1, s_begin=self.s_new0, s_end=self.s_new1, tok_base=self.tok_base)),
+        ])
 
     def index(self):
         csa_index_score(self.qI, self.wI, self.KI, self.q_pos, self.I, m=self.wl.m)

@@ -107,6 +107,59 @@ def test_compress_fp8_output(csa):
     assert mism <= 0.001 * B * n * c
 
 
+def test_compress_batch_matches_separate_calls(csa):
+    """One launch of several jobs (a decode step's window row, KV entry and
+    indexer key, plus an HCA block and an empty job) writes exactly the bytes
+    of the separate calls, and those match the oracle."""
+    g = Gen(160, DEV)
+    B, c, cI, m, T = 3, 512, 128, 4, 4 * 37 + 2
+    n = O.num_entries(T, m)
+    Ca, Za, Cb, Zb = (g.normal(i, (B, T, c), "bf16") for i in (1, 2, 3, 4))
+    ICa, IZa, ICb, IZb = (g.normal(i, (B, T, cI), "bf16") for i in (5, 6, 7, 8))
+    Wr = g.normal(9, (B, T, c), "bf16")
+    H = g.normal(10, (B, 256, c), "bf16")
+    HZ = g.normal(11, (B, 256, c), "bf16")
+    gamma = _gamma(g, 12, c)
+
+    def outputs():
+        return dict(E=torch.full((B, n, c), float("nan"), dtype=torch.bfloat16, device=DEV),
+                    K=torch.zeros((B, n, cI), dtype=torch.float8_e4m3fn, device=DEV),
+                    S=torch.zeros((B, n), dtype=torch.float32, device=DEV),
+                    W=torch.full((B, 16, c), float("nan"), dtype=torch.bfloat16, device=DEV),
+                    Hc=torch.full((B, 2, c), float("nan"), dtype=torch.bfloat16, device=DEV))
+
+    def jobs(o):
+        return [
+            (Wr, None, None, None, o["W"], dict(T=T, m=1, overlap=0, s_begin=T - 16, s_end=T, gamma=gamma,
+                                                 rope_dim=64, out_ring=16)),
+            (Ca, Za, Cb, Zb, o["E"], dict(T=T, m=m, overlap=1, s_begin=0, s_end=n, gamma=gamma, rope_dim=64)),
+            (ICa, IZa, ICb, IZb, o["K"], dict(T=T, m=m, overlap=1, s_begin=n - 5, s_end=n, E_scale=o["S"])),
+            (H, HZ, None, None, o["Hc"], dict(T=256, m=128, overlap=0, s_begin=0, s_end=2, gamma=gamma,
+                                              rope_dim=64)),
+            (Ca, Za, Cb, Zb, o["E"], dict(T=T, m=m, overlap=1, s_begin=3, s_end=3)),   # empty
+        ]
+
+    sep, bat = outputs(), outputs()
+    for C_a, Z_a, C_b, Z_b, E, kw in jobs(sep):
+        csa.csa_compress(C_a, Z_a, C_b, Z_b, E, **kw)
+    csa.csa_compress_batch(jobs(bat))
+    torch.cuda.synchronize()
+    for key in sep:
+        a_, b_ = sep[key], bat[key]
+        if a_.dtype == torch.float8_e4m3fn:
+            a_, b_ = a_.view(torch.uint8), b_.view(torch.uint8)
+        assert torch.equal(torch.nan_to_num(a_.float(), nan=7.0), torch.nan_to_num(b_.float(), nan=7.0)), key
+    # and the batch against the oracle (the KV entries and the HCA block)
+    gam = to_f64(gamma)
+    for b in range(B):
+        ref = O.compress(*(to_f64(x[b]) for x in (Ca, Za, Cb, Zb)), m=m, overlap=1, T=T, gamma=gam,
+                         eps=1e-6, rope_dim=64)
+        assert row_rel_err(to_f64(bat["E"][b]), ref) <= TOL_BF16
+        refh = O.compress(to_f64(H[b]), to_f64(HZ[b]), None, None, m=128, overlap=0, T=256, gamma=gam,
+                          eps=1e-6, rope_dim=64)
+        assert row_rel_err(to_f64(bat["Hc"][b]), refh) <= TOL_BF16
+
+
 # ---------------------------------------------------------------------------
 # a2 indexer score
 # ---------------------------------------------------------------------------
