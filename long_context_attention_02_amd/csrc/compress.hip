@@ -28,6 +28,15 @@ static constexpr int COMP_MAX_G = 8;
 static constexpr int COMP_JU = 8;   // channels per thread whose loads are issued together
 static constexpr int COMP_MAX_JOBS = 8;
 
+// the weights of a missing RMSNorm gamma, so that the gamma loads need no guard
+struct CompOnes {
+  float v[1024];
+  constexpr CompOnes() : v() {
+    for (int i = 0; i < 1024; ++i) v[i] = 1.f;
+  }
+};
+__device__ const CompOnes k_comp_ones{};
+
 // one job's arguments as the kernel reads them (validated on the host)
 struct CompressJob {
   const void *Ca, *Za, *Cb, *Zb;
@@ -78,6 +87,18 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
   const long long ncand = na + nb;
   const size_t base = (size_t)b * (size_t)in_bs;
 
+  // gamma of this thread's output channels and of their RoPE partners, loaded
+  // now so that their latency overlaps the candidates' (c <= 1024)
+  constexpr int OPT = (1024 + COMP_THREADS - 1) / COMP_THREADS;
+  const float* __restrict__ gsrc = gamma ? gamma : k_comp_ones.v;
+  float gj[OPT], gp[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int j = min((int)threadIdx.x + i * COMP_THREADS, c - 1);
+    gj[i] = gsrc[j];
+    gp[i] = gsrc[min(j ^ 1, c - 1)];
+  }
+
   const int tpg = COMP_THREADS / G;
   const int g = threadIdx.x / tpg;
   const int tg = threadIdx.x % tpg;
@@ -101,12 +122,22 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
       const size_t off0 = base + (size_t)(tok - tok_base) * (size_t)c;
       const void* Cp = in_a ? Ca : Cb;
       const void* Zp = in_a ? Za : Zb;
+      // unconditional loads (channel clamped, a missing Z reads C), masked
+      // afterwards: a guarded load becomes a branch with its own wait, and the
+      // COMP_JU loads would then run one memory latency after another
+      const void* Zq = Zp ? Zp : Cp;
       float x[COMP_JU], z[COMP_JU];
 #pragma unroll
       for (int u = 0; u < COMP_JU; ++u) {
-        const int j = j0 + u * tpg;
-        x[u] = j < c ? load_as_f32<IDT>(Cp, off0 + (size_t)j) : 0.f;
-        z[u] = (j < c && Zp) ? load_as_f32<IDT>(Zp, off0 + (size_t)j) : 0.f;
+        const int j = min(j0 + u * tpg, c - 1);
+        x[u] = load_as_f32<IDT>(Cp, off0 + (size_t)j);
+        z[u] = load_as_f32<IDT>(Zq, off0 + (size_t)j);
+      }
+#pragma unroll
+      for (int u = 0; u < COMP_JU; ++u) {
+        const bool live = j0 + u * tpg < c;
+        x[u] = live ? x[u] : 0.f;
+        z[u] = (live && Zp) ? z[u] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < COMP_JU; ++u) {
@@ -137,15 +168,26 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
   // ---- merge the G partials; pooled value per channel
   float ss = 0.f;
   for (int j = threadIdx.x; j < c; j += COMP_THREADS) {
+    // all G partials read at once (group index clamped, the extra ones unused)
+    float pm[COMP_MAX_G], ps[COMP_MAX_G], pa[COMP_MAX_G];
+#pragma unroll
+    for (int q = 0; q < COMP_MAX_G; ++q) {
+      const int o = min(q, G - 1) * c + j;
+      pm[q] = pmax[o];
+      ps[q] = psum[o];
+      pa[q] = pacc[o];
+    }
     float M = -INFINITY;
-    for (int q = 0; q < G; ++q) M = fmaxf(M, pmax[q * c + j]);
+#pragma unroll
+    for (int q = 0; q < COMP_MAX_G; ++q)
+      if (q < G) M = fmaxf(M, pm[q]);
     float S = 0.f, A = 0.f;
-    for (int q = 0; q < G; ++q) {
-      const float mq = pmax[q * c + j];
-      if (mq == -INFINITY) continue;      // group saw no candidate
-      const float f = __expf(mq - M);
-      S += psum[q * c + j] * f;
-      A += pacc[q * c + j] * f;
+#pragma unroll
+    for (int q = 0; q < COMP_MAX_G; ++q) {
+      if (q >= G || pm[q] == -INFINITY) continue;   // no such group, or it saw no candidate
+      const float f = __expf(pm[q] - M);
+      S += ps[q] * f;
+      A += pa[q] * f;
     }
     const float v = S > 0.f ? A / S : 0.f;
     row[j] = v;
@@ -166,15 +208,15 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
   const size_t obase = (size_t)b * (size_t)out_bs + (size_t)orow * (size_t)c;
   const int rbeg = c - rope_dim;
   float amax = 0.f;
-  float outv[(1024 + COMP_THREADS - 1) / COMP_THREADS];
+  float outv[OPT];
   int nv = 0;
   for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) {
-    float v = row[j] * rinv * (gamma ? gamma[j] : 1.f);
+    float v = row[j] * rinv * gj[nv];
     if (j >= rbeg) {
       const int u = (j - rbeg) >> 1;
       float cs, sn;
       rope_cos_sin(pos, u, rope, &cs, &sn);
-      const float other = row[j ^ 1] * rinv * (gamma ? gamma[j ^ 1] : 1.f);
+      const float other = row[j ^ 1] * rinv * gp[nv];
       v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
     }
     outv[nv] = v;

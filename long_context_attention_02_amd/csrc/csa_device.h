@@ -121,27 +121,42 @@ __device__ __forceinline__ void rope_cos_sin(long long pos, int u, RopeRatio rr,
 }
 
 // ---- wave / block reductions ------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+// A butterfly inside each row of 16 lanes through DPP (quad permutes, half-row
+// and row mirrors), then across rows with the gfx950 row swaps; every step
+// combines a lane's value with its partner's symmetrically, so every lane ends
+// with the same bits.  No LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce_f(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  v = op(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));   // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// block-wide sum / max; `red` is __shared__ float[>= blockDim/64]; all threads get the result
+// block-wide sum / max for up to 1024 threads; `red` is __shared__ float[>= blockDim / 64];
+// all threads get the result (the waves' results are combined in wave order)
 template <bool MAX>
 __device__ __forceinline__ float block_reduce(float v, float* red) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-  v = MAX ? wave_max(v) : wave_sum(v);
-  __syncthreads();
+  v = wave_reduce_f<MAX>(v);
+  __syncthreads();   // an earlier reduction may still be reading red
   if (lane == 0) red[wid] = v;
   __syncthreads();
   float r = red[0];
-  for (int w = 1; w < nw; ++w) r = MAX ? fmaxf(r, red[w]) : (r + red[w]);
+#pragma unroll
+  for (int w = 1; w < 16; ++w) {
+    const float x = red[min(w, nw - 1)];   // unguarded reads: all in flight together
+    r = (w < nw) ? (MAX ? fmaxf(r, x) : (r + x)) : r;
+  }
   return r;
 }
 

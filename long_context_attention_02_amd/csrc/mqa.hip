@@ -1214,16 +1214,16 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
     float M = sig, Z, o0 = 0.f, o1 = 0.f;
     if (n_split <= CB) {
       // every split's (max, sum) and this pair of its output, all in flight at once
+      // unconditional loads (split index clamped; the extra ones are never
+      // used): a guarded load becomes a branch with its own wait
       float ms[CB], ls[CB], a0[CB], a1[CB];
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
-        if (s < n_split) {
-          const float* ps = base + s * sstride;
-          ms[s] = ps[D];
-          ls[s] = ps[D + 1];
-          a0[s] = ps[d0];
-          a1[s] = ps[d0 + 1];
-        }
+        const float* ps = base + min(s, n_split - 1) * sstride;
+        ms[s] = ps[D];
+        ls[s] = ps[D + 1];
+        a0[s] = ps[d0];
+        a1[s] = ps[d0 + 1];
       }
 #pragma unroll
       for (int s = 0; s < CB; ++s)
