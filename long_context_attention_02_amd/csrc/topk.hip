@@ -155,11 +155,18 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkS
   int sum = 0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) sum += (int)c[q];
+  // inclusive scan over the lanes: inside each 16-lane row by DPP row shifts
+  // (lanes without a source add 0), then the totals of the rows above
   int incl = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);   // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);   // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);   // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);   // row_shr:8
+  {
+    const int t0 = __builtin_amdgcn_readlane(incl, 15), t1 = __builtin_amdgcn_readlane(incl, 31);
+    const int t2 = __builtin_amdgcn_readlane(incl, 47);
+    const int row = lane >> 4;
+    incl += (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
   }
   const int above = incl - sum;
   if (above < need && need <= incl) {   // exactly one lane
@@ -234,53 +241,73 @@ __device__ void radix_half(const Src& src, long long n, uint32_t lb, uint32_t k_
   }
 }
 
-// value of lane (lane ^ M) for M < 64: DPP quad permutes for 1 and 2,
-// ds_swizzle (bit mode, xor mask) for 4..16, ds_bpermute for 32
+// value of lane (lane ^ M) for M < 64, in VALU only: DPP quad permutes (1, 2),
+// a quad reversal then a half-row mirror (4), a row rotation by 8 (8), and the
+// gfx950 row swaps (16, 32), which hand each lane its own value and its
+// partner's
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
 template <int M>
 __device__ __forceinline__ uint32_t xchg_u32(uint32_t v) {
-  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-  else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x101F);
-  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x201F);
-  else if constexpr (M == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-  else return (uint32_t)__shfl_xor((int)v, M, 64);
+  if constexpr (M == 1) return dpp_u32<0xB1>(v);                  // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_u32<0x4E>(v);             // quad_perm [2,3,0,1]
+  else if constexpr (M == 4) return dpp_u32<0x141>(dpp_u32<0x1B>(v));   // [3,2,1,0], then i <-> 7 - i
+  else if constexpr (M == 8) return dpp_u32<0x128>(v);            // row_ror:8
+  else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "lane distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
 }
 
 // one compare-exchange step of a descending bitonic sort at (size, stride):
-// thread t holds element t
+// thread t holds element t.  Partners in other waves trade through one of two
+// LDS buffers (alternating, so one barrier per step suffices: a buffer is
+// rewritten only after the barrier of the step that follows its readers).
 template <int STRIDE>
-__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int t, int size, TopkShared& sh, int P) {
+__device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int t, bool desc, TopkShared& sh, int P,
+                                                 int& par) {
   uint64_t y;
   if constexpr (STRIDE >= 64) {
+    uint64_t* b = sh.buf + (par ? TK_THREADS : 0);
+    if (t < P) b[t] = x;
     __syncthreads();
-    if (t < P) sh.buf[t] = x;
-    __syncthreads();
-    y = t < P ? sh.buf[t ^ STRIDE] : 0ull;
+    y = t < P ? b[t ^ STRIDE] : 0ull;
+    par ^= 1;
   } else {
     const uint32_t lo = xchg_u32<STRIDE>((uint32_t)x), hi = xchg_u32<STRIDE>((uint32_t)(x >> 32));
     y = ((uint64_t)hi << 32) | lo;
   }
-  const bool desc = (t & size) == 0;
-  const bool lower = (t & STRIDE) == 0;
-  const uint64_t mx = x > y ? x : y, mn = x > y ? y : x;
-  return (lower == desc) ? mx : mn;
+  // the lower lane of a descending block keeps the larger key, the upper the
+  // smaller; ascending blocks the other way round (one compare, one select)
+  const bool take_max = ((t & STRIDE) == 0) == desc;
+  return ((x > y) == take_max) ? x : y;
 }
 
 // all strides of one merge size, largest first (compile-time strides)
 template <int STRIDE>
-__device__ __forceinline__ uint64_t bitonic_merge(uint64_t x, int t, int size, TopkShared& sh, int P) {
-  if (STRIDE < size) x = bitonic_step<STRIDE>(x, t, size, sh, P);
-  if constexpr (STRIDE > 1) x = bitonic_merge<STRIDE / 2>(x, t, size, sh, P);
+__device__ __forceinline__ uint64_t bitonic_merge(uint64_t x, int t, int size, bool desc, TopkShared& sh,
+                                                  int P, int& par) {
+  if (STRIDE < size) x = bitonic_step<STRIDE>(x, t, desc, sh, P, par);
+  if constexpr (STRIDE > 1) x = bitonic_merge<STRIDE / 2>(x, t, size, desc, sh, P, par);
   return x;
 }
 
 // Bitonic sort of sh.buf[0 .. P), descending, P a power of two <= TK_THREADS:
 // thread t holds element t; partners closer than 64 sit in the same wave and
-// trade through DPP / swizzles / lane permutes, farther ones through LDS.
+// trade through lane permutes, farther ones through LDS.
 __device__ void sort_desc_regs(TopkShared& sh, int P) {
+  static_assert(2 * TK_THREADS <= TK_KMAX, "two exchange buffers");
   const int t = threadIdx.x;
-  uint64_t x = t < P ? sh.buf[t] : 0ull;
-  for (int size = 2; size <= P; size <<= 1) x = bitonic_merge<TK_THREADS / 2>(x, t, size, sh, P);
+  uint64_t x = t < P ? sh.buf[t] : 0ull;   // each thread reads and later writes only slot t first
+  int par = 0;
+  for (int size = 2; size <= P; size <<= 1)
+    x = bitonic_merge<TK_THREADS / 2>(x, t, size, (t & size) == 0, sh, P, par);   // block of t descending?
   __syncthreads();
   if (t < P) sh.buf[t] = x;
   __syncthreads();
