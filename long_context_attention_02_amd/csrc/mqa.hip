@@ -63,6 +63,17 @@ __device__ __forceinline__ long long slot_row(long long slot, const QuerySlots& 
   return ((long long)b * W_cap + (tau % W_cap)) * d;
 }
 
+// Split partials in the workspace.  O of (query row, split, head) is the D-float
+// row ws[((row * n_split + sp) * n_h + h) * D] (16-byte aligned rows); the
+// (max, sum) pairs follow all O rows, pair u = (row * n_split + sp) * n_h + h at
+// part_ml(...)[2 u].  n_units = (query rows) * n_split.
+__device__ __forceinline__ float* part_ml(float* ws, long long n_units, int n_h, int D) {
+  return ws + (size_t)n_units * (size_t)n_h * (size_t)D;
+}
+__device__ __forceinline__ const float* part_ml(const float* ws, long long n_units, int n_h, int D) {
+  return ws + (size_t)n_units * (size_t)n_h * (size_t)D;
+}
+
 // ---------------------------------------------------------------------------
 // generic path (fp32 or bf16 storage): one workgroup per (query, head)
 // ---------------------------------------------------------------------------
@@ -426,14 +437,15 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
   } else {
     // ---- partial state: O (unnormalised, relative to m_run), then m_run, l_run
     const size_t pbase = (row * n_split + sp) * (size_t)n_h;
+    float* ml = part_ml(ws, n_units, n_h, D);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        ws[(pbase + h0 + 4 * g + r) * (D + 2) + 16 * nt + j] = O[nt][r];
+        ws[(pbase + h0 + 4 * g + r) * D + 16 * nt + j] = O[nt][r];
     if (g == 0) {
-      ws[(pbase + hq) * (D + 2) + D] = m_run;
-      ws[(pbase + hq) * (D + 2) + D + 1] = l_run;
+      ml[2 * (pbase + hq)] = m_run;
+      ml[2 * (pbase + hq) + 1] = l_run;
     }
   }
 }
@@ -683,11 +695,12 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          ws[(pbase + 16 * mt + 4 * g + r) * (D + 2) + dbase + 16 * nt + j] = O[mt][nt][r];
+          ws[(pbase + 16 * mt + 4 * g + r) * D + dbase + 16 * nt + j] = O[mt][nt][r];
     }
     if (threadIdx.x < 16 * ntiles) {
-      ws[(pbase + threadIdx.x) * (D + 2) + D] = mstat[threadIdx.x];
-      ws[(pbase + threadIdx.x) * (D + 2) + D + 1] = lstat[threadIdx.x];
+      float* ml = part_ml(ws, n_units, n_h, D);
+      ml[2 * (pbase + threadIdx.x)] = mstat[threadIdx.x];
+      ml[2 * (pbase + threadIdx.x) + 1] = lstat[threadIdx.x];
     }
   }
 }
@@ -1177,20 +1190,47 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
         }
       }
   } else {
+    // The partial O goes out through LDS, so that every store writes whole
+    // 16-byte pieces of one head's row (straight from the MFMA layout a store
+    // instruction would write four 64-byte pieces of four rows).  A wave stages
+    // 16 heads x CW dims at a time (rows padded by 4 floats, so the four lane
+    // groups hit distinct banks) in its own part of the chunk ring, and reads
+    // them back 4 dims per lane.
+    constexpr int CW = D >= 512 ? 256 : D / 2;   // dims per staged block
+    constexpr int CRS = CW + 4;                  // staged row stride (floats)
+    constexpr int LPH = CW / 4;                  // lanes per head row on the way out
+    static_assert(16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
+    lds_sync<0>();   // every wave is done with the chunk ring
+    float* stg = (float*)kv + wave * 16 * CRS;
     const size_t pb = (row * n_split + sp) * (size_t)n_h + h0;
 #pragma unroll
     for (int ht = 0; ht < HTW; ++ht)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float* dst = ws + (pb + 16 * ht + 4 * g + r) * (D + 2);
+      for (int cb = 0; cb < D / CW; ++cb) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dst[16 * nt + j] = O[ht][nt][r];
+        for (int nt = 0; nt < CW / 16; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) stg[(4 * g + r) * CRS + 16 * nt + j] = O[ht][cb * (CW / 16) + nt][r];
+        // the writes of every lane land before any lane reads (and the reads below
+        // finish before the next block's writes: their stores consume them first)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int it = 0; it < 16 * CW / 256; ++it) {
+          const int f = it * 64 + lane;   // 4-float piece of the 16 x CW block
+          const int hh = f / LPH, c4 = f % LPH;
+          const f32x4_t v = *(const f32x4_t*)(stg + hh * CRS + 4 * c4);
+          *(f32x4_t*)(ws + (pb + 16 * ht + hh) * D + cb * CW + 4 * c4) = v;
+        }
+        asm volatile("" ::: "memory");
       }
     if (g == 0) {
+      float* ml = part_ml(ws, n_units, n_h, D);
 #pragma unroll
       for (int ht = 0; ht < HTW; ++ht) {
-        ws[(pb + 16 * ht + j) * (D + 2) + D] = ref[ht];
-        ws[(pb + 16 * ht + j) * (D + 2) + D + 1] = lsum[ht];
+        ml[2 * (pb + 16 * ht + j)] = ref[ht];
+        ml[2 * (pb + 16 * ht + j) + 1] = lsum[ht];
       }
     }
   }
@@ -1206,8 +1246,10 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const size_t row = (size_t)b * Tq + t;
   const long long i = q_pos[row];
   const float sig = sink ? sink[h] : -INFINITY;
-  const float* base = ws + (row * n_split * (size_t)n_h + h) * (D + 2);
-  const size_t sstride = (size_t)n_h * (D + 2);
+  const float* base = ws + (row * n_split * (size_t)n_h + h) * D;   // O of split 0
+  const size_t sstride = (size_t)n_h * D;
+  const float* mlb = part_ml(ws, (long long)gridDim.z * Tq * n_split, n_h, D) + 2 * (row * n_split * (size_t)n_h + h);
+  const size_t mstride = 2 * (size_t)n_h;
   const int rbeg = D - rope_dim;
   for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
     const int d0 = 2 * u;
@@ -1216,14 +1258,21 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
       // every split's (max, sum) and this pair of its output, all in flight at once
       // unconditional loads (split index clamped; the extra ones are never
       // used): a guarded load becomes a branch with its own wait
+      // lane l of each wave fetches the (max, sum) of split l % CB with one vector
+      // load in the same batch as the outputs; readlane hands them to every lane
       float ms[CB], ls[CB], a0[CB], a1[CB];
+      const float2 mlv = *(const float2*)(mlb + min((int)(threadIdx.x % CB), n_split - 1) * mstride);
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
-        const float* ps = base + min(s, n_split - 1) * sstride;
-        ms[s] = ps[D];
-        ls[s] = ps[D + 1];
+        const int sc = min(s, n_split - 1);
+        const float* ps = base + sc * sstride;
         a0[s] = ps[d0];
         a1[s] = ps[d0 + 1];
+      }
+#pragma unroll
+      for (int s = 0; s < CB; ++s) {
+        ms[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.x), s));
+        ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.y), s));
       }
 #pragma unroll
       for (int s = 0; s < CB; ++s)
@@ -1241,15 +1290,15 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
         }
       }
     } else {
-      for (int s = 0; s < n_split; ++s) M = fmaxf(M, base[s * sstride + D]);
+      for (int s = 0; s < n_split; ++s) M = fmaxf(M, mlb[s * mstride]);
       Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
       for (int s = 0; s < n_split; ++s) {
-        const float ms = base[s * sstride + D];
-        if (ms != -INFINITY) Z += base[s * sstride + D + 1] * __expf(ms - M);
+        const float ms = mlb[s * mstride];
+        if (ms != -INFINITY) Z += mlb[s * mstride + 1] * __expf(ms - M);
       }
       for (int s = 0; s < n_split; ++s) {
         const float* ps = base + s * sstride;
-        const float ms = ps[D];
+        const float ms = mlb[s * mstride];
         const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
         o0 += ps[d0] * f;
         o1 += ps[d0 + 1] * f;
@@ -1379,6 +1428,10 @@ int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
     mqa_split(a.Tq, a.n_h, a.d, slots_max, &kps, &n_split);
     if (n_split > 1 && a.ws_bytes < mqa_workspace_bytes(a.B, a.Tq, a.n_h, a.d, slots_max, a.dtype)) {
       *why = "workspace smaller than csa_mqa_workspace_size()";
+      return 5;
+    }
+    if (n_split > 1 && ((uintptr_t)a.ws & 15u) != 0) {
+      *why = "workspace must be 16-byte aligned";
       return 5;
     }
     if (mqa_decode_ok(a.Tq, a.n_h, a.d) &&
