@@ -644,13 +644,17 @@ static void launch_mfma(const IndexArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((index_mfma_prefill<QH, KS, KDT, PF_QPW>), grid, dim3(256), 0, st, q, a.w,
                        a.K, a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out);
   } else {
-    // one round of resident waves over the chip, shared evenly by the query
-    // rows; enough waves per row that each wave's scores fit its LDS stage
+    // at most one round of resident waves over the chip, shared by the query
+    // rows: a power of two per row (units then divide evenly at power-of-two
+    // caches: at 16 x 262,144 keys, 128 waves per row of 32 units each beat
+    // 192 waves of 21 or 22 units by 2.5%); enough waves per row that each
+    // wave's scores fit its LDS stage
     auto kfn = index_mfma_decode<QH, KS, KDT>;
     const long long waves = resident_waves((const void*)kfn, 256);
     const long long rows = (long long)a.B * a.Tq;
     const long long nunits = (a.N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT);
-    long long wpr = max(1LL, waves / rows);
+    long long wpr = 1;
+    while (2 * wpr <= waves / rows) wpr *= 2;
     wpr = max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
     wpr = min(wpr, nunits);
     dim3 grid((unsigned)((wpr + 3) / 4), (unsigned)a.Tq, (unsigned)a.B);
