@@ -28,15 +28,6 @@ static constexpr int COMP_MAX_G = 8;
 static constexpr int COMP_JU = 8;   // channels per thread whose loads are issued together
 static constexpr int COMP_MAX_JOBS = 8;
 
-// the weights of a missing RMSNorm gamma, so that the gamma loads need no guard
-struct CompOnes {
-  float v[1024];
-  constexpr CompOnes() : v() {
-    for (int i = 0; i < 1024; ++i) v[i] = 1.f;
-  }
-};
-__device__ const CompOnes k_comp_ones{};
-
 // one job's arguments as the kernel reads them (validated on the host)
 struct CompressJob {
   const void *Ca, *Za, *Cb, *Zb;
@@ -90,7 +81,7 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
   // gamma of this thread's output channels and of their RoPE partners, loaded
   // now so that their latency overlaps the candidates' (c <= 1024)
   constexpr int OPT = (1024 + COMP_THREADS - 1) / COMP_THREADS;
-  const float* __restrict__ gsrc = gamma ? gamma : k_comp_ones.v;
+  const float* __restrict__ gsrc = gamma ? gamma : k_ones.v;
   float gj[OPT], gp[OPT];
 #pragma unroll
   for (int i = 0; i < OPT; ++i) {

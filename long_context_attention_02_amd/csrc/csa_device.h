@@ -120,6 +120,16 @@ __device__ __forceinline__ void rope_cos_sin(long long pos, int u, RopeRatio rr,
   *s = sn;
 }
 
+// 1024 ones: the weights of a missing RMSNorm gamma, so that gamma loads need
+// no guard (a guarded load compiles to a branch with its own wait)
+struct OnesTable {
+  float v[1024];
+  constexpr OnesTable() : v() {
+    for (int i = 0; i < 1024; ++i) v[i] = 1.f;
+  }
+};
+static __device__ const OnesTable k_ones{};
+
 // ---- wave / block reductions ------------------------------------------------
 // A butterfly inside each row of 16 lanes through DPP (quad permutes, half-row
 // and row mirrors), then across rows with the gfx950 row swaps; every step

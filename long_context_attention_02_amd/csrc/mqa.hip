@@ -709,7 +709,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // decode kernel (few queries per sequence, heads a multiple of 16 per wave).
 //
 // A workgroup takes one query, a group of 16 HTW NW heads and a fixed range of
-// at most MQ_DEC_SPLIT_MAX key slots.  Wave w owns HTW 16-head tiles of the group
+// at most MQ_DEC_TABLE key slots.  Wave w owns HTW 16-head tiles of the group
 // (one at D = 512, two below) over all D dims, so scores, softmax and P.V stay
 // inside the wave and need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
 // MQ_DEC_NBUF chunks filled with global_load_lds, MQ_DEC_NBUF - 1 chunks ahead,
@@ -728,6 +728,10 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 static constexpr int MQ_DEC_SPLIT_MAX = 288;
 static constexpr int MQ_DEC_SPLIT_SMALL = 192;
 static constexpr long long MQ_DEC_SMALL_UPTO = 1536;
+// With many queries per sequence (prefill) the queries give the parallelism:
+// one range holds up to MQ_DEC_TABLE slots (the slot table's capacity), so a
+// CSA query (k + n_win slots) is one workgroup and needs no combine.
+static constexpr int MQ_DEC_TABLE = 2048;
 static constexpr int MQ_DEC_NBUF = 3;      // LDS chunk ring
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations complete
@@ -794,21 +798,21 @@ struct DecRows {
 };
 
 // row of slot `rel` of the range (e = its selected entry when sparse); *ok is
-// false for an absent slot, whose row is the dummy
+// false for an absent slot, whose row is the dummy.  Selects only, no branches:
+// a divergent branch here would pull the selection loads into it, each with
+// its own wait.
 template <int D, bool DENSE>
 __device__ __forceinline__ const uint16_t* dec_slot_row(int rel, int e, const DecRows& R, bool* ok) {
-  *ok = false;
-  if (rel >= R.n_rows) return R.dummy;
-  if (rel < R.n_sel) {
-    if (DENSE) e = (int)(R.s0 + rel);
-    if (!DENSE && (e < 0 || e >= R.N_cap)) return R.dummy;
-    *ok = true;
-    return R.E_b + (size_t)e * D;
-  }
+  const bool in_rows = rel < R.n_rows;
+  const bool is_sel = rel < R.n_sel;
+  const long long ent = DENSE ? R.s0 + rel : (long long)e;
+  const bool ent_ok = DENSE || (e >= 0 && e < R.N_cap);
   int ring = R.ring0 + (rel - R.n_sel);   // fewer window slots than ring rows: one wrap at most
-  if (ring >= R.W_cap) ring -= R.W_cap;
-  *ok = true;
-  return R.W_b + (size_t)ring * D;
+  ring = ring >= R.W_cap ? ring - R.W_cap : ring;
+  *ok = in_rows && (!is_sel || ent_ok);
+  const uintptr_t pe = (uintptr_t)R.E_b + (uintptr_t)(max(ent, 0LL) * (2LL * D));
+  const uintptr_t pw = (uintptr_t)R.W_b + (uintptr_t)((long long)max(ring, 0) * (2LL * D));
+  return (const uint16_t*)(!*ok ? (uintptr_t)R.dummy : (is_sel ? pe : pw));
 }
 
 // start loading chunk c: rows RPW w .. RPW w + RPW - 1 of it are this wave's,
@@ -870,9 +874,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_DEC_NBUF * CHB
   __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
   __shared__ float gam[D];
-  constexpr int NCH_MAX = MQ_DEC_SPLIT_MAX / MQ_CH;
-  static_assert(MQ_DEC_SPLIT_MAX % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0, "whole chunks per range");
-  __shared__ const uint16_t* sptr[MQ_DEC_SPLIT_MAX];   // row of every slot of the range
+  constexpr int NCH_MAX = MQ_DEC_TABLE / MQ_CH;
+  static_assert(MQ_DEC_SPLIT_MAX % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0 &&
+                    MQ_DEC_TABLE % MQ_CH == 0 && MQ_DEC_SPLIT_MAX <= MQ_DEC_TABLE,
+                "whole chunks per range");
+  __shared__ const uint16_t* sptr[MQ_DEC_TABLE];   // row of every slot of the range
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
@@ -909,16 +915,19 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   // the range's selection, the query pieces and gamma are loaded and used
   // before any chunk load is issued: a wait on an ordinary load issued before an
   // LDS-DMA load becomes a wait on every load in flight
-  constexpr int IPT = (MQ_DEC_SPLIT_MAX + 64 * NW - 1) / (64 * NW);
+  constexpr int IPT = (MQ_DEC_TABLE + 64 * NW - 1) / (64 * NW);
   int iv[IPT];
   if (!DENSE) {
     // bounded by the row's k selections only, so these loads need not wait for q_pos
-    const int* idx_sp = idx + row * (size_t)k + R.s0;
+    // unguarded loads (index clamped into the row, masked after): a guarded
+    // load compiles to a branch with its own wait
+    const int* idx_row = idx + row * (size_t)k;
     const int kcap = (int)max(0LL, min((long long)kps, (long long)k - R.s0));
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
       const int t = threadIdx.x + 64 * NW * e;
-      iv[e] = t < kcap ? idx_sp[t] : -1;
+      const int v = idx_row[min(R.s0 + t, (long long)k - 1)];
+      iv[e] = t < kcap ? v : -1;
     }
   }
   u32x4_t raw[HTW][KS];
@@ -932,15 +941,18 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
   for (int e = 0; e < GPT; ++e) {
     const int t = threadIdx.x + 64 * NW * e;
-    gv[e] = (t < D && gamma_q) ? gamma_q[t] : 1.f;
+    gv[e] = (gamma_q ? gamma_q : k_ones.v)[min(t, D - 1)];
   }
   // slot table: thread t resolves slot t of the range once, for every wave
+  // (only as many rounds as the range has slots; the condition is uniform)
+  const int ipt = (kps + 64 * NW - 1) / (64 * NW);
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
+    if (e >= ipt) break;
     const int t = threadIdx.x + 64 * NW * e;
     bool ok;
     const uint16_t* p = dec_slot_row<D, DENSE>(t, DENSE ? 0 : iv[e], R, &ok);
-    if (t < MQ_DEC_SPLIT_MAX) sptr[t] = p;
+    if (t < MQ_DEC_TABLE) sptr[t] = p;
     const unsigned long long bal = __ballot(ok);
     if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
   }
@@ -1333,14 +1345,20 @@ long long mqa_slots_max(const MqaArgs& a) {
 
 static int dec_heads_per_wave(int d) { return d >= 512 ? 16 * dec_htw<512>() : 16 * dec_htw<256>(); }
 
+// the streaming kernel (mqa_decode_kernel) covers the shape: decode splits a
+// query's slots over workgroups, prefill gives each query one range
 static bool mqa_decode_ok(int Tq, int n_h, int d) {
-  return Tq < MQ_SPLIT_BELOW_TQ && n_h % dec_heads_per_wave(d) == 0;
+  (void)Tq;
+  return n_h % dec_heads_per_wave(d) == 0;
 }
 
 // slots per workgroup and splits per query; depends on the shape only, never on B
 static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int* n_split) {
   if (mqa_decode_ok(Tq, n_h, d)) {
-    *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_MAX;
+    if (Tq < MQ_SPLIT_BELOW_TQ)
+      *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_MAX;
+    else
+      *kps = (int)min((long long)MQ_DEC_TABLE, max(1LL, (slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH);
     *n_split = (int)max(1LL, (slots_max + *kps - 1) / *kps);
   } else if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
     long long s = ((slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH;
