@@ -101,18 +101,23 @@ def prefill_indexer(steps: int, warmup: int):
     for _ in range(warmup):
         csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
-    for _ in range(steps):
+    # every launch timed on its own (timing-only events); the median is reported,
+    # the mean beside it (single launches vary by a few percent with the clock)
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
         csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
-    ev[1].record()
+        b.record()
     torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    ms = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+    ms_mean = sum(per) / len(per)
     pairs = sum(min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq))
     flops = 2.0 * pairs * wl.H_I * wl.d_I
     tfs = flops / (ms * 1e-3) / 1e12
     del qI, wI, K, I
-    return {"workload": wl.name, "ms": round(ms, 4), "TFLOP/s": round(tfs, 2),
+    return {"workload": wl.name, "ms": round(ms, 4), "ms_mean": round(ms_mean, 4),
+            "ms_min": round(per[0], 4), "launches": steps, "TFLOP/s": round(tfs, 2),
             "causal_flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}}
@@ -303,7 +308,7 @@ def main():
     if not args.no_prefill:
         del run.I
         torch.cuda.empty_cache()
-        result["prefill_indexer"] = prefill_indexer(steps=10, warmup=3)
+        result["prefill_indexer"] = prefill_indexer(steps=11, warmup=5)
     if not args.no_secondary:
         if hasattr(run, "I"):
             del run.I

@@ -854,7 +854,7 @@ __device__ __forceinline__ float quad_sum(float x) {
 template <int D>
 __host__ __device__ constexpr int dec_htw() { return D >= 512 ? 1 : 2; }
 
-template <int D, bool DENSE, int NW>
+template <int D, bool DENSE, int NW, int TBL>
 __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
@@ -874,11 +874,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   extern __shared__ __attribute__((aligned(16))) uint8_t kv[];   // MQ_DEC_NBUF * CHB
   __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
   __shared__ float gam[D];
-  constexpr int NCH_MAX = MQ_DEC_TABLE / MQ_CH;
+  constexpr int NCH_MAX = TBL / MQ_CH;   // TBL: slot table capacity (a range's slots at most)
   static_assert(MQ_DEC_SPLIT_MAX % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0 &&
-                    MQ_DEC_TABLE % MQ_CH == 0 && MQ_DEC_SPLIT_MAX <= MQ_DEC_TABLE,
+                    TBL % MQ_CH == 0 && MQ_DEC_SPLIT_MAX <= MQ_DEC_TABLE,
                 "whole chunks per range");
-  __shared__ const uint16_t* sptr[MQ_DEC_TABLE];   // row of every slot of the range
+  __shared__ const uint16_t* sptr[TBL];   // row of every slot of the range
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
@@ -915,7 +915,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   // the range's selection, the query pieces and gamma are loaded and used
   // before any chunk load is issued: a wait on an ordinary load issued before an
   // LDS-DMA load becomes a wait on every load in flight
-  constexpr int IPT = (MQ_DEC_TABLE + 64 * NW - 1) / (64 * NW);
+  constexpr int IPT = (TBL + 64 * NW - 1) / (64 * NW);
   int iv[IPT];
   if (!DENSE) {
     // bounded by the row's k selections only, so these loads need not wait for q_pos
@@ -941,18 +941,21 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
   for (int e = 0; e < GPT; ++e) {
     const int t = threadIdx.x + 64 * NW * e;
-    gv[e] = (gamma_q ? gamma_q : k_ones.v)[min(t, D - 1)];
+    // unguarded: without gamma the load reads the query array (n_h >= 16 rows of
+    // D bf16, so at least D floats) and the value is replaced by 1
+    const float* gsrc = gamma_q ? gamma_q : (const float*)q;
+    const float gl = gsrc[min(t, D - 1)];
+    gv[e] = gamma_q ? gl : 1.f;
   }
   // slot table: thread t resolves slot t of the range once, for every wave
-  // (only as many rounds as the range has slots; the condition is uniform)
-  const int ipt = (kps + 64 * NW - 1) / (64 * NW);
+  // (straight-line code: no branch for the compiler to sink the selection
+  // loads into, where each would get its own wait)
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    if (e >= ipt) break;
     const int t = threadIdx.x + 64 * NW * e;
     bool ok;
     const uint16_t* p = dec_slot_row<D, DENSE>(t, DENSE ? 0 : iv[e], R, &ok);
-    if (t < MQ_DEC_TABLE) sptr[t] = p;
+    if (t < TBL) sptr[t] = p;
     const unsigned long long bal = __ballot(ok);
     if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
   }
@@ -1407,7 +1410,9 @@ static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
   const size_t lds = (size_t)MQ_DEC_NBUF * MQ_CH * (2 * D + 16);
-  auto kfn = mqa_decode_kernel<D, DENSE, NW>;
+  // the small slot table for decode ranges (<= 288 slots), the large one for prefill
+  auto kfn = kps <= MQ_DEC_SPLIT_MAX ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_SPLIT_MAX>
+                                     : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
