@@ -161,6 +161,12 @@ def test_mqa_validation(lib):
     assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 29 * 64 * 514 * 4
     assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * 514 * 4
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
+    need = lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128)
+    assert sparse(k=1024, nh=128, d=512, B=16, ws=FAKE + 4, wsb=need + 16) == CSA_E_WORKSPACE
+    assert b"16-byte aligned" in lib.csa_last_error()
+    # prefill (16 or more queries per sequence): one range of up to 2,048 slots per query
+    assert lib.csa_mqa_workspace_size(1, 16384, 128, 512, 1024 + 128) == 0
+    assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * 130 * 4
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED
 

@@ -47,6 +47,11 @@ COMPRESS_CASES = [
     ("hca_bf16_partial_block", 2, 300, 300, 0, 256, 128, 0, 0, 3, "bf16", "bf16", True, 64, 0, True),
     ("window_rows_m1_ring", 2, 300, 300, 0, 512, 1, 0, 172, 300, "bf16", "bf16", True, 64, 128, False),
     ("uniform_weights_no_Z", 1, 64, 64, 0, 96, 4, 1, 0, 16, "f32", "f32", False, 0, 0, False),
+    # 256 or more (sequence, entry) pairs: the wave-per-entry kernel
+    ("many_csa_bf16_entries", 2, 2050, 2050, 0, 512, 4, 1, 0, 513, "bf16", "bf16", True, 64, 0, True),
+    ("many_csa_f32_entries_to_bf16", 1, 1203, 1203, 0, 64, 4, 1, 0, 301, "f32", "bf16", True, 16, 0, True),
+    ("many_window_rows_ring", 2, 700, 700, 0, 512, 1, 0, 300, 700, "bf16", "bf16", True, 64, 512, False),
+    ("many_entries_tail_rows", 1, 1400, 1032, 368, 128, 4, 1, 93, 350, "bf16", "f32", False, 0, 0, True),
 ]
 
 
@@ -283,6 +288,9 @@ MQA_CASES = [
     ("bf16_generic_h8", False, "bf16", 1, 2, 8, 64, 100, 20, 4, 10, 10, 16, "normal", True, "all"),
     ("bf16_decode_one_split_h32_d256", False, "bf16", 2, 3, 32, 256, 300, 100, 4, 64, 64, 32, "normal", True, "partial"),
     ("bf16_decode_dense_h96_d128", True, "bf16", 2, 1, 96, 128, 700, 0, 4, 16, 32, 32, "none", False, "all"),
+    # prefill through the streaming kernel: a full 2,048-slot range, then two ranges and a combine
+    ("bf16_sparse_prefill_table_full", False, "bf16", 1, 16, 32, 128, 3000, 2000, 4, 48, 64, 32, "none", False, "all"),
+    ("bf16_dense_prefill_two_ranges", True, "bf16", 1, 16, 32, 128, 2300, 0, 4, 64, 128, 32, "normal", True, "all"),
 ]
 
 
