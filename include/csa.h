@@ -182,8 +182,10 @@ int csa_topk(const float* I, const int* q_pos, int B, int Tq, long long N_cap, i
  *  dtype   : F32 or BF16 for q, E, W and out.  out: [B][Tq][n_h][d].
  *  No key and no sink gives a zero output row.
  *  workspace: at least csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win) bytes,
- *            16-byte aligned (split partials: O rows of d floats, then the
- *            (max, sum) pairs); contents on entry do not matter.
+ *            16-byte aligned (split partials: per (query, split, head) the
+ *            output over that split's keys divided by its softmax sum, as d
+ *            fp16 values saturated at +-65504, then the fp32 (max, sum)
+ *            pairs); contents on entry do not matter.
  */
 size_t csa_mqa_workspace_size(int B, int Tq, int n_h, int d, long long n_keys_max);
 int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,

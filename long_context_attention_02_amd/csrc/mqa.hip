@@ -63,16 +63,26 @@ __device__ __forceinline__ long long slot_row(long long slot, const QuerySlots& 
   return ((long long)b * W_cap + (tau % W_cap)) * d;
 }
 
-// Split partials in the workspace.  O of (query row, split, head) is the D-float
-// row ws[((row * n_split + sp) * n_h + h) * D] (16-byte aligned rows); the
-// (max, sum) pairs follow all O rows, pair u = (row * n_split + sp) * n_h + h at
-// part_ml(...)[2 u].  n_units = (query rows) * n_split.
+// Split partials in the workspace.  The output of (query row, split, head)
+// divided by its softmax sum is the fp16 row part_o(ws)[((row * n_split + sp) *
+// n_h + h) * D] (16-byte aligned rows); the float (max, sum) pairs follow all
+// rows, pair u = (row * n_split + sp) * n_h + h at part_ml(...)[2 u].  n_units =
+// (query rows) * n_split.  Divided by the sum, a row is a weighted mean of the
+// value rows, so fp16 holds it with 11 significant bits (half the bytes of fp32);
+// values beyond the fp16 range saturate at +-65504 (part_h).
+__device__ __forceinline__ _Float16* part_o(float* ws) { return (_Float16*)ws; }
+__device__ __forceinline__ const _Float16* part_o(const float* ws) { return (const _Float16*)ws; }
 __device__ __forceinline__ float* part_ml(float* ws, long long n_units, int n_h, int D) {
-  return ws + (size_t)n_units * (size_t)n_h * (size_t)D;
+  return (float*)(part_o(ws) + (size_t)n_units * (size_t)n_h * (size_t)D);
 }
 __device__ __forceinline__ const float* part_ml(const float* ws, long long n_units, int n_h, int D) {
-  return ws + (size_t)n_units * (size_t)n_h * (size_t)D;
+  return (const float*)(part_o(ws) + (size_t)n_units * (size_t)n_h * (size_t)D);
 }
+__device__ __forceinline__ _Float16 part_h(float x) {
+  return (_Float16)fminf(fmaxf(x, -65504.f), 65504.f);
+}
+// 1 / l, or 0 for a split without visible keys (its O is 0)
+__device__ __forceinline__ float part_inv(float l) { return l > 0.f ? 1.f / l : 0.f; }
 
 // ---------------------------------------------------------------------------
 // generic path (fp32 or bf16 storage): one workgroup per (query, head)
@@ -435,14 +445,19 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
       }
     }
   } else {
-    // ---- partial state: O (unnormalised, relative to m_run), then m_run, l_run
+    // ---- partial state: O / l_run, then m_run, l_run
     const size_t pbase = (row * n_split + sp) * (size_t)n_h;
     float* ml = part_ml(ws, n_units, n_h, D);
+    _Float16* wo = part_o(ws);
+    const float li = part_inv(l_run);
+    float lr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lr[r] = __shfl(li, 4 * g + r, 64);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        ws[(pbase + h0 + 4 * g + r) * D + 16 * nt + j] = O[nt][r];
+        wo[(pbase + h0 + 4 * g + r) * D + 16 * nt + j] = part_h(O[nt][r] * lr[r]);
     if (g == 0) {
       ml[2 * (pbase + hq)] = m_run;
       ml[2 * (pbase + hq) + 1] = l_run;
@@ -688,14 +703,17 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
     }
   } else {
     const size_t pbase = (row * n_split + sp) * (size_t)n_h + hbase;
+    _Float16* wo = part_o(ws);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= ntiles) continue;
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
+      for (int r = 0; r < 4; ++r) {
+        const float li = part_inv(lstat[16 * mt + 4 * g + r]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          ws[(pbase + 16 * mt + 4 * g + r) * D + dbase + 16 * nt + j] = O[mt][nt][r];
+        for (int nt = 0; nt < NTW; ++nt)
+          wo[(pbase + 16 * mt + 4 * g + r) * D + dbase + 16 * nt + j] = part_h(O[mt][nt][r] * li);
+      }
     }
     if (threadIdx.x < 16 * ntiles) {
       float* ml = part_ml(ws, n_units, n_h, D);
@@ -1205,41 +1223,56 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
         }
       }
   } else {
-    // The partial O goes out through LDS, so that every store writes whole
-    // 16-byte pieces of one head's row (straight from the MFMA layout a store
-    // instruction would write four 64-byte pieces of four rows).  A wave stages
-    // 16 heads x CW dims at a time (rows padded by 4 floats, so the four lane
-    // groups hit distinct banks) in its own part of the chunk ring, and reads
-    // them back 4 dims per lane.
+    // The partial O, divided by the head's sum, goes out as fp16 through LDS,
+    // so that every store writes whole 16-byte pieces of one head's row
+    // (straight from the MFMA layout a store instruction would write four
+    // pieces of four rows).  A wave stages 16 heads x CW dims at a time (rows
+    // padded by 4 floats, so the four lane groups hit distinct banks) in its own
+    // part of the chunk ring, and reads them back 8 dims per lane.
     constexpr int CW = D >= 512 ? 256 : D / 2;   // dims per staged block
     constexpr int CRS = CW + 4;                  // staged row stride (floats)
-    constexpr int LPH = CW / 4;                  // lanes per head row on the way out
+    constexpr int LPH = CW / 8;                  // lanes per head row on the way out
     static_assert(16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
     lds_sync<0>();   // every wave is done with the chunk ring
     float* stg = (float*)kv + wave * 16 * CRS;
     const size_t pb = (row * n_split + sp) * (size_t)n_h + h0;
+    _Float16* wo = part_o(ws);
 #pragma unroll
-    for (int ht = 0; ht < HTW; ++ht)
+    for (int ht = 0; ht < HTW; ++ht) {
+      float li[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) li[r] = __shfl(part_inv(lsum[ht]), 4 * g + r, 64);
 #pragma unroll
       for (int cb = 0; cb < D / CW; ++cb) {
 #pragma unroll
         for (int nt = 0; nt < CW / 16; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) stg[(4 * g + r) * CRS + 16 * nt + j] = O[ht][cb * (CW / 16) + nt][r];
+          for (int r = 0; r < 4; ++r)
+            stg[(4 * g + r) * CRS + 16 * nt + j] = O[ht][cb * (CW / 16) + nt][r] * li[r];
         // the writes of every lane land before any lane reads (and the reads below
         // finish before the next block's writes: their stores consume them first)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int it = 0; it < 16 * CW / 256; ++it) {
-          const int f = it * 64 + lane;   // 4-float piece of the 16 x CW block
-          const int hh = f / LPH, c4 = f % LPH;
-          const f32x4_t v = *(const f32x4_t*)(stg + hh * CRS + 4 * c4);
-          *(f32x4_t*)(ws + (pb + 16 * ht + hh) * D + cb * CW + 4 * c4) = v;
+        for (int it = 0; it < 16 * CW / 512; ++it) {
+          const int f = it * 64 + lane;   // 8-value piece of the 16 x CW block
+          const int hh = f / LPH, c8 = f % LPH;
+          const f32x4_t v0 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8);
+          const f32x4_t v1 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8 + 4);
+          u32x4_t pk;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            pk[e] = (uint32_t)__builtin_bit_cast(uint16_t, part_h(v0[2 * e])) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, part_h(v0[2 * e + 1])) << 16);
+            pk[2 + e] = (uint32_t)__builtin_bit_cast(uint16_t, part_h(v1[2 * e])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, part_h(v1[2 * e + 1])) << 16);
+          }
+          *(u32x4_t*)(wo + (pb + 16 * ht + hh) * D + cb * CW + 8 * c8) = pk;
         }
         asm volatile("" ::: "memory");
       }
+    }
     if (g == 0) {
       float* ml = part_ml(ws, n_units, n_h, D);
 #pragma unroll
@@ -1261,7 +1294,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const size_t row = (size_t)b * Tq + t;
   const long long i = q_pos[row];
   const float sig = sink ? sink[h] : -INFINITY;
-  const float* base = ws + (row * n_split * (size_t)n_h + h) * D;   // O of split 0
+  const _Float16* base = part_o(ws) + (row * n_split * (size_t)n_h + h) * D;   // O / l of split 0
   const size_t sstride = (size_t)n_h * D;
   const float* mlb = part_ml(ws, (long long)gridDim.z * Tq * n_split, n_h, D) + 2 * (row * n_split * (size_t)n_h + h);
   const size_t mstride = 2 * (size_t)n_h;
@@ -1280,9 +1313,10 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
         const int sc = min(s, n_split - 1);
-        const float* ps = base + sc * sstride;
-        a0[s] = ps[d0];
-        a1[s] = ps[d0 + 1];
+        const _Float16* ps = base + sc * sstride;
+        const uint32_t w = *(const uint32_t*)(ps + d0);
+        a0[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+        a1[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
       }
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
@@ -1292,14 +1326,13 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
 #pragma unroll
       for (int s = 0; s < CB; ++s)
         if (s < n_split) M = fmaxf(M, ms[s]);
+      // split s weighs l_s exp(m_s - M) (its rows hold O_s / l_s)
       Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
-#pragma unroll
-      for (int s = 0; s < CB; ++s)
-        if (s < n_split && ms[s] != -INFINITY) Z += ls[s] * __expf(ms[s] - M);
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
         if (s < n_split) {
-          const float f = (ms[s] == -INFINITY) ? 0.f : __expf(ms[s] - M);
+          const float f = (ms[s] == -INFINITY) ? 0.f : ls[s] * __expf(ms[s] - M);
+          Z += f;
           o0 += a0[s] * f;
           o1 += a1[s] * f;
         }
@@ -1308,15 +1341,12 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
       for (int s = 0; s < n_split; ++s) M = fmaxf(M, mlb[s * mstride]);
       Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
       for (int s = 0; s < n_split; ++s) {
+        const _Float16* ps = base + s * sstride;
         const float ms = mlb[s * mstride];
-        if (ms != -INFINITY) Z += mlb[s * mstride + 1] * __expf(ms - M);
-      }
-      for (int s = 0; s < n_split; ++s) {
-        const float* ps = base + s * sstride;
-        const float ms = mlb[s * mstride];
-        const float f = (ms == -INFINITY) ? 0.f : __expf(ms - M);
-        o0 += ps[d0] * f;
-        o1 += ps[d0 + 1] * f;
+        const float f = (ms == -INFINITY) ? 0.f : mlb[s * mstride + 1] * __expf(ms - M);
+        Z += f;
+        o0 += (float)ps[d0] * f;
+        o1 += (float)ps[d0 + 1] * f;
       }
     }
     const float inv = Z > 0.f ? 1.f / Z : 0.f;
@@ -1379,7 +1409,8 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
   int kps, n_split;
   mqa_split(Tq, n_h, d, n_slots_max, &kps, &n_split);
   if (n_split == 1) return 0;
-  return (size_t)B * Tq * n_split * n_h * (size_t)(d + 2) * sizeof(float);
+  // per (query row, split, head): d fp16 outputs + a float (max, sum) pair
+  return (size_t)B * Tq * n_split * n_h * (size_t)(2 * d + 8);
 }
 
 template <int D, bool DENSE, bool MULTI>

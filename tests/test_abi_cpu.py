@@ -156,17 +156,17 @@ def test_mqa_validation(lib):
     assert sparse(r=130) == CSA_E_SHAPE
     assert sparse(k=0) == CSA_E_SHAPE
     # a split decode query needs workspace
-    # 1152 slots in ranges of 192: 6 split partials of (O, max, sum) per (query, head);
-    # above 1536 slots the ranges hold 288
-    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 29 * 64 * 514 * 4
-    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * 514 * 4
+    # 1152 slots in ranges of 192: 6 split partials per (query, head), each d fp16
+    # outputs and a float (max, sum) pair; above 1536 slots the ranges hold 288
+    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 29 * 64 * (512 * 2 + 8)
+    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * (512 * 2 + 8)
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
     need = lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128)
     assert sparse(k=1024, nh=128, d=512, B=16, ws=FAKE + 4, wsb=need + 16) == CSA_E_WORKSPACE
     assert b"16-byte aligned" in lib.csa_last_error()
     # prefill (16 or more queries per sequence): one range of up to 2,048 slots per query
     assert lib.csa_mqa_workspace_size(1, 16384, 128, 512, 1024 + 128) == 0
-    assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * 130 * 4
+    assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * (128 * 2 + 8)
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED
 
