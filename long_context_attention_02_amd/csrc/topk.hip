@@ -331,82 +331,79 @@ __device__ void sort_desc_lds(TopkShared& sh, int P) {
   __syncthreads();
 }
 
-// Collection of the selected keys into sh.buf (sh.count = 0 on entry).  Lanes
-// of a wave take consecutive slots of the range the wave claimed, by ballot
-// rank (mbcnt); the range is claimed once per group of V elements.
-template <class Src>
-__device__ __forceinline__ void collect_group(const uint32_t (&h)[Src::V], const uint32_t (&l)[Src::V],
-                                              const bool (&take)[Src::V], TopkShared& sh) {
-  constexpr int V = Src::V;
-  uint64_t bal[V];
+// Collection of the selected keys into sh.buf (sh.count = 0 on entry).  A wave
+// claims the slots for CG groups of V elements per thread (8 elements) with one
+// LDS atomic, so the atomic's return latency is paid once per 8 elements; its
+// lanes fill the range in ballot order (mbcnt rank).
+template <int V>
+__device__ __forceinline__ constexpr int tk_cg() { return V >= 8 ? 1 : 8 / V; }
+template <int V>
+__device__ __forceinline__ void collect_groups(const uint32_t (&h)[tk_cg<V>()][V], const uint32_t (&l)[tk_cg<V>()][V],
+                                               const bool (&take)[tk_cg<V>()][V], TopkShared& sh) {
+  constexpr int CG = tk_cg<V>();
+  uint64_t bal[CG][V];
   int tot = 0;
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    bal[v] = __ballot(take[v]);
-    tot += __popcll(bal[v]);
-  }
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      bal[c][v] = __ballot(take[c][v]);
+      tot += __popcll(bal[c][v]);
+    }
   if (tot == 0) return;   // wave-uniform
   int off = 0;
   if ((threadIdx.x & 63) == 0) off = atomicAdd(&sh.count, tot);
   off = __builtin_amdgcn_readfirstlane(off);
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int slot = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[v] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal[v], 0u));
-    if (take[v] && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[v] << 32) | l[v];
-    off += __popcll(bal[v]);
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int slot = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[c][v] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[c][v], 0u));
+      if (take[c][v] && slot < TK_KMAX) sh.buf[slot] = ((uint64_t)h[c][v] << 32) | l[c][v];
+      off += __popcll(bal[c][v]);
+    }
+}
+
+// every element (hi, lo) with take(hi, lo), n >= 1, CG groups at a time.  The loads are not guarded
+// (a guarded load is a branch with its own wait): past the end they read the
+// last group again, which is in bounds, and the count mask drops it.
+template <class Src, class Take>
+__device__ void collect_if(const Src& src, long long n, Take take_fn, TopkShared& sh) {
+  constexpr int V = Src::V, CG = tk_cg<V>();
+  const long long step = (long long)V * TK_THREADS;
+  const long long last = ((n - 1) / V) * V;   // start of the last group
+  for (long long g0 = 0; g0 < n; g0 += CG * step) {
+    uint32_t h[CG][V], l[CG][V];
+    int rem[CG];
+#pragma unroll
+    for (int c = 0; c < CG; ++c) {
+      const long long e0 = g0 + c * step + (long long)V * threadIdx.x;
+      src.load(min(e0, last), h[c], l[c]);
+      rem[c] = (int)max(0LL, min(n - e0, (long long)V));
+    }
+    bool take[CG][V];
+#pragma unroll
+    for (int c = 0; c < CG; ++c)
+#pragma unroll
+      for (int v = 0; v < V; ++v) take[c][v] = (v < rem[c]) && take_fn(h[c][v], l[c][v]);
+    collect_groups<V>(h, l, take, sh);
   }
 }
 
 // every element with hi >= t (no tie to resolve)
 template <class Src>
 __device__ void collect_ge(const Src& src, long long n, uint32_t t, TopkShared& sh) {
-  constexpr int V = Src::V;
-  const long long step = (long long)V * TK_THREADS;
-  const long long nfull = (n / step) * step;
-  for (long long g0 = 0; g0 < nfull; g0 += step) {   // whole groups: no bounds tests
-    uint32_t h[V], l[V];
-    src.load(g0 + (long long)V * threadIdx.x, h, l);
-    bool take[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) take[v] = h[v] >= t;
-    collect_group<Src>(h, l, take, sh);
-  }
-  if (nfull < n) {
-    const long long e0 = nfull + (long long)V * threadIdx.x;
-    uint32_t h[V] = {}, l[V] = {};
-    int rem = 0;
-    if (e0 < n) {
-      src.load(e0, h, l);
-      rem = (int)min(n - e0, (long long)V);
-    }
-    bool take[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) take[v] = (v < rem) & (h[v] >= t);
-    collect_group<Src>(h, l, take, sh);
-  }
+  collect_if(src, n, [t](uint32_t h, uint32_t) { return h >= t; }, sh);
 }
 
 // hi > thr_hi, plus hi == thr_hi with lo >= thr_lo (the k-th score is tied)
 template <class Src>
 __device__ void collect_tied(const Src& src, long long n, uint32_t lb, uint32_t thr_hi, uint32_t thr_lo,
                              TopkShared& sh) {
-  constexpr int V = Src::V;
-  const long long step = (long long)V * TK_THREADS;
-  for (long long g0 = 0; g0 < n; g0 += step) {
-    const long long e0 = g0 + (long long)V * threadIdx.x;
-    uint32_t h[V] = {}, l[V] = {};
-    int rem = 0;
-    if (e0 < n) {
-      src.load(e0, h, l);
-      rem = (int)min(n - e0, (long long)V);
-    }
-    bool take[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v)
-      take[v] = (v < rem) & (h[v] >= lb) & ((h[v] > thr_hi) | ((h[v] == thr_hi) & (l[v] >= thr_lo)));
-    collect_group<Src>(h, l, take, sh);
-  }
+  collect_if(src, n, [=](uint32_t h, uint32_t l) {
+    return (h >= lb) & ((h > thr_hi) | ((h == thr_hi) & (l >= thr_lo)));
+  }, sh);
 }
 
 // k largest K64 = hi << 32 | lo among n elements -> sh.buf[0 .. min(k, n)), sorted
