@@ -350,3 +350,35 @@ def test_mqa_empty_key_set_is_zero(csa):
         csa.csa_sparse_mqa(q, E, idx, None, pos, out, n_win=0, rope_dim=16)
         torch.cuda.synchronize()
         assert torch.all(out == 0), dt
+
+
+def test_mqa_split_partials_large_values(csa):
+    """A split decode query whose entries reach about +-4.5e4: the split partials
+    (each split's output divided by its softmax sum, kept as fp16) stay inside the
+    fp16 range, and the merged rows match the oracle to the bf16 tolerance.  Large
+    entries also make the softmax close to one-hot, the case where a partial row
+    is as large as the largest value row."""
+    B, Tq, n_h, d, N, k, m, n_win, rope = 2, 1, 64, 512, 900, 512, 4, 128, 64
+    g = Gen(490, DEV)
+    q = g.normal(1, (B, Tq, n_h, d), "bf16")
+    E = (g.normal(2, (B, N, d), "f32") * 1e4).to(torch.bfloat16)
+    W = (g.normal(3, (B, n_win, d), "f32") * 1e4).to(torch.bfloat16)
+    sink = g.normal(4, (n_h,), "f32", per_slot=False)
+    pos = _positions("all", B, Tq, N, m, g)
+    idx = ((g.uniform(6, (B, Tq, k)) * N).to(torch.int32)).contiguous()
+    ws = torch.empty(csa.csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win), dtype=torch.uint8, device=DEV)
+    assert ws.numel() > 0   # the query is split
+    out = torch.full_like(q, float("nan"))
+    scale = 1.0 / math.sqrt(d)
+    csa.csa_sparse_mqa(q, E, idx, W, pos, out, n_win=n_win, sink=sink, rope_dim=rope, scale=scale,
+                       workspace=ws)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    for b in range(B):
+        ref = O.sparse_mqa(to_f64(q[b]), to_f64(E[b]), to_f64(idx[b]), to_f64(W[b]), q_pos=to_f64(pos[b]),
+                           n_win=n_win, W_cap=n_win, gamma_q=None, eps=1e-6, sink=to_f64(sink),
+                           rope_dim=rope, scale=scale)
+        assert np.abs(ref).max() > 3e4
+        err = row_rel_err(got[b], ref)
+        assert err <= TOL_BF16, (b, err)
