@@ -728,7 +728,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 //
 // A workgroup takes one query, a group of 16 HTW NW heads and a fixed range of
 // at most MQ_DEC_TABLE key slots.  Wave w owns HTW 16-head tiles of the group
-// (one at D = 512, two below) over all D dims, so scores, softmax and P.V stay
+// (two, or one for decode at D = 512) over all D dims, so scores, softmax and P.V stay
 // inside the wave and need no exchange.  The slots' rows stream through LDS 32 at a time: a ring of
 // MQ_DEC_NBUF chunks filled with global_load_lds, MQ_DEC_NBUF - 1 chunks ahead,
 // so each row is fetched from memory once per workgroup and then read from LDS
@@ -867,19 +867,14 @@ __device__ __forceinline__ float quad_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// head tiles (16 heads each) per wave: two while the output accumulators of
-// 32 heads fit the register file next to the query fragments, one at D = 512
-template <int D>
-__host__ __device__ constexpr int dec_htw() { return D >= 512 ? 1 : 2; }
-
-template <int D, bool DENSE, int NW, int TBL>
+// HTW: head tiles (16 heads each) per wave (host choice: dec_htw)
+template <int D, bool DENSE, int NW, int TBL, int HTW>
 __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
     const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
     int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
-  constexpr int HTW = dec_htw<D>();   // head tiles per wave
   constexpr int KS = D / 32;          // S^T K-steps (8 dims per lane each)
   constexpr int NT = D / 16;          // 16-dim output tiles
   constexpr int RBP = 2 * D + 16;     // LDS row stride
@@ -1376,13 +1371,21 @@ long long mqa_slots_max(const MqaArgs& a) {
   return (a.idx ? (long long)a.k : a.N_cap) + a.n_win;
 }
 
-static int dec_heads_per_wave(int d) { return d >= 512 ? 16 * dec_htw<512>() : 16 * dec_htw<256>(); }
+// Head tiles (16 heads each) per wave of the streaming kernel.  Below D = 512
+// the output accumulators of two tiles fit the register file next to the query
+// fragments.  At D = 512 two tiles fill it (a few prologue values spill, none
+// in the loop): prefill takes them, since each chunk read from LDS then feeds
+// twice the heads and those reads bound the loop; decode keeps one tile and so
+// twice the workgroups.
+static int dec_htw(int Tq, int n_h, int d) {
+  if (d < 512) return 2;
+  return (Tq >= MQ_SPLIT_BELOW_TQ && n_h % 32 == 0) ? 2 : 1;
+}
 
 // the streaming kernel (mqa_decode_kernel) covers the shape: decode splits a
 // query's slots over workgroups, prefill gives each query one range
 static bool mqa_decode_ok(int Tq, int n_h, int d) {
-  (void)Tq;
-  return n_h % dec_heads_per_wave(d) == 0;
+  return n_h % (16 * dec_htw(Tq, n_h, d)) == 0;
 }
 
 // slots per workgroup and splits per query; depends on the shape only, never on B
@@ -1434,16 +1437,16 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
                        n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
 }
 
-template <int D, bool DENSE, int NW>
+template <int D, bool DENSE, int NW, int HTW>
 static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
-  const int n_hg = a.n_h / (16 * dec_htw<D>() * NW);
+  const int n_hg = a.n_h / (16 * HTW * NW);
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
   const size_t lds = (size_t)MQ_DEC_NBUF * MQ_CH * (2 * D + 16);
   // the small slot table for decode ranges (<= 288 slots), the large one for prefill
-  auto kfn = kps <= MQ_DEC_SPLIT_MAX ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_SPLIT_MAX>
-                                     : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE>;
+  auto kfn = kps <= MQ_DEC_SPLIT_MAX ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_SPLIT_MAX, HTW>
+                                     : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE, HTW>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
@@ -1458,12 +1461,22 @@ static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t
 }
 
 // waves per workgroup: as many head groups of one wave as divide n_h, up to four
+template <int D, bool DENSE, int HTW>
+static void launch_decode_w(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
+  constexpr int HW = 16 * HTW;
+  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4, HTW>(a, kps, n_split, st);
+  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2, HTW>(a, kps, n_split, st);
+  else launch_decode_nw<D, DENSE, 1, HTW>(a, kps, n_split, st);
+}
 template <int D, bool DENSE>
 static void launch_decode(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
-  constexpr int HW = 16 * dec_htw<D>();
-  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4>(a, kps, n_split, st);
-  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2>(a, kps, n_split, st);
-  else launch_decode_nw<D, DENSE, 1>(a, kps, n_split, st);
+  if constexpr (D >= 512) {
+    if (dec_htw(a.Tq, a.n_h, D) == 1) {
+      launch_decode_w<D, DENSE, 1>(a, kps, n_split, st);
+      return;
+    }
+  }
+  launch_decode_w<D, DENSE, 2>(a, kps, n_split, st);
 }
 
 template <int D, bool DENSE>
