@@ -181,6 +181,9 @@ int csa_topk(const float* I, const int* q_pos, int B, int Tq, long long N_cap, i
  *  sink    : [n_h] fp32 or NULL (no sink; -inf is also "no sink").
  *  dtype   : F32 or BF16 for q, E, W and out.  out: [B][Tq][n_h][d].
  *  No key and no sink gives a zero output row.
+ *  Matrix-core path: BF16 with d in {128, 256, 512}, n_h a multiple of 16 and
+ *  q, E, W and out 16-byte aligned; any other call takes the generic path,
+ *  which holds at most 8192 key slots per query (CSA_E_UNSUPPORTED beyond).
  *  workspace: at least csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win) bytes,
  *            16-byte aligned (split partials: per (query, split, head) the
  *            output over that split's keys divided by its softmax sum, as d

@@ -23,6 +23,8 @@
 // Decode queries split their slots across workgroups (fixed 128-slot ranges,
 // independent of the batch) and a combine kernel merges the partial
 // (max, sum, O) in a fixed order.
+#include <type_traits>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -1188,92 +1190,102 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
   for (int ht = 0; ht < HTW; ++ht) lsum[ht] = quad_sum(lsum[ht]);
 
-  // ---- output: lane (g, j) of tile (ht, nt) holds heads h0 + 16 ht + 4 g + r, dim 16 nt + j
-  if (n_split == 1) {
-    float f[HTW];
+  // ---- output: lane (g, j) of tile (ht, nt) holds heads h0 + 16 ht + 4 g + r, dim 16 nt + j.
+  // Unsplit, the output row: O times the head's final factor, rotated at -i,
+  // as bf16.  Split, the partial: O divided by the head's sum, as fp16, then
+  // the (max, sum) pair.  Either goes out through LDS, so that every store
+  // writes a whole 16-byte piece of one head's row (straight from the MFMA
+  // layout a store instruction would write 32-byte pieces of four rows).  A
+  // wave stages 16 heads x CW dims at a time (rows padded by 4 floats, so the
+  // four lane groups hit distinct banks) in its own part of the chunk ring and
+  // reads them back 8 dims per lane.
+  const bool fin = n_split == 1;
+  float fac[HTW];   // factor of head 16 ht + j
 #pragma unroll
-    for (int ht = 0; ht < HTW; ++ht) {
+  for (int ht = 0; ht < HTW; ++ht) {
+    if (fin) {
       const float sig = sink ? sink[h0 + 16 * ht + j] : -INFINITY;
       const float M = fmaxf(ref[ht], sig);
       float Z = 0.f;
       if (ref[ht] != -INFINITY) Z += lsum[ht] * __expf(ref[ht] - M);
       if (sig != -INFINITY) Z += __expf(sig - M);
-      f[ht] = (Z > 0.f && ref[ht] != -INFINITY) ? __expf(ref[ht] - M) / Z : 0.f;
+      fac[ht] = (Z > 0.f && ref[ht] != -INFINITY) ? __expf(ref[ht] - M) / Z : 0.f;
+    } else {
+      fac[ht] = part_inv(lsum[ht]);
     }
-#pragma unroll
-    for (int ht = 0; ht < HTW; ++ht)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float fr = __shfl(f[ht], 4 * g + r, 64);
-        const size_t obase = (row * n_h + h0 + 16 * ht + 4 * g + r) * (size_t)D;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int dim = 16 * nt + j;
-          const float v = O[ht][nt][r] * fr;
-          const float other = __shfl_xor(v, 1, 64);
-          // rotation at -i: cos(-x) = cos x, sin(-x) = -sin x ((1, 0) outside the rotated dims)
-          const float cs = rope_cs[dim & ~1], sn = -rope_cs[(dim & ~1) + 1];
-          const float o = (dim & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
-          out[obase + dim] = f32_to_bf16_bits(o);
-        }
-      }
-  } else {
-    // The partial O, divided by the head's sum, goes out as fp16 through LDS,
-    // so that every store writes whole 16-byte pieces of one head's row
-    // (straight from the MFMA layout a store instruction would write four
-    // pieces of four rows).  A wave stages 16 heads x CW dims at a time (rows
-    // padded by 4 floats, so the four lane groups hit distinct banks) in its own
-    // part of the chunk ring, and reads them back 8 dims per lane.
+  }
+  {
     constexpr int CW = D >= 512 ? 256 : D / 2;   // dims per staged block
     constexpr int CRS = CW + 4;                  // staged row stride (floats)
     constexpr int LPH = CW / 8;                  // lanes per head row on the way out
     static_assert(16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
     lds_sync<0>();   // every wave is done with the chunk ring
     float* stg = (float*)kv + wave * 16 * CRS;
-    const size_t pb = (row * n_split + sp) * (size_t)n_h + h0;
-    _Float16* wo = part_o(ws);
-#pragma unroll
-    for (int ht = 0; ht < HTW; ++ht) {
-      float li[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) li[r] = __shfl(part_inv(lsum[ht]), 4 * g + r, 64);
-#pragma unroll
-      for (int cb = 0; cb < D / CW; ++cb) {
-#pragma unroll
-        for (int nt = 0; nt < CW / 16; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            stg[(4 * g + r) * CRS + 16 * nt + j] = O[ht][cb * (CW / 16) + nt][r] * li[r];
-        // the writes of every lane land before any lane reads (and the reads below
-        // finish before the next block's writes: their stores consume them first)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int it = 0; it < 16 * CW / 512; ++it) {
-          const int f = it * 64 + lane;   // 8-value piece of the 16 x CW block
-          const int hh = f / LPH, c8 = f % LPH;
-          const f32x4_t v0 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8);
-          const f32x4_t v1 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8 + 4);
-          u32x4_t pk;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            pk[e] = (uint32_t)__builtin_bit_cast(uint16_t, part_h(v0[2 * e])) |
-                    ((uint32_t)__builtin_bit_cast(uint16_t, part_h(v0[2 * e + 1])) << 16);
-            pk[2 + e] = (uint32_t)__builtin_bit_cast(uint16_t, part_h(v1[2 * e])) |
-                        ((uint32_t)__builtin_bit_cast(uint16_t, part_h(v1[2 * e + 1])) << 16);
-          }
-          *(u32x4_t*)(wo + (pb + 16 * ht + hh) * D + cb * CW + 8 * c8) = pk;
-        }
-        asm volatile("" ::: "memory");
-      }
-    }
-    if (g == 0) {
-      float* ml = part_ml(ws, n_units, n_h, D);
+    // FIN: compile-time copy of fin (one store loop each)
+    auto write_out = [&](auto fin_c) {
+      constexpr bool FIN = decltype(fin_c)::value;
+      const size_t pb = FIN ? row * n_h + h0 : (row * n_split + sp) * (size_t)n_h + h0;
+      uint16_t* dst = FIN ? out : (uint16_t*)part_o(ws);
 #pragma unroll
       for (int ht = 0; ht < HTW; ++ht) {
-        ml[2 * (pb + 16 * ht + j)] = ref[ht];
-        ml[2 * (pb + 16 * ht + j) + 1] = lsum[ht];
+        float fr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) fr[r] = __shfl(fac[ht], 4 * g + r, 64);
+#pragma unroll
+        for (int cb = 0; cb < D / CW; ++cb) {
+#pragma unroll
+          for (int nt = 0; nt < CW / 16; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              stg[(4 * g + r) * CRS + 16 * nt + j] = O[ht][cb * (CW / 16) + nt][r] * fr[r];
+          // the writes of every lane land before any lane reads (and the reads below
+          // finish before the next block's writes: their stores consume them first)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int it = 0; it < 16 * CW / 512; ++it) {
+            const int f = it * 64 + lane;   // 8-value piece of the 16 x CW block
+            const int hh = f / LPH, c8 = f % LPH;
+            const int d0 = cb * CW + 8 * c8;
+            const f32x4_t v0 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8);
+            const f32x4_t v1 = *(const f32x4_t*)(stg + hh * CRS + 8 * c8 + 4);
+            const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            u32x4_t pk;
+            if constexpr (FIN) {
+              // rotation at -i of the pairs (2u, 2u + 1): cos(-x) = cos x, sin(-x) = -sin x
+              // ((1, 0) outside the rotated dims)
+              const f32x4_t ra = *(const f32x4_t*)&rope_cs[d0], rb = *(const f32x4_t*)&rope_cs[d0 + 4];
+              const float rc[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float a = v[2 * e], bb = v[2 * e + 1], cs = rc[2 * e], sn = rc[2 * e + 1];
+                pk[e] = (uint32_t)f32_to_bf16_bits(a * cs + bb * sn) |
+                        ((uint32_t)f32_to_bf16_bits(bb * cs - a * sn) << 16);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                pk[e] = (uint32_t)__builtin_bit_cast(uint16_t, part_h(v[2 * e])) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, part_h(v[2 * e + 1])) << 16);
+            }
+            *(u32x4_t*)(dst + (pb + 16 * ht + hh) * D + d0) = pk;
+          }
+          asm volatile("" ::: "memory");
+        }
+      }
+    };
+    if (fin) write_out(std::true_type{});
+    else write_out(std::false_type{});
+    if (!fin) {
+      const size_t pbs = (row * n_split + sp) * (size_t)n_h + h0;
+      if (g == 0) {
+        float* ml = part_ml(ws, n_units, n_h, D);
+#pragma unroll
+        for (int ht = 0; ht < HTW; ++ht) {
+          ml[2 * (pbs + 16 * ht + j)] = ref[ht];
+          ml[2 * (pbs + 16 * ht + j) + 1] = lsum[ht];
+        }
       }
     }
   }
@@ -1363,8 +1375,12 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
 // ---------------------------------------------------------------------------
 // dispatch
 // ---------------------------------------------------------------------------
+// the MFMA kernels read q, the entries and the window rows and write the
+// output in 16-byte pieces
+static bool mqa_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool mqa_mfma_ok(const MqaArgs& a) {
-  return a.dtype == DT_BF16 && (a.d == 128 || a.d == 256 || a.d == 512) && a.n_h % 16 == 0;
+  return a.dtype == DT_BF16 && (a.d == 128 || a.d == 256 || a.d == 512) && a.n_h % 16 == 0 &&
+         mqa_aligned16(a.q) && mqa_aligned16(a.E) && mqa_aligned16(a.W) && mqa_aligned16(a.out);
 }
 
 long long mqa_slots_max(const MqaArgs& a) {
