@@ -382,3 +382,31 @@ def test_mqa_split_partials_large_values(csa):
         assert np.abs(ref).max() > 3e4
         err = row_rel_err(got[b], ref)
         assert err <= TOL_BF16, (b, err)
+
+
+def test_mqa_unaligned_output_takes_generic_path(csa):
+    """A bf16 call whose output is not 16-byte aligned (a view 2 bytes into its
+    buffer) takes the generic kernel; it still matches the oracle, and leaves
+    the element before the view untouched."""
+    B, Tq, n_h, d, N, k, m, n_win, rope = 1, 2, 16, 128, 200, 40, 4, 16, 32
+    g = Gen(495, DEV)
+    q = g.normal(1, (B, Tq, n_h, d), "bf16")
+    E = g.normal(2, (B, N, d), "bf16")
+    W = g.normal(3, (B, n_win, d), "bf16")
+    pos = _positions("all", B, Tq, N, m, g)
+    idx = ((g.uniform(6, (B, Tq, k)) * N).to(torch.int32)).contiguous()
+    n = B * Tq * n_h * d
+    buf = torch.full((n + 8,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[1:1 + n].view(B, Tq, n_h, d)
+    assert out.data_ptr() % 16 != 0
+    ws = torch.empty(max(1, csa.csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win)), dtype=torch.uint8, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    csa.csa_sparse_mqa(q, E, idx, W, pos, out, n_win=n_win, rope_dim=rope, scale=scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert float(buf[0]) == 7.0 and float(buf[n + 1]) == 7.0
+    got = to_f64(out)
+    for b in range(B):
+        ref = O.sparse_mqa(to_f64(q[b]), to_f64(E[b]), to_f64(idx[b]), to_f64(W[b]), q_pos=to_f64(pos[b]),
+                           n_win=n_win, W_cap=n_win, gamma_q=None, eps=1e-6, sink=None, rope_dim=rope,
+                           scale=scale)
+        assert row_rel_err(got[b], ref) <= TOL_BF16
