@@ -1012,7 +1012,13 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     if (c < nch) dec_issue<D, NW>(c, sptr, kv + c * CHB, wave, lane);
 
   // q^ = RoPE_i(RMSNorm(q)) as bf16 B fragments of S^T: lane (g, j) holds head 16 ht + j,
-  // dims (D/4) g + 8 ks + 0..7; the RoPE table holds (1, 0) for dims that are not rotated
+  // dims (D/4) g + 8 ks + 0..7; the RoPE table holds (1, 0) for dims that are not rotated.
+  // RoPE is linear, so the head's RMSNorm factor rinv moves onto its scores
+  // (sc below): the fragments hold RoPE_i(gamma q), the same values up to the
+  // common factor, and the bf16 rounding is relative either way.
+  float sc[HTW];
+#pragma unroll
+  for (int ht = 0; ht < HTW; ++ht) sc[ht] = scale * rinv[ht];
   bf16x8_t qf[HTW][KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -1026,8 +1032,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       u32x4_t packed;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v0 = __uint_as_float(raw[ht][ks][e] << 16) * rinv[ht] * gw[2 * e];
-        const float v1 = __uint_as_float(raw[ht][ks][e] & 0xffff0000u) * rinv[ht] * gw[2 * e + 1];
+        const float v0 = __uint_as_float(raw[ht][ks][e] << 16) * gw[2 * e];
+        const float v1 = __uint_as_float(raw[ht][ks][e] & 0xffff0000u) * gw[2 * e + 1];
         const float cs = rc[2 * e], sn = rc[2 * e + 1];
         packed[e] = pack2_bf16_hw(v0 * cs - v1 * sn, v0 * sn + v1 * cs);
       }
@@ -1107,7 +1113,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const bool ok = (vmask >> (16 * kt + 4 * g + r)) & 1u;
-          S[kt][ht][r] = ok ? S[kt][ht][r] * scale : -INFINITY;
+          S[kt][ht][r] = ok ? S[kt][ht][r] * sc[ht] : -INFINITY;
           cm = fmaxf(cm, S[kt][ht][r]);
         }
       cm = quad_max(cm);
