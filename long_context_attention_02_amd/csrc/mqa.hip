@@ -804,6 +804,47 @@ __device__ __forceinline__ void lds_read_tr16(uint32_t a0, uint32_t a1, u32x2_t 
       : "memory");
 }
 
+// The same for sixteen tiles (offsets 0 .. 480): one wait for two blocks of eight.
+__device__ __forceinline__ void lds_read_tr32(uint32_t a0, uint32_t a1, u32x2_t (&r)[32]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %32\n\t"
+      "ds_read_b64_tr_b16 %1, %33\n\t"
+      "ds_read_b64_tr_b16 %2, %32 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %33 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %32 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %33 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %32 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %33 offset:96\n\t"
+      "ds_read_b64_tr_b16 %8, %32 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %33 offset:128\n\t"
+      "ds_read_b64_tr_b16 %10, %32 offset:160\n\t"
+      "ds_read_b64_tr_b16 %11, %33 offset:160\n\t"
+      "ds_read_b64_tr_b16 %12, %32 offset:192\n\t"
+      "ds_read_b64_tr_b16 %13, %33 offset:192\n\t"
+      "ds_read_b64_tr_b16 %14, %32 offset:224\n\t"
+      "ds_read_b64_tr_b16 %15, %33 offset:224\n\t"
+      "ds_read_b64_tr_b16 %16, %32 offset:256\n\t"
+      "ds_read_b64_tr_b16 %17, %33 offset:256\n\t"
+      "ds_read_b64_tr_b16 %18, %32 offset:288\n\t"
+      "ds_read_b64_tr_b16 %19, %33 offset:288\n\t"
+      "ds_read_b64_tr_b16 %20, %32 offset:320\n\t"
+      "ds_read_b64_tr_b16 %21, %33 offset:320\n\t"
+      "ds_read_b64_tr_b16 %22, %32 offset:352\n\t"
+      "ds_read_b64_tr_b16 %23, %33 offset:352\n\t"
+      "ds_read_b64_tr_b16 %24, %32 offset:384\n\t"
+      "ds_read_b64_tr_b16 %25, %33 offset:384\n\t"
+      "ds_read_b64_tr_b16 %26, %32 offset:416\n\t"
+      "ds_read_b64_tr_b16 %27, %33 offset:416\n\t"
+      "ds_read_b64_tr_b16 %28, %32 offset:448\n\t"
+      "ds_read_b64_tr_b16 %29, %33 offset:448\n\t"
+      "ds_read_b64_tr_b16 %30, %32 offset:480\n\t"
+      "ds_read_b64_tr_b16 %31, %33 offset:480\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15]), "=&v"(r[16]), "=&v"(r[17]), "=&v"(r[18]), "=&v"(r[19]), "=&v"(r[20]), "=&v"(r[21]), "=&v"(r[22]), "=&v"(r[23]), "=&v"(r[24]), "=&v"(r[25]), "=&v"(r[26]), "=&v"(r[27]), "=&v"(r[28]), "=&v"(r[29]), "=&v"(r[30]), "=&v"(r[31])
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
 // where the rows of one workgroup's slot range come from (all wave-uniform)
 struct DecRows {
   const uint16_t* E_b;        // this sequence's entries
@@ -1178,17 +1219,20 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     // P.V: V read transposed (keys 4g..4g+3 and 16+4g..16+4g+3 of column j of each tile)
     const uint32_t b0 = lds_addr(kb) + tr0 * RBP + 8 * (j & 3);
     const uint32_t b1 = lds_addr(kb) + tr1 * RBP + 8 * (j & 3);
+    // sixteen tiles per wait where the registers allow (one head tile), else eight
+    constexpr int TPW = (HTW == 1 && NT % 16 == 0) ? 16 : 8;
 #pragma unroll
-    for (int mb = 0; mb < NT / 8; ++mb) {
-      u32x2_t vr[16];
-      lds_read_tr16(b0 + 256 * mb, b1 + 256 * mb, vr);
+    for (int mb = 0; mb < NT / TPW; ++mb) {
+      u32x2_t vr[2 * TPW];
+      if constexpr (TPW == 16) lds_read_tr32(b0 + 512 * mb, b1 + 512 * mb, vr);
+      else lds_read_tr16(b0 + 256 * mb, b1 + 256 * mb, vr);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < TPW; ++u) {
         const u32x4_t vw = {vr[2 * u][0], vr[2 * u][1], vr[2 * u + 1][0], vr[2 * u + 1][1]};
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
 #pragma unroll
         for (int ht = 0; ht < HTW; ++ht)
-          O[ht][8 * mb + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vf, O[ht][8 * mb + u], 0, 0, 0);
+          O[ht][TPW * mb + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vf, O[ht][TPW * mb + u], 0, 0, 0);
       }
     }
   }
