@@ -1358,18 +1358,21 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const int rbeg = D - rope_dim;
   for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
     const int d0 = 2 * u;
-    float M = sig, Z, o0 = 0.f, o1 = 0.f;
-    if (n_split <= CB) {
-      // every split's (max, sum) and this pair of its output, all in flight at once
+    // running maximum M (from the sink on), with Z and (o0, o1) relative to it;
+    // the splits merge CB at a time, in split order
+    float M = sig, Z = (sig != -INFINITY) ? 1.f : 0.f, o0 = 0.f, o1 = 0.f;
+    for (int s0 = 0; s0 < n_split; s0 += CB) {
+      // every (max, sum) and output pair of the batch in flight at once:
       // unconditional loads (split index clamped; the extra ones are never
-      // used): a guarded load becomes a branch with its own wait
-      // lane l of each wave fetches the (max, sum) of split l % CB with one vector
-      // load in the same batch as the outputs; readlane hands them to every lane
+      // used), since a guarded load becomes a branch with its own wait.  Lane
+      // l of each wave fetches the (max, sum) of split s0 + l % CB with one
+      // vector load in the same batch as the outputs; readlane hands them to
+      // every lane.
       float ms[CB], ls[CB], a0[CB], a1[CB];
-      const float2 mlv = *(const float2*)(mlb + min((int)(threadIdx.x % CB), n_split - 1) * mstride);
+      const float2 mlv = *(const float2*)(mlb + min(s0 + (int)(threadIdx.x % CB), n_split - 1) * mstride);
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
-        const int sc = min(s, n_split - 1);
+        const int sc = min(s0 + s, n_split - 1);
         const _Float16* ps = base + sc * sstride;
         const uint32_t w = *(const uint32_t*)(ps + d0);
         a0[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
@@ -1380,30 +1383,27 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
         ms[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.x), s));
         ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.y), s));
       }
+      const int nb = min(CB, n_split - s0);
+      float bm = M;
 #pragma unroll
       for (int s = 0; s < CB; ++s)
-        if (s < n_split) M = fmaxf(M, ms[s]);
+        if (s < nb) bm = fmaxf(bm, ms[s]);
+      if (bm != M) {   // (M = -inf: Z and O are still 0)
+        const float r = (M == -INFINITY) ? 0.f : __expf(M - bm);
+        Z *= r;
+        o0 *= r;
+        o1 *= r;
+        M = bm;
+      }
       // split s weighs l_s exp(m_s - M) (its rows hold O_s / l_s)
-      Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
-        if (s < n_split) {
+        if (s < nb) {
           const float f = (ms[s] == -INFINITY) ? 0.f : ls[s] * __expf(ms[s] - M);
           Z += f;
           o0 += a0[s] * f;
           o1 += a1[s] * f;
         }
-      }
-    } else {
-      for (int s = 0; s < n_split; ++s) M = fmaxf(M, mlb[s * mstride]);
-      Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f;
-      for (int s = 0; s < n_split; ++s) {
-        const _Float16* ps = base + s * sstride;
-        const float ms = mlb[s * mstride];
-        const float f = (ms == -INFINITY) ? 0.f : mlb[s * mstride + 1] * __expf(ms - M);
-        Z += f;
-        o0 += (float)ps[d0] * f;
-        o1 += (float)ps[d0 + 1] * f;
       }
     }
     const float inv = Z > 0.f ? 1.f / Z : 0.f;
