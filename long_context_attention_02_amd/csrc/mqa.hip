@@ -742,12 +742,16 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
 // of a range skips the output rescale (O is still 0).  The split depends
 // only on the slot count; a combine kernel merges split partials in order.
 // ---------------------------------------------------------------------------
-// key slots per workgroup (whole chunks), a function of the query's slot count:
-// 192 up to 1,536 slots (more workgroups for a sparse selection), 288 above
-// (fewer split partials to merge for a long dense context)
-static constexpr int MQ_DEC_SPLIT_MAX = 288;
+// key slots per workgroup (whole chunks), a function of the query's slot count
+// only: 192 up to 1,536 slots, 160 above.  Both keep the decode grids near one
+// workgroup per CU: the 1M CSA decode (1,152 slots, 16 sequences, 2 head
+// groups) makes 192 workgroups, the 1M HCA decode (8,320 slots, 4 sequences,
+// 1 head group) 208.  More ranges mean more split partials to merge.
+static constexpr int MQ_DEC_SPLIT_LONG = 160;
 static constexpr int MQ_DEC_SPLIT_SMALL = 192;
 static constexpr long long MQ_DEC_SMALL_UPTO = 1536;
+// slot table capacity of the decode ranges (the larger of the two range sizes)
+static constexpr int MQ_DEC_TBL_SMALL = MQ_DEC_SPLIT_LONG > MQ_DEC_SPLIT_SMALL ? MQ_DEC_SPLIT_LONG : MQ_DEC_SPLIT_SMALL;
 // With many queries per sequence (prefill) the queries give the parallelism:
 // one range holds up to MQ_DEC_TABLE slots (the slot table's capacity), so a
 // CSA query (k + n_win slots) is one workgroup and needs no combine.
@@ -931,8 +935,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   __shared__ float rope_cs[D];   // (cos, sin) at position i of the pair starting at dim 2u; (1, 0) if not rotated
   __shared__ float gam[D];
   constexpr int NCH_MAX = TBL / MQ_CH;   // TBL: slot table capacity (a range's slots at most)
-  static_assert(MQ_DEC_SPLIT_MAX % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0 &&
-                    TBL % MQ_CH == 0 && MQ_DEC_SPLIT_MAX <= MQ_DEC_TABLE,
+  static_assert(MQ_DEC_SPLIT_LONG % MQ_CH == 0 && MQ_DEC_SPLIT_SMALL % MQ_CH == 0 &&
+                    TBL % MQ_CH == 0 && MQ_DEC_TBL_SMALL <= MQ_DEC_TABLE,
                 "whole chunks per range");
   __shared__ const uint16_t* sptr[TBL];   // row of every slot of the range
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
@@ -1458,7 +1462,7 @@ static bool mqa_decode_ok(int Tq, int n_h, int d) {
 static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int* n_split) {
   if (mqa_decode_ok(Tq, n_h, d)) {
     if (Tq < MQ_SPLIT_BELOW_TQ)
-      *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_MAX;
+      *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_LONG;
     else
       *kps = (int)min((long long)MQ_DEC_TABLE, max(1LL, (slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH);
     *n_split = (int)max(1LL, (slots_max + *kps - 1) / *kps);
@@ -1510,8 +1514,8 @@ static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
   const size_t lds = (size_t)MQ_DEC_NBUF * MQ_CH * (2 * D + 16);
-  // the small slot table for decode ranges (<= 288 slots), the large one for prefill
-  auto kfn = kps <= MQ_DEC_SPLIT_MAX ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_SPLIT_MAX, HTW>
+  // the small slot table for decode ranges (<= 192 slots), the large one for prefill
+  auto kfn = kps <= MQ_DEC_TBL_SMALL ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TBL_SMALL, HTW>
                                      : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE, HTW>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -157,8 +157,8 @@ def test_mqa_validation(lib):
     assert sparse(k=0) == CSA_E_SHAPE
     # a split decode query needs workspace
     # 1152 slots in ranges of 192: 6 split partials per (query, head), each d fp16
-    # outputs and a float (max, sum) pair; above 1536 slots the ranges hold 288
-    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 29 * 64 * (512 * 2 + 8)
+    # outputs and a float (max, sum) pair; above 1536 slots the ranges hold 160
+    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 52 * 64 * (512 * 2 + 8)
     assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * (512 * 2 + 8)
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
     need = lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128)
