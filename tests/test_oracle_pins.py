@@ -389,7 +389,7 @@ def test_no_keys_no_sink_is_zero_and_sink_only_is_zero():
     assert np.all(O.attend_one(q, np.zeros((0, 8)), i=3, sink=[0.5, -1.0], scale=0.3) == 0)
 
 
-def test_north_star_special_case_equals_textbook_causal_attention():
+def test_csa_special_case_equals_textbook_causal_attention():
     """m = 1 without overlap (entries = normalised raw rows), k >= n, no window,
     no sink, no RoPE: CSA is textbook causal softmax attention with K = V."""
     T, n_h, d, H, dI = 24, 3, 16, 2, 8
