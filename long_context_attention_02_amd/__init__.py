@@ -28,7 +28,7 @@ CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m long_context_attention_02_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python long_context_attention_02_amd/build.py` "
         "(or __graft_entry__.build()); the CSA/HCA core has no non-HIP implementation")
 _lib = ctypes.CDLL(LIB_PATH)
 

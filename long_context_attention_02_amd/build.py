@@ -1,6 +1,7 @@
 """Build ``libcsa.so`` (the HIP kernels and the C ABI) for gfx950, in-tree.
 
-Usage: ``python -m long_context_attention_02_amd.build`` or ``build()``.
+Usage: ``python long_context_attention_02_amd/build.py`` or ``__graft_entry__.build()``.
+Run it by path: importing the package first would fail while the library is missing.
 """
 from __future__ import annotations
 
