@@ -12,6 +12,12 @@ e4m3 indexer keys with a per-row scale) because the caches hold those bytes.
 Inputs are fp64 arrays of the exact stored input values; the raw rows of the
 entry cache are fetched on demand through a callable, so only the rows a
 query touches are ever decoded.
+
+Pins (tests/test_oracle_pins.py): each composition equals the plain
+whole-sequence chain (compress every entry from all tokens, store, score,
+select, attend) on small instances, with the cache's newest row planted stale
+so that reading it fails; source mutations of the block offset, the replaced
+row, the entry position and the window are shown to fail those pins.
 """
 from __future__ import annotations
 

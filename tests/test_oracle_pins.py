@@ -577,3 +577,149 @@ def test_chunked_prefill_equals_whole_sequence():
     np.testing.assert_allclose(got["I"], I, rtol=1e-12, atol=1e-12)
     assert np.array_equal(got["idx"], idx)
     np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# decode compositions (oracle.steps) against the plain whole-sequence chain
+# ---------------------------------------------------------------------------
+def _store_like(x, dtype):
+    from oracle.codecs import f64_to_bf16_value
+    return f64_to_bf16_value(x) if dtype == "bf16" else np.asarray(x, dtype=np.float64)
+
+
+def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
+    """One CSA decode step (query at i = m N, cached tokens 0 .. i-1) against the
+    plain chain over the whole sequence: compress every entry from all tokens,
+    store, score, select, attend.  The step's cache rows for entries < N-1 are
+    the pooled pre-norm rows (what an earlier step compressed); entry N-1 is
+    stale in the cache (its last token just arrived) and must come from the
+    step's own compression of tokens m(N-2) .. mN-1 [V4-abs §3.3 compressor
+    geometry; §3.5: the state cache holds the tail until its block completes]."""
+    from oracle.codecs import e4m3_to_f64
+    rng = np.random.default_rng(11)
+    m, N, c, dI, H, n_h, k, n_win, r = 4, 24, 16, 8, 3, 2, 7, 6, 4
+    i = m * N
+    T = m * N                         # tokens that feed entries; the query's own token is i
+    C = {n: rng.standard_normal((T, c)) for n in ("Ca", "Za", "Cb", "Zb")}
+    IC = {n: rng.standard_normal((T, dI)) for n in ("ICa", "IZa", "ICb", "IZb")}
+    win_raw = rng.standard_normal((i + 1, c))
+    qI = rng.standard_normal((H, dI))
+    w = rng.uniform(size=H)
+    q = rng.standard_normal((n_h, c))
+    sink = rng.standard_normal(n_h)
+    eps, scale, base = 1e-6, 1 / np.sqrt(c), 10000.0
+    # plain chain
+    E = _store_like(O.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, eps=eps,
+                               rope_dim=r, rope_base=base), dtype)
+    K = O.compress(IC["ICa"], IC["IZa"], IC["ICb"], IC["IZb"], m=m, overlap=1, T=T, normalize=False)
+    if k_dtype == "e4m3":
+        codes, sc = O.quantize_rows_e4m3(K)
+        K = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
+    else:
+        K = _store_like(K, k_dtype)
+    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, eps=eps, rope_dim=r,
+                               rope_base=base, pos_stride=1), dtype)
+    I = O.index_score(qI[None], w[None], K, [i], m=m)
+    idx, _ = O.topk(I, [i], m=m, k=k)
+    out = O.sparse_mqa(q[None], E, idx, W, q_pos=[i], n_win=n_win, eps=eps, sink=sink, rope_dim=r,
+                       rope_base=base, scale=scale)[0]
+    # the step: cached rows, a stale newest entry and key, the newest blocks' candidates
+    pre = O.pool_entries(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T)
+    pre[N - 1] = 1e3 * rng.standard_normal(c)        # stale: must not be read
+    KI = K.copy()
+    KI[N - 1] = 1e3 * rng.standard_normal(dI)        # stale: replaced by the step's own key
+    tb = m * (N - 2)
+    p = dict(i=i, m=m, N=N, k=k, n_win=n_win, d_I=dI, rope_dim=r, rope_base=base, eps=eps, scale=scale,
+             dtype=dtype, k_dtype=k_dtype, KI=KI, win_raw=win_raw[i - n_win + 1:],
+             **{n: v[tb:] for n, v in C.items()}, **{n: v[tb:] for n, v in IC.items()},
+             qI=qI, w=w, q=q, sink=sink)
+    got = steps_mod.csa_decode_sequence(p, lambda s: pre[np.asarray(s)])
+    np.testing.assert_allclose(got["I"], I[0], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(got["idx"], idx[0])
+    assert (N - 1) in set(idx[0].tolist()), "the fixture must select the newest entry"
+    np.testing.assert_allclose(got["k_new"], K[N - 1], rtol=0, atol=0)
+    np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
+
+
+def _hca_decode_pin(steps_mod, dtype="bf16"):
+    """One HCA decode step (m' = 8, query at i = m' N) against the plain chain:
+    compress every block of the whole sequence without overlap, then dense
+    attention over every visible entry, the window and the sink [V4-abs §3.3:
+    HCA is the non-overlapping, dense variant]."""
+    rng = np.random.default_rng(12)
+    m, N, c, n_h, n_win, r = 8, 12, 16, 3, 9, 4
+    i = m * N
+    T = m * N
+    Cf, Zf = rng.standard_normal((T, c)), rng.standard_normal((T, c))
+    win_raw = rng.standard_normal((i + 1, c))
+    q = rng.standard_normal((n_h, c))
+    sink = rng.standard_normal(n_h)
+    eps, scale, base = 1e-6, 1 / np.sqrt(c), 10000.0
+    E = _store_like(O.compress(Cf, Zf, None, None, m=m, overlap=0, T=T, eps=eps, rope_dim=r,
+                               rope_base=base), dtype)
+    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, eps=eps, rope_dim=r,
+                               rope_base=base, pos_stride=1), dtype)
+    out = O.dense_mqa(q[None], E, W, q_pos=[i], m=m, n_win=n_win, eps=eps, sink=sink, rope_dim=r,
+                      rope_base=base, scale=scale)[0]
+    pre = O.pool_entries(Cf, Zf, None, None, m=m, overlap=0, T=T)
+    pre[N - 1] = 1e3 * rng.standard_normal(c)        # stale newest entry: must not be read
+    tb = m * (N - 1)
+    p = dict(i=i, m=m, N=N, n_win=n_win, rope_dim=r, rope_base=base, eps=eps, scale=scale, dtype=dtype,
+             C=Cf[tb:], Z=Zf[tb:], win_raw=win_raw[i - n_win + 1:], q=q, sink=sink)
+    got = steps_mod.hca_decode_sequence(p, lambda s: pre[np.asarray(s)])
+    np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("dtype,k_dtype", [("bf16", "e4m3"), ("bf16", "bf16"), ("f32", "f32")])
+def test_csa_decode_step_equals_whole_sequence(dtype, k_dtype):
+    from oracle import steps
+    _csa_decode_pin(steps, dtype, k_dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hca_decode_step_equals_whole_sequence(dtype):
+    from oracle import steps
+    _hca_decode_pin(steps, dtype)
+
+
+def _mutant_steps(old: str, new: str):
+    """oracle.steps with one planted mistake (source text replaced once)."""
+    import inspect
+    import types
+
+    from oracle import steps
+    src = inspect.getsource(steps)
+    assert src.count(old) == 1, old
+    mod = types.ModuleType("oracle._steps_mutant")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), "<oracle.steps mutant>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("old,new", [
+    ("tok_base = m * (N - 2)", "tok_base = m * (N - 2) + 1"),          # block offset off by one
+    ("tok_base = m * (N - 2)", "tok_base = m * (N - 2) - 1"),
+    ("KI[N - 1] = k_new[0]", "KI[N - 2] = k_new[0]"),                   # wrong key row replaced
+    ("rows[sel == N - 1] = e_new", "rows[sel == N - 2] = e_new"),       # wrong entry row replaced
+    ("old = sel[sel != N - 1]", "old = sel[sel != -1]"),                # stale cache row read
+    ("s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]\n    e_new = _store",
+     "s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base, pos_offset=1)[0]\n    e_new = _store"),
+])
+def test_csa_decode_pin_catches_planted_mistakes(old, new):
+    bad = _mutant_steps(old, new)
+    with pytest.raises((AssertionError, ValueError)):
+        _csa_decode_pin(bad)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("tok_base=m * (N - 1),\n                       s_begin=N - 1",
+     "tok_base=m * (N - 1) + 1,\n                       s_begin=N - 1"),   # block offset off by one
+    ("E[N - 1] = _store(e_new", "E[N - 2] = _store(e_new"),              # wrong entry replaced
+    ("E[: N - 1] = entry_rows(kv_raw_rows(s[: N - 1]), s[: N - 1]",
+     "E[: N - 1] = entry_rows(kv_raw_rows(s[1: N]), s[: N - 1]"),         # rows shifted by one
+    ("np.concatenate([E, W])", "np.concatenate([E, W[:-1]])"),        # window without the own token
+])
+def test_hca_decode_pin_catches_planted_mistakes(old, new):
+    bad = _mutant_steps(old, new)
+    with pytest.raises((AssertionError, ValueError)):
+        _hca_decode_pin(bad)
