@@ -141,7 +141,8 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
  *  q_pos   : [B][Tq] int32 absolute positions (>= 0).
  *  I_out   : [B][Tq][N_cap] fp32.
  *  Supported: H_I <= 64, d_I <= 256 (any); the matrix-core path covers
- *  H_I % 16 == 0 and d_I in {32, 64, 128} with BF16 queries.
+ *  H_I in {16, 32, 64} and d_I in {32, 64, 128} with BF16 queries (other
+ *  head counts, e.g. 48, take the generic kernel).
  */
 int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos,

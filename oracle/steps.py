@@ -46,8 +46,15 @@ def window_rows(raw_rows: np.ndarray, toks: np.ndarray, *, rope_dim: int, rope_b
     return _store(W, dtype)
 
 
-def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
+def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray],
+                        attend_idx=None) -> dict:
     """One CSA decode step of one sequence.
+
+    ``attend_idx`` (optional, k indices with -1 padding) replaces the oracle's
+    own top-k as the set the query attends over; the scores and the oracle's
+    selection are still returned.  A selection that another implementation
+    made from its own fp32 scores may differ at near-ties of the k-th score,
+    and its attention output is still defined exactly.
 
     p holds: i, m, N, k, n_win, d_I, rope_dim, rope_base, eps, scale, dtype, k_dtype;
     KI (N x d_I fp64, fp8 keys already times their scale), win_raw (n_win x d,
@@ -76,7 +83,8 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     I = O.index_score(p["qI"][None], p["w"][None], KI, [i], m=m)
     idx, vals = O.topk(I, [i], m=m, k=k)
     # rows the query reads
-    sel = idx[0][idx[0] >= 0]
+    use = idx[0] if attend_idx is None else np.asarray(attend_idx, dtype=np.int64)
+    sel = use[use >= 0]
     rows = np.zeros((len(sel), p["q"].shape[-1]))
     old = sel[sel != N - 1]
     if len(old):
@@ -112,8 +120,11 @@ def hca_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     return {"out": out}
 
 
-def csa_prefill_queries(p: dict, ts, kv_raw_rows: Callable[[np.ndarray], np.ndarray]) -> dict:
+def csa_prefill_queries(p: dict, ts, kv_raw_rows: Callable[[np.ndarray], np.ndarray],
+                        attend_idx=None) -> dict:
     """Chunked CSA prefill, evaluated for the chunk queries ``ts`` only.
+    ``attend_idx`` (optional, [len(ts), k]) replaces the oracle's own
+    selections as the sets the queries attend over (see csa_decode_sequence).
 
     The chunk holds queries at positions p0 .. p0 + Tq - 1.  Entries s0 = p0/m ..
     s1 = min(N, (p0 + Tq)/m) complete inside the chunk and are compressed from
@@ -148,7 +159,8 @@ def csa_prefill_queries(p: dict, ts, kv_raw_rows: Callable[[np.ndarray], np.ndar
         i = p0 + int(t)
         I = O.index_score(p["qI"][j][None], p["w"][j][None], KI, [i], m=m)
         idx, _ = O.topk(I, [i], m=m, k=k)
-        sel = idx[0][idx[0] >= 0]
+        use = idx[0] if attend_idx is None else np.asarray(attend_idx[j], dtype=np.int64)
+        sel = use[use >= 0]
         rows = np.zeros((len(sel), p["q"].shape[-1]))
         old = sel < s0
         if old.any():

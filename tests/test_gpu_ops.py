@@ -180,6 +180,7 @@ INDEX_CASES = [
     ("bf16_prefill_h32_d64", 1, 17, 32, 64, 260, 2, "bf16", "bf16", "prefill"),
     ("bf16_generic_h8_d48", 2, 5, 8, 48, 300, 4, "bf16", "bf16", "partial"),
     ("fp8_generic_h48_d128", 1, 3, 48, 128, 500, 4, "bf16", "e4m3", "all"),
+    ("bf16_generic_h48_d128_prefill", 1, 19, 48, 128, 400, 4, "bf16", "bf16", "prefill"),
 ]
 
 
@@ -291,6 +292,14 @@ MQA_CASES = [
     # prefill through the streaming kernel: a full 2,048-slot range, then two ranges and a combine
     ("bf16_sparse_prefill_table_full", False, "bf16", 1, 16, 32, 128, 3000, 2000, 4, 48, 64, 32, "none", False, "all"),
     ("bf16_dense_prefill_two_ranges", True, "bf16", 1, 16, 32, 128, 2300, 0, 4, 64, 128, 32, "normal", True, "all"),
+    # head counts that are not a multiple of 32 at d < 512: the group kernels.  16 or more
+    # queries with more than 128 slots take the multi-group kernel; fewer queries split
+    # the slots into 128-slot ranges (group kernel + combine)
+    ("bf16_multi_group_h16_d128_sparse", False, "bf16", 2, 16, 16, 128, 2000, 300, 4, 64, 128, 64, "normal", True, "partial"),
+    ("bf16_multi_group_h48_d256_dense", True, "bf16", 1, 17, 48, 256, 400, 0, 1, 32, 64, 32, "normal", True, "all"),
+    ("bf16_split_group_h16_d128_sparse", False, "bf16", 3, 1, 16, 128, 3000, 600, 4, 128, 128, 64, "normal", True, "all"),
+    ("bf16_split_group_h48_d256_dense", True, "bf16", 2, 2, 48, 256, 700, 0, 4, 128, 128, 64, "normal", False, "partial"),
+    ("bf16_split_group_h48_d128_sparse_nosink", False, "bf16", 1, 3, 48, 128, 900, 333, 4, 16, 32, 32, "none", True, "partial"),
 ]
 
 
