@@ -1,19 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the CSA/HCA attention core on one MI355X.
 
-Workload: 1M-context CSA decode, Pro-like -- 16 sequences, 1,048,576 cached
-tokens each (262,144 compressed entries, m = 4), fp8 (e4m3) indexer keys with
-per-row scales (64 heads x 128), top-k 1024, bf16 MQA over 512-wide entries for
-128 query heads, 128-token window, sink.  One step = the whole hot path for
-one new token per sequence: compress (window row, newest entry, newest indexer
-key), indexer score, top-k, sparse MQA.  Inputs are synthetic (seeded N(0,1),
-U(0,1) head weights) and resident in HBM before timing starts.
+Headline workload: the 1M-context CSA decode, Pro-like -- 16 sequences,
+1,048,576 cached tokens each (262,144 compressed entries, m = 4), fp8 (e4m3)
+indexer keys with per-row scales (64 heads x 128), top-k 1024, bf16 MQA over
+512-wide entries for 128 query heads, 128-token window, sink.  One step = the
+whole hot path for one new token per sequence: compress (window row, newest
+entry, newest indexer key), indexer score, top-k, sparse MQA.  Inputs are
+synthetic (seeded N(0,1), U(0,1) head weights) and resident in HBM before
+timing starts.
 
-Prints ONE JSON line.  Also reported: the prefill indexer (16,384 queries x
-32,768 entries, 64 heads x 128, bf16) in TFLOP/s; the HCA dense decode (4
-sequences x 8,192 entries) and each call of the chunked-prefill step, each
-against its roofline; and the fp64 oracle timed on a bounded sample of the
-decode workload on the host cores.
+Timing: each input replica's step is captured once as a HIP graph; the timed
+steps replay the graphs round-robin over replicas whose working set exceeds
+twice the 256 MB Infinity Cache, so no step finds the previous step's data
+there.  The K timed steps run back to back between two events (the headline
+ms_per_step); a second pass brackets every step with timing-only events for
+the median and the 10th / 90th percentiles, and times the indexer launch
+inside each step (the roofline's kernel).
+
+Prints ONE JSON line.  Also reported, each against its roofline: the Flash-like
+CSA decode (8 sequences x 16,384 entries, k = 512), the HCA dense decode (4
+sequences x 8,192 entries), the prefill indexer (16,384 queries x 32,768
+entries, bf16) and each call of the chunked-prefill step; and the fp64 oracle
+timed on a bounded sample of the decode workload on the host cores.
 """
 from __future__ import annotations
 
@@ -30,177 +39,29 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0    # dense bf16 matrix peak
+MALL_BYTES = 256 << 20         # Infinity Cache
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the HCA decode and prefill-step measurements")
-    ap.add_argument("--cpu-sample", type=int, default=16, help="sequences the oracle runs")
+                    help="skip the Flash-like decode, HCA decode and prefill-step measurements")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle's sample until this much CPU time has passed")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (3x) to calibrate HBM byte counters")
     return ap.parse_args()
 
 
-def traffic_from_profiles(kernel_tag: str, src_file: str):
-    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE,
-    copy-kernel calibrated), valid only while the kernel source is unchanged."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"{kernel_tag}.pmc.md")
-    if not os.path.exists(path):
-        return None
-    txt = open(path).read()
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
-    if not (m_b and m_h):
-        return None
-    cur = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
-    return float(m_b.group(1)) if cur == m_h.group(1) else None
-
-
-def cpu_baseline(run, n_seq: int):
-    """The fp64 oracle on n_seq sequences of the same workload (host cores)."""
-    from threadpoolctl import threadpool_info
-
-    from oracle import steps
-    from tests._pipeline_ref import csa_decode_params
-
-    wl = run.wl
-    n_seq = max(1, min(n_seq, wl.B))
-    inputs = [csa_decode_params(run, b) for b in range(n_seq)]   # decoding the bytes is not timed
-    t0 = time.perf_counter()
-    for p, rows in inputs:
-        steps.csa_decode_sequence(p, rows)
-    dt = time.perf_counter() - t0
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    return {"value": round(n_seq / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_seq} of {wl.B} sequences, full step each (fp64 numpy; BLAS threads "
-                      f"{threads}, host nproc {os.cpu_count()})",
-            "seconds": round(dt, 3)}
-
-
-def prefill_indexer(steps: int, warmup: int):
-    """csa_index_score on the chunked-prefill shapes: 16,384 queries over 32,768 entries."""
-    import torch
-
-    import long_context_attention_02_amd as csa
-    from synth import Gen
-    from synth.workloads import CSA_PREFILL_PRO as wl, T_KI, T_QI, T_WI
-
-    g = Gen(wl.wid, "cuda")
-    qI = g.normal(T_QI, (1, wl.Tq, wl.H_I, wl.d_I), "bf16")
-    wI = g.uniform(T_WI, (1, wl.Tq, wl.H_I))
-    K = g.normal(T_KI, (1, wl.N_cap, wl.d_I), "bf16")
-    pos = (wl.q_pos0 + torch.arange(wl.Tq, dtype=torch.int32, device="cuda")).view(1, -1).contiguous()
-    I = torch.empty((1, wl.Tq, wl.N_cap), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
-    torch.cuda.synchronize()
-    # every launch timed on its own (timing-only events); the median is reported,
-    # the mean beside it (single launches vary by a few percent with the clock)
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
-        b.record()
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in ev)
-    ms = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
-    ms_mean = sum(per) / len(per)
-    pairs = sum(min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq))
-    flops = 2.0 * pairs * wl.H_I * wl.d_I
-    tfs = flops / (ms * 1e-3) / 1e12
-    del qI, wI, K, I
-    return {"workload": wl.name, "ms": round(ms, 4), "ms_mean": round(ms_mean, 4),
-            "ms_min": round(per[0], 4), "launches": steps, "TFLOP/s": round(tfs, 2),
-            "causal_flops": flops,
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}}
-
-
-def _timed(fn, steps: int, warmup: int) -> float:
-    """Average ms of fn() over `steps` calls, HIP events on the current stream."""
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        fn()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
-
-
-def _roof(achieved: float, bound: str) -> dict:
-    peak, unit = (HBM_PEAK_GBS, "GB/s") if bound == "hbm" else (MFMA_BF16_PEAK_TFS, "TFLOP/s")
-    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4)}
-
-
-def hca_decode(steps: int, warmup: int):
-    """Dense MQA (HCA) decode: 4 sequences over 8,192 entries of 128 tokens each (1M
-    context) plus window and sink; the step also recompresses the newest block."""
-    import torch
-
-    from long_context_attention_02_amd.pipeline import HCADecode
-    from synth.workloads import HCA_DECODE as wl
-
-    run = HCADecode(wl, "cuda", keep_raw=False)
-    step_ms = _timed(run.step, steps, warmup)
-    attn_ms = _timed(run.attend, steps, warmup)
-    n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
-    rows = wl.B * (n_vis + wl.n_win)
-    attn_bytes = rows * wl.d * 2 + 2 * wl.B * wl.n_h * wl.d * 2          # rows read; q and out
-    attn_flops = 4.0 * wl.B * wl.n_h * (n_vis + wl.n_win) * wl.d
-    del run
-    torch.cuda.empty_cache()
-    return {"workload": wl.name, "step_ms": round(step_ms, 5), "tokens/s": round(wl.B / (step_ms * 1e-3), 1),
-            "hca_dense_mqa_ms": round(attn_ms, 5), "algorithmic_bytes": attn_bytes,
-            "flops": attn_flops, "TFLOP/s": round(attn_flops / (attn_ms * 1e-3) / 1e12, 2),
-            "roofline": _roof(attn_bytes / (attn_ms * 1e-3) / 1e9, "hbm")}
-
-
-def prefill_rows(steps: int, warmup: int):
-    """The chunked-prefill step (16,384 queries over 32,768 entries, k = 1024) call by
-    call: compression of the chunk, indexer, top-k and sparse MQA."""
-    import torch
-
-    from long_context_attention_02_amd.pipeline import CSAPrefill
-    from synth.workloads import CSA_PREFILL_PRO as wl
-
-    run = CSAPrefill(wl, "cuda", keep_raw=False)
-    ms = {"compress": _timed(run.compress_new, steps, warmup), "index": _timed(run.index, steps, warmup),
-          "topk": _timed(run.select, steps, warmup), "sparse_mqa": _timed(run.attend, steps, warmup)}
-    n_new = run.s_new1 - run.s_new0
-    n_vis = [min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq)]
-    # compress: window rows (read + write), candidates of the new KV entries and indexer keys
-    # (C and Z of sets a and b, 2 * 2m rows each), entries written
-    comp_bytes = (2 * wl.B * wl.Tq * wl.d * 2 + wl.B * n_new * (4 * wl.m * (wl.d + wl.d_I) * 2
-                                                                + (wl.d + wl.d_I) * 2))
-    topk_bytes = 4 * wl.B * sum(n_vis) + 4 * wl.B * wl.Tq * wl.k
-    attn_flops = 4.0 * wl.B * wl.Tq * wl.n_h * (wl.k + wl.n_win) * wl.d
-    index_flops = 2.0 * wl.B * sum(n_vis) * wl.H_I * wl.d_I
-    out = {"workload": wl.name, "ms": {k: round(v, 4) for k, v in ms.items()},
-           "compress": {"algorithmic_bytes": comp_bytes,
-                        "roofline": _roof(comp_bytes / (ms["compress"] * 1e-3) / 1e9, "hbm")},
-           "index": {"flops": index_flops,
-                     "roofline": _roof(index_flops / (ms["index"] * 1e-3) / 1e12, "mfma")},
-           "topk": {"algorithmic_bytes": topk_bytes,
-                    "roofline": _roof(topk_bytes / (ms["topk"] * 1e-3) / 1e9, "hbm")},
-           "sparse_mqa": {"flops": attn_flops,
-                          "roofline": _roof(attn_flops / (ms["sparse_mqa"] * 1e-3) / 1e12, "mfma")}}
-    del run
-    torch.cuda.empty_cache()
-    return out
-
-
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
 class TimingEvent:
     """A HIP event made for timing only (hipEventDisableSystemFence): recording it
     skips the system-scope cache writeback and invalidation that a default event
@@ -234,6 +95,323 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self.h)
 
 
+def capture(fns, use_graph: bool):
+    """One HIP graph per function (each a replica's step or part of it); returns
+    the replay callables and None, or the eager functions and the reason the
+    capture was not used."""
+    import torch
+    if not use_graph:
+        return list(fns), "disabled"
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    try:
+        with torch.cuda.stream(s):
+            for fn in fns:          # warm on the capture stream first
+                fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graphs = []
+        for fn in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                fn()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        capture.keep.extend(graphs)
+        return [g.replay for g in graphs], None
+    except Exception as e:  # noqa: BLE001 -- reported in the JSON line
+        torch.cuda.synchronize()
+        return list(fns), f"{type(e).__name__}: {e}"
+
+
+capture.keep = []
+
+
+def _pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    pos = q * (len(xs) - 1)
+    lo = int(pos)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (pos - lo)
+
+
+def time_rotating(steps, K: int, warmup: int):
+    """K steps replayed round-robin over the replicas, back to back between two
+    events; returns the average ms per step."""
+    import torch
+    R = len(steps)
+    for s in range(warmup):
+        steps[s % R]()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for s in range(K):
+        steps[s % R]()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / K
+
+
+def time_each(parts, K: int, inner: int | None = None):
+    """K steps, each a sequence of replica parts with a timing-only event before
+    every part and after the last; returns per-step ms and, for part `inner`,
+    per-launch ms."""
+    import torch
+    R = len(parts)
+    n = len(parts[0])
+    ev = [[TimingEvent() for _ in range(n + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for s in range(K):
+        for p in range(n):
+            ev[s][p].record()
+            parts[s % R][p]()
+        ev[s][n].record()
+    torch.cuda.synchronize()
+    per_step = [ev[s][0].elapsed_time(ev[s + 1][0]) for s in range(K - 1)]
+    per_inner = [ev[s][inner].elapsed_time(ev[s][inner + 1]) for s in range(K)] if inner is not None else []
+    return per_step, per_inner
+
+
+def dist(xs):
+    return {"median": round(_pct(xs, 0.5), 5), "p10": round(_pct(xs, 0.1), 5),
+            "p90": round(_pct(xs, 0.9), 5), "mean": round(sum(xs) / len(xs), 5), "n": len(xs)}
+
+
+def _roof(achieved: float, bound: str, **extra) -> dict:
+    peak, unit = (HBM_PEAK_GBS, "GB/s") if bound == "hbm" else (MFMA_BF16_PEAK_TFS, "TFLOP/s")
+    d = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4)}
+    d.update(extra)
+    return d
+
+
+def replicas_for(bytes_per_replica: float, at_least: int = 2) -> int:
+    """Replicas whose combined working set is at least twice the Infinity Cache."""
+    need = int((2 * MALL_BYTES + bytes_per_replica - 1) // max(bytes_per_replica, 1))
+    return max(at_least, need)
+
+
+def traffic_from_profiles(kernel_tag: str, src_file: str):
+    """HBM bytes per launch measured with rocprofv3 --pmc (FETCH_SIZE + WRITE_SIZE,
+    copy-kernel calibrated), valid only while the kernel source is unchanged."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}.pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_h = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    if not (m_b and m_h):
+        return None
+    cur = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if cur == m_h.group(1) else None
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of the decode steps (bytes every step must move once; the
+# fp32 scores between the indexer and the top-k are an intermediate and are
+# not counted)
+# ---------------------------------------------------------------------------
+def csa_decode_bytes(wl) -> dict:
+    esz = {"e4m3": 1, "bf16": 2, "f32": 4}
+    kv = esz[wl.dtype]
+    B, N, dI, H, k, d = wl.B, wl.N_cap, wl.d_I, wl.H_I, wl.k, wl.d
+    keys = B * N * dI * esz[wl.k_dtype]
+    scales = B * N * 4 if wl.k_dtype == "e4m3" else 0
+    q_index = B * (H * dI * 2 + H * 4)
+    gather = B * k * d * kv
+    window = B * wl.n_win * d * kv
+    q = out = B * wl.n_h * d * kv
+    idx = B * k * 4
+    step = keys + scales + gather + window + q + out + q_index + idx
+    return {"step": step, "index_kernel": keys + scales + q_index, "keys": keys, "scales": scales,
+            "gather": gather, "window": window, "q": q, "out": out, "q_index_w_idx": q_index + idx}
+
+
+def hca_decode_bytes(wl) -> dict:
+    n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
+    entries = wl.B * n_vis * wl.d * 2
+    tail = wl.B * 2 * wl.m * wl.d * 2          # C and Z of the recompressed block
+    window = wl.B * wl.n_win * wl.d * 2
+    qo = 2 * wl.B * wl.n_h * wl.d * 2
+    return {"step": entries + tail + window + qo, "attention": entries + window + qo}
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def csa_decode(wl, K: int, warmup: int, use_graph: bool, keep_raw_first: bool = False):
+    """A CSA decode workload: R replicas, whole-step graphs (pass 1) and
+    three-part graphs with events (pass 2: per-step distribution and the
+    indexer's launch time)."""
+    import torch
+
+    from long_context_attention_02_amd.pipeline import CSADecode
+    ab = csa_decode_bytes(wl)
+    per_replica = ab["step"]
+    R = replicas_for(per_replica)
+    runs = [CSADecode(wl, "cuda", keep_raw=(keep_raw_first and r == 0)) for r in range(R)]
+    torch.cuda.synchronize()
+    steps, err = capture([r.step for r in runs], use_graph)
+    ms_step = time_rotating(steps, K, warmup)
+    pre, e1 = capture([r.compress_new for r in runs], use_graph)
+    idx_, e2 = capture([r.index for r in runs], use_graph)
+    post, e3 = capture([(lambda r=r: (r.select(), r.attend())) for r in runs], use_graph)
+    parts = [[pre[r], idx_[r], post[r]] for r in range(R)]
+    per_step, per_index = time_each(parts, K, inner=1)
+    res = {"workload": wl.name, "replicas": R, "graph": err or e1 or e2 or e3 or "hip graph replay",
+           "ms_per_step": ms_step, "step_ms_with_events": dist(per_step),
+           "index_ms": dist(per_index), "bytes": ab}
+    return res, runs
+
+
+def hca_decode(K: int, warmup: int, use_graph: bool):
+    """Dense MQA (HCA) decode: 4 sequences over 8,192 entries of 128 tokens each (1M
+    context) plus window and sink; the step also recompresses the newest block."""
+    import torch
+
+    from long_context_attention_02_amd.pipeline import HCADecode
+    from synth.workloads import HCA_DECODE as wl
+
+    ab = hca_decode_bytes(wl)
+    R = replicas_for(ab["step"])
+    runs = [HCADecode(wl, "cuda", keep_raw=False) for _ in range(R)]
+    steps, err = capture([r.step for r in runs], use_graph)
+    ms_step = time_rotating(steps, K, warmup)
+    pre, _ = capture([r.compress_new for r in runs], use_graph)
+    att, _ = capture([r.attend for r in runs], use_graph)
+    per_step, per_attn = time_each([[pre[r], att[r]] for r in range(R)], K, inner=1)
+    pre_ms = [a - b for a, b in zip(per_step, per_attn)]
+    n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
+    flops = 4.0 * wl.B * wl.n_h * (n_vis + wl.n_win) * wl.d
+    attn_ms = _pct(per_attn, 0.5)
+    out = {"workload": wl.name, "replicas": R, "graph": err or "hip graph replay",
+           "ms_per_step": round(ms_step, 5), "tokens/s": round(wl.B / (ms_step * 1e-3), 1),
+           "step_ms_with_events": dist(per_step), "compress_ms": dist(pre_ms),
+           "hca_dense_mqa_ms": dist(per_attn), "algorithmic_bytes": ab,
+           "roofline": _roof(ab["step"] / (ms_step * 1e-3) / 1e9, "hbm", scope="whole step"),
+           "attention_roofline": _roof(ab["attention"] / (attn_ms * 1e-3) / 1e9, "hbm",
+                                       kernel="hca_dense_mqa (attention + combine)"),
+           "attention_TFLOP/s": round(flops / (attn_ms * 1e-3) / 1e12, 2)}
+    del runs, steps, pre, att
+    capture.keep.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_indexer(steps: int, warmup: int):
+    """csa_index_score on the chunked-prefill shapes: 16,384 queries over 32,768 entries."""
+    import torch
+
+    import long_context_attention_02_amd as csa
+    from synth import Gen
+    from synth.workloads import CSA_PREFILL_PRO as wl, T_KI, T_QI, T_WI
+
+    g = Gen(wl.wid, "cuda")
+    qI = g.normal(T_QI, (1, wl.Tq, wl.H_I, wl.d_I), "bf16")
+    wI = g.uniform(T_WI, (1, wl.Tq, wl.H_I))
+    K = g.normal(T_KI, (1, wl.N_cap, wl.d_I), "bf16")
+    pos = (wl.q_pos0 + torch.arange(wl.Tq, dtype=torch.int32, device="cuda")).view(1, -1).contiguous()
+    I = torch.empty((1, wl.Tq, wl.N_cap), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
+    torch.cuda.synchronize()
+    # every launch timed on its own (timing-only events); the median is reported
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        csa.csa_index_score(qI, wI, K, pos, I, m=wl.m)
+        b.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    ms = _pct(per, 0.5)
+    pairs = sum(min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq))
+    flops = 2.0 * pairs * wl.H_I * wl.d_I
+    tfs = flops / (ms * 1e-3) / 1e12
+    del qI, wI, K, I
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "ms": dist(per), "TFLOP/s": round(tfs, 2), "causal_flops": flops,
+            "roofline": _roof(tfs, "mfma")}
+
+
+def _timed(fn, steps: int, warmup: int) -> list:
+    """Per-call ms of fn() over `steps` calls, timing-only events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def prefill_rows(steps: int, warmup: int):
+    """The chunked-prefill step (16,384 queries over 32,768 entries, k = 1024) call by
+    call: compression of the chunk, indexer, top-k and sparse MQA."""
+    import torch
+
+    from long_context_attention_02_amd.pipeline import CSAPrefill
+    from synth.workloads import CSA_PREFILL_PRO as wl
+
+    run = CSAPrefill(wl, "cuda", keep_raw=False)
+    per = {"compress": _timed(run.compress_new, steps, warmup), "index": _timed(run.index, steps, warmup),
+           "topk": _timed(run.select, steps, warmup), "sparse_mqa": _timed(run.attend, steps, warmup)}
+    ms = {k: _pct(v, 0.5) for k, v in per.items()}
+    n_new = run.s_new1 - run.s_new0
+    n_vis = [min(wl.N_cap, (wl.q_pos0 + t + 1) // wl.m) for t in range(wl.Tq)]
+    # compress: window rows (read + write), candidates of the new KV entries and indexer keys
+    # (C and Z of sets a and b, 2 * 2m rows each), entries written
+    comp_bytes = (2 * wl.B * wl.Tq * wl.d * 2 + wl.B * n_new * (4 * wl.m * (wl.d + wl.d_I) * 2
+                                                                + (wl.d + wl.d_I) * 2))
+    topk_bytes = 4 * wl.B * sum(n_vis) + 4 * wl.B * wl.Tq * wl.k
+    attn_flops = 4.0 * wl.B * wl.Tq * wl.n_h * (wl.k + wl.n_win) * wl.d
+    index_flops = 2.0 * wl.B * sum(n_vis) * wl.H_I * wl.d_I
+    out = {"workload": wl.name, "ms": {k: round(v, 4) for k, v in ms.items()}, "calls": steps,
+           "compress": {"algorithmic_bytes": comp_bytes,
+                        "roofline": _roof(comp_bytes / (ms["compress"] * 1e-3) / 1e9, "hbm")},
+           "index": {"flops": index_flops,
+                     "roofline": _roof(index_flops / (ms["index"] * 1e-3) / 1e12, "mfma")},
+           "topk": {"algorithmic_bytes": topk_bytes,
+                    "roofline": _roof(topk_bytes / (ms["topk"] * 1e-3) / 1e9, "hbm")},
+           "sparse_mqa": {"flops": attn_flops,
+                          "roofline": _roof(attn_flops / (ms["sparse_mqa"] * 1e-3) / 1e12, "mfma")}}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(run, seconds: float):
+    """The fp64 oracle on all sequences of the same decode step, repeated until
+    `seconds` of host time have passed (at least once)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import steps
+    from tests._pipeline_ref import csa_decode_params
+
+    wl = run.wl
+    inputs = [csa_decode_params(run, b) for b in range(wl.B)]   # decoding the bytes is not timed
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for p, rows in inputs:
+            steps.csa_decode_sequence(p, rows)
+            n += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} sequence-steps ({n // wl.B} passes over all {wl.B} sequences of one step), "
+                      f"full step each (fp64 numpy; BLAS threads {threads}, host nproc {os.cpu_count()})",
+            "seconds": round(dt, 3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -242,32 +420,16 @@ def main():
         sys.exit(2)
     import torch
 
-    from long_context_attention_02_amd.pipeline import CSADecode
-    from synth.workloads import CSA_DECODE_1M as wl
+    from synth.workloads import CSA_DECODE_1M as wl, CSA_DECODE_FLASH
 
     torch.cuda.set_device(0)
-    run = CSADecode(wl, "cuda", keep_raw=not args.no_cpu_baseline)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        run.step()
-    torch.cuda.synchronize()
-
+    use_graph = not args.no_graph
     K = args.steps
-    # the indexer's own launch times, from timing-only events on the step's stream
-    ev_idx = [(TimingEvent(), TimingEvent()) for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for s in range(K):
-        run.step(index_events=ev_idx[s])
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / K
-    idx_ms = sum(a.elapsed_time(b) for a, b in ev_idx) / K
-
-    ab = run.algorithmic_bytes()
+    head, runs = csa_decode(wl, K, args.warmup, use_graph, keep_raw_first=not args.no_cpu_baseline)
+    ms_step = head["ms_per_step"]
+    ab = head["bytes"]
     tokens_s = wl.B / (ms_step * 1e-3)
+    idx_ms = head["index_ms"]["mean"]
     idx_gbs = ab["index_kernel"] / (idx_ms * 1e-3) / 1e9
     step_gbs = ab["step"] / (ms_step * 1e-3) / 1e9
     src = os.path.join(ROOT, "long_context_attention_02_amd", "csrc", "index_score.hip")
@@ -289,13 +451,17 @@ def main():
         "config": {"workload": wl.name, "batch": wl.B, "context_tokens": wl.ctx,
                    "compressed_entries": wl.N_cap, "m": wl.m, "top_k": wl.k, "indexer": "64x128 e4m3",
                    "query_heads": wl.n_h, "entry_dim": wl.d, "window": wl.n_win},
-        "step_hbm_GBps": round(step_gbs, 1),
-        "step_algorithmic_bytes": ab["step"],
+        "timing": {"replicas": head["replicas"], "launch": head["graph"],
+                   "step_ms_with_events": head["step_ms_with_events"]},
         "roofline": {"bound": "hbm", "kernel": "index_mfma_decode (csa_index_score)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": ab["index_kernel"],
-                     "avg_launch_ms": round(idx_ms, 5)},
+                     "avg_launch_ms": round(idx_ms, 5), "launch_ms": head["index_ms"]},
+        "step_roofline": {"bound": "hbm", "scope": "whole decode step (compress, index, top-k, attention)",
+                          "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["step"],
+                          "bytes": ab},
     }
     if args.copy_calibration:
         src_t = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -305,18 +471,32 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes_each_way"] = 512 << 20
         del src_t, dst_t
+    keep = runs[0] if not args.no_cpu_baseline else None
+    del runs
+    capture.keep.clear()
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        fl, fl_runs = csa_decode(CSA_DECODE_FLASH, K, args.warmup, use_graph)
+        del fl_runs
+        capture.keep.clear()
+        torch.cuda.empty_cache()
+        fms = fl["ms_per_step"]
+        result["csa_decode_flash"] = {
+            "workload": fl["workload"], "replicas": fl["replicas"], "graph": fl["graph"],
+            "ms_per_step": round(fms, 5), "tokens/s": round(CSA_DECODE_FLASH.B / (fms * 1e-3), 1),
+            "step_ms_with_events": fl["step_ms_with_events"], "index_ms": fl["index_ms"],
+            "algorithmic_bytes": fl["bytes"]["step"],
+            "roofline": _roof(fl["bytes"]["step"] / (fms * 1e-3) / 1e9, "hbm", scope="whole step")}
+        result["hca_decode"] = hca_decode(K, args.warmup, use_graph)
     if not args.no_prefill:
-        del run.I
+        if keep is not None:
+            keep.I = None
         torch.cuda.empty_cache()
         result["prefill_indexer"] = prefill_indexer(steps=11, warmup=5)
-    if not args.no_secondary:
-        if hasattr(run, "I"):
-            del run.I
-        torch.cuda.empty_cache()
-        result["hca_decode"] = hca_decode(steps=20, warmup=5)
-        result["prefill_step"] = prefill_rows(steps=3, warmup=1)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(run, args.cpu_sample)
+        if not args.no_secondary:
+            result["prefill_step"] = prefill_rows(steps=3, warmup=1)
+    if keep is not None:
+        result["cpu_baseline"] = cpu_baseline(keep, args.cpu_seconds)
     print(json.dumps(result))
 
 

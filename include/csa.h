@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 /* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities). */
 enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 };
@@ -75,7 +75,14 @@ const char* csa_last_error(void);
  *      tok_base + r.  Z_a or Z_b may be NULL (all logits 0 = plain mean).
  *      C_b is required iff overlap.  Every candidate token < T of every
  *      requested entry must lie in [tok_base, tok_base + R).
- *  T        : tokens present (same for all B sequences); s_end <= ceil(T/m).
+ *  T        : tokens present, the same for every sequence, or an upper bound
+ *      of the per-sequence counts when T_len is given; s_end <= ceil(T/m).
+ *  T_len    : NULL, or a device array [B] int32 of per-sequence token counts
+ *      (a batch of sequences with ragged tails; the method page's section 3.5
+ *      keeps the tokens of a block that is not yet full in a state cache).
+ *      Sequence b then has min(T, max(0, T_len[b])) tokens: candidates at or
+ *      past it are absent, and an entry s with m s >= that count does not
+ *      exist in sequence b and its output row is not written.
  *  E        : output [B][rows][c] of out_dtype (F32, BF16 or FP8_E4M3), batch
  *      stride out_batch_stride elements; entry s goes to row s, or to row
  *      s mod out_ring when out_ring > 0 (a sliding-window ring; then at most
@@ -86,7 +93,7 @@ const char* csa_last_error(void);
  */
 int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* Z_b, int in_dtype,
                  int B, long long R, long long in_batch_stride, long long tok_base, long long T,
-                 int c, int m, int overlap, long long s_begin, long long s_end,
+                 const int* T_len, int c, int m, int overlap, long long s_begin, long long s_end,
                  const float* gamma, float eps, int rope_dim, float rope_base,
                  long long pos_stride, long long pos_offset,
                  void* E, int out_dtype, float* E_scale, long long out_batch_stride,
@@ -113,6 +120,7 @@ typedef struct csa_compress_job {
   int in_dtype;
   int B;
   long long R, in_batch_stride, tok_base, T;
+  const int* T_len;
   int c, m, overlap;
   long long s_begin, s_end;
   const float* gamma;
@@ -187,9 +195,12 @@ int csa_topk(const float* I, const int* q_pos, int B, int Tq, long long N_cap, i
  *  which holds at most 8192 key slots per query (CSA_E_UNSUPPORTED beyond).
  *  workspace: at least csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win) bytes,
  *            16-byte aligned (split partials: per (query, split, head) the
- *            output over that split's keys divided by its softmax sum, as d
- *            fp16 values saturated at +-65504, then the fp32 (max, sum)
- *            pairs); contents on entry do not matter.
+ *            output over that split's keys divided by its softmax sum and
+ *            scaled by a power of two that puts the row's largest magnitude
+ *            in [2^14, 2^15), as d fp16 values, then fp32 records (max, sum,
+ *            1 / scale, 0); the scaling is exact, so any finite input keeps
+ *            11 significant bits relative to the row's maximum and nothing
+ *            saturates); contents on entry do not matter.
  */
 size_t csa_mqa_workspace_size(int B, int Tq, int n_h, int d, long long n_keys_max);
 int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,

@@ -43,14 +43,14 @@ _lib.csa_status_str.restype = ctypes.c_char_p
 _lib.csa_status_str.argtypes = [_I]
 _lib.csa_last_error.restype = ctypes.c_char_p
 _lib.csa_compress.restype = _I
-_lib.csa_compress.argtypes = [_P, _P, _P, _P, _I, _I, _L, _L, _L, _L, _I, _I, _I, _L, _L, _P, _F, _I,
-                              _F, _L, _L, _P, _I, _P, _L, _L, _P]
+_lib.csa_compress.argtypes = [_P, _P, _P, _P, _I, _I, _L, _L, _L, _L, _P, _I, _I, _I, _L, _L, _P, _F,
+                              _I, _F, _L, _L, _P, _I, _P, _L, _L, _P]
 
 
 class _CompressJob(ctypes.Structure):
     """csa_compress_job of include/csa.h (C layout, natural alignment)."""
     _fields_ = [("C_a", _P), ("Z_a", _P), ("C_b", _P), ("Z_b", _P), ("in_dtype", _I), ("B", _I),
-                ("R", _L), ("in_batch_stride", _L), ("tok_base", _L), ("T", _L),
+                ("R", _L), ("in_batch_stride", _L), ("tok_base", _L), ("T", _L), ("T_len", _P),
                 ("c", _I), ("m", _I), ("overlap", _I), ("s_begin", _L), ("s_end", _L),
                 ("gamma", _P), ("eps", _F), ("rope_dim", _I), ("rope_base", _F),
                 ("pos_stride", _L), ("pos_offset", _L), ("E", _P), ("out_dtype", _I),
@@ -123,7 +123,7 @@ def _stream():
 def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_begin: int,
                    s_end: int, tok_base: int = 0, gamma=None, eps: float = 1e-6, rope_dim: int = 0,
                    rope_base: float = 10000.0, pos_stride: int | None = None, pos_offset: int = 0,
-                   E_scale=None, out_ring: int = 0):
+                   E_scale=None, out_ring: int = 0, T_len=None):
     """The C arguments of one compression (without the stream), in csa_compress order."""
     B, R, c = C_a.shape
     for name, t in (("Z_a", Z_a), ("C_b", C_b), ("Z_b", Z_b)):
@@ -135,8 +135,10 @@ def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_beg
         raise ValueError("E has fewer rows than the entries written")
     if E_scale is not None and tuple(E_scale.shape) != (B, E.shape[1]):
         raise ValueError("E_scale must be [B, rows]")
+    if T_len is not None and tuple(T_len.shape) != (B,):
+        raise ValueError("T_len must be [B]")
     return (_ptr(C_a, "C_a", dims=3), _ptr(Z_a, "Z_a"), _ptr(C_b, "C_b"), _ptr(Z_b, "Z_b"), _dt(C_a),
-            B, R, R * c, tok_base, T, c, m, overlap, s_begin, s_end,
+            B, R, R * c, tok_base, T, _ptr(T_len, "T_len", torch.int32), c, m, overlap, s_begin, s_end,
             _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
             m if pos_stride is None else pos_stride, pos_offset,
             _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.float32), E.shape[1] * c, out_ring)
@@ -147,7 +149,8 @@ def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
     E: [B, rows, c] float32 / bfloat16 / float8_e4m3fn, E_scale: [B, rows] fp32
     for fp8 output.  Row r of the candidates is token tok_base + r.  Keywords:
     T, m, overlap, s_begin, s_end (required); tok_base, gamma, eps, rope_dim,
-    rope_base, pos_stride (default m), pos_offset, E_scale, out_ring."""
+    rope_base, pos_stride (default m), pos_offset, E_scale, out_ring, T_len ([B] int32
+    per-sequence token counts, each <= T)."""
     _check(_lib.csa_compress(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw), _stream()))
 
 

@@ -12,7 +12,9 @@
 // an online softmax (running max, running sum, running weighted sum), and the
 // G partial results are merged in LDS.  This keeps a 128-candidate HCA block
 // from serialising 128 dependent loads per thread.  Reads are coalesced along
-// the channel axis; HBM traffic is one pass over C and Z.
+// the channel axis; HBM traffic is one pass over C and Z.  With per-sequence
+// token counts T_len, an entry whose block starts at or past T_len[b] does not
+// exist in sequence b and its row is left as it was.
 //
 // One launch runs a batch of independent jobs (blockIdx.z): a decode step's
 // window row, KV entry and indexer key are each a few microseconds of memory
@@ -36,6 +38,7 @@ static constexpr int COMP_MAX_JOBS = 8;
 struct CompressJob {
   const void *Ca, *Za, *Cb, *Zb;
   const float* gamma;
+  const int* T_len;   // per-sequence token counts (<= T), or NULL
   void* E;
   float* E_scale;
   long long in_bs, tok_base, T, s_begin, n_entries, pos_stride, pos_offset, out_bs, out_ring;
@@ -47,6 +50,11 @@ struct CompressBatch {
   CompressJob job[COMP_MAX_JOBS];
 };
 
+// tokens present in sequence b: T, or T_len[b] clamped to [0, T]
+__device__ __forceinline__ long long seq_tokens(const CompressJob& J, int b) {
+  return J.T_len ? min(J.T, max(0LL, (long long)J.T_len[b])) : J.T;
+}
+
 template <int IDT, int ODT>
 __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem) {
   const void* __restrict__ Ca = J.Ca;
@@ -56,7 +64,7 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
   const float* __restrict__ gamma = J.gamma;
   void* __restrict__ E = J.E;
   float* __restrict__ E_scale = J.E_scale;
-  const long long in_bs = J.in_bs, tok_base = J.tok_base, T = J.T, s_begin = J.s_begin;
+  const long long in_bs = J.in_bs, tok_base = J.tok_base, s_begin = J.s_begin;
   const long long pos_stride = J.pos_stride, pos_offset = J.pos_offset, out_bs = J.out_bs;
   const long long out_ring = J.out_ring;
   const RopeRatio rope = J.rope;
@@ -70,6 +78,8 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
 
   const long long s = s_begin + blockIdx.x;
   const int b = blockIdx.y;
+  const long long T = seq_tokens(J, b);
+  if ((long long)m * s >= T) return;   // no such entry in this sequence (whole workgroup)
   const long long a_lo = (long long)m * s;
   const long long a_hi = min((long long)m * (s + 1), T);
   long long b_lo = 0, b_hi = 0;
@@ -285,11 +295,13 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
   constexpr int VEC = IDT == DT_F32 ? 4 : 8;   // channels per 16-byte piece
   constexpr int ESZ = IDT == DT_F32 ? 4 : 2;
   const int c = J.c, m = J.m;
-  const long long a_lo = (long long)m * s, a_hi = min((long long)m * (s + 1), J.T);
+  const long long T = seq_tokens(J, b);
+  if ((long long)m * s >= T) return;   // no such entry in this sequence (whole wave)
+  const long long a_lo = (long long)m * s, a_hi = min((long long)m * (s + 1), T);
   long long b_lo = 0, b_hi = 0;
   if (J.overlap) {
     b_lo = max((long long)m * (s - 1), 0LL);
-    b_hi = min((long long)m * s, J.T);
+    b_hi = min((long long)m * s, T);
   }
   const int na = (int)max(a_hi - a_lo, 0LL), nb = (int)max(b_hi - b_lo, 0LL);
   const int ncand = na + nb;   // <= MAXC (host), >= 1 (an entry < ceil(T / m) has a token)
@@ -448,7 +460,7 @@ static size_t compress_lds_bytes(int G, int c) {
 static CompressJob make_job(const CompressArgs& x, int G) {
   CompressJob J{};
   J.Ca = x.C_a; J.Za = x.Z_a; J.Cb = x.C_b; J.Zb = x.Z_b;
-  J.gamma = x.gamma; J.E = x.E; J.E_scale = x.E_scale;
+  J.gamma = x.gamma; J.T_len = x.T_len; J.E = x.E; J.E_scale = x.E_scale;
   J.in_bs = x.in_bs; J.tok_base = x.tok_base; J.T = x.T; J.s_begin = x.s_begin;
   J.n_entries = x.s_end - x.s_begin;
   J.pos_stride = x.pos_stride; J.pos_offset = x.pos_offset;

@@ -7,6 +7,7 @@
 #include "../../include/csa.h"
 #include "csa_internal.h"
 
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -84,7 +85,7 @@ static int check_compress(const csa_compress_job& j, const char* who) {
 
 static csa::CompressArgs compress_args(const csa_compress_job& j) {
   return csa::CompressArgs{j.C_a, j.Z_a, j.C_b, j.Z_b, j.in_dtype, j.B, j.R, j.in_batch_stride,
-                           j.tok_base, j.T, j.c, j.m, j.overlap, j.s_begin, j.s_end, j.gamma, j.eps,
+                           j.tok_base, j.T, j.T_len, j.c, j.m, j.overlap, j.s_begin, j.s_end, j.gamma, j.eps,
                            j.rope_dim, j.rope_base, j.pos_stride, j.pos_offset, j.E, j.out_dtype,
                            j.E_scale, j.out_batch_stride, j.out_ring};
 }
@@ -110,12 +111,12 @@ const char* csa_last_error(void) { return g_err; }
 
 int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* Z_b, int in_dtype,
                  int B, long long R, long long in_batch_stride, long long tok_base, long long T,
-                 int c, int m, int overlap, long long s_begin, long long s_end,
+                 const int* T_len, int c, int m, int overlap, long long s_begin, long long s_end,
                  const float* gamma, float eps, int rope_dim, float rope_base,
                  long long pos_stride, long long pos_offset,
                  void* E, int out_dtype, float* E_scale, long long out_batch_stride,
                  long long out_ring, void* stream) {
-  const csa_compress_job j{C_a, Z_a, C_b, Z_b, in_dtype, B, R, in_batch_stride, tok_base, T, c, m,
+  const csa_compress_job j{C_a, Z_a, C_b, Z_b, in_dtype, B, R, in_batch_stride, tok_base, T, T_len, c, m,
                            overlap, s_begin, s_end, gamma, eps, rope_dim, rope_base, pos_stride,
                            pos_offset, E, out_dtype, E_scale, out_batch_stride, out_ring};
   const int st = check_compress(j, "csa_compress");
@@ -255,3 +256,4 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
 }
 
 }  // extern "C"
+

@@ -13,6 +13,7 @@ struct CompressArgs {
   int in_dtype;
   int B;
   long long R, in_bs, tok_base, T;
+  const int* T_len;
   int c, m, overlap;
   long long s_begin, s_end;
   const float* gamma;

@@ -66,12 +66,14 @@ __device__ __forceinline__ long long slot_row(long long slot, const QuerySlots& 
 }
 
 // Split partials in the workspace.  The output of (query row, split, head)
-// divided by its softmax sum is the fp16 row part_o(ws)[((row * n_split + sp) *
-// n_h + h) * D] (16-byte aligned rows); the float (max, sum) pairs follow all
-// rows, pair u = (row * n_split + sp) * n_h + h at part_ml(...)[2 u].  n_units =
-// (query rows) * n_split.  Divided by the sum, a row is a weighted mean of the
-// value rows, so fp16 holds it with 11 significant bits (half the bytes of fp32);
-// values beyond the fp16 range saturate at +-65504 (part_h).
+// divided by its softmax sum is a weighted mean of the value rows; it is stored
+// times a power of two chosen from the row's own maximum magnitude (the
+// maximum lands in [2^14, 2^15)), as the fp16 row part_o(ws)[((row * n_split +
+// sp) * n_h + h) * D] (16-byte aligned rows).  The scaling is exact, so the row
+// keeps 11 significant bits relative to its maximum whatever the magnitude of
+// the values, and no finite input can saturate fp16.  The float records (max,
+// sum, 1 / scale, 0) follow all rows, record u = (row * n_split + sp) * n_h + h
+// at part_ml(...)[4 u].  n_units = (query rows) * n_split.
 __device__ __forceinline__ _Float16* part_o(float* ws) { return (_Float16*)ws; }
 __device__ __forceinline__ const _Float16* part_o(const float* ws) { return (const _Float16*)ws; }
 __device__ __forceinline__ float* part_ml(float* ws, long long n_units, int n_h, int D) {
@@ -81,7 +83,20 @@ __device__ __forceinline__ const float* part_ml(const float* ws, long long n_uni
   return (const float*)(part_o(ws) + (size_t)n_units * (size_t)n_h * (size_t)D);
 }
 __device__ __forceinline__ _Float16 part_h(float x) {
-  return (_Float16)fminf(fmaxf(x, -65504.f), 65504.f);
+  return (_Float16)fminf(fmaxf(x, -65504.f), 65504.f);   // a no-op once rows are scaled
+}
+// the power of two 2^(15 - k) for a row maximum amax = f 2^k (f in [0.5, 1)),
+// exponent clamped to the normal range; 1 for a zero row
+__device__ __forceinline__ float part_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const int k = (int)((__float_as_uint(amax) >> 23) & 0xff) - 126;
+  const int e = min(max(15 - k + 127, 1), 254);
+  return __uint_as_float((uint32_t)e << 23);
+}
+// 1 / part_scale (also a power of two, exact)
+__device__ __forceinline__ float part_unscale(float sc) {
+  const int e = (int)((__float_as_uint(sc) >> 23) & 0xff);
+  return __uint_as_float((uint32_t)min(max(254 - e, 1), 254) << 23);
 }
 // 1 / l, or 0 for a split without visible keys (its O is 0)
 __device__ __forceinline__ float part_inv(float l) { return l > 0.f ? 1.f / l : 0.f; }
@@ -447,23 +462,34 @@ __global__ __launch_bounds__(256) void mqa_mfma_kernel(
       }
     }
   } else {
-    // ---- partial state: O / l_run, then m_run, l_run
+    // ---- partial state: O / l_run scaled by a power of two, then the record
     const size_t pbase = (row * n_split + sp) * (size_t)n_h;
     float* ml = part_ml(ws, n_units, n_h, D);
     _Float16* wo = part_o(ws);
     const float li = part_inv(l_run);
-    float lr[4];
+    float lr[4], sc[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lr[r] = __shfl(li, 4 * g + r, 64);
+    for (int r = 0; r < 4; ++r) {
+      lr[r] = __shfl(li, 4 * g + r, 64);
+      float a = 0.f;   // row maximum of head 4 g + r (its 16 lanes hold every dim)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) a = fmaxf(a, fabsf(O[nt][r] * lr[r]));
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+      sc[r] = part_scale(a);
+      lr[r] *= sc[r];
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         wo[(pbase + h0 + 4 * g + r) * D + 16 * nt + j] = part_h(O[nt][r] * lr[r]);
-    if (g == 0) {
-      ml[2 * (pbase + hq)] = m_run;
-      ml[2 * (pbase + hq) + 1] = l_run;
-    }
+    // lane (0, j) writes the record of head h0 + j, whose scale lane group j / 4 holds
+    const float s0 = __shfl(sc[0], 16 * (j >> 2), 64), s1 = __shfl(sc[1], 16 * (j >> 2), 64);
+    const float s2 = __shfl(sc[2], 16 * (j >> 2), 64), s3 = __shfl(sc[3], 16 * (j >> 2), 64);
+    const float sj = (j & 3) == 0 ? s0 : (j & 3) == 1 ? s1 : (j & 3) == 2 ? s2 : s3;
+    if (g == 0)
+      *(f32x4_t*)(ml + 4 * (pbase + hq)) = f32x4_t{m_run, l_run, part_unscale(sj), 0.f};
   }
 }
 
@@ -490,6 +516,7 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
   __shared__ float rope_cs[D];
   __shared__ u32x4_t pbuf[4][NKK][64];   // P fragments: [head tile][32-key step][lane]
   __shared__ float fstat[64], mstat[64], lstat[64];
+  __shared__ float amx[4][64];           // split partials: per-wave row maxima of each head
 
   const int n_hg = (n_h + 63) / 64;
   const long long L = blockIdx.x;
@@ -704,23 +731,44 @@ __global__ __launch_bounds__(256) void mqa_group_kernel(
       }
     }
   } else {
+    // O / l scaled by a power of two from the row maximum; a head's row spans the
+    // four waves' dims, so their maxima meet in LDS
     const size_t pbase = (row * n_split + sp) * (size_t)n_h + hbase;
     _Float16* wo = part_o(ws);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float li = part_inv(lstat[16 * mt + 4 * g + r]);
+        float a = 0.f;
+        if (mt < ntiles) {
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) a = fmaxf(a, fabsf(O[mt][nt][r] * li));
+        }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+        if (j == 0) amx[wave][16 * mt + 4 * g + r] = a;
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       if (mt >= ntiles) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float li = part_inv(lstat[16 * mt + 4 * g + r]);
+        const int hl = 16 * mt + 4 * g + r;
+        const float sc = part_scale(fmaxf(fmaxf(amx[0][hl], amx[1][hl]), fmaxf(amx[2][hl], amx[3][hl])));
+        const float li = part_inv(lstat[hl]) * sc;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-          wo[(pbase + 16 * mt + 4 * g + r) * D + dbase + 16 * nt + j] = part_h(O[mt][nt][r] * li);
+          wo[(pbase + hl) * D + dbase + 16 * nt + j] = part_h(O[mt][nt][r] * li);
       }
     }
     if (threadIdx.x < 16 * ntiles) {
+      const int hl = threadIdx.x;
+      const float sc = part_scale(fmaxf(fmaxf(amx[0][hl], amx[1][hl]), fmaxf(amx[2][hl], amx[3][hl])));
       float* ml = part_ml(ws, n_units, n_h, D);
-      ml[2 * (pbase + threadIdx.x)] = mstat[threadIdx.x];
-      ml[2 * (pbase + threadIdx.x) + 1] = lstat[threadIdx.x];
+      *(f32x4_t*)(ml + 4 * (pbase + hl)) = f32x4_t{mstat[hl], lstat[hl], part_unscale(sc), 0.f};
     }
   }
 }
@@ -1275,6 +1323,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     static_assert(16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
     lds_sync<0>();   // every wave is done with the chunk ring
     float* stg = (float*)kv + wave * 16 * CRS;
+    float pscale[HTW];   // split partials: scale of head 16 ht + j
     // FIN: compile-time copy of fin (one store loop each)
     auto write_out = [&](auto fin_c) {
       constexpr bool FIN = decltype(fin_c)::value;
@@ -1285,6 +1334,26 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
         float fr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) fr[r] = __shfl(fac[ht], 4 * g + r, 64);
+        if constexpr (!FIN) {
+          // partial rows: scaled by a power of two from the row maximum (head 4 g + r:
+          // the 16 lanes of group g hold all its dims); lane (0, j) keeps the scale of
+          // head 16 ht + j for the record
+          float sc[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int nt = 0; nt < D / 16; ++nt) a = fmaxf(a, fabsf(O[ht][nt][r] * fr[r]));
+#pragma unroll
+            for (int x = 1; x < 16; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+            sc[r] = part_scale(a);
+            fr[r] *= sc[r];
+          }
+          const int src = 16 * (j >> 2);
+          const float s0 = __shfl(sc[0], src, 64), s1 = __shfl(sc[1], src, 64);
+          const float s2 = __shfl(sc[2], src, 64), s3 = __shfl(sc[3], src, 64);
+          pscale[ht] = (j & 3) == 0 ? s0 : (j & 3) == 1 ? s1 : (j & 3) == 2 ? s2 : s3;
+        }
 #pragma unroll
         for (int cb = 0; cb < D / CW; ++cb) {
 #pragma unroll
@@ -1336,10 +1405,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       if (g == 0) {
         float* ml = part_ml(ws, n_units, n_h, D);
 #pragma unroll
-        for (int ht = 0; ht < HTW; ++ht) {
-          ml[2 * (pbs + 16 * ht + j)] = ref[ht];
-          ml[2 * (pbs + 16 * ht + j) + 1] = lsum[ht];
-        }
+        for (int ht = 0; ht < HTW; ++ht)
+          *(f32x4_t*)(ml + 4 * (pbs + 16 * ht + j)) = f32x4_t{ref[ht], lsum[ht], part_unscale(pscale[ht]), 0.f};
       }
     }
   }
@@ -1357,8 +1424,8 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const float sig = sink ? sink[h] : -INFINITY;
   const _Float16* base = part_o(ws) + (row * n_split * (size_t)n_h + h) * D;   // O / l of split 0
   const size_t sstride = (size_t)n_h * D;
-  const float* mlb = part_ml(ws, (long long)gridDim.z * Tq * n_split, n_h, D) + 2 * (row * n_split * (size_t)n_h + h);
-  const size_t mstride = 2 * (size_t)n_h;
+  const float* mlb = part_ml(ws, (long long)gridDim.z * Tq * n_split, n_h, D) + 4 * (row * n_split * (size_t)n_h + h);
+  const size_t mstride = 4 * (size_t)n_h;
   const int rbeg = D - rope_dim;
   for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
     const int d0 = 2 * u;
@@ -1372,8 +1439,8 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
       // l of each wave fetches the (max, sum) of split s0 + l % CB with one
       // vector load in the same batch as the outputs; readlane hands them to
       // every lane.
-      float ms[CB], ls[CB], a0[CB], a1[CB];
-      const float2 mlv = *(const float2*)(mlb + min(s0 + (int)(threadIdx.x % CB), n_split - 1) * mstride);
+      float ms[CB], ls[CB], us[CB], a0[CB], a1[CB];
+      const f32x4_t mlv = *(const f32x4_t*)(mlb + min(s0 + (int)(threadIdx.x % CB), n_split - 1) * mstride);
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
         const int sc = min(s0 + s, n_split - 1);
@@ -1384,8 +1451,9 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
       }
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
-        ms[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.x), s));
-        ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv.y), s));
+        ms[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[0]), s));
+        ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[1]), s));
+        us[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[2]), s));
       }
       const int nb = min(CB, n_split - s0);
       float bm = M;
@@ -1399,14 +1467,14 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
         o1 *= r;
         M = bm;
       }
-      // split s weighs l_s exp(m_s - M) (its rows hold O_s / l_s)
+      // split s weighs l_s exp(m_s - M) (its rows hold O_s / l_s times 1 / u_s)
 #pragma unroll
       for (int s = 0; s < CB; ++s) {
         if (s < nb) {
           const float f = (ms[s] == -INFINITY) ? 0.f : ls[s] * __expf(ms[s] - M);
           Z += f;
-          o0 += a0[s] * f;
-          o1 += a1[s] * f;
+          o0 += a0[s] * (f * us[s]);
+          o1 += a1[s] * (f * us[s]);
         }
       }
     }
@@ -1482,8 +1550,8 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
   int kps, n_split;
   mqa_split(Tq, n_h, d, n_slots_max, &kps, &n_split);
   if (n_split == 1) return 0;
-  // per (query row, split, head): d fp16 outputs + a float (max, sum) pair
-  return (size_t)B * Tq * n_split * n_h * (size_t)(2 * d + 8);
+  // per (query row, split, head): d fp16 outputs + a float record (max, sum, 1 / scale, 0)
+  return (size_t)B * Tq * n_split * n_h * (size_t)(2 * d + 16);
 }
 
 template <int D, bool DENSE, bool MULTI>

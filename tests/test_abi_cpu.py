@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
     for s in range(7):
         assert lib.csa_status_str(s)
     assert lib.csa_status_str(99) == b"unknown status"
@@ -48,7 +48,7 @@ FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
 def test_compress_validation(lib):
     args = dict(C_a=FAKE, Z_a=FAKE, C_b=FAKE, Z_b=FAKE, in_dtype=1, B=1, R=8, ibs=8 * 64, tok_base=0,
-                T=8, c=64, m=4, overlap=1, s_begin=0, s_end=2, gamma=None, eps=1e-6, rope_dim=0,
+                T=8, T_len=None, c=64, m=4, overlap=1, s_begin=0, s_end=2, gamma=None, eps=1e-6, rope_dim=0,
                 rope_base=1e4, pos_stride=4, pos_offset=0, E=FAKE, out_dtype=1, E_scale=None,
                 obs=2 * 64, out_ring=0, stream=None)
 
@@ -72,6 +72,9 @@ def test_compress_validation(lib):
     assert b"csa_compress" in lib.csa_last_error()
     assert call(s_begin=1, s_end=1) == CSA_OK                 # empty range: nothing to do
     assert lib.csa_last_error() == b""
+    # per-sequence token counts live on the device: the host checks the bound T only
+    assert call(T_len=FAKE, s_end=3) == CSA_E_SHAPE
+    assert call(T_len=FAKE, s_begin=2, s_end=2) == CSA_OK
 
 
 def test_compress_batch_validation(lib):
@@ -157,16 +160,17 @@ def test_mqa_validation(lib):
     assert sparse(k=0) == CSA_E_SHAPE
     # a split decode query needs workspace
     # 1152 slots in ranges of 192: 6 split partials per (query, head), each d fp16
-    # outputs and a float (max, sum) pair; above 1536 slots the ranges hold 160
-    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 52 * 64 * (512 * 2 + 8)
-    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * (512 * 2 + 8)
+    # outputs and a float record (max, sum, 1 / scale, 0); above 1536 slots the
+    # ranges hold 160
+    assert lib.csa_mqa_workspace_size(4, 1, 64, 512, 8192 + 128) == 4 * 52 * 64 * (512 * 2 + 16)
+    assert lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) == 16 * 6 * 128 * (512 * 2 + 16)
     assert sparse(k=1024, nh=128, d=512, B=16) == CSA_E_WORKSPACE
     need = lib.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128)
     assert sparse(k=1024, nh=128, d=512, B=16, ws=FAKE + 4, wsb=need + 16) == CSA_E_WORKSPACE
     assert b"16-byte aligned" in lib.csa_last_error()
     # prefill (16 or more queries per sequence): one range of up to 2,048 slots per query
     assert lib.csa_mqa_workspace_size(1, 16384, 128, 512, 1024 + 128) == 0
-    assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * (128 * 2 + 8)
+    assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * (128 * 2 + 16)
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED
 

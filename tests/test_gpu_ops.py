@@ -86,6 +86,39 @@ def test_compress_parity(csa, case):
         assert torch.isnan(E[:, :s0]).all()
 
 
+@pytest.mark.parametrize("B,T_len,R,c,m,ov,dt", [
+    (3, [203, 150, 97], 203, 512, 4, 1, "bf16"),            # workgroup kernel (few entries)
+    (4, [2050, 1999, 1024, 1], 2050, 128, 4, 1, "bf16"),    # wave kernel (256+ entries)
+    (3, [700, 513, 128], 700, 256, 128, 0, "bf16"),         # HCA blocks, partial tails
+    (2, [0, 37], 37, 64, 4, 1, "f32"),                      # an empty sequence
+])
+def test_compress_ragged_T_len(csa, B, T_len, R, c, m, ov, dt):
+    """Per-sequence token counts: sequence b is compressed exactly as a call with
+    T = T_len[b]; rows of entries that do not exist in it are left untouched."""
+    g = Gen(170 + sum(T_len) % 97, DEV)
+    T = max(T_len)
+    n = O.num_entries(T, m)
+    Ca, Za = g.normal(1, (B, R, c), dt), g.normal(2, (B, R, c), dt)
+    Cb, Zb = (g.normal(3, (B, R, c), dt), g.normal(4, (B, R, c), dt)) if ov else (None, None)
+    gamma = _gamma(g, 5, c)
+    E = torch.full((B, n, c), float("nan"), dtype=TDT[dt], device=DEV)
+    Tl = torch.tensor(T_len, dtype=torch.int32, device=DEV)
+    csa.csa_compress(Ca, Za, Cb, Zb, E, T=T, T_len=Tl, m=m, overlap=ov, s_begin=0, s_end=n, gamma=gamma,
+                     rope_dim=64 if c >= 128 else 16)
+    torch.cuda.synchronize()
+    got = to_f64(E)
+    tol = TOL_F32 if dt == "f32" else TOL_BF16
+    for b in range(B):
+        nb = O.num_entries(T_len[b], m) if T_len[b] > 0 else 0
+        assert np.isnan(got[b, nb:]).all(), (b, "rows past the sequence's entries are untouched")
+        if nb == 0:
+            continue
+        ref = O.compress(to_f64(Ca[b]), to_f64(Za[b]), None if Cb is None else to_f64(Cb[b]),
+                         None if Zb is None else to_f64(Zb[b]), m=m, overlap=ov, T=T_len[b], s_begin=0,
+                         s_end=nb, gamma=to_f64(gamma), eps=1e-6, rope_dim=64 if c >= 128 else 16)
+        assert row_rel_err(got[b, :nb], ref) <= tol, b
+
+
 def test_compress_fp8_output(csa):
     """Indexer keys stored as e4m3fn with a per-row absmax scale: the code must be
     a correct RNE rounding of the oracle value (up to midpoint ties of the
@@ -361,24 +394,29 @@ def test_mqa_empty_key_set_is_zero(csa):
         assert torch.all(out == 0), dt
 
 
-def test_mqa_split_partials_large_values(csa):
-    """A split decode query whose entries reach about +-4.5e4: the split partials
-    (each split's output divided by its softmax sum, kept as fp16) stay inside the
-    fp16 range, and the merged rows match the oracle to the bf16 tolerance.  Large
-    entries also make the softmax close to one-hot, the case where a partial row
-    is as large as the largest value row."""
-    B, Tq, n_h, d, N, k, m, n_win, rope = 2, 1, 64, 512, 900, 512, 4, 128, 64
+@pytest.mark.parametrize("mag", [1e7, 1e-7])
+@pytest.mark.parametrize("n_h,d,k", [(64, 512, 512), (16, 128, 600)])
+def test_mqa_split_partials_any_magnitude(csa, mag, n_h, d, k):
+    """Split decode queries whose entries reach about 4.5 mag: far beyond the fp16
+    range (1e7) or deep in its subnormals (1e-7).  Each split partial row is
+    scaled by a power of two from its own maximum before it is stored as fp16, so
+    the merged rows match the oracle to the bf16 tolerance at either magnitude
+    (the streaming decode kernel at d = 512, the group kernel at d = 128).  The
+    softmax scale is divided by the magnitude at 1e7, so the logits stay of
+    order one: logits of order 1e6 carry fp32 rounding errors of order 10 in
+    any implementation and the near-one-hot softmax is then ill-conditioned."""
+    B, Tq, N, m, n_win, rope = 2, 1, 900, 4, 128, 64
     g = Gen(490, DEV)
     q = g.normal(1, (B, Tq, n_h, d), "bf16")
-    E = (g.normal(2, (B, N, d), "f32") * 1e4).to(torch.bfloat16)
-    W = (g.normal(3, (B, n_win, d), "f32") * 1e4).to(torch.bfloat16)
+    E = (g.normal(2, (B, N, d), "f32") * mag).to(torch.bfloat16)
+    W = (g.normal(3, (B, n_win, d), "f32") * mag).to(torch.bfloat16)
     sink = g.normal(4, (n_h,), "f32", per_slot=False)
     pos = _positions("all", B, Tq, N, m, g)
     idx = ((g.uniform(6, (B, Tq, k)) * N).to(torch.int32)).contiguous()
     ws = torch.empty(csa.csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win), dtype=torch.uint8, device=DEV)
     assert ws.numel() > 0   # the query is split
     out = torch.full_like(q, float("nan"))
-    scale = 1.0 / math.sqrt(d)
+    scale = 1.0 / math.sqrt(d) / (mag if mag > 1 else 1.0)
     csa.csa_sparse_mqa(q, E, idx, W, pos, out, n_win=n_win, sink=sink, rope_dim=rope, scale=scale,
                        workspace=ws)
     torch.cuda.synchronize()
@@ -388,7 +426,10 @@ def test_mqa_split_partials_large_values(csa):
         ref = O.sparse_mqa(to_f64(q[b]), to_f64(E[b]), to_f64(idx[b]), to_f64(W[b]), q_pos=to_f64(pos[b]),
                            n_win=n_win, W_cap=n_win, gamma_q=None, eps=1e-6, sink=to_f64(sink),
                            rope_dim=rope, scale=scale)
-        assert np.abs(ref).max() > 3e4
+        if mag > 1:
+            assert np.abs(ref).max() > 65504.0          # beyond the fp16 range
+        else:
+            assert 0 < np.abs(ref).max() < 2.0 ** -14   # below the smallest normal fp16
         err = row_rel_err(got[b], ref)
         assert err <= TOL_BF16, (b, err)
 

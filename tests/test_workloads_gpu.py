@@ -261,3 +261,45 @@ def test_decode_bitwise_repeatable_and_batch_invariant(lib):
     assert torch.equal(out1.view(torch.uint8), run.out[sl].view(torch.uint8))
     del run
     _free()
+
+
+# ---------------------------------------------------------------------------
+# graph replay (the benchmark replays captured steps)
+# ---------------------------------------------------------------------------
+def test_graph_replay_equals_eager_step(lib):
+    """A decode step captured as a HIP graph and replayed three times, with eager
+    work and synchronisations between the replays, writes the eager step's bytes
+    every time (CSA Flash-like decode and HCA decode)."""
+    from long_context_attention_02_amd.pipeline import CSADecode, HCADecode
+    from synth.workloads import CSA_DECODE_FLASH, HCA_DECODE
+
+    def as_bytes(t):
+        return t.view(torch.uint8) if t.dtype == torch.bfloat16 else t
+
+    for cls, wl, outs in ((CSADecode, CSA_DECODE_FLASH, ("I", "idx", "out", "E", "KI", "W")),
+                          (HCADecode, HCA_DECODE, ("out", "E", "W"))):
+        run = cls(wl, "cuda", keep_raw=False)
+        run.step()
+        torch.cuda.synchronize()
+        ref = {k: as_bytes(getattr(run, k)).clone() for k in outs}
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            run.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run.step()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for k in outs:                       # eager work between replays: scribble the outputs
+                if k in ("I", "idx", "out"):
+                    getattr(run, k).zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for k in outs:
+                assert torch.equal(as_bytes(getattr(run, k)), ref[k]), (wl.name, rep, k)
+        del g, run
+        _free()
