@@ -11,9 +11,14 @@ Written from the format definitions, not from any library routine:
   S.1111.111 (0x7F / 0xFF) is NaN; there are no infinities; the largest
   finite magnitude is 448 = S.1111.110.
 
+* OCP Microscaling (MX) formats, v1.0: FP4 E2M1 elements (1 sign, 2 exponent,
+  1 mantissa bit, bias 1; e >= 1: (-1)^s 2^(e-1) (1 + m/2); e = 0: (-1)^s m/2;
+  no infinities or NaN; largest magnitude 6) and the E8M0 block scale
+  (an unsigned exponent: 2^(e - 127); 0xFF is NaN).
+
 The DeepSeek-V4 abstract page (section 3.3) stores KV entries partly in BF16
-and partly in FP8; the 1M-context decode workload stores indexer keys as e4m3
-with a per-row scale.
+and partly in FP8, and section 3.6 runs the indexer's QK path in FP4; the
+1M-context decode workload stores indexer keys as e4m3 with a per-row scale.
 """
 from __future__ import annotations
 
@@ -82,3 +87,81 @@ def e4m3_code(v) -> np.ndarray:
             hits = [0x80 if np.signbit(val) else 0x00]
         flat_o[n] = hits[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# OCP MX: FP4 E2M1 elements with an E8M0 scale per block of 32
+# ---------------------------------------------------------------------------
+E2M1_MAX = 6.0
+E2M1_EMAX = 2          # exponent of the largest power of two in E2M1 (4 = 2^2)
+MX_BLOCK = 32
+
+
+def e2m1_to_f64(u4) -> np.ndarray:
+    """Exact value of FP4 E2M1 codes (0..15), by the closed form."""
+    u = np.asarray(u4).astype(np.int64)
+    s = (u >> 3) & 1
+    e = (u >> 1) & 3
+    m = u & 1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, e - 1))
+    return np.where(s == 1, -mag, mag)
+
+
+def e8m0_to_f64(u8) -> np.ndarray:
+    """Exact value of E8M0 scale codes: 2^(code - 127); 255 is NaN."""
+    u = np.asarray(u8).astype(np.int64)
+    return np.where(u == 255, np.nan, np.ldexp(1.0, u - 127))
+
+
+def f64_to_e2m1_value(x) -> np.ndarray:
+    """RNE rounding to the E2M1 grid with saturation to +-6 (as fp64).  The
+    grid has 2 significant bits above 1 and a spacing of 0.5 below it."""
+    r = _round_sig(x, 2, 0)
+    return np.clip(r, -E2M1_MAX, E2M1_MAX)
+
+
+def e2m1_code(v) -> np.ndarray:
+    """Code of an E2M1-representable value (inverse of ``e2m1_to_f64``; -0.0 -> 8)."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.abs(v)
+    table = e2m1_to_f64(np.arange(8))
+    hits = mag[..., None] == table
+    if not np.all(hits.any(axis=-1)):
+        raise ValueError("not an E2M1 value")
+    return (np.argmax(hits, axis=-1) | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def mx_quantize_fp4(x) -> tuple[np.ndarray, np.ndarray]:
+    """OCP MX conversion of rows to MXFP4, blocks of 32 along the last axis.
+
+    Per block: the shared exponent is floor(log2(max |x|)) - 2 (E2M1's largest
+    power of two is 2^2), clamped to E8M0's [-127, 127]; an all-zero block
+    takes -127.  Each element is x / 2^shared rounded to E2M1 (RNE, saturated
+    to +-6).  The decisions are taken on the given values, which callers
+    round to the precision the values are stored or computed in first.
+    Returns (element codes uint8 [..., n], scale codes uint8 [..., n / 32]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if n % MX_BLOCK:
+        raise ValueError("the last axis must be a multiple of 32")
+    xb = x.reshape(*x.shape[:-1], n // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(xb), axis=-1)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.floor(np.log2(amax[nz])).astype(np.int64)
+    # log2 may be off by one right at powers of two: correct with exact checks
+    e = np.where(nz & (np.ldexp(1.0, e) > amax), e - 1, e)
+    e = np.where(nz & (np.ldexp(1.0, e + 1) <= amax), e + 1, e)
+    shared = np.where(nz, np.clip(e - E2M1_EMAX, -127, 127), -127)
+    y = xb / np.ldexp(1.0, shared)[..., None]
+    codes = e2m1_code(f64_to_e2m1_value(y)).reshape(x.shape)
+    return codes, (shared + 127).astype(np.uint8)
+
+
+def mx_fp4_to_f64(codes, scales) -> np.ndarray:
+    """Values of MXFP4 rows: element value times its block's scale."""
+    v = e2m1_to_f64(codes)
+    n = v.shape[-1]
+    sc = e8m0_to_f64(scales)
+    return (v.reshape(*v.shape[:-1], n // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(v.shape)

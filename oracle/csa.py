@@ -30,7 +30,7 @@ import math
 
 import numpy as np
 
-from .codecs import f64_to_e4m3_value, e4m3_code
+from .codecs import e4m3_code, f64_to_e4m3_value, mx_fp4_to_f64, mx_quantize_fp4
 
 NEG_INF = -np.inf
 
@@ -201,6 +201,30 @@ def index_score(qI, w, K, q_pos, *, m: int, N_cap: int | None = None) -> np.ndar
         dots = qI[t] @ K[:n].T                     # [H, n]
         out[t, :n] = w[t] @ np.maximum(dots, 0.0)  # sum over heads
     return out
+
+
+def quantize_rows_mxfp4(E) -> tuple[np.ndarray, np.ndarray]:
+    """Store rows in MXFP4 (OCP MX: E2M1 elements, one E8M0 scale per 32
+    channels).  The decisions are taken on the fp32 value, the precision the
+    pooled keys are computed in.  Returns (element codes uint8, scale codes
+    uint8 [..., c / 32])."""
+    x32 = np.asarray(E, dtype=np.float64).astype(np.float32).astype(np.float64)
+    return mx_quantize_fp4(x32)
+
+
+def index_score_mxfp4(qI, w, K_codes, K_scales, q_pos, *, m: int) -> np.ndarray:
+    """The indexer score with the QK path in FP4 [V4-abs §3.6: the indexer's
+    query-key path runs in FP4; §3.3: the score formula].
+
+    Reading: both operands of every q . K product are MXFP4 -- the keys as
+    stored (codes and block scales) and the query quantised from its stored
+    (bf16) value by the OCP MX conversion, per head, blocks of 32 dims; the
+    head weights stay fp32.  The score is then the plain formula on those
+    values, I[t, s] = sum_h w[t,h] ReLU(q~[t,h] . K~[s]), exact in fp64.
+    """
+    qI = np.asarray(qI, dtype=np.float64)
+    qc, qs = mx_quantize_fp4(qI)
+    return index_score(mx_fp4_to_f64(qc, qs), w, mx_fp4_to_f64(K_codes, K_scales), q_pos, m=m)
 
 
 # ---------------------------------------------------------------------------

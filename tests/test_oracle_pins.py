@@ -723,3 +723,126 @@ def test_hca_decode_pin_catches_planted_mistakes(old, new):
     bad = _mutant_steps(old, new)
     with pytest.raises((AssertionError, ValueError)):
         _hca_decode_pin(bad)
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP MX v1.0: FP4 E2M1 elements, E8M0 scale per 32) for the FP4 indexer
+# ---------------------------------------------------------------------------
+def test_e2m1_codes_are_the_spec_table():
+    """The 16 E2M1 codes: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0-7), the
+    sign in bit 3 (OCP MX v1.0, FP4 E2M1 element format)."""
+    table = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = oc.e2m1_to_f64(np.arange(16))
+    assert list(got[:8]) == table
+    assert list(-got[8:]) == table and np.all(np.signbit(got[8:]))
+    assert [oc.e2m1_code(v) for v in table] == list(range(8))
+    assert oc.e2m1_code(-0.0) == 8 and oc.e2m1_code(-6.0) == 15
+    assert oc.e8m0_to_f64(127) == 1.0 and oc.e8m0_to_f64(0) == 2.0 ** -127
+    assert oc.e8m0_to_f64(254) == 2.0 ** 127 and np.isnan(oc.e8m0_to_f64(255))
+
+
+def _e2m1_brute(y: float) -> float:
+    """Nearest E2M1 value by exhaustive search; ties to the even code (mantissa
+    bit 0); beyond +-6 saturates."""
+    mags = oc.e2m1_to_f64(np.arange(8))
+    a = min(abs(y), 6.0)
+    d = np.abs(mags - a)
+    best = np.flatnonzero(d == d.min())
+    code = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+    return float(np.copysign(mags[code], y))
+
+
+def test_e2m1_rne_matches_brute_force():
+    rng = np.random.default_rng(31)
+    mags = oc.e2m1_to_f64(np.arange(8))
+    mids = (mags[1:] + mags[:-1]) / 2                      # every tie point
+    ys = np.concatenate([rng.uniform(-9, 9, 4000), mids, -mids, mags, [6.5, 7.999, 100.0, -1e9, 0.25]])
+    got = oc.f64_to_e2m1_value(ys)
+    want = np.array([_e2m1_brute(y) for y in ys])
+    assert np.array_equal(got, want)
+
+
+def test_mx_shared_exponent_and_elements_brute_force():
+    """Shared exponent = (largest e with 2^e <= block max) - 2, found by search over
+    e; elements = E2M1 rounding of x / 2^shared; zero blocks take exponent -127."""
+    rng = np.random.default_rng(32)
+    rows = rng.standard_normal((40, 128)) * np.exp2(rng.integers(-30, 30, size=(40, 1)))
+    rows[3, 32:64] = 0.0
+    rows[5, :32] = np.exp2(rng.integers(-8, 8, size=32))   # powers of two exactly
+    codes, sc = oc.mx_quantize_fp4(rows)
+    for r in range(rows.shape[0]):
+        for blk in range(4):
+            x = rows[r, 32 * blk:32 * blk + 32]
+            amax = np.max(np.abs(x))
+            if amax == 0:
+                assert sc[r, blk] == 0 and np.all(oc.e2m1_to_f64(codes[r, 32 * blk:32 * blk + 32]) == 0)
+                continue
+            e = max(e for e in range(-200, 200) if 2.0 ** e <= amax)
+            assert sc[r, blk] == e - 2 + 127
+            want = [_e2m1_brute(v / 2.0 ** (e - 2)) for v in x]
+            assert np.array_equal(oc.e2m1_to_f64(codes[r, 32 * blk:32 * blk + 32]), want)
+
+
+def test_mx_roundtrip_error_bound():
+    """|x - dequant(quant(x))| is at most half the E2M1 spacing at |x| / X (times
+    X), or |x| - 6 X for saturated elements, whose magnitude is below 8 X."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((64, 256)) * 3.7
+    codes, sc = oc.mx_quantize_fp4(x)
+    xh = oc.mx_fp4_to_f64(codes, sc)
+    X = np.repeat(oc.e8m0_to_f64(sc), 32, axis=-1)
+    y = np.abs(x) / X
+    assert np.all(y < 8)
+    spacing = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    bound = np.where(y <= 6, 0.5 * spacing * X, (y - 6) * X)
+    assert np.all(np.abs(x - xh) <= bound * (1 + 1e-12))
+
+
+def test_index_score_mxfp4_brute_force():
+    """Tiny MXFP4 scores by plain loops over the decoded query and key values."""
+    rng = np.random.default_rng(34)
+    H, dI, N, m = 3, 64, 9, 2
+    qI = oc.f64_to_bf16_value(rng.standard_normal((2, H, dI)))
+    w = rng.standard_normal((2, H))
+    Kc, Ks = oc.mx_quantize_fp4(rng.standard_normal((N, dI)) * 0.4)
+    pos = [9, 17]
+    got = O.index_score_mxfp4(qI, w, Kc, Ks, pos, m=m)
+    for t in range(2):
+        n_vis = min(N, (pos[t] + 1) // m)
+        for s in range(N):
+            if s >= n_vis:
+                assert got[t, s] == -np.inf
+                continue
+            want = 0.0
+            for h in range(H):
+                qc, qs = oc.mx_quantize_fp4(qI[t, h])
+                dot = 0.0
+                for dd in range(dI):
+                    qv = oc.e2m1_to_f64(qc[dd]) * 2.0 ** (int(qs[dd // 32]) - 127)
+                    kv = oc.e2m1_to_f64(Kc[s, dd]) * 2.0 ** (int(Ks[s, dd // 32]) - 127)
+                    dot += qv * kv
+                want += w[t, h] * max(dot, 0.0)
+            assert abs(got[t, s] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_mx_planted_mistakes_are_caught(monkeypatch):
+    # (1) shared exponent minus 1 instead of minus 2 (E2M1's emax taken as 1)
+    with monkeypatch.context() as mp:
+        mp.setattr(oc, "E2M1_EMAX", 1)
+        with pytest.raises(AssertionError):
+            test_mx_shared_exponent_and_elements_brute_force()
+    # (2) ties rounded away from zero instead of to the even code
+    real = oc.f64_to_e2m1_value
+
+    def ties_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        r = real(x)
+        mags = oc.e2m1_to_f64(np.arange(8))
+        mids = (mags[1:] + mags[:-1]) / 2
+        up = {a: b for a, b in zip(mids, mags[1:])}
+        return np.where(np.isin(np.abs(x), mids),
+                        np.copysign([up.get(abs(v), 0.0) for v in x.ravel()], x.ravel()).reshape(x.shape), r)
+    with monkeypatch.context() as mp:
+        mp.setattr(oc, "f64_to_e2m1_value", ties_away)
+        with pytest.raises(AssertionError):
+            test_e2m1_rne_matches_brute_force()
