@@ -221,6 +221,28 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
                   float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
                   void* stream);
 
+/*
+ * csa_sparse_mqa without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus workspace and
+ * ws_bytes), checks and results as csa_sparse_mqa, bit for bit.  The split
+ * partials go to a static device array of CSA_NOALLOC_SCRATCH_BYTES that each
+ * GPU holds from the library's first use on it until the process ends; the
+ * call allocates and frees nothing.  A call whose partials need more than that
+ * (csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win) > CSA_NOALLOC_SCRATCH_BYTES;
+ * the 1M-context decode of 16 sequences x 128 heads x 512 needs 12.8 MB)
+ * returns CSA_E_UNSUPPORTED and launches nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap in time on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ * Nothing in the array needs to hold any value on entry.
+ */
+#define CSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int csa_sparse_mqa_noalloc(const void* q, const float* gamma_q, float eps, const void* E,
+                           long long N_cap, const int* idx, int k, const void* W, int W_cap,
+                           int n_win, const float* sink, const int* q_pos, int B, int Tq, int n_h,
+                           int d, int rope_dim, float rope_base, float scale, int dtype, void* out,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_index_score",
     "csa_topk",
-    "csa_topk_workspace_size", "csa_sparse_mqa", "hca_dense_mqa", "csa_mqa_workspace_size",
+    "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
+    "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES",
     "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3",
 ]
 
@@ -70,6 +71,10 @@ _lib.csa_mqa_workspace_size.argtypes = [_I, _I, _I, _I, _L]
 _lib.csa_sparse_mqa.restype = _I
 _lib.csa_sparse_mqa.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I,
                                 _F, _F, _I, _P, _P, _S, _P]
+_lib.csa_sparse_mqa_noalloc.restype = _I
+_lib.csa_sparse_mqa_noalloc.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                                        _I, _F, _F, _I, _P, _P]
+NOALLOC_SCRATCH_BYTES = 16 << 20
 _lib.hca_dense_mqa.restype = _I
 _lib.hca_dense_mqa.argtypes = [_P, _P, _F, _P, _L, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _F,
                                _F, _I, _P, _P, _S, _P]
@@ -238,6 +243,23 @@ def csa_sparse_mqa(q, E, idx, W, q_pos, out, *, n_win: int, sink=None, gamma_q=N
         _ptr(sink, "sink", torch.float32), _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d,
         rope_dim, rope_base, (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
         _ptr(workspace, "workspace"), ws_bytes, _stream()))
+
+
+def csa_sparse_mqa_noalloc(q, E, idx, W, q_pos, out, *, n_win: int, sink=None, gamma_q=None,
+                           eps: float = 1e-6, rope_dim: int = 0, rope_base: float = 10000.0,
+                           scale: float | None = None):
+    """a4 without a workspace: the split partials live in the library's static
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES); calls that overlap on one GPU race."""
+    B, Tq, n_h, d = _mqa_common(q, E, W, q_pos, out, sink, gamma_q)
+    k = idx.shape[2]
+    if tuple(idx.shape[:2]) != (B, Tq):
+        raise ValueError("idx must be [B, Tq, k]")
+    _check(_lib.csa_sparse_mqa_noalloc(
+        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), E.shape[1],
+        _ptr(idx, "idx", torch.int32, 3), k, _ptr(W, "W"), 0 if W is None else W.shape[1], n_win,
+        _ptr(sink, "sink", torch.float32), _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d,
+        rope_dim, rope_base, (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
+        _stream()))
 
 
 def hca_dense_mqa(q, E, W, q_pos, out, *, m: int, n_win: int, sink=None, gamma_q=None, eps: float = 1e-6,

@@ -4,9 +4,17 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/csa.h"
 #include "csa_internal.h"
 
+// Device scratch of csa_sparse_mqa_noalloc: the split partials of attention,
+// for callers that cannot allocate.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: host code uses the address that
+// hipGetSymbolAddress returns for the current device (scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[CSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -257,3 +265,56 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// the no-allocation variant of csa_sparse_mqa
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// the device address of `scratch` on the current device, looked up once per
+// device with that device current
+int scratch_ptr(const char* fn, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(CSA_E_HIP, "%s: no current HIP device", fn);
+  if (dev >= kMaxDevices) return fail(CSA_E_UNSUPPORTED, "%s: device %d >= %d", fn, dev, kMaxDevices);
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(CSA_E_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                hipGetErrorString(g_scratch_err[dev]));
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" int csa_sparse_mqa_noalloc(const void* q, const float* gamma_q, float eps, const void* E,
+                                      long long N_cap, const int* idx, int k, const void* W, int W_cap,
+                                      int n_win, const float* sink, const int* q_pos, int B, int Tq,
+                                      int n_h, int d, int rope_dim, float rope_base, float scale,
+                                      int dtype, void* out, void* stream) {
+  const char* fn = "csa_sparse_mqa_noalloc";
+  int st = mqa_common(fn, q, E, N_cap, W, W_cap, n_win, q_pos, B, Tq, n_h, d, rope_dim, dtype, out);
+  if (st != CSA_OK) return st;
+  if (!idx) return fail(CSA_E_NULL, "%s: idx is required", fn);
+  if (k < 1 || k > 65536) return fail(CSA_E_SHAPE, "%s: k outside [1, 65536]", fn);
+  const size_t need = csa_mqa_workspace_size(B, Tq, n_h, d, (long long)k + n_win);
+  if (need > (size_t)CSA_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA_E_UNSUPPORTED,
+                "%s: this call needs %zu bytes of split partials, more than the %u-byte static "
+                "scratch; use csa_sparse_mqa with a workspace", fn, need, (unsigned)CSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_ptr(fn, &ws)) != CSA_OK) return st;
+  csa::MqaArgs a{q, gamma_q, eps, E, N_cap, idx, k, 1, W, W_cap, n_win, sink, q_pos, B, Tq, n_h, d,
+                 rope_dim, rope_base, scale, dtype, out, ws, need > 0 ? (size_t)CSA_NOALLOC_SCRATCH_BYTES : 0};
+  const char* why = "";
+  st = csa::launch_mqa(a, (hipStream_t)stream, &why);
+  if (st != 0) return fail(st, "%s: %s", fn, why);
+  return ok();
+}

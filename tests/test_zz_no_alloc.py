@@ -1,0 +1,87 @@
+"""csa_sparse_mqa_noalloc: the variant of csa_sparse_mqa that allocates nothing
+(its split partials live in the library's static per-GPU scratch).
+
+Checked through the C ABI against csa_sparse_mqa with a caller workspace, bit
+for bit, on two calls in a row (the second one smaller, so it runs on what the
+first one left in the scratch), then a call that needs no partials, and a call
+whose partials exceed the scratch (rejected on the host, nothing written).
+"""
+from __future__ import annotations
+
+import math
+
+import pytest
+import torch
+
+from synth import Gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def csa():
+    import long_context_attention_02_amd as lib
+    return lib
+
+
+def _case(seed, B, Tq, n_h, d, N, k, n_win):
+    g = Gen(seed, DEV)
+    q = g.normal(1, (B, Tq, n_h, d), "bf16")
+    E = g.normal(2, (B, N, d), "bf16")
+    W = g.normal(3, (B, n_win, d), "bf16")
+    sink = g.normal(4, (n_h,), "f32", per_slot=False)
+    gamma = (1.0 + 0.25 * g.normal(5, (d,), "f32", per_slot=False)).contiguous()
+    pos = torch.full((B, Tq), 4 * N + 5, dtype=torch.int32, device=DEV)
+    pos += torch.arange(Tq, dtype=torch.int32, device=DEV).view(1, Tq)
+    idx = (g.uniform(6, (B, Tq, k)) * (N + 8)).to(torch.int32) - 4   # some out of range
+    idx[..., ::7] = -1
+    return dict(q=q, E=E, idx=idx.contiguous(), W=W, q_pos=pos.contiguous(), sink=sink, gamma_q=gamma,
+                n_win=n_win, rope_dim=64, scale=1 / math.sqrt(d))
+
+
+def _both(csa, c):
+    B, Tq, n_h, d = c["q"].shape
+    k = c["idx"].shape[2]
+    kw = dict(n_win=c["n_win"], sink=c["sink"], gamma_q=c["gamma_q"], rope_dim=c["rope_dim"],
+              scale=c["scale"])
+    ref = torch.full_like(c["q"], float("nan"))
+    ws = torch.empty(max(csa.csa_mqa_workspace_size(B, Tq, n_h, d, k + c["n_win"]), 1), dtype=torch.uint8,
+                     device=DEV)
+    csa.csa_sparse_mqa(c["q"], c["E"], c["idx"], c["W"], c["q_pos"], ref, workspace=ws, **kw)
+    got = torch.full_like(c["q"], float("nan"))
+    csa.csa_sparse_mqa_noalloc(c["q"], c["E"], c["idx"], c["W"], c["q_pos"], got, **kw)
+    torch.cuda.synchronize()
+    return ref, got
+
+
+def test_noalloc_equals_workspace_variant_twice_then_smaller(csa):
+    # 1: the 1M-decode attention shape (16 x 128 heads x 512, 1024 + 128 slots: 6 split
+    # partials per (query, head), 12.8 MB of the 16 MiB scratch)
+    big = _case(801, 16, 1, 128, 512, 4096, 1024, 128)
+    assert csa.csa_mqa_workspace_size(16, 1, 128, 512, 1024 + 128) <= csa.NOALLOC_SCRATCH_BYTES
+    ref, got = _both(csa, big)
+    assert torch.isfinite(ref.float()).all()
+    assert torch.equal(ref.view(torch.uint8), got.view(torch.uint8))
+    # 2: a smaller call right after, on what the first one left in the scratch
+    small = _case(802, 3, 2, 64, 512, 900, 300, 128)
+    ref, got = _both(csa, small)
+    assert torch.isfinite(ref.float()).all()
+    assert torch.equal(ref.view(torch.uint8), got.view(torch.uint8))
+    # 3: prefill-like (16 queries per sequence): one range per query, no partials
+    pre = _case(803, 1, 16, 32, 128, 500, 200, 64)
+    assert csa.csa_mqa_workspace_size(1, 16, 32, 128, 200 + 64) == 0
+    ref, got = _both(csa, pre)
+    assert torch.equal(ref.view(torch.uint8), got.view(torch.uint8))
+
+
+def test_noalloc_rejects_calls_beyond_the_scratch(csa):
+    c = _case(804, 32, 1, 128, 512, 64, 1024, 128)   # 25.6 MB of partials
+    assert csa.csa_mqa_workspace_size(32, 1, 128, 512, 1024 + 128) > csa.NOALLOC_SCRATCH_BYTES
+    out = torch.full_like(c["q"], float("nan"))
+    with pytest.raises(csa.CsaError) as ei:
+        csa.csa_sparse_mqa_noalloc(c["q"], c["E"], c["idx"], c["W"], c["q_pos"], out, n_win=c["n_win"],
+                                   sink=c["sink"], rope_dim=64)
+    assert ei.value.status == 4 and "static" in str(ei.value)
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
