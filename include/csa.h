@@ -37,8 +37,13 @@ extern "C" {
 
 #define CSA_ABI_VERSION 3
 
-/* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities). */
-enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2 };
+/* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities).
+ * CSA_MXFP4 is OCP MXFP4: FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6
+ * and their negatives) packed two per byte, the even channel in the low
+ * nibble, with one E8M0 scale byte (2^(byte - 127)) per 32 channels in a
+ * separate array; quantised by the OCP MX rule (shared exponent
+ * floor(log2(block max)) - 2, elements rounded to nearest even, saturating). */
+enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 };
 
 enum csa_status {
   CSA_OK = 0,
@@ -83,13 +88,16 @@ const char* csa_last_error(void);
  *      Sequence b then has min(T, max(0, T_len[b])) tokens: candidates at or
  *      past it are absent, and an entry s with m s >= that count does not
  *      exist in sequence b and its output row is not written.
- *  E        : output [B][rows][c] of out_dtype (F32, BF16 or FP8_E4M3), batch
- *      stride out_batch_stride elements; entry s goes to row s, or to row
- *      s mod out_ring when out_ring > 0 (a sliding-window ring; then at most
- *      out_ring entries per call, so that no two write the same row).
- *  E_scale  : FP8_E4M3 only: fp32 per-row scale at
- *      E_scale[b * (out_batch_stride / c) + row] (row absmax / 448, or 1 for
- *      a zero row); codes are RNE(value / scale), saturated to +-448.
+ *  E        : output [B][rows][c] of out_dtype (F32, BF16, FP8_E4M3 or MXFP4),
+ *      batch stride out_batch_stride elements (channels); entry s goes to row
+ *      s, or to row s mod out_ring when out_ring > 0 (a sliding-window ring;
+ *      then at most out_ring entries per call, so that no two write the same
+ *      row).  MXFP4 rows are c / 2 bytes (c % 32 == 0).
+ *  E_scale  : FP8_E4M3: fp32 per-row scale at E_scale[b * (out_batch_stride /
+ *      c) + row] (row absmax / 448, or 1 for a zero row); codes are
+ *      RNE(value / scale), saturated to +-448.  MXFP4: the E8M0 block scales,
+ *      bytes [B][rows][c / 32] (pass the byte array's address); the
+ *      quantisation decisions are taken on the fp32 value.  NULL otherwise.
  */
 int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* Z_b, int in_dtype,
                  int B, long long R, long long in_batch_stride, long long tok_base, long long T,
@@ -143,14 +151,20 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
  *   own block).
  *  q_I     : [B][Tq][H_I][d_I], q_dtype F32 or BF16.
  *  w_I     : [B][Tq][H_I] fp32 (any sign).
- *  K_I     : [B][N_cap][d_I]; k_dtype F32 (with q F32), BF16 (with q BF16) or
+ *  K_I     : [B][N_cap][d_I]; k_dtype F32 (with q F32), BF16 (with q BF16),
  *            FP8_E4M3 (with q BF16), then K = code * K_scale[b][s] and
- *            K_scale ([B][N_cap] fp32, every entry > 0) is required.
+ *            K_scale ([B][N_cap] fp32, every entry > 0) is required, or
+ *            MXFP4 (with q BF16; d_I % 32 == 0): the FP4 query-key path of the
+ *            method page's section 3.6 -- K_I holds [B][N_cap][d_I / 2] packed
+ *            codes, K_scale the E8M0 bytes [B][N_cap][d_I / 32] (pass the byte
+ *            array's address), and the query is quantised to MXFP4 by the same
+ *            rule (per head, 32-dim blocks) before the products.
  *  q_pos   : [B][Tq] int32 absolute positions (>= 0).
  *  I_out   : [B][Tq][N_cap] fp32.
  *  Supported: H_I <= 64, d_I <= 256 (any); the matrix-core path covers
  *  H_I in {16, 32, 64} and d_I in {32, 64, 128} with BF16 queries (other
- *  head counts, e.g. 48, take the generic kernel).
+ *  head counts, e.g. 48, take the generic kernel); for MXFP4 keys it covers
+ *  d_I = 128 with fewer than 8 queries per sequence (decode).
  */
 int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos,

@@ -21,11 +21,11 @@ __all__ = [
     "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
     "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES",
-    "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3",
+    "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3", "CSA_MXFP4",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
-CSA_F32, CSA_BF16, CSA_FP8_E4M3 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -96,7 +96,9 @@ def _check(status: int):
         raise CsaError(status, _lib.csa_last_error().decode())
 
 
-_DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16, torch.float8_e4m3fn: CSA_FP8_E4M3}
+# uint8 tensors hold MXFP4 (two E2M1 codes per byte, E8M0 block scales beside them)
+_DT = {torch.float32: CSA_F32, torch.bfloat16: CSA_BF16, torch.float8_e4m3fn: CSA_FP8_E4M3,
+       torch.uint8: CSA_MXFP4}
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -134,11 +136,14 @@ def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_beg
     for name, t in (("Z_a", Z_a), ("C_b", C_b), ("Z_b", Z_b)):
         if t is not None and (t.shape != C_a.shape or t.dtype != C_a.dtype):
             raise ValueError(f"{name} must match C_a in shape and dtype")
-    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != c:
-        raise ValueError("E must be [B, rows, c]")
+    mx = E.dtype == torch.uint8
+    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != (c // 2 if mx else c):
+        raise ValueError("E must be [B, rows, c] ([B, rows, c / 2] bytes for MXFP4)")
     if E.shape[1] < (out_ring if out_ring > 0 else s_end):
         raise ValueError("E has fewer rows than the entries written")
-    if E_scale is not None and tuple(E_scale.shape) != (B, E.shape[1]):
+    if mx and (E_scale is None or E_scale.dtype != torch.uint8 or tuple(E_scale.shape) != (B, E.shape[1], c // 32)):
+        raise ValueError("MXFP4 output needs E_scale uint8 [B, rows, c / 32]")
+    if not mx and E_scale is not None and tuple(E_scale.shape) != (B, E.shape[1]):
         raise ValueError("E_scale must be [B, rows]")
     if T_len is not None and tuple(T_len.shape) != (B,):
         raise ValueError("T_len must be [B]")
@@ -146,7 +151,8 @@ def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_beg
             B, R, R * c, tok_base, T, _ptr(T_len, "T_len", torch.int32), c, m, overlap, s_begin, s_end,
             _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
             m if pos_stride is None else pos_stride, pos_offset,
-            _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.float32), E.shape[1] * c, out_ring)
+            _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.uint8 if mx else torch.float32),
+            E.shape[1] * c, out_ring)
 
 
 def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
@@ -171,18 +177,23 @@ def csa_compress_batch(jobs):
 
 def csa_index_score(q_I, w_I, K_I, q_pos, I_out, *, m: int, K_scale=None):
     """a2.  q_I [B, Tq, H, dI], w_I [B, Tq, H] fp32, K_I [B, N, dI],
-    q_pos [B, Tq] int32, I_out [B, Tq, N] fp32, K_scale [B, N] for fp8 keys."""
+    q_pos [B, Tq] int32, I_out [B, Tq, N] fp32, K_scale [B, N] for fp8 keys.
+    MXFP4 keys: K_I uint8 [B, N, dI / 2] and K_scale uint8 [B, N, dI / 32]."""
     B, Tq, H, dI = q_I.shape
     N = K_I.shape[1]
-    if tuple(w_I.shape) != (B, Tq, H) or K_I.shape[0] != B or K_I.shape[2] != dI:
+    mx = K_I.dtype == torch.uint8
+    if tuple(w_I.shape) != (B, Tq, H) or K_I.shape[0] != B or K_I.shape[2] != (dI // 2 if mx else dI):
         raise ValueError("shape mismatch among q_I, w_I, K_I")
-    if K_scale is not None and tuple(K_scale.shape) != (B, N):
+    if mx and (K_scale is None or K_scale.dtype != torch.uint8 or tuple(K_scale.shape) != (B, N, dI // 32)):
+        raise ValueError("MXFP4 keys need K_scale uint8 [B, N, dI / 32]")
+    if not mx and K_scale is not None and tuple(K_scale.shape) != (B, N):
         raise ValueError("K_scale must be [B, N]")
     if tuple(I_out.shape) != (B, Tq, N) or tuple(q_pos.shape) != (B, Tq):
         raise ValueError("I_out must be [B, Tq, N] and q_pos [B, Tq]")
     _check(_lib.csa_index_score(
         _ptr(q_I, "q_I", dims=4), _dt(q_I), _ptr(w_I, "w_I", torch.float32), _ptr(K_I, "K_I", dims=3),
-        _dt(K_I), _ptr(K_scale, "K_scale", torch.float32), _ptr(q_pos, "q_pos", torch.int32),
+        _dt(K_I), _ptr(K_scale, "K_scale", torch.uint8 if mx else torch.float32),
+        _ptr(q_pos, "q_pos", torch.int32),
         B, Tq, H, dI, N, m, _ptr(I_out, "I_out", torch.float32), _stream()))
 
 

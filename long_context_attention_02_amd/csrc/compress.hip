@@ -234,6 +234,24 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
     for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv)
       ((uint8_t*)E)[obase + j] = f32_to_e4m3(outv[nv] / scale);
     if (threadIdx.x == 0) E_scale[(size_t)b * (size_t)(out_bs / c) + (size_t)orow] = scale;
+  } else if constexpr (ODT == DT_MX4) {
+    // MXFP4: channel j sits in thread j (c % 32 == 0, so a 32-channel block is
+    // 32 consecutive lanes of one wave): block maximum by lane exchange, codes,
+    // the even channel's thread writes the byte of the pair, the block's first
+    // thread its scale byte
+    nv = 0;
+    for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) {
+      float a = fabsf(outv[nv]);
+#pragma unroll
+      for (int x = 1; x < 32; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+      const int se = mx4_shared_exp(a);
+      const uint32_t code = f32_to_e2m1(ldexpf(outv[nv], -se));
+      const uint32_t other = (uint32_t)__shfl_xor((int)code, 1, 64);
+      if ((j & 1) == 0) ((uint8_t*)E)[(obase + j) / 2] = (uint8_t)(code | (other << 4));
+      if ((j & 31) == 0)
+        ((uint8_t*)E_scale)[((size_t)b * (size_t)(out_bs / c) + (size_t)orow) * (size_t)(c / 32) + j / 32] =
+            (uint8_t)(se + 127);
+    }
   } else {
     nv = 0;
     for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) store_from_f32<ODT>(E, obase + j, outv[nv]);
@@ -244,13 +262,15 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(const CompressBa
   extern __shared__ float smem[];
   const CompressJob& J = jb.job[blockIdx.z];
   if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
-  switch (J.in_dtype * 3 + J.out_dtype) {
-    case DT_F32 * 3 + DT_F32: compress_entry<DT_F32, DT_F32>(J, smem); break;
-    case DT_F32 * 3 + DT_BF16: compress_entry<DT_F32, DT_BF16>(J, smem); break;
-    case DT_F32 * 3 + DT_FP8: compress_entry<DT_F32, DT_FP8>(J, smem); break;
-    case DT_BF16 * 3 + DT_F32: compress_entry<DT_BF16, DT_F32>(J, smem); break;
-    case DT_BF16 * 3 + DT_BF16: compress_entry<DT_BF16, DT_BF16>(J, smem); break;
-    default: compress_entry<DT_BF16, DT_FP8>(J, smem); break;
+  switch (J.in_dtype * 4 + J.out_dtype) {
+    case DT_F32 * 4 + DT_F32: compress_entry<DT_F32, DT_F32>(J, smem); break;
+    case DT_F32 * 4 + DT_BF16: compress_entry<DT_F32, DT_BF16>(J, smem); break;
+    case DT_F32 * 4 + DT_FP8: compress_entry<DT_F32, DT_FP8>(J, smem); break;
+    case DT_F32 * 4 + DT_MX4: compress_entry<DT_F32, DT_MX4>(J, smem); break;
+    case DT_BF16 * 4 + DT_F32: compress_entry<DT_BF16, DT_F32>(J, smem); break;
+    case DT_BF16 * 4 + DT_BF16: compress_entry<DT_BF16, DT_BF16>(J, smem); break;
+    case DT_BF16 * 4 + DT_FP8: compress_entry<DT_BF16, DT_FP8>(J, smem); break;
+    default: compress_entry<DT_BF16, DT_MX4>(J, smem); break;
   }
 }
 
@@ -412,6 +432,33 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
     scale = am > 0.f ? am / 448.0f : 1.0f;
     if (lane == 0) J.E_scale[(size_t)b * (size_t)(J.out_bs / c) + (size_t)orow] = scale;
   }
+  if constexpr (ODT == DT_MX4) {
+    // MXFP4: a 32-channel block is 32 / VEC consecutive lanes (c % 32 == 0);
+    // the lane holding a block's first channel writes the scale byte
+    constexpr int LPB = 32 / VEC;
+#pragma unroll
+    for (int pi = 0; pi < COMPW_MAXP; ++pi) {
+      if (64 * pi >= npieces) break;
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a = fmaxf(a, fabsf(pooled[pi][e]));
+#pragma unroll
+      for (int x = 1; x < LPB; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+      const int se = mx4_shared_exp(a);
+      const int piece = lane + 64 * pi;
+      if (piece >= npieces) continue;
+      uint32_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) pk |= f32_to_e2m1(ldexpf(pooled[pi][e], -se)) << (4 * e);
+      uint8_t* ob = (uint8_t*)J.E + (obase + (size_t)piece * VEC) / 2;
+      if constexpr (VEC == 8) *(uint32_t*)ob = pk;
+      else *(uint16_t*)ob = (uint16_t)pk;
+      if (piece % LPB == 0)
+        ((uint8_t*)J.E_scale)[((size_t)b * (size_t)(J.out_bs / c) + (size_t)orow) * (size_t)(c / 32) +
+                              (size_t)piece / LPB] = (uint8_t)(se + 127);
+    }
+    return;
+  }
 #pragma unroll
   for (int pi = 0; pi < COMPW_MAXP; ++pi) {
     if (64 * pi >= npieces) break;
@@ -443,13 +490,15 @@ __global__ __launch_bounds__(64 * COMPW_WAVES) void compress_wave_kernel(const C
   const long long e = item - jb.first[q];
   const long long s = J.s_begin + e % J.n_entries;
   const int b = (int)(e / J.n_entries);
-  switch (J.in_dtype * 3 + J.out_dtype) {
-    case DT_F32 * 3 + DT_F32: compress_entry_wave<DT_F32, DT_F32, MAXC>(J, s, b, lane); break;
-    case DT_F32 * 3 + DT_BF16: compress_entry_wave<DT_F32, DT_BF16, MAXC>(J, s, b, lane); break;
-    case DT_F32 * 3 + DT_FP8: compress_entry_wave<DT_F32, DT_FP8, MAXC>(J, s, b, lane); break;
-    case DT_BF16 * 3 + DT_F32: compress_entry_wave<DT_BF16, DT_F32, MAXC>(J, s, b, lane); break;
-    case DT_BF16 * 3 + DT_BF16: compress_entry_wave<DT_BF16, DT_BF16, MAXC>(J, s, b, lane); break;
-    default: compress_entry_wave<DT_BF16, DT_FP8, MAXC>(J, s, b, lane); break;
+  switch (J.in_dtype * 4 + J.out_dtype) {
+    case DT_F32 * 4 + DT_F32: compress_entry_wave<DT_F32, DT_F32, MAXC>(J, s, b, lane); break;
+    case DT_F32 * 4 + DT_BF16: compress_entry_wave<DT_F32, DT_BF16, MAXC>(J, s, b, lane); break;
+    case DT_F32 * 4 + DT_FP8: compress_entry_wave<DT_F32, DT_FP8, MAXC>(J, s, b, lane); break;
+    case DT_F32 * 4 + DT_MX4: compress_entry_wave<DT_F32, DT_MX4, MAXC>(J, s, b, lane); break;
+    case DT_BF16 * 4 + DT_F32: compress_entry_wave<DT_BF16, DT_F32, MAXC>(J, s, b, lane); break;
+    case DT_BF16 * 4 + DT_BF16: compress_entry_wave<DT_BF16, DT_BF16, MAXC>(J, s, b, lane); break;
+    case DT_BF16 * 4 + DT_FP8: compress_entry_wave<DT_BF16, DT_FP8, MAXC>(J, s, b, lane); break;
+    default: compress_entry_wave<DT_BF16, DT_MX4, MAXC>(J, s, b, lane); break;
   }
 }
 
@@ -480,7 +529,8 @@ static bool wave_job(const CompressArgs& x) {
   // 16-byte pieces: every input row and (for bf16 output) every output row starts 16-byte aligned
   const bool in_al = aligned16(x.C_a) && (!x.C_b || aligned16(x.C_b)) && (!x.Z_a || aligned16(x.Z_a)) &&
                      (!x.Z_b || aligned16(x.Z_b)) && (x.in_bs * (x.in_dtype == DT_F32 ? 4 : 2)) % 16 == 0;
-  const bool out_al = x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0);
+  const bool out_al = (x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0)) &&
+                      (x.out_dtype != DT_MX4 || ((uintptr_t)x.E & 3u) == 0);
   // a job of a few dozen entries (decode) is pure latency, where one workgroup per
   // entry is quicker; many entries (prefill) are throughput, where a wave each is
   const long long items = (long long)x.B * (x.s_end - x.s_begin);

@@ -33,7 +33,7 @@ int ok() {
   return CSA_OK;
 }
 
-bool dtype_valid(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3; }
+bool dtype_valid(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; }
 
 }  // namespace
 
@@ -55,8 +55,10 @@ static int check_compress(const csa_compress_job& j, const char* who) {
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16)
     return fail(CSA_E_DTYPE, "%s: in_dtype must be F32 or BF16", who);
   if (!dtype_valid(out_dtype)) return fail(CSA_E_DTYPE, "%s: unknown out_dtype", who);
-  if (out_dtype == CSA_FP8_E4M3 && !E_scale)
-    return fail(CSA_E_NULL, "%s: E_scale is required for FP8 output", who);
+  if ((out_dtype == CSA_FP8_E4M3 || out_dtype == CSA_MXFP4) && !E_scale)
+    return fail(CSA_E_NULL, "%s: E_scale is required for FP8 and MXFP4 output", who);
+  if (out_dtype == CSA_MXFP4 && (c % 32 || out_batch_stride % c))
+    return fail(CSA_E_SHAPE, "%s: MXFP4 output needs c %% 32 == 0 and out_batch_stride %% c == 0", who);
   if (B < 1 || R < 1 || c < 1 || m < 1 || T < 1)
     return fail(CSA_E_SHAPE, "%s: B, R, c, m and T must be >= 1", who);
   if (c > 1024) return fail(CSA_E_UNSUPPORTED, "%s: c = %d exceeds 1024", who, c);
@@ -167,9 +169,11 @@ int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
   if (q_dtype == CSA_F32 && k_dtype != CSA_F32)
     return fail(CSA_E_DTYPE, "csa_index_score: F32 queries need F32 keys");
   if (q_dtype == CSA_BF16 && k_dtype == CSA_F32)
-    return fail(CSA_E_DTYPE, "csa_index_score: BF16 queries need BF16 or FP8 keys");
-  if (k_dtype == CSA_FP8_E4M3 && !K_scale)
-    return fail(CSA_E_NULL, "csa_index_score: K_scale is required for FP8 keys");
+    return fail(CSA_E_DTYPE, "csa_index_score: BF16 queries need BF16, FP8 or MXFP4 keys");
+  if ((k_dtype == CSA_FP8_E4M3 || k_dtype == CSA_MXFP4) && !K_scale)
+    return fail(CSA_E_NULL, "csa_index_score: K_scale is required for FP8 and MXFP4 keys");
+  if (k_dtype == CSA_MXFP4 && d_I % 32)
+    return fail(CSA_E_SHAPE, "csa_index_score: MXFP4 keys need d_I %% 32 == 0");
   if (B < 1 || Tq < 1 || H_I < 1 || d_I < 1 || N_cap < 1 || m < 1)
     return fail(CSA_E_SHAPE, "csa_index_score: sizes must be >= 1");
   if (H_I > 64 || d_I > 256 || H_I * (d_I + 1) > 16384)

@@ -15,7 +15,9 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+// DT_MX4: OCP MXFP4 -- FP4 E2M1 codes packed two per byte (the even channel in
+// the low nibble) with one E8M0 scale byte per 32 channels in a separate array
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MX4 = 3 };
 
 // ---- scalar conversions ---------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -54,6 +56,31 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
     code = ((uint32_t)(E + 7) << 3) | f;
   }
   return (uint8_t)(sign | code);
+}
+
+// ---- OCP MX, FP4 E2M1 elements with an E8M0 scale per block of 32 ----------
+// Shared exponent of a block: floor(log2(amax)) - 2 (E2M1's largest power of
+// two is 2^2), clamped to E8M0's [-127, 127]; a zero (or fp32-subnormal)
+// maximum gives -127.  The scale byte is the exponent + 127.
+__device__ __forceinline__ int mx4_shared_exp(float amax) {
+  const int e = (int)((__float_as_uint(amax) >> 23) & 0xff);   // amax >= 0
+  return e == 0 ? -127 : min(max(e - 127 - 2, -127), 127);
+}
+// E2M1 code of y (a value already divided by its block scale): round to the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code (mantissa bit
+// 0), saturating at 6; the sign goes to bit 3
+__device__ __forceinline__ uint32_t f32_to_e2m1(float y) {
+  const float a = fabsf(y);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+// value of an E2M1 code (exact)
+__device__ __forceinline__ float e2m1_to_f32(uint32_t code) {
+  const uint32_t e = (code >> 1) & 3u, m = code & 1u;
+  const float mag = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+  return (code & 8u) ? -mag : mag;
 }
 
 // order-preserving map of a float score to uint32 (-0.0 canonicalised to +0.0)

@@ -18,7 +18,9 @@
 //
 // fp8 keys (OCP e4m3fn) are widened to bf16 exactly (3 mantissa bits fit in
 // 7) and the per-row scale (> 0) multiplies the head sum, which equals
-// scaling the key inside the ReLU.
+// scaling the key inside the ReLU.  MXFP4 keys (OCP MX: FP4 E2M1 with an
+// E8M0 scale per 32 dims) run the QK products in FP4 on both sides, with the
+// block-scaled matrix instruction (index_mx4_decode).
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -61,6 +63,17 @@ __global__ __launch_bounds__(256) void index_valu_kernel(
     sq[e] = load_as_f32<QDT>(q, qrow * (size_t)(H * dI) + e);
   for (int e = threadIdx.x; e < H; e += blockDim.x) sq[H * dI + e] = w[qrow * H + e];
   __syncthreads();
+  if constexpr (KDT == DT_MX4) {
+    // the FP4 QK path: the query too is MXFP4, quantised per head and 32-dim block
+    for (int p = threadIdx.x; p < H * (dI / 32); p += blockDim.x) {
+      float* x = sq + (p / (dI / 32)) * dI + 32 * (p % (dI / 32));
+      float a = 0.f;
+      for (int e = 0; e < 32; ++e) a = fmaxf(a, fabsf(x[e]));
+      const int se = mx4_shared_exp(a);
+      for (int e = 0; e < 32; ++e) x[e] = ldexpf(e2m1_to_f32(f32_to_e2m1(ldexpf(x[e], -se))), se);
+    }
+    __syncthreads();
+  }
   const long long s = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= N_cap) return;
   const long long i = q_pos[qrow];
@@ -72,7 +85,14 @@ __global__ __launch_bounds__(256) void index_valu_kernel(
     for (int h = 0; h < VALU_HMAX; ++h) dot[h] = 0.f;
     const size_t kb = ((size_t)b * (size_t)N_cap + (size_t)s) * (size_t)dI;
     for (int d = 0; d < dI; ++d) {
-      const float kv = load_key<KDT>(K, kb + d);
+      float kv;
+      if constexpr (KDT == DT_MX4) {
+        const uint32_t byte = ((const uint8_t*)K)[(kb + d) >> 1];
+        const uint32_t sc = ((const uint8_t*)Ks)[((size_t)b * (size_t)N_cap + (size_t)s) * (size_t)(dI / 32) + d / 32];
+        kv = ldexpf(e2m1_to_f32((byte >> (4 * (d & 1))) & 15u), (int)sc - 127);
+      } else {
+        kv = load_key<KDT>(K, kb + d);
+      }
 #pragma unroll
       for (int h = 0; h < VALU_HMAX; ++h)
         if (h < H) dot[h] += sq[h * dI + d] * kv;
@@ -469,6 +489,163 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
 }
 
 // ---------------------------------------------------------------------------
+// decode with MXFP4 keys: the FP4 query-key path (DeepSeek-V4 method page,
+// section 3.6).  Keys are E2M1 codes, 64 bytes per 128-dim row, with four E8M0
+// block scales per row in a separate array; the query is quantised to MXFP4
+// by the same rule in the prologue.  One v_mfma_scale_f32_16x16x128_f8f6f4
+// per 16-head tile covers all 128 dims of 16 keys: lane (g, j) holds dims
+// 32 g .. 32 g + 31 (low nibble first) of head row j (A) and of key j (B) and
+// the scale byte of that block, so a 16-key subtile is one contiguous kilobyte
+// that every lane loads straight into its operand (16 bytes; four lanes per
+// 64-byte row), with no LDS transpose.  The work split over waves, the score
+// staging in LDS and the flushes are those of index_mfma_decode.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
+
+template <int QH>
+__device__ __forceinline__ float mx4_partial(const u32x4_t (&qa)[QH], const int (&qsc)[QH],
+                                             const float (&wv)[QH][4], const u32x4_t kc, int ksc) {
+  const i32x8_t Bv = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+  float part = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+    const i32x8_t Av = {(int)qa[mt][0], (int)qa[mt][1], (int)qa[mt][2], (int)qa[mt][3], 0, 0, 0, 0};
+    // cbsz = blgp = 4: both operands FP4 E2M1; op_sel 0: the scale is byte 0
+    const f32x4_t acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        Av, Bv, f32x4_t{0.f, 0.f, 0.f, 0.f}, 4, 4, 0, qsc[mt], 0, ksc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part += wv[mt][r] * __int_as_float(max(__float_as_int(acc[r]), 0));
+  }
+  return part;
+}
+
+template <int QH>
+__global__ __launch_bounds__(256) void index_mx4_decode(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ K,
+    const uint8_t* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
+    float* __restrict__ out, int flush_ok) {
+  constexpr int H = 16 * QH, DI = 128, RB = DI / 2, SB = DI / 32;   // code and scale bytes per key
+  constexpr int PF = 8;   // subtiles in flight per wave (two groups of four)
+  constexpr int U = IDX_UNIT;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  const int b = blockIdx.z, t = blockIdx.y;
+  const size_t qrow = (size_t)b * Tq + t;
+  const long long W = 4LL * gridDim.x;
+  const long long wid = 4LL * blockIdx.x + wave;
+  const long long nunits = (N_cap + 16 * U - 1) / (16 * U);
+  if (wid >= nunits) return;
+  const int nls = (int)((nunits - 1 - wid) / W + 1) * U;   // subtiles of this wave (a multiple of 4)
+  __builtin_assume(nls >= 1);
+  const long long i = q_pos[qrow];
+  const long long nvis = min(N_cap, (i + 1) / m);
+  const int wid32 = (int)wid, W32 = (int)W;
+  auto key0 = [&](int ls) -> int { return 16 * ((wid32 + W32 * (ls / U)) * U + ls % U); };
+  const int klast = (int)(N_cap - 1);
+  const uint8_t* Kb = K + (size_t)b * (size_t)N_cap * RB;
+  const uint8_t* Sb = Ks + (size_t)b * (size_t)N_cap * SB;
+  float* orow = out + qrow * (size_t)N_cap;
+
+  // the key ring, issued first: subtile p's codes (lane (g, j): bytes 16 g of
+  // key j) and the key's scale dword (byte g is this lane's block)
+  u32x4_t rc[PF];
+  uint32_t rs[PF];
+  auto load_sub = [&](int first, u32x4_t& c, uint32_t& sc) {
+    const uint32_t row = min((uint32_t)first + (uint32_t)j, (uint32_t)klast);
+    c = __builtin_nontemporal_load((const u32x4_t*)(Kb + (size_t)row * RB + 16 * g));
+    sc = __builtin_nontemporal_load((const uint32_t*)(Sb + (size_t)row * SB));
+  };
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    load_sub(p < nls ? key0(p) : klast, rc[p], rs[p]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // query: head 16 mt + j, dims 32 g .. 32 g + 31, quantised to MXFP4
+  u32x4_t qa[QH];
+  int qsc[QH];
+  float wv[QH][4];
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+    const uint16_t* qp = q + (qrow * H + 16 * mt + j) * (size_t)DI + 32 * g;
+    u32x4_t raw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *(const u32x4_t*)(qp + 8 * c);
+    float x[32];
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = __uint_as_float(raw[c][e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(raw[c][e] & 0xffff0000u);
+        a = fmaxf(a, fmaxf(fabsf(x[8 * c + 2 * e]), fabsf(x[8 * c + 2 * e + 1])));
+      }
+    const int se = mx4_shared_exp(a);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk |= f32_to_e2m1(ldexpf(x[8 * d + e], -se)) << (4 * e);
+      qa[mt][d] = pk;
+    }
+    qsc[mt] = se + 127;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = w[qrow * H + 16 * mt + 4 * g + r];
+  }
+
+  __shared__ __attribute__((aligned(16))) float stage[4][IDX_STAGE];
+  int flushed = 0;
+#pragma unroll 1
+  for (int st0 = 0; st0 < nls; st0 += 8) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int gs = st0 + 4 * half;   // first subtile of this group of four
+      if (gs >= nls) break;            // (wave-uniform)
+      float P[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int slot = 4 * half + u;
+        const u32x4_t c = rc[slot];
+        const int sc = (int)((rs[slot] >> (8 * g)) & 0xffu);
+        const int nx = gs + u + PF;
+        load_sub(nx < nls ? key0(nx) : klast, rc[slot], rs[slot]);
+        P[u] = mx4_partial<QH>(qa, qsc, wv, c, sc);
+        asm volatile("" : "+v"(P[u]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float v = reduce_scatter4(P, g);
+      const int ls = gs + g;
+      if (ls < nls) stage[wave][16 * ls + j] = key0(ls) + j < nvis ? v : -INFINITY;
+      if constexpr (IDX_FLUSH > 0) {
+        if ((gs + 4) % IDX_FLUSH == 0 && gs + 4 <= nls && flush_ok) {
+          const int e0 = 16 * (gs + 4 - IDX_FLUSH) + 4 * lane;
+#pragma unroll
+          for (int c = 0; c < IDX_FLUSH / 16; ++c) {
+            const int e = e0 + 256 * c;
+            __builtin_nontemporal_store(*(const f32x4_t*)&stage[wave][e],
+                                        (f32x4_t*)(orow + key0(e >> 4) + (e & 15)));
+          }
+          flushed = gs + 4;
+        }
+      }
+    }
+  }
+  for (int e = 16 * flushed + 4 * lane; e < 16 * nls; e += 256) {
+    const int key = key0(e >> 4) + (e & 15);
+    if (key > klast) continue;
+    const f32x4_t v = *(const f32x4_t*)&stage[wave][e];
+    if (key + 3 <= klast && (((uintptr_t)(orow + key)) & 15u) == 0) {
+      __builtin_nontemporal_store(v, (f32x4_t*)(orow + key));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (key + c <= klast) orow[key + c] = v[c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // prefill: a workgroup owns 4*QPW consecutive query rows (QPW per wave, query
 // fragments resident in registers) and sweeps the visible keys in tiles of
 // 64 staged through LDS (double-buffered, widened to bf16), so every key tile
@@ -636,6 +813,31 @@ static long long resident_waves(const void* kfn, int block) {
 static constexpr int PF_MIN_TQ = 8;   // query rows per sequence at which the LDS-tiled kernel is used
 static constexpr int PF_QPW = 2;
 
+// decode grid: at most one round of resident waves over the chip, shared by the
+// query rows, a power of two per row (units then divide evenly at power-of-two
+// caches: at 16 x 262,144 keys, 128 waves per row of 32 units each beat 192
+// waves of 21 or 22 units by 2.5%), and enough waves per row that each wave's
+// scores fit its LDS stage
+static dim3 decode_grid(const IndexArgs& a, const void* kfn) {
+  const long long waves = resident_waves(kfn, 256);
+  const long long rows = (long long)a.B * a.Tq;
+  const long long nunits = (a.N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT);
+  long long wpr = 1;
+  while (2 * wpr <= waves / rows) wpr *= 2;
+  wpr = max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
+  wpr = min(wpr, nunits);
+  return dim3((unsigned)((wpr + 3) / 4), (unsigned)a.Tq, (unsigned)a.B);
+}
+
+template <int QH>
+static void launch_mx4(const IndexArgs& a, hipStream_t st) {
+  auto kfn = index_mx4_decode<QH>;
+  const dim3 grid = decode_grid(a, (const void*)kfn);
+  const int flush_ok = (((uintptr_t)a.out) & 15u) == 0 && a.N_cap % (16 * IDX_UNIT) == 0;
+  hipLaunchKernelGGL(kfn, grid, dim3(256), 0, st, (const uint16_t*)a.q, a.w, (const uint8_t*)a.K,
+                     (const uint8_t*)a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out, flush_ok);
+}
+
 template <int QH, int KS, int KDT>
 static void launch_mfma(const IndexArgs& a, hipStream_t st) {
   const uint16_t* q = (const uint16_t*)a.q;
@@ -644,20 +846,8 @@ static void launch_mfma(const IndexArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((index_mfma_prefill<QH, KS, KDT, PF_QPW>), grid, dim3(256), 0, st, q, a.w,
                        a.K, a.K_scale, a.q_pos, a.Tq, a.N_cap, a.m, a.out);
   } else {
-    // at most one round of resident waves over the chip, shared by the query
-    // rows: a power of two per row (units then divide evenly at power-of-two
-    // caches: at 16 x 262,144 keys, 128 waves per row of 32 units each beat
-    // 192 waves of 21 or 22 units by 2.5%); enough waves per row that each
-    // wave's scores fit its LDS stage
     auto kfn = index_mfma_decode<QH, KS, KDT>;
-    const long long waves = resident_waves((const void*)kfn, 256);
-    const long long rows = (long long)a.B * a.Tq;
-    const long long nunits = (a.N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT);
-    long long wpr = 1;
-    while (2 * wpr <= waves / rows) wpr *= 2;
-    wpr = max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
-    wpr = min(wpr, nunits);
-    dim3 grid((unsigned)((wpr + 3) / 4), (unsigned)a.Tq, (unsigned)a.B);
+    const dim3 grid = decode_grid(a, (const void*)kfn);
     // early flushes use 16-byte stores of whole units
     const int flush_ok = (((uintptr_t)a.out) & 15u) == 0 && a.N_cap % (16 * IDX_UNIT) == 0;
     hipLaunchKernelGGL((index_mfma_decode<QH, KS, KDT>), grid, dim3(256), 0, st, q, a.w, a.K,
@@ -678,8 +868,19 @@ static void launch_mfma_ks(const IndexArgs& a, hipStream_t st) {
   else launch_mfma_k<QH, 4>(a, st);
 }
 
+// the MXFP4 matrix-core kernel: decode rows, 128-dim keys
+static bool index_mx4_supported(const IndexArgs& a) {
+  return a.k_dtype == DT_MX4 && a.q_dtype == DT_BF16 && a.dI == 128 && a.Tq < PF_MIN_TQ &&
+         (a.H == 16 || a.H == 32 || a.H == 64) && (((uintptr_t)a.K) & 15u) == 0 &&
+         (((uintptr_t)a.K_scale) & 3u) == 0 && (((uintptr_t)a.q) & 15u) == 0;
+}
+
 int launch_index_score(const IndexArgs& a, hipStream_t st) {
-  if (index_mfma_supported(a)) {
+  if (index_mx4_supported(a)) {
+    if (a.H == 16) launch_mx4<1>(a, st);
+    else if (a.H == 32) launch_mx4<2>(a, st);
+    else launch_mx4<4>(a, st);
+  } else if (index_mfma_supported(a)) {
     if (a.H == 16) launch_mfma_ks<1>(a, st);
     else if (a.H == 32) launch_mfma_ks<2>(a, st);
     else launch_mfma_ks<4>(a, st);
@@ -696,7 +897,8 @@ int launch_index_score(const IndexArgs& a, hipStream_t st) {
     } else {
       if (a.k_dtype == DT_F32) CSA_IDX_VALU(DT_BF16, DT_F32);
       else if (a.k_dtype == DT_BF16) CSA_IDX_VALU(DT_BF16, DT_BF16);
-      else CSA_IDX_VALU(DT_BF16, DT_FP8);
+      else if (a.k_dtype == DT_FP8) CSA_IDX_VALU(DT_BF16, DT_FP8);
+      else CSA_IDX_VALU(DT_BF16, DT_MX4);
     }
 #undef CSA_IDX_VALU
   }

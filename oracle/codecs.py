@@ -124,11 +124,11 @@ def e2m1_code(v) -> np.ndarray:
     """Code of an E2M1-representable value (inverse of ``e2m1_to_f64``; -0.0 -> 8)."""
     v = np.asarray(v, dtype=np.float64)
     mag = np.abs(v)
-    table = e2m1_to_f64(np.arange(8))
-    hits = mag[..., None] == table
-    if not np.all(hits.any(axis=-1)):
+    table = e2m1_to_f64(np.arange(8))           # increasing magnitudes
+    idx = np.minimum(np.searchsorted(table, mag), 7)
+    if not np.all(table[idx] == mag):
         raise ValueError("not an E2M1 value")
-    return (np.argmax(hits, axis=-1) | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+    return (idx | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
 
 
 def mx_quantize_fp4(x) -> tuple[np.ndarray, np.ndarray]:
@@ -165,3 +165,12 @@ def mx_fp4_to_f64(codes, scales) -> np.ndarray:
     n = v.shape[-1]
     sc = e8m0_to_f64(scales)
     return (v.reshape(*v.shape[:-1], n // MX_BLOCK, MX_BLOCK) * sc[..., None]).reshape(v.shape)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """E2M1 codes from bytes holding two each, the even element in the low nibble."""
+    b = np.asarray(packed).astype(np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = b & 15
+    out[..., 1::2] = b >> 4
+    return out

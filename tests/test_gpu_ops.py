@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import codecs as oc
 from oracle import csa as O
 from synth import Gen
 from tests._util import TOL_BF16, TOL_F32, e4m3_ulp, row_rel_err, to_f64
@@ -460,3 +461,92 @@ def test_mqa_unaligned_output_takes_generic_path(csa):
                            n_win=n_win, W_cap=n_win, gamma_q=None, eps=1e-6, sink=None, rope_dim=rope,
                            scale=scale)
         assert row_rel_err(got[b], ref) <= TOL_BF16
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (OCP MX: FP4 E2M1 + E8M0 per 32): compressor output and FP4 indexer
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,N", [(2, 37), (3, 300)])   # workgroup kernel, then the wave kernel
+def test_compress_mxfp4_output_exact_on_unpooled_rows(csa, B, N):
+    """With m = 1 (one candidate: the pooled value is the candidate itself, exactly)
+    fp32 rows are stored as MXFP4 with codes and scale bytes equal to the
+    oracle's OCP MX quantisation, bit for bit."""
+    c = 128
+    g = Gen(180 + N, DEV)
+    x = g.normal(1, (B, N, c), "f32") * torch.exp2(torch.randint(-20, 20, (B, N, 1), device=DEV).float())
+    x[0, 0, :32] = 0.0                                   # a zero block
+    x[0, 1, :] = 2.0 ** torch.arange(-64, 64, device=DEV, dtype=torch.float32)   # powers of two
+    x = x.contiguous()
+    E = torch.zeros((B, N, c // 2), dtype=torch.uint8, device=DEV)
+    S = torch.zeros((B, N, c // 32), dtype=torch.uint8, device=DEV)
+    csa.csa_compress(x, None, None, None, E, T=N, m=1, overlap=0, s_begin=0, s_end=N, E_scale=S)
+    torch.cuda.synchronize()
+    for b in range(B):
+        rc, rs = O.quantize_rows_mxfp4(to_f64(x[b]))
+        assert np.array_equal(S[b].cpu().numpy(), rs), b
+        assert np.array_equal(oc.unpack_fp4(E[b].cpu().numpy()), rc), b
+
+
+@pytest.mark.parametrize("B,T,m", [(3, 400, 4), (2, 2050, 4)])
+def test_compress_mxfp4_output_pooled(csa, B, T, m):
+    """Pooled indexer keys stored as MXFP4: every element is a correct E2M1 rounding
+    of the oracle's value in units of the device's block scale, and the scale
+    bytes match the oracle's except where the block maximum lies within fp32
+    rounding of a power of two."""
+    c = 128
+    g = Gen(185 + T, DEV)
+    Ca, Za, Cb, Zb = (g.normal(i, (B, T, c), "bf16") for i in (1, 2, 3, 4))
+    n = O.num_entries(T, m)
+    E = torch.zeros((B, n, c // 2), dtype=torch.uint8, device=DEV)
+    S = torch.zeros((B, n, c // 32), dtype=torch.uint8, device=DEV)
+    csa.csa_compress(Ca, Za, Cb, Zb, E, T=T, m=m, overlap=1, s_begin=0, s_end=n, E_scale=S)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.compress(*(to_f64(t[b]) for t in (Ca, Za, Cb, Zb)), m=m, overlap=1, T=T, normalize=False)
+        rc, rs = O.quantize_rows_mxfp4(ref)
+        got_s = S[b].cpu().numpy().astype(np.int64)
+        bmax = np.abs(ref).reshape(n, c // 32, 32).max(axis=-1)
+        near = np.abs(np.log2(bmax) - np.round(np.log2(bmax))) < 1e-5
+        assert np.all((got_s == rs) | near)
+        X = np.repeat(np.ldexp(1.0, got_s - 127), 32, axis=-1)
+        y = ref / X
+        dec = oc.e2m1_to_f64(oc.unpack_fp4(E[b].cpu().numpy()))
+        spacing = np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+        err = np.abs(dec - np.clip(y, -6, 6))
+        assert np.all(err <= 0.5 * spacing * (1 + 1e-3) + 1e-6)
+        mism = np.sum(oc.unpack_fp4(E[b].cpu().numpy()) != rc)
+        assert mism <= 1e-3 * rc.size
+
+
+MX_INDEX_CASES = [
+    # name, B, Tq, H, dI, N, m, positions
+    ("mx4_decode_h64", 2, 1, 64, 128, 5000, 4, "all"),
+    ("mx4_decode_h32_tq3_masked", 2, 3, 32, 128, 3001, 4, "partial"),
+    ("mx4_decode_h16_ragged", 1, 2, 16, 128, 999, 1, "all"),
+    ("mx4_generic_prefill_h64", 1, 9, 64, 128, 700, 4, "prefill"),
+    ("mx4_generic_d64_h48", 2, 1, 48, 64, 600, 4, "partial"),
+]
+
+
+@pytest.mark.parametrize("case", MX_INDEX_CASES, ids=[c[0] for c in MX_INDEX_CASES])
+def test_index_score_mxfp4_parity(csa, case):
+    """Random code and scale bytes (any code is an E2M1 value; scales 2^-7 .. 2^3)
+    against the oracle's FP4-QK score, which quantises the bf16 query itself."""
+    name, B, Tq, H, dI, N, m, pmode = case
+    g = Gen(260 + MX_INDEX_CASES.index(case), DEV)
+    qI = g.normal(1, (B, Tq, H, dI), "bf16")
+    w = g.uniform(2, (B, Tq, H))
+    K = (g.uniform(3, (B, N, dI // 2)) * 256).to(torch.uint8).contiguous()
+    Ks = (120 + g.uniform(4, (B, N, dI // 32)) * 11).to(torch.uint8).contiguous()
+    pos = _positions(pmode, B, Tq, N, m, g)
+    I = torch.full((B, Tq, N), float("nan"), dtype=torch.float32, device=DEV)
+    csa.csa_index_score(qI, w, K, pos, I, m=m, K_scale=Ks)
+    torch.cuda.synchronize()
+    got = to_f64(I)
+    for b in range(B):
+        ref = O.index_score_mxfp4(to_f64(qI[b]), to_f64(w[b]), oc.unpack_fp4(K[b].cpu().numpy()),
+                                  Ks[b].cpu().numpy(), to_f64(pos[b]), m=m)
+        assert np.array_equal(np.isneginf(got[b]), np.isneginf(ref)), name
+        fin = np.isfinite(ref)
+        err = row_rel_err(np.where(fin, got[b], 0.0), np.where(fin, ref, 0.0))
+        assert err <= TOL_F32, (name, b, err)
