@@ -18,11 +18,13 @@ ms_per_step); a second pass brackets every step with timing-only events for
 the median and the 10th / 90th percentiles, and times the indexer launch
 inside each step (the roofline's kernel).
 
-Prints ONE JSON line.  Also reported, each against its roofline: the Flash-like
-CSA decode (8 sequences x 16,384 entries, k = 512), the HCA dense decode (4
-sequences x 8,192 entries), the prefill indexer (16,384 queries x 32,768
-entries, bf16) and each call of the chunked-prefill step; and the fp64 oracle
-timed on a bounded sample of the decode workload on the host cores.
+Prints ONE JSON line.  Also reported, each against its roofline: the same 1M
+decode with MXFP4 indexer keys (the FP4 query-key path) and the recall of its
+selection against the fp8 one, the Flash-like CSA decode (8 sequences x 16,384
+entries, k = 512), the HCA dense decode (4 sequences x 8,192 entries), the
+prefill indexer (16,384 queries x 32,768 entries, bf16) and each call of the
+chunked-prefill step; and the fp64 oracle timed on a bounded sample of the
+decode workload on the host cores.
 """
 from __future__ import annotations
 
@@ -215,11 +217,11 @@ def traffic_from_profiles(kernel_tag: str, src_file: str):
 # not counted)
 # ---------------------------------------------------------------------------
 def csa_decode_bytes(wl) -> dict:
-    esz = {"e4m3": 1, "bf16": 2, "f32": 4}
+    esz = {"mxfp4": 0.5, "e4m3": 1, "bf16": 2, "f32": 4}
     kv = esz[wl.dtype]
     B, N, dI, H, k, d = wl.B, wl.N_cap, wl.d_I, wl.H_I, wl.k, wl.d
-    keys = B * N * dI * esz[wl.k_dtype]
-    scales = B * N * 4 if wl.k_dtype == "e4m3" else 0
+    keys = int(B * N * dI * esz[wl.k_dtype])
+    scales = {"e4m3": B * N * 4, "mxfp4": B * N * (dI // 32)}.get(wl.k_dtype, 0)
     q_index = B * (H * dI * 2 + H * 4)
     gather = B * k * d * kv
     window = B * wl.n_win * d * kv
@@ -243,9 +245,10 @@ def hca_decode_bytes(wl) -> dict:
 # workloads
 # ---------------------------------------------------------------------------
 def csa_decode(wl, K: int, warmup: int, use_graph: bool, keep_raw_first: bool = False):
-    """A CSA decode workload: R replicas, whole-step graphs (pass 1) and
-    three-part graphs with events (pass 2: per-step distribution and the
-    indexer's launch time)."""
+    """A CSA decode workload: R replicas, whole-step graphs (pass 1) and the
+    step's three parts launched directly between timing-only events (pass 2:
+    per-step distribution and the indexer's launch time; an event pair around
+    a graph launch would also count the graph's own launch latency)."""
     import torch
 
     from long_context_attention_02_amd.pipeline import CSADecode
@@ -256,12 +259,12 @@ def csa_decode(wl, K: int, warmup: int, use_graph: bool, keep_raw_first: bool = 
     torch.cuda.synchronize()
     steps, err = capture([r.step for r in runs], use_graph)
     ms_step = time_rotating(steps, K, warmup)
-    pre, e1 = capture([r.compress_new for r in runs], use_graph)
-    idx_, e2 = capture([r.index for r in runs], use_graph)
-    post, e3 = capture([(lambda r=r: (r.select(), r.attend())) for r in runs], use_graph)
-    parts = [[pre[r], idx_[r], post[r]] for r in range(R)]
+    parts = [[r.compress_new, r.index, (lambda r=r: (r.select(), r.attend()))] for r in runs]
+    for s in range(warmup):
+        for f in parts[s % R]:
+            f()
     per_step, per_index = time_each(parts, K, inner=1)
-    res = {"workload": wl.name, "replicas": R, "graph": err or e1 or e2 or e3 or "hip graph replay",
+    res = {"workload": wl.name, "replicas": R, "graph": err or "hip graph replay",
            "ms_per_step": ms_step, "step_ms_with_events": dist(per_step),
            "index_ms": dist(per_index), "bytes": ab}
     return res, runs
@@ -280,8 +283,8 @@ def hca_decode(K: int, warmup: int, use_graph: bool):
     runs = [HCADecode(wl, "cuda", keep_raw=False) for _ in range(R)]
     steps, err = capture([r.step for r in runs], use_graph)
     ms_step = time_rotating(steps, K, warmup)
-    pre, _ = capture([r.compress_new for r in runs], use_graph)
-    att, _ = capture([r.attend for r in runs], use_graph)
+    pre = [r.compress_new for r in runs]
+    att = [r.attend for r in runs]
     per_step, per_attn = time_each([[pre[r], att[r]] for r in range(R)], K, inner=1)
     pre_ms = [a - b for a, b in zip(per_step, per_attn)]
     n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
@@ -420,7 +423,7 @@ def main():
         sys.exit(2)
     import torch
 
-    from synth.workloads import CSA_DECODE_1M as wl, CSA_DECODE_FLASH
+    from synth.workloads import CSA_DECODE_1M as wl, CSA_DECODE_1M_MX4, CSA_DECODE_FLASH
 
     torch.cuda.set_device(0)
     use_graph = not args.no_graph
@@ -472,10 +475,34 @@ def main():
         result["copy_calibration_bytes_each_way"] = 512 << 20
         del src_t, dst_t
     keep = runs[0] if not args.no_cpu_baseline else None
+    fp8_idx = runs[0].idx[:, 0].cpu()
     del runs
     capture.keep.clear()
     torch.cuda.empty_cache()
     if not args.no_secondary:
+        # the same step with MXFP4 indexer keys (the FP4 query-key path); its
+        # selection against the fp8 selection of the same underlying keys
+        mx, mx_runs = csa_decode(CSA_DECODE_1M_MX4, K, args.warmup, use_graph)
+        mx_idx = mx_runs[0].idx[:, 0].cpu()
+        del mx_runs
+        capture.keep.clear()
+        torch.cuda.empty_cache()
+        recall = [len(set(fp8_idx[b].tolist()) & set(mx_idx[b].tolist())) / wl.k for b in range(wl.B)]
+        mms = mx["ms_per_step"]
+        mab = mx["bytes"]
+        mx_idx_ms = mx["index_ms"]["mean"]
+        result["csa_decode_mxfp4"] = {
+            "workload": mx["workload"], "replicas": mx["replicas"], "graph": mx["graph"],
+            "ms_per_step": round(mms, 5), "tokens/s": round(wl.B / (mms * 1e-3), 1),
+            "step_ms_with_events": mx["step_ms_with_events"], "index_ms": mx["index_ms"],
+            "algorithmic_bytes": mab,
+            "roofline": _roof(mab["index_kernel"] / (mx_idx_ms * 1e-3) / 1e9, "hbm",
+                              kernel="index_mx4_decode (csa_index_score, MXFP4 keys)"),
+            "step_roofline": _roof(mab["step"] / (mms * 1e-3) / 1e9, "hbm", scope="whole step"),
+            "recall_at_k_vs_fp8_selection": {"mean": round(sum(recall) / len(recall), 5),
+                                             "min": round(min(recall), 5), "k": wl.k,
+                                             "note": "synthetic N(0,1) keys and queries; the pages' "
+                                                     "recall figure is for trained weights"}}
         fl, fl_runs = csa_decode(CSA_DECODE_FLASH, K, args.warmup, use_graph)
         del fl_runs
         capture.keep.clear()

@@ -78,8 +78,17 @@ class CSADecode(_Common):
         self.E = torch.empty((B, N, d), dtype=_TD[wl.dtype], device=self.dev)
         self._fill_entries(self.E, kv_raw, m, True, True)
         self.kv_raw = kv_raw if keep_raw else None
+        self.KI_raw = None
         if wl.k_dtype == "e4m3":
             self.KI, self.KI_scale = g.normal_e4m3(W_.T_KI, (B, N, wl.d_I))
+        elif wl.k_dtype == "mxfp4":
+            # fp32 rows stored as MXFP4 by the compressor with m = 1 (pooling is the identity)
+            raw = g.normal(W_.T_KI, (B, N, wl.d_I), "f32")
+            self.KI = torch.empty((B, N, wl.d_I // 2), dtype=torch.uint8, device=self.dev)
+            self.KI_scale = torch.empty((B, N, wl.d_I // 32), dtype=torch.uint8, device=self.dev)
+            csa_compress(raw, None, None, None, self.KI, T=N, m=1, overlap=0, s_begin=0, s_end=N,
+                         E_scale=self.KI_scale)
+            self.KI_raw = raw if keep_raw else None
         else:
             self.KI, self.KI_scale = g.normal(W_.T_KI, (B, N, wl.d_I), wl.k_dtype), None
         self._window_setup(g, wl, i - wl.n_win + 1, wl.n_win, W_.T_WINRAW)

@@ -26,7 +26,7 @@ from typing import Callable
 import numpy as np
 
 from . import csa as O
-from .codecs import e4m3_to_f64, f64_to_bf16_value
+from .codecs import e4m3_to_f64, f64_to_bf16_value, mx_fp4_to_f64
 
 
 def _store(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -57,7 +57,9 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     and its attention output is still defined exactly.
 
     p holds: i, m, N, k, n_win, d_I, rope_dim, rope_base, eps, scale, dtype, k_dtype;
-    KI (N x d_I fp64, fp8 keys already times their scale), win_raw (n_win x d,
+    KI (N x d_I fp64, fp8 keys already times their scale; for MXFP4 keys
+    instead KI_codes (N x d_I E2M1 codes) and KI_scales (N x d_I / 32 E8M0
+    codes), scored on the FP4 query-key path), win_raw (n_win x d,
     tokens i-n_win+1..i), Ca/Za/Cb/Zb (2m x d, tokens m(N-2)..mN-1),
     ICa/IZa/ICb/IZb (2m x d_I), qI (H x d_I), w (H), q (n_h x d), sink (n_h).
     kv_raw_rows(s) returns the pre-norm rows of entries s.
@@ -72,15 +74,22 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     e_new = _store(e_new, p["dtype"])
     k_new = O.compress(p["ICa"], p["IZa"], p["ICb"], p["IZb"], m=m, overlap=1, T=T, tok_base=tok_base,
                        s_begin=N - 1, s_end=N, normalize=False)
-    if p["k_dtype"] == "e4m3":
-        codes, sc = O.quantize_rows_e4m3(k_new)
-        k_new = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
+    if p["k_dtype"] == "mxfp4":
+        kc, ks = O.quantize_rows_mxfp4(k_new)
+        KIc, KIs = p["KI_codes"].copy(), p["KI_scales"].copy()
+        KIc[N - 1], KIs[N - 1] = kc[0], ks[0]
+        k_new = mx_fp4_to_f64(kc, ks)
+        I = O.index_score_mxfp4(p["qI"][None], p["w"][None], KIc, KIs, [i], m=m)
     else:
-        k_new = _store(k_new, p["k_dtype"])
-    KI = p["KI"].copy()
-    KI[N - 1] = k_new[0]
-    # index, top-k
-    I = O.index_score(p["qI"][None], p["w"][None], KI, [i], m=m)
+        if p["k_dtype"] == "e4m3":
+            codes, sc = O.quantize_rows_e4m3(k_new)
+            k_new = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
+        else:
+            k_new = _store(k_new, p["k_dtype"])
+        KI = p["KI"].copy()
+        KI[N - 1] = k_new[0]
+        I = O.index_score(p["qI"][None], p["w"][None], KI, [i], m=m)
+    # top-k
     idx, vals = O.topk(I, [i], m=m, k=k)
     # rows the query reads
     use = idx[0] if attend_idx is None else np.asarray(attend_idx, dtype=np.int64)

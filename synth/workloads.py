@@ -26,7 +26,7 @@ class Workload:
     wid: int
     kind: str            # "csa" (top-k sparse) or "hca" (dense)
     dtype: str           # storage of q, entries, window rows, outputs: "f32" | "bf16"
-    k_dtype: str         # indexer key storage: "f32" | "bf16" | "e4m3"
+    k_dtype: str         # indexer key storage: "f32" | "bf16" | "e4m3" | "mxfp4"
     B: int
     ctx: int             # tokens present before the first query (decode) / total (prefill)
     Tq: int              # queries per sequence
@@ -91,4 +91,10 @@ CSA_DECODE_1M = Workload(
     B=16, ctx=1048576, Tq=1, q_pos0=1048576, m=4, N_cap=262144, d=512, rope_dim=64, n_h=128,
     H_I=64, d_I=128, k=1024, n_win=128, W_cap=128)
 
-WORKLOADS = {w.name: w for w in (TINY, CSA_DECODE_FLASH, HCA_DECODE, CSA_PREFILL_PRO, CSA_DECODE_1M)}
+# the same workload with the indexer keys in MXFP4 (the FP4 query-key path); same
+# seeds as the fp8-key workload, so the two selections can be compared
+CSA_DECODE_1M_MX4 = CSA_DECODE_1M.scaled(name="csa_decode_pro_b16_ctx1M_mxfp4keys", k_dtype="mxfp4",
+                                         notes="fp32 N(0,1) keys stored as OCP MXFP4")
+
+WORKLOADS = {w.name: w for w in (TINY, CSA_DECODE_FLASH, HCA_DECODE, CSA_PREFILL_PRO, CSA_DECODE_1M,
+                                 CSA_DECODE_1M_MX4)}

@@ -21,12 +21,19 @@ def _raw_rows(raw_b: torch.Tensor):
 def csa_decode_params(run, b: int):
     """(p, kv_raw_rows) of sequence b of a CSADecode run, for oracle.steps.csa_decode_sequence."""
     wl = run.wl
-    KI = to_f64(run.KI[b])
-    if run.KI_scale is not None:
-        KI = KI * to_f64(run.KI_scale[b])[:, None]
+    keys = {}
+    if wl.k_dtype == "mxfp4":
+        # the oracle quantises the raw fp32 keys itself (never the device's cache bytes)
+        from oracle import csa as O
+        keys["KI_codes"], keys["KI_scales"] = O.quantize_rows_mxfp4(to_f64(run.KI_raw[b]))
+    else:
+        KI = to_f64(run.KI[b])
+        if run.KI_scale is not None:
+            KI = KI * to_f64(run.KI_scale[b])[:, None]
+        keys["KI"] = KI
     p = dict(i=run.i, m=wl.m, N=wl.N_cap, k=wl.k, n_win=wl.n_win, d_I=wl.d_I, rope_dim=wl.rope_dim,
              rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.dtype, k_dtype=wl.k_dtype,
-             KI=KI, win_raw=to_f64(run.win_raw[b]),
+             **keys, win_raw=to_f64(run.win_raw[b]),
              Ca=to_f64(run.Ca[b]), Za=to_f64(run.Za[b]), Cb=to_f64(run.Cb[b]), Zb=to_f64(run.Zb[b]),
              ICa=to_f64(run.ICa[b]), IZa=to_f64(run.IZa[b]), ICb=to_f64(run.ICb[b]),
              IZb=to_f64(run.IZb[b]), qI=to_f64(run.qI[b, 0]), w=to_f64(run.wI[b, 0]),
@@ -86,6 +93,17 @@ def new_key_slack(qI: np.ndarray, w: np.ndarray, k_new: np.ndarray, k_dtype: str
         return 0.0
     if k_dtype == "bf16":
         return float(score_slack(qI, w, k_new[None])[0])
+    if k_dtype == "mxfp4":
+        # an E2M1 spacing per element at its block scale (doubled: near a power of two
+        # the block scale itself may differ by one step), against the MXFP4 query
+        from oracle import codecs as oc
+        qc, qs = oc.mx_quantize_fp4(qI)
+        qq = oc.mx_fp4_to_f64(qc, qs)
+        kc, ks = oc.mx_quantize_fp4(k_new.astype(np.float32).astype(np.float64))
+        X = np.repeat(oc.e8m0_to_f64(ks), 32, axis=-1)
+        y = np.abs(k_new) / X
+        ulp = 2.0 * np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0)) * X
+        return float((np.abs(w)[:, None] * np.abs(qq)).sum(axis=0) @ ulp)
     from tests._util import e4m3_ulp
     sc = np.max(np.abs(k_new)) / 448.0
     ulp = e4m3_ulp(k_new / sc) * sc if sc > 0 else np.zeros_like(k_new)

@@ -598,6 +598,8 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
     from oracle.codecs import e4m3_to_f64
     rng = np.random.default_rng(11)
     m, N, c, dI, H, n_h, k, n_win, r = 4, 24, 16, 8, 3, 2, 7, 6, 4
+    if k_dtype == "mxfp4":
+        dI = 32                       # one MX block per key
     i = m * N
     T = m * N                         # tokens that feed entries; the query's own token is i
     C = {n: rng.standard_normal((T, c)) for n in ("Ca", "Za", "Cb", "Zb")}
@@ -612,25 +614,37 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
     E = _store_like(O.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, eps=eps,
                                rope_dim=r, rope_base=base), dtype)
     K = O.compress(IC["ICa"], IC["IZa"], IC["ICb"], IC["IZb"], m=m, overlap=1, T=T, normalize=False)
-    if k_dtype == "e4m3":
+    if k_dtype == "mxfp4":
+        Kc, Ks = O.quantize_rows_mxfp4(K)
+    elif k_dtype == "e4m3":
         codes, sc = O.quantize_rows_e4m3(K)
         K = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
     else:
         K = _store_like(K, k_dtype)
     W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, eps=eps, rope_dim=r,
                                rope_base=base, pos_stride=1), dtype)
-    I = O.index_score(qI[None], w[None], K, [i], m=m)
+    if k_dtype == "mxfp4":
+        I = O.index_score_mxfp4(qI[None], w[None], Kc, Ks, [i], m=m)
+    else:
+        I = O.index_score(qI[None], w[None], K, [i], m=m)
     idx, _ = O.topk(I, [i], m=m, k=k)
     out = O.sparse_mqa(q[None], E, idx, W, q_pos=[i], n_win=n_win, eps=eps, sink=sink, rope_dim=r,
                        rope_base=base, scale=scale)[0]
     # the step: cached rows, a stale newest entry and key, the newest blocks' candidates
     pre = O.pool_entries(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T)
     pre[N - 1] = 1e3 * rng.standard_normal(c)        # stale: must not be read
-    KI = K.copy()
-    KI[N - 1] = 1e3 * rng.standard_normal(dI)        # stale: replaced by the step's own key
+    if k_dtype == "mxfp4":
+        KIc, KIs = Kc.copy(), Ks.copy()
+        KIc[N - 1], KIs[N - 1] = 7, 140              # stale: replaced by the step's own key
+        keys = dict(KI_codes=KIc, KI_scales=KIs)
+        K = oc.mx_fp4_to_f64(Kc, Ks)
+    else:
+        KI = K.copy()
+        KI[N - 1] = 1e3 * rng.standard_normal(dI)    # stale: replaced by the step's own key
+        keys = dict(KI=KI)
     tb = m * (N - 2)
     p = dict(i=i, m=m, N=N, k=k, n_win=n_win, d_I=dI, rope_dim=r, rope_base=base, eps=eps, scale=scale,
-             dtype=dtype, k_dtype=k_dtype, KI=KI, win_raw=win_raw[i - n_win + 1:],
+             dtype=dtype, k_dtype=k_dtype, **keys, win_raw=win_raw[i - n_win + 1:],
              **{n: v[tb:] for n, v in C.items()}, **{n: v[tb:] for n, v in IC.items()},
              qI=qI, w=w, q=q, sink=sink)
     got = steps_mod.csa_decode_sequence(p, lambda s: pre[np.asarray(s)])
@@ -670,7 +684,8 @@ def _hca_decode_pin(steps_mod, dtype="bf16"):
     np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("dtype,k_dtype", [("bf16", "e4m3"), ("bf16", "bf16"), ("f32", "f32")])
+@pytest.mark.parametrize("dtype,k_dtype", [("bf16", "e4m3"), ("bf16", "bf16"), ("f32", "f32"),
+                                           ("bf16", "mxfp4")])
 def test_csa_decode_step_equals_whole_sequence(dtype, k_dtype):
     from oracle import steps
     _csa_decode_pin(steps, dtype, k_dtype)
