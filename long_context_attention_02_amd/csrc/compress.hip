@@ -24,6 +24,8 @@
 // candidates per entry (CSA m = 4, window rows) take the wave-per-entry kernel
 // below instead: no LDS, no barriers.  The choice depends on the job alone, so
 // a job gives the same result in any batch.
+#include <algorithm>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -53,6 +55,80 @@ struct CompressBatch {
 // tokens present in sequence b: T, or T_len[b] clamped to [0, T]
 __device__ __forceinline__ long long seq_tokens(const CompressJob& J, int b) {
   return J.T_len ? min(J.T, max(0LL, (long long)J.T_len[b])) : J.T;
+}
+
+// RMSNorm over the c channels of the pooled row (row[] in LDS; ss = this
+// thread's share of the sum of squares), RoPE on the last rope_dim channels,
+// then the store in the output format; NT threads, channel j in thread j mod NT
+template <int ODT, int NT>
+__device__ __forceinline__ void compress_store(const CompressJob& J, long long s, int b, const float* row,
+                                               float ss, float* red, const float* gj, const float* gp) {
+  constexpr int OPT = (1024 + NT - 1) / NT;
+  void* __restrict__ E = J.E;
+  float* __restrict__ E_scale = J.E_scale;
+  const float* __restrict__ gamma = J.gamma;
+  const long long pos_stride = J.pos_stride, pos_offset = J.pos_offset, out_bs = J.out_bs;
+  const long long out_ring = J.out_ring;
+  const RopeRatio rope = J.rope;
+  const float eps = J.eps;
+  const int c = J.c, rope_dim = J.rope_dim;
+  // ---- RMSNorm over the c channels
+  float rinv = 1.f;
+  if (gamma) {
+    const float tot = block_reduce<false>(ss, red);
+    rinv = 1.f / sqrtf(tot / (float)c + eps);
+  }
+  __syncthreads();
+
+  // ---- RoPE on the last rope_dim channels, pairs (2u, 2u+1); then store
+  const long long pos = pos_stride * s + pos_offset;
+  const long long orow = out_ring > 0 ? (s % out_ring) : s;
+  const size_t obase = (size_t)b * (size_t)out_bs + (size_t)orow * (size_t)c;
+  const int rbeg = c - rope_dim;
+  float amax = 0.f;
+  float outv[OPT];
+  int nv = 0;
+  for (int j = threadIdx.x; j < c; j += NT, ++nv) {
+    float v = row[j] * rinv * gj[nv];
+    if (j >= rbeg) {
+      const int u = (j - rbeg) >> 1;
+      float cs, sn;
+      rope_cos_sin(pos, u, rope, &cs, &sn);
+      const float other = row[j ^ 1] * rinv * gp[nv];
+      v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+    }
+    outv[nv] = v;
+    amax = fmaxf(amax, fabsf(v));
+  }
+  if constexpr (ODT == DT_FP8) {
+    const float am = block_reduce<true>(amax, red);
+    const float scale = am > 0.f ? am / 448.0f : 1.0f;
+    nv = 0;
+    for (int j = threadIdx.x; j < c; j += NT, ++nv)
+      ((uint8_t*)E)[obase + j] = f32_to_e4m3(outv[nv] / scale);
+    if (threadIdx.x == 0) E_scale[(size_t)b * (size_t)(out_bs / c) + (size_t)orow] = scale;
+  } else if constexpr (ODT == DT_MX4) {
+    // MXFP4: channel j sits in thread j (c % 32 == 0, so a 32-channel block is
+    // 32 consecutive lanes of one wave): block maximum by lane exchange, codes,
+    // the even channel's thread writes the byte of the pair, the block's first
+    // thread its scale byte
+    nv = 0;
+    for (int j = threadIdx.x; j < c; j += NT, ++nv) {
+      float a = fabsf(outv[nv]);
+#pragma unroll
+      for (int x = 1; x < 32; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
+      const int se = mx4_shared_exp(a);
+      const uint32_t code = f32_to_e2m1(ldexpf(outv[nv], -se));
+      const uint32_t other = (uint32_t)__shfl_xor((int)code, 1, 64);
+      if ((j & 1) == 0) ((uint8_t*)E)[(obase + j) / 2] = (uint8_t)(code | (other << 4));
+      if ((j & 31) == 0)
+        ((uint8_t*)E_scale)[((size_t)b * (size_t)(out_bs / c) + (size_t)orow) * (size_t)(c / 32) + j / 32] =
+            (uint8_t)(se + 127);
+    }
+  } else {
+    nv = 0;
+    for (int j = threadIdx.x; j < c; j += NT, ++nv) store_from_f32<ODT>(E, obase + j, outv[nv]);
+  }
 }
 
 template <int IDT, int ODT>
@@ -199,63 +275,7 @@ __device__ __forceinline__ void compress_entry(const CompressJob& J, float* smem
     ss += v * v;
   }
 
-  // ---- RMSNorm over the c channels
-  float rinv = 1.f;
-  if (gamma) {
-    const float tot = block_reduce<false>(ss, red);
-    rinv = 1.f / sqrtf(tot / (float)c + eps);
-  }
-  __syncthreads();
-
-  // ---- RoPE on the last rope_dim channels, pairs (2u, 2u+1); then store
-  const long long pos = pos_stride * s + pos_offset;
-  const long long orow = out_ring > 0 ? (s % out_ring) : s;
-  const size_t obase = (size_t)b * (size_t)out_bs + (size_t)orow * (size_t)c;
-  const int rbeg = c - rope_dim;
-  float amax = 0.f;
-  float outv[OPT];
-  int nv = 0;
-  for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) {
-    float v = row[j] * rinv * gj[nv];
-    if (j >= rbeg) {
-      const int u = (j - rbeg) >> 1;
-      float cs, sn;
-      rope_cos_sin(pos, u, rope, &cs, &sn);
-      const float other = row[j ^ 1] * rinv * gp[nv];
-      v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
-    }
-    outv[nv] = v;
-    amax = fmaxf(amax, fabsf(v));
-  }
-  if constexpr (ODT == DT_FP8) {
-    const float am = block_reduce<true>(amax, red);
-    const float scale = am > 0.f ? am / 448.0f : 1.0f;
-    nv = 0;
-    for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv)
-      ((uint8_t*)E)[obase + j] = f32_to_e4m3(outv[nv] / scale);
-    if (threadIdx.x == 0) E_scale[(size_t)b * (size_t)(out_bs / c) + (size_t)orow] = scale;
-  } else if constexpr (ODT == DT_MX4) {
-    // MXFP4: channel j sits in thread j (c % 32 == 0, so a 32-channel block is
-    // 32 consecutive lanes of one wave): block maximum by lane exchange, codes,
-    // the even channel's thread writes the byte of the pair, the block's first
-    // thread its scale byte
-    nv = 0;
-    for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) {
-      float a = fabsf(outv[nv]);
-#pragma unroll
-      for (int x = 1; x < 32; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
-      const int se = mx4_shared_exp(a);
-      const uint32_t code = f32_to_e2m1(ldexpf(outv[nv], -se));
-      const uint32_t other = (uint32_t)__shfl_xor((int)code, 1, 64);
-      if ((j & 1) == 0) ((uint8_t*)E)[(obase + j) / 2] = (uint8_t)(code | (other << 4));
-      if ((j & 31) == 0)
-        ((uint8_t*)E_scale)[((size_t)b * (size_t)(out_bs / c) + (size_t)orow) * (size_t)(c / 32) + j / 32] =
-            (uint8_t)(se + 127);
-    }
-  } else {
-    nv = 0;
-    for (int j = threadIdx.x; j < c; j += COMP_THREADS, ++nv) store_from_f32<ODT>(E, obase + j, outv[nv]);
-  }
+  compress_store<ODT, COMP_THREADS>(J, s, b, row, ss, red, gj, gp);
 }
 
 __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(const CompressBatch jb) {
@@ -502,6 +522,159 @@ __global__ __launch_bounds__(64 * COMPW_WAVES) void compress_wave_kernel(const C
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel: one 1024-thread workgroup per (entry, sequence) for entries of
+// many candidates (HCA blocks of m' = 128 tokens; also the few entries of a
+// decode step).  Thread (token group tg, channel vector cv) owns 16-byte
+// pieces (8 bf16 or 4 fp32 channels) of every TG-th candidate and issues the
+// loads of up to COMPX_TPT candidates at once, so a 128-token block costs one
+// memory latency rather than one per pair of candidates; each thread keeps an
+// online softmax per channel, the TG partials of a channel merge in LDS, and
+// the RMSNorm / RoPE / store epilogue is the one of the kernel above.
+// ---------------------------------------------------------------------------
+static constexpr int COMPX_THREADS = 1024;
+static constexpr int COMPX_TPT = 4;    // candidates per thread whose loads are in flight together
+static constexpr int COMPX_MAXTG = 16; // token groups (bounds the merge of a channel's partials)
+// (1024 threads leave 128 VGPRs a thread; eight candidates in flight spilled)
+
+template <int IDT, int ODT>
+__device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float* smem) {
+  constexpr int VEC = IDT == DT_F32 ? 4 : 8;   // channels per 16-byte piece
+  constexpr int ESZ = IDT == DT_F32 ? 4 : 2;
+  const int c = J.c, m = J.m;
+  const int CV = c / VEC;                      // pieces per row (host: c % VEC == 0, c <= 1024)
+  const int TG = J.G;                          // token groups (host: wide_groups)
+  const long long s = J.s_begin + blockIdx.x;
+  const int b = blockIdx.y;
+  const long long T = seq_tokens(J, b);
+  if ((long long)m * s >= T) return;   // no such entry in this sequence (whole workgroup)
+  const long long a_lo = (long long)m * s, a_hi = min((long long)m * (s + 1), T);
+  long long b_lo = 0, b_hi = 0;
+  if (J.overlap) {
+    b_lo = max((long long)m * (s - 1), 0LL);
+    b_hi = min((long long)m * s, T);
+  }
+  const long long na = max(a_hi - a_lo, 0LL), nb = max(b_hi - b_lo, 0LL);
+  const long long ncand = na + nb;   // >= 1: the entry's block starts below T
+  const size_t base = (size_t)b * (size_t)J.in_bs;
+  float* pm = smem;              // [TG][c] running maxima
+  float* ps = pm + TG * c;       // [TG][c] sums
+  float* pa = ps + TG * c;       // [TG][c] weighted sums
+  float* row = pa + TG * c;      // [c]
+  float* red = row + c;          // [16]
+
+  // gamma of channel tid and of its RoPE partner, loaded with the candidates
+  const float* __restrict__ gsrc = J.gamma ? J.gamma : k_ones.v;
+  const int jc = min((int)threadIdx.x, c - 1);
+  float gj[1] = {gsrc[jc]}, gp[1] = {gsrc[min(jc ^ 1, c - 1)]};
+
+  const int tg = threadIdx.x / CV, cv = threadIdx.x % CV;
+  if (tg < TG) {
+    float mx[VEC], sum[VEC], acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      mx[e] = -INFINITY;
+      sum[e] = 0.f;
+      acc[e] = 0.f;
+    }
+    for (long long q0 = tg; q0 < ncand; q0 += (long long)TG * COMPX_TPT) {
+      u32x4_t xc[COMPX_TPT], zc[COMPX_TPT];
+      bool hz[COMPX_TPT];
+#pragma unroll
+      for (int u = 0; u < COMPX_TPT; ++u) {
+        // unguarded loads (candidate clamped, a missing Z reads C); the extra ones unused
+        const long long q = min(q0 + (long long)u * TG, ncand - 1);
+        const bool in_a = q < na;
+        const long long tok = in_a ? a_lo + q : b_lo + (q - na);
+        const size_t off = (base + (size_t)(tok - J.tok_base) * (size_t)c + (size_t)cv * VEC) * ESZ;
+        const char* Cp = (const char*)(in_a ? J.Ca : J.Cb);
+        const char* Zp = (const char*)(in_a ? J.Za : J.Zb);
+        hz[u] = Zp != nullptr;
+        xc[u] = *(const u32x4_t*)(Cp + off);
+        zc[u] = *(const u32x4_t*)((Zp ? Zp : Cp) + off);
+      }
+      // the round's maximum first, then one rescale of the running sums
+      float bm[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) bm[e] = mx[e];
+#pragma unroll
+      for (int u = 0; u < COMPX_TPT; ++u) {
+        if (q0 + (long long)u * TG >= ncand) break;
+        float z[VEC];
+        unpack_piece<IDT>(zc[u], z);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) bm[e] = fmaxf(bm[e], hz[u] ? z[e] : 0.f);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float r = mx[e] == -INFINITY ? 0.f : __expf(mx[e] - bm[e]);
+        sum[e] *= r;
+        acc[e] *= r;
+        mx[e] = bm[e];
+      }
+#pragma unroll
+      for (int u = 0; u < COMPX_TPT; ++u) {
+        if (q0 + (long long)u * TG >= ncand) break;
+        float x[VEC], z[VEC];
+        unpack_piece<IDT>(xc[u], x);
+        unpack_piece<IDT>(zc[u], z);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float wgt = __expf((hz[u] ? z[e] : 0.f) - mx[e]);
+          sum[e] += wgt;
+          acc[e] += wgt * x[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int j = cv * VEC + e;
+      pm[tg * c + j] = mx[e];
+      ps[tg * c + j] = sum[e];
+      pa[tg * c + j] = acc[e];
+    }
+  }
+  __syncthreads();
+
+  // merge the TG partials of channel j = tid, in group order
+  float ss = 0.f;
+  if ((int)threadIdx.x < c) {
+    const int j = threadIdx.x;
+    float M = -INFINITY;
+#pragma unroll 4
+    for (int q = 0; q < TG; ++q) M = fmaxf(M, pm[q * c + j]);
+    float S = 0.f, A = 0.f;
+#pragma unroll 4
+    for (int q = 0; q < TG; ++q) {
+      const float mq = pm[q * c + j];
+      const float f = mq == -INFINITY ? 0.f : __expf(mq - M);   // a group that saw no candidate adds 0
+      S += ps[q * c + j] * f;
+      A += pa[q * c + j] * f;
+    }
+    const float v = S > 0.f ? A / S : 0.f;
+    row[j] = v;
+    ss = v * v;
+  }
+  __syncthreads();   // row[] complete (the epilogue reads RoPE partners)
+  compress_store<ODT, COMPX_THREADS>(J, s, b, row, ss, red, gj, gp);
+}
+
+__global__ __launch_bounds__(COMPX_THREADS) void compress_wide_kernel(const CompressBatch jb) {
+  extern __shared__ float smem[];
+  const CompressJob& J = jb.job[blockIdx.z];
+  if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
+  switch (J.in_dtype * 4 + J.out_dtype) {
+    case DT_F32 * 4 + DT_F32: compress_entry_wide<DT_F32, DT_F32>(J, smem); break;
+    case DT_F32 * 4 + DT_BF16: compress_entry_wide<DT_F32, DT_BF16>(J, smem); break;
+    case DT_F32 * 4 + DT_FP8: compress_entry_wide<DT_F32, DT_FP8>(J, smem); break;
+    case DT_F32 * 4 + DT_MX4: compress_entry_wide<DT_F32, DT_MX4>(J, smem); break;
+    case DT_BF16 * 4 + DT_F32: compress_entry_wide<DT_BF16, DT_F32>(J, smem); break;
+    case DT_BF16 * 4 + DT_BF16: compress_entry_wide<DT_BF16, DT_BF16>(J, smem); break;
+    case DT_BF16 * 4 + DT_FP8: compress_entry_wide<DT_BF16, DT_FP8>(J, smem); break;
+    default: compress_entry_wide<DT_BF16, DT_MX4>(J, smem); break;
+  }
+}
+
 static size_t compress_lds_bytes(int G, int c) {
   return (size_t)(3 * G * c + c + COMP_THREADS / 64) * sizeof(float);
 }
@@ -523,12 +696,24 @@ static CompressJob make_job(const CompressArgs& x, int G) {
 
 // a job for the wave-per-entry kernel: few candidates per entry, whole 16-byte pieces
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// every input row starts 16-byte aligned (16-byte pieces of the channel axis)
+static bool inputs_in_pieces(const CompressArgs& x) {
+  const int vec = x.in_dtype == DT_F32 ? 4 : 8;
+  return x.c % vec == 0 && aligned16(x.C_a) && (!x.C_b || aligned16(x.C_b)) && (!x.Z_a || aligned16(x.Z_a)) &&
+         (!x.Z_b || aligned16(x.Z_b)) && (x.in_bs * (x.in_dtype == DT_F32 ? 4 : 2)) % 16 == 0;
+}
+// a job for the wide kernel: rows in 16-byte pieces (the choice depends on the
+// job alone, so a job gives the same bytes in any batch)
+static bool wide_job(const CompressArgs& x) { return x.c <= 1024 && inputs_in_pieces(x); }
+// token groups of a wide job: enough for its candidates, at most COMPX_MAXTG
+static int wide_groups(int c, int vec, int ncand_max) {
+  return std::max(1, std::min(std::min(COMPX_THREADS / (c / vec), COMPX_MAXTG), ncand_max));
+}
 static bool wave_job(const CompressArgs& x) {
   const int ncand_max = x.overlap ? 2 * x.m : x.m;
   const int vec = x.in_dtype == DT_F32 ? 4 : 8;
   // 16-byte pieces: every input row and (for bf16 output) every output row starts 16-byte aligned
-  const bool in_al = aligned16(x.C_a) && (!x.C_b || aligned16(x.C_b)) && (!x.Z_a || aligned16(x.Z_a)) &&
-                     (!x.Z_b || aligned16(x.Z_b)) && (x.in_bs * (x.in_dtype == DT_F32 ? 4 : 2)) % 16 == 0;
+  const bool in_al = inputs_in_pieces(x);
   const bool out_al = (x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0)) &&
                       (x.out_dtype != DT_MX4 || ((uintptr_t)x.E & 3u) == 0);
   // a job of a few dozen entries (decode) is pure latency, where one workgroup per
@@ -555,16 +740,46 @@ int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
     if (blocks > 2147483647LL) return -1;
     hipLaunchKernelGGL(compress_wave_kernel<COMPW_MAXC>, dim3((unsigned)blocks), dim3(64 * COMPW_WAVES), 0,
                        st, wb);
-    if (nw == n_jobs) return hipGetLastError() == hipSuccess ? 0 : -1;
   }
-  // the rest (HCA blocks of many candidates): one workgroup per entry
+  // jobs whose rows come in 16-byte pieces: one 1024-thread workgroup per entry
+  auto to_wide = [&](const CompressArgs& x) { return !wave_job(x) && wide_job(x); };
+  {
+    CompressBatch xb{};
+    size_t lds = 0;
+    long long gx = 1;
+    int gy = 1;
+    int nx = 0;
+    for (int q = 0; q < n_jobs; ++q) {
+      if (!to_wide(a[q])) continue;
+      const CompressArgs& x = a[q];
+      const int vec = x.in_dtype == DT_F32 ? 4 : 8;
+      xb.job[nx] = make_job(x, wide_groups(x.c, vec, x.overlap ? 2 * x.m : x.m));
+      const int TG = wide_groups(x.c, vec, x.overlap ? 2 * x.m : x.m);
+      const size_t l = (size_t)(3 * TG * x.c + x.c + 16) * sizeof(float);
+      if (l > lds) lds = l;
+      if (xb.job[nx].n_entries > gx) gx = xb.job[nx].n_entries;
+      if (x.B > gy) gy = x.B;
+      ++nx;
+    }
+    if (nx > 0) {
+      if (gx > 2147483647LL || gy > 65535) return -1;
+      if (lds > 65536 && hipFuncSetAttribute((const void*)compress_wide_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)lds) != hipSuccess)
+        return -1;
+      hipLaunchKernelGGL(compress_wide_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)nx),
+                         dim3(COMPX_THREADS), lds, st, xb);
+    }
+    if (nw + nx == n_jobs) return hipGetLastError() == hipSuccess ? 0 : -1;
+  }
+  // the rest (rows not in 16-byte pieces): one 512-thread workgroup per entry
   CompressBatch jb{};
   size_t lds = 0;
   long long gx = 1;
   int gy = 1;
   int nb = 0;
   for (int q0 = 0; q0 < n_jobs; ++q0) {
-    if (wave_job(a[q0])) continue;
+    if (wave_job(a[q0]) || to_wide(a[q0])) continue;
     const int q = nb++;
     const CompressArgs& x = a[q0];
     const int ncand_max = x.overlap ? 2 * x.m : x.m;
