@@ -861,3 +861,59 @@ def test_mx_planted_mistakes_are_caught(monkeypatch):
         mp.setattr(oc, "f64_to_e2m1_value", ties_away)
         with pytest.raises(AssertionError):
             test_e2m1_rne_matches_brute_force()
+
+
+# ---------------------------------------------------------------------------
+# grouped output projection (method page §3.3)
+# ---------------------------------------------------------------------------
+def test_grouped_projection_equals_block_diagonal_matmul():
+    """The grouped down-projection equals one product with a block-diagonal
+    matrix built from the groups' matrices; g = 1 is two plain products."""
+    from oracle.proj import grouped_output_projection as gop
+    rng = np.random.default_rng(41)
+    T, g, Wq, d_g, d = 5, 4, 6, 3, 7
+    o = rng.standard_normal((T, g * Wq))
+    W1 = rng.standard_normal((g, d_g, Wq))
+    W2 = rng.standard_normal((d, g * d_g))
+    y, out = gop(o, W1, W2, groups=g, y_dtype="f64")
+    big = np.zeros((g * d_g, g * Wq))
+    for q in range(g):
+        big[q * d_g:(q + 1) * d_g, q * Wq:(q + 1) * Wq] = W1[q]
+    np.testing.assert_allclose(y, o @ big.T, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out, (o @ big.T) @ W2.T, rtol=1e-12, atol=1e-12)
+    # g = 1: two plain products
+    W1one = rng.standard_normal((1, d_g, g * Wq))
+    y1, out1 = gop(o, W1one, W2[:, :d_g], groups=1, y_dtype="f64")
+    np.testing.assert_allclose(y1, o @ W1one[0].T, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(out1, (o @ W1one[0].T) @ W2[:, :d_g].T, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_projection_brute_force_and_bf16_intermediate():
+    from oracle.codecs import f64_to_bf16_value
+    from oracle.proj import grouped_output_projection as gop
+    rng = np.random.default_rng(42)
+    T, g, Wq, d_g, d = 2, 3, 4, 2, 3
+    o, W1, W2 = rng.standard_normal((T, g * Wq)), rng.standard_normal((g, d_g, Wq)), rng.standard_normal((d, g * d_g))
+    y, out = gop(o, W1, W2, groups=g)
+    for t in range(T):
+        yb = []
+        for q in range(g):
+            for e in range(d_g):
+                yb.append(sum(o[t, q * Wq + i] * W1[q, e, i] for i in range(Wq)))
+        yb = f64_to_bf16_value(np.array(yb))
+        assert np.array_equal(y[t], yb)
+        for n in range(d):
+            assert abs(out[t, n] - sum(yb[u] * W2[n, u] for u in range(g * d_g))) < 1e-12
+
+
+def test_grouped_projection_planted_group_mixup_is_caught(monkeypatch):
+    """A projection that gives group q the columns of group g-1-q fails the pins."""
+    import oracle.proj as P
+    real = P.grouped_output_projection
+
+    def mixed(o, W1, W2, *, groups, y_dtype="bf16"):
+        return real(o, W1[::-1].copy(), W2, groups=groups, y_dtype=y_dtype)
+    with monkeypatch.context() as mp:
+        mp.setattr(P, "grouped_output_projection", mixed)
+        with pytest.raises(AssertionError):
+            test_grouped_projection_equals_block_diagonal_matmul()
