@@ -22,9 +22,10 @@ Prints ONE JSON line.  Also reported, each against its roofline: the same 1M
 decode with MXFP4 indexer keys (the FP4 query-key path) and the recall of its
 selection against the fp8 one, the Flash-like CSA decode (8 sequences x 16,384
 entries, k = 512), the HCA dense decode (4 sequences x 8,192 entries), the
-prefill indexer (16,384 queries x 32,768 entries, bf16) and each call of the
-chunked-prefill step; and the fp64 oracle timed on a bounded sample of the
-decode workload on the host cores.
+prefill indexer (16,384 queries x 32,768 entries, bf16), each call of the
+chunked-prefill step and the grouped output projection (prefill and decode
+rows); and the fp64 oracle timed on a bounded sample of the decode workload on
+the host cores.
 """
 from __future__ import annotations
 
@@ -389,6 +390,50 @@ def prefill_rows(steps: int, warmup: int):
     return out
 
 
+def grouped_out_proj(steps: int, warmup: int):
+    """The grouped output projection of the Pro-like attention outputs: 128 heads x 512
+    in 16 groups, each projected to 1,024, then the 16,384-wide concatenation to 7,168.
+    At 16,384 rows (a prefill chunk) against the bf16 MFMA peak; at 16 rows (a decode
+    step) against HBM, since the 369 MB of weights dominate (two weight replicas
+    alternate, so the Infinity Cache cannot hold them)."""
+    import torch
+
+    import long_context_attention_02_amd as csa
+    from synth import Gen
+
+    n_h, c, G, d_g, d = 128, 512, 16, 1024, 7168
+    W = n_h * c // G
+    g = Gen(7, "cuda")
+    weights = [((g.normal(2 + 10 * r, (G, d_g, W), "f32", per_slot=False) / W ** 0.5).to(torch.bfloat16),
+                (g.normal(3 + 10 * r, (d, G * d_g), "f32", per_slot=False) / (G * d_g) ** 0.5).to(torch.bfloat16))
+               for r in range(2)]
+    wbytes = (G * d_g * W + d * G * d_g) * 2
+    out = {"shape": {"heads": n_h, "head_dim": c, "groups": G, "d_g": d_g, "d": d}}
+    for T, label in ((16384, "prefill_16384_rows"), (16, "decode_16_rows")):
+        o = g.normal(1, (T, n_h, c), "bf16", per_slot=False)
+        y = torch.empty((T, G * d_g), dtype=torch.bfloat16, device="cuda")
+        res = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(csa.csa_out_proj_workspace_size(T, n_h, c, G, d_g, d), 1), dtype=torch.uint8,
+                         device="cuda")
+        calls = [(lambda W1=W1, W2=W2: csa.csa_grouped_out_proj(o, W1, W2, y, res, workspace=ws))
+                 for W1, W2 in weights]
+        it = iter(range(10 ** 9))
+        per = _timed(lambda: calls[next(it) % 2](), steps, warmup)
+        ms = _pct(per, 0.5)
+        flops = 2.0 * T * (n_h * c * d_g + G * d_g * d)
+        nbytes = wbytes + (T * n_h * c + 2 * T * G * d_g + T * d) * 2
+        entry = {"ms": dist(per), "flops": flops, "bytes": nbytes,
+                 "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+        entry["roofline"] = (_roof(flops / (ms * 1e-3) / 1e12, "mfma") if T > 64
+                             else _roof(nbytes / (ms * 1e-3) / 1e9, "hbm"))
+        out[label] = entry
+        del o, y, res, ws
+        torch.cuda.empty_cache()
+    del weights
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(run, seconds: float):
     """The fp64 oracle on all sequences of the same decode step, repeated until
     `seconds` of host time have passed (at least once)."""
@@ -515,6 +560,7 @@ def main():
             "algorithmic_bytes": fl["bytes"]["step"],
             "roofline": _roof(fl["bytes"]["step"] / (fms * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["hca_decode"] = hca_decode(K, args.warmup, use_graph)
+        result["grouped_out_proj"] = grouped_out_proj(steps=20, warmup=3)
     if not args.no_prefill:
         if keep is not None:
             keep.I = None

@@ -236,6 +236,32 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
                   void* stream);
 
 /*
+ * Grouped output projection of the attention outputs (method page §3.3:
+ * because c * n_h is large, the output projection is grouped -- each group of
+ * heads is projected down to d_g, the results are concatenated and projected
+ * back to d).  For each of T rows (queries):
+ *   y[t, q d_g + e] = sum_i o[t, q W + i] * W1[q, e, i]   (W = n_h c / groups;
+ *                     group q is heads [q n_h / groups, (q+1) n_h / groups)),
+ *   out[t, :]       = y[t, :] @ W2^T.
+ *  o   : [T][n_h][c] bf16 (the attention output, e.g. B * Tq rows).
+ *  W1  : [groups][d_g][W] bf16 (output-major: the input axis contiguous).
+ *  W2  : [d][groups * d_g] bf16 (output-major).
+ *  y   : [T][groups * d_g] bf16, written: the intermediate, rounded to bf16
+ *        (RNE) from the fp32 sums before the second product reads it.
+ *  out : [T][d] bf16, written (fp32 sums, RNE).
+ *  Needs W % 64 == 0 and (groups d_g) % 64 == 0; o, W1, W2 and y 16-byte
+ *  aligned (CSA_E_UNSUPPORTED otherwise).  Few rows (T <= 64) split the
+ *  contraction over workgroups and need a workspace of
+ *  csa_out_proj_workspace_size(...) bytes (16-byte aligned) for the fp32
+ *  partials, which are summed in a fixed order: results do not depend on
+ *  anything but the inputs.
+ */
+size_t csa_out_proj_workspace_size(int T, int n_h, int c, int groups, int d_g, int d);
+int csa_grouped_out_proj(const void* o, const void* W1, const void* W2, void* y, void* out, int T,
+                         int n_h, int c, int groups, int d_g, int d, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/*
  * csa_sparse_mqa without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments (minus workspace and

@@ -20,7 +20,8 @@ __all__ = [
     "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_index_score",
     "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
-    "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES",
+    "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES", "csa_out_proj_workspace_size",
+    "csa_grouped_out_proj",
     "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3", "CSA_MXFP4",
 ]
 
@@ -75,6 +76,10 @@ _lib.csa_sparse_mqa_noalloc.restype = _I
 _lib.csa_sparse_mqa_noalloc.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I,
                                         _I, _F, _F, _I, _P, _P]
 NOALLOC_SCRATCH_BYTES = 16 << 20
+_lib.csa_out_proj_workspace_size.restype = _S
+_lib.csa_out_proj_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+_lib.csa_grouped_out_proj.restype = _I
+_lib.csa_grouped_out_proj.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _S, _P]
 _lib.hca_dense_mqa.restype = _I
 _lib.hca_dense_mqa.argtypes = [_P, _P, _F, _P, _L, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _F,
                                _F, _I, _P, _P, _S, _P]
@@ -285,3 +290,26 @@ def hca_dense_mqa(q, E, W, q_pos, out, *, m: int, n_win: int, sink=None, gamma_q
         _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d, rope_dim, rope_base,
         (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
         _ptr(workspace, "workspace"), ws_bytes, _stream()))
+
+
+def csa_out_proj_workspace_size(T: int, n_h: int, c: int, groups: int, d_g: int, d: int) -> int:
+    return int(_lib.csa_out_proj_workspace_size(T, n_h, c, groups, d_g, d))
+
+
+def csa_grouped_out_proj(o, W1, W2, y, out, *, workspace=None):
+    """Grouped output projection.  o [T, n_h, c] (or [B, Tq, n_h, c]) bf16, W1 [g, d_g, n_h c / g],
+    W2 [d, g d_g], y [T, g d_g] and out [T, d] (written), all bf16."""
+    if o.dim() == 4:
+        o = o.reshape(-1, o.shape[2], o.shape[3])
+    T, n_h, c = o.shape
+    g, d_g, W = W1.shape
+    d = W2.shape[0]
+    if g * W != n_h * c or tuple(W2.shape) != (d, g * d_g):
+        raise ValueError("W1 must be [g, d_g, n_h c / g] and W2 [d, g d_g]")
+    if tuple(y.shape) != (T, g * d_g) or tuple(out.shape) != (T, d):
+        raise ValueError("y must be [T, g d_g] and out [T, d]")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    bf = torch.bfloat16
+    _check(_lib.csa_grouped_out_proj(
+        _ptr(o, "o", bf), _ptr(W1, "W1", bf, 3), _ptr(W2, "W2", bf, 2), _ptr(y, "y", bf, 2),
+        _ptr(out, "out", bf, 2), T, n_h, c, g, d_g, d, _ptr(workspace, "workspace"), ws_bytes, _stream()))

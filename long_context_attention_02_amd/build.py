@@ -14,7 +14,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["compress.hip", "index_score.hip", "topk.hip", "mqa.hip", "csa_abi.hip"]
+SOURCES = ["compress.hip", "index_score.hip", "topk.hip", "mqa.hip", "proj.hip", "csa_abi.hip"]
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -267,6 +267,43 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
   return ok();
 }
 
+static int proj_check(const char* fn, int T, int n_h, int c, int groups, int d_g, int d) {
+  if (T < 1 || n_h < 1 || c < 1 || groups < 1 || d_g < 1 || d < 1)
+    return fail(CSA_E_SHAPE, "%s: sizes must be >= 1", fn);
+  const long long HC = (long long)n_h * c;
+  if (HC % groups) return fail(CSA_E_SHAPE, "%s: n_h * c must be a multiple of groups", fn);
+  if ((HC / groups) % 64 || ((long long)groups * d_g) % 64)
+    return fail(CSA_E_UNSUPPORTED, "%s: n_h c / groups and groups d_g must be multiples of 64", fn);
+  if (HC > 2147483647LL || (long long)groups * d_g > 2147483647LL || T > 65535 * 16)
+    return fail(CSA_E_UNSUPPORTED, "%s: sizes beyond the supported range", fn);
+  return CSA_OK;
+}
+
+size_t csa_out_proj_workspace_size(int T, int n_h, int c, int groups, int d_g, int d) {
+  if (proj_check("csa_out_proj_workspace_size", T, n_h, c, groups, d_g, d) != CSA_OK) return 0;
+  csa::ProjArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, T, n_h, c, groups, d_g, d, nullptr, 0};
+  return csa::proj_workspace_bytes(a);
+}
+
+int csa_grouped_out_proj(const void* o, const void* W1, const void* W2, void* y, void* out, int T, int n_h,
+                         int c, int groups, int d_g, int d, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "csa_grouped_out_proj";
+  if (!o || !W1 || !W2 || !y || !out) return fail(CSA_E_NULL, "%s: o, W1, W2, y and out are required", fn);
+  int st = proj_check(fn, T, n_h, c, groups, d_g, d);
+  if (st != CSA_OK) return st;
+  const void* ptrs[] = {o, W1, W2, y};
+  for (const void* p : ptrs)
+    if (((uintptr_t)p) & 15u) return fail(CSA_E_UNSUPPORTED, "%s: o, W1, W2 and y must be 16-byte aligned", fn);
+  if (((uintptr_t)out) & 1u) return fail(CSA_E_SHAPE, "%s: out must be 2-byte aligned", fn);
+  csa::ProjArgs a{o, W1, W2, y, out, T, n_h, c, groups, d_g, d, workspace, ws_bytes};
+  const size_t need = csa::proj_workspace_bytes(a);
+  if (need > 0 && (!workspace || ws_bytes < need || (((uintptr_t)workspace) & 15u)))
+    return fail(CSA_E_WORKSPACE, "%s: a 16-byte aligned workspace of %zu bytes is needed, %zu given", fn, need,
+                ws_bytes);
+  if (csa::launch_proj(a, (hipStream_t)stream) != 0) return fail(CSA_E_HIP, "%s: kernel launch failed", fn);
+  return ok();
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------------------

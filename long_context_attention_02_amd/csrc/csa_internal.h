@@ -86,4 +86,17 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
 // returns 0 or a CSA status (UNSUPPORTED / HIP) and fills *why on failure
 int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why);
 
+struct ProjArgs {
+  const void* o;    // [T][n_h c] bf16
+  const void* W1;   // [groups][d_g][n_h c / groups] bf16
+  const void* W2;   // [d][groups d_g] bf16
+  void* y;          // [T][groups d_g] bf16 (intermediate, written)
+  void* out;        // [T][d] bf16
+  int T, n_h, c, groups, d_g, d;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t proj_workspace_bytes(const ProjArgs& a);
+int launch_proj(const ProjArgs& a, hipStream_t st);
+
 }  // namespace csa

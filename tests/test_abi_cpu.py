@@ -183,3 +183,20 @@ def test_mqa_validation(lib):
 
     assert dense() == CSA_E_SHAPE                             # m = 0
     assert dense(m=128, out=None) == CSA_E_NULL
+
+
+def test_grouped_out_proj_validation(lib):
+    def call(**kw):
+        a = dict(o=FAKE, W1=FAKE, W2=FAKE, y=FAKE, out=FAKE, T=16, n_h=128, c=512, g=16, d_g=1024,
+                 d=7168, ws=None, wsb=0, st=None)
+        a.update(kw)
+        return lib.csa_grouped_out_proj(*a.values())
+
+    assert call(o=None) == CSA_E_NULL
+    assert call(g=3) == CSA_E_SHAPE                           # n_h c not a multiple of groups
+    assert call(d_g=1001) == CSA_E_UNSUPPORTED                # groups d_g not a multiple of 64
+    assert call(o=FAKE + 2) == CSA_E_UNSUPPORTED              # unaligned
+    need = lib.csa_out_proj_workspace_size(16, 128, 512, 16, 1024, 7168)
+    assert need > 0                                           # few rows split the contraction
+    assert call() == CSA_E_WORKSPACE
+    assert lib.csa_out_proj_workspace_size(16384, 128, 512, 16, 1024, 7168) == 0

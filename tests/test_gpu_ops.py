@@ -550,3 +550,41 @@ def test_index_score_mxfp4_parity(csa, case):
         fin = np.isfinite(ref)
         err = row_rel_err(np.where(fin, got[b], 0.0), np.where(fin, ref, 0.0))
         assert err <= TOL_F32, (name, b, err)
+
+
+# ---------------------------------------------------------------------------
+# grouped output projection (method page §3.3)
+# ---------------------------------------------------------------------------
+PROJ_CASES = [
+    # name, T, n_h, c, groups, d_g, d
+    ("decode_pro_16x128x512_g16_dg1024_d7168", 16, 128, 512, 16, 1024, 7168),   # split K
+    ("ragged_tiles_T300", 300, 16, 128, 4, 192, 320),                          # 128-row tiles, tails
+    ("split_T40", 40, 64, 128, 8, 256, 512),
+]
+
+
+@pytest.mark.parametrize("case", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_grouped_out_proj_parity(csa, case):
+    from oracle.proj import grouped_output_projection
+    name, T, n_h, c, G, d_g, d = case
+    W = n_h * c // G
+    g = Gen(600 + PROJ_CASES.index(case), DEV)
+    o = g.normal(1, (T, n_h, c), "bf16")
+    W1 = (g.normal(2, (G, d_g, W), "f32") / math.sqrt(W)).to(torch.bfloat16).contiguous()
+    W2 = (g.normal(3, (d, G * d_g), "f32") / math.sqrt(G * d_g)).to(torch.bfloat16).contiguous()
+    y = torch.full((T, G * d_g), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(csa.csa_out_proj_workspace_size(T, n_h, c, G, d_g, d), 1), dtype=torch.uint8,
+                     device=DEV)
+    csa.csa_grouped_out_proj(o, W1, W2, y, out, workspace=ws)
+    torch.cuda.synchronize()
+    ry, rout = grouped_output_projection(to_f64(o).reshape(T, n_h * c), to_f64(W1), to_f64(W2), groups=G)
+    assert row_rel_err(to_f64(y), ry) <= TOL_BF16, name
+    assert row_rel_err(to_f64(out), rout) <= TOL_BF16, name
+    # the second product against the device's own intermediate: only fp32 summation order differs
+    assert row_rel_err(to_f64(out), to_f64(y) @ to_f64(W2).T) <= 1e-2, name
+    # run to run: the same bytes (split partials are summed in a fixed order)
+    out2 = torch.empty_like(out)
+    csa.csa_grouped_out_proj(o, W1, W2, y, out2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
