@@ -917,3 +917,63 @@ def test_grouped_projection_planted_group_mixup_is_caught(monkeypatch):
         mp.setattr(P, "grouped_output_projection", mixed)
         with pytest.raises(AssertionError):
             test_grouped_projection_equals_block_diagonal_matmul()
+
+
+# ---------------------------------------------------------------------------
+# heterogeneous cache maintenance (method page §3.5)
+# ---------------------------------------------------------------------------
+def _cache_tokens(rng, T, c=16, dI=8):
+    tok = {k: rng.standard_normal((T, c)) for k in ("Ca", "Za", "Cb", "Zb", "Ch", "Zh", "Wraw")}
+    tok.update({k: rng.standard_normal((T, dI)) for k in ("ICa", "IZa", "ICb", "IZb")})
+    return tok
+
+
+@pytest.mark.parametrize("chunks", [[1] * 70, [5, 1, 30, 2, 32], [70], [3, 64, 3]])
+def test_incremental_cache_equals_full_recompression(chunks):
+    """Appending tokens in any chunking, with only a ring of lcm(m, m') raw rows
+    kept for the unfinished blocks, gives the caches that compressing the whole
+    sequence gives (m = 4, m' = 16, so lcm = 16 and the ring wraps)."""
+    from oracle import cache as Cc
+    rng = np.random.default_rng(51)
+    T = sum(chunks)
+    m, m_hca, n_win, r = 4, 16, 6, 4
+    tok = _cache_tokens(rng, T)
+    kw = dict(m=m, m_hca=m_hca, n_win=n_win, rope_dim=r, rope_base=10000.0, eps=1e-6)
+    R = Cc.ring_slots(m, m_hca)
+    state = {"E_csa": [], "K_idx": [], "E_hca": [], "window": {}}
+    ring = {k: np.full((R, tok[k].shape[1]), np.nan) for k in Cc.STREAMS_CSA + Cc.STREAMS_IDX + Cc.STREAMS_HCA}
+    t0 = 0
+    for n in chunks:
+        t0 = Cc.append_incremental(state, ring, {k: v[t0:t0 + n] for k, v in tok.items()}, t0, **kw)
+        full = Cc.cache_state(tok, t0, **kw)
+        assert len(state["E_csa"]) == len(full["E_csa"]) == t0 // m
+        assert len(state["E_hca"]) == len(full["E_hca"]) == t0 // m_hca
+        if len(full["E_csa"]):
+            np.testing.assert_allclose(np.stack(state["E_csa"]), full["E_csa"], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(np.stack(state["K_idx"]), full["K_idx"], rtol=0, atol=1e-12)
+        if len(full["E_hca"]):
+            np.testing.assert_allclose(np.stack(state["E_hca"]), full["E_hca"], rtol=0, atol=1e-12)
+        assert sorted(state["window"]) == list(full["window_tokens"])
+        np.testing.assert_allclose(np.stack([state["window"][t] for t in full["window_tokens"]]), full["window"],
+                                   rtol=0, atol=1e-12)
+        for k, rows in full["tail"].items():
+            for u, t in enumerate(range(t0 - len(rows), t0)):
+                assert np.array_equal(ring[k][t % R], rows[u])
+
+
+def test_cache_ring_is_lcm_of_the_rates():
+    from oracle import cache as Cc
+    assert Cc.ring_slots(4, 16) == 16 and Cc.ring_slots(4, 128) == 128 and Cc.ring_slots(4, 6) == 12
+
+
+def test_incremental_cache_planted_short_ring_is_caught():
+    """A ring of m' - 1 slots loses the first token of an HCA block before the
+    block completes: the pin fails."""
+    from oracle import cache as Cc
+    real = Cc.ring_slots
+    Cc.ring_slots = lambda m, mh: real(m, mh) - 1
+    try:
+        with pytest.raises((AssertionError, ValueError)):
+            test_incremental_cache_equals_full_recompression([1] * 70)
+    finally:
+        Cc.ring_slots = real
