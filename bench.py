@@ -434,6 +434,53 @@ def grouped_out_proj(steps: int, warmup: int):
     return out
 
 
+def cache_append(steps: int, warmup: int):
+    """csa_cache_append at the Pro shapes (c = 512, indexer 128 fp8, m = 4, m' = 128,
+    window 128): a decode step appending one token to 16 sequences at a position
+    where a CSA and an HCA block complete (the step's most work), and a 16,384-token
+    prefill chunk of one sequence."""
+    import torch
+
+    import long_context_attention_02_amd as csa
+    from synth import Gen
+
+    c, dI, m, mh, W_cap = 512, 128, 4, 128, 128
+    R = csa.cache_ring_slots(m, mh)
+    names = ("Ca", "Za", "Cb", "Zb", "ICa", "IZa", "ICb", "IZb", "Ch", "Zh", "Wraw")
+    g = Gen(9, "cuda")
+    out = {}
+    for B, n_new, T0, label in ((16, 1, 1048575, "decode_16x1_token"), (1, 16384, 114688, "prefill_1x16384")):
+        new = {k: g.normal(i + 1, (B, n_new, dI if k.startswith("I") else c), "bf16", per_slot=False)
+               for i, k in enumerate(names)}
+        N_csa, N_hca = (T0 + n_new) // m + 1, (T0 + n_new) // mh + 1
+        st = dict(tail=torch.zeros((B, R, 6 * c + 4 * dI), dtype=torch.bfloat16, device="cuda"),
+                  E_csa=torch.zeros((B, N_csa, c), dtype=torch.bfloat16, device="cuda"),
+                  K_idx=torch.zeros((B, N_csa, dI), dtype=torch.float8_e4m3fn, device="cuda"),
+                  K_scale=torch.ones((B, N_csa), dtype=torch.float32, device="cuda"),
+                  E_hca=torch.zeros((B, N_hca, c), dtype=torch.bfloat16, device="cuda"),
+                  W=torch.zeros((B, W_cap, c), dtype=torch.bfloat16, device="cuda"))
+        T0t = torch.full((B,), T0, dtype=torch.int32, device="cuda")
+        gamma = torch.ones(c, dtype=torch.float32, device="cuda")
+
+        def call():
+            csa.csa_cache_append(T0t, new, st["tail"], st["E_csa"], st["K_idx"], st["E_hca"], st["W"], m=m,
+                                 m_hca=mh, K_scale=st["K_scale"], gamma=gamma, rope_dim=64)
+        per = _timed(call, steps, warmup)
+        ms = _pct(per, 0.5)
+        n_csa = (T0 + n_new) // m - T0 // m
+        n_hca = (T0 + n_new) // mh - T0 // mh
+        nbytes = B * (n_new * (7 * c + 4 * dI) * 2            # new rows read
+                      + min(n_new, W_cap) * c * 2               # window rows written
+                      + n_csa * (c * 2 + dI + 4)                # entries and keys written
+                      + n_hca * c * 2                           # HCA entries written
+                      + min(n_new, R) * (6 * c + 4 * dI) * 2)   # tail ring written
+        out[label] = {"ms": dist(per), "csa_entries": n_csa, "hca_entries": n_hca, "bytes": nbytes,
+                      "roofline": _roof(nbytes / (ms * 1e-3) / 1e9, "hbm")}
+        del new, st
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(run, seconds: float):
     """The fp64 oracle on all sequences of the same decode step, repeated until
     `seconds` of host time have passed (at least once)."""
@@ -561,6 +608,7 @@ def main():
             "roofline": _roof(fl["bytes"]["step"] / (fms * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["hca_decode"] = hca_decode(K, args.warmup, use_graph)
         result["grouped_out_proj"] = grouped_out_proj(steps=20, warmup=3)
+        result["cache_append"] = cache_append(steps=50, warmup=5)
     if not args.no_prefill:
         if keep is not None:
             keep.I = None

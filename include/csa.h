@@ -236,6 +236,46 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
                   void* stream);
 
 /*
+ * Cache append (method page §3.5: the inference cache is heterogeneous -- a
+ * classical cache whose blocks cover lcm(m, m') raw tokens holds the compressed
+ * entries, and a state cache holds the sliding-window KV and the tokens of the
+ * compression blocks that are not yet complete).  For every sequence b, the
+ * n_new tokens T0[b] .. T0[b] + n_new - 1 arrive; in one call:
+ *   - their window rows (RMSNorm with gamma, RoPE at the token's position) go
+ *     to the sliding-window ring W (token t at row t mod W_cap; when n_new >
+ *     W_cap only the last W_cap are written);
+ *   - every CSA entry s with T0[b] < m (s + 1) <= T0[b] + n_new is compressed
+ *     (overlapping, m; RMSNorm + RoPE at m s) into E_csa[b][s], and its indexer
+ *     key (no norm, no RoPE) into K_idx[b][s] in k_dtype;
+ *   - every HCA entry h with T0[b] < m' (h + 1) <= T0[b] + n_new is compressed
+ *     (disjoint, m'; RMSNorm + RoPE at m' h) into E_hca[b][h];
+ *   - the raw candidate rows of the last min(n_new, lcm(m, m')) new tokens go to
+ *     the tail ring: tail[b][t mod lcm][...] holds, side by side, the token's
+ *     C_a, Z_a, C_b, Z_b (c each), IC_a, IZ_a, IC_b, IZ_b (d_I each), C_h, Z_h
+ *     (c each), 6 c + 4 d_I bf16 values.
+ * Candidates of tokens before T0[b] are read from the tail ring, so a sequence's
+ * appends must follow one another with the ring kept between them (T0[b] = 0
+ * needs no ring contents).  The caches then equal the compression of the whole
+ * sequence, entry by entry (appends in any chunking give the same bytes).
+ *  T0      : [B] int32 on the device, tokens present before this append.
+ *  C_a .. Z_h, W_raw : [B][n_new][c] (d_I for IC_*) bf16 rows of the new tokens.
+ *  E_csa   : [B][N_csa][c] bf16;  K_idx: [B][N_csa][d_I] of k_dtype (BF16,
+ *            FP8_E4M3 with K_scale fp32 [B][N_csa], or MXFP4 with K_scale
+ *            E8M0 bytes [B][N_csa][d_I / 32]);  E_hca: [B][N_hca][c] bf16.
+ *            Entries at or past the capacities are not written.
+ *  W       : [B][W_cap][c] bf16;  gamma: [c] fp32 or NULL (1).
+ *  Needs c, d_I multiples of 8 (at most 1024), lcm(m, m') in [2 m, 4096] and
+ *  16-byte aligned inputs and tail.
+ */
+int csa_cache_append(int B, const int* T0, int n_new, int c, int d_I, int m, int m_hca,
+                     const void* C_a, const void* Z_a, const void* C_b, const void* Z_b,
+                     const void* IC_a, const void* IZ_a, const void* IC_b, const void* IZ_b,
+                     const void* C_h, const void* Z_h, const void* W_raw, void* tail,
+                     void* E_csa, void* K_idx, void* K_scale, int k_dtype, long long N_csa,
+                     void* E_hca, long long N_hca, void* W, int W_cap, const float* gamma, float eps,
+                     int rope_dim, float rope_base, void* stream);
+
+/*
  * Grouped output projection of the attention outputs (method page §3.3:
  * because c * n_h is large, the output projection is grouped -- each group of
  * heads is projected down to d_g, the results are concatenated and projected

@@ -21,7 +21,7 @@ __all__ = [
     "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
     "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES", "csa_out_proj_workspace_size",
-    "csa_grouped_out_proj",
+    "csa_grouped_out_proj", "csa_cache_append", "cache_ring_slots",
     "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3", "CSA_MXFP4",
 ]
 
@@ -76,6 +76,9 @@ _lib.csa_sparse_mqa_noalloc.restype = _I
 _lib.csa_sparse_mqa_noalloc.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I,
                                         _I, _F, _F, _I, _P, _P]
 NOALLOC_SCRATCH_BYTES = 16 << 20
+_lib.csa_cache_append.restype = _I
+_lib.csa_cache_append.argtypes = [_I, _P, _I, _I, _I, _I, _I] + [_P] * 15 + [_I, _L, _P, _L, _P, _I, _P, _F, _I,
+                                                                              _F, _P]
 _lib.csa_out_proj_workspace_size.restype = _S
 _lib.csa_out_proj_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.csa_grouped_out_proj.restype = _I
@@ -313,3 +316,36 @@ def csa_grouped_out_proj(o, W1, W2, y, out, *, workspace=None):
     _check(_lib.csa_grouped_out_proj(
         _ptr(o, "o", bf), _ptr(W1, "W1", bf, 3), _ptr(W2, "W2", bf, 2), _ptr(y, "y", bf, 2),
         _ptr(out, "out", bf, 2), T, n_h, c, g, d_g, d, _ptr(workspace, "workspace"), ws_bytes, _stream()))
+
+
+def cache_ring_slots(m: int, m_hca: int) -> int:
+    """Token slots of the tail ring: lcm(m, m')."""
+    import math
+    return m * m_hca // math.gcd(m, m_hca)
+
+
+def csa_cache_append(T0, new: dict, tail, E_csa, K_idx, E_hca, W, *, m: int, m_hca: int, K_scale=None,
+                     gamma=None, eps: float = 1e-6, rope_dim: int = 0, rope_base: float = 10000.0):
+    """Heterogeneous cache append.  T0 [B] int32 (tokens before); new: dict of [B, n_new, width]
+    bf16 rows "Ca", "Za", "Cb", "Zb", "ICa", "IZa", "ICb", "IZb", "Ch", "Zh", "Wraw";
+    tail [B, lcm(m, m'), 6 c + 4 d_I] bf16; E_csa [B, N_csa, c]; K_idx [B, N_csa, d_I] (bf16,
+    float8_e4m3fn with K_scale [B, N_csa], or uint8 MXFP4 [B, N_csa, d_I / 2] with K_scale
+    uint8 [B, N_csa, d_I / 32]); E_hca [B, N_hca, c]; W [B, W_cap, c]."""
+    names = ("Ca", "Za", "Cb", "Zb", "ICa", "IZa", "ICb", "IZb", "Ch", "Zh", "Wraw")
+    B, n_new, c = new["Ca"].shape
+    d_I = new["ICa"].shape[2]
+    for k in names:
+        want = (B, n_new, d_I if k.startswith("I") else c)
+        if tuple(new[k].shape) != want or new[k].dtype != torch.bfloat16:
+            raise ValueError(f"{k} must be bf16 {want}")
+    R = cache_ring_slots(m, m_hca)
+    if tuple(tail.shape) != (B, R, 6 * c + 4 * d_I):
+        raise ValueError(f"tail must be [B, {R}, {6 * c + 4 * d_I}]")
+    N_csa, N_hca, W_cap = E_csa.shape[1], E_hca.shape[1], W.shape[1]
+    kd = _dt(K_idx)
+    _check(_lib.csa_cache_append(
+        B, _ptr(T0, "T0", torch.int32), n_new, c, d_I, m, m_hca, *(_ptr(new[k], k) for k in names),
+        _ptr(tail, "tail", torch.bfloat16), _ptr(E_csa, "E_csa", torch.bfloat16), _ptr(K_idx, "K_idx"),
+        _ptr(K_scale, "K_scale"), kd, N_csa, _ptr(E_hca, "E_hca", torch.bfloat16), N_hca,
+        _ptr(W, "W", torch.bfloat16), W_cap, _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
+        _stream()))

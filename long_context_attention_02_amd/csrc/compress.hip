@@ -47,6 +47,16 @@ struct CompressJob {
   RopeRatio rope;
   float eps;
   int in_dtype, out_dtype, B, c, m, overlap, G, rope_dim;
+  // append mode (wide kernel only): T0[b] tokens were present before, n_new
+  // arrive (rows of token T0[b] + r at row r of the inputs); entries whose
+  // blocks complete are s = floor(T0[b] / m) + s_begin + blockIdx.x, those
+  // with m (s + 1) <= T0[b] + n_new; candidates of earlier tokens are read from a ring of in_ring
+  // token slots (token t at slot t mod in_ring, slot stride r_stride, batch
+  // stride r_bs elements); output rows at or past out_rows are skipped
+  const int* T0;
+  const void *rCa, *rZa, *rCb, *rZb;
+  long long n_new, r_stride, r_bs, out_rows;
+  int in_ring;
 };
 struct CompressBatch {
   CompressJob job[COMP_MAX_JOBS];
@@ -544,10 +554,21 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
   const int c = J.c, m = J.m;
   const int CV = c / VEC;                      // pieces per row (host: c % VEC == 0, c <= 1024)
   const int TG = J.G;                          // token groups (host: wide_groups)
-  const long long s = J.s_begin + blockIdx.x;
   const int b = blockIdx.y;
-  const long long T = seq_tokens(J, b);
-  if ((long long)m * s >= T) return;   // no such entry in this sequence (whole workgroup)
+  long long s, T, tbase;
+  if (J.T0) {   // append: the entries whose blocks complete with the new tokens
+    const long long t0 = J.T0[b];
+    s = t0 / m + J.s_begin + blockIdx.x;
+    T = t0 + J.n_new;
+    if ((long long)m * (s + 1) > T) return;   // (whole workgroup)
+    tbase = t0;
+  } else {
+    s = J.s_begin + blockIdx.x;
+    T = seq_tokens(J, b);
+    if ((long long)m * s >= T) return;   // no such entry in this sequence (whole workgroup)
+    tbase = J.tok_base;
+  }
+  if (J.out_rows > 0 && (J.out_ring > 0 ? s % J.out_ring : s) >= J.out_rows) return;
   const long long a_lo = (long long)m * s, a_hi = min((long long)m * (s + 1), T);
   long long b_lo = 0, b_hi = 0;
   if (J.overlap) {
@@ -557,6 +578,7 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
   const long long na = max(a_hi - a_lo, 0LL), nb = max(b_hi - b_lo, 0LL);
   const long long ncand = na + nb;   // >= 1: the entry's block starts below T
   const size_t base = (size_t)b * (size_t)J.in_bs;
+  const size_t rbase = (size_t)b * (size_t)J.r_bs;
   float* pm = smem;              // [TG][c] running maxima
   float* ps = pm + TG * c;       // [TG][c] sums
   float* pa = ps + TG * c;       // [TG][c] weighted sums
@@ -586,12 +608,16 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
         const long long q = min(q0 + (long long)u * TG, ncand - 1);
         const bool in_a = q < na;
         const long long tok = in_a ? a_lo + q : b_lo + (q - na);
-        const size_t off = (base + (size_t)(tok - J.tok_base) * (size_t)c + (size_t)cv * VEC) * ESZ;
-        const char* Cp = (const char*)(in_a ? J.Ca : J.Cb);
-        const char* Zp = (const char*)(in_a ? J.Za : J.Zb);
+        // a token before the appended ones comes from the ring (append mode only)
+        const bool from_ring = tok < tbase;
+        const size_t off = (from_ring ? rbase + (size_t)(tok % J.in_ring) * (size_t)J.r_stride
+                                      : base + (size_t)(tok - tbase) * (size_t)c) + (size_t)cv * VEC;
+        const char* Cp = (const char*)(from_ring ? (in_a ? J.rCa : J.rCb) : (in_a ? J.Ca : J.Cb)) + off * ESZ;
+        const char* Zp0 = (const char*)(from_ring ? (in_a ? J.rZa : J.rZb) : (in_a ? J.Za : J.Zb));
+        const char* Zp = Zp0 ? Zp0 + off * ESZ : nullptr;
         hz[u] = Zp != nullptr;
-        xc[u] = *(const u32x4_t*)(Cp + off);
-        zc[u] = *(const u32x4_t*)((Zp ? Zp : Cp) + off);
+        xc[u] = *(const u32x4_t*)Cp;
+        zc[u] = *(const u32x4_t*)(Zp ? Zp : Cp);
       }
       // the round's maximum first, then one rescale of the running sums
       float bm[VEC];
@@ -799,6 +825,106 @@ int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
     return -1;
   hipLaunchKernelGGL(compress_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)nb),
                      dim3(COMP_THREADS), lds, st, jb);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Cache append (heterogeneous cache, method page section 3.5): the new tokens'
+// window rows into the sliding-window ring, every CSA entry, indexer key and
+// HCA entry whose block completes, then the new tokens' raw candidate rows
+// into the tail ring of lcm(m, m') slots that the next append reads.
+// ---------------------------------------------------------------------------
+struct TailCopy {
+  const uint16_t* src[10];   // Ca, Za, Cb, Zb, ICa, IZa, ICb, IZb, Ch, Zh: [B][n_new][width]
+  int width[10], off[10];    // row width and offset within a tail slot (elements)
+};
+
+// block (u, b): the u-th of the last min(n_new, ring) new tokens of sequence b
+__global__ __launch_bounds__(256) void tail_copy_kernel(const TailCopy tc, const int* __restrict__ T0,
+                                                        uint16_t* __restrict__ tail, int n_new, int n_copy,
+                                                        int ring, int TR) {
+  const int b = blockIdx.y;
+  const int r = n_new - n_copy + blockIdx.x;   // row among the new tokens
+  const long long t = (long long)T0[b] + r;
+  uint16_t* dst = tail + ((size_t)b * ring + (size_t)(t % ring)) * TR;
+  for (int p = threadIdx.x; p < TR / 8; p += 256) {
+    const int e = 8 * p;
+    int k = 0;
+#pragma unroll
+    for (int q = 1; q < 10; ++q) k = e >= tc.off[q] ? q : k;
+    const int w = tc.width[k];
+    const uint16_t* src = tc.src[k] + ((size_t)b * n_new + r) * (size_t)w + (e - tc.off[k]);
+    *(u32x4_t*)(dst + e) = *(const u32x4_t*)src;
+  }
+}
+
+int launch_cache_append(const CacheAppendArgs& a, hipStream_t st) {
+  const int c = a.c, dI = a.d_I, R = a.ring, TR = 6 * c + 4 * dI;
+  const uint16_t* tail = (const uint16_t*)a.tail;
+  auto job = [&](const void* Ca, const void* Za, const void* Cb, const void* Zb, int width, int m, int overlap,
+                 const uint16_t* rCa, const uint16_t* rZa, const uint16_t* rCb, const uint16_t* rZb,
+                 const float* gamma, int rope_dim, void* E, int out_dtype, float* E_scale, long long rows,
+                 long long out_ring, long long s_begin, long long n_entries) {
+    CompressArgs x{};
+    x.C_a = Ca; x.Z_a = Za; x.C_b = Cb; x.Z_b = Zb; x.in_dtype = DT_BF16; x.B = a.B;
+    x.R = a.n_new; x.in_bs = (long long)a.n_new * width; x.tok_base = 0; x.T = 1; x.T_len = nullptr;
+    x.c = width; x.m = m; x.overlap = overlap; x.s_begin = 0; x.s_end = n_entries;
+    x.gamma = gamma; x.eps = a.eps; x.rope_dim = rope_dim; x.rope_base = a.rope_base;
+    x.pos_stride = m; x.pos_offset = 0; x.E = E; x.out_dtype = out_dtype; x.E_scale = E_scale;
+    x.out_bs = rows * width; x.out_ring = out_ring;
+    const int vec = 8;
+    CompressJob J = make_job(x, wide_groups(width, vec, overlap ? 2 * m : m));
+    J.T0 = a.T0;
+    J.n_new = a.n_new;
+    J.s_begin = s_begin;
+    J.rCa = rCa; J.rZa = rZa; J.rCb = rCb; J.rZb = rZb;
+    J.r_stride = TR;
+    J.r_bs = (long long)R * TR;
+    J.in_ring = R;
+    J.out_rows = out_ring > 0 ? 0 : rows;
+    return J;
+  };
+  CompressBatch xb{};
+  const long long n_win_rows = std::min<long long>(a.n_new, a.W_cap);
+  xb.job[0] = job(a.Wraw, nullptr, nullptr, nullptr, c, 1, 0, nullptr, nullptr, nullptr, nullptr, a.gamma,
+                  a.rope_dim, a.W, DT_BF16, nullptr, a.W_cap, a.W_cap, a.n_new - n_win_rows, n_win_rows);
+  xb.job[1] = job(a.Ca, a.Za, a.Cb, a.Zb, c, a.m, 1, tail, tail + c, tail + 2 * c, tail + 3 * c, a.gamma,
+                  a.rope_dim, a.E_csa, DT_BF16, nullptr, a.N_csa, 0, 0, a.n_new / a.m + 1);
+  xb.job[2] = job(a.ICa, a.IZa, a.ICb, a.IZb, dI, a.m, 1, tail + 4 * c, tail + 4 * c + dI, tail + 4 * c + 2 * dI,
+                  tail + 4 * c + 3 * dI, nullptr, 0, a.K_idx, a.k_dtype, (float*)a.K_scale, a.N_csa, 0, 0,
+                  a.n_new / a.m + 1);
+  xb.job[3] = job(a.Ch, a.Zh, nullptr, nullptr, c, a.m_hca, 0, tail + 4 * c + 4 * dI, tail + 5 * c + 4 * dI,
+                  nullptr, nullptr, a.gamma, a.rope_dim, a.E_hca, DT_BF16, nullptr, a.N_hca, 0, 0,
+                  a.n_new / a.m_hca + 1);
+  // (window rows: pos_stride 1)
+  xb.job[0].pos_stride = 1;
+  long long gx = 1;
+  size_t lds = 0;
+  for (int q = 0; q < 4; ++q) {
+    gx = std::max(gx, xb.job[q].n_entries);
+    const int TG = xb.job[q].G;
+    lds = std::max(lds, (size_t)(3 * TG * xb.job[q].c + xb.job[q].c + 16) * sizeof(float));
+  }
+  if (gx > 2147483647LL || a.B > 65535) return -1;
+  if (lds > 65536 && hipFuncSetAttribute((const void*)compress_wide_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+    return -1;
+  hipLaunchKernelGGL(compress_wide_kernel, dim3((unsigned)gx, (unsigned)a.B, 4u), dim3(COMPX_THREADS), lds, st,
+                     xb);
+  // the tail ring, after the compressions have read it
+  TailCopy tc{};
+  const void* src[10] = {a.Ca, a.Za, a.Cb, a.Zb, a.ICa, a.IZa, a.ICb, a.IZb, a.Ch, a.Zh};
+  const int wid[10] = {c, c, c, c, dI, dI, dI, dI, c, c};
+  int off = 0;
+  for (int q = 0; q < 10; ++q) {
+    tc.src[q] = (const uint16_t*)src[q];
+    tc.width[q] = wid[q];
+    tc.off[q] = off;
+    off += wid[q];
+  }
+  const int n_copy = std::min(a.n_new, R);
+  hipLaunchKernelGGL(tail_copy_kernel, dim3((unsigned)n_copy, (unsigned)a.B), dim3(256), 0, st, tc, a.T0,
+                     (uint16_t*)a.tail, a.n_new, n_copy, R, TR);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -267,6 +267,45 @@ int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E,
   return ok();
 }
 
+int csa_cache_append(int B, const int* T0, int n_new, int c, int d_I, int m, int m_hca,
+                     const void* C_a, const void* Z_a, const void* C_b, const void* Z_b,
+                     const void* IC_a, const void* IZ_a, const void* IC_b, const void* IZ_b,
+                     const void* C_h, const void* Z_h, const void* W_raw, void* tail,
+                     void* E_csa, void* K_idx, void* K_scale, int k_dtype, long long N_csa,
+                     void* E_hca, long long N_hca, void* W, int W_cap, const float* gamma, float eps,
+                     int rope_dim, float rope_base, void* stream) {
+  const char* fn = "csa_cache_append";
+  const void* req[] = {T0, C_a, Z_a, C_b, Z_b, IC_a, IZ_a, IC_b, IZ_b, C_h, Z_h, W_raw, tail, E_csa, K_idx,
+                       E_hca, W};
+  for (const void* p : req)
+    if (!p) return fail(CSA_E_NULL, "%s: every array argument except gamma and K_scale is required", fn);
+  if (B < 1 || n_new < 1 || c < 8 || d_I < 8 || m < 1 || m_hca < 1 || N_csa < 1 || N_hca < 1 || W_cap < 1)
+    return fail(CSA_E_SHAPE, "%s: sizes must be >= 1 (c, d_I >= 8)", fn);
+  if (B > 65535) return fail(CSA_E_UNSUPPORTED, "%s: B <= 65535", fn);
+  if (c % 8 || d_I % 8 || c > 1024 || d_I > 1024)
+    return fail(CSA_E_UNSUPPORTED, "%s: c and d_I must be multiples of 8, at most 1024", fn);
+  long long a = m, bb = m_hca;
+  while (bb) { const long long t = a % bb; a = bb; bb = t; }
+  const long long ring = (long long)m / a * m_hca;   // lcm(m, m')
+  if (ring < 2LL * m || ring > 4096)
+    return fail(CSA_E_UNSUPPORTED, "%s: lcm(m, m') must lie in [2 m, 4096]", fn);
+  if (k_dtype != CSA_BF16 && k_dtype != CSA_FP8_E4M3 && k_dtype != CSA_MXFP4)
+    return fail(CSA_E_DTYPE, "%s: k_dtype must be BF16, FP8_E4M3 or MXFP4", fn);
+  if (k_dtype != CSA_BF16 && !K_scale) return fail(CSA_E_NULL, "%s: K_scale is required for FP8 and MXFP4 keys", fn);
+  if (k_dtype == CSA_MXFP4 && d_I % 32) return fail(CSA_E_SHAPE, "%s: MXFP4 keys need d_I %% 32 == 0", fn);
+  if (rope_dim < 0 || rope_dim > c || (rope_dim & 1) || ((c - rope_dim) & 1))
+    return fail(CSA_E_SHAPE, "%s: rope_dim must be even and <= c", fn);
+  if (gamma && !(eps >= 0.f)) return fail(CSA_E_SHAPE, "%s: eps must be >= 0", fn);
+  const void* al[] = {C_a, Z_a, C_b, Z_b, IC_a, IZ_a, IC_b, IZ_b, C_h, Z_h, W_raw, tail};
+  for (const void* p : al)
+    if (((uintptr_t)p) & 15u) return fail(CSA_E_UNSUPPORTED, "%s: input arrays and tail must be 16-byte aligned", fn);
+  csa::CacheAppendArgs x{B, T0, n_new, c, d_I, m, m_hca, (int)ring, C_a, Z_a, C_b, Z_b, IC_a, IZ_a, IC_b,
+                         IZ_b, C_h, Z_h, W_raw, tail, E_csa, K_idx, K_scale, k_dtype, N_csa, E_hca, N_hca, W,
+                         W_cap, gamma, eps, rope_dim, rope_base};
+  if (csa::launch_cache_append(x, (hipStream_t)stream) != 0) return fail(CSA_E_HIP, "%s: kernel launch failed", fn);
+  return ok();
+}
+
 static int proj_check(const char* fn, int T, int n_h, int c, int groups, int d_g, int d) {
   if (T < 1 || n_h < 1 || c < 1 || groups < 1 || d_g < 1 || d < 1)
     return fail(CSA_E_SHAPE, "%s: sizes must be >= 1", fn);

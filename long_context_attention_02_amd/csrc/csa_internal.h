@@ -86,6 +86,28 @@ size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max,
 // returns 0 or a CSA status (UNSUPPORTED / HIP) and fills *why on failure
 int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why);
 
+struct CacheAppendArgs {
+  int B;
+  const int* T0;    // [B] tokens present before the append (device)
+  int n_new, c, d_I, m, m_hca, ring;
+  const void *Ca, *Za, *Cb, *Zb, *ICa, *IZa, *ICb, *IZb, *Ch, *Zh, *Wraw;   // [B][n_new][width] bf16
+  void* tail;       // [B][ring][6 c + 4 d_I] bf16
+  void* E_csa;      // [B][N_csa][c] bf16
+  void* K_idx;      // [B][N_csa][d_I] of k_dtype
+  void* K_scale;
+  int k_dtype;
+  long long N_csa;
+  void* E_hca;      // [B][N_hca][c] bf16
+  long long N_hca;
+  void* W;          // [B][W_cap][c] bf16
+  int W_cap;
+  const float* gamma;
+  float eps;
+  int rope_dim;
+  float rope_base;
+};
+int launch_cache_append(const CacheAppendArgs& a, hipStream_t st);
+
 struct ProjArgs {
   const void* o;    // [T][n_h c] bf16
   const void* W1;   // [groups][d_g][n_h c / groups] bf16

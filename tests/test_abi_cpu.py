@@ -200,3 +200,22 @@ def test_grouped_out_proj_validation(lib):
     assert need > 0                                           # few rows split the contraction
     assert call() == CSA_E_WORKSPACE
     assert lib.csa_out_proj_workspace_size(16384, 128, 512, 16, 1024, 7168) == 0
+
+
+def test_cache_append_validation(lib):
+    def call(**kw):
+        a = dict(B=2, T0=FAKE, n=1, c=512, dI=128, m=4, mh=128, **{f"p{i}": FAKE for i in range(11)},
+                 tail=FAKE, E=FAKE, K=FAKE, Ks=None, kd=1, Nc=100, H=FAKE, Nh=10, W=FAKE, Wc=128, g=None,
+                 eps=1e-6, r=64, base=1e4, st=None)
+        a.update(kw)
+        return lib.csa_cache_append(*a.values())
+
+    assert call(T0=None) == CSA_E_NULL
+    assert call(p3=None) == CSA_E_NULL
+    assert call(kd=2) == CSA_E_NULL                           # fp8 keys need K_scale
+    assert call(kd=0) == CSA_E_DTYPE
+    assert call(mh=4) == CSA_E_UNSUPPORTED                    # lcm(4, 4) < 2 m: the ring is too short
+    assert call(c=500) == CSA_E_UNSUPPORTED
+    assert call(p0=FAKE + 8) == CSA_E_UNSUPPORTED             # 16-byte alignment
+    assert call(r=65) == CSA_E_SHAPE
+    assert call(n=0) == CSA_E_SHAPE
