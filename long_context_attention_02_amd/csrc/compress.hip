@@ -462,33 +462,6 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
     scale = am > 0.f ? am / 448.0f : 1.0f;
     if (lane == 0) J.E_scale[(size_t)b * (size_t)(J.out_bs / c) + (size_t)orow] = scale;
   }
-  if constexpr (ODT == DT_MX4) {
-    // MXFP4: a 32-channel block is 32 / VEC consecutive lanes (c % 32 == 0);
-    // the lane holding a block's first channel writes the scale byte
-    constexpr int LPB = 32 / VEC;
-#pragma unroll
-    for (int pi = 0; pi < COMPW_MAXP; ++pi) {
-      if (64 * pi >= npieces) break;
-      float a = 0.f;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) a = fmaxf(a, fabsf(pooled[pi][e]));
-#pragma unroll
-      for (int x = 1; x < LPB; x <<= 1) a = fmaxf(a, __shfl_xor(a, x, 64));
-      const int se = mx4_shared_exp(a);
-      const int piece = lane + 64 * pi;
-      if (piece >= npieces) continue;
-      uint32_t pk = 0;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) pk |= f32_to_e2m1(ldexpf(pooled[pi][e], -se)) << (4 * e);
-      uint8_t* ob = (uint8_t*)J.E + (obase + (size_t)piece * VEC) / 2;
-      if constexpr (VEC == 8) *(uint32_t*)ob = pk;
-      else *(uint16_t*)ob = (uint16_t)pk;
-      if (piece % LPB == 0)
-        ((uint8_t*)J.E_scale)[((size_t)b * (size_t)(J.out_bs / c) + (size_t)orow) * (size_t)(c / 32) +
-                              (size_t)piece / LPB] = (uint8_t)(se + 127);
-    }
-    return;
-  }
 #pragma unroll
   for (int pi = 0; pi < COMPW_MAXP; ++pi) {
     if (64 * pi >= npieces) break;
@@ -524,11 +497,9 @@ __global__ __launch_bounds__(64 * COMPW_WAVES) void compress_wave_kernel(const C
     case DT_F32 * 4 + DT_F32: compress_entry_wave<DT_F32, DT_F32, MAXC>(J, s, b, lane); break;
     case DT_F32 * 4 + DT_BF16: compress_entry_wave<DT_F32, DT_BF16, MAXC>(J, s, b, lane); break;
     case DT_F32 * 4 + DT_FP8: compress_entry_wave<DT_F32, DT_FP8, MAXC>(J, s, b, lane); break;
-    case DT_F32 * 4 + DT_MX4: compress_entry_wave<DT_F32, DT_MX4, MAXC>(J, s, b, lane); break;
     case DT_BF16 * 4 + DT_F32: compress_entry_wave<DT_BF16, DT_F32, MAXC>(J, s, b, lane); break;
     case DT_BF16 * 4 + DT_BF16: compress_entry_wave<DT_BF16, DT_BF16, MAXC>(J, s, b, lane); break;
-    case DT_BF16 * 4 + DT_FP8: compress_entry_wave<DT_BF16, DT_FP8, MAXC>(J, s, b, lane); break;
-    default: compress_entry_wave<DT_BF16, DT_MX4, MAXC>(J, s, b, lane); break;
+    default: compress_entry_wave<DT_BF16, DT_FP8, MAXC>(J, s, b, lane); break;
   }
 }
 
@@ -740,8 +711,9 @@ static bool wave_job(const CompressArgs& x) {
   const int vec = x.in_dtype == DT_F32 ? 4 : 8;
   // 16-byte pieces: every input row and (for bf16 output) every output row starts 16-byte aligned
   const bool in_al = inputs_in_pieces(x);
+  // (MXFP4 output takes the wide kernel: its store in this kernel spilled registers)
   const bool out_al = (x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0)) &&
-                      (x.out_dtype != DT_MX4 || ((uintptr_t)x.E & 3u) == 0);
+                      x.out_dtype != DT_MX4;
   // a job of a few dozen entries (decode) is pure latency, where one workgroup per
   // entry is quicker; many entries (prefill) are throughput, where a wave each is
   const long long items = (long long)x.B * (x.s_end - x.s_begin);

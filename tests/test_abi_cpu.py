@@ -219,3 +219,59 @@ def test_cache_append_validation(lib):
     assert call(p0=FAKE + 8) == CSA_E_UNSUPPORTED             # 16-byte alignment
     assert call(r=65) == CSA_E_SHAPE
     assert call(n=0) == CSA_E_SHAPE
+
+
+def _kernel_scratch_sizes():
+    """(kernel, private segment bytes) of every gfx950 kernel in libcsa.so, read from
+    the code objects the build embedded (one offload bundle per source file)."""
+    import shutil
+    import subprocess
+    import tempfile
+    llvm = "/opt/rocm/llvm/bin"
+    tools = [os.path.join(llvm, t) for t in ("llvm-objcopy", "clang-offload-bundler", "llvm-readelf")]
+    if not all(shutil.which(t) or os.path.exists(t) for t in tools):
+        pytest.skip("ROCm LLVM tools not found")
+    out = []
+    with tempfile.TemporaryDirectory() as td:
+        fb = os.path.join(td, "fatbin")
+        subprocess.run([tools[0], "--dump-section", f".hip_fatbin={fb}", LIB, os.path.join(td, "copy.so")],
+                       check=True, capture_output=True)
+        data = open(fb, "rb").read()
+        magic = b"__CLANG_OFFLOAD_BUNDLE__"
+        starts, i = [], data.find(magic)
+        while i >= 0:
+            starts.append(i)
+            i = data.find(magic, i + 1)
+        for n, a in enumerate(starts):
+            # a bundle's header gives its entries' offsets: everything from its start will do
+            part, co = os.path.join(td, f"b{n}"), os.path.join(td, f"b{n}.co")
+            open(part, "wb").write(data[a:])
+            r = subprocess.run([tools[1], "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                                f"--input={part}", f"--output={co}", "--unbundle"], capture_output=True)
+            if r.returncode != 0:
+                continue
+            notes = subprocess.run([tools[2], "--notes", co], capture_output=True, text=True).stdout
+            name = None
+            for ln in notes.splitlines():
+                m = re.match(r"\s+\.name:\s+(\S+)", ln)
+                if m:
+                    name = m.group(1)
+                m = re.match(r"\s+\.private_segment_fixed_size:\s+(\d+)", ln)
+                if m and name:
+                    out.append((name, int(m.group(1))))
+                    name = None
+    return out
+
+
+def test_no_kernel_spills_to_scratch():
+    """Register spills to scratch memory have made kernels here many times slower
+    (a wave-per-entry compressor went from 0.044 to 0.5 ms); every kernel of the
+    library must fit its registers.  The one exception: the streaming attention
+    kernel at d = 512 with two 16-head tiles per wave, whose 256 accumulator
+    registers leave a few prologue values (at most 64 bytes) to scratch, none in
+    the loop."""
+    sizes = _kernel_scratch_sizes()
+    assert len(sizes) >= 100, sizes
+    allowed = re.compile(r"mqa_decode_kernelILi512ELb[01]ELi\d+ELi\d+ELi2EE")
+    spilled = [(n, s) for n, s in sizes if s > 0 and not (allowed.search(n) and s <= 64)]
+    assert not spilled, spilled
