@@ -22,6 +22,8 @@ Prints ONE JSON line.  Also reported, each against its roofline: the same 1M
 decode with MXFP4 indexer keys (the FP4 query-key path) and the recall of its
 selection against the fp8 one, the Flash-like CSA decode (8 sequences x 16,384
 entries, k = 512), the HCA dense decode (4 sequences x 8,192 entries), the
+HCA and 1M CSA decodes with mixed KV rows (e4m3 codes under a row scale plus
+bf16 rotated dims, 580 bytes per row instead of 1,024), the cache append, the
 prefill indexer (16,384 queries x 32,768 entries, bf16), each call of the
 chunked-prefill step and the grouped output projection (prefill and decode
 rows); and the fp64 oracle timed on a bounded sample of the decode workload on
@@ -217,6 +219,14 @@ def traffic_from_profiles(kernel_tag: str, src_file: str):
 # fp32 scores between the indexer and the top-k are an intermediate and are
 # not counted)
 # ---------------------------------------------------------------------------
+def kv_row_bytes(wl) -> int:
+    """Bytes of one stored entry or window row: d values of the storage type, or
+    a mixed row (d - rope_dim e4m3 codes, rope_dim bf16 values, an fp32 scale)."""
+    if wl.kv_dtype == "mixed":
+        return (wl.d - wl.rope_dim) + 2 * wl.rope_dim + 4
+    return wl.d * {"bf16": 2, "f32": 4}[wl.kv_dtype]
+
+
 def csa_decode_bytes(wl) -> dict:
     esz = {"mxfp4": 0.5, "e4m3": 1, "bf16": 2, "f32": 4}
     kv = esz[wl.dtype]
@@ -224,8 +234,8 @@ def csa_decode_bytes(wl) -> dict:
     keys = int(B * N * dI * esz[wl.k_dtype])
     scales = {"e4m3": B * N * 4, "mxfp4": B * N * (dI // 32)}.get(wl.k_dtype, 0)
     q_index = B * (H * dI * 2 + H * 4)
-    gather = B * k * d * kv
-    window = B * wl.n_win * d * kv
+    gather = B * k * kv_row_bytes(wl)
+    window = B * wl.n_win * kv_row_bytes(wl)
     q = out = B * wl.n_h * d * kv
     idx = B * k * 4
     step = keys + scales + gather + window + q + out + q_index + idx
@@ -235,9 +245,9 @@ def csa_decode_bytes(wl) -> dict:
 
 def hca_decode_bytes(wl) -> dict:
     n_vis = min(wl.N_cap, (wl.q_pos0 + 1) // wl.m)
-    entries = wl.B * n_vis * wl.d * 2
+    entries = wl.B * n_vis * kv_row_bytes(wl)
     tail = wl.B * 2 * wl.m * wl.d * 2          # C and Z of the recompressed block
-    window = wl.B * wl.n_win * wl.d * 2
+    window = wl.B * wl.n_win * kv_row_bytes(wl)
     qo = 2 * wl.B * wl.n_h * wl.d * 2
     return {"step": entries + tail + window + qo, "attention": entries + window + qo}
 
@@ -271,13 +281,15 @@ def csa_decode(wl, K: int, warmup: int, use_graph: bool, keep_raw_first: bool = 
     return res, runs
 
 
-def hca_decode(K: int, warmup: int, use_graph: bool):
+def hca_decode(K: int, warmup: int, use_graph: bool, wl=None):
     """Dense MQA (HCA) decode: 4 sequences over 8,192 entries of 128 tokens each (1M
-    context) plus window and sink; the step also recompresses the newest block."""
+    context) plus window and sink; the step also recompresses the newest block.
+    Entries and window rows in bf16, or as mixed rows (wl = HCA_DECODE_MIXED)."""
     import torch
 
     from long_context_attention_02_amd.pipeline import HCADecode
-    from synth.workloads import HCA_DECODE as wl
+    from synth.workloads import HCA_DECODE
+    wl = wl or HCA_DECODE
 
     ab = hca_decode_bytes(wl)
     R = replicas_for(ab["step"])
@@ -515,7 +527,8 @@ def main():
         sys.exit(2)
     import torch
 
-    from synth.workloads import CSA_DECODE_1M as wl, CSA_DECODE_1M_MX4, CSA_DECODE_FLASH
+    from synth.workloads import (CSA_DECODE_1M as wl, CSA_DECODE_1M_MIXED, CSA_DECODE_1M_MX4, CSA_DECODE_FLASH,
+                                 HCA_DECODE_MIXED)
 
     torch.cuda.set_device(0)
     use_graph = not args.no_graph
@@ -607,6 +620,20 @@ def main():
             "algorithmic_bytes": fl["bytes"]["step"],
             "roofline": _roof(fl["bytes"]["step"] / (fms * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["hca_decode"] = hca_decode(K, args.warmup, use_graph)
+        # mixed KV rows (fp8 codes + bf16 rotated dims): the dense attention of the
+        # HCA step and the CSA 1M step
+        result["hca_decode_mixed_kv"] = hca_decode(K, args.warmup, use_graph, wl=HCA_DECODE_MIXED)
+        mk, mk_runs = csa_decode(CSA_DECODE_1M_MIXED, K, args.warmup, use_graph)
+        del mk_runs
+        capture.keep.clear()
+        torch.cuda.empty_cache()
+        result["csa_decode_mixed_kv"] = {
+            "workload": mk["workload"], "replicas": mk["replicas"], "graph": mk["graph"],
+            "ms_per_step": round(mk["ms_per_step"], 5),
+            "tokens/s": round(CSA_DECODE_1M_MIXED.B / (mk["ms_per_step"] * 1e-3), 1),
+            "step_ms_with_events": mk["step_ms_with_events"], "index_ms": mk["index_ms"],
+            "algorithmic_bytes": mk["bytes"],
+            "roofline": _roof(mk["bytes"]["step"] / (mk["ms_per_step"] * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["grouped_out_proj"] = grouped_out_proj(steps=20, warmup=3)
         result["cache_append"] = cache_append(steps=50, warmup=5)
     if not args.no_prefill:

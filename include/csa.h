@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 3
+#define CSA_ABI_VERSION 4
 
 /* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities).
  * CSA_MXFP4 is OCP MXFP4: FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6
@@ -43,7 +43,13 @@ extern "C" {
  * nibble, with one E8M0 scale byte (2^(byte - 127)) per 32 channels in a
  * separate array; quantised by the OCP MX rule (shared exponent
  * floor(log2(block max)) - 2, elements rounded to nearest even, saturating). */
-enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3 };
+enum csa_dtype { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3 = 2, CSA_MXFP4 = 3, CSA_KV_MIXED = 4 };
+/* CSA_KV_MIXED: KV rows (compressed entries and window rows) with the RoPE dims
+ * in BF16 and the rest in FP8 (method page §3.3, storage of the KV entries):
+ * of a row of c channels, the first c - rope_dim are e4m3fn codes under one
+ * fp32 scale per row (absmax / 448 of those channels, in a separate array),
+ * followed by the last rope_dim channels as bf16: c + rope_dim bytes per row
+ * (576 instead of 1024 at c = 512, rope_dim = 64). */
 
 enum csa_status {
   CSA_OK = 0,
@@ -92,12 +98,14 @@ const char* csa_last_error(void);
  *      batch stride out_batch_stride elements (channels); entry s goes to row
  *      s, or to row s mod out_ring when out_ring > 0 (a sliding-window ring;
  *      then at most out_ring entries per call, so that no two write the same
- *      row).  MXFP4 rows are c / 2 bytes (c % 32 == 0).
+ *      row).  MXFP4 rows are c / 2 bytes (c % 32 == 0); KV_MIXED rows c +
+ *      rope_dim bytes (rope_dim and c - rope_dim multiples of 8).
  *  E_scale  : FP8_E4M3: fp32 per-row scale at E_scale[b * (out_batch_stride /
  *      c) + row] (row absmax / 448, or 1 for a zero row); codes are
  *      RNE(value / scale), saturated to +-448.  MXFP4: the E8M0 block scales,
  *      bytes [B][rows][c / 32] (pass the byte array's address); the
- *      quantisation decisions are taken on the fp32 value.  NULL otherwise.
+ *      quantisation decisions are taken on the fp32 value.  KV_MIXED: the
+ *      fp32 row scale of the e4m3 part, like FP8.  NULL otherwise.
  */
 int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* Z_b, int in_dtype,
                  int B, long long R, long long in_batch_stride, long long tok_base, long long T,
@@ -202,11 +210,22 @@ int csa_topk(const float* I, const int* q_pos, int B, int Tq, long long N_cap, i
  *  W       : [B][W_cap][d] window ring (token tau at row tau mod W_cap), NULL
  *            iff n_win == 0; W_cap >= n_win.
  *  sink    : [n_h] fp32 or NULL (no sink; -inf is also "no sink").
- *  dtype   : F32 or BF16 for q, E, W and out.  out: [B][Tq][n_h][d].
+ *  dtype   : F32 or BF16 for q, E, W and out; or KV_MIXED: q and out BF16,
+ *            E and W mixed rows ([B][N_cap][d + rope_dim] and
+ *            [B][W_cap][d + rope_dim] bytes) whose fp8 part is decoded as
+ *            code * row scale, with the row scales in E_scale ([B][N_cap]
+ *            fp32) and W_scale ([B][W_cap] fp32, NULL iff n_win == 0).
+ *            E_scale and W_scale are ignored (may be NULL) for F32 and BF16.
+ *            out: [B][Tq][n_h][d].
  *  No key and no sink gives a zero output row.
  *  Matrix-core path: BF16 with d in {128, 256, 512}, n_h a multiple of 16 and
  *  q, E, W and out 16-byte aligned; any other call takes the generic path,
  *  which holds at most 8192 key slots per query (CSA_E_UNSUPPORTED beyond).
+ *  KV_MIXED runs on the matrix-core path only, at d = 512 with rope_dim = 64
+ *  (the entry width and rotated share of the method page's models;
+ *  CSA_E_UNSUPPORTED otherwise).  The stored values enter exactly: the row
+ *  scale multiplies the code part of each score and each softmax weight, never
+ *  a rounded copy of the row.
  *  workspace: at least csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win) bytes,
  *            16-byte aligned (split partials: per (query, split, head) the
  *            output over that split's keys divided by its softmax sum and
@@ -217,11 +236,11 @@ int csa_topk(const float* I, const int* q_pos, int B, int Tq, long long N_cap, i
  *            saturates); contents on entry do not matter.
  */
 size_t csa_mqa_workspace_size(int B, int Tq, int n_h, int d, long long n_keys_max);
-int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,
-                   const int* idx, int k, const void* W, int W_cap, int n_win, const float* sink,
-                   const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim, float rope_base,
-                   float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
-                   void* stream);
+int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, const float* E_scale,
+                   long long N_cap, const int* idx, int k, const void* W, const float* W_scale, int W_cap,
+                   int n_win, const float* sink, const int* q_pos, int B, int Tq, int n_h, int d,
+                   int rope_dim, float rope_base, float scale, int dtype, void* out, void* workspace,
+                   size_t ws_bytes, void* stream);
 
 /*
  * a5 — HCA core attention (method page §3.3: larger m', no overlap, dense
@@ -229,10 +248,10 @@ int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E
  * replaced by every visible entry s < min(N_cap, floor((i + 1) / m)).
  * workspace: at least csa_mqa_workspace_size(B, Tq, n_h, d, N_cap + n_win).
  */
-int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,
-                  int m, const void* W, int W_cap, int n_win, const float* sink,
-                  const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim, float rope_base,
-                  float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
+int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E, const float* E_scale,
+                  long long N_cap, int m, const void* W, const float* W_scale, int W_cap, int n_win,
+                  const float* sink, const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim,
+                  float rope_base, float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
                   void* stream);
 
 /*
@@ -318,10 +337,10 @@ int csa_grouped_out_proj(const void* o, const void* W1, const void* W2, void* y,
  */
 #define CSA_NOALLOC_SCRATCH_BYTES (16u << 20)
 int csa_sparse_mqa_noalloc(const void* q, const float* gamma_q, float eps, const void* E,
-                           long long N_cap, const int* idx, int k, const void* W, int W_cap,
-                           int n_win, const float* sink, const int* q_pos, int B, int Tq, int n_h,
-                           int d, int rope_dim, float rope_base, float scale, int dtype, void* out,
-                           void* stream);
+                           const float* E_scale, long long N_cap, const int* idx, int k, const void* W,
+                           const float* W_scale, int W_cap, int n_win, const float* sink,
+                           const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim,
+                           float rope_base, float scale, int dtype, void* out, void* stream);
 
 #ifdef __cplusplus
 }

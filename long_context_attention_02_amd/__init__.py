@@ -22,11 +22,11 @@ __all__ = [
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
     "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES", "csa_out_proj_workspace_size",
     "csa_grouped_out_proj", "csa_cache_append", "cache_ring_slots",
-    "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3", "CSA_MXFP4",
+    "CSA_F32", "CSA_BF16", "CSA_FP8_E4M3", "CSA_MXFP4", "CSA_KV_MIXED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
-CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4 = 0, 1, 2, 3
+CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4, CSA_KV_MIXED = 0, 1, 2, 3, 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -70,11 +70,11 @@ _lib.csa_topk.argtypes = [_P, _P, _I, _I, _L, _I, _I, _P, _P, _P, _S, _P]
 _lib.csa_mqa_workspace_size.restype = _S
 _lib.csa_mqa_workspace_size.argtypes = [_I, _I, _I, _I, _L]
 _lib.csa_sparse_mqa.restype = _I
-_lib.csa_sparse_mqa.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I,
-                                _F, _F, _I, _P, _P, _S, _P]
+_lib.csa_sparse_mqa.argtypes = [_P, _P, _F, _P, _P, _L, _P, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                                _I, _F, _F, _I, _P, _P, _S, _P]
 _lib.csa_sparse_mqa_noalloc.restype = _I
-_lib.csa_sparse_mqa_noalloc.argtypes = [_P, _P, _F, _P, _L, _P, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I,
-                                        _I, _F, _F, _I, _P, _P]
+_lib.csa_sparse_mqa_noalloc.argtypes = [_P, _P, _F, _P, _P, _L, _P, _I, _P, _P, _I, _I, _P, _P, _I, _I,
+                                        _I, _I, _I, _F, _F, _I, _P, _P]
 NOALLOC_SCRATCH_BYTES = 16 << 20
 _lib.csa_cache_append.restype = _I
 _lib.csa_cache_append.argtypes = [_I, _P, _I, _I, _I, _I, _I] + [_P] * 15 + [_I, _L, _P, _L, _P, _I, _P, _F, _I,
@@ -84,8 +84,8 @@ _lib.csa_out_proj_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.csa_grouped_out_proj.restype = _I
 _lib.csa_grouped_out_proj.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _S, _P]
 _lib.hca_dense_mqa.restype = _I
-_lib.hca_dense_mqa.argtypes = [_P, _P, _F, _P, _L, _I, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _F,
-                               _F, _I, _P, _P, _S, _P]
+_lib.hca_dense_mqa.argtypes = [_P, _P, _F, _P, _P, _L, _I, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I,
+                               _I, _F, _F, _I, _P, _P, _S, _P]
 
 
 class CsaError(RuntimeError):
@@ -144,9 +144,12 @@ def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_beg
     for name, t in (("Z_a", Z_a), ("C_b", C_b), ("Z_b", Z_b)):
         if t is not None and (t.shape != C_a.shape or t.dtype != C_a.dtype):
             raise ValueError(f"{name} must match C_a in shape and dtype")
-    mx = E.dtype == torch.uint8
-    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != (c // 2 if mx else c):
-        raise ValueError("E must be [B, rows, c] ([B, rows, c / 2] bytes for MXFP4)")
+    # uint8 rows: mixed (c + rope_dim bytes: fp8 codes, then bf16 rotated dims) or MXFP4 (c / 2)
+    mixed = E.dtype == torch.uint8 and E.dim() == 3 and rope_dim > 0 and E.shape[2] == c + rope_dim
+    mx = E.dtype == torch.uint8 and not mixed
+    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != (c // 2 if mx else c + rope_dim if mixed else c):
+        raise ValueError("E must be [B, rows, c] ([B, rows, c / 2] bytes for MXFP4, "
+                         "[B, rows, c + rope_dim] for mixed rows)")
     if E.shape[1] < (out_ring if out_ring > 0 else s_end):
         raise ValueError("E has fewer rows than the entries written")
     if mx and (E_scale is None or E_scale.dtype != torch.uint8 or tuple(E_scale.shape) != (B, E.shape[1], c // 32)):
@@ -159,8 +162,8 @@ def _compress_args(C_a, Z_a, C_b, Z_b, E, *, T: int, m: int, overlap: int, s_beg
             B, R, R * c, tok_base, T, _ptr(T_len, "T_len", torch.int32), c, m, overlap, s_begin, s_end,
             _ptr(gamma, "gamma", torch.float32), eps, rope_dim, rope_base,
             m if pos_stride is None else pos_stride, pos_offset,
-            _ptr(E, "E"), _dt(E), _ptr(E_scale, "E_scale", torch.uint8 if mx else torch.float32),
-            E.shape[1] * c, out_ring)
+            _ptr(E, "E"), CSA_KV_MIXED if mixed else _dt(E),
+            _ptr(E_scale, "E_scale", torch.uint8 if mx else torch.float32), E.shape[1] * c, out_ring)
 
 
 def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
@@ -229,12 +232,28 @@ def csa_mqa_workspace_size(B: int, Tq: int, n_h: int, d: int, n_keys_max: int) -
     return int(_lib.csa_mqa_workspace_size(B, Tq, n_h, d, n_keys_max))
 
 
-def _mqa_common(q, E, W, q_pos, out, sink, gamma_q):
+def _mqa_common(q, E, W, q_pos, out, sink, gamma_q, rope_dim=0, E_scale=None, W_scale=None):
+    """Shape checks; returns (B, Tq, n_h, d, dtype code, E_scale ptr, W_scale ptr).  uint8 E and W
+    are mixed rows of d + rope_dim bytes with fp32 row scales E_scale [B, N], W_scale [B, W_cap]."""
     B, Tq, n_h, d = q.shape
-    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != d or E.dtype != q.dtype:
-        raise ValueError("E must be [B, N, d] with q's dtype")
-    if W is not None and (W.dim() != 3 or W.shape[0] != B or W.shape[2] != d or W.dtype != q.dtype):
-        raise ValueError("W must be [B, W_cap, d] with q's dtype")
+    mixed = E.dtype == torch.uint8
+    row = d + rope_dim if mixed else d
+    kv_dt = torch.uint8 if mixed else q.dtype
+    if mixed and q.dtype != torch.bfloat16:
+        raise TypeError("mixed entries need bf16 queries")
+    if E.dim() != 3 or E.shape[0] != B or E.shape[2] != row or E.dtype != kv_dt:
+        raise ValueError("E must be [B, N, d] with q's dtype (uint8 [B, N, d + rope_dim] mixed rows)")
+    if W is not None and (W.dim() != 3 or W.shape[0] != B or W.shape[2] != row or W.dtype != kv_dt):
+        raise ValueError("W must be laid out as E ([B, W_cap, ...])")
+    es = ws = None
+    if mixed:
+        if E_scale is None or tuple(E_scale.shape) != (B, E.shape[1]):
+            raise ValueError("mixed entries need E_scale [B, N]")
+        es = _ptr(E_scale, "E_scale", torch.float32)
+        if W is not None:
+            if W_scale is None or tuple(W_scale.shape) != (B, W.shape[1]):
+                raise ValueError("mixed window rows need W_scale [B, W_cap]")
+            ws = _ptr(W_scale, "W_scale", torch.float32)
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if tuple(q_pos.shape) != (B, Tq):
@@ -243,55 +262,57 @@ def _mqa_common(q, E, W, q_pos, out, sink, gamma_q):
         raise ValueError("sink must be [n_h]")
     if gamma_q is not None and tuple(gamma_q.shape) != (d,):
         raise ValueError("gamma_q must be [d]")
-    return B, Tq, n_h, d
+    return B, Tq, n_h, d, (CSA_KV_MIXED if mixed else _dt(q)), es, ws
 
 
 def csa_sparse_mqa(q, E, idx, W, q_pos, out, *, n_win: int, sink=None, gamma_q=None, eps: float = 1e-6,
                    rope_dim: int = 0, rope_base: float = 10000.0, scale: float | None = None,
-                   workspace=None):
+                   workspace=None, E_scale=None, W_scale=None):
     """a4.  q [B, Tq, n_h, d], E [B, N, d], idx [B, Tq, k] int32, W [B, W_cap, d]
-    or None, q_pos [B, Tq] int32, out like q; sink [n_h], gamma_q [d] fp32."""
-    B, Tq, n_h, d = _mqa_common(q, E, W, q_pos, out, sink, gamma_q)
+    or None, q_pos [B, Tq] int32, out like q; sink [n_h], gamma_q [d] fp32.
+    Mixed entries: E uint8 [B, N, d + rope_dim] with E_scale [B, N] fp32, W
+    likewise with W_scale [B, W_cap]; q and out bf16."""
+    B, Tq, n_h, d, dt, es, wsc = _mqa_common(q, E, W, q_pos, out, sink, gamma_q, rope_dim, E_scale, W_scale)
     k = idx.shape[2]
     if tuple(idx.shape[:2]) != (B, Tq):
         raise ValueError("idx must be [B, Tq, k]")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.csa_sparse_mqa(
-        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), E.shape[1],
-        _ptr(idx, "idx", torch.int32, 3), k, _ptr(W, "W"), 0 if W is None else W.shape[1], n_win,
+        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), es, E.shape[1],
+        _ptr(idx, "idx", torch.int32, 3), k, _ptr(W, "W"), wsc, 0 if W is None else W.shape[1], n_win,
         _ptr(sink, "sink", torch.float32), _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d,
-        rope_dim, rope_base, (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
+        rope_dim, rope_base, (d ** -0.5) if scale is None else scale, dt, _ptr(out, "out"),
         _ptr(workspace, "workspace"), ws_bytes, _stream()))
 
 
 def csa_sparse_mqa_noalloc(q, E, idx, W, q_pos, out, *, n_win: int, sink=None, gamma_q=None,
                            eps: float = 1e-6, rope_dim: int = 0, rope_base: float = 10000.0,
-                           scale: float | None = None):
+                           scale: float | None = None, E_scale=None, W_scale=None):
     """a4 without a workspace: the split partials live in the library's static
     per-GPU scratch (NOALLOC_SCRATCH_BYTES); calls that overlap on one GPU race."""
-    B, Tq, n_h, d = _mqa_common(q, E, W, q_pos, out, sink, gamma_q)
+    B, Tq, n_h, d, dt, es, wsc = _mqa_common(q, E, W, q_pos, out, sink, gamma_q, rope_dim, E_scale, W_scale)
     k = idx.shape[2]
     if tuple(idx.shape[:2]) != (B, Tq):
         raise ValueError("idx must be [B, Tq, k]")
     _check(_lib.csa_sparse_mqa_noalloc(
-        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), E.shape[1],
-        _ptr(idx, "idx", torch.int32, 3), k, _ptr(W, "W"), 0 if W is None else W.shape[1], n_win,
+        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), es, E.shape[1],
+        _ptr(idx, "idx", torch.int32, 3), k, _ptr(W, "W"), wsc, 0 if W is None else W.shape[1], n_win,
         _ptr(sink, "sink", torch.float32), _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d,
-        rope_dim, rope_base, (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
+        rope_dim, rope_base, (d ** -0.5) if scale is None else scale, dt, _ptr(out, "out"),
         _stream()))
 
 
 def hca_dense_mqa(q, E, W, q_pos, out, *, m: int, n_win: int, sink=None, gamma_q=None, eps: float = 1e-6,
                   rope_dim: int = 0, rope_base: float = 10000.0, scale: float | None = None,
-                  workspace=None):
+                  workspace=None, E_scale=None, W_scale=None):
     """a5.  As csa_sparse_mqa over every visible entry s < floor((i+1)/m)."""
-    B, Tq, n_h, d = _mqa_common(q, E, W, q_pos, out, sink, gamma_q)
+    B, Tq, n_h, d, dt, es, wsc = _mqa_common(q, E, W, q_pos, out, sink, gamma_q, rope_dim, E_scale, W_scale)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.hca_dense_mqa(
-        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), E.shape[1], m,
-        _ptr(W, "W"), 0 if W is None else W.shape[1], n_win, _ptr(sink, "sink", torch.float32),
+        _ptr(q, "q", dims=4), _ptr(gamma_q, "gamma_q", torch.float32), eps, _ptr(E, "E"), es, E.shape[1], m,
+        _ptr(W, "W"), wsc, 0 if W is None else W.shape[1], n_win, _ptr(sink, "sink", torch.float32),
         _ptr(q_pos, "q_pos", torch.int32), B, Tq, n_h, d, rope_dim, rope_base,
-        (d ** -0.5) if scale is None else scale, _dt(q), _ptr(out, "out"),
+        (d ** -0.5) if scale is None else scale, dt, _ptr(out, "out"),
         _ptr(workspace, "workspace"), ws_bytes, _stream()))
 
 

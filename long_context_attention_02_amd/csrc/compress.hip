@@ -108,9 +108,21 @@ __device__ __forceinline__ void compress_store(const CompressJob& J, long long s
       v = (j & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
     }
     outv[nv] = v;
-    amax = fmaxf(amax, fabsf(v));
+    if (ODT != DT_MIX || j < rbeg) amax = fmaxf(amax, fabsf(v));   // mixed rows: the fp8 part only
   }
-  if constexpr (ODT == DT_FP8) {
+  if constexpr (ODT == DT_MIX) {
+    // mixed row: e4m3 codes of channels [0, rbeg) under one row scale, bf16 of the rest
+    const float am = block_reduce<true>(amax, red);
+    const float scale = am > 0.f ? am / 448.0f : 1.0f;
+    const size_t rowi = (size_t)b * (size_t)(out_bs / c) + (size_t)orow;
+    uint8_t* rb = (uint8_t*)E + rowi * (size_t)(c + rope_dim);
+    nv = 0;
+    for (int j = threadIdx.x; j < c; j += NT, ++nv) {
+      if (j < rbeg) rb[j] = f32_to_e4m3(outv[nv] / scale);
+      else *(uint16_t*)(rb + rbeg + 2 * (j - rbeg)) = f32_to_bf16_bits(outv[nv]);
+    }
+    if (threadIdx.x == 0) E_scale[rowi] = scale;
+  } else if constexpr (ODT == DT_FP8) {
     const float am = block_reduce<true>(amax, red);
     const float scale = am > 0.f ? am / 448.0f : 1.0f;
     nv = 0;
@@ -292,15 +304,17 @@ __global__ __launch_bounds__(COMP_THREADS) void compress_kernel(const CompressBa
   extern __shared__ float smem[];
   const CompressJob& J = jb.job[blockIdx.z];
   if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
-  switch (J.in_dtype * 4 + J.out_dtype) {
-    case DT_F32 * 4 + DT_F32: compress_entry<DT_F32, DT_F32>(J, smem); break;
-    case DT_F32 * 4 + DT_BF16: compress_entry<DT_F32, DT_BF16>(J, smem); break;
-    case DT_F32 * 4 + DT_FP8: compress_entry<DT_F32, DT_FP8>(J, smem); break;
-    case DT_F32 * 4 + DT_MX4: compress_entry<DT_F32, DT_MX4>(J, smem); break;
-    case DT_BF16 * 4 + DT_F32: compress_entry<DT_BF16, DT_F32>(J, smem); break;
-    case DT_BF16 * 4 + DT_BF16: compress_entry<DT_BF16, DT_BF16>(J, smem); break;
-    case DT_BF16 * 4 + DT_FP8: compress_entry<DT_BF16, DT_FP8>(J, smem); break;
-    default: compress_entry<DT_BF16, DT_MX4>(J, smem); break;
+  switch (J.in_dtype * 5 + J.out_dtype) {
+    case DT_F32 * 5 + DT_F32: compress_entry<DT_F32, DT_F32>(J, smem); break;
+    case DT_F32 * 5 + DT_BF16: compress_entry<DT_F32, DT_BF16>(J, smem); break;
+    case DT_F32 * 5 + DT_FP8: compress_entry<DT_F32, DT_FP8>(J, smem); break;
+    case DT_F32 * 5 + DT_MX4: compress_entry<DT_F32, DT_MX4>(J, smem); break;
+    case DT_F32 * 5 + DT_MIX: compress_entry<DT_F32, DT_MIX>(J, smem); break;
+    case DT_BF16 * 5 + DT_F32: compress_entry<DT_BF16, DT_F32>(J, smem); break;
+    case DT_BF16 * 5 + DT_BF16: compress_entry<DT_BF16, DT_BF16>(J, smem); break;
+    case DT_BF16 * 5 + DT_FP8: compress_entry<DT_BF16, DT_FP8>(J, smem); break;
+    case DT_BF16 * 5 + DT_MX4: compress_entry<DT_BF16, DT_MX4>(J, smem); break;
+    default: compress_entry<DT_BF16, DT_MIX>(J, smem); break;
   }
 }
 
@@ -493,12 +507,12 @@ __global__ __launch_bounds__(64 * COMPW_WAVES) void compress_wave_kernel(const C
   const long long e = item - jb.first[q];
   const long long s = J.s_begin + e % J.n_entries;
   const int b = (int)(e / J.n_entries);
-  switch (J.in_dtype * 4 + J.out_dtype) {
-    case DT_F32 * 4 + DT_F32: compress_entry_wave<DT_F32, DT_F32, MAXC>(J, s, b, lane); break;
-    case DT_F32 * 4 + DT_BF16: compress_entry_wave<DT_F32, DT_BF16, MAXC>(J, s, b, lane); break;
-    case DT_F32 * 4 + DT_FP8: compress_entry_wave<DT_F32, DT_FP8, MAXC>(J, s, b, lane); break;
-    case DT_BF16 * 4 + DT_F32: compress_entry_wave<DT_BF16, DT_F32, MAXC>(J, s, b, lane); break;
-    case DT_BF16 * 4 + DT_BF16: compress_entry_wave<DT_BF16, DT_BF16, MAXC>(J, s, b, lane); break;
+  switch (J.in_dtype * 5 + J.out_dtype) {
+    case DT_F32 * 5 + DT_F32: compress_entry_wave<DT_F32, DT_F32, MAXC>(J, s, b, lane); break;
+    case DT_F32 * 5 + DT_BF16: compress_entry_wave<DT_F32, DT_BF16, MAXC>(J, s, b, lane); break;
+    case DT_F32 * 5 + DT_FP8: compress_entry_wave<DT_F32, DT_FP8, MAXC>(J, s, b, lane); break;
+    case DT_BF16 * 5 + DT_F32: compress_entry_wave<DT_BF16, DT_F32, MAXC>(J, s, b, lane); break;
+    case DT_BF16 * 5 + DT_BF16: compress_entry_wave<DT_BF16, DT_BF16, MAXC>(J, s, b, lane); break;
     default: compress_entry_wave<DT_BF16, DT_FP8, MAXC>(J, s, b, lane); break;
   }
 }
@@ -658,17 +672,23 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
 
 __global__ __launch_bounds__(COMPX_THREADS) void compress_wide_kernel(const CompressBatch jb) {
   extern __shared__ float smem[];
-  const CompressJob& J = jb.job[blockIdx.z];
+  // the job is read where it lies, in the kernel-argument segment (jb is the only
+  // argument, at offset 0): indexing the by-value batch with blockIdx.z made the
+  // compiler copy all of it to scratch memory first
+  (void)jb;
+  const CompressJob& J = ((const CompressBatch*)__builtin_amdgcn_kernarg_segment_ptr())->job[blockIdx.z];
   if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
-  switch (J.in_dtype * 4 + J.out_dtype) {
-    case DT_F32 * 4 + DT_F32: compress_entry_wide<DT_F32, DT_F32>(J, smem); break;
-    case DT_F32 * 4 + DT_BF16: compress_entry_wide<DT_F32, DT_BF16>(J, smem); break;
-    case DT_F32 * 4 + DT_FP8: compress_entry_wide<DT_F32, DT_FP8>(J, smem); break;
-    case DT_F32 * 4 + DT_MX4: compress_entry_wide<DT_F32, DT_MX4>(J, smem); break;
-    case DT_BF16 * 4 + DT_F32: compress_entry_wide<DT_BF16, DT_F32>(J, smem); break;
-    case DT_BF16 * 4 + DT_BF16: compress_entry_wide<DT_BF16, DT_BF16>(J, smem); break;
-    case DT_BF16 * 4 + DT_FP8: compress_entry_wide<DT_BF16, DT_FP8>(J, smem); break;
-    default: compress_entry_wide<DT_BF16, DT_MX4>(J, smem); break;
+  switch (J.in_dtype * 5 + J.out_dtype) {
+    case DT_F32 * 5 + DT_F32: compress_entry_wide<DT_F32, DT_F32>(J, smem); break;
+    case DT_F32 * 5 + DT_BF16: compress_entry_wide<DT_F32, DT_BF16>(J, smem); break;
+    case DT_F32 * 5 + DT_FP8: compress_entry_wide<DT_F32, DT_FP8>(J, smem); break;
+    case DT_F32 * 5 + DT_MX4: compress_entry_wide<DT_F32, DT_MX4>(J, smem); break;
+    case DT_F32 * 5 + DT_MIX: compress_entry_wide<DT_F32, DT_MIX>(J, smem); break;
+    case DT_BF16 * 5 + DT_F32: compress_entry_wide<DT_BF16, DT_F32>(J, smem); break;
+    case DT_BF16 * 5 + DT_BF16: compress_entry_wide<DT_BF16, DT_BF16>(J, smem); break;
+    case DT_BF16 * 5 + DT_FP8: compress_entry_wide<DT_BF16, DT_FP8>(J, smem); break;
+    case DT_BF16 * 5 + DT_MX4: compress_entry_wide<DT_BF16, DT_MX4>(J, smem); break;
+    default: compress_entry_wide<DT_BF16, DT_MIX>(J, smem); break;
   }
 }
 
@@ -711,9 +731,9 @@ static bool wave_job(const CompressArgs& x) {
   const int vec = x.in_dtype == DT_F32 ? 4 : 8;
   // 16-byte pieces: every input row and (for bf16 output) every output row starts 16-byte aligned
   const bool in_al = inputs_in_pieces(x);
-  // (MXFP4 output takes the wide kernel: its store in this kernel spilled registers)
+  // (MXFP4 and mixed output take the other kernels: another store format here spilled registers)
   const bool out_al = (x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0)) &&
-                      x.out_dtype != DT_MX4;
+                      x.out_dtype != DT_MX4 && x.out_dtype != DT_MIX;
   // a job of a few dozen entries (decode) is pure latency, where one workgroup per
   // entry is quicker; many entries (prefill) are throughput, where a wave each is
   const long long items = (long long)x.B * (x.s_end - x.s_begin);

@@ -33,7 +33,9 @@ int ok() {
   return CSA_OK;
 }
 
-bool dtype_valid(int dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3 || dt == CSA_MXFP4; }
+bool dtype_valid(int dt) {
+  return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP8_E4M3 || dt == CSA_MXFP4 || dt == CSA_KV_MIXED;
+}
 
 }  // namespace
 
@@ -55,8 +57,11 @@ static int check_compress(const csa_compress_job& j, const char* who) {
   if (in_dtype != CSA_F32 && in_dtype != CSA_BF16)
     return fail(CSA_E_DTYPE, "%s: in_dtype must be F32 or BF16", who);
   if (!dtype_valid(out_dtype)) return fail(CSA_E_DTYPE, "%s: unknown out_dtype", who);
-  if ((out_dtype == CSA_FP8_E4M3 || out_dtype == CSA_MXFP4) && !E_scale)
-    return fail(CSA_E_NULL, "%s: E_scale is required for FP8 and MXFP4 output", who);
+  if ((out_dtype == CSA_FP8_E4M3 || out_dtype == CSA_MXFP4 || out_dtype == CSA_KV_MIXED) && !E_scale)
+    return fail(CSA_E_NULL, "%s: E_scale is required for FP8, MXFP4 and mixed output", who);
+  if (out_dtype == CSA_KV_MIXED && (rope_dim % 8 || (c - rope_dim) % 8 || out_batch_stride % c))
+    return fail(CSA_E_SHAPE, "%s: mixed rows need rope_dim and c - rope_dim multiples of 8 and "
+                "out_batch_stride %% c == 0", who);
   if (out_dtype == CSA_MXFP4 && (c % 32 || out_batch_stride % c))
     return fail(CSA_E_SHAPE, "%s: MXFP4 output needs c %% 32 == 0 and out_batch_stride %% c == 0", who);
   if (B < 1 || R < 1 || c < 1 || m < 1 || T < 1)
@@ -213,11 +218,14 @@ size_t csa_mqa_workspace_size(int B, int Tq, int n_h, int d, long long n_keys_ma
   return csa::mqa_workspace_bytes(B, Tq, n_h, d, n_keys_max, CSA_BF16);
 }
 
-static int mqa_common(const char* fn, const void* q, const void* E, long long N_cap, const void* W,
-                      int W_cap, int n_win, const int* q_pos, int B, int Tq, int n_h, int d,
-                      int rope_dim, int dtype, void* out) {
+static int mqa_common(const char* fn, const void* q, const void* E, const float* E_scale, long long N_cap,
+                      const void* W, const float* W_scale, int W_cap, int n_win, const int* q_pos, int B,
+                      int Tq, int n_h, int d, int rope_dim, int dtype, void* out) {
   if (!q || !E || !q_pos || !out) return fail(CSA_E_NULL, "%s: q, E, q_pos and out are required", fn);
-  if (dtype != CSA_F32 && dtype != CSA_BF16) return fail(CSA_E_DTYPE, "%s: dtype must be F32 or BF16", fn);
+  if (dtype != CSA_F32 && dtype != CSA_BF16 && dtype != CSA_KV_MIXED)
+    return fail(CSA_E_DTYPE, "%s: dtype must be F32, BF16 or KV_MIXED", fn);
+  if (dtype == CSA_KV_MIXED && (!E_scale || (n_win > 0 && !W_scale)))
+    return fail(CSA_E_NULL, "%s: KV_MIXED rows need E_scale (and W_scale with a window)", fn);
   if (B < 1 || Tq < 1 || n_h < 1 || d < 2 || N_cap < 1)
     return fail(CSA_E_SHAPE, "%s: sizes must be >= 1 (d >= 2)", fn);
   if (d & 1) return fail(CSA_E_SHAPE, "%s: d must be even", fn);
@@ -231,17 +239,17 @@ static int mqa_common(const char* fn, const void* q, const void* E, long long N_
   return CSA_OK;
 }
 
-int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,
-                   const int* idx, int k, const void* W, int W_cap, int n_win, const float* sink,
-                   const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim, float rope_base,
-                   float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
-                   void* stream) {
-  int st = mqa_common("csa_sparse_mqa", q, E, N_cap, W, W_cap, n_win, q_pos, B, Tq, n_h, d,
-                      rope_dim, dtype, out);
+int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E, const float* E_scale,
+                   long long N_cap, const int* idx, int k, const void* W, const float* W_scale, int W_cap,
+                   int n_win, const float* sink, const int* q_pos, int B, int Tq, int n_h, int d,
+                   int rope_dim, float rope_base, float scale, int dtype, void* out, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  int st = mqa_common("csa_sparse_mqa", q, E, E_scale, N_cap, W, W_scale, W_cap, n_win, q_pos, B, Tq, n_h,
+                      d, rope_dim, dtype, out);
   if (st != CSA_OK) return st;
   if (!idx) return fail(CSA_E_NULL, "csa_sparse_mqa: idx is required");
   if (k < 1 || k > 65536) return fail(CSA_E_SHAPE, "csa_sparse_mqa: k outside [1, 65536]");
-  csa::MqaArgs a{q, gamma_q, eps, E, N_cap, idx, k, 1, W, W_cap, n_win, sink, q_pos, B, Tq, n_h, d,
+  csa::MqaArgs a{q, gamma_q, eps, E, E_scale, N_cap, idx, k, 1, W, W_scale, W_cap, n_win, sink, q_pos, B, Tq, n_h, d,
                  rope_dim, rope_base, scale, dtype, out, workspace, ws_bytes};
   const char* why = "";
   st = csa::launch_mqa(a, (hipStream_t)stream, &why);
@@ -249,17 +257,17 @@ int csa_sparse_mqa(const void* q, const float* gamma_q, float eps, const void* E
   return ok();
 }
 
-int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E, long long N_cap,
-                  int m, const void* W, int W_cap, int n_win, const float* sink,
-                  const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim, float rope_base,
-                  float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
+int hca_dense_mqa(const void* q, const float* gamma_q, float eps, const void* E, const float* E_scale,
+                  long long N_cap, int m, const void* W, const float* W_scale, int W_cap, int n_win,
+                  const float* sink, const int* q_pos, int B, int Tq, int n_h, int d, int rope_dim,
+                  float rope_base, float scale, int dtype, void* out, void* workspace, size_t ws_bytes,
                   void* stream) {
-  int st = mqa_common("hca_dense_mqa", q, E, N_cap, W, W_cap, n_win, q_pos, B, Tq, n_h, d,
-                      rope_dim, dtype, out);
+  int st = mqa_common("hca_dense_mqa", q, E, E_scale, N_cap, W, W_scale, W_cap, n_win, q_pos, B, Tq, n_h,
+                      d, rope_dim, dtype, out);
   if (st != CSA_OK) return st;
   if (m < 1) return fail(CSA_E_SHAPE, "hca_dense_mqa: m must be >= 1");
   if (N_cap > 2147483647LL) return fail(CSA_E_UNSUPPORTED, "hca_dense_mqa: N_cap must fit int32");
-  csa::MqaArgs a{q, gamma_q, eps, E, N_cap, nullptr, 0, m, W, W_cap, n_win, sink, q_pos, B, Tq, n_h,
+  csa::MqaArgs a{q, gamma_q, eps, E, E_scale, N_cap, nullptr, 0, m, W, W_scale, W_cap, n_win, sink, q_pos, B, Tq, n_h,
                  d, rope_dim, rope_base, scale, dtype, out, workspace, ws_bytes};
   const char* why = "";
   st = csa::launch_mqa(a, (hipStream_t)stream, &why);
@@ -375,12 +383,14 @@ int scratch_ptr(const char* fn, void** out) {
 }  // namespace
 
 extern "C" int csa_sparse_mqa_noalloc(const void* q, const float* gamma_q, float eps, const void* E,
-                                      long long N_cap, const int* idx, int k, const void* W, int W_cap,
-                                      int n_win, const float* sink, const int* q_pos, int B, int Tq,
-                                      int n_h, int d, int rope_dim, float rope_base, float scale,
-                                      int dtype, void* out, void* stream) {
+                                      const float* E_scale, long long N_cap, const int* idx, int k,
+                                      const void* W, const float* W_scale, int W_cap, int n_win,
+                                      const float* sink, const int* q_pos, int B, int Tq, int n_h, int d,
+                                      int rope_dim, float rope_base, float scale, int dtype, void* out,
+                                      void* stream) {
   const char* fn = "csa_sparse_mqa_noalloc";
-  int st = mqa_common(fn, q, E, N_cap, W, W_cap, n_win, q_pos, B, Tq, n_h, d, rope_dim, dtype, out);
+  int st = mqa_common(fn, q, E, E_scale, N_cap, W, W_scale, W_cap, n_win, q_pos, B, Tq, n_h, d, rope_dim,
+                      dtype, out);
   if (st != CSA_OK) return st;
   if (!idx) return fail(CSA_E_NULL, "%s: idx is required", fn);
   if (k < 1 || k > 65536) return fail(CSA_E_SHAPE, "%s: k outside [1, 65536]", fn);
@@ -391,7 +401,7 @@ extern "C" int csa_sparse_mqa_noalloc(const void* q, const float* gamma_q, float
                 "scratch; use csa_sparse_mqa with a workspace", fn, need, (unsigned)CSA_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
   if (need > 0 && (st = scratch_ptr(fn, &ws)) != CSA_OK) return st;
-  csa::MqaArgs a{q, gamma_q, eps, E, N_cap, idx, k, 1, W, W_cap, n_win, sink, q_pos, B, Tq, n_h, d,
+  csa::MqaArgs a{q, gamma_q, eps, E, E_scale, N_cap, idx, k, 1, W, W_scale, W_cap, n_win, sink, q_pos, B, Tq, n_h, d,
                  rope_dim, rope_base, scale, dtype, out, ws, need > 0 ? (size_t)CSA_NOALLOC_SCRATCH_BYTES : 0};
   const char* why = "";
   st = csa::launch_mqa(a, (hipStream_t)stream, &why);

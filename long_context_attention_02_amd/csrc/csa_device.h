@@ -17,7 +17,10 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // DT_MX4: OCP MXFP4 -- FP4 E2M1 codes packed two per byte (the even channel in
 // the low nibble) with one E8M0 scale byte per 32 channels in a separate array
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MX4 = 3 };
+// DT_MIX: mixed KV rows -- the first c - rope_dim channels as e4m3 codes (one
+// fp32 scale per row in a separate array), then the last rope_dim channels as
+// bf16: c + rope_dim bytes per row
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MX4 = 3, DT_MIX = 4 };
 
 // ---- scalar conversions ---------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

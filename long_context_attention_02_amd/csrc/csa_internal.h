@@ -65,11 +65,13 @@ struct MqaArgs {
   const float* gamma_q;
   float eps;
   const void* E;
+  const float* E_scale;   // mixed entries: the row scales ([B][N_cap]); else NULL
   long long N_cap;
   const int* idx;   // NULL for dense
   int k;            // sparse slots
   int m;            // dense visibility
   const void* W;
+  const float* W_scale;   // mixed window rows: the row scales ([B][W_cap]); else NULL
   int W_cap, n_win;
   const float* sink;
   const int* q_pos;

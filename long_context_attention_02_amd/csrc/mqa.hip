@@ -805,6 +805,7 @@ static constexpr int MQ_DEC_TBL_SMALL = MQ_DEC_SPLIT_LONG > MQ_DEC_SPLIT_SMALL ?
 // CSA query (k + n_win slots) is one workgroup and needs no combine.
 static constexpr int MQ_DEC_TABLE = 2048;
 static constexpr int MQ_DEC_NBUF = 3;      // LDS chunk ring
+static constexpr int MQ_MIX_ROPE = 64;     // rotated (bf16) dims of a mixed row
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations complete
 // (lgkmcnt 0) and its vector-memory operations drop to at most VM outstanding
@@ -902,6 +903,9 @@ struct DecRows {
   const uint16_t* E_b;        // this sequence's entries
   const uint16_t* W_b;        // this sequence's window ring
   const uint16_t* dummy;      // a valid row, loaded for absent slots (their scores are masked)
+  const float* Es_b;          // mixed rows: this sequence's entry row scales
+  const float* Ws_b;          // mixed rows: this sequence's window row scales
+  long long row_bytes;        // bytes per stored row (2 D, or D + rope_dim for mixed rows)
   long long s0;               // first slot of the range
   int n_rows;                 // slots in the range
   int n_sel;                  // of them, entry slots (the rest are window slots)
@@ -914,8 +918,9 @@ struct DecRows {
 // false for an absent slot, whose row is the dummy.  Selects only, no branches:
 // a divergent branch here would pull the selection loads into it, each with
 // its own wait.
-template <int D, bool DENSE>
-__device__ __forceinline__ const uint16_t* dec_slot_row(int rel, int e, const DecRows& R, bool* ok) {
+template <int D, bool DENSE, bool MIX = false>
+__device__ __forceinline__ const uint16_t* dec_slot_row(int rel, int e, const DecRows& R, bool* ok,
+                                                        float* rs = nullptr) {
   const bool in_rows = rel < R.n_rows;
   const bool is_sel = rel < R.n_sel;
   const long long ent = DENSE ? R.s0 + rel : (long long)e;
@@ -923,26 +928,34 @@ __device__ __forceinline__ const uint16_t* dec_slot_row(int rel, int e, const De
   int ring = R.ring0 + (rel - R.n_sel);   // fewer window slots than ring rows: one wrap at most
   ring = ring >= R.W_cap ? ring - R.W_cap : ring;
   *ok = in_rows && (!is_sel || ent_ok);
-  const uintptr_t pe = (uintptr_t)R.E_b + (uintptr_t)(max(ent, 0LL) * (2LL * D));
-  const uintptr_t pw = (uintptr_t)R.W_b + (uintptr_t)((long long)max(ring, 0) * (2LL * D));
+  const long long rb = MIX ? R.row_bytes : 2LL * D;
+  const uintptr_t pe = (uintptr_t)R.E_b + (uintptr_t)(max(ent, 0LL) * rb);
+  const uintptr_t pw = (uintptr_t)R.W_b + (uintptr_t)((long long)max(ring, 0) * rb);
+  if constexpr (MIX) {
+    // the row's scale (unguarded loads at clamped rows, selected after)
+    const float se = R.Es_b[max(min(ent, (long long)R.N_cap - 1), 0LL)];
+    const float sw = R.Ws_b ? R.Ws_b[max(min(ring, R.W_cap - 1), 0)] : 1.f;
+    *rs = !*ok ? 1.f : (is_sel ? se : sw);
+  }
   return (const uint16_t*)(!*ok ? (uintptr_t)R.dummy : (is_sel ? pe : pw));
 }
 
 // start loading chunk c: rows RPW w .. RPW w + RPW - 1 of it are this wave's,
 // their addresses read from the workgroup's slot table
+// (mixed rows: cpr = row bytes / 16 pieces per row, rows at a stride of rbp bytes)
 template <int D, int NW>
 __device__ __forceinline__ void dec_issue(int c, const uint16_t* const* sptr, uint8_t* buf, int wave,
-                                          int lane) {
-  constexpr int RBP = 2 * D + 16, CPR = 2 * D / 16, RPW = MQ_CH / NW;
+                                          int lane, int cpr = 2 * D / 16, int rbp = 2 * D + 16) {
+  constexpr int RPW = MQ_CH / NW;
   const int rel0 = MQ_CH * c + RPW * wave;
   const uint16_t* p[RPW];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr) p[rr] = sptr[rel0 + rr];
 #pragma unroll
   for (int rr = 0; rr < RPW; ++rr)
-    if (lane < CPR)
+    if (lane < cpr)
       __builtin_amdgcn_global_load_lds((const void*)(p[rr] + 8 * lane),
-                                       (__attribute__((address_space(3))) void*)(buf + (RPW * wave + rr) * RBP),
+                                       (__attribute__((address_space(3))) void*)(buf + (RPW * wave + rr) * rbp),
                                        16, 0, 0);
 }
 
@@ -963,13 +976,24 @@ __device__ __forceinline__ float quad_sum(float x) {
 }
 
 // HTW: head tiles (16 heads each) per wave (host choice: dec_htw)
-template <int D, bool DENSE, int NW, int TBL, int HTW>
+// MIX: entries and window rows are mixed rows (e4m3 codes of the first
+// D - MQ_MIX_ROPE dims under a row scale, then bf16 of the MQ_MIX_ROPE rotated
+// dims; scales in Es and Ws).  Their raw bytes stream through the LDS ring as
+// the bf16 rows do; once a chunk has landed every thread widens its share of
+// the codes into one bf16 chunk buffer (exact: every e4m3 value is a bf16
+// value) and copies the rotated dims.  The row scale never rounds a stored
+// value: the scores take it as s_key * (q . codes) + (q . rotated dims), the
+// rotated share accumulated a second time on its own (the query with the other
+// dims zeroed), and P.V as (p * s_key) . codes on the code dims and
+// p . rotated on the rest, split at a 16-dim output tile boundary.
+template <int D, bool DENSE, int NW, int TBL, int HTW, bool MIX = false>
 __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, float eps,
     const uint16_t* __restrict__ E, long long N_cap, const int* __restrict__ idx, int k, int m,
     const uint16_t* __restrict__ W, int W_cap, int n_win, const float* __restrict__ sink,
     const int* __restrict__ q_pos, int Tq, int n_h, int rope_dim, RopeRatio rope, float scale,
-    int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws) {
+    int kps, int n_split, long long n_units, uint16_t* __restrict__ out, float* __restrict__ ws,
+    const float* __restrict__ Es, const float* __restrict__ Ws) {
   constexpr int KS = D / 32;          // S^T K-steps (8 dims per lane each)
   constexpr int NT = D / 16;          // 16-dim output tiles
   constexpr int RBP = 2 * D + 16;     // LDS row stride
@@ -987,6 +1011,16 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
                     TBL % MQ_CH == 0 && MQ_DEC_TBL_SMALL <= MQ_DEC_TABLE,
                 "whole chunks per range");
   __shared__ const uint16_t* sptr[TBL];   // row of every slot of the range
+  __shared__ __attribute__((aligned(16))) float sscale[MIX ? TBL : 4];  // mixed rows: each slot's row scale
+  constexpr int NOPE = MIX ? D - MQ_MIX_ROPE : D;              // mixed rows: the e4m3 dims
+  // lane group g feeds dims D/4 g + 8 ks .. of K-step ks: the rotated dims are those
+  // of group 3 from K-step MIX_KS0 on, and whole 16-dim output tiles from NOPE on
+  constexpr int MIX_KS0 = (D / 4 - (D - NOPE)) / 8;
+  static_assert(!MIX || (MQ_MIX_ROPE <= D / 4 && MQ_MIX_ROPE % 16 == 0), "rotated dims in the last quarter");
+  constexpr int RAW_ROW = MIX ? NOPE + 2 * MQ_MIX_ROPE : 2 * D;   // stored bytes per row
+  constexpr int raw_rb = RAW_ROW + 16;                         // LDS ring row stride
+  constexpr int raw_cpr = RAW_ROW / 16;                        // 16-byte pieces per row
+  uint8_t* const convb = kv + MQ_DEC_NBUF * MQ_CH * raw_rb;   // mixed rows: the widened chunk
   __shared__ uint32_t smask[NCH_MAX];              // bit r of chunk c: slot 32 c + r exists
   __shared__ f32x4_t rs_tmp[NW * 8 * 64];   // per wave: eight output tiles, for the rare rescale
 
@@ -1012,9 +1046,12 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   R.s0 = (long long)sp * kps;
   R.n_rows = (int)max(0LL, min((long long)kps, qs.n_slots - R.s0));
   R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
-  R.E_b = E + (size_t)b * (size_t)N_cap * D;
-  R.W_b = W ? W + (size_t)b * (size_t)W_cap * D : nullptr;
+  R.row_bytes = RAW_ROW;
+  R.E_b = (const uint16_t*)((const uint8_t*)E + (size_t)b * (size_t)N_cap * (size_t)R.row_bytes);
+  R.W_b = W ? (const uint16_t*)((const uint8_t*)W + (size_t)b * (size_t)W_cap * (size_t)R.row_bytes) : nullptr;
   R.dummy = R.E_b;
+  R.Es_b = MIX ? Es + (size_t)b * (size_t)N_cap : nullptr;
+  R.Ws_b = (MIX && W) ? Ws + (size_t)b * (size_t)W_cap : nullptr;
   R.W_cap = W_cap;
   R.N_cap = (int)min(N_cap, 2147483647LL);
   R.ring0 = W_cap > 0 ? (int)((qs.win_lo + max(0LL, R.s0 - qs.n_sel)) % W_cap) : 0;
@@ -1062,8 +1099,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   for (int e = 0; e < IPT; ++e) {
     const int t = threadIdx.x + 64 * NW * e;
     bool ok;
-    const uint16_t* p = dec_slot_row<D, DENSE>(t, DENSE ? 0 : iv[e], R, &ok);
+    float rs = 1.f;
+    const uint16_t* p = dec_slot_row<D, DENSE, MIX>(t, DENSE ? 0 : iv[e], R, &ok, &rs);
     if (t < TBL) sptr[t] = p;
+    if constexpr (MIX)
+      if (t < TBL) sscale[t] = rs;
     const unsigned long long bal = __ballot(ok);
     if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
   }
@@ -1102,7 +1142,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   lds_sync<0>();   // selection, RoPE table and gamma visible
 #pragma unroll
   for (int c = 0; c < PF; ++c)
-    if (c < nch) dec_issue<D, NW>(c, sptr, kv + c * CHB, wave, lane);
+    if (c < nch) dec_issue<D, NW>(c, sptr, kv + c * MQ_CH * raw_rb, wave, lane, raw_cpr, raw_rb);
 
   // q^ = RoPE_i(RMSNorm(q)) as bf16 B fragments of S^T: lane (g, j) holds head 16 ht + j,
   // dims (D/4) g + 8 ks + 0..7; the RoPE table holds (1, 0) for dims that are not rotated.
@@ -1154,15 +1194,52 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     else lds_sync<0>();
     const uint32_t vmask = smask[c];
     const uint8_t* kb = kv + (c % MQ_DEC_NBUF) * CHB;
+    float skey[2][4];   // mixed rows: scales of keys 16 kt + 4 g + r of the chunk
+    if constexpr (MIX) {
+      // widen the landed chunk into the bf16 chunk buffer, 8 dims per piece: e4m3
+      // codes to bf16 (exact), the rotated dims copied as they are
+      const uint8_t* rawc = kv + (c % MQ_DEC_NBUF) * MQ_CH * raw_rb;
+      constexpr int PPR = D / 8;
+      for (int p = threadIdx.x; p < MQ_CH * PPR; p += 64 * NW) {
+        const int rr = p / PPR, d0 = 8 * (p % PPR);
+        u32x4_t o;
+        if (d0 < NOPE) {
+          const u32x2_t w = *(const u32x2_t*)(rawc + rr * raw_rb + d0);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], false);
+            const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[h], true);
+            o[2 * h] = pack2_bf16_hw(lo[0], lo[1]);
+            o[2 * h + 1] = pack2_bf16_hw(hi[0], hi[1]);
+          }
+        } else {
+          o = *(const u32x4_t*)(rawc + rr * raw_rb + NOPE + 2 * (d0 - NOPE));
+        }
+        *(u32x4_t*)(convb + rr * RBP + 2 * d0) = o;
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x4_t v = *(const f32x4_t*)(&sscale[MQ_CH * c + 16 * kt + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) skey[kt][r] = v[r];
+      }
+      if (c + 1 < nch && PF >= 2) lds_sync<(PF >= 2 ? RPW : 0)>();
+      else lds_sync<0>();
+      kb = convb;
+    }
 
     // S^T: 32 keys x 16 HTW heads over all D dims.  The key operands stream in
     // groups of four K-steps (both key tiles); a group's LDS reads are issued
     // before the previous group's MFMAs, so their latency hides behind them.
     f32x4_t S[2][HTW];
+    f32x4_t Sr[2][MIX ? HTW : 1];   // mixed rows: the rotated dims' share of the scores
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ht = 0; ht < HTW; ++ht) S[kt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int ht = 0; ht < HTW; ++ht) {
+        S[kt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (MIX) Sr[kt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     constexpr int NGRP = KS / 4;
     static_assert(KS % 4 == 0, "K-steps in groups of four");
     bf16x8_t ka[2][8];
@@ -1184,15 +1261,38 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int ht = 0; ht < HTW; ++ht)
+            for (int ht = 0; ht < HTW; ++ht) {
               S[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[pg & 1][2 * u + kt], qf[ht][4 * pg + u],
                                                                   S[kt][ht], 0, 0, 0);
+              if constexpr (MIX) {
+                // the rotated dims' share alone: the query with every other dim zeroed
+                // (lane group 3 holds the last quarter of the dims, the rotated ones
+                // from K-step MIX_KS0 on)
+                if (4 * pg + u >= MIX_KS0) {
+                  const bf16x8_t qr = g == 3 ? qf[ht][4 * pg + u] : bf16x8_t{};
+                  Sr[kt][ht] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[pg & 1][2 * u + kt], qr, Sr[kt][ht],
+                                                                       0, 0, 0);
+                }
+              }
+            }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (MIX) {
+      // score = s_key * (code share) + rotated share; the code share is the whole
+      // fp32 sum minus the rotated one (fp32 sums: far below the bf16 inputs' precision)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < HTW; ++ht)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            S[kt][ht][r] = skey[kt][r] * (S[kt][ht][r] - Sr[kt][ht][r]) + Sr[kt][ht][r];
+    }
     // the next chunk into the slot that chunk c - 1 left (every wave is past it);
     // issued after the scores, so a full load queue cannot hold them up
-    if (c + PF < nch) dec_issue<D, NW>(c + PF, sptr, kv + ((c + PF) % MQ_DEC_NBUF) * CHB, wave, lane);
+    if (c + PF < nch)
+      dec_issue<D, NW>(c + PF, sptr, kv + ((c + PF) % MQ_DEC_NBUF) * MQ_CH * raw_rb, wave, lane, raw_cpr, raw_rb);
 
     // online softmax per head; the reference only moves when a chunk maximum
     // exceeds it by MQ_REF_SLACK, so O is rarely rescaled
@@ -1259,6 +1359,7 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       }
     }
     bf16x8_t pf[HTW];
+    bf16x8_t pfs[MIX ? HTW : 1];   // mixed rows: p times its key's scale, for the code dims
 #pragma unroll
     for (int ht = 0; ht < HTW; ++ht) {
       u32x4_t pw;
@@ -1267,6 +1368,13 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       pw[2] = pack2_bf16_hw(S[1][ht][0], S[1][ht][1]);
       pw[3] = pack2_bf16_hw(S[1][ht][2], S[1][ht][3]);
       pf[ht] = __builtin_bit_cast(bf16x8_t, pw);
+      if constexpr (MIX) {
+        pw[0] = pack2_bf16_hw(S[0][ht][0] * skey[0][0], S[0][ht][1] * skey[0][1]);
+        pw[1] = pack2_bf16_hw(S[0][ht][2] * skey[0][2], S[0][ht][3] * skey[0][3]);
+        pw[2] = pack2_bf16_hw(S[1][ht][0] * skey[1][0], S[1][ht][1] * skey[1][1]);
+        pw[3] = pack2_bf16_hw(S[1][ht][2] * skey[1][2], S[1][ht][3] * skey[1][3]);
+        pfs[ht] = __builtin_bit_cast(bf16x8_t, pw);
+      }
     }
     // P.V: V read transposed (keys 4g..4g+3 and 16+4g..16+4g+3 of column j of each tile)
     const uint32_t b0 = lds_addr(kb) + tr0 * RBP + 8 * (j & 3);
@@ -1283,8 +1391,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
         const u32x4_t vw = {vr[2 * u][0], vr[2 * u][1], vr[2 * u + 1][0], vr[2 * u + 1][1]};
         const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vw);
 #pragma unroll
-        for (int ht = 0; ht < HTW; ++ht)
-          O[ht][TPW * mb + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht], vf, O[ht][TPW * mb + u], 0, 0, 0);
+        for (int ht = 0; ht < HTW; ++ht) {
+          const bool code_tile = MIX && 16 * (TPW * mb + u) < NOPE;
+          O[ht][TPW * mb + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(code_tile ? pfs[MIX ? ht : 0] : pf[ht], vf,
+                                                                        O[ht][TPW * mb + u], 0, 0, 0);
+        }
       }
     }
   }
@@ -1320,7 +1431,8 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     constexpr int CW = D >= 512 ? 256 : D / 2;   // dims per staged block
     constexpr int CRS = CW + 4;                  // staged row stride (floats)
     constexpr int LPH = CW / 8;                  // lanes per head row on the way out
-    static_assert(16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
+    // (mixed rows: the host sizes the dynamic LDS to hold the staging as well)
+    static_assert(MIX || 16 * CRS * 4 * NW <= MQ_DEC_NBUF * CHB, "staging fits the chunk ring");
     lds_sync<0>();   // every wave is done with the chunk ring
     float* stg = (float*)kv + wave * 16 * CRS;
     float pscale[HTW];   // split partials: scale of head 16 ht + j
@@ -1501,7 +1613,7 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
 // output in 16-byte pieces
 static bool mqa_aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 static bool mqa_mfma_ok(const MqaArgs& a) {
-  return a.dtype == DT_BF16 && (a.d == 128 || a.d == 256 || a.d == 512) && a.n_h % 16 == 0 &&
+  return (a.dtype == DT_BF16 || a.dtype == DT_MIX) && (a.d == 128 || a.d == 256 || a.d == 512) && a.n_h % 16 == 0 &&
          mqa_aligned16(a.q) && mqa_aligned16(a.E) && mqa_aligned16(a.W) && mqa_aligned16(a.out);
 }
 
@@ -1546,7 +1658,7 @@ static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int
 }
 
 size_t mqa_workspace_bytes(int B, int Tq, int n_h, int d, long long n_slots_max, int dtype) {
-  if (!(dtype == DT_BF16 && (d == 128 || d == 256 || d == 512) && n_h % 16 == 0)) return 0;
+  if (!((dtype == DT_BF16 || dtype == DT_MIX) && (d == 128 || d == 256 || d == 512) && n_h % 16 == 0)) return 0;
   int kps, n_split;
   mqa_split(Tq, n_h, d, n_slots_max, &kps, &n_split);
   if (n_split == 1) return 0;
@@ -1575,23 +1687,35 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
                        n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
 }
 
-template <int D, bool DENSE, int NW, int HTW>
+// dynamic LDS of the streaming kernel: the chunk ring (raw mixed rows plus the
+// widened chunk for mixed entries) and, reusing it, the output staging
+template <int D, int NW, bool MIX>
+static size_t decode_lds_bytes() {
+  const size_t bf_row = 2 * D + 16;
+  if (!MIX) return (size_t)MQ_DEC_NBUF * MQ_CH * bf_row;
+  const size_t ring = (size_t)MQ_DEC_NBUF * MQ_CH * (D + MQ_MIX_ROPE + 16) + MQ_CH * bf_row;
+  constexpr int CW = D >= 512 ? 256 : D / 2;
+  const size_t stage = (size_t)16 * (CW + 4) * 4 * NW;
+  return ring > stage ? ring : stage;
+}
+
+template <int D, bool DENSE, int NW, int HTW, bool MIX>
 static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const int n_hg = a.n_h / (16 * HTW * NW);
   const long long units = (long long)a.B * a.Tq * n_split;
   const long long blocks = ((units + 7) / 8) * 8 * n_hg;
-  const size_t lds = (size_t)MQ_DEC_NBUF * MQ_CH * (2 * D + 16);
+  const size_t lds = decode_lds_bytes<D, NW, MIX>();
   // the small slot table for decode ranges (<= 192 slots), the large one for prefill
-  auto kfn = kps <= MQ_DEC_TBL_SMALL ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TBL_SMALL, HTW>
-                                     : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE, HTW>;
+  auto kfn = kps <= MQ_DEC_TBL_SMALL ? mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TBL_SMALL, HTW, MIX>
+                                     : mqa_decode_kernel<D, DENSE, NW, MQ_DEC_TABLE, HTW, MIX>;
   if (lds > 65536)
     (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(kfn, dim3((unsigned)blocks), dim3(64 * NW), lds, st,
                      (const uint16_t*)a.q, a.gamma_q, a.eps, (const uint16_t*)a.E, a.N_cap, a.idx,
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
                      a.rope_dim, rope_rr, a.scale, kps, n_split, units, (uint16_t*)a.out,
-                     (float*)a.ws);
+                     (float*)a.ws, a.E_scale, a.W_scale);
   if (n_split > 1)
     hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
                        dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
@@ -1599,27 +1723,39 @@ static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t
 }
 
 // waves per workgroup: as many head groups of one wave as divide n_h, up to four
-template <int D, bool DENSE, int HTW>
+template <int D, bool DENSE, int HTW, bool MIX>
 static void launch_decode_w(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
   constexpr int HW = 16 * HTW;
-  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4, HTW>(a, kps, n_split, st);
-  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2, HTW>(a, kps, n_split, st);
-  else launch_decode_nw<D, DENSE, 1, HTW>(a, kps, n_split, st);
+  if (a.n_h % (4 * HW) == 0) launch_decode_nw<D, DENSE, 4, HTW, MIX>(a, kps, n_split, st);
+  else if (a.n_h % (2 * HW) == 0) launch_decode_nw<D, DENSE, 2, HTW, MIX>(a, kps, n_split, st);
+  else launch_decode_nw<D, DENSE, 1, HTW, MIX>(a, kps, n_split, st);
 }
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool MIX>
 static void launch_decode(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
-  if constexpr (D >= 512) {
-    if (dec_htw(a.Tq, a.n_h, D) == 1) {
-      launch_decode_w<D, DENSE, 1>(a, kps, n_split, st);
-      return;
+  if constexpr (MIX) {
+    // mixed rows keep one head tile per wave: with two, the second score and
+    // weight sets they need do not fit the registers
+    launch_decode_w<D, DENSE, 1, MIX>(a, kps, n_split, st);
+  } else {
+    if constexpr (D >= 512) {
+      if (dec_htw(a.Tq, a.n_h, D) == 1) {
+        launch_decode_w<D, DENSE, 1, MIX>(a, kps, n_split, st);
+        return;
+      }
     }
+    launch_decode_w<D, DENSE, 2, MIX>(a, kps, n_split, st);
   }
-  launch_decode_w<D, DENSE, 2>(a, kps, n_split, st);
 }
 
 template <int D, bool DENSE>
 static void launch_mfma_d(const MqaArgs& a, int kps, int n_split, hipStream_t st) {
-  if (mqa_decode_ok(a.Tq, a.n_h, a.d)) launch_decode<D, DENSE>(a, kps, n_split, st);
+  if constexpr (D == 512) {
+    if (a.dtype == DT_MIX) {
+      launch_decode<D, DENSE, true>(a, kps, n_split, st);
+      return;
+    }
+  }
+  if (mqa_decode_ok(a.Tq, a.n_h, a.d)) launch_decode<D, DENSE, false>(a, kps, n_split, st);
   else if (kps <= MQ_GROUP) launch_mfma_v<D, DENSE, false>(a, kps, n_split, st);
   else launch_mfma_v<D, DENSE, true>(a, kps, n_split, st);
 }
@@ -1628,6 +1764,17 @@ int launch_mqa(const MqaArgs& a, hipStream_t st, const char** why) {
   const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
   const bool dense = a.idx == nullptr;
   const long long slots_max = mqa_slots_max(a);
+  if (a.dtype == DT_MIX) {
+    // mixed rows: the streaming kernel only
+    if (a.d != 512 || !mqa_mfma_ok(a) || !mqa_decode_ok(a.Tq, a.n_h, a.d)) {
+      *why = "mixed-precision entries need d = 512, n_h a multiple of 16 and 16-byte aligned q, E, W and out";
+      return 4;
+    }
+    if (a.rope_dim != MQ_MIX_ROPE) {
+      *why = "mixed-precision entries need rope_dim = 64 (the bf16 part of the row)";
+      return 4;
+    }
+  }
   if (mqa_mfma_ok(a)) {
     int kps, n_split;
     mqa_split(a.Tq, a.n_h, a.d, slots_max, &kps, &n_split);

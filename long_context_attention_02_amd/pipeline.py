@@ -27,12 +27,32 @@ def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _kv_rows(wl, rows: int, device):
+    """A cache of KV rows (entries or window rows) in the workload's storage:
+    (rows tensor, row scales or None).  Mixed rows are d + rope_dim bytes (e4m3
+    codes of the first d - rope_dim dims, then the rotated dims as bf16) with
+    one fp32 scale per row."""
+    if wl.kv_dtype == "mixed":
+        return (torch.zeros((wl.B, rows, wl.d + wl.rope_dim), dtype=torch.uint8, device=device),
+                torch.zeros((wl.B, rows), dtype=torch.float32, device=device))
+    return torch.zeros((wl.B, rows, wl.d), dtype=_TD[wl.kv_dtype], device=device), None
+
+
 class _Common:
+    E_scale = W_scale = None
+
+    def _kv_gamma(self, g, wl):
+        """RMSNorm weight of the entries and window rows: 1, or 1 + N(0, 1/16)."""
+        from synth import workloads as W_
+        if wl.kv_gamma == "normal":
+            return (1.0 + 0.25 * g.normal(W_.T_GAMMA, (wl.d,), "f32", per_slot=False)).contiguous()
+        return torch.ones(wl.d, dtype=torch.float32, device=self.dev)
+
     def _window_setup(self, g, wl, lo_tok: int, n_rows: int, tid_raw: int):
         """Window rows of tokens lo_tok .. lo_tok + n_rows - 1 into the ring W."""
         B, d = wl.B, wl.d
         self.win_raw = g.normal(tid_raw, (B, n_rows, d), wl.dtype)
-        self.W = torch.zeros((B, wl.W_cap, d), dtype=_TD[wl.dtype], device=self.dev)
+        self.W, self.W_scale = _kv_rows(wl, wl.W_cap, self.dev)
         self._win_rows(lo_tok, lo_tok + n_rows, self.win_raw, lo_tok)
 
     def _win_job(self, s0: int, s1: int, raw: torch.Tensor, tok_base: int):
@@ -41,7 +61,7 @@ class _Common:
         return (raw, None, None, None, self.W,
                 dict(T=s1, m=1, overlap=0, s_begin=s0, s_end=s1, tok_base=tok_base, gamma=self.gamma_kv,
                      eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base, pos_stride=1,
-                     out_ring=wl.W_cap))
+                     out_ring=wl.W_cap, E_scale=self.W_scale))
 
     def _win_rows(self, s0: int, s1: int, raw: torch.Tensor, tok_base: int):
         C_a, Z_a, C_b, Z_b, E, kw = self._win_job(s0, s1, raw, tok_base)
@@ -71,12 +91,12 @@ class CSADecode(_Common):
         B, N, d, m, i = wl.B, wl.N_cap, wl.d, wl.m, wl.q_pos0
         assert wl.Tq == 1 and i >= m * N, "decode: every cached entry is complete"
         self.i = i
-        self.gamma_kv = torch.ones(d, dtype=torch.float32, device=self.dev)
+        self.gamma_kv = self._kv_gamma(g, wl)
         self.gamma_q = torch.ones(d, dtype=torch.float32, device=self.dev)
         # caches
         kv_raw = g.normal(W_.T_KVRAW, (B, N, d), wl.dtype)
-        self.E = torch.empty((B, N, d), dtype=_TD[wl.dtype], device=self.dev)
-        self._fill_entries(self.E, kv_raw, m, True, True)
+        self.E, self.E_scale = _kv_rows(wl, N, self.dev)
+        self._fill_entries(self.E, kv_raw, m, True, True, E_scale=self.E_scale)
         self.kv_raw = kv_raw if keep_raw else None
         self.KI_raw = None
         if wl.k_dtype == "e4m3":
@@ -124,7 +144,8 @@ class CSADecode(_Common):
             self._win_job(i, i + 1, self.win_new, i),
             (self.Ca, self.Za, self.Cb, self.Zb, self.E,
              dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
-                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)),
+                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base,
+                  E_scale=self.E_scale)),
             (self.ICa, self.IZa, self.ICb, self.IZb, self.KI,
              dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
                   E_scale=self.KI_scale)),
@@ -140,7 +161,8 @@ class CSADecode(_Common):
         wl = self.wl
         csa_sparse_mqa(self.q, self.E, self.idx, self.W, self.q_pos, self.out, n_win=wl.n_win,
                        sink=self.sink, gamma_q=self.gamma_q, eps=wl.eps, rope_dim=wl.rope_dim,
-                       rope_base=wl.rope_base, scale=wl.scale, workspace=self.ws_mqa)
+                       rope_base=wl.rope_base, scale=wl.scale, workspace=self.ws_mqa,
+                       E_scale=self.E_scale, W_scale=self.W_scale)
 
     def step(self, index_events=None):
         self.compress_new()
@@ -188,11 +210,11 @@ class HCADecode(_Common):
         g = Gen(wl.wid, self.dev)
         B, N, d, m, i = wl.B, wl.N_cap, wl.d, wl.m, wl.q_pos0
         self.i = i
-        self.gamma_kv = torch.ones(d, dtype=torch.float32, device=self.dev)
+        self.gamma_kv = self._kv_gamma(g, wl)
         self.gamma_q = torch.ones(d, dtype=torch.float32, device=self.dev)
         kv_raw = g.normal(W_.T_KVRAW, (B, N, d), wl.dtype)
-        self.E = torch.empty((B, N, d), dtype=_TD[wl.dtype], device=self.dev)
-        self._fill_entries(self.E, kv_raw, m, True, True)
+        self.E, self.E_scale = _kv_rows(wl, N, self.dev)
+        self._fill_entries(self.E, kv_raw, m, True, True, E_scale=self.E_scale)
         self.kv_raw = kv_raw if keep_raw else None
         self._window_setup(g, wl, i - wl.n_win + 1, wl.n_win, W_.T_WINRAW)
         self.win_new = self.win_raw[:, -1:].contiguous()
@@ -212,14 +234,16 @@ class HCADecode(_Common):
             self._win_job(i, i + 1, self.win_new, i),
             (self.C, self.Z, None, None, self.E,
              dict(T=wl.m * N, m=wl.m, overlap=0, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
-                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base)),
+                  gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base,
+                  E_scale=self.E_scale)),
         ])
 
     def attend(self):
         wl = self.wl
         hca_dense_mqa(self.q, self.E, self.W, self.q_pos, self.out, m=wl.m, n_win=wl.n_win,
                       sink=self.sink, gamma_q=self.gamma_q, eps=wl.eps, rope_dim=wl.rope_dim,
-                      rope_base=wl.rope_base, scale=wl.scale, workspace=self.ws_mqa)
+                      rope_base=wl.rope_base, scale=wl.scale, workspace=self.ws_mqa,
+                      E_scale=self.E_scale, W_scale=self.W_scale)
 
     def step(self):
         self.compress_new()
@@ -238,7 +262,7 @@ class CSAPrefill(_Common):
         self.wl, self.dev = wl, torch.device(device)
         g = Gen(wl.wid, self.dev)
         B, N, d, m, Tq, p0 = wl.B, wl.N_cap, wl.d, wl.m, wl.Tq, wl.q_pos0
-        self.gamma_kv = torch.ones(d, dtype=torch.float32, device=self.dev)
+        self.gamma_kv = self._kv_gamma(g, wl)
         self.gamma_q = torch.ones(d, dtype=torch.float32, device=self.dev)
         # entries completed before the chunk come from the cache; those inside it are compressed
         self.s_new0, self.s_new1 = p0 // m, (p0 + Tq) // m

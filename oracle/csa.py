@@ -203,6 +203,22 @@ def index_score(qI, w, K, q_pos, *, m: int, N_cap: int | None = None) -> np.ndar
     return out
 
 
+def quantize_rows_mixed(E, rope_dim: int):
+    """Store KV rows in the mixed format [V4-abs §3.3: the KV entries keep their
+    RoPE dims in BF16 and the rest in FP8]: the first c - rope_dim channels as
+    e4m3fn codes with one per-row scale over them (absmax / 448, decided in fp32
+    like ``quantize_rows_e4m3``), the last rope_dim channels rounded to bf16.
+    Returns (stored values fp64 [..., c], codes uint8 [..., c - rope_dim], scale
+    float32 [...])."""
+    from .codecs import e4m3_to_f64, f64_to_bf16_value
+    E = np.asarray(E, dtype=np.float64)
+    nope = E.shape[-1] - rope_dim
+    codes, sc = quantize_rows_e4m3(E[..., :nope])
+    vals = np.concatenate([e4m3_to_f64(codes) * sc.astype(np.float64)[..., None],
+                           f64_to_bf16_value(E[..., nope:])], axis=-1)
+    return vals, codes, sc
+
+
 def quantize_rows_mxfp4(E) -> tuple[np.ndarray, np.ndarray]:
     """Store rows in MXFP4 (OCP MX: E2M1 elements, one E8M0 scale per 32
     channels).  The decisions are taken on the fp32 value, the precision the

@@ -8,7 +8,9 @@ indexer scores every visible entry, the top-k is taken, and the query attends
 over the selected entries, the window rows and the sink.
 
 Stored rows are rounded to their storage format (bf16 entries and window rows,
-e4m3 indexer keys with a per-row scale) because the caches hold those bytes.
+or mixed rows -- e4m3 codes under a row scale for the non-rotated dims, bf16 for
+the rotated ones; e4m3 indexer keys with a per-row scale) because the caches
+hold those bytes.
 Inputs are fp64 arrays of the exact stored input values; the raw rows of the
 entry cache are fetched on demand through a callable, so only the rows a
 query touches are ever decoded.
@@ -29,21 +31,26 @@ from . import csa as O
 from .codecs import e4m3_to_f64, f64_to_bf16_value, mx_fp4_to_f64
 
 
-def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+def _store(x: np.ndarray, dtype: str, rope_dim: int = 0) -> np.ndarray:
+    """The value a cache row holds in storage format ``dtype`` ("mixed": the
+    KV-entry format of the method page, section 3.3 -- see quantize_rows_mixed)."""
+    if dtype == "mixed":
+        return O.quantize_rows_mixed(x, rope_dim)[0]
     return f64_to_bf16_value(x) if dtype == "bf16" else np.asarray(x, dtype=np.float64)
 
 
 def entry_rows(raw_rows: np.ndarray, s: np.ndarray, *, m: int, rope_dim: int, rope_base: float,
-               eps: float, dtype: str) -> np.ndarray:
-    """Cache rows built from pre-norm rows: RMSNorm, RoPE at position m*s, storage rounding."""
-    E = O.rope(O.rmsnorm(raw_rows, None, eps), m * np.asarray(s), rope_dim, rope_base)
-    return _store(E, dtype)
+               eps: float, dtype: str, gamma=None) -> np.ndarray:
+    """Cache rows built from pre-norm rows: RMSNorm (weight gamma, None = 1), RoPE at
+    position m*s, storage rounding."""
+    E = O.rope(O.rmsnorm(raw_rows, gamma, eps), m * np.asarray(s), rope_dim, rope_base)
+    return _store(E, dtype, rope_dim)
 
 
 def window_rows(raw_rows: np.ndarray, toks: np.ndarray, *, rope_dim: int, rope_base: float,
-                eps: float, dtype: str) -> np.ndarray:
-    W = O.rope(O.rmsnorm(raw_rows, None, eps), np.asarray(toks), rope_dim, rope_base)
-    return _store(W, dtype)
+                eps: float, dtype: str, gamma=None) -> np.ndarray:
+    W = O.rope(O.rmsnorm(raw_rows, gamma, eps), np.asarray(toks), rope_dim, rope_base)
+    return _store(W, dtype, rope_dim)
 
 
 def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray],
@@ -56,12 +63,14 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     made from its own fp32 scores may differ at near-ties of the k-th score,
     and its attention output is still defined exactly.
 
-    p holds: i, m, N, k, n_win, d_I, rope_dim, rope_base, eps, scale, dtype, k_dtype;
+    p holds: i, m, N, k, n_win, d_I, rope_dim, rope_base, eps, scale, dtype (storage of the
+    entries and window rows: "bf16", "f32" or "mixed"), k_dtype;
     KI (N x d_I fp64, fp8 keys already times their scale; for MXFP4 keys
     instead KI_codes (N x d_I E2M1 codes) and KI_scales (N x d_I / 32 E8M0
     codes), scored on the FP4 query-key path), win_raw (n_win x d,
     tokens i-n_win+1..i), Ca/Za/Cb/Zb (2m x d, tokens m(N-2)..mN-1),
-    ICa/IZa/ICb/IZb (2m x d_I), qI (H x d_I), w (H), q (n_h x d), sink (n_h).
+    ICa/IZa/ICb/IZb (2m x d_I), qI (H x d_I), w (H), q (n_h x d), sink (n_h); optionally
+    gamma (d, the RMSNorm weight of the KV rows; default 1).
     kv_raw_rows(s) returns the pre-norm rows of entries s.
     """
     i, m, N, k, n_win = p["i"], p["m"], p["N"], p["k"], p["n_win"]
@@ -69,9 +78,10 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     T = m * N
     tok_base = m * (N - 2)
     # newest complete block: KV entry (norm + RoPE) and indexer key (no norm, stored format)
+    gam = p.get("gamma")
     e_new = O.compress(p["Ca"], p["Za"], p["Cb"], p["Zb"], m=m, overlap=1, T=T, tok_base=tok_base,
-                       s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]
-    e_new = _store(e_new, p["dtype"])
+                       s_begin=N - 1, s_end=N, gamma=gam, eps=eps, rope_dim=r, rope_base=base)[0]
+    e_new = _store(e_new, p["dtype"], r)
     k_new = O.compress(p["ICa"], p["IZa"], p["ICb"], p["IZb"], m=m, overlap=1, T=T, tok_base=tok_base,
                        s_begin=N - 1, s_end=N, normalize=False)
     if p["k_dtype"] == "mxfp4":
@@ -98,10 +108,10 @@ def csa_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     old = sel[sel != N - 1]
     if len(old):
         rows[sel != N - 1] = entry_rows(kv_raw_rows(old), old, m=m, rope_dim=r, rope_base=base,
-                                        eps=eps, dtype=p["dtype"])
+                                        eps=eps, dtype=p["dtype"], gamma=gam)
     rows[sel == N - 1] = e_new
     toks = np.arange(i - n_win + 1, i + 1)
-    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
+    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"], gamma=gam)
     out = O.attend_one(p["q"], np.concatenate([rows, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
                        rope_base=base, scale=p["scale"])
     return {"I": I[0], "idx": idx[0], "vals": vals[0], "out": out, "k_new": k_new[0]}
@@ -111,19 +121,20 @@ def hca_decode_sequence(p: dict, kv_raw_rows: Callable[[np.ndarray], np.ndarray]
     """One HCA decode step of one sequence: recompress the just-completed block,
     then dense attention over every visible entry, the window and the sink.
     p holds: i, m, N, n_win, rope_dim, rope_base, eps, scale, dtype, C, Z (m x d),
-    win_raw, q, sink."""
+    win_raw, q, sink; optionally gamma (d, the RMSNorm weight of the KV rows; default 1)."""
     i, m, N, n_win = p["i"], p["m"], p["N"], p["n_win"]
     r, base, eps = p["rope_dim"], p["rope_base"], p["eps"]
     n_vis = O.n_visible(i, m, N)
     s = np.arange(n_vis)
+    gam = p.get("gamma")
     E = np.zeros((n_vis, p["q"].shape[-1]))
     E[: N - 1] = entry_rows(kv_raw_rows(s[: N - 1]), s[: N - 1], m=m, rope_dim=r, rope_base=base,
-                            eps=eps, dtype=p["dtype"])
+                            eps=eps, dtype=p["dtype"], gamma=gam)
     e_new = O.compress(p["C"], p["Z"], None, None, m=m, overlap=0, T=m * N, tok_base=m * (N - 1),
-                       s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]
-    E[N - 1] = _store(e_new, p["dtype"])
+                       s_begin=N - 1, s_end=N, gamma=gam, eps=eps, rope_dim=r, rope_base=base)[0]
+    E[N - 1] = _store(e_new, p["dtype"], r)
     toks = np.arange(i - n_win + 1, i + 1)
-    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"])
+    W = window_rows(p["win_raw"], toks, rope_dim=r, rope_base=base, eps=eps, dtype=p["dtype"], gamma=gam)
     out = O.attend_one(p["q"], np.concatenate([E, W]), i=i, eps=eps, sink=p["sink"], rope_dim=r,
                        rope_base=base, scale=p["scale"])
     return {"out": out}
@@ -154,7 +165,7 @@ def csa_prefill_queries(p: dict, ts, kv_raw_rows: Callable[[np.ndarray], np.ndar
     s0, s1 = p0 // m, min(N, T // m)
     E_new = _store(O.compress(p["Ca"], p["Za"], p["Cb"], p["Zb"], m=m, overlap=1, T=T,
                               tok_base=p["tok_base"], s_begin=s0, s_end=s1, eps=eps,
-                              rope_dim=r, rope_base=base), p["dtype"])
+                              rope_dim=r, rope_base=base), p["dtype"], r)
     K_new = _store(O.compress(p["ICa"], p["IZa"], p["ICb"], p["IZb"], m=m, overlap=1, T=T,
                               tok_base=p["tok_base"], s_begin=s0, s_end=s1, normalize=False),
                    p["k_dtype"])

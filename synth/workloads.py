@@ -18,6 +18,7 @@ T_QI, T_WI, T_KI = 9, 10, 11                 # indexer query, head weights, key 
 T_Q, T_SINK = 12, 13                         # attention query, sink logits
 T_KVRAW, T_WINRAW = 14, 15                   # pre-norm entry rows / per-token window rows
 T_SCORES = 16                                # score rows for stand-alone top-k cases
+T_GAMMA = 17                                 # RMSNorm weight of the KV rows (when not 1)
 
 
 @dataclass(frozen=True)
@@ -44,7 +45,16 @@ class Workload:
     sink: str = "normal"  # "normal" (N(0,1) per head) | "zero"
     rope_base: float = 10000.0
     eps: float = 1e-6
+    kv_store: str = ""   # storage of the entries and window rows if not dtype: "mixed"
+    kv_gamma: str = "ones"   # RMSNorm weight of the KV rows: "ones" | "normal" (1 + N(0, 1/16))
     notes: str = field(default="", compare=False)
+
+    @property
+    def kv_dtype(self) -> str:
+        """Storage of the compressed entries and window rows: dtype, or "mixed"
+        (e4m3 codes with a row scale for the first d - rope_dim dims, bf16 for
+        the rotated ones)."""
+        return self.kv_store or self.dtype
 
     @property
     def overlap(self) -> int:
@@ -96,5 +106,14 @@ CSA_DECODE_1M = Workload(
 CSA_DECODE_1M_MX4 = CSA_DECODE_1M.scaled(name="csa_decode_pro_b16_ctx1M_mxfp4keys", k_dtype="mxfp4",
                                          notes="fp32 N(0,1) keys stored as OCP MXFP4")
 
+# Mixed KV rows take a non-unit RMSNorm weight, as a trained model has: with a
+# unit weight and bf16 rows, 448 x / amax is often exactly an e4m3 rounding
+# midpoint, where the order of fp32 operations alone decides the code.
+HCA_DECODE_MIXED = HCA_DECODE.scaled(name="hca_decode_b4_ctx1M_mixedkv", kv_store="mixed", kv_gamma="normal",
+                                     notes="entries and window rows stored as mixed rows")
+CSA_DECODE_1M_MIXED = CSA_DECODE_1M.scaled(name="csa_decode_pro_b16_ctx1M_fp8keys_mixedkv", kv_store="mixed",
+                                           kv_gamma="normal",
+                                           notes="entries and window rows stored as mixed rows")
+
 WORKLOADS = {w.name: w for w in (TINY, CSA_DECODE_FLASH, HCA_DECODE, CSA_PREFILL_PRO, CSA_DECODE_1M,
-                                 CSA_DECODE_1M_MX4)}
+                                 CSA_DECODE_1M_MX4, HCA_DECODE_MIXED, CSA_DECODE_1M_MIXED)}

@@ -32,12 +32,12 @@ def csa_decode_params(run, b: int):
             KI = KI * to_f64(run.KI_scale[b])[:, None]
         keys["KI"] = KI
     p = dict(i=run.i, m=wl.m, N=wl.N_cap, k=wl.k, n_win=wl.n_win, d_I=wl.d_I, rope_dim=wl.rope_dim,
-             rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.dtype, k_dtype=wl.k_dtype,
+             rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.kv_dtype, k_dtype=wl.k_dtype,
              **keys, win_raw=to_f64(run.win_raw[b]),
              Ca=to_f64(run.Ca[b]), Za=to_f64(run.Za[b]), Cb=to_f64(run.Cb[b]), Zb=to_f64(run.Zb[b]),
              ICa=to_f64(run.ICa[b]), IZa=to_f64(run.IZa[b]), ICb=to_f64(run.ICb[b]),
              IZb=to_f64(run.IZb[b]), qI=to_f64(run.qI[b, 0]), w=to_f64(run.wI[b, 0]),
-             q=to_f64(run.q[b, 0]), sink=to_f64(run.sink))
+             q=to_f64(run.q[b, 0]), sink=to_f64(run.sink), gamma=to_f64(run.gamma_kv))
     return p, _raw_rows(run.kv_raw[b])
 
 
@@ -45,9 +45,9 @@ def hca_decode_params(run, b: int):
     """(p, kv_raw_rows) of sequence b of an HCADecode run, for oracle.steps.hca_decode_sequence."""
     wl = run.wl
     p = dict(i=run.i, m=wl.m, N=wl.N_cap, n_win=wl.n_win, rope_dim=wl.rope_dim,
-             rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.dtype,
+             rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale, dtype=wl.kv_dtype,
              C=to_f64(run.C[b]), Z=to_f64(run.Z[b]), win_raw=to_f64(run.win_raw[b]),
-             q=to_f64(run.q[b, 0]), sink=to_f64(run.sink))
+             q=to_f64(run.q[b, 0]), sink=to_f64(run.sink), gamma=to_f64(run.gamma_kv))
     return p, _raw_rows(run.kv_raw[b])
 
 
@@ -58,7 +58,7 @@ def csa_prefill_params(run, ts):
     ts_t = torch.as_tensor(np.asarray(ts), device=run.q.device)
     p = dict(p0=wl.q_pos0, Tq=wl.Tq, m=wl.m, N=wl.N_cap, k=wl.k, n_win=wl.n_win,
              rope_dim=wl.rope_dim, rope_base=wl.rope_base, eps=wl.eps, scale=wl.scale,
-             dtype=wl.dtype, k_dtype=wl.k_dtype, KI=to_f64(run.KI_init[0]), tok_base=run.tok_base,
+             dtype=wl.kv_dtype, k_dtype=wl.k_dtype, KI=to_f64(run.KI_init[0]), tok_base=run.tok_base,
              Ca=to_f64(run.Ca[0]), Za=to_f64(run.Za[0]), Cb=to_f64(run.Cb[0]), Zb=to_f64(run.Zb[0]),
              ICa=to_f64(run.ICa[0]), IZa=to_f64(run.IZa[0]), ICb=to_f64(run.ICb[0]),
              IZb=to_f64(run.IZb[0]), win_before=to_f64(run.win_raw[0]),

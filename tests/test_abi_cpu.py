@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
     for s in range(7):
         assert lib.csa_status_str(s)
     assert lib.csa_status_str(99) == b"unknown status"
@@ -144,8 +144,8 @@ def test_topk_validation_and_workspace(lib):
 
 def test_mqa_validation(lib):
     def sparse(**kw):
-        a = dict(q=FAKE, g=None, eps=1e-6, E=FAKE, N=100, idx=FAKE, k=16, W=FAKE, Wc=16, nw=16,
-                 sink=None, pos=FAKE, B=1, Tq=1, nh=16, d=128, r=64, base=1e4, scale=0.1, dt=1,
+        a = dict(q=FAKE, g=None, eps=1e-6, E=FAKE, Es=None, N=100, idx=FAKE, k=16, W=FAKE, Ws=None, Wc=16,
+                 nw=16, sink=None, pos=FAKE, B=1, Tq=1, nh=16, d=128, r=64, base=1e4, scale=0.1, dt=1,
                  out=FAKE, ws=None, wsb=0, st=None)
         a.update(kw)
         return lib.csa_sparse_mqa(*a.values())
@@ -173,10 +173,16 @@ def test_mqa_validation(lib):
     assert lib.csa_mqa_workspace_size(1, 16, 32, 128, 2300 + 64) == 16 * 2 * 32 * (128 * 2 + 16)
     # the generic path caps the key count
     assert sparse(dt=0, k=9000) == CSA_E_UNSUPPORTED
+    # mixed rows: row scales required; d = 512 and rope_dim = 64 only
+    assert sparse(dt=4) == CSA_E_NULL
+    assert sparse(dt=4, Es=FAKE) == CSA_E_NULL                # window rows need W_scale
+    assert sparse(dt=4, Es=FAKE, Ws=FAKE) == CSA_E_UNSUPPORTED   # d = 128
+    assert sparse(dt=4, Es=FAKE, Ws=FAKE, d=512, r=32) == CSA_E_UNSUPPORTED
+    assert sparse(dt=5) == CSA_E_DTYPE
 
     def dense(**kw):
-        a = dict(q=FAKE, g=None, eps=1e-6, E=FAKE, N=100, m=0, W=FAKE, Wc=16, nw=16, sink=None,
-                 pos=FAKE, B=1, Tq=1, nh=16, d=128, r=64, base=1e4, scale=0.1, dt=1, out=FAKE,
+        a = dict(q=FAKE, g=None, eps=1e-6, E=FAKE, Es=None, N=100, m=0, W=FAKE, Ws=None, Wc=16, nw=16,
+                 sink=None, pos=FAKE, B=1, Tq=1, nh=16, d=128, r=64, base=1e4, scale=0.1, dt=1, out=FAKE,
                  ws=None, wsb=0, st=None)
         a.update(kw)
         return lib.hca_dense_mqa(*a.values())
@@ -272,6 +278,6 @@ def test_no_kernel_spills_to_scratch():
     the loop."""
     sizes = _kernel_scratch_sizes()
     assert len(sizes) >= 100, sizes
-    allowed = re.compile(r"mqa_decode_kernelILi512ELb[01]ELi\d+ELi\d+ELi2EE")
+    allowed = re.compile(r"mqa_decode_kernelILi512ELb[01]ELi\d+ELi\d+ELi2ELb[01]EE")
     spilled = [(n, s) for n, s in sizes if s > 0 and not (allowed.search(n) and s <= 64)]
     assert not spilled, spilled

@@ -588,3 +588,155 @@ def test_grouped_out_proj_parity(csa, case):
     csa.csa_grouped_out_proj(o, W1, W2, y, out2, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# mixed KV rows (e4m3 codes with a row scale for the first c - r dims, bf16 for
+# the r rotated dims; method page section 3.3, storage of the KV entries)
+# ---------------------------------------------------------------------------
+def _mixed_split(E, c, r):
+    """(e4m3 codes [.., c - r] uint8, rotated dims [.., r] fp64) of mixed rows."""
+    codes = E[..., : c - r].cpu().numpy()
+    rot = E[..., c - r:].contiguous().view(torch.bfloat16)
+    return codes, to_f64(rot)
+
+
+@pytest.mark.parametrize("B,T,R,tok_base,c,m,ov,s0,s1,ring", [
+    (3, 203, 203, 0, 512, 4, 1, 0, 51, 0),          # CSA entries, ragged tail
+    (2, 2050, 2050, 0, 512, 4, 1, 0, 513, 0),       # many entries: the wide kernel
+    (2, 300, 300, 0, 512, 128, 0, 0, 3, 0),         # HCA entries, partial block
+    (2, 700, 700, 0, 512, 1, 0, 300, 700, 512),     # window rows into a ring
+])
+def test_compress_mixed_output(csa, B, T, R, tok_base, c, m, ov, s0, s1, ring):
+    """Mixed rows: the rotated dims are the oracle's values rounded to bf16, the
+    row scale is fp32(absmax) / 448 of the other dims, and every code is a
+    correct e4m3 rounding of the oracle's value in units of that scale (up to
+    rounding ties of the fp32-vs-fp64 value)."""
+    r = 64
+    g = Gen(170 + s1, DEV)
+    Ca, Za = g.normal(1, (B, R, c), "bf16"), g.normal(2, (B, R, c), "bf16")
+    Cb, Zb = (g.normal(3, (B, R, c), "bf16"), g.normal(4, (B, R, c), "bf16")) if ov else (None, None)
+    gamma = _gamma(g, 5, c)
+    rows = ring if ring else s1
+    kw = dict(T=T, m=m, overlap=ov, s_begin=s0, s_end=s1, tok_base=tok_base, gamma=gamma, rope_dim=r,
+              out_ring=ring)
+    if m == 1:
+        kw["pos_stride"] = 1
+    Eb = torch.full((B, rows, c), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Em = torch.zeros((B, rows, c + r), dtype=torch.uint8, device=DEV)
+    S = torch.zeros((B, rows), dtype=torch.float32, device=DEV)
+    csa.csa_compress(Ca, Za, Cb, Zb, Eb, **kw)
+    csa.csa_compress(Ca, Za, Cb, Zb, Em, E_scale=S, **kw)
+    torch.cuda.synchronize()
+    ents = np.arange(max(s0, s1 - ring), s1) if ring else np.arange(s0, s1)   # rows that survive
+    slots = ents % ring if ring else ents
+    codes, rot = _mixed_split(Em, c, r)
+    nope = c - r
+    mism = 0
+    for b in range(B):
+        ref = O.compress(*(None if x is None else to_f64(x[b]) for x in (Ca, Za, Cb, Zb)), m=m, overlap=ov, T=T,
+                         tok_base=tok_base, s_begin=s0, s_end=s1, gamma=to_f64(gamma), rope_dim=r,
+                         pos_stride=kw.get("pos_stride", m))[ents - s0]
+        # the rotated dims: within bf16 of the oracle (and of the bf16 output, which another
+        # kernel may compute: its fp32 sums can differ in the last bits)
+        assert row_rel_err(rot[b, slots], ref[:, nope:]) <= TOL_BF16
+        assert row_rel_err(rot[b, slots], to_f64(Eb[b, slots][:, nope:])) <= 2 ** -7
+        vals, rc, rs = O.quantize_rows_mixed(ref, r)
+        sc = to_f64(S[b, slots])
+        assert np.allclose(sc, rs, rtol=2e-6, atol=0), b
+        y = ref[:, :nope] / sc[:, None]
+        dec = oc.e4m3_to_f64(codes[b, slots])
+        assert np.all(np.abs(dec - y) <= 0.5 * e4m3_ulp(y) * (1 + 1e-3) + 1e-6 * 448), b
+        mism += int(np.sum(codes[b, slots] != rc))
+    assert mism <= 0.001 * B * len(slots) * nope
+
+
+def _mixed_rows_from_oracle(x64, r):
+    """Mixed rows quantised by the oracle: (device bytes [.., c + r], device scales, fp64 values)."""
+    vals, codes, sc = O.quantize_rows_mixed(x64, r)
+    rot = torch.from_numpy(np.ascontiguousarray(vals[..., -r:])).to(torch.bfloat16).view(torch.uint8)
+    raw = torch.cat([torch.from_numpy(codes), rot], dim=-1).contiguous()
+    return raw.to(DEV), torch.from_numpy(sc).to(DEV), vals
+
+
+MIXED_MQA_CASES = [
+    # name, dense, B, Tq, n_h, N, k, m, n_win, W_cap, positions
+    ("mixed_sparse_decode_split", False, 3, 1, 64, 900, 512, 4, 128, 128, "all"),
+    ("mixed_sparse_decode_h128_k1024", False, 2, 1, 128, 3000, 1024, 4, 128, 128, "all"),
+    ("mixed_dense_decode_split", True, 2, 1, 64, 1500, 0, 128, 128, 128, "all"),
+    ("mixed_sparse_prefill", False, 1, 24, 32, 500, 64, 4, 128, 4096, "prefill"),
+    ("mixed_dense_prefill_h16_masked", True, 2, 5, 16, 300, 0, 4, 0, 0, "partial"),
+]
+
+
+@pytest.mark.parametrize("case", MIXED_MQA_CASES, ids=[c[0] for c in MIXED_MQA_CASES])
+def test_mqa_mixed_rows_parity(csa, case):
+    """Attention over mixed entries and window rows (d = 512, rope 64) against the
+    oracle on the stored values (codes times row scale, bf16 rotated dims)."""
+    name, dense, B, Tq, n_h, N, k, m, n_win, W_cap, pmode = case
+    d, r = 512, 64
+    g = Gen(490 + MIXED_MQA_CASES.index(case), DEV)
+    q = g.normal(1, (B, Tq, n_h, d), "bf16")
+    # rows of magnitudes 2^-4 .. 2, so the row scales differ (the logits' spread
+    # stays that of N(0, 1) rows or below: a spread of tens would make the softmax
+    # hinge on the bf16 rounding of the query)
+    mag = torch.exp2(torch.randint(-4, 2, (B, N, 1), device=DEV).float())
+    Em, Es, Ev = _mixed_rows_from_oracle(to_f64(g.normal(2, (B, N, d), "f32") * mag), r)
+    Wm = Ws = Wv = None
+    if n_win:
+        Wm, Ws, Wv = _mixed_rows_from_oracle(to_f64(g.normal(3, (B, W_cap, d), "f32")), r)
+    sink = g.normal(4, (n_h,), "f32", per_slot=False)
+    gamma = _gamma(g, 5, d)
+    pos = _positions(pmode, B, Tq, N, m, g)
+    scale = 1.0 / math.sqrt(d)
+    slots = (N if dense else k) + n_win
+    ws = torch.empty(max(csa.csa_mqa_workspace_size(B, Tq, n_h, d, slots), 1), dtype=torch.uint8, device=DEV)
+    idx = None
+    if not dense:
+        u = g.uniform(6, (B, Tq, k))
+        idx = ((u * (N + 8)).to(torch.int32) - 4)
+        idx[..., ::5] = -1
+        idx = idx.contiguous()
+
+    def run(E, W, Esc, Wsc):
+        out = torch.full_like(q, float("nan"))
+        kw = dict(n_win=n_win, sink=sink, gamma_q=gamma, rope_dim=r, scale=scale, workspace=ws, E_scale=Esc,
+                  W_scale=Wsc)
+        if dense:
+            csa.hca_dense_mqa(q, E, W, pos, out, m=m, **kw)
+        else:
+            csa.csa_sparse_mqa(q, E, idx, W, pos, out, **kw)
+        torch.cuda.synchronize()
+        return out
+
+    out = run(Em, Wm, Es, Ws)
+
+    got = to_f64(out)
+    sk, gm = to_f64(sink), to_f64(gamma)
+    for b in range(B):
+        kw = dict(q_pos=to_f64(pos[b]), n_win=n_win, W_cap=W_cap if n_win else None, gamma_q=gm, eps=1e-6,
+                  sink=sk, rope_dim=r, scale=scale)
+        Wb = Wv[b] if n_win else None
+        if dense:
+            ref = O.dense_mqa(to_f64(q[b]), Ev[b], Wb, m=m, **kw)
+        else:
+            ref = O.sparse_mqa(to_f64(q[b]), Ev[b], to_f64(idx[b]), Wb, **kw)
+        err = row_rel_err(got[b], ref)
+        assert err <= TOL_BF16, (name, b, err)
+
+
+def test_mqa_mixed_rows_rejects_unsupported(csa):
+    """Mixed rows need d = 512 and rope_dim = 64: other shapes raise."""
+    g = Gen(499, DEV)
+    q = g.normal(1, (1, 1, 16, 128), "bf16")
+    E = torch.zeros((1, 10, 128 + 32), dtype=torch.uint8, device=DEV)
+    S = torch.ones((1, 10), dtype=torch.float32, device=DEV)
+    idx = torch.zeros((1, 1, 4), dtype=torch.int32, device=DEV)
+    pos = torch.full((1, 1), 40, dtype=torch.int32, device=DEV)
+    out = torch.zeros_like(q)
+    with pytest.raises(csa.CsaError):
+        csa.csa_sparse_mqa(q, E, idx, None, pos, out, n_win=0, rope_dim=32, E_scale=S)
+    q5 = g.normal(2, (1, 1, 16, 512), "bf16")
+    E5 = torch.zeros((1, 10, 512 + 32), dtype=torch.uint8, device=DEV)
+    with pytest.raises(csa.CsaError):
+        csa.csa_sparse_mqa(q5, E5, idx, None, pos, torch.zeros_like(q5), n_win=0, rope_dim=32, E_scale=S)

@@ -582,12 +582,14 @@ def test_chunked_prefill_equals_whole_sequence():
 # ---------------------------------------------------------------------------
 # decode compositions (oracle.steps) against the plain whole-sequence chain
 # ---------------------------------------------------------------------------
-def _store_like(x, dtype):
+def _store_like(x, dtype, rope_dim=0):
     from oracle.codecs import f64_to_bf16_value
+    if dtype == "mixed":
+        return O.quantize_rows_mixed(x, rope_dim)[0]
     return f64_to_bf16_value(x) if dtype == "bf16" else np.asarray(x, dtype=np.float64)
 
 
-def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
+def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3", with_gamma=False):
     """One CSA decode step (query at i = m N, cached tokens 0 .. i-1) against the
     plain chain over the whole sequence: compress every entry from all tokens,
     store, score, select, attend.  The step's cache rows for entries < N-1 are
@@ -609,10 +611,11 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
     w = rng.uniform(size=H)
     q = rng.standard_normal((n_h, c))
     sink = rng.standard_normal(n_h)
+    gamma = 1.0 + 0.25 * rng.standard_normal(c) if with_gamma else None
     eps, scale, base = 1e-6, 1 / np.sqrt(c), 10000.0
     # plain chain
-    E = _store_like(O.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, eps=eps,
-                               rope_dim=r, rope_base=base), dtype)
+    E = _store_like(O.compress(C["Ca"], C["Za"], C["Cb"], C["Zb"], m=m, overlap=1, T=T, gamma=gamma, eps=eps,
+                               rope_dim=r, rope_base=base), dtype, r)
     K = O.compress(IC["ICa"], IC["IZa"], IC["ICb"], IC["IZb"], m=m, overlap=1, T=T, normalize=False)
     if k_dtype == "mxfp4":
         Kc, Ks = O.quantize_rows_mxfp4(K)
@@ -621,8 +624,8 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
         K = e4m3_to_f64(codes) * sc.astype(np.float64)[:, None]
     else:
         K = _store_like(K, k_dtype)
-    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, eps=eps, rope_dim=r,
-                               rope_base=base, pos_stride=1), dtype)
+    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, gamma=gamma, eps=eps,
+                               rope_dim=r, rope_base=base, pos_stride=1), dtype, r)
     if k_dtype == "mxfp4":
         I = O.index_score_mxfp4(qI[None], w[None], Kc, Ks, [i], m=m)
     else:
@@ -647,6 +650,8 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
              dtype=dtype, k_dtype=k_dtype, **keys, win_raw=win_raw[i - n_win + 1:],
              **{n: v[tb:] for n, v in C.items()}, **{n: v[tb:] for n, v in IC.items()},
              qI=qI, w=w, q=q, sink=sink)
+    if with_gamma:
+        p["gamma"] = gamma
     got = steps_mod.csa_decode_sequence(p, lambda s: pre[np.asarray(s)])
     np.testing.assert_allclose(got["I"], I[0], rtol=1e-12, atol=1e-12)
     assert np.array_equal(got["idx"], idx[0])
@@ -655,7 +660,7 @@ def _csa_decode_pin(steps_mod, dtype="bf16", k_dtype="e4m3"):
     np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
 
 
-def _hca_decode_pin(steps_mod, dtype="bf16"):
+def _hca_decode_pin(steps_mod, dtype="bf16", with_gamma=False):
     """One HCA decode step (m' = 8, query at i = m' N) against the plain chain:
     compress every block of the whole sequence without overlap, then dense
     attention over every visible entry, the window and the sink [V4-abs §3.3:
@@ -668,11 +673,12 @@ def _hca_decode_pin(steps_mod, dtype="bf16"):
     win_raw = rng.standard_normal((i + 1, c))
     q = rng.standard_normal((n_h, c))
     sink = rng.standard_normal(n_h)
+    gamma = 1.0 + 0.25 * rng.standard_normal(c) if with_gamma else None
     eps, scale, base = 1e-6, 1 / np.sqrt(c), 10000.0
-    E = _store_like(O.compress(Cf, Zf, None, None, m=m, overlap=0, T=T, eps=eps, rope_dim=r,
-                               rope_base=base), dtype)
-    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, eps=eps, rope_dim=r,
-                               rope_base=base, pos_stride=1), dtype)
+    E = _store_like(O.compress(Cf, Zf, None, None, m=m, overlap=0, T=T, gamma=gamma, eps=eps, rope_dim=r,
+                               rope_base=base), dtype, r)
+    W = _store_like(O.compress(win_raw, None, None, None, m=1, overlap=0, T=i + 1, gamma=gamma, eps=eps,
+                               rope_dim=r, rope_base=base, pos_stride=1), dtype, r)
     out = O.dense_mqa(q[None], E, W, q_pos=[i], m=m, n_win=n_win, eps=eps, sink=sink, rope_dim=r,
                       rope_base=base, scale=scale)[0]
     pre = O.pool_entries(Cf, Zf, None, None, m=m, overlap=0, T=T)
@@ -680,21 +686,24 @@ def _hca_decode_pin(steps_mod, dtype="bf16"):
     tb = m * (N - 1)
     p = dict(i=i, m=m, N=N, n_win=n_win, rope_dim=r, rope_base=base, eps=eps, scale=scale, dtype=dtype,
              C=Cf[tb:], Z=Zf[tb:], win_raw=win_raw[i - n_win + 1:], q=q, sink=sink)
+    if with_gamma:
+        p["gamma"] = gamma
     got = steps_mod.hca_decode_sequence(p, lambda s: pre[np.asarray(s)])
     np.testing.assert_allclose(got["out"], out, rtol=1e-10, atol=1e-12)
 
 
-@pytest.mark.parametrize("dtype,k_dtype", [("bf16", "e4m3"), ("bf16", "bf16"), ("f32", "f32"),
-                                           ("bf16", "mxfp4")])
-def test_csa_decode_step_equals_whole_sequence(dtype, k_dtype):
+@pytest.mark.parametrize("dtype,k_dtype,with_gamma", [
+    ("bf16", "e4m3", False), ("bf16", "bf16", False), ("f32", "f32", False), ("bf16", "mxfp4", False),
+    ("mixed", "e4m3", True), ("bf16", "bf16", True)])
+def test_csa_decode_step_equals_whole_sequence(dtype, k_dtype, with_gamma):
     from oracle import steps
-    _csa_decode_pin(steps, dtype, k_dtype)
+    _csa_decode_pin(steps, dtype, k_dtype, with_gamma)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_hca_decode_step_equals_whole_sequence(dtype):
+@pytest.mark.parametrize("dtype,with_gamma", [("bf16", False), ("f32", False), ("mixed", True)])
+def test_hca_decode_step_equals_whole_sequence(dtype, with_gamma):
     from oracle import steps
-    _hca_decode_pin(steps, dtype)
+    _hca_decode_pin(steps, dtype, with_gamma)
 
 
 def _mutant_steps(old: str, new: str):
@@ -717,13 +726,16 @@ def _mutant_steps(old: str, new: str):
     ("KI[N - 1] = k_new[0]", "KI[N - 2] = k_new[0]"),                   # wrong key row replaced
     ("rows[sel == N - 1] = e_new", "rows[sel == N - 2] = e_new"),       # wrong entry row replaced
     ("old = sel[sel != N - 1]", "old = sel[sel != -1]"),                # stale cache row read
-    ("s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base)[0]\n    e_new = _store",
-     "s_begin=N - 1, s_end=N, eps=eps, rope_dim=r, rope_base=base, pos_offset=1)[0]\n    e_new = _store"),
+    ("s_begin=N - 1, s_end=N, gamma=gam, eps=eps, rope_dim=r, rope_base=base)[0]\n    e_new = _store",
+     "s_begin=N - 1, s_end=N, gamma=gam, eps=eps, rope_dim=r, rope_base=base, pos_offset=1)[0]\n"
+     "    e_new = _store"),
+    ("gam = p.get(\"gamma\")\n    e_new", "gam = None\n    e_new"),     # the norm weight dropped
+    ("e_new = _store(e_new, p[\"dtype\"], r)", "e_new = _store(e_new, \"f64\", r)"),   # new entry unrounded
 ])
 def test_csa_decode_pin_catches_planted_mistakes(old, new):
     bad = _mutant_steps(old, new)
     with pytest.raises((AssertionError, ValueError)):
-        _csa_decode_pin(bad)
+        _csa_decode_pin(bad, "mixed", "e4m3", True)
 
 
 @pytest.mark.parametrize("old,new", [
@@ -733,11 +745,13 @@ def test_csa_decode_pin_catches_planted_mistakes(old, new):
     ("E[: N - 1] = entry_rows(kv_raw_rows(s[: N - 1]), s[: N - 1]",
      "E[: N - 1] = entry_rows(kv_raw_rows(s[1: N]), s[: N - 1]"),         # rows shifted by one
     ("np.concatenate([E, W])", "np.concatenate([E, W[:-1]])"),        # window without the own token
+    ("eps=eps, dtype=p[\"dtype\"], gamma=gam)\n    out = O.attend_one(p[\"q\"], np.concatenate([E, W])",
+     "eps=eps, dtype=p[\"dtype\"])\n    out = O.attend_one(p[\"q\"], np.concatenate([E, W])"),   # window unweighted
 ])
 def test_hca_decode_pin_catches_planted_mistakes(old, new):
     bad = _mutant_steps(old, new)
     with pytest.raises((AssertionError, ValueError)):
-        _hca_decode_pin(bad)
+        _hca_decode_pin(bad, "mixed", True)
 
 
 # ---------------------------------------------------------------------------
@@ -977,3 +991,24 @@ def test_incremental_cache_planted_short_ring_is_caught():
             test_incremental_cache_equals_full_recompression([1] * 70)
     finally:
         Cc.ring_slots = real
+
+
+# ---------------------------------------------------------------------------
+# mixed KV rows: RoPE dims bf16, the rest e4m3 with a row scale (method page §3.3)
+# ---------------------------------------------------------------------------
+def test_mixed_rows_split_into_the_two_codecs():
+    """The mixed format is the e4m3 row quantisation of the first c - r channels
+    and bf16 rounding of the last r, each checked against torch's own casts."""
+    rng = np.random.default_rng(61)
+    E = rng.standard_normal((20, 64)) * np.exp2(rng.integers(-4, 4, size=(20, 1)))
+    r = 16
+    vals, codes, sc = O.quantize_rows_mixed(E, r)
+    x32 = torch.tensor(E[:, :48], dtype=torch.float32)
+    amax = x32.abs().amax(dim=-1)
+    want_sc = (amax / 448.0).numpy()
+    assert np.array_equal(sc, want_sc)
+    want_codes = (x32 / torch.tensor(want_sc)[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want_codes)
+    want_rope = torch.tensor(E[:, 48:]).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(vals[:, 48:], want_rope)
+    assert np.all(np.abs(vals[:, :48] - E[:, :48]) <= 2.0 ** -4 * np.abs(E[:, :48]) + sc[:, None] * 2.0 ** -9)

@@ -135,19 +135,21 @@ def test_tiny_fp32_end_to_end(lib):
 # decode workloads at full size
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("name", ["csa_decode_flash_b8_ctx65536", "csa_decode_pro_b16_ctx1M_fp8keys",
-                                  "csa_decode_pro_b16_ctx1M_mxfp4keys"])
+                                  "csa_decode_pro_b16_ctx1M_mxfp4keys",
+                                  "csa_decode_pro_b16_ctx1M_fp8keys_mixedkv"])
 def test_csa_decode_full_size(lib, name):
     """A whole decode step at full size.  Every sequence is checked, except for
     MXFP4 keys, where the oracle's own quantisation of 262,144 keys per sequence
-    bounds the CPU time: four sequences spread over the batch (and the device's
-    key cache is first checked against that quantisation, bit for bit)."""
+    bounds the CPU time, and for mixed KV rows (a second 1M-context run): there
+    four sequences spread over the batch (for MXFP4 the device's key cache is
+    first checked against the oracle's quantisation, bit for bit)."""
     from long_context_attention_02_amd.pipeline import CSADecode
     from oracle import codecs as oc
     from synth.workloads import WORKLOADS
     wl = WORKLOADS[name]
     run = CSADecode(wl, "cuda", keep_raw=True)
     torch.cuda.synchronize()
-    bs = [0, 5, 10, 15] if wl.k_dtype == "mxfp4" else list(range(wl.B))
+    bs = [0, 5, 10, 15] if (wl.k_dtype == "mxfp4" or wl.kv_dtype == "mixed") else list(range(wl.B))
     params = [csa_decode_params(run, b) for b in bs]   # stored inputs, before the step
     if wl.k_dtype == "mxfp4":
         for b, (p, _) in zip(bs, params):
@@ -170,9 +172,11 @@ def test_csa_decode_full_size(lib, name):
     _free()
 
 
-def test_hca_decode_full_size(lib):
+@pytest.mark.parametrize("name", ["hca_decode_b4_ctx1M", "hca_decode_b4_ctx1M_mixedkv"])
+def test_hca_decode_full_size(lib, name):
     from long_context_attention_02_amd.pipeline import HCADecode
-    from synth.workloads import HCA_DECODE as wl
+    from synth.workloads import WORKLOADS
+    wl = WORKLOADS[name]
     run = HCADecode(wl, "cuda", keep_raw=True)
     torch.cuda.synchronize()
     params = [hca_decode_params(run, b) for b in range(wl.B)]
@@ -282,15 +286,16 @@ def test_decode_bitwise_repeatable_and_batch_invariant(lib):
 def test_graph_replay_equals_eager_step(lib):
     """A decode step captured as a HIP graph and replayed three times, with eager
     work and synchronisations between the replays, writes the eager step's bytes
-    every time (CSA Flash-like decode and HCA decode)."""
+    every time (CSA Flash-like decode, HCA decode with bf16 and with mixed KV rows)."""
     from long_context_attention_02_amd.pipeline import CSADecode, HCADecode
-    from synth.workloads import CSA_DECODE_FLASH, HCA_DECODE
+    from synth.workloads import CSA_DECODE_FLASH, HCA_DECODE, HCA_DECODE_MIXED
 
     def as_bytes(t):
         return t.view(torch.uint8) if t.dtype == torch.bfloat16 else t
 
     for cls, wl, outs in ((CSADecode, CSA_DECODE_FLASH, ("I", "idx", "out", "E", "KI", "W")),
-                          (HCADecode, HCA_DECODE, ("out", "E", "W"))):
+                          (HCADecode, HCA_DECODE, ("out", "E", "W")),
+                          (HCADecode, HCA_DECODE_MIXED, ("out", "E", "W", "E_scale", "W_scale"))):
         run = cls(wl, "cuda", keep_raw=False)
         run.step()
         torch.cuda.synchronize()
