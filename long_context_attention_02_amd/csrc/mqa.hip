@@ -1524,13 +1524,21 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   }
 }
 
-// merge the split partial states of one (query, head) in split order, one pass
-// with a running maximum; each thread owns one pair of output dims
+// merge the split partial states of one (query, head): first the maximum M of
+// every split's m (and the sink), then split s weighed by l_s exp(m_s - M) (its
+// row holds O_s / l_s times 1 / u_s), summed in split order.  A block of CB
+// splits' partials is loaded at once (one memory round trip for up to CB
+// splits).  Lane l of each wave reads the record of split s0 + l % CB and
+// forms its weight; readlane hands the weights to every lane.  Thread u owns
+// output dims 2u, 2u + 1 (the launcher keeps D / 2 <= blockDim); every thread
+// runs the split loop, so the wave reductions see full waves.
+template <int CB>
 __global__ __launch_bounds__(256) void mqa_combine_kernel(
     const float* __restrict__ ws, const float* __restrict__ sink, const int* __restrict__ q_pos,
     int Tq, int n_h, int D, int n_split, int rope_dim, RopeRatio rope, uint16_t* __restrict__ out) {
-  constexpr int CB = 8;   // splits whose partials are loaded in one batch
+  static_assert(CB == 8 || CB == 64, "a block is a power of two of lanes");
   const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
   const size_t row = (size_t)b * Tq + t;
   const long long i = q_pos[row];
   const float sig = sink ? sink[h] : -INFINITY;
@@ -1539,71 +1547,62 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
   const float* mlb = part_ml(ws, (long long)gridDim.z * Tq * n_split, n_h, D) + 4 * (row * n_split * (size_t)n_h + h);
   const size_t mstride = 4 * (size_t)n_h;
   const int rbeg = D - rope_dim;
-  for (int u = threadIdx.x; u < D / 2; u += blockDim.x) {
-    const int d0 = 2 * u;
-    // running maximum M (from the sink on), with Z and (o0, o1) relative to it;
-    // the splits merge CB at a time, in split order
-    float M = sig, Z = (sig != -INFINITY) ? 1.f : 0.f, o0 = 0.f, o1 = 0.f;
-    for (int s0 = 0; s0 < n_split; s0 += CB) {
-      // every (max, sum) and output pair of the batch in flight at once:
-      // unconditional loads (split index clamped; the extra ones are never
-      // used), since a guarded load becomes a branch with its own wait.  Lane
-      // l of each wave fetches the (max, sum) of split s0 + l % CB with one
-      // vector load in the same batch as the outputs; readlane hands them to
-      // every lane.
-      float ms[CB], ls[CB], us[CB], a0[CB], a1[CB];
-      const f32x4_t mlv = *(const f32x4_t*)(mlb + min(s0 + (int)(threadIdx.x % CB), n_split - 1) * mstride);
+  const bool has = (int)threadIdx.x < D / 2;
+  const int d0 = has ? 2 * (int)threadIdx.x : 0;
+  // every partial of a block in flight at once: unconditional loads (split index
+  // clamped; the extra ones get weight 0), since a guarded load becomes a branch
+  // with its own wait.  The first block's loads go out with the maximum's.
+  uint32_t w[CB];
+  auto load_block = [&](int s0) {
 #pragma unroll
-      for (int s = 0; s < CB; ++s) {
-        const int sc = min(s0 + s, n_split - 1);
-        const _Float16* ps = base + sc * sstride;
-        const uint32_t w = *(const uint32_t*)(ps + d0);
-        a0[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-        a1[s] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-      }
-#pragma unroll
-      for (int s = 0; s < CB; ++s) {
-        ms[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[0]), s));
-        ls[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[1]), s));
-        us[s] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mlv[2]), s));
-      }
-      const int nb = min(CB, n_split - s0);
-      float bm = M;
-#pragma unroll
-      for (int s = 0; s < CB; ++s)
-        if (s < nb) bm = fmaxf(bm, ms[s]);
-      if (bm != M) {   // (M = -inf: Z and O are still 0)
-        const float r = (M == -INFINITY) ? 0.f : __expf(M - bm);
-        Z *= r;
-        o0 *= r;
-        o1 *= r;
-        M = bm;
-      }
-      // split s weighs l_s exp(m_s - M) (its rows hold O_s / l_s times 1 / u_s)
-#pragma unroll
-      for (int s = 0; s < CB; ++s) {
-        if (s < nb) {
-          const float f = (ms[s] == -INFINITY) ? 0.f : ls[s] * __expf(ms[s] - M);
-          Z += f;
-          o0 += a0[s] * (f * us[s]);
-          o1 += a1[s] * (f * us[s]);
-        }
-      }
-    }
-    const float inv = Z > 0.f ? 1.f / Z : 0.f;
-    o0 *= inv;
-    o1 *= inv;
-    if (d0 >= rbeg) {
-      float cs, sn;
-      rope_cos_sin(-i, (d0 - rbeg) >> 1, rope, &cs, &sn);
-      const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
-      o0 = r0;
-      o1 = r1;
-    }
-    const size_t ob = (row * n_h + h) * (size_t)D + d0;
-    out[ob] = f32_to_bf16_bits(o0);
-    out[ob + 1] = f32_to_bf16_bits(o1);
+    for (int s = 0; s < CB; ++s) w[s] = *(const uint32_t*)(base + (size_t)min(s0 + s, n_split - 1) * sstride + d0);
+  };
+  load_block(0);
+  // M over the splits and the sink
+  float M = sig;
+  for (int s0 = 0; s0 < n_split; s0 += 64) {
+    const int sl = s0 + lane;
+    const float m = mlb[(size_t)min(sl, n_split - 1) * mstride];
+    M = fmaxf(M, wave_reduce_f<true>(sl < n_split ? m : -INFINITY));
   }
+  float Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f, o0 = 0.f, o1 = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += CB) {
+    if (s0 > 0) load_block(s0);
+    const int sl = s0 + (lane & (CB - 1));
+    const f32x4_t rec = *(const f32x4_t*)(mlb + (size_t)min(sl, n_split - 1) * mstride);
+    const float f = (sl < n_split && rec[0] != -INFINITY) ? rec[1] * __expf(rec[0] - M) : 0.f;
+    Z += wave_reduce_f<false>(lane < CB ? f : 0.f);
+    const float gl = f * rec[2];
+#pragma unroll
+    for (int s = 0; s < CB; ++s) {
+      const float gs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), s));
+      o0 += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[s] & 0xffffu)) * gs;
+      o1 += (float)__builtin_bit_cast(_Float16, (uint16_t)(w[s] >> 16)) * gs;
+    }
+  }
+  if (!has) return;
+  const float inv = Z > 0.f ? 1.f / Z : 0.f;
+  o0 *= inv;
+  o1 *= inv;
+  if (d0 >= rbeg) {
+    float cs, sn;
+    rope_cos_sin(-i, (d0 - rbeg) >> 1, rope, &cs, &sn);
+    const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
+    o0 = r0;
+    o1 = r1;
+  }
+  const size_t ob = (row * n_h + h) * (size_t)D + d0;
+  out[ob] = f32_to_bf16_bits(o0);
+  out[ob + 1] = f32_to_bf16_bits(o1);
+}
+
+// the combine launch: blocks of 8 splits up to 8, else of 64
+static void launch_combine(const MqaArgs& a, int n_split, hipStream_t st) {
+  const RopeRatio rope_rr = rope_ratio(a.rope_dim, a.rope_base);
+  auto kfn = n_split <= 8 ? mqa_combine_kernel<8> : mqa_combine_kernel<64>;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B), dim3(256), 0, st,
+                     (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d, n_split, a.rope_dim, rope_rr,
+                     (uint16_t*)a.out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1681,10 +1680,7 @@ static void launch_mfma_v(const MqaArgs& a, int kps, int n_split, hipStream_t st
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
                      a.rope_dim, rope_rr, a.scale, kps, n_split, units, (uint16_t*)a.out,
                      (float*)a.ws);
-  if (n_split > 1)
-    hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
-                       dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
-                       n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
+  if (n_split > 1) launch_combine(a, n_split, st);
 }
 
 // dynamic LDS of the streaming kernel: the chunk ring (raw mixed rows plus the
@@ -1716,10 +1712,7 @@ static void launch_decode_nw(const MqaArgs& a, int kps, int n_split, hipStream_t
                      a.k, a.m, (const uint16_t*)a.W, a.W_cap, a.n_win, a.sink, a.q_pos, a.Tq, a.n_h,
                      a.rope_dim, rope_rr, a.scale, kps, n_split, units, (uint16_t*)a.out,
                      (float*)a.ws, a.E_scale, a.W_scale);
-  if (n_split > 1)
-    hipLaunchKernelGGL(mqa_combine_kernel, dim3((unsigned)a.n_h, (unsigned)a.Tq, (unsigned)a.B),
-                       dim3(256), 0, st, (const float*)a.ws, a.sink, a.q_pos, a.Tq, a.n_h, a.d,
-                       n_split, a.rope_dim, rope_rr, (uint16_t*)a.out);
+  if (n_split > 1) launch_combine(a, n_split, st);
 }
 
 // waves per workgroup: as many head groups of one wave as divide n_h, up to four
