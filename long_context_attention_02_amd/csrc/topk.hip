@@ -22,6 +22,9 @@
 // Long rows with few queries (decode) run in two stages: workgroups select
 // the top-k of chunks of 16 k elements (any global top-k element is in its
 // chunk's top-k), then one workgroup per row selects from their union.
+#include <algorithm>
+#include <cmath>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -190,7 +193,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int need, TopkS
 // count still needed from the final group in *need; *tied reports whether the
 // final group holds more elements than needed (only possible for HALF = 0).
 template <class Src, int HALF>
-__device__ void radix_half(const Src& src, long long n, uint32_t lb, uint32_t k_and, uint32_t k_or,
+__device__ __forceinline__ void radix_half(const Src& src, long long n, uint32_t lb, uint32_t k_and, uint32_t k_or,
                            uint32_t hi_val, int& need, uint32_t& prefix, bool& tied, TopkShared& sh,
                            int& hb) {
   constexpr int V = Src::V;
@@ -301,7 +304,7 @@ __device__ __forceinline__ uint64_t bitonic_merge(uint64_t x, int t, int size, b
 // Bitonic sort of sh.buf[0 .. P), descending, P a power of two <= TK_THREADS:
 // thread t holds element t; partners closer than 64 sit in the same wave and
 // trade through lane permutes, farther ones through LDS.
-__device__ void sort_desc_regs(TopkShared& sh, int P) {
+__device__ __forceinline__ void sort_desc_regs(TopkShared& sh, int P) {
   static_assert(2 * TK_THREADS <= TK_KMAX, "two exchange buffers");
   const int t = threadIdx.x;
   uint64_t x = t < P ? sh.buf[t] : 0ull;   // each thread reads and later writes only slot t first
@@ -314,7 +317,7 @@ __device__ void sort_desc_regs(TopkShared& sh, int P) {
 }
 
 // the same order for P up to TK_KMAX, every compare-exchange through LDS
-__device__ void sort_desc_lds(TopkShared& sh, int P) {
+__device__ __forceinline__ void sort_desc_lds(TopkShared& sh, int P) {
   const int tid = threadIdx.x;
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -369,7 +372,7 @@ __device__ __forceinline__ void collect_groups(const uint32_t (&h)[tk_cg<V>()][V
 // (a guarded load is a branch with its own wait): past the end they read the
 // last group again, which is in bounds, and the count mask drops it.
 template <class Src, class Take>
-__device__ void collect_if(const Src& src, long long n, Take take_fn, TopkShared& sh) {
+__device__ __forceinline__ void collect_if(const Src& src, long long n, Take take_fn, TopkShared& sh) {
   constexpr int V = Src::V, CG = tk_cg<V>();
   const long long step = (long long)V * TK_THREADS;
   const long long last = ((n - 1) / V) * V;   // start of the last group
@@ -393,13 +396,13 @@ __device__ void collect_if(const Src& src, long long n, Take take_fn, TopkShared
 
 // every element with hi >= t (no tie to resolve)
 template <class Src>
-__device__ void collect_ge(const Src& src, long long n, uint32_t t, TopkShared& sh) {
+__device__ __forceinline__ void collect_ge(const Src& src, long long n, uint32_t t, TopkShared& sh) {
   collect_if(src, n, [t](uint32_t h, uint32_t) { return h >= t; }, sh);
 }
 
 // hi > thr_hi, plus hi == thr_hi with lo >= thr_lo (the k-th score is tied)
 template <class Src>
-__device__ void collect_tied(const Src& src, long long n, uint32_t lb, uint32_t thr_hi, uint32_t thr_lo,
+__device__ __forceinline__ void collect_tied(const Src& src, long long n, uint32_t lb, uint32_t thr_hi, uint32_t thr_lo,
                              TopkShared& sh) {
   collect_if(src, n, [=](uint32_t h, uint32_t l) {
     return (h >= lb) & ((h > thr_hi) | ((h == thr_hi) & (l >= thr_lo)));
@@ -411,7 +414,7 @@ __device__ void collect_tied(const Src& src, long long n, uint32_t lb, uint32_t 
 // block_lower_bound, which keeps at least min(k, n) of them); hi_and / hi_or:
 // AND / OR of their hi keys.
 template <class Src, bool SORT>
-__device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint32_t hi_and,
+__device__ __forceinline__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint32_t hi_and,
                            uint32_t hi_or, TopkShared& sh) {
   constexpr int V = Src::V;
   const int tid = threadIdx.x;
@@ -476,7 +479,7 @@ __device__ int select_topk(const Src& src, long long n, uint32_t lb, int k, uint
 
 // top-k of the scores p[0 .. n) (indices base + e): cached in LDS when they fit
 template <bool SORT>
-__device__ int select_row(const float* __restrict__ p, long long n, long long base, int k,
+__device__ __forceinline__ int select_row(const float* __restrict__ p, long long n, long long base, int k,
                           uint32_t* cache, bool use_cache, TopkShared& sh) {
   const int want = (int)min((long long)k, n);
   uint32_t a = ~0u, o = 0u, lmax = ~0u;
@@ -661,6 +664,133 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two stages with sorted lists.  A chunk of 16 k elements holds on average
+// k / nchunks of the row's top-k (the scores of a row are spread over its
+// chunks), so stage 1 keeps only the T largest of each chunk, sorted, plus the
+// (T+1)-th as the chunk's threshold, with T a few standard deviations above
+// that mean.  Stage 2 merges the sorted lists pairwise in LDS: an element's
+// place in the merged list is its place in its own list plus the number of
+// the partner list's elements above it (a binary search; the even list counts
+// strictly greater keys, the odd one greater-or-equal, so the 0 padding keys
+// land in distinct places), truncated to k.  The result is exact when every
+// chunk was reported whole (threshold 0) or the want-th merged key is above
+// every threshold: any unreported element lies below its chunk's threshold.
+// Otherwise the workgroup selects from the whole row (a rare, slow path).
+// ---------------------------------------------------------------------------
+static constexpr int TK_LIST_KEYS = 8192;   // merged keys held in LDS (two buffers of this many)
+
+// stage 1: the T largest keys of one chunk, descending, padded with 0 to Tp,
+// and the chunk's threshold (its (T+1)-th largest key, 0 if it has at most T)
+__global__ __launch_bounds__(TK_THREADS) void topk_chunk_sorted_kernel(
+    const float* __restrict__ I, const int* __restrict__ q_pos, long long N_cap, int m, int T, int Tp,
+    long long chunk, int nchunks, int use_cache, uint64_t* __restrict__ lists, uint64_t* __restrict__ thr) {
+  __shared__ TopkShared sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t cache[];
+  const size_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const long long n = row_nvis(q_pos, row, N_cap, m);
+  const long long lo = (long long)c * chunk;
+  const long long len = max(0LL, min(n, lo + chunk) - lo);
+  int got = 0;
+  if (len > 0) got = select_row<true>(I + row * (size_t)N_cap + lo, len, lo, T + 1, cache, use_cache != 0, sh);
+  uint64_t* dst = lists + (row * (size_t)nchunks + c) * (size_t)Tp;
+  for (int e = threadIdx.x; e < Tp; e += TK_THREADS) dst[e] = (e < got && e < T) ? sh.buf[e] : 0ull;
+  if (threadIdx.x == 0) thr[row * (size_t)nchunks + c] = got > T ? sh.buf[T] : 0ull;
+}
+
+// number of keys of the descending list p[0 .. L) above x (GE: at or above)
+template <bool GE>
+__device__ __forceinline__ int count_above(const uint64_t* p, int L, uint64_t x) {
+  int lo = 0, len = L;
+  while (len > 0) {
+    const int half = len >> 1;
+    const uint64_t v = p[lo + half];
+    if (GE ? (v >= x) : (v > x)) {
+      lo += half + 1;
+      len -= half + 1;
+    } else {
+      len = half;
+    }
+  }
+  return lo;
+}
+
+// stage 2: the k largest of the union of the row's nchunks sorted lists
+__global__ __launch_bounds__(TK_THREADS) void topk_merge_lists_kernel(
+    const uint64_t* __restrict__ lists, const uint64_t* __restrict__ thr, const float* __restrict__ I,
+    const int* __restrict__ q_pos, long long N_cap, int m, int k, int nchunks, int Tp,
+    int* __restrict__ idx_out, float* __restrict__ val_out) {
+  __shared__ TopkShared sh;
+  __shared__ uint64_t sthr;
+  extern __shared__ __attribute__((aligned(16))) uint64_t lds64[];   // two buffers of npow * Tp keys
+  const size_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const long long n = row_nvis(q_pos, row, N_cap, m);
+  const int want = (int)min((long long)k, n);
+  int npow = 1;
+  while (npow < nchunks) npow <<= 1;
+  const int tot = npow * Tp;
+  uint64_t* A = lds64;
+  uint64_t* Bf = lds64 + tot;
+  const uint64_t* lp = lists + row * (size_t)nchunks * (size_t)Tp;
+  // the thresholds: wave 0, one chunk per lane, loaded with the lists
+  uint64_t tl = 0ull;
+  if (tid < 64)
+    for (int c = tid; c < nchunks; c += 64) tl = max(tl, thr[row * (size_t)nchunks + c]);
+  for (int e = tid; e < tot; e += TK_THREADS) A[e] = e < nchunks * Tp ? lp[e] : 0ull;
+  if (tid < 64) {
+#pragma unroll
+    for (int x = 1; x < 64; x <<= 1) {
+      const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)tl, x, 64);
+      const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(tl >> 32), x, 64);
+      tl = max(tl, ((uint64_t)hi << 32) | lo);
+    }
+    if (tid == 0) sthr = tl;
+  }
+  __syncthreads();
+  int L = Tp, nl = npow;
+  while (nl > 1) {
+    const int Lo = min(2 * L, k);   // merged lists keep their k largest
+    for (int e = tid; e < nl * L; e += TK_THREADS) {
+      const int li = e / L, p = e - li * L;
+      const uint64_t x = A[e];
+      const uint64_t* part = A + (li ^ 1) * L;
+      // counts strictly above in the partner list (even lists) and at or above (odd)
+      const int pos = p + ((li & 1) ? count_above<true>(part, L, x) : count_above<false>(part, L, x));
+      if (pos < Lo) Bf[(li >> 1) * Lo + pos] = x;
+    }
+    __syncthreads();
+    uint64_t* t = A;
+    A = Bf;
+    Bf = t;
+    L = Lo;
+    nl >>= 1;
+  }
+  // exact unless some chunk left out keys that could rank among the want largest
+  const uint64_t maxthr = sthr;
+  const int nreal = count_above<false>(A, L, 0ull);
+  const bool exact = maxthr == 0ull || want == 0 || (nreal >= want && A[want - 1] > maxthr);
+  const float* rp = I + row * (size_t)N_cap;
+  const uint64_t* res = A;
+  int got = min(want, nreal);
+  if (!exact) {   // uniform: every thread read the same values
+    __syncthreads();
+    got = select_row<true>(rp, n, 0, k, (uint32_t*)lds64, false, sh);
+    res = sh.buf;
+  }
+  for (int e = tid; e < k; e += TK_THREADS) {
+    int idx = -1;
+    float val = -INFINITY;
+    if (e < got) {
+      idx = (int)(0xFFFFFFFFu - (uint32_t)res[e]);
+      val = rp[idx];
+    }
+    idx_out[row * (size_t)k + e] = idx;
+    if (val_out) val_out[row * (size_t)k + e] = val;
+  }
+}
+
 static bool topk_two_stage(long long rows, long long N_cap, int k, long long* chunk, int* nchunks) {
   const long long ch = 16LL * k;
   if (rows >= 512 || N_cap < 2 * ch) return false;
@@ -669,11 +799,28 @@ static bool topk_two_stage(long long rows, long long N_cap, int k, long long* ch
   return true;
 }
 
+// keys kept per chunk for the sorted-list stages: T (the chunk selects T + 1),
+// list stride Tp; false when the lists do not fit the merge's LDS
+static bool topk_lists(int k, int nchunks, int* T, int* Tp) {
+  const double mean = (double)k / nchunks;
+  const int est = (int)std::min<double>((double)k, std::ceil(mean + 6.0 * std::sqrt(mean) + 2.0));
+  int p = 1;
+  while (p < est) p <<= 1;
+  *Tp = p;
+  *T = p <= k ? p - 1 : k;   // a selection of T + 1 = p keys sorts in a power-of-two block
+  if (*T < 1) *T = std::min(k, 1);
+  int npow = 1;
+  while (npow < nchunks) npow <<= 1;
+  return (long long)npow * p <= TK_LIST_KEYS && *T + 1 <= TK_KMAX;
+}
+
 size_t topk_workspace_bytes(int B, int Tq, long long N_cap, int k) {
   long long chunk;
-  int nchunks;
+  int nchunks, T, Tp;
   const long long rows = (long long)B * Tq;
   if (!topk_two_stage(rows, N_cap, k, &chunk, &nchunks)) return 0;
+  if (topk_lists(k, nchunks, &T, &Tp))
+    return (size_t)rows * (size_t)nchunks * ((size_t)Tp + 1) * sizeof(uint64_t);
   return (size_t)rows * (size_t)nchunks * (size_t)k * sizeof(uint64_t);
 }
 
@@ -686,7 +833,22 @@ int launch_topk(const TopkArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.Tq;
   long long chunk;
   int nchunks;
-  if (topk_two_stage(rows, a.N_cap, a.k, &chunk, &nchunks)) {
+  int T, Tp;
+  if (topk_two_stage(rows, a.N_cap, a.k, &chunk, &nchunks) && topk_lists(a.k, nchunks, &T, &Tp)) {
+    uint64_t* lists = (uint64_t*)a.ws;
+    uint64_t* thr = lists + (size_t)rows * nchunks * Tp;
+    const bool c1 = chunk <= TK_CACHE32;
+    const size_t l1 = c1 ? ((size_t)chunk * 4 + 15) / 16 * 16 : 0;
+    int npow = 1;
+    while (npow < nchunks) npow <<= 1;
+    const size_t l2 = 2 * (size_t)npow * Tp * sizeof(uint64_t);
+    if (!set_lds((const void*)topk_chunk_sorted_kernel, l1) || !set_lds((const void*)topk_merge_lists_kernel, l2))
+      return -1;
+    hipLaunchKernelGGL(topk_chunk_sorted_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l1, st,
+                       a.I, a.q_pos, a.N_cap, a.m, T, Tp, chunk, nchunks, (int)c1, lists, thr);
+    hipLaunchKernelGGL(topk_merge_lists_kernel, dim3((unsigned)rows), dim3(TK_THREADS), l2, st, lists, thr, a.I,
+                       a.q_pos, a.N_cap, a.m, a.k, nchunks, Tp, a.idx, a.val);
+  } else if (topk_two_stage(rows, a.N_cap, a.k, &chunk, &nchunks)) {
     uint64_t* cand = (uint64_t*)a.ws;
     const bool c1 = chunk <= TK_CACHE32;
     const long long ncand = (long long)nchunks * a.k;

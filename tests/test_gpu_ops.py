@@ -272,15 +272,26 @@ TOPK_CASES = [
     ("prefill_rows", 1, 600, 2000, 4, 1024, "normal", "prefill"),
     ("decode_1M_full_shape", 16, 1, 262144, 4, 1024, "normal", "all"),
     ("prefill_full_row_length", 1, 40, 32768, 4, 1024, "normal", "prefill"),
+    # rows whose top scores crowd one chunk: the two-stage selection falls back to the row
+    ("two_stage_clustered_fallback", 3, 1, 70000, 4, 1024, "clustered", "all"),
+    ("two_stage_k512_clustered", 3, 1, 16384, 4, 512, "clustered", "all"),
 ]
 
 
-def _scores(g, kind, shape):
+def _scores(g, kind, shape, k=0):
     x = g.normal(1, shape, "f32")
     if kind == "ties":
         x = torch.floor(x * 2.0) / 2.0                 # few distinct values
         x[..., ::7] = 0.0
         x[..., 3::7] = -0.0
+    if kind == "clustered":
+        # the two-stage top-k reports a few standard deviations above k / chunks of each
+        # 16 k-element chunk: row 1 puts every top score in its second chunk, row 2
+        # rises with the index (all in the last chunk); row 0 stays N(0, 1)
+        ch = 16 * k
+        x[1, :, ch:2 * ch] += 10.0
+        if shape[0] > 2:
+            x[2] = torch.arange(shape[-1], dtype=torch.float32, device=x.device) / 1000.0
     return x.contiguous()
 
 
@@ -288,7 +299,7 @@ def _scores(g, kind, shape):
 def test_topk_bit_exact(csa, case):
     name, B, Tq, N, m, k, kind, pmode = case
     g = Gen(300 + TOPK_CASES.index(case), DEV)
-    I = _scores(g, kind, (B, Tq, N))
+    I = _scores(g, kind, (B, Tq, N), k)
     pos = _positions(pmode, B, Tq, N, m, g)
     ws_n = csa.csa_topk_workspace_size(B, Tq, N, k)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=DEV)
@@ -649,6 +660,31 @@ def test_compress_mixed_output(csa, B, T, R, tok_base, c, m, ov, s0, s1, ring):
         assert np.all(np.abs(dec - y) <= 0.5 * e4m3_ulp(y) * (1 + 1e-3) + 1e-6 * 448), b
         mism += int(np.sum(codes[b, slots] != rc))
     assert mism <= 0.001 * B * len(slots) * nope
+
+
+def test_compress_mixed_zero_rows(csa):
+    """A row whose code part is all zero stores scale 1 and zero codes (the rotated
+    dims are their bf16 values); rows that saturate nothing keep |code| <= 448."""
+    B, N, c, r = 2, 40, 512, 64
+    g = Gen(178, DEV)
+    x = g.normal(1, (B, N, c), "f32")
+    x[0, 3, : c - r] = 0.0                     # code part zero, rotated part not
+    x[1, 7, :] = 0.0                            # the whole row zero
+    x = x.contiguous()
+    E = torch.full((B, N, c + r), 0xAB, dtype=torch.uint8, device=DEV)
+    S = torch.full((B, N), float("nan"), dtype=torch.float32, device=DEV)
+    csa.csa_compress(x, None, None, None, E, T=N, m=1, overlap=0, s_begin=0, s_end=N, rope_dim=r, E_scale=S)
+    torch.cuda.synchronize()
+    for b, s in ((0, 3), (1, 7)):
+        assert float(S[b, s]) == 1.0
+        assert int(E[b, s, : c - r].max()) == 0
+    for b in range(B):
+        ref = O.rope(to_f64(x[b]), np.arange(N), r)   # no gamma: no norm; RoPE at position s (m = 1)
+        vals, rc, rs = O.quantize_rows_mixed(ref, r)
+        assert np.array_equal(S[b].cpu().numpy(), rs), b
+        assert np.mean(E[b, :, : c - r].cpu().numpy() == rc) > 0.999, b
+        got_rot = to_f64(E[b, :, c - r:].contiguous().view(torch.bfloat16))
+        assert row_rel_err(got_rot, vals[:, c - r:]) <= 2 ** -8, b   # fp32 vs fp64 RoPE, then bf16
 
 
 def _mixed_rows_from_oracle(x64, r):

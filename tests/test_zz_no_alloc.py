@@ -85,3 +85,32 @@ def test_noalloc_rejects_calls_beyond_the_scratch(csa):
     assert ei.value.status == 4 and "static" in str(ei.value)
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all()
+
+
+def test_noalloc_mixed_rows_equals_workspace_variant(csa):
+    """Mixed KV rows (e4m3 codes + row scale, bf16 rotated dims), stored by the
+    compressor: the no-allocation call equals the workspace call bit for bit."""
+    B, Tq, n_h, d, N, k, n_win, r = 4, 1, 64, 512, 700, 512, 128, 64
+    c = _case(805, B, Tq, n_h, d, N, k, n_win)
+    g = Gen(806, DEV)
+    gam = (1.0 + 0.25 * g.normal(1, (d,), "f32", per_slot=False)).contiguous()
+    E = torch.zeros((B, N, d + r), dtype=torch.uint8, device=DEV)
+    Es = torch.zeros((B, N), dtype=torch.float32, device=DEV)
+    W = torch.zeros((B, n_win, d + r), dtype=torch.uint8, device=DEV)
+    Ws = torch.zeros((B, n_win), dtype=torch.float32, device=DEV)
+    csa.csa_compress(g.normal(2, (B, N, d), "bf16"), None, None, None, E, T=N, m=1, overlap=0, s_begin=0,
+                     s_end=N, gamma=gam, rope_dim=r, pos_stride=4, E_scale=Es)
+    i = int(c["q_pos"][0, 0])
+    csa.csa_compress(g.normal(3, (B, n_win, d), "bf16"), None, None, None, W, T=i + 1, m=1, overlap=0,
+                     s_begin=i - n_win + 1, s_end=i + 1, tok_base=i - n_win + 1, gamma=gam, rope_dim=r,
+                     pos_stride=1, out_ring=n_win, E_scale=Ws)
+    kw = dict(n_win=n_win, sink=c["sink"], gamma_q=c["gamma_q"], rope_dim=r, scale=c["scale"], E_scale=Es,
+              W_scale=Ws)
+    ref = torch.full_like(c["q"], float("nan"))
+    ws = torch.empty(max(csa.csa_mqa_workspace_size(B, Tq, n_h, d, k + n_win), 1), dtype=torch.uint8, device=DEV)
+    csa.csa_sparse_mqa(c["q"], E, c["idx"], W, c["q_pos"], ref, workspace=ws, **kw)
+    got = torch.full_like(c["q"], float("nan"))
+    csa.csa_sparse_mqa_noalloc(c["q"], E, c["idx"], W, c["q_pos"], got, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref.float()).all()
+    assert torch.equal(ref.view(torch.uint8), got.view(torch.uint8))
