@@ -776,3 +776,27 @@ def test_mqa_mixed_rows_rejects_unsupported(csa):
     E5 = torch.zeros((1, 10, 512 + 32), dtype=torch.uint8, device=DEV)
     with pytest.raises(csa.CsaError):
         csa.csa_sparse_mqa(q5, E5, idx, None, pos, torch.zeros_like(q5), n_win=0, rope_dim=32, E_scale=S)
+
+
+def test_grouped_out_proj_full_size_sampled_rows(csa):
+    """The prefill-chunk shape (16,384 rows of 128 heads x 512 -> 16 groups x 1,024 ->
+    7,168, the 128 x 128 tiles without split): sampled rows of y and of the output
+    against the oracle's projection of those rows (rows are independent)."""
+    from oracle.proj import grouped_output_projection
+    T, n_h, c, G, d_g, d = 16384, 128, 512, 16, 1024, 7168
+    W = n_h * c // G
+    g = Gen(640, DEV)
+    o = g.normal(1, (T, n_h, c), "bf16")
+    W1 = (g.normal(2, (G, d_g, W), "f32") / math.sqrt(W)).to(torch.bfloat16).contiguous()
+    W2 = (g.normal(3, (d, G * d_g), "f32") / math.sqrt(G * d_g)).to(torch.bfloat16).contiguous()
+    y = torch.full((T, G * d_g), float("nan"), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(max(csa.csa_out_proj_workspace_size(T, n_h, c, G, d_g, d), 1), dtype=torch.uint8, device=DEV)
+    csa.csa_grouped_out_proj(o, W1, W2, y, out, workspace=ws)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 127, 128, 8191, 12345, 16383], device=DEV)
+    ry, rout = grouped_output_projection(to_f64(o[rows]).reshape(len(rows), n_h * c), to_f64(W1), to_f64(W2),
+                                         groups=G)
+    assert row_rel_err(to_f64(y[rows]), ry) <= TOL_BF16
+    assert row_rel_err(to_f64(out[rows]), rout) <= TOL_BF16
+    assert torch.isfinite(out.float()).all() and torch.isfinite(y.float()).all()
