@@ -19,9 +19,12 @@
 // The elements of a row (or chunk) are first copied into LDS once; on the way
 // the block forms the AND and the OR of all score keys, so the bits every key
 // shares are skipped and the digits start at the highest bit that differs.
-// Long rows with few queries (decode) run in two stages: workgroups select
-// the top-k of chunks of 16 k elements (any global top-k element is in its
-// chunk's top-k), then one workgroup per row selects from their union.
+// Long rows with few queries (decode) run in two stages over chunks of 16 k
+// elements: workgroups keep the T largest keys of each chunk, sorted, with the
+// chunk's (T+1)-th key as its threshold, then one workgroup per row merges the
+// sorted lists and checks the result against the thresholds (the sorted-list
+// stages below; when the lists do not fit its LDS, each chunk's top-k and a
+// selection over their union instead).
 #include <algorithm>
 #include <cmath>
 
