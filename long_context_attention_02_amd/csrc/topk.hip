@@ -21,10 +21,10 @@
 // shares are skipped and the digits start at the highest bit that differs.
 // Long rows with few queries (decode) run in two stages over chunks of 16 k
 // elements: workgroups keep the T largest keys of each chunk, sorted, with the
-// chunk's (T+1)-th key as its threshold, then one workgroup per row merges the
-// sorted lists and checks the result against the thresholds (the sorted-list
-// stages below; when the lists do not fit its LDS, each chunk's top-k and a
-// selection over their union instead).
+// chunk's (T+1)-th key as its threshold, then one workgroup per list places
+// its keys in the merged order and checks the result against the thresholds
+// (the sorted-list stages below; when the lists do not fit LDS, each chunk's
+// top-k and a selection over their union instead).
 #include <algorithm>
 #include <cmath>
 
@@ -672,16 +672,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 // k / nchunks of the row's top-k (the scores of a row are spread over its
 // chunks), so stage 1 keeps only the T largest of each chunk, sorted, plus the
 // (T+1)-th as the chunk's threshold, with T a few standard deviations above
-// that mean.  Stage 2 merges the sorted lists pairwise in LDS: an element's
-// place in the merged list is its place in its own list plus the number of
-// the partner list's elements above it (a binary search; the even list counts
-// strictly greater keys, the odd one greater-or-equal, so the 0 padding keys
-// land in distinct places), truncated to k.  The result is exact when every
-// chunk was reported whole (threshold 0) or the want-th merged key is above
-// every threshold: any unreported element lies below its chunk's threshold.
-// Otherwise the workgroup selects from the whole row (a rare, slow path).
+// that mean.  Stage 2 places every listed key in the merged order directly
+// (its place in its own list plus the keys above it in the other lists), one
+// workgroup per list.  The result is exact when every chunk was reported whole
+// (threshold 0) or the want-th merged key is above every threshold: any
+// unreported element lies below its chunk's threshold.  Otherwise one
+// workgroup selects from the whole row (a rare, slow path).
 // ---------------------------------------------------------------------------
-static constexpr int TK_LIST_KEYS = 8192;   // merged keys held in LDS (two buffers of this many)
+static constexpr int TK_LIST_KEYS = 8192;   // list keys of a row held in LDS by the merge
 
 // stage 1: the T largest keys of one chunk, descending, padded with 0 to Tp,
 // and the chunk's threshold (its (T+1)-th largest key, 0 if it has at most T)
@@ -719,29 +717,41 @@ __device__ __forceinline__ int count_above(const uint64_t* p, int L, uint64_t x)
   return lo;
 }
 
-// stage 2: the k largest of the union of the row's nchunks sorted lists
-__global__ __launch_bounds__(TK_THREADS) void topk_merge_lists_kernel(
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+
+// stage 2: the k largest of the union of a row's sorted lists, one workgroup
+// per (list, row).  Keys are unique and every real key is nonzero, so a key's
+// place in the merged order is its place in its own list plus the number of
+// keys above it in the other lists (binary searches in LDS); the workgroup
+// writes the keys of its list whose place is below want.  All workgroups of a
+// row reach the same exactness verdict from the same lists: the result is exact
+// when every chunk was reported whole (threshold 0) or at least want keys of
+// the union lie above the largest threshold (then no key a chunk left out can
+// rank among the want largest).  Otherwise the row's first workgroup selects
+// from the whole row and the others write nothing.
+__global__ __launch_bounds__(TK_THREADS) void topk_rank_lists_kernel(
     const uint64_t* __restrict__ lists, const uint64_t* __restrict__ thr, const float* __restrict__ I,
-    const int* __restrict__ q_pos, long long N_cap, int m, int k, int nchunks, int Tp,
+    const int* __restrict__ q_pos, long long N_cap, int m, int k, int nchunks, int T, int Tp,
     int* __restrict__ idx_out, float* __restrict__ val_out) {
   __shared__ TopkShared sh;
-  __shared__ uint64_t sthr;
-  extern __shared__ __attribute__((aligned(16))) uint64_t lds64[];   // two buffers of npow * Tp keys
-  const size_t row = blockIdx.x;
+  __shared__ int s_exact;
+  extern __shared__ __attribute__((aligned(16))) uint64_t lds64[];   // nchunks * Tp keys, then Tp places
+  const int own = blockIdx.x;
+  const size_t row = blockIdx.y;
   const int tid = threadIdx.x;
   const long long n = row_nvis(q_pos, row, N_cap, m);
   const int want = (int)min((long long)k, n);
-  int npow = 1;
-  while (npow < nchunks) npow <<= 1;
-  const int tot = npow * Tp;
+  const int tot = nchunks * Tp;
   uint64_t* A = lds64;
-  uint64_t* Bf = lds64 + tot;
-  const uint64_t* lp = lists + row * (size_t)nchunks * (size_t)Tp;
+  int* place = (int*)(lds64 + tot);
+  const uint64_t* lp = lists + row * (size_t)tot;
   // the thresholds: wave 0, one chunk per lane, loaded with the lists
   uint64_t tl = 0ull;
   if (tid < 64)
     for (int c = tid; c < nchunks; c += 64) tl = max(tl, thr[row * (size_t)nchunks + c]);
-  for (int e = tid; e < tot; e += TK_THREADS) A[e] = e < nchunks * Tp ? lp[e] : 0ull;
+  for (int e = tid; e < tot; e += TK_THREADS) A[e] = lp[e];
+  for (int e = tid; e < Tp; e += TK_THREADS) place[e] = e;
+  __syncthreads();
   if (tid < 64) {
 #pragma unroll
     for (int x = 1; x < 64; x <<= 1) {
@@ -749,44 +759,51 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_lists_kernel(
       const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(tl >> 32), x, 64);
       tl = max(tl, ((uint64_t)hi << 32) | lo);
     }
-    if (tid == 0) sthr = tl;
+    uint32_t above = 0;
+    if (tl != 0ull)
+      for (int c = tid; c < nchunks; c += 64) above += (uint32_t)count_above<false>(A + (size_t)c * Tp, Tp, tl);
+    above = wave_reduce_u32(above, OpAdd{});
+    if (tid == 0) s_exact = (tl == 0ull || want == 0 || (int)above >= want) ? 1 : 0;
+  }
+  // places: (element, other list) pairs spread over the threads
+  const uint64_t* mine = A + (size_t)own * Tp;
+  const int others = nchunks - 1;
+  for (int q = tid; q < T * others; q += TK_THREADS) {
+    const int e = q / others, li = q - e * others;
+    const int l = li + (li >= own ? 1 : 0);
+    const uint64_t x = mine[e];
+    if (x != 0ull) {
+      const int c = count_above<false>(A + (size_t)l * Tp, Tp, x);
+      if (c) atomicAdd(&place[e], c);
+    }
   }
   __syncthreads();
-  int L = Tp, nl = npow;
-  while (nl > 1) {
-    const int Lo = min(2 * L, k);   // merged lists keep their k largest
-    for (int e = tid; e < nl * L; e += TK_THREADS) {
-      const int li = e / L, p = e - li * L;
-      const uint64_t x = A[e];
-      const uint64_t* part = A + (li ^ 1) * L;
-      // counts strictly above in the partner list (even lists) and at or above (odd)
-      const int pos = p + ((li & 1) ? count_above<true>(part, L, x) : count_above<false>(part, L, x));
-      if (pos < Lo) Bf[(li >> 1) * Lo + pos] = x;
-    }
-    __syncthreads();
-    uint64_t* t = A;
-    A = Bf;
-    Bf = t;
-    L = Lo;
-    nl >>= 1;
-  }
-  // exact unless some chunk left out keys that could rank among the want largest
-  const uint64_t maxthr = sthr;
-  const int nreal = count_above<false>(A, L, 0ull);
-  const bool exact = maxthr == 0ull || want == 0 || (nreal >= want && A[want - 1] > maxthr);
   const float* rp = I + row * (size_t)N_cap;
-  const uint64_t* res = A;
-  int got = min(want, nreal);
-  if (!exact) {   // uniform: every thread read the same values
-    __syncthreads();
-    got = select_row<true>(rp, n, 0, k, (uint32_t*)lds64, false, sh);
-    res = sh.buf;
+  if (s_exact) {
+    for (int e = tid; e < T; e += TK_THREADS) {
+      const uint64_t x = mine[e];
+      const int r = place[e];
+      if (x != 0ull && r < want) {
+        const int idx = (int)(0xFFFFFFFFu - (uint32_t)x);
+        idx_out[row * (size_t)k + r] = idx;
+        if (val_out) val_out[row * (size_t)k + r] = rp[idx];
+      }
+    }
+    // exact means the union holds at least want keys: places want .. k - 1 are empty
+    if (own == 0)
+      for (int e = want + tid; e < k; e += TK_THREADS) {
+        idx_out[row * (size_t)k + e] = -1;
+        if (val_out) val_out[row * (size_t)k + e] = -INFINITY;
+      }
+    return;
   }
+  if (own != 0) return;   // uniform per workgroup
+  const int got = select_row<true>(rp, n, 0, k, (uint32_t*)lds64, false, sh);
   for (int e = tid; e < k; e += TK_THREADS) {
     int idx = -1;
     float val = -INFINITY;
     if (e < got) {
-      idx = (int)(0xFFFFFFFFu - (uint32_t)res[e]);
+      idx = (int)(0xFFFFFFFFu - (uint32_t)sh.buf[e]);
       val = rp[idx];
     }
     idx_out[row * (size_t)k + e] = idx;
@@ -812,9 +829,7 @@ static bool topk_lists(int k, int nchunks, int* T, int* Tp) {
   *Tp = p;
   *T = p <= k ? p - 1 : k;   // a selection of T + 1 = p keys sorts in a power-of-two block
   if (*T < 1) *T = std::min(k, 1);
-  int npow = 1;
-  while (npow < nchunks) npow <<= 1;
-  return (long long)npow * p <= TK_LIST_KEYS && *T + 1 <= TK_KMAX;
+  return (long long)nchunks * p <= TK_LIST_KEYS && *T + 1 <= TK_KMAX;
 }
 
 size_t topk_workspace_bytes(int B, int Tq, long long N_cap, int k) {
@@ -842,15 +857,13 @@ int launch_topk(const TopkArgs& a, hipStream_t st) {
     uint64_t* thr = lists + (size_t)rows * nchunks * Tp;
     const bool c1 = chunk <= TK_CACHE32;
     const size_t l1 = c1 ? ((size_t)chunk * 4 + 15) / 16 * 16 : 0;
-    int npow = 1;
-    while (npow < nchunks) npow <<= 1;
-    const size_t l2 = 2 * (size_t)npow * Tp * sizeof(uint64_t);
-    if (!set_lds((const void*)topk_chunk_sorted_kernel, l1) || !set_lds((const void*)topk_merge_lists_kernel, l2))
+    const size_t l2 = (size_t)nchunks * Tp * sizeof(uint64_t) + (size_t)Tp * sizeof(int);
+    if (!set_lds((const void*)topk_chunk_sorted_kernel, l1) || !set_lds((const void*)topk_rank_lists_kernel, l2))
       return -1;
     hipLaunchKernelGGL(topk_chunk_sorted_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l1, st,
                        a.I, a.q_pos, a.N_cap, a.m, T, Tp, chunk, nchunks, (int)c1, lists, thr);
-    hipLaunchKernelGGL(topk_merge_lists_kernel, dim3((unsigned)rows), dim3(TK_THREADS), l2, st, lists, thr, a.I,
-                       a.q_pos, a.N_cap, a.m, a.k, nchunks, Tp, a.idx, a.val);
+    hipLaunchKernelGGL(topk_rank_lists_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l2, st,
+                       lists, thr, a.I, a.q_pos, a.N_cap, a.m, a.k, nchunks, T, Tp, a.idx, a.val);
   } else if (topk_two_stage(rows, a.N_cap, a.k, &chunk, &nchunks)) {
     uint64_t* cand = (uint64_t*)a.ws;
     const bool c1 = chunk <= TK_CACHE32;
