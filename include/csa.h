@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 4
+#define CSA_ABI_VERSION 5
 
 /* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities).
  * CSA_MXFP4 is OCP MXFP4: FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6
@@ -118,13 +118,23 @@ int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* 
 /*
  * a1, batched: n_jobs compressions in one kernel launch.  jobs[q] holds the
  * arguments of one csa_compress call, with the same meaning, layout and
- * checks; the results equal those of the n_jobs separate calls bit for bit.
- * One launch lets the jobs' memory and barrier latencies overlap: a decode
- * step compresses a window row, a KV entry and an indexer key, each a few
- * microseconds of latency for a few kilobytes of data.
+ * checks.  One launch lets the jobs' memory and barrier latencies overlap: a
+ * decode step compresses a window row, a KV entry and an indexer key, each a
+ * few microseconds of latency for a few kilobytes of data.
  *
  *  jobs   : host array of n_jobs job descriptors, read during the call only.
  *  n_jobs : 1 .. CSA_COMPRESS_MAX_JOBS.
+ *  workspace / workspace_bytes : NULL / 0, or device memory of at least
+ *      csa_compress_workspace_size(jobs, n_jobs) bytes (any contents; owned by
+ *      the caller).  Without it the results equal those of the n_jobs
+ *      separate csa_compress calls bit for bit.  With it, jobs whose entries
+ *      pool 64 or more candidates (HCA blocks) over at most 256 (sequence,
+ *      entry) pairs spread each entry's channels over several workgroups (64
+ *      channels each; a second kernel normalises and stores the rows): the
+ *      same pooling summed in another order, so within rounding of the
+ *      separate calls, and deterministic.  A workspace smaller than required
+ *      is CSA_E_WORKSPACE.  Calls that share a workspace must not run
+ *      concurrently.
  *  Jobs must not write overlapping output rows (they run concurrently); a job
  *  with s_end == s_begin is a no-op.  Every job is checked before anything is
  *  launched; the first failing job's status is returned and csa_last_error()
@@ -149,7 +159,11 @@ typedef struct csa_compress_job {
   float* E_scale;
   long long out_batch_stride, out_ring;
 } csa_compress_job;
-int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream);
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* workspace, size_t workspace_bytes,
+                       void* stream);
+/* Workspace bytes csa_compress_batch takes for these jobs (0: none needed; a
+ * job that fails the checks counts for nothing). */
+size_t csa_compress_workspace_size(const csa_compress_job* jobs, int n_jobs);
 
 /*
  * a2 — lightning-indexer score (method page §3.3):

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_index_score",
+    "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_compress_workspace_size",
+    "csa_index_score",
     "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
     "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES", "csa_out_proj_workspace_size",
@@ -60,7 +61,9 @@ class _CompressJob(ctypes.Structure):
 
 
 _lib.csa_compress_batch.restype = _I
-_lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _I, _P]
+_lib.csa_compress_batch.argtypes = [ctypes.POINTER(_CompressJob), _I, _P, _S, _P]
+_lib.csa_compress_workspace_size.restype = _S
+_lib.csa_compress_workspace_size.argtypes = [ctypes.POINTER(_CompressJob), _I]
 _lib.csa_index_score.restype = _I
 _lib.csa_index_score.argtypes = [_P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P]
 _lib.csa_topk_workspace_size.restype = _S
@@ -176,14 +179,28 @@ def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
     _check(_lib.csa_compress(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw), _stream()))
 
 
-def csa_compress_batch(jobs):
-    """a1, several compressions in one launch.  ``jobs`` is a list of
-    (C_a, Z_a, C_b, Z_b, E, kwargs) with the arguments of csa_compress; the
-    outputs equal those of the separate calls."""
+def _compress_jobs(jobs):
     arr = (_CompressJob * max(len(jobs), 1))()
     for q, (C_a, Z_a, C_b, Z_b, E, kw) in enumerate(jobs):
         arr[q] = _CompressJob(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw))
-    _check(_lib.csa_compress_batch(arr, len(jobs), _stream()))
+    return arr
+
+
+def csa_compress_workspace_size(jobs) -> int:
+    """Bytes of the workspace csa_compress_batch takes for these jobs (0: none)."""
+    return int(_lib.csa_compress_workspace_size(_compress_jobs(jobs), len(jobs)))
+
+
+def csa_compress_batch(jobs, workspace=None):
+    """a1, several compressions in one launch.  ``jobs`` is a list of
+    (C_a, Z_a, C_b, Z_b, E, kwargs) with the arguments of csa_compress.
+    Without a workspace the outputs equal those of the separate calls; with one
+    (uint8 device tensor of csa_compress_workspace_size bytes) entries of many
+    candidates pool their channels over several workgroups."""
+    arr = _compress_jobs(jobs)
+    wp, wb = (workspace.data_ptr(), workspace.numel() * workspace.element_size()) if workspace is not None \
+        else (None, 0)
+    _check(_lib.csa_compress_batch(arr, len(jobs), wp, wb, _stream()))
 
 
 def csa_index_score(q_I, w_I, K_I, q_pos, I_out, *, m: int, K_scale=None):

@@ -57,6 +57,12 @@ struct CompressJob {
   const void *rCa, *rZa, *rCb, *rZb;
   long long n_new, r_stride, r_bs, out_rows;
   int in_ring;
+  // channel split (wide kernel): ns workgroups per entry, each pooling c / ns
+  // channels into slot b * n_entries + entry of the workspace arrays: the
+  // entry's pooled row (ws_rows, c floats) and the slices' sums of squares
+  // (ws_ss, ns floats); compress_finish_kernel then normalises and stores
+  int ns;
+  float *ws_ss, *ws_rows;
 };
 struct CompressBatch {
   CompressJob job[COMP_MAX_JOBS];
@@ -537,18 +543,23 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
   constexpr int VEC = IDT == DT_F32 ? 4 : 8;   // channels per 16-byte piece
   constexpr int ESZ = IDT == DT_F32 ? 4 : 2;
   const int c = J.c, m = J.m;
-  const int CV = c / VEC;                      // pieces per row (host: c % VEC == 0, c <= 1024)
+  const int ns = J.ns;                         // channel slices (1: whole rows)
+  const int cs = c / ns;                       // channels of this workgroup (host: whole pieces)
+  const int slice = ns > 1 ? (int)(blockIdx.x % (unsigned)ns) : 0;
+  const long long ent = ns > 1 ? (long long)(blockIdx.x / (unsigned)ns) : (long long)blockIdx.x;
+  const int c0 = slice * cs;
+  const int CV = cs / VEC;                     // pieces per slice row (host: cs % VEC == 0, c <= 1024)
   const int TG = J.G;                          // token groups (host: wide_groups)
   const int b = blockIdx.y;
   long long s, T, tbase;
   if (J.T0) {   // append: the entries whose blocks complete with the new tokens
     const long long t0 = J.T0[b];
-    s = t0 / m + J.s_begin + blockIdx.x;
+    s = t0 / m + J.s_begin + ent;
     T = t0 + J.n_new;
     if ((long long)m * (s + 1) > T) return;   // (whole workgroup)
     tbase = t0;
   } else {
-    s = J.s_begin + blockIdx.x;
+    s = J.s_begin + ent;
     T = seq_tokens(J, b);
     if ((long long)m * s >= T) return;   // no such entry in this sequence (whole workgroup)
     tbase = J.tok_base;
@@ -564,10 +575,10 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
   const long long ncand = na + nb;   // >= 1: the entry's block starts below T
   const size_t base = (size_t)b * (size_t)J.in_bs;
   const size_t rbase = (size_t)b * (size_t)J.r_bs;
-  float* pm = smem;              // [TG][c] running maxima
-  float* ps = pm + TG * c;       // [TG][c] sums
-  float* pa = ps + TG * c;       // [TG][c] weighted sums
-  float* row = pa + TG * c;      // [c]
+  float* pm = smem;              // [TG][cs] running maxima
+  float* ps = pm + TG * cs;      // [TG][cs] sums
+  float* pa = ps + TG * cs;      // [TG][cs] weighted sums
+  float* row = pa + TG * cs;     // [c]
   float* red = row + c;          // [16]
 
   // gamma of channel tid and of its RoPE partner, loaded with the candidates
@@ -596,7 +607,7 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
         // a token before the appended ones comes from the ring (append mode only)
         const bool from_ring = tok < tbase;
         const size_t off = (from_ring ? rbase + (size_t)(tok % J.in_ring) * (size_t)J.r_stride
-                                      : base + (size_t)(tok - tbase) * (size_t)c) + (size_t)cv * VEC;
+                                      : base + (size_t)(tok - tbase) * (size_t)c) + (size_t)(c0 + cv * VEC);
         const char* Cp = (const char*)(from_ring ? (in_a ? J.rCa : J.rCb) : (in_a ? J.Ca : J.Cb)) + off * ESZ;
         const char* Zp0 = (const char*)(from_ring ? (in_a ? J.rZa : J.rZb) : (in_a ? J.Za : J.Zb));
         const char* Zp = Zp0 ? Zp0 + off * ESZ : nullptr;
@@ -640,34 +651,79 @@ __device__ __forceinline__ void compress_entry_wide(const CompressJob& J, float*
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       const int j = cv * VEC + e;
-      pm[tg * c + j] = mx[e];
-      ps[tg * c + j] = sum[e];
-      pa[tg * c + j] = acc[e];
+      pm[tg * cs + j] = mx[e];
+      ps[tg * cs + j] = sum[e];
+      pa[tg * cs + j] = acc[e];
     }
   }
   __syncthreads();
 
   // merge the TG partials of channel j = tid, in group order
-  float ss = 0.f;
-  if ((int)threadIdx.x < c) {
+  float ss = 0.f, v = 0.f;
+  if ((int)threadIdx.x < cs) {
     const int j = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll 4
-    for (int q = 0; q < TG; ++q) M = fmaxf(M, pm[q * c + j]);
+    for (int q = 0; q < TG; ++q) M = fmaxf(M, pm[q * cs + j]);
     float S = 0.f, A = 0.f;
 #pragma unroll 4
     for (int q = 0; q < TG; ++q) {
-      const float mq = pm[q * c + j];
+      const float mq = pm[q * cs + j];
       const float f = mq == -INFINITY ? 0.f : __expf(mq - M);   // a group that saw no candidate adds 0
-      S += ps[q * c + j] * f;
-      A += pa[q * c + j] * f;
+      S += ps[q * cs + j] * f;
+      A += pa[q * cs + j] * f;
     }
-    const float v = S > 0.f ? A / S : 0.f;
-    row[j] = v;
+    v = S > 0.f ? A / S : 0.f;
     ss = v * v;
   }
-  __syncthreads();   // row[] complete (the epilogue reads RoPE partners)
-  compress_store<ODT, COMPX_THREADS>(J, s, b, row, ss, red, gj, gp);
+  if (ns == 1) {
+    if ((int)threadIdx.x < c) row[threadIdx.x] = v;
+    __syncthreads();   // row[] complete (the epilogue reads RoPE partners)
+    compress_store<ODT, COMPX_THREADS>(J, s, b, row, ss, red, gj, gp);
+    return;
+  }
+  // channel split: the slice's values and its sum of squares go to the
+  // workspace (compress_finish_kernel adds the slices' sums in slice order).
+  // Handing the row to a second kernel costs a launch; finishing it in the
+  // last slice to arrive took device-scope fences, each a cache writeback that
+  // cost more than the launch.
+  const size_t slot = (size_t)b * (size_t)J.n_entries + (size_t)ent;
+  if ((int)threadIdx.x < cs) J.ws_rows[slot * (size_t)c + c0 + threadIdx.x] = v;
+  float w = ss;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int q = 0; q < (cs + 63) / 64; ++q) t += red[q];
+    J.ws_ss[slot * (size_t)ns + slice] = t;
+  }
+}
+
+// The rows of split entries: the pooled row from the workspace, the slices'
+// sums of squares in slice order, then the RMSNorm / RoPE / store epilogue.
+// One workgroup per (entry, sequence) of each split job (jobs on whole rows
+// return at once).
+template <int ODT>
+__device__ __forceinline__ void compress_finish(const CompressJob& J, float* smem) {
+  const int c = J.c, ns = J.ns, b = blockIdx.y;
+  const long long ent = blockIdx.x;
+  const long long s = J.s_begin + ent;
+  if ((long long)J.m * s >= seq_tokens(J, b)) return;   // no such entry in this sequence (whole workgroup)
+  if (J.out_rows > 0 && (J.out_ring > 0 ? s % J.out_ring : s) >= J.out_rows) return;
+  float* row = smem;       // [c]
+  float* red = row + c;    // [16]
+  const size_t slot = (size_t)b * (size_t)J.n_entries + (size_t)ent;
+  const float* __restrict__ gsrc = J.gamma ? J.gamma : k_ones.v;
+  const int jc = min((int)threadIdx.x, c - 1);
+  float gj[1] = {gsrc[jc]}, gp[1] = {gsrc[min(jc ^ 1, c - 1)]};
+  if ((int)threadIdx.x < c) row[threadIdx.x] = J.ws_rows[slot * (size_t)c + threadIdx.x];
+  float tot = 0.f;
+  if (threadIdx.x == 0)
+    for (int q = 0; q < ns; ++q) tot += J.ws_ss[slot * (size_t)ns + q];
+  __syncthreads();
+  compress_store<ODT, COMPX_THREADS>(J, s, b, row, tot, red, gj, gp);
 }
 
 __global__ __launch_bounds__(COMPX_THREADS) void compress_wide_kernel(const CompressBatch jb) {
@@ -677,7 +733,7 @@ __global__ __launch_bounds__(COMPX_THREADS) void compress_wide_kernel(const Comp
   // compiler copy all of it to scratch memory first
   (void)jb;
   const CompressJob& J = ((const CompressBatch*)__builtin_amdgcn_kernarg_segment_ptr())->job[blockIdx.z];
-  if ((long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
+  if ((long long)blockIdx.x >= J.n_entries * J.ns || (int)blockIdx.y >= J.B) return;
   switch (J.in_dtype * 5 + J.out_dtype) {
     case DT_F32 * 5 + DT_F32: compress_entry_wide<DT_F32, DT_F32>(J, smem); break;
     case DT_F32 * 5 + DT_BF16: compress_entry_wide<DT_F32, DT_BF16>(J, smem); break;
@@ -689,6 +745,20 @@ __global__ __launch_bounds__(COMPX_THREADS) void compress_wide_kernel(const Comp
     case DT_BF16 * 5 + DT_FP8: compress_entry_wide<DT_BF16, DT_FP8>(J, smem); break;
     case DT_BF16 * 5 + DT_MX4: compress_entry_wide<DT_BF16, DT_MX4>(J, smem); break;
     default: compress_entry_wide<DT_BF16, DT_MIX>(J, smem); break;
+  }
+}
+
+__global__ __launch_bounds__(COMPX_THREADS) void compress_finish_kernel(const CompressBatch jb) {
+  extern __shared__ float smem[];
+  (void)jb;
+  const CompressJob& J = ((const CompressBatch*)__builtin_amdgcn_kernarg_segment_ptr())->job[blockIdx.z];
+  if (J.ns == 1 || (long long)blockIdx.x >= J.n_entries || (int)blockIdx.y >= J.B) return;
+  switch (J.out_dtype) {
+    case DT_F32: compress_finish<DT_F32>(J, smem); break;
+    case DT_BF16: compress_finish<DT_BF16>(J, smem); break;
+    case DT_FP8: compress_finish<DT_FP8>(J, smem); break;
+    case DT_MX4: compress_finish<DT_MX4>(J, smem); break;
+    default: compress_finish<DT_MIX>(J, smem); break;
   }
 }
 
@@ -708,6 +778,7 @@ static CompressJob make_job(const CompressArgs& x, int G) {
   J.eps = x.eps;
   J.in_dtype = x.in_dtype; J.out_dtype = x.out_dtype;
   J.B = x.B; J.c = x.c; J.m = x.m; J.overlap = x.overlap; J.G = G; J.rope_dim = x.rope_dim;
+  J.ns = 1;
   return J;
 }
 
@@ -726,6 +797,37 @@ static bool wide_job(const CompressArgs& x) { return x.c <= 1024 && inputs_in_pi
 static int wide_groups(int c, int vec, int ncand_max) {
   return std::max(1, std::min(std::min(COMPX_THREADS / (c / vec), COMPX_MAXTG), ncand_max));
 }
+static bool wave_job(const CompressArgs& x);
+
+// Channel slices of a wide job on the split path: entries of many candidates
+// (HCA blocks) in a launch of few workgroups, where one workgroup per entry is
+// bound by its own ALU work (every candidate's exponentials); 64-channel slices
+// spread it over c / 64 workgroups.  1: whole rows.
+static constexpr int COMPX_SLICE = 64;
+static constexpr int COMPX_SPLIT_MAXTG = 32;     // token groups of a slice
+static constexpr long long COMPX_SPLIT_ITEMS = 256;   // (sequence, entry) pairs at most
+static int split_slices(const CompressArgs& x) {
+  const int ncand_max = x.overlap ? 2 * x.m : x.m;
+  const long long items = (long long)x.B * (x.s_end - x.s_begin);
+  if (ncand_max < 64 || x.c % COMPX_SLICE != 0 || x.c < 2 * COMPX_SLICE || items > COMPX_SPLIT_ITEMS) return 1;
+  return x.c / COMPX_SLICE;
+}
+static size_t ws_align(size_t x) { return (x + 255) / 256 * 256; }
+size_t compress_workspace_bytes(const CompressArgs* a, int n_jobs) {
+  size_t ss = 0, rows = 0;
+  for (int q = 0; q < n_jobs; ++q) {
+    const CompressArgs& x = a[q];
+    if (wave_job(x) || !wide_job(x)) continue;
+    const int ns = split_slices(x);
+    if (ns == 1) continue;
+    const size_t slots = (size_t)x.B * (size_t)(x.s_end - x.s_begin);
+    ss += slots * ns;
+    rows += slots * x.c;
+  }
+  if (ss == 0) return 0;
+  return ws_align(ss * 4) + rows * 4;
+}
+
 static bool wave_job(const CompressArgs& x) {
   const int ncand_max = x.overlap ? 2 * x.m : x.m;
   const int vec = x.in_dtype == DT_F32 ? 4 : 8;
@@ -741,7 +843,7 @@ static bool wave_job(const CompressArgs& x) {
          x.c <= 64 * COMPW_MAXP * vec && x.rope_dim <= COMPW_MAXR && in_al && out_al;
 }
 
-int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
+int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st, void* ws, size_t ws_bytes) {
   if (n_jobs < 1 || n_jobs > COMP_MAX_JOBS) return -1;
   // jobs with few candidates per entry: one wave per entry, all in one launch
   CompressWaveBatch wb{};
@@ -767,15 +869,43 @@ int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
     long long gx = 1;
     int gy = 1;
     int nx = 0;
+    // the split path's workspace: slice sums, then rows (compress_workspace_bytes)
+    const size_t need = compress_workspace_bytes(a, n_jobs);
+    const bool split = ws != nullptr && need > 0 && ws_bytes >= need;
+    size_t o_rows = 0;
+    if (split) {
+      size_t ss = 0;
+      for (int q = 0; q < n_jobs; ++q)
+        if (to_wide(a[q]) && split_slices(a[q]) > 1)
+          ss += (size_t)a[q].B * (size_t)(a[q].s_end - a[q].s_begin) * split_slices(a[q]);
+      o_rows = ws_align(ss * 4);
+    }
+    size_t u_ss = 0, u_rows = 0;   // workspace elements taken so far
+    long long fx = 0;              // entries of the largest split job
+    size_t flds = 0;
     for (int q = 0; q < n_jobs; ++q) {
       if (!to_wide(a[q])) continue;
       const CompressArgs& x = a[q];
       const int vec = x.in_dtype == DT_F32 ? 4 : 8;
-      xb.job[nx] = make_job(x, wide_groups(x.c, vec, x.overlap ? 2 * x.m : x.m));
-      const int TG = wide_groups(x.c, vec, x.overlap ? 2 * x.m : x.m);
-      const size_t l = (size_t)(3 * TG * x.c + x.c + 16) * sizeof(float);
+      const int ns = split ? split_slices(x) : 1;
+      const int cs = x.c / ns;
+      const int ncand_max = x.overlap ? 2 * x.m : x.m;
+      const int TG = ns == 1 ? wide_groups(x.c, vec, ncand_max)
+                             : std::max(1, std::min(std::min(COMPX_THREADS / (cs / vec), COMPX_SPLIT_MAXTG), ncand_max));
+      xb.job[nx] = make_job(x, TG);
+      if (ns > 1) {
+        const size_t slots = (size_t)x.B * (size_t)(x.s_end - x.s_begin);
+        xb.job[nx].ns = ns;
+        xb.job[nx].ws_ss = (float*)ws + u_ss;
+        xb.job[nx].ws_rows = (float*)((char*)ws + o_rows) + u_rows;
+        u_ss += slots * ns;
+        u_rows += slots * x.c;
+        fx = std::max(fx, xb.job[nx].n_entries);
+        flds = std::max(flds, (size_t)(x.c + 16) * sizeof(float));
+      }
+      const size_t l = (size_t)(3 * TG * cs + x.c + 16) * sizeof(float);
       if (l > lds) lds = l;
-      if (xb.job[nx].n_entries > gx) gx = xb.job[nx].n_entries;
+      if (xb.job[nx].n_entries * ns > gx) gx = xb.job[nx].n_entries * ns;
       if (x.B > gy) gy = x.B;
       ++nx;
     }
@@ -787,6 +917,9 @@ int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st) {
         return -1;
       hipLaunchKernelGGL(compress_wide_kernel, dim3((unsigned)gx, (unsigned)gy, (unsigned)nx),
                          dim3(COMPX_THREADS), lds, st, xb);
+      if (fx > 0)
+        hipLaunchKernelGGL(compress_finish_kernel, dim3((unsigned)fx, (unsigned)gy, (unsigned)nx),
+                           dim3(COMPX_THREADS), flds, st, xb);
     }
     if (nw + nx == n_jobs) return hipGetLastError() == hipSuccess ? 0 : -1;
   }

@@ -143,7 +143,8 @@ int csa_compress(const void* C_a, const void* Z_a, const void* C_b, const void* 
   return ok();
 }
 
-int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
+int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (!jobs) return fail(CSA_E_NULL, "csa_compress_batch: jobs is NULL");
   if (n_jobs < 1 || n_jobs > CSA_COMPRESS_MAX_JOBS)
     return fail(CSA_E_SHAPE, "csa_compress_batch: n_jobs = %d outside [1, %d]", n_jobs,
@@ -157,9 +158,27 @@ int csa_compress_batch(const csa_compress_job* jobs, int n_jobs, void* stream) {
     if (st != CSA_OK) return st;
     if (jobs[q].s_end > jobs[q].s_begin) a[n++] = compress_args(jobs[q]);
   }
-  if (n > 0 && csa::launch_compress(a, n, (hipStream_t)stream) != 0)
+  if (workspace) {
+    const size_t need = n > 0 ? csa::compress_workspace_bytes(a, n) : 0;
+    if (workspace_bytes < need)
+      return fail(CSA_E_WORKSPACE, "csa_compress_batch: workspace of %zu bytes, %zu needed", workspace_bytes,
+                  need);
+  }
+  if (n > 0 && csa::launch_compress(a, n, (hipStream_t)stream, workspace, workspace_bytes) != 0)
     return fail(CSA_E_HIP, "csa_compress_batch: kernel launch failed");
   return ok();
+}
+
+size_t csa_compress_workspace_size(const csa_compress_job* jobs, int n_jobs) {
+  if (!jobs || n_jobs < 1 || n_jobs > CSA_COMPRESS_MAX_JOBS) return 0;
+  csa::CompressArgs a[CSA_COMPRESS_MAX_JOBS];
+  int n = 0;
+  for (int q = 0; q < n_jobs; ++q)
+    if (check_compress(jobs[q], "csa_compress_workspace_size") == CSA_OK && jobs[q].s_end > jobs[q].s_begin)
+      a[n++] = compress_args(jobs[q]);
+  const size_t need = n > 0 ? csa::compress_workspace_bytes(a, n) : 0;
+  ok();   // a failing job counts for nothing; it leaves no error behind
+  return need;
 }
 
 int csa_index_score(const void* q_I, int q_dtype, const float* w_I,

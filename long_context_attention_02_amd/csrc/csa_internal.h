@@ -26,8 +26,11 @@ struct CompressArgs {
   float* E_scale;
   long long out_bs, out_ring;
 };
-// n_jobs (1 .. 8) independent compressions in one launch
-int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st);
+// n_jobs (1 .. 8) independent compressions in one launch.  ws / ws_bytes: the
+// optional workspace of the channel-split path (compress_workspace_bytes; NULL:
+// every job runs whole rows)
+int launch_compress(const CompressArgs* a, int n_jobs, hipStream_t st, void* ws = nullptr, size_t ws_bytes = 0);
+size_t compress_workspace_bytes(const CompressArgs* a, int n_jobs);
 
 struct IndexArgs {
   const void* q;

@@ -19,8 +19,8 @@
 // The elements of a row (or chunk) are first copied into LDS once; on the way
 // the block forms the AND and the OR of all score keys, so the bits every key
 // shares are skipped and the digits start at the highest bit that differs.
-// Long rows with few queries (decode) run in two stages over chunks of 16 k
-// elements: workgroups keep the T largest keys of each chunk, sorted, with the
+// Long rows with few queries (decode) run in two stages over chunks of up to
+// 16 k elements: workgroups keep the T largest keys of each chunk, sorted, with the
 // chunk's (T+1)-th key as its threshold, then one workgroup per list places
 // its keys in the merged order and checks the result against the thresholds
 // (the sorted-list stages below; when the lists do not fit LDS, each chunk's
@@ -286,6 +286,9 @@ __device__ __forceinline__ uint64_t bitonic_step(uint64_t x, int t, bool desc, T
     y = t < P ? b[t ^ STRIDE] : 0ull;
     par ^= 1;
   } else {
+    // a wave whose threads all lie past P holds no key: it skips the work
+    // (wave-uniform, so the lane exchanges of the other waves see whole waves)
+    if (__builtin_amdgcn_readfirstlane(t & ~63) >= P) return x;
     const uint32_t lo = xchg_u32<STRIDE>((uint32_t)x), hi = xchg_u32<STRIDE>((uint32_t)(x >> 32));
     y = ((uint64_t)hi << 32) | lo;
   }
@@ -347,6 +350,12 @@ template <int V>
 __device__ __forceinline__ void collect_groups(const uint32_t (&h)[tk_cg<V>()][V], const uint32_t (&l)[tk_cg<V>()][V],
                                                const bool (&take)[tk_cg<V>()][V], TopkShared& sh) {
   constexpr int CG = tk_cg<V>();
+  bool any = false;
+#pragma unroll
+  for (int c = 0; c < CG; ++c)
+#pragma unroll
+    for (int v = 0; v < V; ++v) any = any || take[c][v];
+  if (__ballot(any) == 0ull) return;   // wave-uniform: most waves take nothing near the end of a select
   uint64_t bal[CG][V];
   int tot = 0;
 #pragma unroll
@@ -476,6 +485,119 @@ __device__ __forceinline__ int select_topk(const Src& src, long long n, uint32_t
     __syncthreads();
     if (P <= TK_THREADS) sort_desc_regs(sh, P);
     else sort_desc_lds(sh, P);
+  }
+  return want;
+}
+
+// Sort of the cnt unique keys in sh.buf (cnt <= TK_THREADS) by rank: the
+// place of a key is the number of keys above it, counted by S = TK_THREADS / P
+// threads per key (P: cnt rounded up to a power of two, at least 16) and
+// summed over those lanes; keys placed below want are written back in order.
+// Cheaper than the bitonic sort for a few hundred keys (its work grows with
+// cnt squared).  Reads past cnt stay inside sh.buf (cnt + 8 S <= TK_KMAX) and
+// are masked.
+__device__ __forceinline__ void sort_desc_rank(TopkShared& sh, int cnt, int P, int want) {
+  const int tid = threadIdx.x;
+  const int S = TK_THREADS / P;
+  const int i = tid / S, part = tid - i * S;
+  const uint64_t x = i < cnt ? sh.buf[i] : 0ull;
+  int above = 0;
+  for (int j0 = part; j0 < cnt; j0 += 8 * S) {
+    uint64_t y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) y[u] = sh.buf[j0 + u * S];   // eight reads in flight
+#pragma unroll
+    for (int u = 0; u < 8; ++u) above += (j0 + u * S < cnt && y[u] > x) ? 1 : 0;
+  }
+  for (int w = 1; w < S; w <<= 1) above += __shfl_xor(above, w, 64);
+  __syncthreads();   // every read of the unsorted keys is done
+  if (part == 0 && i < cnt && above < want) sh.buf[above] = x;
+  __syncthreads();
+}
+
+// The want largest keys of a whole chunk of NV * 4 * TK_THREADS scores at p
+// (16-byte aligned; indices base + e), sorted into sh.buf, with the scores
+// held in registers (NV vectors of 4 per thread).  A bound b with at least
+// want threads whose largest key is at or above it, so at least want
+// elements, comes from two histogram passes over the thread maxima: the top
+// 10 bits of the order key, then the next 10 inside the bin where the count
+// from the top reaches want.  The elements at or above b are collected and,
+// when they fit one sort (TK_THREADS), sorted; the first want are the answer.
+// Returns want, or -1 when too many elements lie at or above b (heavy ties):
+// the caller then runs the general selection.
+template <int NV>
+__device__ __forceinline__ int chunk_select_regs(const float* __restrict__ p, long long base, int want,
+                                                 TopkShared& sh) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 2 * TK_BINS; e += TK_THREADS) sh.hist[e / TK_BINS][e % TK_BINS] = 0u;
+  if (tid == 0) sh.count = 0;
+  f32x4_t v[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) v[u] = *(const f32x4_t*)(p + 4 * tid + 4 * TK_THREADS * u);
+  uint32_t h[NV][4];
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      h[u][q] = ord_key(v[u][q]);
+      lmax = max(lmax, h[u][q]);
+    }
+  __syncthreads();   // the histograms are clear
+  atomicAdd(&sh.hist[0][lmax >> 22], 1u);
+  __syncthreads();
+  find_digit(sh.hist[0], want, sh);
+  __syncthreads();
+  const uint32_t d1 = (uint32_t)sh.digit;
+  const int need = want - sh.cum;
+  if ((lmax >> 22) == d1) atomicAdd(&sh.hist[1][(lmax >> 12) & (TK_BINS - 1)], 1u);
+  __syncthreads();
+  find_digit(sh.hist[1], need, sh);
+  __syncthreads();
+  const uint32_t b = (d1 << 22) | ((uint32_t)sh.digit << 12);
+  // collect every element at or above b: one atomic per wave for its range of slots
+  bool any = false;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) any = any || h[u][q] >= b;
+  if (__ballot(any) != 0ull) {   // wave-uniform
+    uint64_t bal[NV][4];
+    int tot = 0;
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bal[u][q] = __ballot(h[u][q] >= b);
+        tot += __popcll(bal[u][q]);
+      }
+    int off = 0;
+    if ((tid & 63) == 0) off = atomicAdd(&sh.count, tot);
+    off = __builtin_amdgcn_readfirstlane(off);
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int slot = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u][q] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u][q], 0u));
+        if (h[u][q] >= b && slot < TK_KMAX)
+          sh.buf[slot] = ((uint64_t)h[u][q] << 32) |
+                         (0xFFFFFFFFu - (uint32_t)(base + 4 * tid + 4 * TK_THREADS * u + q));
+        off += __popcll(bal[u][q]);
+      }
+  }
+  __syncthreads();
+  const int cnt = sh.count;
+  __syncthreads();   // every thread has the count before anything rewrites it
+  if (cnt > TK_THREADS) return -1;
+  int P = 16;
+  while (P < cnt) P <<= 1;
+  if (P <= 512) {
+    sort_desc_rank(sh, cnt, P, want);
+  } else {
+    for (int e = cnt + tid; e < P; e += TK_THREADS) sh.buf[e] = 0ull;
+    __syncthreads();
+    sort_desc_regs(sh, P);
   }
   return want;
 }
@@ -668,8 +790,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Two stages with sorted lists.  A chunk of 16 k elements holds on average
-// k / nchunks of the row's top-k (the scores of a row are spread over its
+// Two stages with sorted lists.  A chunk (16 k elements, or shorter so that a
+// row has 16 of them) holds on average k / nchunks of the row's top-k (the scores of a row are spread over its
 // chunks), so stage 1 keeps only the T largest of each chunk, sorted, plus the
 // (T+1)-th as the chunk's threshold, with T a few standard deviations above
 // that mean.  Stage 2 places every listed key in the merged order directly
@@ -682,7 +804,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 static constexpr int TK_LIST_KEYS = 8192;   // list keys of a row held in LDS by the merge
 
 // stage 1: the T largest keys of one chunk, descending, padded with 0 to Tp,
-// and the chunk's threshold (its (T+1)-th largest key, 0 if it has at most T)
+// and the chunk's threshold (its (T+1)-th largest key, 0 if it has at most T).
+// NV > 0: chunks of NV * 4 * TK_THREADS elements; whole, aligned chunks take
+// the register path
+template <int NV>
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_sorted_kernel(
     const float* __restrict__ I, const int* __restrict__ q_pos, long long N_cap, int m, int T, int Tp,
     long long chunk, int nchunks, int use_cache, uint64_t* __restrict__ lists, uint64_t* __restrict__ thr) {
@@ -693,8 +818,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_sorted_kernel(
   const long long n = row_nvis(q_pos, row, N_cap, m);
   const long long lo = (long long)c * chunk;
   const long long len = max(0LL, min(n, lo + chunk) - lo);
-  int got = 0;
-  if (len > 0) got = select_row<true>(I + row * (size_t)N_cap + lo, len, lo, T + 1, cache, use_cache != 0, sh);
+  const float* cp = I + row * (size_t)N_cap + lo;
+  int got = -1;
+  if constexpr (NV > 0) {
+    if (len == chunk && ((uintptr_t)cp & 15u) == 0 && T + 1 <= TK_THREADS) got = chunk_select_regs<NV>(cp, lo, T + 1, sh);
+  }
+  if (got < 0) got = len > 0 ? select_row<true>(cp, len, lo, T + 1, cache, use_cache != 0, sh) : 0;
   uint64_t* dst = lists + (row * (size_t)nchunks + c) * (size_t)Tp;
   for (int e = threadIdx.x; e < Tp; e += TK_THREADS) dst[e] = (e < got && e < T) ? sh.buf[e] : 0ull;
   if (threadIdx.x == 0) thr[row * (size_t)nchunks + c] = got > T ? sh.buf[T] : 0ull;
@@ -812,8 +941,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rank_lists_kernel(
 }
 
 static bool topk_two_stage(long long rows, long long N_cap, int k, long long* chunk, int* nchunks) {
-  const long long ch = 16LL * k;
+  long long ch = 16LL * k;
   if (rows >= 512 || N_cap < 2 * ch) return false;
+  // shorter chunks, down to 4 elements per thread, until a row has 16: more
+  // workgroups for short rows and shorter lists to merge (depends on the row
+  // length and k only, so a workspace sized for some rows serves fewer)
+  while (ch / 2 >= 4LL * TK_THREADS && (N_cap + ch - 1) / ch < 16) ch /= 2;
   *chunk = ch;
   *nchunks = (int)((N_cap + ch - 1) / ch);
   return true;
@@ -858,9 +991,13 @@ int launch_topk(const TopkArgs& a, hipStream_t st) {
     const bool c1 = chunk <= TK_CACHE32;
     const size_t l1 = c1 ? ((size_t)chunk * 4 + 15) / 16 * 16 : 0;
     const size_t l2 = (size_t)nchunks * Tp * sizeof(uint64_t) + (size_t)Tp * sizeof(int);
-    if (!set_lds((const void*)topk_chunk_sorted_kernel, l1) || !set_lds((const void*)topk_rank_lists_kernel, l2))
-      return -1;
-    hipLaunchKernelGGL(topk_chunk_sorted_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l1, st,
+    const long long per = 4LL * TK_THREADS;   // elements per register vector over the workgroup
+    auto kfn = chunk == per ? topk_chunk_sorted_kernel<1>
+             : chunk == 2 * per ? topk_chunk_sorted_kernel<2>
+             : chunk == 4 * per ? topk_chunk_sorted_kernel<4>
+             : chunk == 8 * per ? topk_chunk_sorted_kernel<8> : topk_chunk_sorted_kernel<0>;
+    if (!set_lds((const void*)kfn, l1) || !set_lds((const void*)topk_rank_lists_kernel, l2)) return -1;
+    hipLaunchKernelGGL(kfn, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l1, st,
                        a.I, a.q_pos, a.N_cap, a.m, T, Tp, chunk, nchunks, (int)c1, lists, thr);
     hipLaunchKernelGGL(topk_rank_lists_kernel, dim3((unsigned)nchunks, (unsigned)rows), dim3(TK_THREADS), l2, st,
                        lists, thr, a.I, a.q_pos, a.N_cap, a.m, a.k, nchunks, T, Tp, a.idx, a.val);

@@ -17,7 +17,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (csa_compress, csa_compress_batch, csa_index_score, csa_mqa_workspace_size,
+from . import (csa_compress, csa_compress_batch, csa_compress_workspace_size, csa_index_score,
+               csa_mqa_workspace_size,
                csa_sparse_mqa, csa_topk, csa_topk_workspace_size, hca_dense_mqa)
 
 _TD = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -226,17 +227,23 @@ class HCADecode(_Common):
         self.q_pos = torch.full((B, 1), i, dtype=torch.int32, device=self.dev)
         self.out = torch.empty_like(self.q)
         self.ws_mqa = _ws(csa_mqa_workspace_size(B, 1, wl.n_h, d, N + wl.n_win), self.dev)
+        # the compressor's channel-split workspace (pooled rows between its two kernels)
+        self.ws_compress = _ws(csa_compress_workspace_size(self._compress_jobs()), self.dev)
 
-    def compress_new(self):
-        """The new token's window row and the just-completed block's entry, one launch."""
+    def _compress_jobs(self):
         wl, i, N = self.wl, self.i, self.wl.N_cap
-        csa_compress_batch([
+        return [
             self._win_job(i, i + 1, self.win_new, i),
             (self.C, self.Z, None, None, self.E,
              dict(T=wl.m * N, m=wl.m, overlap=0, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
                   gamma=self.gamma_kv, eps=wl.eps, rope_dim=wl.rope_dim, rope_base=wl.rope_base,
                   E_scale=self.E_scale)),
-        ])
+        ]
+
+    def compress_new(self):
+        """The new token's window row and the just-completed block's entry, one
+        launch (the entry's 512 channels pooled by 8 workgroups)."""
+        csa_compress_batch(self._compress_jobs(), workspace=self.ws_compress)
 
     def attend(self):
         wl = self.wl

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 4
+    assert lib.csa_abi_version() == 5
     for s in range(7):
         assert lib.csa_status_str(s)
     assert lib.csa_status_str(99) == b"unknown status"
@@ -90,9 +90,9 @@ def test_compress_batch_validation(lib):
         arr = (csa._CompressJob * max(len(jobs), 1))()
         for q, kw in enumerate(jobs):
             arr[q] = csa._CompressJob(**dict(good, **kw))
-        return lib.csa_compress_batch(arr, len(jobs) if n is None else n, None)
+        return lib.csa_compress_batch(arr, len(jobs) if n is None else n, None, 0, None)
 
-    assert lib.csa_compress_batch(None, 1, None) == CSA_E_NULL
+    assert lib.csa_compress_batch(None, 1, None, 0, None) == CSA_E_NULL
     assert batch({}, n=0) == CSA_E_SHAPE
     assert batch(*([{}] * 9)) == CSA_E_SHAPE                  # at most CSA_COMPRESS_MAX_JOBS
     assert batch({}, {"m": 0}) == CSA_E_SHAPE
@@ -103,6 +103,35 @@ def test_compress_batch_validation(lib):
     # only empty ranges: valid, nothing launched
     assert batch({"s_begin": 1, "s_end": 1}, {"s_begin": 0, "s_end": 0}) == CSA_OK
     assert lib.csa_last_error() == b""
+
+
+def test_compress_batch_workspace(lib):
+    """The channel-split path's workspace: HCA-like entries (128 candidates, 512
+    channels) in a small launch take 8 slices each; slice sums (a 256-byte
+    aligned region), then rows.  Too small a workspace is refused before any
+    launch; jobs of few candidates or many entries need none."""
+    import long_context_attention_02_amd as csa
+    hca = dict(C_a=FAKE, Z_a=FAKE, C_b=None, Z_b=None, in_dtype=1, B=4, R=128, in_batch_stride=128 * 512,
+               tok_base=8191 * 128, T=8192 * 128, c=512, m=128, overlap=0, s_begin=8191, s_end=8192, gamma=None,
+               eps=1e-6, rope_dim=64, rope_base=1e4, pos_stride=128, pos_offset=0, E=FAKE, out_dtype=1,
+               E_scale=None, out_batch_stride=8192 * 512, out_ring=0)
+    win = dict(hca, m=1, s_begin=0, s_end=1, R=1, in_batch_stride=512, tok_base=0, T=1, pos_stride=1)
+
+    def arr(*jobs):
+        a = (csa._CompressJob * len(jobs))()
+        for q, kw in enumerate(jobs):
+            a[q] = csa._CompressJob(**kw)
+        return a
+
+    slots = 4
+    need = 256 + slots * 512 * 4            # 4 x 8 slice sums, 4 rows of 512 floats
+    assert lib.csa_compress_workspace_size(arr(win, hca), 2) == need
+    assert lib.csa_compress_workspace_size(arr(win), 1) == 0                       # one candidate
+    many = dict(hca, s_begin=8000, tok_base=8000 * 128, R=192 * 128, in_batch_stride=192 * 128 * 512)
+    assert lib.csa_compress_workspace_size(arr(dict(many, B=1)), 1) > 0              # 192 items
+    assert lib.csa_compress_workspace_size(arr(many), 1) == 0                        # 4 x 192 > 256 items
+    assert lib.csa_compress_workspace_size(arr(dict(hca, m=0)), 1) == 0            # invalid: counts nothing
+    assert lib.csa_compress_batch(arr(win, hca), 2, FAKE, need - 1, None) == CSA_E_WORKSPACE
 
 
 def test_index_score_validation(lib):

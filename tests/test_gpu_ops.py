@@ -199,6 +199,92 @@ def test_compress_batch_matches_separate_calls(csa):
         assert row_rel_err(to_f64(bat["Hc"][b]), refh) <= TOL_BF16
 
 
+SPLIT_CASES = [
+    # name, B, T, R, tok_base, c, m, overlap, s_begin, s_end, in, out
+    ("hca_tail_recompress_1M", 4, 1048576, 128, 1048448, 512, 128, 0, 8191, 8192, "bf16", "bf16"),
+    ("hca_blocks_partial_tail", 2, 300, 300, 0, 256, 128, 0, 0, 3, "bf16", "bf16"),
+    ("overlapping_m64_f32_in", 3, 520, 520, 0, 128, 64, 1, 0, 9, "f32", "f32"),
+    ("hca_mixed_rows_out", 3, 384, 384, 0, 512, 128, 0, 0, 3, "bf16", "mixed"),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_compress_channel_split(csa, case):
+    """With a workspace, entries of 64 or more candidates in a small launch pool
+    their channels in 64-channel slices over several workgroups, and a second
+    kernel normalises and stores the rows.  The rows match the oracle, on two
+    calls in a row (the second on other inputs, with another job in the same
+    launch ahead of the split one), the workspace starting as garbage."""
+    name, B, T, R, tok_base, c, m, ov, s0, s1, idt, odt = case
+    g = Gen(190 + SPLIT_CASES.index(case), DEV)
+    n_rows = s1
+    gamma = _gamma(g, 5, c)
+    rope = 64 if c >= 256 else 16
+    mixed = odt == "mixed"
+
+    def inputs(seed):
+        Ca = g.normal(seed, (B, R, c), idt)
+        Za = g.normal(seed + 1, (B, R, c), idt)
+        Cb = g.normal(seed + 2, (B, R, c), idt) if ov else None
+        Zb = g.normal(seed + 3, (B, R, c), idt) if ov else None
+        return Ca, Za, Cb, Zb
+
+    def out():
+        if mixed:
+            return (torch.zeros((B, n_rows, c + rope), dtype=torch.uint8, device=DEV),
+                    torch.zeros((B, n_rows), dtype=torch.float32, device=DEV))
+        return torch.full((B, n_rows, c), float("nan"), dtype=TDT[odt], device=DEV), None
+
+    def job(x, E, S):
+        return (*x, E, dict(T=T, m=m, overlap=ov, s_begin=s0, s_end=s1, tok_base=tok_base, gamma=gamma,
+                            eps=1e-6, rope_dim=rope, E_scale=S))
+
+    # a window-row job (one candidate) ahead of the split job in the second launch
+    Wr = g.normal(20, (B, 8, c), idt)
+    Wout = torch.full((B, 8, c), float("nan"), dtype=TDT["f32" if idt == "f32" else "bf16"], device=DEV)
+    wjob = (Wr, None, None, None, Wout, dict(T=8, m=1, overlap=0, s_begin=0, s_end=8, gamma=gamma, rope_dim=rope))
+    x1, x2 = inputs(1), inputs(11)
+    E1, S1 = out()
+    E2, S2 = out()
+    need = csa.csa_compress_workspace_size([job(x1, E1, S1)])
+    assert need > 0, "the split path applies"
+    assert csa.csa_compress_workspace_size([wjob, job(x2, E2, S2)]) == need
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=DEV)
+    csa.csa_compress_batch([job(x1, E1, S1)], workspace=ws)
+    csa.csa_compress_batch([wjob, job(x2, E2, S2)], workspace=ws)
+    torch.cuda.synchronize()
+    gam = to_f64(gamma)
+    for x, E, S in ((x1, E1, S1), (x2, E2, S2)):
+        for b in range(B):
+            ref = O.compress(*(None if t is None else to_f64(t[b]) for t in x), m=m, overlap=ov, T=T,
+                             tok_base=tok_base, s_begin=s0, s_end=s1, gamma=gam, eps=1e-6, rope_dim=rope)
+            if mixed:
+                # the e4m3 codes under the row scale, then the bf16 rotated dims
+                codes = E[b, s0:s1, :c - rope].contiguous().view(torch.float8_e4m3fn).double()
+                got = torch.cat([codes * S[b, s0:s1, None].double(),
+                                 E[b, s0:s1, c - rope:].contiguous().view(torch.bfloat16).double()], dim=1)
+                err = row_rel_err(got.cpu().numpy(), ref)
+                assert err <= 0.045, (name, b, err)   # e4m3: half a step of 32 at codes up to 448
+            else:
+                tol = TOL_F32 if odt == "f32" else TOL_BF16
+                err = row_rel_err(to_f64(E[b, s0:s1]), ref)
+                assert err <= tol, (name, b, err)
+    refw = O.compress(to_f64(Wr[0]), None, None, None, m=1, overlap=0, T=8, gamma=gam, eps=1e-6, rope_dim=rope)
+    assert row_rel_err(to_f64(Wout[0]), refw) <= (TOL_F32 if idt == "f32" else TOL_BF16)
+
+
+def test_compress_split_rejects_small_workspace(csa):
+    g = Gen(199, DEV)
+    C, Z = g.normal(1, (2, 128, 512), "bf16"), g.normal(2, (2, 128, 512), "bf16")
+    E = torch.zeros((2, 1, 512), dtype=torch.bfloat16, device=DEV)
+    jobs = [(C, Z, None, None, E, dict(T=128, m=128, overlap=0, s_begin=0, s_end=1))]
+    need = csa.csa_compress_workspace_size(jobs)
+    assert need > 0
+    with pytest.raises(csa.CsaError) as ei:
+        csa.csa_compress_batch(jobs, workspace=torch.zeros(need - 16, dtype=torch.uint8, device=DEV))
+    assert ei.value.status == 5
+
+
 # ---------------------------------------------------------------------------
 # a2 indexer score
 # ---------------------------------------------------------------------------
