@@ -350,12 +350,6 @@ template <int V>
 __device__ __forceinline__ void collect_groups(const uint32_t (&h)[tk_cg<V>()][V], const uint32_t (&l)[tk_cg<V>()][V],
                                                const bool (&take)[tk_cg<V>()][V], TopkShared& sh) {
   constexpr int CG = tk_cg<V>();
-  bool any = false;
-#pragma unroll
-  for (int c = 0; c < CG; ++c)
-#pragma unroll
-    for (int v = 0; v < V; ++v) any = any || take[c][v];
-  if (__ballot(any) == 0ull) return;   // wave-uniform: most waves take nothing near the end of a select
   uint64_t bal[CG][V];
   int tot = 0;
 #pragma unroll
