@@ -888,16 +888,44 @@ __global__ __launch_bounds__(TK_THREADS) void topk_rank_lists_kernel(
     above = wave_reduce_u32(above, OpAdd{});
     if (tid == 0) s_exact = (tl == 0ull || want == 0 || (int)above >= want) ? 1 : 0;
   }
-  // places: (element, other list) pairs spread over the threads
+  // places: thread (e = tid mod Tp, group tid / Tp) counts the keys above key e
+  // of this list in lists group, group + G, ... (G = TK_THREADS / Tp groups; Tp
+  // is a power of two), two fixed-step searches at a time, and adds the count
+  // to the key's place once
   const uint64_t* mine = A + (size_t)own * Tp;
-  const int others = nchunks - 1;
-  for (int q = tid; q < T * others; q += TK_THREADS) {
-    const int e = q / others, li = q - e * others;
-    const int l = li + (li >= own ? 1 : 0);
-    const uint64_t x = mine[e];
+  if (Tp <= TK_THREADS) {
+    const int G = TK_THREADS / Tp;
+    const int e = tid & (Tp - 1), grp = tid / Tp;
+    const uint64_t x = e < T ? mine[e] : 0ull;
     if (x != 0ull) {
-      const int c = count_above<false>(A + (size_t)l * Tp, Tp, x);
-      if (c) atomicAdd(&place[e], c);
+      int cnt = 0;
+      for (int l0 = grp; l0 < nchunks; l0 += 2 * G) {
+        const int l1 = l0 + G;
+        const uint64_t* p0 = A + (size_t)l0 * Tp;
+        const uint64_t* p1 = A + (size_t)min(l1, nchunks - 1) * Tp;
+        int c0 = 0, c1 = 0;
+        for (int st = Tp >> 1; st > 0; st >>= 1) {
+          const uint64_t v0 = p0[c0 + st - 1], v1 = p1[c1 + st - 1];
+          c0 += v0 > x ? st : 0;
+          c1 += v1 > x ? st : 0;
+        }
+        c0 += p0[c0] > x ? 1 : 0;
+        c1 += p1[c1] > x ? 1 : 0;
+        cnt += (l0 != own ? c0 : 0) + (l1 < nchunks && l1 != own ? c1 : 0);
+      }
+      if (cnt) atomicAdd(&place[e], cnt);
+    }
+  } else {
+    // (element, other list) pairs spread over the threads
+    const int others = nchunks - 1;
+    for (int q = tid; q < T * others; q += TK_THREADS) {
+      const int e = q / others, li = q - e * others;
+      const int l = li + (li >= own ? 1 : 0);
+      const uint64_t x = mine[e];
+      if (x != 0ull) {
+        const int c = count_above<false>(A + (size_t)l * Tp, Tp, x);
+        if (c) atomicAdd(&place[e], c);
+      }
     }
   }
   __syncthreads();
