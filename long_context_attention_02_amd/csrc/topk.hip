@@ -144,6 +144,19 @@ __device__ __forceinline__ uint32_t block_lower_bound(uint32_t lmax, int want, T
   return (total >= want && total > 0) ? t : 0u;
 }
 
+// inclusive sum of v over lanes 0 .. lane: DPP row shifts inside each 16-lane row
+// (lanes without a source add 0), then the totals of the rows below
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(v, 15), t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
+}
+
 // wave 0 finds the digit where the count from the top reaches `need` in hist
 // (bins in descending order); writes sh.digit / cum / cnt_d.  Lane l holds the
 // 16 bins just below TK_BINS - 16 l in registers.
@@ -496,7 +509,7 @@ __device__ __forceinline__ void sort_desc_rank(TopkShared& sh, int cnt, int P, i
   const int i = tid / S, part = tid - i * S;
   const uint64_t x = i < cnt ? sh.buf[i] : 0ull;
   int above = 0;
-  for (int j0 = part; j0 < cnt; j0 += 8 * S) {
+  for (int j0 = part; i < cnt && j0 < cnt; j0 += 8 * S) {
     uint64_t y[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) y[u] = sh.buf[j0 + u * S];   // eight reads in flight
@@ -549,36 +562,29 @@ __device__ __forceinline__ int chunk_select_regs(const float* __restrict__ p, lo
   find_digit(sh.hist[1], need, sh);
   __syncthreads();
   const uint32_t b = (d1 << 22) | ((uint32_t)sh.digit << 12);
-  // collect every element at or above b: one atomic per wave for its range of slots
-  bool any = false;
+  // collect every element at or above b: a thread's count, its place among the
+  // wave's by an inclusive scan, one atomic per wave for the wave's range of slots
+  int mine = 0;
 #pragma unroll
   for (int u = 0; u < NV; ++u)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) any = any || h[u][q] >= b;
-  if (__ballot(any) != 0ull) {   // wave-uniform
-    uint64_t bal[NV][4];
-    int tot = 0;
-#pragma unroll
-    for (int u = 0; u < NV; ++u)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bal[u][q] = __ballot(h[u][q] >= b);
-        tot += __popcll(bal[u][q]);
-      }
+    for (int q = 0; q < 4; ++q) mine += h[u][q] >= b ? 1 : 0;
+  const int incl = wave_incl_scan(mine);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  if (wtot > 0) {   // wave-uniform
     int off = 0;
-    if ((tid & 63) == 0) off = atomicAdd(&sh.count, tot);
-    off = __builtin_amdgcn_readfirstlane(off);
+    if ((tid & 63) == 0) off = atomicAdd(&sh.count, wtot);
+    off = __builtin_amdgcn_readfirstlane(off) + incl - mine;
 #pragma unroll
     for (int u = 0; u < NV; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int slot = off + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u][q] >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u][q], 0u));
-        if (h[u][q] >= b && slot < TK_KMAX)
-          sh.buf[slot] = ((uint64_t)h[u][q] << 32) |
-                         (0xFFFFFFFFu - (uint32_t)(base + 4 * tid + 4 * TK_THREADS * u + q));
-        off += __popcll(bal[u][q]);
-      }
+      for (int q = 0; q < 4; ++q)
+        if (h[u][q] >= b) {
+          if (off < TK_KMAX)
+            sh.buf[off] = ((uint64_t)h[u][q] << 32) |
+                          (0xFFFFFFFFu - (uint32_t)(base + 4 * tid + 4 * TK_THREADS * u + q));
+          ++off;
+        }
   }
   __syncthreads();
   const int cnt = sh.count;
