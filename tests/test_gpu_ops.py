@@ -273,6 +273,32 @@ def test_compress_channel_split(csa, case):
     assert row_rel_err(to_f64(Wout[0]), refw) <= (TOL_F32 if idt == "f32" else TOL_BF16)
 
 
+def test_compress_channel_split_ragged_T_len(csa):
+    """The split path with per-sequence token counts: entries a sequence does not
+    have are left untouched by both kernels, the others match the oracle."""
+    B, R, c, m = 3, 700, 256, 128
+    T_len = [700, 513, 128]
+    g = Gen(198, DEV)
+    Ca, Za = g.normal(1, (B, R, c), "bf16"), g.normal(2, (B, R, c), "bf16")
+    gamma = _gamma(g, 5, c)
+    n = O.num_entries(max(T_len), m)
+    E = torch.full((B, n, c), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Tl = torch.tensor(T_len, dtype=torch.int32, device=DEV)
+    jobs = [(Ca, Za, None, None, E, dict(T=max(T_len), T_len=Tl, m=m, overlap=0, s_begin=0, s_end=n,
+                                          gamma=gamma, rope_dim=64))]
+    need = csa.csa_compress_workspace_size(jobs)
+    assert need > 0
+    csa.csa_compress_batch(jobs, workspace=torch.full((need,), 0x5A, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    got = to_f64(E)
+    for b in range(B):
+        nb = O.num_entries(T_len[b], m)
+        assert np.isnan(got[b, nb:]).all(), b
+        ref = O.compress(to_f64(Ca[b]), to_f64(Za[b]), None, None, m=m, overlap=0, T=T_len[b], s_begin=0,
+                         s_end=nb, gamma=to_f64(gamma), eps=1e-6, rope_dim=64)
+        assert row_rel_err(got[b, :nb], ref) <= TOL_BF16, b
+
+
 def test_compress_split_rejects_small_workspace(csa):
     g = Gen(199, DEV)
     C, Z = g.normal(1, (2, 128, 512), "bf16"), g.normal(2, (2, 128, 512), "bf16")
@@ -361,6 +387,11 @@ TOPK_CASES = [
     # rows whose top scores crowd one chunk: the two-stage selection falls back to the row
     ("two_stage_clustered_fallback", 3, 1, 70000, 4, 1024, "clustered", "all"),
     ("two_stage_k512_clustered", 3, 1, 16384, 4, 512, "clustered", "all"),
+    # chunks of 8,192 (two register vectors a thread), of 32,768 (eight), and of a
+    # length that is no multiple of 4,096 (the radix select on every chunk)
+    ("two_stage_k512_chunks_8k", 2, 1, 262144, 4, 512, "normal", "all"),
+    ("two_stage_k2048_chunks_32k", 2, 1, 1048576, 4, 2048, "normal", "partial"),
+    ("two_stage_k1000_chunks_16000", 2, 1, 200000, 4, 1000, "normal", "partial"),
 ]
 
 
