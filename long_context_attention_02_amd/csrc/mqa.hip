@@ -1298,35 +1298,46 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     // exceeds it by MQ_REF_SLACK, so O is rarely rescaled
     float alpha[HTW];
     bool moved = false;
+    // FULL: every slot of the chunk exists (the common case), so no score is
+    // masked and every score is finite: the per-score mask and -inf tests drop out
+    auto softmax = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll
-    for (int ht = 0; ht < HTW; ++ht) {
-      float cm = -INFINITY;
+      for (int ht = 0; ht < HTW; ++ht) {
+        float cm = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (vmask >> (16 * kt + 4 * g + r)) & 1u;
-          S[kt][ht][r] = ok ? S[kt][ht][r] * sc[ht] : -INFINITY;
-          cm = fmaxf(cm, S[kt][ht][r]);
-        }
-      cm = quad_max(cm);
-      const float nr = (cm > ref[ht] + MQ_REF_SLACK) ? cm : ref[ht];
-      alpha[ht] = (nr == ref[ht]) ? 1.f : (ref[ht] == -INFINITY ? 0.f : __expf(ref[ht] - nr));
-      // while the reference is -inf every P so far was 0 and O is still 0
-      moved |= nr != ref[ht] && ref[ht] != -INFINITY;
-      float ps = 0.f;
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (FULL) {
+              S[kt][ht][r] *= sc[ht];
+            } else {
+              const bool ok = (vmask >> (16 * kt + 4 * g + r)) & 1u;
+              S[kt][ht][r] = ok ? S[kt][ht][r] * sc[ht] : -INFINITY;
+            }
+            cm = fmaxf(cm, S[kt][ht][r]);
+          }
+        cm = quad_max(cm);
+        const float nr = (cm > ref[ht] + MQ_REF_SLACK) ? cm : ref[ht];
+        alpha[ht] = (nr == ref[ht]) ? 1.f : (ref[ht] == -INFINITY ? 0.f : __expf(ref[ht] - nr));
+        // while the reference is -inf every P so far was 0 and O is still 0
+        moved |= nr != ref[ht] && ref[ht] != -INFINITY;
+        float ps = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = (S[kt][ht][r] == -INFINITY) ? 0.f : __expf(S[kt][ht][r] - nr);
-          S[kt][ht][r] = e;
-          ps += e;
-        }
-      // this lane's share of the head's sum; the four shares add up after the loop
-      lsum[ht] = lsum[ht] * alpha[ht] + ps;
-      ref[ht] = nr;
-    }
+          for (int r = 0; r < 4; ++r) {
+            const float e = (!FULL && S[kt][ht][r] == -INFINITY) ? 0.f : __expf(S[kt][ht][r] - nr);
+            S[kt][ht][r] = e;
+            ps += e;
+          }
+        // this lane's share of the head's sum; the four shares add up after the loop
+        lsum[ht] = lsum[ht] * alpha[ht] + ps;
+        ref[ht] = nr;
+      }
+    };
+    if (vmask == 0xFFFFFFFFu) softmax(std::true_type{});
+    else softmax(std::false_type{});
     if (__any(moved)) {
       // Rare (a chunk maximum passed the reference by MQ_REF_SLACK).  O is scaled
       // through this wave's LDS scratch, eight tiles at a time, so that on the
