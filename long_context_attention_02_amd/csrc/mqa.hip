@@ -1651,9 +1651,15 @@ static bool mqa_decode_ok(int Tq, int n_h, int d) {
 // slots per workgroup and splits per query; depends on the shape only, never on B
 static void mqa_split(int Tq, int n_h, int d, long long slots_max, int* kps, int* n_split) {
   if (mqa_decode_ok(Tq, n_h, d)) {
-    if (Tq < MQ_SPLIT_BELOW_TQ)
-      *kps = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_LONG;
-    else
+    if (Tq < MQ_SPLIT_BELOW_TQ) {
+      // as many ranges as ranges of the nominal length take, each as long as a
+      // balanced share rounded up to whole chunks (640 slots: 4 of 160, not
+      // 3 of 192 and one of 64)
+      const long long nom = slots_max <= MQ_DEC_SMALL_UPTO ? MQ_DEC_SPLIT_SMALL : MQ_DEC_SPLIT_LONG;
+      const long long nsp = max(1LL, (slots_max + nom - 1) / nom);
+      const long long share = (slots_max + nsp - 1) / nsp;
+      *kps = (int)max((long long)MQ_CH, (share + MQ_CH - 1) / MQ_CH * MQ_CH);
+    } else
       *kps = (int)min((long long)MQ_DEC_TABLE, max(1LL, (slots_max + MQ_CH - 1) / MQ_CH) * MQ_CH);
     *n_split = (int)max(1LL, (slots_max + *kps - 1) / *kps);
   } else if (Tq >= MQ_SPLIT_BELOW_TQ || slots_max <= MQ_SPLIT_KEYS) {
