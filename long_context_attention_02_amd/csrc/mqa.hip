@@ -1035,31 +1035,17 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
   const unsigned row32 = unit / (unsigned)n_split;
   const size_t row = row32;
   const int b = (int)(row32 / (unsigned)Tq);
-  const long long i = q_pos[row];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
   const int h0 = HG * hg + 16 * HTW * wave;   // first head of this wave
+  const long long s0 = (long long)sp * kps;   // the range's first slot
 
-  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
-  DecRows R;
-  R.s0 = (long long)sp * kps;
-  R.n_rows = (int)max(0LL, min((long long)kps, qs.n_slots - R.s0));
-  R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
-  R.row_bytes = RAW_ROW;
-  R.E_b = (const uint16_t*)((const uint8_t*)E + (size_t)b * (size_t)N_cap * (size_t)R.row_bytes);
-  R.W_b = W ? (const uint16_t*)((const uint8_t*)W + (size_t)b * (size_t)W_cap * (size_t)R.row_bytes) : nullptr;
-  R.dummy = R.E_b;
-  R.Es_b = MIX ? Es + (size_t)b * (size_t)N_cap : nullptr;
-  R.Ws_b = (MIX && W) ? Ws + (size_t)b * (size_t)W_cap : nullptr;
-  R.W_cap = W_cap;
-  R.N_cap = (int)min(N_cap, 2147483647LL);
-  R.ring0 = W_cap > 0 ? (int)((qs.win_lo + max(0LL, R.s0 - qs.n_sel)) % W_cap) : 0;
-  const int nch = (R.n_rows + MQ_CH - 1) / MQ_CH;
-
-  // the range's selection, the query pieces and gamma are loaded and used
+  // The loads come first: the range's selection, the query pieces and gamma need
+  // only the grid position, so their latency runs under the work on the query
+  // position (its load, the slot counts, the RoPE table).  They are all used
   // before any chunk load is issued: a wait on an ordinary load issued before an
-  // LDS-DMA load becomes a wait on every load in flight
+  // LDS-DMA load becomes a wait on every load in flight.
   constexpr int IPT = (TBL + 64 * NW - 1) / (64 * NW);
   int iv[IPT];
   if (!DENSE) {
@@ -1067,11 +1053,11 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     // unguarded loads (index clamped into the row, masked after): a guarded
     // load compiles to a branch with its own wait
     const int* idx_row = idx + row * (size_t)k;
-    const int kcap = (int)max(0LL, min((long long)kps, (long long)k - R.s0));
+    const int kcap = (int)max(0LL, min((long long)kps, (long long)k - s0));
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
       const int t = threadIdx.x + 64 * NW * e;
-      const int v = idx_row[min(R.s0 + t, (long long)k - 1)];
+      const int v = idx_row[min(s0 + t, (long long)k - 1)];
       iv[e] = t < kcap ? v : -1;
     }
   }
@@ -1092,6 +1078,31 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
     const float gl = gsrc[min(t, D - 1)];
     gv[e] = gamma_q ? gl : 1.f;
   }
+
+  const long long i = q_pos[row];
+  const QuerySlots qs = query_slots<DENSE>(i, N_cap, k, m, n_win);
+  DecRows R;
+  R.s0 = s0;
+  R.n_rows = (int)max(0LL, min((long long)kps, qs.n_slots - R.s0));
+  R.n_sel = (int)max(0LL, min((long long)R.n_rows, qs.n_sel - R.s0));
+  R.row_bytes = RAW_ROW;
+  R.E_b = (const uint16_t*)((const uint8_t*)E + (size_t)b * (size_t)N_cap * (size_t)R.row_bytes);
+  R.W_b = W ? (const uint16_t*)((const uint8_t*)W + (size_t)b * (size_t)W_cap * (size_t)R.row_bytes) : nullptr;
+  R.dummy = R.E_b;
+  R.Es_b = MIX ? Es + (size_t)b * (size_t)N_cap : nullptr;
+  R.Ws_b = (MIX && W) ? Ws + (size_t)b * (size_t)W_cap : nullptr;
+  R.W_cap = W_cap;
+  R.N_cap = (int)min(N_cap, 2147483647LL);
+  R.ring0 = W_cap > 0 ? (int)((qs.win_lo + max(0LL, R.s0 - qs.n_sel)) % W_cap) : 0;
+  const int nch = (R.n_rows + MQ_CH - 1) / MQ_CH;
+  // the RoPE table needs the position alone, so it is built while the loads are in flight
+  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
+    const int u = t - (D - rope_dim) / 2;
+    float cs = 1.f, sn = 0.f;
+    if (u >= 0) rope_cos_sin(i, u, rope, &cs, &sn);
+    rope_cs[2 * t] = cs;
+    rope_cs[2 * t + 1] = sn;
+  }
   // slot table: thread t resolves slot t of the range once, for every wave
   // (straight-line code: no branch for the compiler to sink the selection
   // loads into, where each would get its own wait)
@@ -1106,13 +1117,6 @@ __global__ __launch_bounds__(64 * NW) void mqa_decode_kernel(
       if (t < TBL) sscale[t] = rs;
     const unsigned long long bal = __ballot(ok);
     if ((lane & 31) == 0 && (t >> 5) < NCH_MAX) smask[t >> 5] = (uint32_t)(bal >> (lane & 32));
-  }
-  for (int t = threadIdx.x; t < D / 2; t += 64 * NW) {
-    const int u = t - (D - rope_dim) / 2;
-    float cs = 1.f, sn = 0.f;
-    if (u >= 0) rope_cos_sin(i, u, rope, &cs, &sn);
-    rope_cs[2 * t] = cs;
-    rope_cs[2 * t + 1] = sn;
   }
 #pragma unroll
   for (int e = 0; e < GPT; ++e) {

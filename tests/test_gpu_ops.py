@@ -319,6 +319,9 @@ INDEX_CASES = [
     ("tiny_f32_prefill", 1, 256, 2, 32, 64, 4, "f32", "f32", "prefill0"),
     ("bf16_decode_h64_d128", 2, 1, 64, 128, 5000, 4, "bf16", "bf16", "all"),
     ("fp8_decode_h64_d128_masked", 3, 1, 64, 128, 7000, 4, "bf16", "e4m3", "partial"),
+    # 1,563 units of 64 keys over 128 waves per row: 27 waves take 13 units, the
+    # rest 12 (uneven shares, each wave's last flush window partly its own)
+    ("fp8_decode_b16_odd_unit_counts", 16, 1, 64, 128, 100032, 4, "bf16", "e4m3", "all"),
     ("bf16_decode_tq3_h32_d64", 2, 3, 32, 64, 3001, 4, "bf16", "bf16", "partial"),
     ("bf16_decode_h16_d32", 1, 2, 16, 32, 999, 1, "bf16", "bf16", "all"),
     ("bf16_prefill_h64_d128", 1, 45, 64, 128, 700, 4, "bf16", "bf16", "prefill"),
