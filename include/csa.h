@@ -35,7 +35,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 5
+#define CSA_ABI_VERSION 6
 
 /* Storage types. CSA_FP8_E4M3 is OCP FP8 E4M3FN (max 448, no infinities).
  * CSA_MXFP4 is OCP MXFP4: FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6
@@ -192,6 +192,38 @@ int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos,
                     int B, int Tq, int H_I, int d_I, long long N_cap, int m,
                     float* I_out, void* stream);
+
+/*
+ * a1 + a2 of a decode step in one launch (method page §3.3: the step's new
+ * compressed rows, then the indexer's scores over every visible entry).  The
+ * compressions of jobs[] (csa_compress_batch's descriptors: typically the new
+ * token's window row, the newest KV entry and the newest indexer key) run
+ * beside the scoring of csa_index_score with Tq = 1, instead of in a launch of
+ * their own in front of it.  Exactly one job writes the indexer's key rows
+ * (its E is K_I, with K_I's layout: out_batch_stride = N_cap * d_I, no ring,
+ * E_scale = K_scale for FP8 keys), and its entries lie in the last 64 rows of
+ * K_I; the indexer scores the other rows while the job runs, and the wave that
+ * wrote the key then scores those last 64 rows.  Other jobs must not write
+ * memory the indexer reads.
+ *  Arguments: as csa_compress_batch (jobs, n_jobs <= CSA_DECODE_FRONT_MAX_JOBS,
+ *  no workspace) and csa_index_score (Tq = 1: q_I [B][1][H_I][d_I], w_I,
+ *  q_pos [B][1], I_out [B][1][N_cap]).
+ *  Results: I_out equals csa_index_score's on the same key rows bit for bit.
+ *  The compressed rows come from the wave-per-entry compressor (one wave per
+ *  entry: all candidates of a lane in flight, wave reductions), whose results
+ *  agree with csa_compress_batch's to rounding (the RMSNorm sum and the
+ *  pooling are added in another order); they are deterministic.
+ *  Covered: BF16 queries; BF16 or FP8 keys with H_I in {16, 32, 64} and d_I
+ *  in {32, 64, 128}; N_cap a multiple of 64, at least 128; 16-byte aligned
+ *  q_I and K_I; jobs with BF16 inputs in 16-byte pieces, at most 8 candidates
+ *  per entry (m <= 4 with overlap, m <= 8 without), c % 8 == 0, BF16 or FP8
+ *  output.  Anything else returns CSA_E_UNSUPPORTED with nothing launched, and
+ *  the caller makes the two separate calls.
+ */
+#define CSA_DECODE_FRONT_MAX_JOBS 4
+int csa_decode_front(const csa_compress_job* jobs, int n_jobs, const void* q_I, int q_dtype, const float* w_I,
+                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos, int B, int H_I,
+                     int d_I, long long N_cap, int m, float* I_out, void* stream);
 
 /*
  * a3 — per-query top-k (method page §3.3; k = 512 / 1024 in the report

@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "CsaError", "LIB_PATH", "abi_version", "csa_compress", "csa_compress_batch", "csa_compress_workspace_size",
-    "csa_index_score",
+    "CompressJobs", "compress_jobs",
+    "csa_index_score", "csa_decode_front", "CSA_E_UNSUPPORTED",
     "csa_topk",
     "csa_topk_workspace_size", "csa_sparse_mqa", "csa_sparse_mqa_noalloc", "hca_dense_mqa",
     "csa_mqa_workspace_size", "NOALLOC_SCRATCH_BYTES", "csa_out_proj_workspace_size",
@@ -28,6 +29,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 CSA_F32, CSA_BF16, CSA_FP8_E4M3, CSA_MXFP4, CSA_KV_MIXED = 0, 1, 2, 3, 4
+CSA_E_UNSUPPORTED = 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -66,6 +68,8 @@ _lib.csa_compress_workspace_size.restype = _S
 _lib.csa_compress_workspace_size.argtypes = [ctypes.POINTER(_CompressJob), _I]
 _lib.csa_index_score.restype = _I
 _lib.csa_index_score.argtypes = [_P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _I, _L, _I, _P, _P]
+_lib.csa_decode_front.restype = _I
+_lib.csa_decode_front.argtypes = [ctypes.c_void_p, _I, _P, _I, _P, _P, _I, _P, _P, _I, _I, _I, _L, _I, _P, _P]
 _lib.csa_topk_workspace_size.restype = _S
 _lib.csa_topk_workspace_size.argtypes = [_I, _I, _L, _I]
 _lib.csa_topk.restype = _I
@@ -179,11 +183,27 @@ def csa_compress(C_a, Z_a, C_b, Z_b, E, **kw):
     _check(_lib.csa_compress(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw), _stream()))
 
 
+class CompressJobs:
+    """Job descriptors marshalled once (compress_jobs), for calls repeated on the
+    same tensors: csa_compress_batch and csa_decode_front take it in place of
+    the list.  It keeps the tensors alive."""
+
+    def __init__(self, jobs):
+        self.jobs = list(jobs)
+        self.arr = (_CompressJob * max(len(self.jobs), 1))()
+        for q, (C_a, Z_a, C_b, Z_b, E, kw) in enumerate(self.jobs):
+            self.arr[q] = _CompressJob(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw))
+
+    def __len__(self):
+        return len(self.jobs)
+
+
+def compress_jobs(jobs) -> CompressJobs:
+    return jobs if isinstance(jobs, CompressJobs) else CompressJobs(jobs)
+
+
 def _compress_jobs(jobs):
-    arr = (_CompressJob * max(len(jobs), 1))()
-    for q, (C_a, Z_a, C_b, Z_b, E, kw) in enumerate(jobs):
-        arr[q] = _CompressJob(*_compress_args(C_a, Z_a, C_b, Z_b, E, **kw))
-    return arr
+    return compress_jobs(jobs).arr
 
 
 def csa_compress_workspace_size(jobs) -> int:
@@ -223,6 +243,31 @@ def csa_index_score(q_I, w_I, K_I, q_pos, I_out, *, m: int, K_scale=None):
         _dt(K_I), _ptr(K_scale, "K_scale", torch.uint8 if mx else torch.float32),
         _ptr(q_pos, "q_pos", torch.int32),
         B, Tq, H, dI, N, m, _ptr(I_out, "I_out", torch.float32), _stream()))
+
+
+def csa_decode_front(jobs, q_I, w_I, K_I, q_pos, I_out, *, m: int, K_scale=None):
+    """a1 + a2 of a decode step in one launch: the compressions ``jobs`` (as in
+    csa_compress_batch; one of them writes K_I's last rows) beside the scores of
+    csa_index_score (one query row per sequence: q_I [B, 1, H, dI], w_I [B, 1, H],
+    q_pos [B, 1], I_out [B, 1, N]).  Raises CsaError with status
+    CSA_E_UNSUPPORTED, having launched nothing, when the combination is not
+    covered; the caller then makes the two separate calls."""
+    B, Tq, H, dI = q_I.shape
+    N = K_I.shape[1]
+    if Tq != 1 or tuple(w_I.shape) != (B, 1, H) or tuple(q_pos.shape) != (B, 1) or tuple(I_out.shape) != (B, 1, N):
+        raise ValueError("csa_decode_front: one query row per sequence (q_I [B, 1, H, dI], w_I [B, 1, H], "
+                         "q_pos [B, 1], I_out [B, 1, N])")
+    mx = K_I.dtype == torch.uint8
+    if K_I.dim() != 3 or K_I.shape[0] != B or K_I.shape[2] != (dI // 2 if mx else dI):
+        raise ValueError("K_I must be [B, N, dI] ([B, N, dI / 2] bytes for MXFP4)")
+    if K_scale is not None and tuple(K_scale.shape) != ((B, N, dI // 32) if mx else (B, N)):
+        raise ValueError("K_scale must be [B, N] ([B, N, dI / 32] bytes for MXFP4)")
+    arr = _compress_jobs(jobs)
+    _check(_lib.csa_decode_front(
+        ctypes.cast(arr, ctypes.c_void_p), len(jobs), _ptr(q_I, "q_I", dims=4), _dt(q_I),
+        _ptr(w_I, "w_I", torch.float32), _ptr(K_I, "K_I", dims=3), _dt(K_I),
+        _ptr(K_scale, "K_scale", torch.uint8 if mx else torch.float32), _ptr(q_pos, "q_pos", torch.int32),
+        B, H, dI, N, m, _ptr(I_out, "I_out", torch.float32), _stream()))
 
 
 def csa_topk_workspace_size(B: int, Tq: int, N: int, k: int) -> int:

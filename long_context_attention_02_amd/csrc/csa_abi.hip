@@ -181,33 +181,70 @@ size_t csa_compress_workspace_size(const csa_compress_job* jobs, int n_jobs) {
   return need;
 }
 
+}  // extern "C"
+
+// the checks of csa_index_score's arguments (fn names the caller in the error)
+static int check_index(const char* fn, const void* q_I, int q_dtype, const float* w_I, const void* K_I,
+                       int k_dtype, const float* K_scale, const int* q_pos, int B, int Tq, int H_I, int d_I,
+                       long long N_cap, int m, float* I_out) {
+  if (!q_I || !w_I || !K_I || !q_pos || !I_out)
+    return fail(CSA_E_NULL, "%s: q_I, w_I, K_I, q_pos and I_out are required", fn);
+  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16) return fail(CSA_E_DTYPE, "%s: q_dtype must be F32 or BF16", fn);
+  if (!dtype_valid(k_dtype)) return fail(CSA_E_DTYPE, "%s: unknown k_dtype", fn);
+  if (q_dtype == CSA_F32 && k_dtype != CSA_F32) return fail(CSA_E_DTYPE, "%s: F32 queries need F32 keys", fn);
+  if (q_dtype == CSA_BF16 && k_dtype == CSA_F32)
+    return fail(CSA_E_DTYPE, "%s: BF16 queries need BF16, FP8 or MXFP4 keys", fn);
+  if ((k_dtype == CSA_FP8_E4M3 || k_dtype == CSA_MXFP4) && !K_scale)
+    return fail(CSA_E_NULL, "%s: K_scale is required for FP8 and MXFP4 keys", fn);
+  if (k_dtype == CSA_MXFP4 && d_I % 32) return fail(CSA_E_SHAPE, "%s: MXFP4 keys need d_I %% 32 == 0", fn);
+  if (B < 1 || Tq < 1 || H_I < 1 || d_I < 1 || N_cap < 1 || m < 1)
+    return fail(CSA_E_SHAPE, "%s: sizes must be >= 1", fn);
+  if (H_I > 64 || d_I > 256 || H_I * (d_I + 1) > 16384)
+    return fail(CSA_E_UNSUPPORTED, "%s: H_I <= 64 and d_I <= 256 are supported", fn);
+  if (N_cap > 2147483647LL || (long long)B * Tq > 65535LL * 65535LL)
+    return fail(CSA_E_UNSUPPORTED, "%s: N_cap must fit int32", fn);
+  if (Tq > 65535 || B > 65535) return fail(CSA_E_UNSUPPORTED, "%s: B, Tq <= 65535", fn);
+  return CSA_OK;
+}
+
+extern "C" {
+
 int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos,
                     int B, int Tq, int H_I, int d_I, long long N_cap, int m,
                     float* I_out, void* stream) {
-  if (!q_I || !w_I || !K_I || !q_pos || !I_out)
-    return fail(CSA_E_NULL, "csa_index_score: q_I, w_I, K_I, q_pos and I_out are required");
-  if (q_dtype != CSA_F32 && q_dtype != CSA_BF16)
-    return fail(CSA_E_DTYPE, "csa_index_score: q_dtype must be F32 or BF16");
-  if (!dtype_valid(k_dtype)) return fail(CSA_E_DTYPE, "csa_index_score: unknown k_dtype");
-  if (q_dtype == CSA_F32 && k_dtype != CSA_F32)
-    return fail(CSA_E_DTYPE, "csa_index_score: F32 queries need F32 keys");
-  if (q_dtype == CSA_BF16 && k_dtype == CSA_F32)
-    return fail(CSA_E_DTYPE, "csa_index_score: BF16 queries need BF16, FP8 or MXFP4 keys");
-  if ((k_dtype == CSA_FP8_E4M3 || k_dtype == CSA_MXFP4) && !K_scale)
-    return fail(CSA_E_NULL, "csa_index_score: K_scale is required for FP8 and MXFP4 keys");
-  if (k_dtype == CSA_MXFP4 && d_I % 32)
-    return fail(CSA_E_SHAPE, "csa_index_score: MXFP4 keys need d_I %% 32 == 0");
-  if (B < 1 || Tq < 1 || H_I < 1 || d_I < 1 || N_cap < 1 || m < 1)
-    return fail(CSA_E_SHAPE, "csa_index_score: sizes must be >= 1");
-  if (H_I > 64 || d_I > 256 || H_I * (d_I + 1) > 16384)
-    return fail(CSA_E_UNSUPPORTED, "csa_index_score: H_I <= 64 and d_I <= 256 are supported");
-  if (N_cap > 2147483647LL || (long long)B * Tq > 65535LL * 65535LL)
-    return fail(CSA_E_UNSUPPORTED, "csa_index_score: N_cap must fit int32");
-  if (Tq > 65535 || B > 65535) return fail(CSA_E_UNSUPPORTED, "csa_index_score: B, Tq <= 65535");
+  const int st = check_index("csa_index_score", q_I, q_dtype, w_I, K_I, k_dtype, K_scale, q_pos, B, Tq, H_I, d_I,
+                             N_cap, m, I_out);
+  if (st != CSA_OK) return st;
   csa::IndexArgs a{q_I, q_dtype, w_I, K_I, k_dtype, K_scale, q_pos, B, Tq, H_I, d_I, N_cap, m, I_out};
   if (csa::launch_index_score(a, (hipStream_t)stream) != 0)
     return fail(CSA_E_HIP, "csa_index_score: kernel launch failed");
+  return ok();
+}
+
+int csa_decode_front(const csa_compress_job* jobs, int n_jobs, const void* q_I, int q_dtype, const float* w_I,
+                     const void* K_I, int k_dtype, const float* K_scale, const int* q_pos, int B, int H_I,
+                     int d_I, long long N_cap, int m, float* I_out, void* stream) {
+  if (!jobs) return fail(CSA_E_NULL, "csa_decode_front: jobs is NULL");
+  if (n_jobs < 1 || n_jobs > CSA_DECODE_FRONT_MAX_JOBS)
+    return fail(CSA_E_SHAPE, "csa_decode_front: n_jobs = %d outside [1, %d]", n_jobs, CSA_DECODE_FRONT_MAX_JOBS);
+  csa::CompressArgs a[CSA_DECODE_FRONT_MAX_JOBS];
+  for (int q = 0; q < n_jobs; ++q) {
+    char who[48];
+    snprintf(who, sizeof(who), "csa_decode_front: job %d", q);
+    const int st = check_compress(jobs[q], who);
+    if (st != CSA_OK) return st;
+    if (jobs[q].s_end <= jobs[q].s_begin) return fail(CSA_E_SHAPE, "%s: no entries", who);
+    a[q] = compress_args(jobs[q]);
+  }
+  const int st = check_index("csa_decode_front", q_I, q_dtype, w_I, K_I, k_dtype, K_scale, q_pos, B, 1, H_I, d_I,
+                             N_cap, m, I_out);
+  if (st != CSA_OK) return st;
+  csa::IndexArgs ia{q_I, q_dtype, w_I, K_I, k_dtype, K_scale, q_pos, B, 1, H_I, d_I, N_cap, m, I_out};
+  const char* why = nullptr;
+  if (csa::launch_decode_front(a, n_jobs, ia, (hipStream_t)stream, &why) != 0)
+    return fail(CSA_E_UNSUPPORTED, "csa_decode_front: %s", why ? why : "not covered");
+  if (hipGetLastError() != hipSuccess) return fail(CSA_E_HIP, "csa_decode_front: kernel launch failed");
   return ok();
 }
 

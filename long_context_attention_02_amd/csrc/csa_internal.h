@@ -48,6 +48,10 @@ struct IndexArgs {
 // true when the matrix-core kernels cover the shape
 bool index_mfma_supported(const IndexArgs& a);
 int launch_index_score(const IndexArgs& a, hipStream_t st);
+// compress jobs and the decode indexer in one launch (validated here: returns
+// -1 with *why set when the combination is not covered, 0 once launched)
+int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a, hipStream_t st,
+                        const char** why);
 
 struct TopkArgs {
   const float* I;

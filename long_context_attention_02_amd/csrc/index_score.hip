@@ -21,6 +21,9 @@
 // scaling the key inside the ReLU.  MXFP4 keys (OCP MX: FP4 E2M1 with an
 // E8M0 scale per 32 dims) run the QK products in FP4 on both sides, with the
 // block-scaled matrix instruction (index_mx4_decode).
+#include <algorithm>
+
+#include "compress_wave.h"
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -348,23 +351,27 @@ static_assert(IDX_STAGE % (16 * IDX_UNIT) == 0, "stage holds whole units");
 // in units of IDX_UNIT subtiles (wave w takes units w, w + W, w + 2W, ...), so
 // at any moment the device reads a few narrow moving windows of the key array
 // rather than one far-apart stream per wave.
+//
+// One wave's share of query row (b, t): units wid, wid + W, ... below nunits,
+// over key rows 0 .. n_keys - 1 (rows of N_cap, the row stride of K and of
+// the scores; n_keys <= N_cap).
 template <int QH, int KS, int KDT>
-__global__ __launch_bounds__(256) void index_mfma_decode(
+__device__ __forceinline__ void index_decode_wave(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ K,
-    const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
-    float* __restrict__ out, int flush_ok) {
+    const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, long long n_keys,
+    int m, float* __restrict__ out, int flush_ok, int b, int t, long long wid, long long W,
+    long long nunits) {
   constexpr int H = 16 * QH, DI = 32 * KS;
-  constexpr int PF = 4;   // subtiles in flight per wave
+  // subtiles in flight per wave (a ring of 8 measured no faster: the loop is
+  // not short of loads in flight)
+  constexpr int PF = 4;
+  static_assert(PF % 4 == 0, "whole groups of four slots");
   constexpr int U = IDX_UNIT;
   // the wave index through readfirstlane: the compiler then knows everything
   // derived from it is wave-uniform (scalar registers, uniform branches)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int b = blockIdx.z, t = blockIdx.y;
   const size_t qrow = (size_t)b * Tq + t;
-  const long long W = 4LL * gridDim.x;                  // waves of this query row
-  const long long wid = 4LL * blockIdx.x + wave;
-  const long long nunits = (N_cap + 16 * U - 1) / (16 * U);
   if (wid >= nunits) return;
   const int nls = (int)((nunits - 1 - wid) / W + 1) * U;   // subtiles of this wave
   // (at least one: stated so that the ring's first loads are not sunk into a
@@ -381,7 +388,7 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
   load_query_frags_dec<QH, KS, KDT>(f, q + qrow * (size_t)(H * DI), w + qrow * H, g, j);
   const size_t kbase = (size_t)b * (size_t)N_cap;
   float* orow = out + qrow * (size_t)N_cap;
-  const int klast = (int)(N_cap - 1);   // absent keys load this row (their scores are never stored)
+  const int klast = (int)(n_keys - 1);   // absent keys load this row (their scores are never stored)
   const uint8_t* Kb = (const uint8_t*)K + kbase * SubGeom<KS, KDT>::RB;
 
   // Scores are staged in LDS (slot 16 ls + j for key j of local subtile ls)
@@ -403,9 +410,8 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
     }
   }
 
-  // The key ring holds PF = 4 subtiles in flight (slot u of a group of four);
-  // a slot is consumed (moved through the LDS tile), then refilled with the
-  // subtile one group later.
+  // The key ring holds PF subtiles in flight; a slot is consumed (moved
+  // through the LDS tile), then refilled with the subtile PF later.
   RawSub<KS, KDT> ring[PF];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
@@ -427,49 +433,59 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
   }
   __shared__ __attribute__((aligned(16))) uint8_t tile[4][SubGeom<KS, KDT>::SB];
   int flushed = 0;   // subtiles already written out
+  // two groups of four slots per pass, so every slot index is a constant
 #pragma unroll 1
-  for (int st0 = 0; st0 < nls; st0 += 4) {
-    float P[4];
+  for (int st0 = 0; st0 < nls; st0 += PF) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      static_assert(PF == 4, "slot u of each group");
-      RawSub<KS, KDT> T;
-      lds_transpose<KS, KDT>(T, ring[u], tile[wave], lane, g, j);
-      const int nx = st0 + u + PF;
-      load_lin<KS, KDT>(ring[u], Kb, nx < nls ? key0(nx) : klast, klast, lane);
-      P[u] = partial_column_raw<QH, KS, KDT>(f, T);
-      // the sum is materialised here, so the epilogue is not sunk below the
-      // later subtiles (which would keep 64 accumulators live instead of 16)
-      asm volatile("" : "+v"(P[u]));
-      // keep the next slot's conversions out of this one (they would wait on its load)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // (the scale fetch is older than every key load waited for above, and the
-    // memory counter retires loads in order, so the scales are in LDS by now)
-    const float v = reduce_scatter4(P, g);
-    const int ls = st0 + g;
-    if (ls < nls) {
-      const int e = 16 * ls + j;
-      float r = v;
-      if constexpr (KDT == DT_FP8) r *= stage[wave][e];
-      stage[wave][e] = key0(ls) + j < nvis ? r : -INFINITY;
-    }
-    // Every IDX_FLUSH subtiles, write the window out: spreading the stores
-    // over the loop keeps them off the wave's tail.  flush_ok (set by the
-    // launcher) says every output row is 16-byte aligned and every unit lies
-    // inside the sequence, so a window of the wave's subtiles holds only keys
-    // that exist.  (A test in terms other than nls and such a flag here makes
-    // the compiler lose its count of the loads in flight and wait for all.)
-    if constexpr (IDX_FLUSH > 0) {
-      if ((st0 + 4) % IDX_FLUSH == 0 && st0 + 4 <= nls && flush_ok) {
-        const int e0 = 16 * (st0 + 4 - IDX_FLUSH) + 4 * lane;
+    for (int half = 0; half < PF / 4; ++half) {
+      // first subtile of this group of four.  A group past the wave's last
+      // subtile still runs (its slots hold row klast, and nothing of it is
+      // staged or stored): an early exit here would make the compiler merge
+      // two orders of the ring's loads at the loop head and wait for most of
+      // the ring at every slot.
+      const int gs = st0 + 4 * half;
+      float P[4];
 #pragma unroll
-        for (int c = 0; c < IDX_FLUSH / 16; ++c) {
-          const int e = e0 + 256 * c;
-          __builtin_nontemporal_store(*(const f32x4_t*)&stage[wave][e],
-                                      (f32x4_t*)(orow + key0(e >> 4) + (e & 15)));
+      for (int u = 0; u < 4; ++u) {
+        const int slot = 4 * half + u;
+        RawSub<KS, KDT> T;
+        lds_transpose<KS, KDT>(T, ring[slot], tile[wave], lane, g, j);
+        const int nx = gs + u + PF;
+        load_lin<KS, KDT>(ring[slot], Kb, nx < nls ? key0(nx) : klast, klast, lane);
+        P[u] = partial_column_raw<QH, KS, KDT>(f, T);
+        // the sum is materialised here, so the epilogue is not sunk below the
+        // later subtiles (which would keep 64 accumulators live instead of 16)
+        asm volatile("" : "+v"(P[u]));
+        // keep the next slot's conversions out of this one (they would wait on its load)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // (the scale fetch is older than every key load waited for above, and the
+      // memory counter retires loads in order, so the scales are in LDS by now)
+      const float v = reduce_scatter4(P, g);
+      const int ls = gs + g;
+      if (ls < nls) {
+        const int e = 16 * ls + j;
+        float r = v;
+        if constexpr (KDT == DT_FP8) r *= stage[wave][e];
+        stage[wave][e] = key0(ls) + j < nvis ? r : -INFINITY;
+      }
+      // Every IDX_FLUSH subtiles, write the window out: spreading the stores
+      // over the loop keeps them off the wave's tail.  flush_ok (set by the
+      // launcher) says every output row is 16-byte aligned and every unit lies
+      // inside the sequence, so a window of the wave's subtiles holds only keys
+      // that exist.  (A test in terms other than nls and such a flag here makes
+      // the compiler lose its count of the loads in flight and wait for all.)
+      if constexpr (IDX_FLUSH > 0) {
+        if ((gs + 4) % IDX_FLUSH == 0 && gs + 4 <= nls && flush_ok) {
+          const int e0 = 16 * (gs + 4 - IDX_FLUSH) + 4 * lane;
+#pragma unroll
+          for (int c = 0; c < IDX_FLUSH / 16; ++c) {
+            const int e = e0 + 256 * c;
+            __builtin_nontemporal_store(*(const f32x4_t*)&stage[wave][e],
+                                        (f32x4_t*)(orow + key0(e >> 4) + (e & 15)));
+          }
+          flushed = gs + 4;
         }
-        flushed = st0 + 4;
       }
     }
   }
@@ -486,6 +502,129 @@ __global__ __launch_bounds__(256) void index_mfma_decode(
         if (key + c <= klast) orow[key + c] = v[c];
     }
   }
+}
+
+template <int QH, int KS, int KDT>
+__global__ __launch_bounds__(256) void index_mfma_decode(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const void* __restrict__ K,
+    const float* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
+    float* __restrict__ out, int flush_ok) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  index_decode_wave<QH, KS, KDT>(q, w, K, Ks, q_pos, Tq, N_cap, N_cap, m, out, flush_ok, blockIdx.z, blockIdx.y,
+                                 4LL * blockIdx.x + wave, 4LL * gridDim.x,
+                                 (N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT));
+}
+
+// ---------------------------------------------------------------------------
+// The front of a decode step in one launch: the step's compressions (the new
+// token's window row, the newest KV entry, the newest indexer key) run as one
+// extra workgroup per sequence beside the indexer, instead of as a launch of
+// their own in front of it.  The indexer workgroups score every unit of 64
+// keys but the last; the wave that writes the new key then scores that last
+// unit with the same code, so every score equals the one the indexer alone
+// computes from the same key rows.  Each job of the extra workgroup runs on
+// one wave, with the wave-per-entry compressor's arithmetic.  One query row
+// per sequence.
+// ---------------------------------------------------------------------------
+// The scores of one unit (four subtiles of 16 keys from key0, a multiple of
+// 64) of decode row b (one query row per sequence), by one wave, with the
+// per-key arithmetic of index_decode_wave (the same subtile products,
+// reduce-scatter over the unit's four subtiles, scale and mask): used on the
+// unit whose key rows the same launch writes.  The operands are loaded
+// straight into their lane layout, without the LDS tile: a second LDS object
+// in the launch hides from the compiler that the indexer's tile and its
+// score-stage DMA do not overlap, and its loop then waits for every load in
+// flight.
+template <int QH, int KS, int KDT>
+__device__ __forceinline__ void index_score_unit(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                                 const void* __restrict__ K, const float* __restrict__ Ks,
+                                                 const int* __restrict__ q_pos, long long N_cap, int m,
+                                                 float* __restrict__ out, int b, long long key0) {
+  constexpr int H = 16 * QH, DI = 32 * KS;
+  const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
+  IdxFrags<QH, KS> f;
+  load_query_frags_dec<QH, KS, KDT>(f, q + (size_t)b * (H * DI), w + (size_t)b * H, g, j);
+  const uint8_t* Kb = (const uint8_t*)K + (size_t)b * (size_t)N_cap * SubGeom<KS, KDT>::RB;
+  using G = SubGeom<KS, KDT>;
+  float P[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    // lane (g, j) loads what lds_transpose hands it: row j, 16-byte pieces
+    // g + 4 c (or the 8 bytes at 8 g when its share is 8 bytes)
+    RawSub<KS, KDT> T;
+    const uint8_t* row = Kb + (size_t)(key0 + 16 * u + j) * G::RB;
+    if constexpr (G::LB >= 16) {
+#pragma unroll
+      for (int c = 0; c < G::LB / 16; ++c) {
+        const u32x4_t v = *(const u32x4_t*)(row + 16 * (g + 4 * c));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) T.w[4 * c + e] = v[e];
+      }
+    } else {
+      const u32x2_t v = *(const u32x2_t*)(row + 8 * g);
+      T.w[0] = v[0];
+      T.w[1] = v[1];
+    }
+    P[u] = partial_column_raw<QH, KS, KDT>(f, T);
+  }
+  float v = reduce_scatter4(P, g);   // key key0 + 16 g + j
+  const long long key = key0 + 16 * g + j;
+  if constexpr (KDT == DT_FP8) v *= Ks[(size_t)b * (size_t)N_cap + (size_t)key];
+  const long long nvis = min(N_cap, ((long long)q_pos[b] + 1) / m);
+  out[(size_t)b * (size_t)N_cap + (size_t)key] = key < nvis ? v : -INFINITY;
+}
+
+static constexpr int FRONT_MAX_JOBS = 4;   // one wave each
+struct FrontJobs {
+  CompressJob job[FRONT_MAX_JOBS];
+  int n_jobs, key_job;   // key_job: the job that writes the indexer's key rows
+};
+
+template <int QH, int KS, int KDT>
+__global__ __launch_bounds__(256) void index_decode_front(
+    const FrontJobs fj, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const void* __restrict__ K, const float* __restrict__ Ks, const int* __restrict__ q_pos,
+    long long N_cap, int m, float* __restrict__ out, int flush_ok, int gx, int B) {
+  // the jobs are read where they lie, in the kernel-argument segment (fj is
+  // the first argument, at offset 0): indexing the by-value record with the
+  // wave index would make the compiler copy all of it to scratch memory
+  (void)fj;
+  const FrontJobs& F = *(const FrontJobs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long nunits = N_cap / (16 * IDX_UNIT);   // (host: N_cap % 64 == 0)
+  // a 1-D grid: gx indexer workgroups per sequence, then one front workgroup
+  // per sequence at the end, so the indexer's workgroups spread over the
+  // compute units as they do alone (two per unit at the 1M decode) and the
+  // light front workgroups take the slots left over
+  const int nidx = gx * B;
+  if ((int)blockIdx.x < nidx) {
+    // the indexer over every unit but the last; its rows past the scored ones
+    // are never read, so no load meets the key row being written
+    const int b = (int)blockIdx.x / gx, x = (int)blockIdx.x - b * gx;
+    index_decode_wave<QH, KS, KDT>(q, w, K, Ks, q_pos, 1, N_cap, N_cap - 16 * IDX_UNIT, m, out, flush_ok, b, 0,
+                                   4LL * x + wave, 4LL * gx, nunits - 1);
+    return;
+  }
+  const int b = (int)blockIdx.x - nidx;
+  if (wave < F.n_jobs) {
+    const CompressJob& J = F.job[wave];
+    for (long long e = 0; e < J.n_entries; ++e) {
+      const long long s = J.s_begin + e;
+      if (J.out_dtype == DT_FP8) compress_entry_wave<DT_BF16, DT_FP8, COMPW_MAXC>(J, s, b, lane);
+      else compress_entry_wave<DT_BF16, DT_BF16, COMPW_MAXC>(J, s, b, lane);
+    }
+  }
+  if (wave != F.key_job) return;
+  // the key rows and scales written above are complete before the unit's loads
+  // (the wave's own stores, read back through the same compute unit)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // (the key rows through the key job's own pointers, equal to K and Ks: a load
+  // through K after the stores above makes the compiler wait for every load in
+  // flight at the head of the indexer's loop)
+  index_score_unit<QH, KS, KDT>(q, w, F.job[F.key_job].E, F.job[F.key_job].E_scale, q_pos, N_cap, m, out, b,
+                                16 * IDX_UNIT * (nunits - 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -546,8 +685,21 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
   const uint8_t* Sb = Ks + (size_t)b * (size_t)N_cap * SB;
   float* orow = out + qrow * (size_t)N_cap;
 
-  // the key ring, issued first: subtile p's codes (lane (g, j): bytes 16 g of
-  // key j) and the key's scale dword (byte g is this lane's block)
+  // the query rows and head weights first (head 16 mt + j, dims 32 g ..
+  // 32 g + 31), then the key ring: subtile p's codes (lane (g, j): bytes 16 g
+  // of key j) and the key's scale dword (byte g is this lane's block).  The
+  // memory counter retires loads in order, so waiting for the query leaves
+  // the ring in flight.
+  u32x4_t raw[QH][4];
+  float wv[QH][4];
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+    const uint16_t* qp = q + (qrow * H + 16 * mt + j) * (size_t)DI + 32 * g;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[mt][c] = *(const u32x4_t*)(qp + 8 * c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = w[qrow * H + 16 * mt + 4 * g + r];
+  }
   u32x4_t rc[PF];
   uint32_t rs[PF];
   auto load_sub = [&](int first, u32x4_t& c, uint32_t& sc) {
@@ -561,24 +713,19 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // query: head 16 mt + j, dims 32 g .. 32 g + 31, quantised to MXFP4
+  // the query quantised to MXFP4
   u32x4_t qa[QH];
   int qsc[QH];
-  float wv[QH][4];
 #pragma unroll
   for (int mt = 0; mt < QH; ++mt) {
-    const uint16_t* qp = q + (qrow * H + 16 * mt + j) * (size_t)DI + 32 * g;
-    u32x4_t raw[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) raw[c] = *(const u32x4_t*)(qp + 8 * c);
     float x[32];
     float a = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        x[8 * c + 2 * e] = __uint_as_float(raw[c][e] << 16);
-        x[8 * c + 2 * e + 1] = __uint_as_float(raw[c][e] & 0xffff0000u);
+        x[8 * c + 2 * e] = __uint_as_float(raw[mt][c][e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(raw[mt][c][e] & 0xffff0000u);
         a = fmaxf(a, fmaxf(fabsf(x[8 * c + 2 * e]), fabsf(x[8 * c + 2 * e + 1])));
       }
     const int se = mx4_shared_exp(a);
@@ -590,9 +737,14 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
       qa[mt][d] = pk;
     }
     qsc[mt] = se + 127;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wv[mt][r] = w[qrow * H + 16 * mt + 4 * g + r];
   }
+  // Retire the weight loads here (an empty register-only rewrite): their first
+  // use inside the loop would otherwise carry a wait for them, and that wait,
+  // counted in every pass, would drain the ring each time.
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) asm("" : "+v"(wv[mt][r]));
 
   __shared__ __attribute__((aligned(16))) float stage[4][IDX_STAGE];
   int flushed = 0;
@@ -600,17 +752,23 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
   for (int st0 = 0; st0 < nls; st0 += 8) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int gs = st0 + 4 * half;   // first subtile of this group of four
-      if (gs >= nls) break;            // (wave-uniform)
+      // first subtile of this group of four.  A group past the wave's last
+      // subtile still runs (its slots hold row klast, and nothing of it is
+      // staged or stored): an early exit here would make the compiler merge
+      // two orders of the ring's loads at the loop head and wait for most of
+      // the ring at every slot.
+      const int gs = st0 + 4 * half;
       float P[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int slot = 4 * half + u;
-        const u32x4_t c = rc[slot];
         const int sc = (int)((rs[slot] >> (8 * g)) & 0xffu);
         const int nx = gs + u + PF;
+        P[u] = mx4_partial<QH>(qa, qsc, wv, rc[slot], sc);
+        // the refill after the products that read the slot: loading first
+        // made the compiler load into a temporary and copy it into the slot
+        // at the loop's end, a copy that waits for nearly the whole ring
         load_sub(nx < nls ? key0(nx) : klast, rc[slot], rs[slot]);
-        P[u] = mx4_partial<QH>(qa, qsc, wv, c, sc);
         asm volatile("" : "+v"(P[u]));
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -873,6 +1031,75 @@ static bool index_mx4_supported(const IndexArgs& a) {
   return a.k_dtype == DT_MX4 && a.q_dtype == DT_BF16 && a.dI == 128 && a.Tq < PF_MIN_TQ &&
          (a.H == 16 || a.H == 32 || a.H == 64) && (((uintptr_t)a.K) & 15u) == 0 &&
          (((uintptr_t)a.K_scale) & 3u) == 0 && (((uintptr_t)a.q) & 15u) == 0;
+}
+
+// the decode front: compress jobs beside the indexer (index_decode_front)
+template <int QH, int KS, int KDT>
+static void launch_front(const FrontJobs& fj, const IndexArgs& a, hipStream_t st) {
+  auto kfn = index_decode_front<QH, KS, KDT>;
+  // the indexer part's grid: the decode grid over every unit but the last
+  const long long waves = resident_waves((const void*)kfn, 256);
+  const long long nunits = a.N_cap / (16 * IDX_UNIT) - 1;
+  long long wpr = 1;
+  while (2 * wpr <= waves / a.B) wpr *= 2;
+  wpr = std::max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
+  wpr = std::min(wpr, nunits);
+  const int gx = (int)((wpr + 3) / 4);
+  const int flush_ok = (((uintptr_t)a.out) & 15u) == 0;   // (N_cap % 64 == 0: checked)
+  hipLaunchKernelGGL(kfn, dim3((unsigned)((gx + 1) * a.B)), dim3(256), 0, st, fj, (const uint16_t*)a.q, a.w, a.K,
+                     a.K_scale, a.q_pos, a.N_cap, a.m, a.out, flush_ok, gx, a.B);
+}
+template <int QH, int KS>
+static void launch_front_k(const FrontJobs& fj, const IndexArgs& a, hipStream_t st) {
+  if (a.k_dtype == DT_FP8) launch_front<QH, KS, DT_FP8>(fj, a, st);
+  else launch_front<QH, KS, DT_BF16>(fj, a, st);
+}
+template <int QH>
+static void launch_front_ks(const FrontJobs& fj, const IndexArgs& a, hipStream_t st) {
+  if (a.dI == 32) launch_front_k<QH, 1>(fj, a, st);
+  else if (a.dI == 64) launch_front_k<QH, 2>(fj, a, st);
+  else launch_front_k<QH, 4>(fj, a, st);
+}
+
+int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a, hipStream_t st,
+                        const char** why) {
+  *why = nullptr;
+  auto no = [&](const char* w) {
+    *why = w;
+    return -1;
+  };
+  if (!index_mfma_supported(a)) return no("the indexer shape has no matrix-core kernel");
+  if (a.Tq != 1) return no("one query row per sequence");
+  if (a.N_cap % (16 * IDX_UNIT) != 0 || a.N_cap < 2 * 16 * IDX_UNIT)
+    return no("N_cap must be a multiple of 64, at least 128");
+  if ((((uintptr_t)a.q) & 15u) != 0 || (((uintptr_t)a.K) & 15u) != 0)
+    return no("q_I and K_I must be 16-byte aligned");
+  if (n_jobs < 1 || n_jobs > FRONT_MAX_JOBS) return no("1 to 4 compress jobs");
+  FrontJobs fj{};
+  fj.n_jobs = n_jobs;
+  fj.key_job = -1;
+  for (int q = 0; q < n_jobs; ++q) {
+    const CompressArgs& x = jobs[q];
+    if (x.in_dtype != DT_BF16 || (x.out_dtype != DT_BF16 && x.out_dtype != DT_FP8) || !compress_wave_ok(x))
+      return no("a compress job the wave-per-entry compressor does not cover (bf16 inputs in 16-byte pieces, "
+                "at most 8 candidates, bf16 or fp8 output)");
+    if (x.B != a.B) return no("every compress job has the indexer's batch");
+    if (x.E == a.K) {
+      if (fj.key_job >= 0) return no("one compress job writes the key rows");
+      if (x.out_dtype != a.k_dtype || x.c != a.dI || x.out_ring != 0 || x.out_bs != a.N_cap * (long long)a.dI ||
+          (a.k_dtype == DT_FP8 && x.E_scale != a.K_scale))
+        return no("the key job must write K_I's rows (and K_scale) in the indexer's layout");
+      if (x.s_begin < a.N_cap - 16 * IDX_UNIT || x.s_end > a.N_cap)
+        return no("the key job's entries must lie in the last 64 rows of K_I");
+      fj.key_job = q;
+    }
+    fj.job[q] = make_compress_job(x, 1);
+  }
+  if (fj.key_job < 0) return no("no compress job writes K_I");
+  if (a.H == 16) launch_front_ks<1>(fj, a, st);
+  else if (a.H == 32) launch_front_ks<2>(fj, a, st);
+  else launch_front_ks<4>(fj, a, st);
+  return 0;
 }
 
 int launch_index_score(const IndexArgs& a, hipStream_t st) {

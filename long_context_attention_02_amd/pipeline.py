@@ -17,9 +17,10 @@ from __future__ import annotations
 
 import torch
 
-from . import (csa_compress, csa_compress_batch, csa_compress_workspace_size, csa_index_score,
-               csa_mqa_workspace_size,
-               csa_sparse_mqa, csa_topk, csa_topk_workspace_size, hca_dense_mqa)
+from . import (CSA_E_UNSUPPORTED, CsaError, compress_jobs, csa_compress, csa_compress_batch,
+               csa_compress_workspace_size,
+               csa_decode_front, csa_index_score, csa_mqa_workspace_size, csa_sparse_mqa, csa_topk,
+               csa_topk_workspace_size, hca_dense_mqa)
 
 _TD = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -134,14 +135,22 @@ class CSADecode(_Common):
         self.out = torch.empty_like(self.q)
         self.ws_topk = _ws(csa_topk_workspace_size(B, 1, N, wl.k), self.dev)
         self.ws_mqa = _ws(csa_mqa_workspace_size(B, 1, wl.n_h, d, wl.k + wl.n_win), self.dev)
+        self.fused_front = None   # decided by the first front()
+        self._jobs = None
 
     # -- the step ------------------------------------------------------------
-    def compress_new(self):
-        """The new token's window row, the newest KV entry and its indexer key:
-        three independent compressions, one launch."""
+    def _new_row_jobs(self):
+        """The step's three compressions: the new token's window row, the newest
+        KV entry and its indexer key (entry N - 1, the block just completed),
+        marshalled once."""
+        if self._jobs is None:
+            self._jobs = compress_jobs(self._new_row_job_list())
+        return self._jobs
+
+    def _new_row_job_list(self):
         wl, i, N = self.wl, self.i, self.wl.N_cap
         T_done = wl.m * N
-        csa_compress_batch([
+        return [
             self._win_job(i, i + 1, self.win_new, i),
             (self.Ca, self.Za, self.Cb, self.Zb, self.E,
              dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
@@ -150,7 +159,28 @@ class CSADecode(_Common):
             (self.ICa, self.IZa, self.ICb, self.IZb, self.KI,
              dict(T=T_done, m=wl.m, overlap=1, s_begin=N - 1, s_end=N, tok_base=self.blk_tok_base,
                   E_scale=self.KI_scale)),
-        ])
+        ]
+
+    def compress_new(self):
+        """The three compressions in one launch of their own."""
+        csa_compress_batch(self._new_row_jobs())
+
+    def front(self):
+        """Compressions and indexer scores: one launch (csa_decode_front) where
+        the library covers the combination (fp8 or bf16 keys, bf16 rows),
+        otherwise the two launches.  ``fused_front`` records which ran."""
+        if self.fused_front is not False:
+            try:
+                csa_decode_front(self._new_row_jobs(), self.qI, self.wI, self.KI, self.q_pos, self.I,
+                                 m=self.wl.m, K_scale=self.KI_scale)
+                self.fused_front = True
+                return
+            except CsaError as e:
+                if e.status != CSA_E_UNSUPPORTED:
+                    raise
+                self.fused_front = False
+        self.compress_new()
+        self.index()
 
     def index(self):
         csa_index_score(self.qI, self.wI, self.KI, self.q_pos, self.I, m=self.wl.m, K_scale=self.KI_scale)
@@ -165,13 +195,8 @@ class CSADecode(_Common):
                        rope_base=wl.rope_base, scale=wl.scale, workspace=self.ws_mqa,
                        E_scale=self.E_scale, W_scale=self.W_scale)
 
-    def step(self, index_events=None):
-        self.compress_new()
-        if index_events is not None:
-            index_events[0].record()
-        self.index()
-        if index_events is not None:
-            index_events[1].record()
+    def step(self):
+        self.front()
         self.select()
         self.attend()
 

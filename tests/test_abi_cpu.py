@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.csa_abi_version() == 5
+    assert lib.csa_abi_version() == 6
     for s in range(7):
         assert lib.csa_status_str(s)
     assert lib.csa_status_str(99) == b"unknown status"
@@ -154,6 +154,53 @@ def test_index_score_validation(lib):
     assert call(N=0) == CSA_E_SHAPE
     assert call(H=65) == CSA_E_UNSUPPORTED
     assert call(dI=512) == CSA_E_UNSUPPORTED
+
+
+def test_decode_front_validation(lib):
+    """csa_decode_front checks its jobs and the indexer's arguments as the two
+    separate calls do, then refuses (CSA_E_UNSUPPORTED, nothing launched) what
+    the one-launch path does not cover."""
+    import long_context_attention_02_amd as csa
+    B, H, dI, N = 2, 64, 128, 4096
+    KEYS, SCALES = FAKE + 4096, FAKE + 8192
+    win = dict(C_a=FAKE, Z_a=None, C_b=None, Z_b=None, in_dtype=1, B=B, R=1, in_batch_stride=512, tok_base=4 * N,
+               T=4 * N + 1, c=512, m=1, overlap=0, s_begin=4 * N, s_end=4 * N + 1, gamma=FAKE, eps=1e-6,
+               rope_dim=64, rope_base=1e4, pos_stride=1, pos_offset=0, E=FAKE + 65536, out_dtype=1,
+               E_scale=None, out_batch_stride=128 * 512, out_ring=128)
+    key = dict(C_a=FAKE, Z_a=FAKE, C_b=FAKE, Z_b=FAKE, in_dtype=1, B=B, R=8, in_batch_stride=8 * dI,
+               tok_base=4 * (N - 2), T=4 * N, c=dI, m=4, overlap=1, s_begin=N - 1, s_end=N, gamma=None,
+               eps=1e-6, rope_dim=0, rope_base=1e4, pos_stride=4, pos_offset=0, E=KEYS, out_dtype=2,
+               E_scale=SCALES, out_batch_stride=N * dI, out_ring=0)
+
+    def call(jobs=(win, key), n=None, N_=N, kd=2, Ks=SCALES, K=KEYS, H_=H, q=FAKE):
+        arr = (csa._CompressJob * max(len(jobs), 1))()
+        for i, kw in enumerate(jobs):
+            arr[i] = csa._CompressJob(**kw)
+        return lib.csa_decode_front(ctypes.cast(arr, ctypes.c_void_p), len(jobs) if n is None else n, q, 1, FAKE,
+                                    K, kd, Ks, FAKE, B, H_, dI, N_, 4, FAKE, None)
+
+    assert lib.csa_decode_front(None, 1, FAKE, 1, FAKE, KEYS, 2, SCALES, FAKE, B, H, dI, N, 4, FAKE,
+                                None) == CSA_E_NULL
+    assert call(n=0) == CSA_E_SHAPE
+    assert call(jobs=[win] * 5) == CSA_E_SHAPE                                  # at most 4 jobs
+    assert call(jobs=(win, dict(key, m=0))) == CSA_E_SHAPE
+    assert b"job 1" in lib.csa_last_error()
+    assert call(jobs=(win, dict(key, s_end=N - 1))) == CSA_E_SHAPE              # a job with no entries
+    assert call(q=None) == CSA_E_NULL
+    assert call(Ks=None) == CSA_E_NULL                                           # fp8 keys need K_scale
+    assert call(H_=65) == CSA_E_UNSUPPORTED
+    # not covered by the one-launch path
+    assert call(N_=N + 32) == CSA_E_UNSUPPORTED                                 # N_cap % 64
+    assert call(jobs=(win,)) == CSA_E_UNSUPPORTED and b"K_I" in lib.csa_last_error()
+    early = dict(key, tok_base=4 * (N - 101), T=4 * (N - 99), s_begin=N - 100, s_end=N - 99)
+    assert call(jobs=(win, early)) == CSA_E_UNSUPPORTED                           # not the last 64 rows
+    assert call(jobs=(win, dict(key, out_dtype=1, E_scale=None))) == CSA_E_UNSUPPORTED   # key format != k_dtype
+    nine = dict(win, m=9, R=9, in_batch_stride=9 * 512, tok_base=0, T=9, s_begin=0, s_end=1, pos_stride=9)
+    assert call(jobs=(nine, key)) == CSA_E_UNSUPPORTED                            # 9 candidates per entry
+    assert call(jobs=(dict(win, in_dtype=0, in_batch_stride=512), key)) == CSA_E_UNSUPPORTED   # f32 inputs
+    assert call(jobs=(win, key, key)) == CSA_E_UNSUPPORTED                       # two jobs write the keys
+    assert call(K=KEYS + 8, jobs=(win, dict(key, E=KEYS + 8))) == CSA_E_UNSUPPORTED   # 16-byte alignment
+    assert call(kd=3) == CSA_E_UNSUPPORTED                                       # MXFP4 keys
 
 
 def test_topk_validation_and_workspace(lib):
