@@ -242,7 +242,7 @@ def csa_decode_bytes(wl) -> dict:
     # row), the newest KV entry and indexer key (2m candidates of C and Z
     # each); the three rows written
     new_in = B * 2 * (d + 4 * wl.m * d + 4 * wl.m * dI)
-    new_out = B * (2 * kv_row_bytes(wl) + int(dI * esz[wl.k_dtype]) + (4 if wl.k_dtype == "e4m3" else 0))
+    new_out = B * (2 * kv_row_bytes(wl) + int(dI * esz[wl.k_dtype]) + {"e4m3": 4, "mxfp4": dI // 32}.get(wl.k_dtype, 0))
     compress = new_in + new_out
     step = keys + scales + gather + window + q + out + q_index + idx + compress
     return {"step": step, "index_kernel": keys + scales + q_index, "front_kernel": keys + scales + q_index + compress,
@@ -616,10 +616,12 @@ def main():
         result["csa_decode_mxfp4"] = {
             "workload": mx["workload"], "replicas": mx["replicas"], "graph": mx["graph"],
             "ms_per_step": round(mms, 5), "tokens/s": round(wl.B / (mms * 1e-3), 1),
-            "step_ms_with_events": mx["step_ms_with_events"], "index_ms": mx["index_ms"],
-            "algorithmic_bytes": mab,
-            "roofline": _roof(mab["index_kernel"] / (mx_idx_ms * 1e-3) / 1e9, "hbm",
-                              kernel="index_mx4_decode (csa_index_score, MXFP4 keys)"),
+            "step_ms_with_events": mx["step_ms_with_events"], "fused_front": mx["fused_front"],
+            "index_ms": mx["index_ms"], "algorithmic_bytes": mab,
+            "roofline": _roof(mab["front_kernel" if mx["fused_front"] else "index_kernel"] / (mx_idx_ms * 1e-3) / 1e9,
+                              "hbm", kernel=("index_mx4_front (csa_decode_front, MXFP4 keys: the step's "
+                                             "compressions beside the indexer)") if mx["fused_front"]
+                              else "index_mx4_decode (csa_index_score, MXFP4 keys)"),
             "step_roofline": _roof(mab["step"] / (mms * 1e-3) / 1e9, "hbm", scope="whole step"),
             "recall_at_k_vs_fp8_selection": {"mean": round(sum(recall) / len(recall), 5),
                                              "min": round(min(recall), 5), "k": wl.k,
@@ -633,7 +635,8 @@ def main():
         result["csa_decode_flash"] = {
             "workload": fl["workload"], "replicas": fl["replicas"], "graph": fl["graph"],
             "ms_per_step": round(fms, 5), "tokens/s": round(CSA_DECODE_FLASH.B / (fms * 1e-3), 1),
-            "step_ms_with_events": fl["step_ms_with_events"], "index_ms": fl["index_ms"],
+            "step_ms_with_events": fl["step_ms_with_events"], "fused_front": fl["fused_front"],
+            "index_ms": fl["index_ms"],
             "algorithmic_bytes": fl["bytes"]["step"],
             "roofline": _roof(fl["bytes"]["step"] / (fms * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["hca_decode"] = hca_decode(K, args.warmup, use_graph)

@@ -214,11 +214,13 @@ int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
  *  agree with csa_compress_batch's to rounding (the RMSNorm sum and the
  *  pooling are added in another order); they are deterministic.
  *  Covered: BF16 queries; BF16 or FP8 keys with H_I in {16, 32, 64} and d_I
- *  in {32, 64, 128}; N_cap a multiple of 64, at least 128; 16-byte aligned
- *  q_I and K_I; jobs with BF16 inputs in 16-byte pieces, at most 8 candidates
- *  per entry (m <= 4 with overlap, m <= 8 without), c % 8 == 0, BF16 or FP8
- *  output.  Anything else returns CSA_E_UNSUPPORTED with nothing launched, and
- *  the caller makes the two separate calls.
+ *  in {32, 64, 128}, or MXFP4 keys with H_I in {16, 32, 64} and d_I = 128
+ *  (K_scale the E8M0 bytes, 4-byte aligned); N_cap a multiple of 64, at least
+ *  128; 16-byte aligned q_I and K_I; jobs with BF16 inputs in 16-byte pieces,
+ *  at most 8 candidates per entry (m <= 4 with overlap, m <= 8 without),
+ *  c % 8 == 0, BF16 output or the key format (FP8 beside FP8 keys, MXFP4 beside
+ *  MXFP4 keys).  Anything else returns CSA_E_UNSUPPORTED with nothing launched,
+ *  and the caller makes the two separate calls.
  */
 #define CSA_DECODE_FRONT_MAX_JOBS 4
 int csa_decode_front(const csa_compress_job* jobs, int n_jobs, const void* q_I, int q_dtype, const float* w_I,

@@ -218,6 +218,28 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
     } else if constexpr (ODT == DT_FP8) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) ((uint8_t*)J.E)[o + e] = f32_to_e4m3(pooled[pi][e] / scale);
+    } else if constexpr (ODT == DT_MX4) {
+      // MXFP4 (OCP MX: E2M1 codes, one E8M0 scale per 32 channels): a block is
+      // the 8-channel pieces of four consecutive lanes (c % 32 == 0, VEC = 8);
+      // the block maximum by exchange within the four, the codes packed two per
+      // byte (low nibble first), the block's first lane writes its scale byte.
+      // Used by the decode front only (the wave kernel's other variants
+      // would carry its registers).
+      static_assert(VEC == 8, "MXFP4 output from bf16 pieces");
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) a = fmaxf(a, fabsf(pooled[pi][e]));
+      a = fmaxf(a, __shfl_xor(a, 1, 64));
+      a = fmaxf(a, __shfl_xor(a, 2, 64));
+      const int se = mx4_shared_exp(a);
+      uint32_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) pk |= f32_to_e2m1(ldexpf(pooled[pi][e], -se)) << (4 * e);
+      *(uint32_t*)((uint8_t*)J.E + o / 2) = pk;
+      const int piece = lane + 64 * pi;
+      if ((piece & 3) == 0)
+        ((uint8_t*)J.E_scale)[((size_t)b * (size_t)(J.out_bs / c) + (size_t)orow) * (size_t)(c / 32) + piece / 4] =
+            (uint8_t)(se + 127);
     } else {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) store_from_f32<ODT>(J.E, o + e, pooled[pi][e]);
@@ -227,7 +249,8 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
 
 // the job record of one compression (host): G token groups (wide kernel)
 CompressJob make_compress_job(const CompressArgs& x, int G);
-// true when the wave-per-entry arithmetic covers the job (any entry count)
-bool compress_wave_ok(const CompressArgs& x);
+// true when the wave-per-entry arithmetic covers the job (any entry count);
+// MXFP4 output only where the caller instantiates it (the decode front)
+bool compress_wave_ok(const CompressArgs& x, bool mx4_out = false);
 
 }  // namespace csa

@@ -595,7 +595,13 @@ __global__ __launch_bounds__(256) void index_decode_front(
   // a 1-D grid: gx indexer workgroups per sequence, then one front workgroup
   // per sequence at the end, so the indexer's workgroups spread over the
   // compute units as they do alone (two per unit at the 1M decode) and the
-  // light front workgroups take the slots left over
+  // light front workgroups take the slots left over.  Measured slower: the
+  // front workgroups first (1M decode 106 against 102 us); leaving their slots
+  // out of the indexer's round when bf16 keys allow two waves per SIMD
+  // (Flash-like decode 17.6 against 16.8 us: half the indexer's waves); and
+  // the key wave scoring the unit's older subtiles before its compression
+  // (Flash-like 19.1 against 16.8 us: at that shape the front workgroup runs
+  // after an indexer workgroup ends, and the extra round trip is in its path)
   const int nidx = gx * B;
   if ((int)blockIdx.x < nidx) {
     // the indexer over every unit but the last; its rows past the scored ones
@@ -658,21 +664,19 @@ __device__ __forceinline__ float mx4_partial(const u32x4_t (&qa)[QH], const int 
   return part;
 }
 
+// One wave's share of query row (b, t) (as index_decode_wave): units wid,
+// wid + W, ... below nunits, over key rows 0 .. n_keys - 1 of N_cap.
 template <int QH>
-__global__ __launch_bounds__(256) void index_mx4_decode(
+__device__ __forceinline__ void index_mx4_wave(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ K,
-    const uint8_t* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
-    float* __restrict__ out, int flush_ok) {
+    const uint8_t* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, long long n_keys, int m,
+    float* __restrict__ out, int flush_ok, int b, int t, long long wid, long long W, long long nunits) {
   constexpr int H = 16 * QH, DI = 128, RB = DI / 2, SB = DI / 32;   // code and scale bytes per key
   constexpr int PF = 8;   // subtiles in flight per wave (two groups of four)
   constexpr int U = IDX_UNIT;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int b = blockIdx.z, t = blockIdx.y;
   const size_t qrow = (size_t)b * Tq + t;
-  const long long W = 4LL * gridDim.x;
-  const long long wid = 4LL * blockIdx.x + wave;
-  const long long nunits = (N_cap + 16 * U - 1) / (16 * U);
   if (wid >= nunits) return;
   const int nls = (int)((nunits - 1 - wid) / W + 1) * U;   // subtiles of this wave (a multiple of 4)
   __builtin_assume(nls >= 1);
@@ -680,7 +684,7 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
   const long long nvis = min(N_cap, (i + 1) / m);
   const int wid32 = (int)wid, W32 = (int)W;
   auto key0 = [&](int ls) -> int { return 16 * ((wid32 + W32 * (ls / U)) * U + ls % U); };
-  const int klast = (int)(N_cap - 1);
+  const int klast = (int)(n_keys - 1);
   const uint8_t* Kb = K + (size_t)b * (size_t)N_cap * RB;
   const uint8_t* Sb = Ks + (size_t)b * (size_t)N_cap * SB;
   float* orow = out + qrow * (size_t)N_cap;
@@ -801,6 +805,108 @@ __global__ __launch_bounds__(256) void index_mx4_decode(
         if (key + c <= klast) orow[key + c] = v[c];
     }
   }
+}
+
+template <int QH>
+__global__ __launch_bounds__(256) void index_mx4_decode(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint8_t* __restrict__ K,
+    const uint8_t* __restrict__ Ks, const int* __restrict__ q_pos, int Tq, long long N_cap, int m,
+    float* __restrict__ out, int flush_ok) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  index_mx4_wave<QH>(q, w, K, Ks, q_pos, Tq, N_cap, N_cap, m, out, flush_ok, blockIdx.z, blockIdx.y,
+                     4LL * blockIdx.x + wave, 4LL * gridDim.x, (N_cap + 16 * IDX_UNIT - 1) / (16 * IDX_UNIT));
+}
+
+// The decode front with MXFP4 keys (as index_decode_front): the last unit's
+// scores by the key wave, with index_mx4_wave's arithmetic -- the query
+// quantised by the same rule, one block-scaled product per 16-head tile,
+// the reduce-scatter over the unit's four subtiles, the mask.
+template <int QH>
+__device__ __forceinline__ void mx4_score_unit(const uint16_t* __restrict__ q, const float* __restrict__ w,
+                                               const uint8_t* __restrict__ K, const uint8_t* __restrict__ Ks,
+                                               const int* __restrict__ q_pos, long long N_cap, int m,
+                                               float* __restrict__ out, int b, long long key0) {
+  constexpr int H = 16 * QH, DI = 128, RB = DI / 2, SB = DI / 32;
+  const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15;
+  u32x4_t qa[QH];
+  int qsc[QH];
+  float wv[QH][4];
+#pragma unroll
+  for (int mt = 0; mt < QH; ++mt) {
+    const uint16_t* qp = q + ((size_t)b * H + 16 * mt + j) * (size_t)DI + 32 * g;
+    u32x4_t raw[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[c] = *(const u32x4_t*)(qp + 8 * c);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = w[(size_t)b * H + 16 * mt + 4 * g + r];
+    float x[32];
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[8 * c + 2 * e] = __uint_as_float(raw[c][e] << 16);
+        x[8 * c + 2 * e + 1] = __uint_as_float(raw[c][e] & 0xffff0000u);
+        a = fmaxf(a, fmaxf(fabsf(x[8 * c + 2 * e]), fabsf(x[8 * c + 2 * e + 1])));
+      }
+    const int se = mx4_shared_exp(a);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t pk = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk |= f32_to_e2m1(ldexpf(x[8 * d + e], -se)) << (4 * e);
+      qa[mt][d] = pk;
+    }
+    qsc[mt] = se + 127;
+  }
+  const uint8_t* Kb = K + (size_t)b * (size_t)N_cap * RB;
+  const uint8_t* Sb = Ks + (size_t)b * (size_t)N_cap * SB;
+  float P[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t row = (size_t)(key0 + 16 * u + j);
+    const u32x4_t c = *(const u32x4_t*)(Kb + row * RB + 16 * g);
+    const uint32_t sc = *(const uint32_t*)(Sb + row * SB);
+    P[u] = mx4_partial<QH>(qa, qsc, wv, c, (int)((sc >> (8 * g)) & 0xffu));
+  }
+  const float v = reduce_scatter4(P, g);
+  const long long key = key0 + 16 * g + j;
+  const long long nvis = min(N_cap, ((long long)q_pos[b] + 1) / m);
+  out[(size_t)b * (size_t)N_cap + (size_t)key] = key < nvis ? v : -INFINITY;
+}
+
+template <int QH>
+__global__ __launch_bounds__(256) void index_mx4_front(
+    const FrontJobs fj, const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ K, const uint8_t* __restrict__ Ks, const int* __restrict__ q_pos,
+    long long N_cap, int m, float* __restrict__ out, int flush_ok, int gx, int B) {
+  (void)fj;
+  const FrontJobs& F = *(const FrontJobs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long nunits = N_cap / (16 * IDX_UNIT);   // (host: N_cap % 64 == 0)
+  const int nidx = gx * B;
+  if ((int)blockIdx.x < nidx) {
+    const int b = (int)blockIdx.x / gx, x = (int)blockIdx.x - b * gx;
+    index_mx4_wave<QH>(q, w, K, Ks, q_pos, 1, N_cap, N_cap - 16 * IDX_UNIT, m, out, flush_ok, b, 0,
+                       4LL * x + wave, 4LL * gx, nunits - 1);
+    return;
+  }
+  const int b = (int)blockIdx.x - nidx;
+  if (wave < F.n_jobs) {
+    const CompressJob& J = F.job[wave];
+    for (long long e = 0; e < J.n_entries; ++e) {
+      const long long s = J.s_begin + e;
+      if (J.out_dtype == DT_MX4) compress_entry_wave<DT_BF16, DT_MX4, COMPW_MAXC>(J, s, b, lane);
+      else compress_entry_wave<DT_BF16, DT_BF16, COMPW_MAXC>(J, s, b, lane);
+    }
+  }
+  if (wave != F.key_job) return;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // (through the key job's own pointers, equal to K and Ks; see index_decode_front)
+  mx4_score_unit<QH>(q, w, (const uint8_t*)F.job[F.key_job].E, (const uint8_t*)F.job[F.key_job].E_scale, q_pos,
+                     N_cap, m, out, b, 16 * IDX_UNIT * (nunits - 1));
 }
 
 // ---------------------------------------------------------------------------
@@ -1061,6 +1167,23 @@ static void launch_front_ks(const FrontJobs& fj, const IndexArgs& a, hipStream_t
   else launch_front_k<QH, 4>(fj, a, st);
 }
 
+// the decode front with MXFP4 keys (index_mx4_front)
+template <int QH>
+static void launch_front_mx4(const FrontJobs& fj, const IndexArgs& a, hipStream_t st) {
+  auto kfn = index_mx4_front<QH>;
+  const long long waves = resident_waves((const void*)kfn, 256);
+  const long long nunits = a.N_cap / (16 * IDX_UNIT) - 1;
+  long long wpr = 1;
+  while (2 * wpr <= waves / a.B) wpr *= 2;
+  wpr = std::max(wpr, (nunits * 16 * IDX_UNIT + IDX_STAGE - 1) / IDX_STAGE);
+  wpr = std::min(wpr, nunits);
+  const int gx = (int)((wpr + 3) / 4);
+  const int flush_ok = (((uintptr_t)a.out) & 15u) == 0;
+  hipLaunchKernelGGL(kfn, dim3((unsigned)((gx + 1) * a.B)), dim3(256), 0, st, fj, (const uint16_t*)a.q, a.w,
+                     (const uint8_t*)a.K, (const uint8_t*)a.K_scale, a.q_pos, a.N_cap, a.m, a.out, flush_ok, gx,
+                     a.B);
+}
+
 int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a, hipStream_t st,
                         const char** why) {
   *why = nullptr;
@@ -1068,7 +1191,9 @@ int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a
     *why = w;
     return -1;
   };
-  if (!index_mfma_supported(a)) return no("the indexer shape has no matrix-core kernel");
+  const bool mx4 = a.k_dtype == DT_MX4;
+  if (mx4 ? !index_mx4_supported(a) : !index_mfma_supported(a))
+    return no("the indexer shape has no matrix-core decode kernel");
   if (a.Tq != 1) return no("one query row per sequence");
   if (a.N_cap % (16 * IDX_UNIT) != 0 || a.N_cap < 2 * 16 * IDX_UNIT)
     return no("N_cap must be a multiple of 64, at least 128");
@@ -1080,14 +1205,17 @@ int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a
   fj.key_job = -1;
   for (int q = 0; q < n_jobs; ++q) {
     const CompressArgs& x = jobs[q];
-    if (x.in_dtype != DT_BF16 || (x.out_dtype != DT_BF16 && x.out_dtype != DT_FP8) || !compress_wave_ok(x))
+    // bf16 rows beside either indexer; fp8 key rows beside the fp8 one, MXFP4 beside the MXFP4 one
+    const bool fmt = x.out_dtype == DT_BF16 || x.out_dtype == (mx4 ? DT_MX4 : DT_FP8);
+    if (x.in_dtype != DT_BF16 || !fmt || !compress_wave_ok(x, mx4))
       return no("a compress job the wave-per-entry compressor does not cover (bf16 inputs in 16-byte pieces, "
-                "at most 8 candidates, bf16 or fp8 output)");
+                "at most 8 candidates, bf16 output, or the key format)");
     if (x.B != a.B) return no("every compress job has the indexer's batch");
     if (x.E == a.K) {
       if (fj.key_job >= 0) return no("one compress job writes the key rows");
+      const bool scaled = a.k_dtype == DT_FP8 || mx4;
       if (x.out_dtype != a.k_dtype || x.c != a.dI || x.out_ring != 0 || x.out_bs != a.N_cap * (long long)a.dI ||
-          (a.k_dtype == DT_FP8 && x.E_scale != a.K_scale))
+          (scaled && (const void*)x.E_scale != (const void*)a.K_scale))
         return no("the key job must write K_I's rows (and K_scale) in the indexer's layout");
       if (x.s_begin < a.N_cap - 16 * IDX_UNIT || x.s_end > a.N_cap)
         return no("the key job's entries must lie in the last 64 rows of K_I");
@@ -1096,9 +1224,17 @@ int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a
     fj.job[q] = make_compress_job(x, 1);
   }
   if (fj.key_job < 0) return no("no compress job writes K_I");
-  if (a.H == 16) launch_front_ks<1>(fj, a, st);
-  else if (a.H == 32) launch_front_ks<2>(fj, a, st);
-  else launch_front_ks<4>(fj, a, st);
+  if (mx4) {
+    if (a.H == 16) launch_front_mx4<1>(fj, a, st);
+    else if (a.H == 32) launch_front_mx4<2>(fj, a, st);
+    else launch_front_mx4<4>(fj, a, st);
+  } else if (a.H == 16) {
+    launch_front_ks<1>(fj, a, st);
+  } else if (a.H == 32) {
+    launch_front_ks<2>(fj, a, st);
+  } else {
+    launch_front_ks<4>(fj, a, st);
+  }
   return 0;
 }
 

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import codecs as oc
 from oracle import csa as O
 from synth import Gen
 from tests._util import TOL_BF16, TOL_F32, e4m3_ulp, row_rel_err, to_f64
@@ -29,6 +30,8 @@ CASES = [
     ("bf16_h32_d64_kv256", 2, 256, 32, 64, 256, "bf16", "all"),
     ("fp8_h16_d32_masked_last_unit", 2, 320, 16, 32, 128, "e4m3", "partial"),
     ("bf16_flash_like_shape", 8, 16384, 64, 128, 512, "bf16", "all"),
+    ("mxfp4_h64_d128_kv512", 3, 512, 64, 128, 512, "mxfp4", "all"),
+    ("mxfp4_h32_d128_masked_last_unit", 2, 320, 32, 128, 256, "mxfp4", "partial"),
 ]
 
 
@@ -53,6 +56,9 @@ def _inputs(case):
     x["W"] = g.normal(12, (B, W_CAP, d), "bf16")
     if kdt == "e4m3":
         x["K"], x["Ks"] = g.normal_e4m3(13, (B, N, dI))
+    elif kdt == "mxfp4":   # any code byte is two E2M1 values; scales 2^-7 .. 2^3
+        x["K"] = (g.uniform(13, (B, N, dI // 2)) * 256).to(torch.uint8).contiguous()
+        x["Ks"] = (120 + g.uniform(16, (B, N, dI // 32)) * 11).to(torch.uint8).contiguous()
     else:
         x["K"], x["Ks"] = g.normal(13, (B, N, dI), "bf16"), None
     x["qI"] = g.normal(14, (B, 1, H, dI), "bf16")
@@ -124,6 +130,26 @@ def test_decode_front_parity(csa, case):
                            s_end=i0 + 1, gamma=gam, rope_dim=ROPE)
         assert row_rel_err(to_f64(Wa[b, slot:slot + 1]), ref_w) <= TOL_BF16
         ref_k = O.compress(f64["ICa"], f64["IZa"], f64["ICb"], f64["IZb"], normalize=False, **kv)
+        if x["kdt"] == "mxfp4":
+            # scale bytes as the oracle's except where the block maximum lies within
+            # fp32 rounding of a power of two; every code a correct E2M1 rounding in
+            # units of the device's scale
+            _, rs = O.quantize_rows_mxfp4(ref_k)
+            got_s = Ksa[b, N - 1:].cpu().numpy().astype(np.int64)
+            bmax = np.abs(ref_k).reshape(1, x["dI"] // 32, 32).max(axis=-1)
+            near = np.abs(np.log2(bmax) - np.round(np.log2(bmax))) < 1e-5
+            assert np.all((got_s == rs) | near)
+            y = ref_k / np.repeat(np.ldexp(1.0, got_s - 127), 32, axis=-1)
+            dec = oc.e2m1_to_f64(oc.unpack_fp4(Ka[b, N - 1:].cpu().numpy()))
+            spacing = np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+            assert np.all(np.abs(dec - np.clip(y, -6, 6)) <= 0.5 * spacing * (1 + 1e-3) + 1e-6)
+            ref = O.index_score_mxfp4(to_f64(x["qI"][b]), to_f64(x["w"][b]), oc.unpack_fp4(Ka[b].cpu().numpy()),
+                                      Ksa[b].cpu().numpy(), to_f64(x["pos"][b]), m=M)
+            got = to_f64(Ia[b])
+            assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+            fin = np.isfinite(ref)
+            assert row_rel_err(np.where(fin, got, 0.0), np.where(fin, ref, 0.0)) <= TOL_F32
+            continue
         if Ksa is None:
             assert row_rel_err(to_f64(Ka[b, N - 1:]), ref_k) <= TOL_BF16
             keys = to_f64(Ka[b])
@@ -144,7 +170,8 @@ def test_decode_front_parity(csa, case):
 
 
 def test_decode_front_unsupported_launches_nothing(csa):
-    """MXFP4 keys are not covered: CSA_E_UNSUPPORTED, every buffer untouched."""
+    """MXFP4 keys with no job writing them (the key job writes fp8 rows elsewhere):
+    CSA_E_UNSUPPORTED, every buffer untouched."""
     x = _inputs(CASES[0])
     B, N, dI = x["B"], x["N"], x["dI"]
     Ea, Wa, Ka, Ksa = _clones(x)
