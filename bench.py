@@ -651,8 +651,8 @@ def main():
             "workload": mk["workload"], "replicas": mk["replicas"], "graph": mk["graph"],
             "ms_per_step": round(mk["ms_per_step"], 5),
             "tokens/s": round(CSA_DECODE_1M_MIXED.B / (mk["ms_per_step"] * 1e-3), 1),
-            "step_ms_with_events": mk["step_ms_with_events"], "index_ms": mk["index_ms"],
-            "algorithmic_bytes": mk["bytes"],
+            "step_ms_with_events": mk["step_ms_with_events"], "fused_front": mk["fused_front"],
+            "index_ms": mk["index_ms"], "algorithmic_bytes": mk["bytes"],
             "roofline": _roof(mk["bytes"]["step"] / (mk["ms_per_step"] * 1e-3) / 1e9, "hbm", scope="whole step")}
         result["grouped_out_proj"] = grouped_out_proj(steps=20, warmup=3)
         result["cache_append"] = cache_append(steps=50, warmup=5)

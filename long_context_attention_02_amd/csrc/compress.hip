@@ -616,7 +616,7 @@ size_t compress_workspace_bytes(const CompressArgs* a, int n_jobs) {
   return ws_align(ss * 4) + rows * 4;
 }
 
-bool compress_wave_ok(const CompressArgs& x, bool mx4_out) {
+bool compress_wave_ok(const CompressArgs& x, bool mx4_out, bool mix_out) {
   const int ncand_max = x.overlap ? 2 * x.m : x.m;
   const int vec = x.in_dtype == DT_F32 ? 4 : 8;
   // 16-byte pieces: every input row and (for bf16 output) every output row starts 16-byte aligned
@@ -627,8 +627,12 @@ bool compress_wave_ok(const CompressArgs& x, bool mx4_out) {
   // 4-byte words)
   const bool mx4 = mx4_out && x.out_dtype == DT_MX4 && x.in_dtype == DT_BF16 && x.c % 32 == 0 &&
                    (((uintptr_t)x.E) & 3u) == 0 && x.out_bs % 8 == 0;
+  // mixed rows of c + rope_dim bytes whose pieces stay whole: 8-byte code words,
+  // 16-byte bf16 words
+  const bool mix = mix_out && x.out_dtype == DT_MIX && x.in_dtype == DT_BF16 && x.rope_dim % 8 == 0 &&
+                   aligned16(x.E) && (x.c + x.rope_dim) % 16 == 0 && (x.c - x.rope_dim) % 16 == 0;
   const bool out_al = (x.out_dtype != DT_BF16 || (aligned16(x.E) && x.out_bs % 8 == 0)) &&
-                      (x.out_dtype != DT_MX4 || mx4) && x.out_dtype != DT_MIX;
+                      (x.out_dtype != DT_MX4 || mx4) && (x.out_dtype != DT_MIX || mix);
   return ncand_max <= COMPW_MAXC && x.c % 8 == 0 && x.c <= 64 * COMPW_MAXP * vec &&
          x.rope_dim <= COMPW_MAXR && in_al && out_al;
 }

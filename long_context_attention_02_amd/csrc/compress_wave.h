@@ -196,11 +196,12 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
       }
       pooled[pi][e] = v0;
       pooled[pi][e + 1] = v1;
-      if (lane + 64 * pi < npieces) amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
+      // (mixed rows: the maximum of the fp8 part only)
+      if (lane + 64 * pi < npieces && (ODT != DT_MIX || j < rbeg)) amax = fmaxf(amax, fmaxf(fabsf(v0), fabsf(v1)));
     }
   }
   float scale = 1.f;
-  if constexpr (ODT == DT_FP8) {
+  if constexpr (ODT == DT_FP8 || ODT == DT_MIX) {
     const float am = wave_reduce_f<true>(amax);
     scale = am > 0.f ? am / 448.0f : 1.0f;
     if (lane == 0) J.E_scale[(size_t)b * (size_t)(J.out_bs / c) + (size_t)orow] = scale;
@@ -218,6 +219,24 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
     } else if constexpr (ODT == DT_FP8) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) ((uint8_t*)J.E)[o + e] = f32_to_e4m3(pooled[pi][e] / scale);
+    } else if constexpr (ODT == DT_MIX) {
+      // mixed row (c + rope_dim bytes): e4m3 codes of channels [0, rbeg) under
+      // the row scale, then bf16 of the rotated channels; a piece lies wholly
+      // on one side (rope_dim % 8 == 0).  Used by the decode front only.
+      static_assert(VEC == 8, "mixed rows from bf16 pieces");
+      const int j0 = (lane + 64 * pi) * VEC;
+      uint8_t* rb = (uint8_t*)J.E + ((size_t)b * (size_t)(J.out_bs / c) + (size_t)orow) * (size_t)(c + J.rope_dim);
+      if (j0 < rbeg) {
+        u32x2_t w2 = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) w2[e / 4] |= (uint32_t)f32_to_e4m3(pooled[pi][e] / scale) << (8 * (e % 4));
+        *(u32x2_t*)(rb + j0) = w2;
+      } else {
+        u32x4_t w4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(pooled[pi][2 * e], pooled[pi][2 * e + 1]);
+        *(u32x4_t*)(rb + rbeg + 2 * (j0 - rbeg)) = w4;
+      }
     } else if constexpr (ODT == DT_MX4) {
       // MXFP4 (OCP MX: E2M1 codes, one E8M0 scale per 32 channels): a block is
       // the 8-channel pieces of four consecutive lanes (c % 32 == 0, VEC = 8);
@@ -250,7 +269,8 @@ __device__ __forceinline__ void compress_entry_wave(const CompressJob& J, long l
 // the job record of one compression (host): G token groups (wide kernel)
 CompressJob make_compress_job(const CompressArgs& x, int G);
 // true when the wave-per-entry arithmetic covers the job (any entry count);
-// MXFP4 output only where the caller instantiates it (the decode front)
-bool compress_wave_ok(const CompressArgs& x, bool mx4_out = false);
+// MXFP4 and mixed-row output only where the caller instantiates them (the
+// decode front)
+bool compress_wave_ok(const CompressArgs& x, bool mx4_out = false, bool mix_out = false);
 
 }  // namespace csa

@@ -617,6 +617,7 @@ __global__ __launch_bounds__(256) void index_decode_front(
     for (long long e = 0; e < J.n_entries; ++e) {
       const long long s = J.s_begin + e;
       if (J.out_dtype == DT_FP8) compress_entry_wave<DT_BF16, DT_FP8, COMPW_MAXC>(J, s, b, lane);
+      else if (J.out_dtype == DT_MIX) compress_entry_wave<DT_BF16, DT_MIX, COMPW_MAXC>(J, s, b, lane);
       else compress_entry_wave<DT_BF16, DT_BF16, COMPW_MAXC>(J, s, b, lane);
     }
   }
@@ -897,6 +898,7 @@ __global__ __launch_bounds__(256) void index_mx4_front(
     for (long long e = 0; e < J.n_entries; ++e) {
       const long long s = J.s_begin + e;
       if (J.out_dtype == DT_MX4) compress_entry_wave<DT_BF16, DT_MX4, COMPW_MAXC>(J, s, b, lane);
+      else if (J.out_dtype == DT_MIX) compress_entry_wave<DT_BF16, DT_MIX, COMPW_MAXC>(J, s, b, lane);
       else compress_entry_wave<DT_BF16, DT_BF16, COMPW_MAXC>(J, s, b, lane);
     }
   }
@@ -1205,11 +1207,12 @@ int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a
   fj.key_job = -1;
   for (int q = 0; q < n_jobs; ++q) {
     const CompressArgs& x = jobs[q];
-    // bf16 rows beside either indexer; fp8 key rows beside the fp8 one, MXFP4 beside the MXFP4 one
-    const bool fmt = x.out_dtype == DT_BF16 || x.out_dtype == (mx4 ? DT_MX4 : DT_FP8);
-    if (x.in_dtype != DT_BF16 || !fmt || !compress_wave_ok(x, mx4))
+    // bf16 or mixed rows beside either indexer; fp8 key rows beside the fp8
+    // one, MXFP4 beside the MXFP4 one
+    const bool fmt = x.out_dtype == DT_BF16 || x.out_dtype == DT_MIX || x.out_dtype == (mx4 ? DT_MX4 : DT_FP8);
+    if (x.in_dtype != DT_BF16 || !fmt || !compress_wave_ok(x, mx4, true))
       return no("a compress job the wave-per-entry compressor does not cover (bf16 inputs in 16-byte pieces, "
-                "at most 8 candidates, bf16 output, or the key format)");
+                "at most 8 candidates, bf16 or mixed-row output, or the key format)");
     if (x.B != a.B) return no("every compress job has the indexer's batch");
     if (x.E == a.K) {
       if (fj.key_job >= 0) return no("one compress job writes the key rows");

@@ -32,7 +32,10 @@ CASES = [
     ("bf16_flash_like_shape", 8, 16384, 64, 128, 512, "bf16", "all"),
     ("mxfp4_h64_d128_kv512", 3, 512, 64, 128, 512, "mxfp4", "all"),
     ("mxfp4_h32_d128_masked_last_unit", 2, 320, 32, 128, 256, "mxfp4", "partial"),
+    # KV entry and window row stored as mixed rows (e4m3 codes + row scale, bf16 rotated dims)
+    ("fp8_keys_mixed_kv_rows", 3, 512, 64, 128, 512, "e4m3", "all"),
 ]
+MIXED = {"fp8_keys_mixed_kv_rows"}
 
 
 @pytest.fixture(scope="module")
@@ -47,13 +50,20 @@ def _inputs(case):
     name, B, N, H, dI, d, kdt, pmode = case
     g = Gen(900 + CASES.index(case), DEV)
     i0 = M * N                                       # the new token (its block starts a new entry)
-    x = dict(B=B, N=N, H=H, dI=dI, d=d, kdt=kdt, i0=i0)
+    x = dict(B=B, N=N, H=H, dI=dI, d=d, kdt=kdt, i0=i0, mixed=name in MIXED)
     x["Ca"], x["Za"], x["Cb"], x["Zb"] = (g.normal(t, (B, 2 * M, d), "bf16") for t in (1, 2, 3, 4))
     x["ICa"], x["IZa"], x["ICb"], x["IZb"] = (g.normal(t, (B, 2 * M, dI), "bf16") for t in (5, 6, 7, 8))
     x["win"] = g.normal(9, (B, 1, d), "bf16")
     x["gamma"] = (1.0 + 0.25 * g.normal(10, (d,), "f32", per_slot=False)).contiguous()
-    x["E"] = g.normal(11, (B, N, d), "bf16")
-    x["W"] = g.normal(12, (B, W_CAP, d), "bf16")
+    if x["mixed"]:   # any bytes (overwritten rows are compared, the others must not change)
+        x["E"] = (g.uniform(11, (B, N, d + ROPE)) * 256).to(torch.uint8).contiguous()
+        x["W"] = (g.uniform(12, (B, W_CAP, d + ROPE)) * 256).to(torch.uint8).contiguous()
+        x["Es"] = g.uniform(17, (B, N)) + 0.5
+        x["Ws"] = g.uniform(18, (B, W_CAP)) + 0.5
+    else:
+        x["E"] = g.normal(11, (B, N, d), "bf16")
+        x["W"] = g.normal(12, (B, W_CAP, d), "bf16")
+        x["Es"] = x["Ws"] = None
     if kdt == "e4m3":
         x["K"], x["Ks"] = g.normal_e4m3(13, (B, N, dI))
     elif kdt == "mxfp4":   # any code byte is two E2M1 values; scales 2^-7 .. 2^3
@@ -71,20 +81,39 @@ def _inputs(case):
     return x
 
 
-def _jobs(x, E, W, K, Ks):
+def _jobs(x, E, W, K, Ks, Es=None, Ws=None):
     N, i0 = x["N"], x["i0"]
     kv = dict(T=M * N, m=M, overlap=1, s_begin=N - 1, s_end=N, tok_base=M * (N - 2))
     return [
         (x["win"], None, None, None, W,
          dict(T=i0 + 1, m=1, overlap=0, s_begin=i0, s_end=i0 + 1, tok_base=i0, gamma=x["gamma"],
-              rope_dim=ROPE, out_ring=W_CAP)),
-        (x["Ca"], x["Za"], x["Cb"], x["Zb"], E, dict(kv, gamma=x["gamma"], rope_dim=ROPE)),
+              rope_dim=ROPE, out_ring=W_CAP, pos_stride=1, E_scale=Ws)),
+        (x["Ca"], x["Za"], x["Cb"], x["Zb"], E, dict(kv, gamma=x["gamma"], rope_dim=ROPE, E_scale=Es)),
         (x["ICa"], x["IZa"], x["ICb"], x["IZb"], K, dict(kv, E_scale=Ks)),
     ]
 
 
+def _cl(t):
+    return None if t is None else t.clone()
+
+
 def _clones(x):
-    return (x["E"].clone(), x["W"].clone(), x["K"].clone(), None if x["Ks"] is None else x["Ks"].clone())
+    return tuple(_cl(x[k]) for k in ("E", "W", "K", "Ks", "Es", "Ws"))
+
+
+def _check_mixed_rows(got, got_s, ref, d):
+    """Mixed rows against the oracle: rotated dims within bf16, the row scale
+    fp32(absmax) / 448 of the other dims, every code a correct e4m3 rounding in
+    units of that scale (up to rounding ties of the fp32-vs-fp64 value)."""
+    nope = d - ROPE
+    rot = to_f64(got[:, nope:].contiguous().view(torch.bfloat16))
+    assert row_rel_err(rot, ref[:, nope:]) <= TOL_BF16
+    _, _, rs = O.quantize_rows_mixed(ref, ROPE)
+    sc = to_f64(got_s)
+    assert np.allclose(sc, rs, rtol=2e-6, atol=0)
+    y = ref[:, :nope] / sc[:, None]
+    dec = oc.e4m3_to_f64(got[:, :nope].cpu().numpy())
+    assert np.all(np.abs(dec - y) <= 0.5 * e4m3_ulp(y) * (1 + 1e-3) + 1e-6 * 448)
 
 
 def _bits(t):
@@ -96,13 +125,13 @@ def test_decode_front_parity(csa, case):
     x = _inputs(case)
     B, N, d, i0 = x["B"], x["N"], x["d"], x["i0"]
     # one launch
-    Ea, Wa, Ka, Ksa = _clones(x)
+    Ea, Wa, Ka, Ksa, Esa, Wsa = _clones(x)
     Ia = torch.full((B, 1, N), float("nan"), device=DEV)
-    csa.csa_decode_front(_jobs(x, Ea, Wa, Ka, Ksa), x["qI"], x["w"], Ka, x["pos"], Ia, m=M, K_scale=Ksa)
+    csa.csa_decode_front(_jobs(x, Ea, Wa, Ka, Ksa, Esa, Wsa), x["qI"], x["w"], Ka, x["pos"], Ia, m=M, K_scale=Ksa)
     # the two launches
-    Eb, Wb, Kb, Ksb = _clones(x)
+    Eb, Wb, Kb, Ksb, Esb, Wsb = _clones(x)
     Ib = torch.full((B, 1, N), float("nan"), device=DEV)
-    csa.csa_compress_batch(_jobs(x, Eb, Wb, Kb, Ksb))
+    csa.csa_compress_batch(_jobs(x, Eb, Wb, Kb, Ksb, Esb, Wsb))
     csa.csa_index_score(x["qI"], x["w"], Kb, x["pos"], Ib, m=M, K_scale=Ksb)
     # the indexer alone on the rows the one launch wrote
     Ic = torch.full((B, 1, N), float("nan"), device=DEV)
@@ -119,16 +148,22 @@ def test_decode_front_parity(csa, case):
     assert torch.equal(Wa[:, keep], x["W"][:, keep])
     if Ksa is not None:
         assert torch.equal(Ksa[:, :N - 1], x["Ks"][:, :N - 1])
+    if x["mixed"]:
+        assert torch.equal(Esa[:, :N - 1], x["Es"][:, :N - 1]) and torch.equal(Wsa[:, keep], x["Ws"][:, keep])
 
     gam = to_f64(x["gamma"])
     for b in range(B):
         f64 = {k: to_f64(x[k][b]) for k in ("Ca", "Za", "Cb", "Zb", "ICa", "IZa", "ICb", "IZb", "win")}
         kv = dict(m=M, overlap=1, T=M * N, tok_base=M * (N - 2), s_begin=N - 1, s_end=N)
         ref_e = O.compress(f64["Ca"], f64["Za"], f64["Cb"], f64["Zb"], gamma=gam, rope_dim=ROPE, **kv)
-        assert row_rel_err(to_f64(Ea[b, N - 1:]), ref_e) <= TOL_BF16
         ref_w = O.compress(f64["win"], None, None, None, m=1, overlap=0, T=i0 + 1, tok_base=i0, s_begin=i0,
-                           s_end=i0 + 1, gamma=gam, rope_dim=ROPE)
-        assert row_rel_err(to_f64(Wa[b, slot:slot + 1]), ref_w) <= TOL_BF16
+                           s_end=i0 + 1, gamma=gam, rope_dim=ROPE, pos_stride=1)
+        if x["mixed"]:
+            _check_mixed_rows(Ea[b, N - 1:], Esa[b, N - 1:], ref_e, d)
+            _check_mixed_rows(Wa[b, slot:slot + 1], Wsa[b, slot:slot + 1], ref_w, d)
+        else:
+            assert row_rel_err(to_f64(Ea[b, N - 1:]), ref_e) <= TOL_BF16
+            assert row_rel_err(to_f64(Wa[b, slot:slot + 1]), ref_w) <= TOL_BF16
         ref_k = O.compress(f64["ICa"], f64["IZa"], f64["ICb"], f64["IZb"], normalize=False, **kv)
         if x["kdt"] == "mxfp4":
             # scale bytes as the oracle's except where the block maximum lies within
@@ -174,7 +209,7 @@ def test_decode_front_unsupported_launches_nothing(csa):
     CSA_E_UNSUPPORTED, every buffer untouched."""
     x = _inputs(CASES[0])
     B, N, dI = x["B"], x["N"], x["dI"]
-    Ea, Wa, Ka, Ksa = _clones(x)
+    Ea, Wa, Ka, Ksa, _, _ = _clones(x)
     K4 = torch.zeros((B, N, dI // 2), dtype=torch.uint8, device=DEV)
     S4 = torch.full((B, N, dI // 32), 127, dtype=torch.uint8, device=DEV)
     I = torch.full((B, 1, N), 7.0, device=DEV)
