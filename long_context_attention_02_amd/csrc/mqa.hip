@@ -1573,18 +1573,22 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
     for (int s = 0; s < CB; ++s) w[s] = *(const uint32_t*)(base + (size_t)min(s0 + s, n_split - 1) * sstride + d0);
   };
   load_block(0);
-  // M over the splits and the sink
+  // M over the splits and the sink.  The first 64 splits' whole records come
+  // with it: for lanes below CB they are the first block's records below (lane
+  // l holds split l), so that block needs no second, dependent load.
   float M = sig;
+  f32x4_t rec0;
   for (int s0 = 0; s0 < n_split; s0 += 64) {
     const int sl = s0 + lane;
-    const float m = mlb[(size_t)min(sl, n_split - 1) * mstride];
-    M = fmaxf(M, wave_reduce_f<true>(sl < n_split ? m : -INFINITY));
+    const f32x4_t r = *(const f32x4_t*)(mlb + (size_t)min(sl, n_split - 1) * mstride);
+    if (s0 == 0) rec0 = r;
+    M = fmaxf(M, wave_reduce_f<true>(sl < n_split ? r[0] : -INFINITY));
   }
   float Z = (sig != -INFINITY) ? __expf(sig - M) : 0.f, o0 = 0.f, o1 = 0.f;
   for (int s0 = 0; s0 < n_split; s0 += CB) {
     if (s0 > 0) load_block(s0);
     const int sl = s0 + (lane & (CB - 1));
-    const f32x4_t rec = *(const f32x4_t*)(mlb + (size_t)min(sl, n_split - 1) * mstride);
+    const f32x4_t rec = s0 == 0 ? rec0 : *(const f32x4_t*)(mlb + (size_t)min(sl, n_split - 1) * mstride);
     const float f = (sl < n_split && rec[0] != -INFINITY) ? rec[1] * __expf(rec[0] - M) : 0.f;
     Z += wave_reduce_f<false>(lane < CB ? f : 0.f);
     const float gl = f * rec[2];
@@ -1606,9 +1610,13 @@ __global__ __launch_bounds__(256) void mqa_combine_kernel(
     o0 = r0;
     o1 = r1;
   }
-  const size_t ob = (row * n_h + h) * (size_t)D + d0;
-  out[ob] = f32_to_bf16_bits(o0);
-  out[ob + 1] = f32_to_bf16_bits(o1);
+  const size_t ob = (row * n_h + h) * (size_t)D + d0;   // even: D is
+  if ((((uintptr_t)out) & 3u) == 0) {
+    *(uint32_t*)(out + ob) = (uint32_t)f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
+  } else {
+    out[ob] = f32_to_bf16_bits(o0);
+    out[ob + 1] = f32_to_bf16_bits(o1);
+  }
 }
 
 // the combine launch: blocks of 8 splits up to 8, else of 64
