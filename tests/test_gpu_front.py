@@ -223,3 +223,71 @@ def test_decode_front_unsupported_launches_nothing(csa):
     torch.cuda.synchronize()
     assert torch.all(I == 7.0)
     assert torch.equal(Ea, x["E"]) and torch.equal(Wa, x["W"])
+
+
+@pytest.mark.parametrize("kind", ["two_new_entries_fp8", "key_job_only_bf16"])
+def test_decode_front_job_shapes(csa, kind):
+    """A key job that writes two entries (an append completing two blocks), with
+    the KV job beside it; and a call whose only job is the key.  Scores equal
+    the indexer's on the written rows bit for bit, and the rows the oracle's."""
+    two = kind.startswith("two")
+    B, N, H, dI, d = (2, 256, 64, 128, 256) if two else (2, 192, 16, 64, 128)
+    n_new = 2 if two else 1
+    g = Gen(950 + int(two), DEV)
+    R = (n_new + 1) * M                                    # candidates of the new entries
+    tok_base = M * (N - n_new - 1)
+    Ca, Za, Cb, Zb = (g.normal(t, (B, R, d), "bf16") for t in (1, 2, 3, 4))
+    ICa, IZa, ICb, IZb = (g.normal(t, (B, R, dI), "bf16") for t in (5, 6, 7, 8))
+    gamma = (1.0 + 0.25 * g.normal(10, (d,), "f32", per_slot=False)).contiguous()
+    E0 = g.normal(11, (B, N, d), "bf16")
+    if two:
+        K0, Ks0 = g.normal_e4m3(13, (B, N, dI))
+    else:
+        K0, Ks0 = g.normal(13, (B, N, dI), "bf16"), None
+    qI, w = g.normal(14, (B, 1, H, dI), "bf16"), g.uniform(15, (B, 1, H))
+    pos = torch.full((B, 1), M * N, dtype=torch.int32, device=DEV)
+    kv = dict(T=M * N, m=M, overlap=1, s_begin=N - n_new, s_end=N, tok_base=tok_base)
+
+    def jobs(E, K, Ks):
+        key = (ICa, IZa, ICb, IZb, K, dict(kv, E_scale=Ks))
+        return [(Ca, Za, Cb, Zb, E, dict(kv, gamma=gamma, rope_dim=ROPE)), key] if two else [key]
+
+    Ea, Ka, Ksa = E0.clone(), K0.clone(), _cl(Ks0)
+    Ia = torch.full((B, 1, N), float("nan"), device=DEV)
+    csa.csa_decode_front(jobs(Ea, Ka, Ksa), qI, w, Ka, pos, Ia, m=M, K_scale=Ksa)
+    Eb, Kb, Ksb = E0.clone(), K0.clone(), _cl(Ks0)
+    Ib = torch.full((B, 1, N), float("nan"), device=DEV)
+    csa.csa_compress_batch(jobs(Eb, Kb, Ksb))
+    csa.csa_index_score(qI, w, Kb, pos, Ib, m=M, K_scale=Ksb)
+    Ic = torch.full((B, 1, N), float("nan"), device=DEV)
+    csa.csa_index_score(qI, w, Ka, pos, Ic, m=M, K_scale=Ksa)
+    torch.cuda.synchronize()
+
+    assert torch.equal(_bits(Ia), _bits(Ic))
+    assert torch.equal(_bits(Ia[..., :N - 64]), _bits(Ib[..., :N - 64]))
+    assert torch.equal(Ka[:, :N - n_new].view(torch.uint8), K0[:, :N - n_new].view(torch.uint8))
+    assert torch.equal(Ea[:, :N - n_new], E0[:, :N - n_new])
+    if not two:
+        assert torch.equal(Ea, E0)
+    okv = dict(m=M, overlap=1, T=M * N, tok_base=tok_base, s_begin=N - n_new, s_end=N)
+    for b in range(B):
+        f = [to_f64(t[b]) for t in (Ca, Za, Cb, Zb, ICa, IZa, ICb, IZb)]
+        if two:
+            ref_e = O.compress(*f[:4], gamma=to_f64(gamma), rope_dim=ROPE, **okv)
+            assert row_rel_err(to_f64(Ea[b, N - n_new:]), ref_e) <= TOL_BF16
+        ref_k = O.compress(*f[4:], normalize=False, **okv)
+        if Ksa is None:
+            assert row_rel_err(to_f64(Ka[b, N - n_new:]), ref_k) <= TOL_BF16
+            keys = to_f64(Ka[b])
+        else:
+            _, rs = O.quantize_rows_e4m3(ref_k)
+            sc = to_f64(Ksa[b, N - n_new:])
+            assert np.allclose(sc, rs, rtol=2e-6, atol=0)
+            y = ref_k / sc[:, None]
+            assert np.all(np.abs(to_f64(Ka[b, N - n_new:]) - y) <= 0.5 * e4m3_ulp(y) * (1 + 1e-3) + 1e-6 * 448)
+            keys = to_f64(Ka[b]) * to_f64(Ksa[b])[:, None]
+        ref = O.index_score(to_f64(qI[b]), to_f64(w[b]), keys, to_f64(pos[b]), m=M)
+        got = to_f64(Ia[b])
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+        fin = np.isfinite(ref)
+        assert row_rel_err(np.where(fin, got, 0.0), np.where(fin, ref, 0.0)) <= TOL_F32
