@@ -138,7 +138,8 @@ def test_tiny_fp32_end_to_end(lib):
                                   "csa_decode_pro_b16_ctx1M_mxfp4keys",
                                   "csa_decode_pro_b16_ctx1M_fp8keys_mixedkv"])
 def test_csa_decode_full_size(lib, name):
-    """A whole decode step at full size.  Every sequence is checked, except for
+    """A whole decode step at full size, through the one-launch front.  Every
+    sequence is checked, except for
     MXFP4 keys, where the oracle's own quantisation of 262,144 keys per sequence
     bounds the CPU time, and for mixed KV rows (a second 1M-context run): there
     four sequences spread over the batch (for MXFP4 the device's key cache is
@@ -157,6 +158,10 @@ def test_csa_decode_full_size(lib, name):
             assert np.array_equal(oc.unpack_fp4(run.KI[b].cpu().numpy()), p["KI_codes"]), b
     run.step()
     torch.cuda.synchronize()
+    # every decode workload's step runs its compressions beside the indexer in one
+    # launch (csa_decode_front); the two-launch path is what the benchmark would
+    # time otherwise
+    assert run.fused_front is True, name
     sel = torch.as_tensor(bs, device="cuda")
     got_I, got_idx = to_f64(run.I[sel, 0]), run.idx[sel, 0].cpu().numpy()
     got_out = to_f64(run.out[sel, 0])
