@@ -1205,8 +1205,16 @@ int launch_decode_front(const CompressArgs* jobs, int n_jobs, const IndexArgs& a
   FrontJobs fj{};
   fj.n_jobs = n_jobs;
   fj.key_job = -1;
+  // the key rows and their scales: only the key job may write there
+  const size_t key_bytes = (size_t)a.B * (size_t)a.N_cap * (size_t)(mx4 ? a.dI / 2 : a.dI * (a.k_dtype == DT_FP8 ? 1 : 2));
+  const size_t ks_bytes = (size_t)a.B * (size_t)a.N_cap * (mx4 ? (size_t)(a.dI / 32) : sizeof(float));
+  auto inside = [](const void* p, const void* lo, size_t n) {
+    return lo && (uintptr_t)p >= (uintptr_t)lo && (uintptr_t)p < (uintptr_t)lo + n;
+  };
   for (int q = 0; q < n_jobs; ++q) {
     const CompressArgs& x = jobs[q];
+    if (x.E != a.K && (inside(x.E, a.K, key_bytes) || inside(x.E_scale, a.K_scale, ks_bytes)))
+      return no("a job other than the key job writes into K_I or K_scale");
     // bf16 or mixed rows beside either indexer; fp8 key rows beside the fp8
     // one, MXFP4 beside the MXFP4 one
     const bool fmt = x.out_dtype == DT_BF16 || x.out_dtype == DT_MIX || x.out_dtype == (mx4 ? DT_MX4 : DT_FP8);

@@ -162,10 +162,11 @@ def test_decode_front_validation(lib):
     the one-launch path does not cover."""
     import long_context_attention_02_amd as csa
     B, H, dI, N = 2, 64, 128, 4096
-    KEYS, SCALES = FAKE + 4096, FAKE + 8192
+    # fake buffers far apart: keys (1 MiB), their scales, the KV rows and the window ring
+    KEYS, SCALES, ROWS = FAKE + (1 << 24), FAKE + (2 << 24), FAKE + (3 << 24)
     win = dict(C_a=FAKE, Z_a=None, C_b=None, Z_b=None, in_dtype=1, B=B, R=1, in_batch_stride=512, tok_base=4 * N,
                T=4 * N + 1, c=512, m=1, overlap=0, s_begin=4 * N, s_end=4 * N + 1, gamma=FAKE, eps=1e-6,
-               rope_dim=64, rope_base=1e4, pos_stride=1, pos_offset=0, E=FAKE + 65536, out_dtype=1,
+               rope_dim=64, rope_base=1e4, pos_stride=1, pos_offset=0, E=ROWS, out_dtype=1,
                E_scale=None, out_batch_stride=128 * 512, out_ring=128)
     key = dict(C_a=FAKE, Z_a=FAKE, C_b=FAKE, Z_b=FAKE, in_dtype=1, B=B, R=8, in_batch_stride=8 * dI,
                tok_base=4 * (N - 2), T=4 * N, c=dI, m=4, overlap=1, s_begin=N - 1, s_end=N, gamma=None,
@@ -191,7 +192,7 @@ def test_decode_front_validation(lib):
     assert call(H_=65) == CSA_E_UNSUPPORTED
     # not covered by the one-launch path
     assert call(N_=N + 32) == CSA_E_UNSUPPORTED                                 # N_cap % 64
-    assert call(jobs=(win,)) == CSA_E_UNSUPPORTED and b"K_I" in lib.csa_last_error()
+    assert call(jobs=(win,)) == CSA_E_UNSUPPORTED and b"no compress job writes K_I" in lib.csa_last_error()
     early = dict(key, tok_base=4 * (N - 101), T=4 * (N - 99), s_begin=N - 100, s_end=N - 99)
     assert call(jobs=(win, early)) == CSA_E_UNSUPPORTED                           # not the last 64 rows
     assert call(jobs=(win, dict(key, out_dtype=1, E_scale=None))) == CSA_E_UNSUPPORTED   # key format != k_dtype
@@ -201,6 +202,10 @@ def test_decode_front_validation(lib):
     assert call(jobs=(win, key, key)) == CSA_E_UNSUPPORTED                       # two jobs write the keys
     assert call(K=KEYS + 8, jobs=(win, dict(key, E=KEYS + 8))) == CSA_E_UNSUPPORTED   # 16-byte alignment
     assert call(kd=3) == CSA_E_UNSUPPORTED                                       # MXFP4 keys
+    # another job writing inside the key rows (or their scales) would race with the indexer
+    assert call(jobs=(dict(win, E=KEYS + 4096), key)) == CSA_E_UNSUPPORTED
+    assert b"K_I or K_scale" in lib.csa_last_error()
+    assert call(jobs=(dict(key, E=ROWS, E_scale=SCALES + 64), key)) == CSA_E_UNSUPPORTED
 
 
 def test_topk_validation_and_workspace(lib):
