@@ -204,7 +204,8 @@ int csa_index_score(const void* q_I, int q_dtype, const float* w_I,
  * E_scale = K_scale for FP8 keys), and its entries lie in the last 64 rows of
  * K_I; the indexer scores the other rows while the job runs, and the wave that
  * wrote the key then scores those last 64 rows.  Other jobs must not write
- * memory the indexer reads.
+ * memory the indexer reads: one whose E or E_scale starts inside K_I or
+ * K_scale is refused (CSA_E_UNSUPPORTED).
  *  Arguments: as csa_compress_batch (jobs, n_jobs <= CSA_DECODE_FRONT_MAX_JOBS,
  *  no workspace) and csa_index_score (Tq = 1: q_I [B][1][H_I][d_I], w_I,
  *  q_pos [B][1], I_out [B][1][N_cap]).
