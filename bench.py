@@ -621,7 +621,9 @@ def main():
             "roofline": _roof(mab["front_kernel" if mx["fused_front"] else "index_kernel"] / (mx_idx_ms * 1e-3) / 1e9,
                               "hbm", kernel=("index_mx4_front (csa_decode_front, MXFP4 keys: the step's "
                                              "compressions beside the indexer)") if mx["fused_front"]
-                              else "index_mx4_decode (csa_index_score, MXFP4 keys)"),
+                              else "index_mx4_decode (csa_index_score, MXFP4 keys)",
+                              traffic=traffic_from_profiles("index_mx4_front_1M", src) if mx["fused_front"] else None,
+                              algorithmic_bytes=mab["front_kernel" if mx["fused_front"] else "index_kernel"]),
             "step_roofline": _roof(mab["step"] / (mms * 1e-3) / 1e9, "hbm", scope="whole step"),
             "recall_at_k_vs_fp8_selection": {"mean": round(sum(recall) / len(recall), 5),
                                              "min": round(min(recall), 5), "k": wl.k,
