@@ -291,6 +291,11 @@ def csa_decode(wl, K: int, warmup: int, use_graph: bool, keep_raw_first: bool = 
     res = {"workload": wl.name, "replicas": R, "graph": err or "hip graph replay",
            "ms_per_step": ms_step, "step_ms_with_events": dist(per_step), "fused_front": fused,
            "index_ms": dist(per_index), "bytes": ab}
+    if fused:
+        # the indexer launch alone (csa_index_score on the same rows), for comparison
+        # with the fused launch that also runs the step's compressions
+        _, alone = time_each([[r.index] for r in runs], K, inner=0)
+        res["index_alone_ms"] = dist(alone)
     return res, runs
 
 
@@ -582,7 +587,12 @@ def main():
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": kern_bytes,
-                     "avg_launch_ms": round(idx_ms, 5), "launch_ms": head["index_ms"]},
+                     "avg_launch_ms": round(idx_ms, 5), "launch_ms": head["index_ms"],
+                     "indexer_alone": None if "index_alone_ms" not in head else {
+                         "kernel": "index_mfma_decode (csa_index_score, the same rows)",
+                         "launch_ms": head["index_alone_ms"],
+                         "frac": round(ab["index_kernel"] / (head["index_alone_ms"]["mean"] * 1e-3) / 1e9
+                                       / HBM_PEAK_GBS, 4)}},
         "step_roofline": {"bound": "hbm", "scope": "whole decode step (compress, index, top-k, attention)",
                           "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(step_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": ab["step"],
