@@ -34,6 +34,10 @@ CASES = [
     ("mxfp4_h32_d128_masked_last_unit", 2, 320, 32, 128, 256, "mxfp4", "partial"),
     # KV entry and window row stored as mixed rows (e4m3 codes + row scale, bf16 rotated dims)
     ("fp8_keys_mixed_kv_rows", 3, 512, 64, 128, 512, "e4m3", "all"),
+    # the smallest cache: one unit for the indexer workgroups, one for the front's key wave
+    ("fp8_h32_d128_min_ncap", 2, 128, 32, 128, 256, "e4m3", "all"),
+    ("bf16_h16_d32_min_ncap_masked", 3, 128, 16, 32, 128, "bf16", "partial"),
+    ("mxfp4_h16_d128_min_ncap", 2, 128, 16, 128, 128, "mxfp4", "all"),
 ]
 MIXED = {"fp8_keys_mixed_kv_rows"}
 
